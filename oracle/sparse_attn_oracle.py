@@ -1,0 +1,240 @@
+"""fp64 CPU oracle for dynamic top-k sparse attention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the tests, the smoke check and the benchmark's CPU
+baseline use it.  It shares no code with the HIP library.
+
+The oracle is the plain definition of what the method computes, written in
+float64 with NumPy, one step per statement, following the pages:
+
+  1. Scorer (page "mhpq.cn/news/1098205", §2.2, LightweightScorer): each
+     head's queries and keys are projected to a low dimension d_proj,
+     q_low = Q·Pq and k_low = K·Pk, and every query-key pair is scored with a
+     scaled dot product, S_ij = score_scale · q_low_i · k_low_j
+     (score_scale defaults to d_proj^-1/2, as in that section).
+  2. Selection (same page, §1.3 two-step allocation and §3.2 torch.topk):
+     each query keeps the k highest-scoring keys.  Keys excluded by a mask
+     (j > i when causal) are removed before selection (§3.2, third
+     implementation note).  With fewer than k valid keys the query keeps all
+     of them (§3.2, second implementation note: fall back to full
+     attention).  Ties go to the lower key index.  A row is written in
+     ascending key order and padded with -1.
+  3. Attention over the kept keys (same page §1.2 formula and §3.2 forward;
+     page "Attention机制优化：原理、挑战与工程实践", §1.1 scaled dot-product
+     steps): logits softmax_scale · q·k_j, a max-subtracted softmax, and the
+     weighted sum of the kept V rows.  softmax_scale defaults to D^-1/2.
+  4. Band mode (page "Attention机制改进：稀疏注意力应用", create_local_mask;
+     page "nxmr.cn/news/163144", §2.2): query i keeps keys
+     max(0, i-w_left) .. min(N-1, i+w_right).
+
+Every function below is pinned by tests against things other than itself
+(brute force, closed forms, dense attention, a hand-derived example); see
+tests/test_oracle_pins.py.  Nothing here is "parity unpinned".
+"""
+from __future__ import annotations
+
+import itertools
+import math
+from typing import Iterable, Optional, Sequence
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- inputs ---
+
+def f64(x) -> np.ndarray:
+    """Exact upcast of a stored tensor (numpy or torch, fp32 or bf16) to fp64."""
+    if isinstance(x, np.ndarray):
+        return x.astype(np.float64)
+    try:  # torch tensor: bf16 -> fp32 is exact, fp32 -> fp64 is exact
+        import torch
+        if isinstance(x, torch.Tensor):
+            return x.detach().to("cpu", torch.float32).numpy().astype(np.float64)
+    except ImportError:  # pragma: no cover
+        pass
+    return np.asarray(x, dtype=np.float64)
+
+
+# ----------------------------------------------------------- 1. scorer ---
+
+def project(X: np.ndarray, P: np.ndarray) -> np.ndarray:
+    """Low-dimensional projection X·P for X [..., D], P [D, d_proj]
+    (page "mhpq.cn/news/1098205", §2.2: q_proj / k_proj to d_proj)."""
+    return np.matmul(X, P)
+
+
+def valid_keys(N: int, i: int, causal: bool) -> np.ndarray:
+    """Boolean mask of the keys query i may select: all N, or j <= i when
+    causal (masked keys are excluded before selection, §3.2 of the same page)."""
+    m = np.ones(N, dtype=bool)
+    if causal:
+        m[i + 1:] = False
+    return m
+
+
+def score_rows(q_low: np.ndarray, k_low: np.ndarray, score_scale: float) -> np.ndarray:
+    """S[r, j] = score_scale · q_low[r] · k_low[j] for the given query rows
+    (one head): q_low [R, d_proj], k_low [N, d_proj] -> [R, N]."""
+    return score_scale * np.matmul(q_low, k_low.T)
+
+
+def scores(Q, K, Pq, Pk, score_scale: float, b: int, h: int,
+           rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """fp64 scores of head (b, h) for the requested query rows (all rows if
+    None) against every key: [R, N].  Masking is not applied here."""
+    Qh = f64(Q[b, h])
+    Kh = f64(K[b, h])
+    q_low = project(Qh if rows is None else Qh[np.asarray(rows)], f64(Pq))
+    k_low = project(Kh, f64(Pk))
+    return score_rows(q_low, k_low, score_scale)
+
+
+# -------------------------------------------------------- 2. selection ---
+
+def topk_row(s: np.ndarray, valid: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of one score row by (score descending, key index ascending),
+    over valid keys only; returned in ascending key order, padded with -1
+    up to k entries."""
+    cand = np.nonzero(valid)[0]
+    keep = min(k, cand.size)
+    # np.lexsort sorts by the last key first: -score ascending (score
+    # descending), then key index ascending for equal scores.
+    order = np.lexsort((cand, -s[cand]))
+    chosen = np.sort(cand[order[:keep]])
+    out = np.full(k, -1, dtype=np.int32)
+    out[:keep] = chosen
+    return out
+
+
+def topk_rows(S: np.ndarray, rows: Sequence[int], k: int, causal: bool) -> np.ndarray:
+    """Apply topk_row to score rows S [R, N] of query rows ``rows``."""
+    N = S.shape[1]
+    return np.stack([topk_row(S[r], valid_keys(N, int(i), causal), k)
+                     for r, i in enumerate(rows)])
+
+
+def topk_indices(Q, K, Pq, Pk, k: int, causal: bool, score_scale: float,
+                 rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """idx [B, H, R, k] (R = N when rows is None) of the full method's
+    selection, computed from fp64 scores."""
+    B, H, N = Q.shape[0], Q.shape[1], Q.shape[2]
+    rows = list(range(N)) if rows is None else [int(r) for r in rows]
+    out = np.empty((B, H, len(rows), k), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            S = scores(Q, K, Pq, Pk, score_scale, b, h, rows)
+            out[b, h] = topk_rows(S, rows, k, causal)
+    return out
+
+
+def brute_force_topk(s: Sequence[float], valid: Sequence[bool], k: int) -> list:
+    """Pure-Python enumeration for tiny rows: the unique subset of
+    min(k, #valid) valid keys in which every member beats every non-member,
+    where a beats b iff s_a > s_b, or s_a == s_b and a < b."""
+    keys = [j for j, ok in enumerate(valid) if ok]
+    size = min(k, len(keys))
+
+    def beats(a, b):
+        return s[a] > s[b] or (s[a] == s[b] and a < b)
+
+    found = []
+    for subset in itertools.combinations(keys, size):
+        inside = set(subset)
+        if all(beats(a, b) for a in subset for b in keys if b not in inside):
+            found.append(sorted(subset))
+    assert len(found) == 1, "the order is total, so exactly one subset qualifies"
+    return found[0]
+
+
+# ------------------------------------------------ 3. attention on a set ---
+
+def attend_row(q: np.ndarray, Kh: np.ndarray, Vh: np.ndarray, sel: np.ndarray,
+               softmax_scale: float) -> np.ndarray:
+    """One query's output over the key list ``sel`` (entries < 0 skipped,
+    repeated entries counted as often as they appear): logits, a
+    max-subtracted softmax, weighted sum of V rows.  No valid entry -> 0."""
+    sel = sel[sel >= 0]
+    if sel.size == 0:
+        return np.zeros(Vh.shape[1])
+    logits = softmax_scale * (Kh[sel] @ q)
+    w = np.exp(logits - logits.max())
+    return (w @ Vh[sel]) / w.sum()
+
+
+def gather_attention(Q, K, V, idx, softmax_scale: float,
+                     rows: Optional[Sequence[int]] = None) -> np.ndarray:
+    """O [B, H, R, D]: attention of each query row over its idx row.
+    ``idx`` is [B, H, R, k] for the given rows (all rows when None)."""
+    Qa, Ka, Va = f64(Q), f64(K), f64(V)
+    idx = np.asarray(idx)
+    B, H, N, D = Qa.shape
+    rows = list(range(N)) if rows is None else [int(r) for r in rows]
+    O = np.zeros((B, H, len(rows), D))
+    for b in range(B):
+        for h in range(H):
+            for r, i in enumerate(rows):
+                O[b, h, r] = attend_row(Qa[b, h, i], Ka[b, h], Va[b, h],
+                                        idx[b, h, r].astype(np.int64), softmax_scale)
+    return O
+
+
+def sparse_attn_fwd(Q, K, V, Pq, Pk, k: int, causal: bool, score_scale: float,
+                    softmax_scale: float, rows: Optional[Sequence[int]] = None):
+    """The whole forward: selection then attention.  Returns (idx, O)."""
+    idx = topk_indices(Q, K, Pq, Pk, k, causal, score_scale, rows)
+    O = gather_attention(Q, K, V, idx, softmax_scale, rows)
+    return idx, O
+
+
+# ------------------------------------------------------- 4. band mode ---
+
+def band_indices(N: int, w_left: int, w_right: int, width: int) -> np.ndarray:
+    """idx [N, width]: keys max(0, i-w_left) .. min(N-1, i+w_right) in
+    ascending order, then -1 padding."""
+    out = np.full((N, width), -1, dtype=np.int32)
+    for i in range(N):
+        lo, hi = max(0, i - w_left), min(N - 1, i + w_right)
+        keys = np.arange(lo, hi + 1)[:width]
+        out[i, :keys.size] = keys
+    return out
+
+
+# --------------------------------- independent dense references (pins) ---
+
+def dense_attention(Q, K, V, softmax_scale: float, mask: Optional[np.ndarray] = None,
+                    causal: bool = False) -> np.ndarray:
+    """Full softmax(Q·Kᵀ·scale [masked]) · V in fp64 over [B,H,N,D]: the
+    standard scaled dot-product attention of page "mhpq.cn/news/1098205"
+    §1.2 and page "Attention机制优化：原理、挑战与工程实践" §1.1, with the
+    -inf masking of page "Attention机制改进：稀疏注意力应用" (mask [N,N],
+    True = allowed).  Written without any index list."""
+    Qa, Ka, Va = f64(Q), f64(K), f64(V)
+    N = Qa.shape[2]
+    logits = np.matmul(Qa, np.swapaxes(Ka, -1, -2)) * softmax_scale
+    allowed = np.ones((N, N), dtype=bool) if mask is None else np.asarray(mask, bool)
+    if causal:
+        allowed = allowed & np.tril(np.ones((N, N), dtype=bool))
+    logits = np.where(allowed, logits, -np.inf)
+    mx = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - mx)
+    p = e / e.sum(axis=-1, keepdims=True)
+    return np.matmul(p, Va)
+
+
+def local_mask(N: int, w: int) -> np.ndarray:
+    """Band mask: key j allowed for query i iff i-w <= j <= i+w."""
+    i = np.arange(N)[:, None]
+    j = np.arange(N)[None, :]
+    return (j >= i - w) & (j <= i + w)
+
+
+def brute_force_attention(q: Sequence[float], Krows: Iterable[Sequence[float]],
+                          Vrows: Iterable[Sequence[float]], softmax_scale: float) -> list:
+    """Direct summation in pure Python floats (tiny inputs only)."""
+    Krows, Vrows = list(Krows), list(Vrows)
+    logits = [softmax_scale * sum(a * b for a, b in zip(q, kr)) for kr in Krows]
+    m = max(logits)
+    w = [math.exp(x - m) for x in logits]
+    tot = sum(w)
+    D = len(Vrows[0])
+    return [sum(w[t] * Vrows[t][d] for t in range(len(w))) / tot for d in range(D)]
