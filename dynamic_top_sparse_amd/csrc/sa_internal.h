@@ -1,0 +1,88 @@
+// Host-side plan of one scores/top-k pass and the kernel launch wrappers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sa_common.h"
+
+namespace sa {
+
+// Tunables of the selection pipeline.
+constexpr int kQueriesPerBlock = 256;   // scorer workgroup: 4 waves x 64 queries
+constexpr int kKeysPerChunk = 128;      // keys staged in LDS per step
+constexpr int kSampleStride = 16;       // the threshold sample takes every 16th key
+constexpr int kRowPad = 2048;           // N is padded to a multiple of this
+constexpr float kTauBeta = 2.0f;        // sample rank slack (see threshold kernel)
+constexpr int kFallbackBlocks = 64;     // workgroups of the exact fallback
+constexpr int kKMax = 2048;             // largest supported k
+
+// Byte offsets of one head chunk's buffers inside the workspace.
+struct Plan {
+  int B, H, N, D, dp, k, causal, dtype;
+  int BH;         // B*H heads
+  int hc;         // heads per chunk
+  int Npad;       // N rounded up to kRowPad
+  int Ns;         // sample keys: ceil(N / kSampleStride)
+  int Nspad;      // Npad / kSampleStride
+  int NB;         // block maxima per query: 2 * ceil(Ns / 32)
+  int capH;       // candidate capacity of one query half
+  int with_idx;   // room for idx rows of the chunk
+  size_t off_hdr, off_qlo32, off_klo32, off_qlo16, off_klo16, off_ksamp, off_qstat,
+      off_kstat, off_bm, off_tau, off_cand, off_cnt, off_fblist, off_fbscratch, off_idx,
+      total;
+};
+
+// Fills every field from the arguments and heads_per_chunk; returns false
+// when the sizes do not fit the index arithmetic.
+bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, int dtype,
+               int with_idx, int heads_per_chunk);
+
+// Pointers of the chunk buffers for a given workspace base.
+struct Bufs {
+  WsHeader* hdr;
+  float* qlo32;
+  float* klo32;
+  bf16_t* qlo16;
+  bf16_t* klo16;
+  bf16_t* ksamp;
+  float2* qstat;        // (||q_low||, ||q_low - bf16(q_low)||), upper bounds
+  uint32_t* kstat;      // per head: max ||k_low||, max residual (fp32 bits)
+  float* bm;            // sample block maxima [hc][NB][Npad]
+  float* tau;           // per-query threshold [hc][Npad]
+  uint2* cand;          // candidates [hc][Npad][2][capH] = (key, raw MFMA sum bits)
+  int* cnt;             // candidates per query half [hc][Npad][2]
+  int* fblist;          // queries queued for the exact fallback
+  float* fbscratch;     // [kFallbackBlocks][Npad] exact scores
+  int32_t* idx;         // optional idx rows [hc][N][k]
+};
+Bufs bufs_of(const Plan& p, void* ws);
+
+// ---------------------------------------------------------- launches ---
+// All return hipSuccess or the launch error.  `h0` is the first head of the
+// chunk, `nh` the number of heads in it; Q, K, V are the full tensors.
+hipError_t launch_init_chunk(const Plan& p, const Bufs& b, int first_chunk, hipStream_t s);
+hipError_t launch_project(const Plan& p, const Bufs& b, const void* Q, const void* K,
+                          const void* Pq, const void* Pk, int h0, int nh, hipStream_t s);
+hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, hipStream_t s);
+hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_scale,
+                            hipStream_t s);
+hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale,
+                         hipStream_t s);
+hipError_t launch_finalize(const Plan& p, const Bufs& b, int nh, float score_scale,
+                           int32_t* idx_chunk, hipStream_t s);
+hipError_t launch_fallback(const Plan& p, const Bufs& b, int nh, float score_scale,
+                           int32_t* idx_chunk, hipStream_t s);
+hipError_t launch_dump(const Plan& p, const Bufs& b, int nh, float score_scale,
+                       int row_begin, int row_count, float* S_chunk, hipStream_t s);
+hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
+                         int k, int nheads, int N, int D, float softmax_scale, int dtype,
+                         void* O, hipStream_t s);
+hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
+                       hipStream_t s);
+
+// Sticky device flag set by the gather when an index is >= N.
+hipError_t read_and_clear_device_flag(int* value, hipStream_t s);
+
+}  // namespace sa

@@ -1,0 +1,358 @@
+// The scorer contraction on bf16 MFMA and the streaming per-query filter
+// (page "mhpq.cn/news/1098205", §2.2: scores are scaled dot products of the
+// low-dimensional rows, S = d_proj^-1/2 · q_low·k_lowᵀ; §3.2: torch.topk
+// keeps the k best keys per query).  No score matrix is ever written: tiles of
+// 32 keys x 32 queries live in MFMA accumulators and are reduced on the spot.
+//
+// The bf16 MFMA result s~ differs from the exact fp32 score s by at most a
+// margin m_i per query (a Cauchy-Schwarz bound built from the row norms the
+// projection kernel stores).  The filter therefore proves, rather than
+// guesses, that it keeps every key of the exact top-k:
+//   1. sample pass: every 16th key is scored and each lane keeps the maximum
+//      of its 16 rows per tile ("block maxima");
+//   2. threshold: tau_i is (a lower rounding of) the r-th largest block
+//      maximum, r = ceil(beta * k * sample / valid keys);
+//   3. filter pass: every valid key with s~ >= tau_i - m_i is appended to the
+//      query's candidate list.
+// The re-rank kernel then checks that at least k candidates have
+// s~ - m_i >= tau_i; that makes tau_i a lower bound of the k-th best exact
+// score, so no key outside the list can belong to the top-k.  Queries whose
+// check fails, or whose list overflows, are handed to the exact fallback.
+//
+// MFMA orientation (v_mfma_f32_32x32x16_bf16): A = 32 keys from LDS, B = 32
+// queries held in registers.  Lane l then owns query l%32 and, in its 16
+// accumulators, keys 8*(r/4) + 4*(l/32) + r%4 of the tile, so the threshold
+// is one register per lane and each lane appends to its own list.
+#include <float.h>
+
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;   // 4 waves
+constexpr int kWaveQueries = 64;
+
+template <int DP>
+struct Tile {
+  static constexpr int kUnits = DP / 8;          // 16-byte units per key row
+  static constexpr int kKSteps = DP / 16;        // MFMA k-steps
+  static constexpr int kChunkUnits = kKeysPerChunk * kUnits;
+};
+
+// Swizzled position (in 16-byte units) of unit u of key row `key` within a
+// staged chunk: the XOR spreads the 32 rows an A-fragment read touches over
+// the LDS banks.
+template <int DP>
+__device__ __forceinline__ int lds_unit(int key, int u) {
+  constexpr int U = Tile<DP>::kUnits;
+  return key * U + (u ^ (key & (U - 1)));
+}
+
+template <int DP>
+__device__ __forceinline__ void stage_chunk(uint4* __restrict__ lds, const bf16_t* __restrict__ rows,
+                                            int key0) {
+  constexpr int U = Tile<DP>::kUnits;
+  const uint4* src = reinterpret_cast<const uint4*>(rows + static_cast<size_t>(key0) * DP);
+  for (int e = threadIdx.x; e < Tile<DP>::kChunkUnits; e += kThreads) {
+    const int key = e / U, u = e % U;
+    lds[lds_unit<DP>(key, u)] = src[e];
+  }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
+  bf16x8 r;
+  __builtin_memcpy(&r, &v, 16);
+  return r;
+}
+
+// B fragments (queries) of one 32-query block: lane l holds query row l%32,
+// model coordinates [16*ks + 8*(l/32), +8).
+template <int DP>
+__device__ __forceinline__ void load_query_frags(bf16x8 (&b)[Tile<DP>::kKSteps],
+                                                 const bf16_t* __restrict__ q16, int q) {
+  const int l = lane_id();
+  const uint4* row = reinterpret_cast<const uint4*>(q16 + static_cast<size_t>(q) * DP);
+#pragma unroll
+  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks) b[ks] = as_bf16x8(row[2 * ks + (l >> 5)]);
+}
+
+template <int DP>
+__device__ __forceinline__ f32x16 tile_scores(const uint4* __restrict__ lds, int tile_in_chunk,
+                                              const bf16x8 (&b)[Tile<DP>::kKSteps]) {
+  const int l = lane_id();
+  const int key = tile_in_chunk * 32 + (l & 31);
+  f32x16 acc = {};
+#pragma unroll
+  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks) {
+    const bf16x8 a = as_bf16x8(lds[lds_unit<DP>(key, 2 * ks + (l >> 5))]);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[ks], acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// Key row of accumulator r for this lane, relative to the tile base.
+__device__ __forceinline__ int acc_row(int r, int half) {
+  return 8 * (r >> 2) + 4 * half + (r & 3);
+}
+
+// ------------------------------------------------------------ sample pass ---
+template <int DP>
+__global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
+    const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp, int N, int Npad, int Ns,
+    int NB, int causal, float* __restrict__ bm) {
+  __shared__ uint4 lds[Tile<DP>::kChunkUnits];
+  const int h = blockIdx.y;
+  const int q0 = blockIdx.x * kQueriesPerBlock;
+  const int w = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int half = l >> 5;
+  const int qw = q0 + w * kWaveQueries;
+  const bf16_t* qh = q16 + static_cast<size_t>(h) * Npad * DP;
+  const bf16_t* sh = samp + static_cast<size_t>(h) * (Npad / kSampleStride) * DP;
+  float* bmh = bm + static_cast<size_t>(h) * NB * Npad;
+
+  bf16x8 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
+  load_query_frags<DP>(b0, qh, qw + (l & 31));
+  load_query_frags<DP>(b1, qh, qw + 32 + (l & 31));
+  const int qa = qw + (l & 31), qb = qw + 32 + (l & 31);
+
+  // sample keys t with stride*t <= last query of the block (causal), else all
+  int s_end = Ns;
+  if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / kSampleStride + 1);
+  const int nchunks = (s_end + kKeysPerChunk - 1) / kKeysPerChunk;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    __syncthreads();
+    stage_chunk<DP>(lds, sh, ch * kKeysPerChunk);
+    __syncthreads();
+#pragma unroll 1
+    for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
+      const int tbase = ch * kKeysPerChunk + tt * 32;
+      if (tbase >= s_end) break;
+      f32x16 a0 = tile_scores<DP>(lds, tt, b0);
+      f32x16 a1 = tile_scores<DP>(lds, tt, b1);
+      float m0 = -INFINITY, m1 = -INFINITY;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int t = tbase + acc_row(r, half);
+        const int j = t * kSampleStride;
+        const bool ok = t < s_end && t < Ns;
+        const bool ok0 = ok && (!causal || j <= qa);
+        const bool ok1 = ok && (!causal || j <= qb);
+        m0 = fmaxf(m0, ok0 ? a0[r] : -INFINITY);
+        m1 = fmaxf(m1, ok1 ? a1[r] : -INFINITY);
+      }
+      const int tile = tbase / 32;
+      bmh[static_cast<size_t>(2 * tile + half) * Npad + qa] = m0;
+      bmh[static_cast<size_t>(2 * tile + half) * Npad + qb] = m1;
+    }
+  }
+}
+
+// -------------------------------------------------------------- threshold ---
+// One thread per query: a 4-bit-digit radix select over the top 16 bits of
+// the block maxima's order keys gives a value <= the r-th largest block
+// maximum (rounding down only adds candidates).
+__global__ __launch_bounds__(kThreads) void threshold_kernel(
+    const float* __restrict__ bm, int N, int Npad, int Ns, int NB, int k, int causal, int capH,
+    float beta, float scale, float* __restrict__ tau) {
+  __shared__ int hist[16 * kThreads];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int q = blockIdx.x * kThreads + tid;
+  const float* bmh = bm + static_cast<size_t>(h) * NB * Npad;
+  if (q >= Npad) return;  // whole-block uniform: Npad is a multiple of 256
+  float result = -INFINITY;
+  const int n_valid = causal ? q + 1 : N;
+  const bool active = q < N && n_valid > 2 * capH - 64;
+  const int ns_valid = causal ? min(Ns, q / kSampleStride + 1) : Ns;
+  const int nb = 2 * ((ns_valid + 31) / 32);
+  const int k_i = min(k, n_valid);
+  int r = static_cast<int>(ceilf(beta * static_cast<float>(k_i) * static_cast<float>(ns_valid) /
+                                  static_cast<float>(n_valid)));
+  r = max(1, min(r, nb));
+  uint32_t prefix = 0;
+  int K = r;
+  for (int pass = 0; pass < 4; ++pass) {
+    const int shift = 28 - 4 * pass;
+    const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 4));
+#pragma unroll
+    for (int d = 0; d < 16; ++d) hist[d * kThreads + tid] = 0;
+    if (active) {
+      for (int e = 0; e < nb; ++e) {
+        const uint32_t key = order_key(bmh[static_cast<size_t>(e) * Npad + q]);
+        if ((key & pmask) == prefix) hist[((key >> shift) & 15u) * kThreads + tid] += 1;
+      }
+      int cum = 0, digit = 0;
+      for (int d = 15; d >= 0; --d) {
+        const int c = hist[d * kThreads + tid];
+        if (cum + c >= K) { digit = d; break; }
+        cum += c;
+      }
+      K -= cum;
+      prefix |= static_cast<uint32_t>(digit) << shift;
+    }
+  }
+  if (active) {
+    if (prefix > order_key(-INFINITY)) result = key_to_float(prefix) * scale;
+  }
+  tau[static_cast<size_t>(h) * Npad + q] = active ? result : -INFINITY;
+}
+
+// ------------------------------------------------------------ filter pass ---
+template <int DP>
+__global__ __launch_bounds__(kThreads) void filter_kernel(
+    const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
+    const float2* __restrict__ qstat, const uint32_t* __restrict__ kstat,
+    const float* __restrict__ tau, int N, int Npad, int causal, int capH, float scale,
+    uint2* __restrict__ cand, int* __restrict__ cnt, WsHeader* __restrict__ hdr) {
+  __shared__ uint4 lds[Tile<DP>::kChunkUnits];
+  const int h = blockIdx.y;
+  const int nqb = Npad / kQueriesPerBlock;
+  // causal rows near the end see the most keys: start with them
+  const int qblk = causal ? (nqb - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
+  const int q0 = qblk * kQueriesPerBlock;
+  const int w = threadIdx.x >> 6;
+  const int l = lane_id();
+  const int half = l >> 5;
+  const int qw = q0 + w * kWaveQueries;
+  const size_t hq = static_cast<size_t>(h) * Npad;
+  const bf16_t* qh = q16 + hq * DP;
+  const bf16_t* kh = k16 + hq * DP;
+  const float kn = __uint_as_float(kstat[2 * h]);
+  const float kr = __uint_as_float(kstat[2 * h + 1]);
+
+  const int qa = qw + (l & 31), qb = qw + 32 + (l & 31);
+  bf16x8 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
+  load_query_frags<DP>(b0, qh, qa);
+  load_query_frags<DP>(b1, qh, qb);
+
+  // Per-lane threshold on the raw MFMA sum: pairs with s~ >= tau - m pass.
+  // The bound is moved down by a few ulps so that rounding of the scaled
+  // score can never drop such a pair.
+  float thr[2];
+  const int qq[2] = {qa, qb};
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int q = qq[bb];
+    float t = INFINITY;
+    if (q < N) {
+      const float tq = tau[hq + q];
+      if (tq == -INFINITY) {
+        t = -FLT_MAX;
+      } else {
+        const float2 st = qstat[hq + q];
+        const float m = score_margin(st.x, st.y, kn, kr, scale);
+        float lim = tq - m;
+        lim -= fabsf(lim) * (1.0f / 1048576.0f) + 1e-30f;
+        t = lim / scale;
+        t -= fabsf(t) * (1.0f / 1048576.0f) + 1e-30f;
+      }
+    }
+    thr[bb] = t;
+  }
+  uint2* list[2];
+  list[0] = cand + ((hq + qa) * 2 + half) * static_cast<size_t>(capH);
+  list[1] = cand + ((hq + qb) * 2 + half) * static_cast<size_t>(capH);
+  int count[2] = {0, 0};
+
+  const int kend = causal ? min(N, q0 + kQueriesPerBlock) : N;
+  const int nchunks = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
+  for (int ch = 0; ch < nchunks; ++ch) {
+    __syncthreads();
+    stage_chunk<DP>(lds, kh, ch * kKeysPerChunk);
+    __syncthreads();
+#pragma unroll 1
+    for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
+      const int tbase = ch * kKeysPerChunk + tt * 32;
+      if (tbase >= kend) break;
+      f32x16 acc[2];
+      acc[0] = tile_scores<DP>(lds, tt, b0);
+      acc[1] = tile_scores<DP>(lds, tt, b1);
+      const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = tbase + acc_row(r, half);
+            if (j >= N || (causal && j > qq[bb])) acc[bb][r] = -INFINITY;
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const bool hit = acc[bb][r] >= thr[bb];
+          if (__ballot(hit)) {
+            if (hit) {
+              const int pos = count[bb];
+              if (pos < capH)
+                list[bb][pos] = make_uint2(static_cast<uint32_t>(tbase + acc_row(r, half)),
+                                           __float_as_uint(acc[bb][r]));
+              count[bb] = pos + 1;
+            }
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    if (qq[bb] < N) cnt[(hq + qq[bb]) * 2 + half] = count[bb];
+  }
+  int mine = 0;
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) mine += (qq[bb] < N) ? min(count[bb], capH) : 0;
+  const int tot = wave_sum_i(mine);
+  if (l == 0 && tot) atomicAdd(&hdr->candidates, static_cast<unsigned long long>(tot));
+}
+
+template <int DP>
+hipError_t sample_t(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
+  const dim3 grid(p.Npad / kQueriesPerBlock, nh);
+  hipLaunchKernelGGL((sample_maxima_kernel<DP>), grid, dim3(kThreads), 0, s, b.qlo16, b.ksamp,
+                     p.N, p.Npad, p.Ns, p.NB, p.causal, b.bm);
+  return hipGetLastError();
+}
+
+template <int DP>
+hipError_t filter_t(const Plan& p, const Bufs& b, int nh, float scale, hipStream_t s) {
+  const dim3 grid(p.Npad / kQueriesPerBlock, nh);
+  hipLaunchKernelGGL((filter_kernel<DP>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16, b.qstat,
+                     b.kstat, b.tau, p.N, p.Npad, p.causal, p.capH, scale, b.cand, b.cnt,
+                     b.hdr);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
+  switch (p.dp) {
+    case 16: return sample_t<16>(p, b, nh, s);
+    case 32: return sample_t<32>(p, b, nh, s);
+    case 64: return sample_t<64>(p, b, nh, s);
+    case 128: return sample_t<128>(p, b, nh, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_scale,
+                            hipStream_t s) {
+  const dim3 grid(p.Npad / kThreads, nh);
+  hipLaunchKernelGGL(threshold_kernel, grid, dim3(kThreads), 0, s, b.bm, p.N, p.Npad, p.Ns,
+                     p.NB, p.k, p.causal, p.capH, kTauBeta, score_scale, b.tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale,
+                         hipStream_t s) {
+  switch (p.dp) {
+    case 16: return filter_t<16>(p, b, nh, score_scale, s);
+    case 32: return filter_t<32>(p, b, nh, score_scale, s);
+    case 64: return filter_t<64>(p, b, nh, score_scale, s);
+    case 128: return filter_t<128>(p, b, nh, score_scale, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace sa
