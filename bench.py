@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the dynamic top-k sparse attention forward on one MI355X.
+
+One step = one call of sparse_attn_fwd (projection -> bf16-MFMA scorer and
+filter -> exact re-rank -> gather attention) over the whole 128K headline
+workload: B=1, H=32, N=131072, D=128, d_proj=64, k=512, bf16, non-causal,
+seeded synthetic inputs resident in HBM before timing starts.
+
+Prints one JSON line.  value = queries/s (a query is one (b, h, i) row);
+eff_tflops counts algorithmic flops only:
+  F_proj = 4·B·H·N·D·d_proj, F_score = 2·d_proj·(pairs), F_gather = 4·D·Σk_i.
+Per-kernel times come from HIP events the library records around each of its
+launches on the launch stream (sparse_attn_profile_enable).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "queries/s + eff. TFLOP/s, top-k sparse attn fwd, N=128K H=32 D=128 k=512"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def algorithmic(w) -> dict:
+    """Algorithmic work of one forward over workload w."""
+    B, H, N, D, dp, k = w.B, w.H, w.N, w.D, w.d_proj, w.k
+    BH = B * H
+    pairs = N * (N + 1) // 2 if w.causal else N * N
+    if w.causal:
+        sum_k = sum(min(k, i + 1) for i in range(N))
+    else:
+        sum_k = N * min(k, N)
+    e = 2 if w.dtype == "bf16" else 4
+    return {
+        "F_proj": 4.0 * BH * N * D * dp,
+        "F_score": 2.0 * dp * pairs * BH,
+        "F_gather": 4.0 * D * sum_k * BH,
+        # per head: K and V rows of every kept key, the idx row, q in, O out
+        "gather_bytes_per_head": float(sum_k * 2 * D * e + N * k * 4 + N * 2 * D * e),
+        "pairs_per_head": float(pairs),
+    }
+
+
+def cpu_baseline(x, w, target_s: float = 15.0) -> dict:
+    """The fp64 oracle, as it stands, on a bounded sample of the same
+    workload: query rows of head (0, 0), including that head's projections."""
+    import numpy as np
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    Q1, K1, V1 = (x[n][:1, :1] for n in ("Q", "K", "V"))
+    sscale, ascale = w.d_proj ** -0.5, w.D ** -0.5
+    rng = np.random.default_rng(0)
+
+    def run(rows):
+        t = time.perf_counter()
+        O.sparse_attn_fwd(Q1, K1, V1, x["Pq"], x["Pk"], w.k, w.causal, sscale, ascale, rows)
+        return time.perf_counter() - t
+
+    pilot = sorted(rng.choice(w.N, 16, replace=False).tolist())
+    tp = run(pilot)
+    n_rows = int(min(4096, max(32, 16 * target_s / max(tp, 1e-3))))
+    rows = sorted(rng.choice(w.N, n_rows, replace=False).tolist())
+    t = run(rows)
+    return {"value": n_rows / t, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n_rows} random query rows of head (0,0) of the {w.name} workload "
+                      f"through the fp64 oracle forward (scores, top-k, softmax gather), "
+                      f"including that head's key projection; {t:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="headline_128k")
+    ap.add_argument("--heads-per-chunk", type=int, default=0,
+                    help="workspace sized for this many heads per chunk (0 = library default)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import torch
+    import dynamic_top_sparse_amd as sa
+    from dynamic_top_sparse_amd import workloads as W
+
+    w = W.get(args.workload)
+    if w.mode != "topk":
+        print("bench.py times the top-k forward; choose a top-k workload", file=sys.stderr)
+        return 2
+    x = W.make_inputs(w, W.default_seed())
+    g = {k: v.cuda() for k, v in x.items()}
+    hc = args.heads_per_chunk or None
+    ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
+                               heads_per_chunk=hc)
+    out = torch.empty_like(g["Q"])
+    torch.cuda.synchronize()
+
+    def step():
+        sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
+                           O=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    sa.sparse_attn_profile_enable(True)
+    sa.sparse_attn_profile_read()          # drop anything recorded before
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    recs = sa.sparse_attn_profile_read()
+    sa.sparse_attn_profile_enable(False)
+    stats = sa.sparse_attn_workspace_stats(ws)
+
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    a = algorithmic(w)
+    queries = w.queries
+    flops = a["F_proj"] + a["F_score"] + a["F_gather"]
+    # per-kernel totals per step and per-launch averages
+    kern = {}
+    for name, ms in recs:
+        d = kern.setdefault(name, {"launches": 0, "ms_total": 0.0})
+        d["launches"] += 1
+        d["ms_total"] += ms
+    per_step = {n: d["ms_total"] / args.steps for n, d in kern.items()}
+    scorer_names = ("init", "project", "sample", "threshold", "filter", "rerank", "fallback")
+    t_scorer = sum(per_step.get(n, 0.0) for n in scorer_names) / 1e3
+    t_gather = per_step.get("gather", 0.0) / 1e3
+
+    heads_per_launch = None
+    n_gather = kern.get("gather", {}).get("launches", 0)
+    if n_gather:
+        heads_per_launch = (w.B * w.H * args.steps) / n_gather
+    # roofline of the kernel with the largest time per step
+    dom = max(per_step, key=per_step.get)
+    avg_launch_s = kern[dom]["ms_total"] / kern[dom]["launches"] / 1e3
+    launches_per_step = kern[dom]["launches"] / args.steps
+    heads = w.B * w.H / launches_per_step
+    if dom == "filter":
+        amount = 2.0 * w.d_proj * a["pairs_per_head"] * heads
+        roof = {"kernel": dom, "bound": "mfma", "achieved": amount / avg_launch_s / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+        roof["algorithmic_per_launch"] = f"{amount:.4g} flop (2*d_proj*pairs, {heads:g} heads)"
+    else:
+        amount = a["gather_bytes_per_head"] * heads
+        roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_launch_s / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof["algorithmic_per_launch"] = (f"{amount:.4g} B (K,V rows of kept keys + idx + q + o, "
+                                          f"{heads:g} heads)")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["avg_launch_ms"] = avg_launch_s * 1e3
+
+    result = {
+        "metric": METRIC,
+        "value": queries / (ms_step / 1e3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
+                   "d_proj": w.d_proj, "k": w.k, "causal": w.causal, "dist": w.dist,
+                   "seed": W.default_seed(), "heads_per_chunk": heads_per_launch},
+        "eff_tflops": flops / (ms_step / 1e3) / 1e12,
+        "scorer_frac_of_bf16_peak": ((a["F_proj"] + a["F_score"]) / t_scorer / 1e12
+                                     / PEAK_BF16_TFLOPS) if t_scorer else None,
+        "gather_frac_of_hbm_peak": ((a["gather_bytes_per_head"] * w.B * w.H) / t_gather / 1e9
+                                    / PEAK_HBM_GBS) if t_gather else None,
+        "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
+                                                                  key=lambda kv: -kv[1])},
+        "selection": {"candidates_per_query": stats["candidates"] / max(stats["queries"], 1),
+                      "rescored_per_query": stats["rescored"] / max(stats["queries"], 1),
+                      "fallback_queries": stats["fallback_queries"],
+                      "overflow_queries": stats["overflow_queries"]},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(x, w)
+    print(json.dumps(result))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -35,13 +35,18 @@ EXPORTS = (
     "sparse_attn_workspace_size", "sparse_attn_workspace_size_for_chunk",
     "sparse_attn_scores_topk", "sparse_attn_gather", "sparse_attn_fwd",
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
-    "sparse_attn_workspace_stats", "sparse_attn_status_string",
+    "sparse_attn_workspace_stats", "sparse_attn_profile_enable", "sparse_attn_profile_read",
+    "sparse_attn_status_string",
 )
 
 
 class sa_dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("D", ctypes.c_int32)]
+
+
+class sa_kernel_time(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 48), ("ms", ctypes.c_float)]
 
 
 class SparseAttnError(RuntimeError):
@@ -77,6 +82,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "sparse_attn_check_status": (ctypes.c_int, [vp]),
         "sparse_attn_workspace_stats": (ctypes.c_int, [vp, sz, ctypes.POINTER(ctypes.c_int64),
                                                        i32, vp]),
+        "sparse_attn_profile_enable": (ctypes.c_int, [i32]),
+        "sparse_attn_profile_read": (ctypes.c_int, [ctypes.POINTER(sa_kernel_time), i32]),
         "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -275,10 +282,25 @@ def sparse_attn_workspace_stats(workspace: torch.Tensor) -> dict:
     return {kk: int(out[i]) for i, kk in enumerate(keys[:n])}
 
 
+def sparse_attn_profile_enable(on: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events (for benchmarks)."""
+    _check(load_library().sparse_attn_profile_enable(int(on)), "sparse_attn_profile_enable")
+
+
+def sparse_attn_profile_read(max_records: int = 65536) -> list:
+    """[(kernel name, ms)] of the launches timed since the last read."""
+    buf = (sa_kernel_time * max_records)()
+    n = load_library().sparse_attn_profile_read(buf, max_records)
+    if n < 0:
+        raise SparseAttnError(n, "sparse_attn_profile_read")
+    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]
+
+
 __all__ = [
     "sa_dims", "SparseAttnError", "load_library", "status_string", "LIB_PATH", "EXPORTS",
     "sparse_attn_workspace_size", "allocate_workspace", "sparse_attn_scores_topk",
     "sparse_attn_gather", "sparse_attn_fwd", "sparse_attn_band_indices",
     "sparse_attn_scores_dump", "sparse_attn_check_status", "sparse_attn_workspace_stats",
-    "default_score_scale", "default_softmax_scale",
+    "default_score_scale", "default_softmax_scale", "sparse_attn_profile_enable",
+    "sparse_attn_profile_read",
 ]

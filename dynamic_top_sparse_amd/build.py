@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libsparse_attn.so")
-SOURCES = ["api.cpp", "proj.hip", "scorer.hip", "finalize.hip", "gather.hip", "dump.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "proj.hip", "scorer.hip", "finalize.hip", "gather.hip", "dump.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -47,20 +47,51 @@ int check_scorer_args(const void* Q, const void* K, const void* Pq, const void* 
   return SA_OK;
 }
 
+// Runs `call` between the optional timing events of `name`.
+#define SA_TIMED(name, call)          \
+  do {                                \
+    prof_begin(name, s);              \
+    hipError_t e_ = (call);           \
+    prof_end(s);                      \
+    if (e_ != hipSuccess) return e_;  \
+  } while (0)
+
 hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, float scale,
                           int32_t* idx_chunk, int first, hipStream_t s) {
-  hipError_t e;
-  if ((e = launch_init_chunk(p, b, first, s)) != hipSuccess) return e;
-  if ((e = launch_project(p, b, Q, K, Pq, Pk, h0, nh, s)) != hipSuccess) return e;
+  SA_TIMED("init", launch_init_chunk(p, b, first, s));
+  SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
   // the sample pass only matters when some query has more valid keys than
   // its candidate lists can hold outright
   const bool need_sample = p.N > 2 * p.capH - 64;
-  if (need_sample && (e = launch_sample_maxima(p, b, nh, s)) != hipSuccess) return e;
-  if ((e = launch_threshold(p, b, nh, scale, s)) != hipSuccess) return e;
-  if ((e = launch_filter(p, b, nh, scale, s)) != hipSuccess) return e;
-  if ((e = launch_finalize(p, b, nh, scale, idx_chunk, s)) != hipSuccess) return e;
-  return launch_fallback(p, b, nh, scale, idx_chunk, s);
+  if (need_sample) SA_TIMED("sample", launch_sample_maxima(p, b, nh, s));
+  SA_TIMED("threshold", launch_threshold(p, b, nh, scale, s));
+  SA_TIMED("filter", launch_filter(p, b, nh, scale, s));
+  SA_TIMED("rerank", launch_finalize(p, b, nh, scale, idx_chunk, s));
+  SA_TIMED("fallback", launch_fallback(p, b, nh, scale, idx_chunk, s));
+  return hipSuccess;
+}
+
+hipError_t timed_gather(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
+                        int nheads, int N, int D, float scale, int dtype, void* O,
+                        hipStream_t s) {
+  SA_TIMED("gather", launch_gather(Q, K, V, idx, k, nheads, N, D, scale, dtype, O, s));
+  return hipSuccess;
+}
+
+hipError_t timed_dump(const Plan& p, const Bufs& b, const void* Q, const void* K, const void* Pq,
+                      const void* Pk, int h0, int nh, float scale, int row_begin, int row_count,
+                      float* Sc, int first, hipStream_t s) {
+  SA_TIMED("init", launch_init_chunk(p, b, first, s));
+  SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
+  SA_TIMED("dump", launch_dump(p, b, nh, scale, row_begin, row_count, Sc, s));
+  return hipSuccess;
+}
+
+hipError_t timed_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
+                      hipStream_t s) {
+  SA_TIMED("band", launch_band(nheads, N, w_left, w_right, idx, k, s));
+  return hipSuccess;
 }
 
 // Largest chunk (in heads) whose workspace fits ws_bytes; 0 if none.
@@ -211,8 +242,8 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
   if (!std::isfinite(softmax_scale)) return SA_ERR_SHAPE;
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O))
     return SA_ERR_ALIGN;
-  return launch_gather(Q, K, V, idx, k, d.B * d.H, d.N, d.D, softmax_scale, dtype, O,
-                       static_cast<hipStream_t>(stream)) == hipSuccess
+  return timed_gather(Q, K, V, idx, k, d.B * d.H, d.N, d.D, softmax_scale, dtype, O,
+                      static_cast<hipStream_t>(stream)) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
 }
@@ -248,7 +279,7 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
     const unsigned char* Kc = static_cast<const unsigned char*>(K) + off;
     const unsigned char* Vc = static_cast<const unsigned char*>(V) + off;
     unsigned char* Oc = static_cast<unsigned char*>(O) + off;
-    if (launch_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc, s) !=
+    if (timed_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc, s) !=
         hipSuccess)
       return SA_ERR_HIP;
   }
@@ -262,8 +293,8 @@ int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t
   if (st != SA_OK) return st;
   if (w_left < 0 || w_right < 0) return SA_ERR_SHAPE;
   if (!aligned16(idx)) return SA_ERR_ALIGN;
-  return launch_band(d.B * d.H, d.N, w_left, w_right, idx, k,
-                     static_cast<hipStream_t>(stream)) == hipSuccess
+  return timed_band(d.B * d.H, d.N, w_left, w_right, idx, k,
+                    static_cast<hipStream_t>(stream)) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
 }
@@ -286,10 +317,9 @@ int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const 
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int h0 = 0; h0 < p.BH; h0 += p.hc) {
     const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
-    if (launch_init_chunk(p, b, h0 == 0, s) != hipSuccess) return SA_ERR_HIP;
-    if (launch_project(p, b, Q, K, Pq, Pk, h0, nh, s) != hipSuccess) return SA_ERR_HIP;
     float* Sc = S + static_cast<size_t>(h0) * row_count * d.N;
-    if (launch_dump(p, b, nh, score_scale, row_begin, row_count, Sc, s) != hipSuccess)
+    if (timed_dump(p, b, Q, K, Pq, Pk, h0, nh, score_scale, row_begin, row_count, Sc, h0 == 0,
+                   s) != hipSuccess)
       return SA_ERR_HIP;
   }
   return SA_OK;

@@ -82,6 +82,11 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
 hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
                        hipStream_t s);
 
+// Optional per-launch timing (see sparse_attn_profile_enable).  Launch
+// wrappers call prof_begin before and prof_end after a launch.
+void prof_begin(const char* name, hipStream_t s);
+void prof_end(hipStream_t s);
+
 // Sticky device flag set by the gather when an index is >= N.
 hipError_t read_and_clear_device_flag(int* value, hipStream_t s);
 

@@ -164,6 +164,17 @@ int sparse_attn_check_status(void* stream);
 int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, int32_t n,
                                 void* stream);
 
+/*
+ * Per-kernel timing for benchmarks.  While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the launch
+ * stream; sparse_attn_profile_read synchronizes those events and returns
+ * (kernel name, milliseconds) records in launch order, then forgets them.
+ * Disabled by default; enabling it costs two event records per launch.
+ */
+typedef struct { char name[48]; float ms; } sa_kernel_time;
+int sparse_attn_profile_enable(int32_t on);
+int sparse_attn_profile_read(sa_kernel_time* out, int32_t n);
+
 /* Static description of a status code. */
 const char* sparse_attn_status_string(int status);
 
