@@ -27,6 +27,8 @@ FLAGS = [
     # packed fp32 vector ops stay off: only scalar fp32 arithmetic is emitted
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-result",
+    # MFMA results in VGPRs: the filter reads every accumulator with VALU ops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 

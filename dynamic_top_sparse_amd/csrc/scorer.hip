@@ -50,16 +50,27 @@ __device__ __forceinline__ int lds_unit(int key, int u) {
   return key * U + (u ^ (key & (U - 1)));
 }
 
+// One thread's share of a staged key chunk, held in registers between the
+// global loads (issued a chunk ahead) and the LDS writes.
 template <int DP>
-__device__ __forceinline__ void stage_chunk(uint4* __restrict__ lds, const bf16_t* __restrict__ rows,
-                                            int key0) {
-  constexpr int U = Tile<DP>::kUnits;
-  const uint4* src = reinterpret_cast<const uint4*>(rows + static_cast<size_t>(key0) * DP);
-  for (int e = threadIdx.x; e < Tile<DP>::kChunkUnits; e += kThreads) {
-    const int key = e / U, u = e % U;
-    lds[lds_unit<DP>(key, u)] = src[e];
+struct ChunkRegs {
+  static constexpr int kPerThread = Tile<DP>::kChunkUnits / kThreads;
+  uint4 r[kPerThread];
+
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ rows, int key0) {
+    const uint4* src = reinterpret_cast<const uint4*>(rows + static_cast<size_t>(key0) * DP);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) r[i] = src[threadIdx.x + i * kThreads];
   }
-}
+  __device__ __forceinline__ void store(uint4* __restrict__ lds) const {
+    constexpr int U = Tile<DP>::kUnits;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = threadIdx.x + i * kThreads;
+      lds[lds_unit<DP>(e / U, e % U)] = r[i];
+    }
+  }
+};
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
   bf16x8 r;
@@ -102,7 +113,7 @@ template <int DP>
 __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp, int N, int Npad, int Ns,
     int NB, int causal, float* __restrict__ bm) {
-  __shared__ uint4 lds[Tile<DP>::kChunkUnits];
+  __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kQueriesPerBlock;
   const int w = threadIdx.x >> 6;
@@ -122,22 +133,26 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
   int s_end = Ns;
   if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / kSampleStride + 1);
   const int nchunks = (s_end + kKeysPerChunk - 1) / kKeysPerChunk;
+  ChunkRegs<DP> regs;
+  regs.load(sh, 0);
+  regs.store(lds);
+  __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
-    __syncthreads();
-    stage_chunk<DP>(lds, sh, ch * kKeysPerChunk);
-    __syncthreads();
+    const bool more = ch + 1 < nchunks;
+    if (more) regs.load(sh, (ch + 1) * kKeysPerChunk);
+    const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
 #pragma unroll 1
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       const int tbase = ch * kKeysPerChunk + tt * 32;
       if (tbase >= s_end) break;
-      f32x16 a0 = tile_scores<DP>(lds, tt, b0);
-      f32x16 a1 = tile_scores<DP>(lds, tt, b1);
+      f32x16 a0 = tile_scores<DP>(buf, tt, b0);
+      f32x16 a1 = tile_scores<DP>(buf, tt, b1);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int t = tbase + acc_row(r, half);
         const int j = t * kSampleStride;
-        const bool ok = t < s_end && t < Ns;
+        const bool ok = t < s_end;
         const bool ok0 = ok && (!causal || j <= qa);
         const bool ok1 = ok && (!causal || j <= qb);
         m0 = fmaxf(m0, ok0 ? a0[r] : -INFINITY);
@@ -147,6 +162,8 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
       bmh[static_cast<size_t>(2 * tile + half) * Npad + qa] = m0;
       bmh[static_cast<size_t>(2 * tile + half) * Npad + qb] = m1;
     }
+    if (more) regs.store(lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
+    __syncthreads();
   }
 }
 
@@ -201,13 +218,38 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
 }
 
 // ------------------------------------------------------------ filter pass ---
+// Bit r of the result is set when accumulator r misses the threshold: the
+// sign bit of v - thr is shifted in with one v_alignbit per accumulator
+// (v >= thr exactly when v - thr >= +0; masked -inf scores always miss).
+__device__ __forceinline__ unsigned miss_bits(const f32x16& a, float thr) {
+  unsigned nb = 0;
+#pragma unroll
+  for (int r = 15; r >= 0; --r) nb = __builtin_amdgcn_alignbit(nb, __float_as_uint(a[r] - thr), 31);
+  return nb;
+}
+
+// Rows of a lane's accumulators are key offsets r + (r & 12) (+4 for the
+// upper half-wave), increasing in r, so the keys beyond `lim` (relative to
+// the lane's first key) form a suffix of r.  Returns the mask of the valid
+// accumulators.
+__device__ __forceinline__ unsigned valid_rows(int lim) {
+  if (lim < 0) return 0u;
+  int r0 = min(4, lim + 1) + min(4, max(0, lim - 7)) + min(4, max(0, lim - 15)) +
+           min(4, max(0, lim - 23));
+  return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
+}
+
+
 template <int DP>
 __global__ __launch_bounds__(kThreads) void filter_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
     const float2* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ tau, int N, int Npad, int causal, int capH, float scale,
     uint2* __restrict__ cand, int* __restrict__ cnt, WsHeader* __restrict__ hdr) {
-  __shared__ uint4 lds[Tile<DP>::kChunkUnits];
+  __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
+  __shared__ float4 stash_all[8 * kThreads];   // 32 scores per lane, [8][threads]
+  float4* stash4 = stash_all + threadIdx.x;
+  const float* stash = reinterpret_cast<const float*>(stash4);
   const int h = blockIdx.y;
   const int nqb = Npad / kQueriesPerBlock;
   // causal rows near the end see the most keys: start with them
@@ -255,54 +297,81 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   uint2* list[2];
   list[0] = cand + ((hq + qa) * 2 + half) * static_cast<size_t>(capH);
   list[1] = cand + ((hq + qb) * 2 + half) * static_cast<size_t>(capH);
-  int count[2] = {0, 0};
+  unsigned count[2] = {0u, 0u};
+  const unsigned last = static_cast<unsigned>(capH - 1);
 
   const int kend = causal ? min(N, q0 + kQueriesPerBlock) : N;
   const int nchunks = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
+  ChunkRegs<DP> regs;
+  regs.load(kh, 0);
+  regs.store(lds);
+  __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
-    __syncthreads();
-    stage_chunk<DP>(lds, kh, ch * kKeysPerChunk);
-    __syncthreads();
-#pragma unroll 1
+    const bool more = ch + 1 < nchunks;
+    if (more) regs.load(kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
+    const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
+    const int ntiles = min(kKeysPerChunk / 32, (kend - ch * kKeysPerChunk + 31) / 32);
+    // accumulators of two tiles: the next tile's MFMAs run while this tile's
+    // scores are filtered (past the last tile they read stale LDS, unused)
+    f32x16 acc[2][2];
+    acc[0][0] = tile_scores<DP>(buf, 0, b0);
+    acc[0][1] = tile_scores<DP>(buf, 0, b1);
+#pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
+      if (tt >= ntiles) break;
+      if (tt + 1 < kKeysPerChunk / 32) {
+        acc[(tt + 1) & 1][0] = tile_scores<DP>(buf, tt + 1, b0);
+        acc[(tt + 1) & 1][1] = tile_scores<DP>(buf, tt + 1, b1);
+      }
       const int tbase = ch * kKeysPerChunk + tt * 32;
-      if (tbase >= kend) break;
-      f32x16 acc[2];
-      acc[0] = tile_scores<DP>(lds, tt, b0);
-      acc[1] = tile_scores<DP>(lds, tt, b1);
+      const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
+      // bits 0-15: hits of query block 0, bits 16-31: query block 1
+      unsigned bits = (~miss_bits(acc[tt & 1][0], thr[0]) & 0xFFFFu) |
+                      (~miss_bits(acc[tt & 1][1], thr[1]) << 16);
+      if (edge) {
+        const int lim0 = (causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase);
+        const int lim1 = (causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase);
+        bits &= valid_rows(lim0) | (valid_rows(lim1) << 16);
+      }
+      if (bits) {
+        // park this lane's 32 tile scores (lane-interleaved: conflict-free)
+        // so that its hits can be read by index
 #pragma unroll
-      for (int bb = 0; bb < 2; ++bb) {
-        if (edge) {
+        for (int bb = 0; bb < 2; ++bb) {
+          const f32x16& a = acc[tt & 1][bb];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = tbase + acc_row(r, half);
-            if (j >= N || (causal && j > qq[bb])) acc[bb][r] = -INFINITY;
-          }
+          for (int v4 = 0; v4 < 4; ++v4)
+            stash4[(4 * bb + v4) * kThreads] =
+                make_float4(a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]);
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const bool hit = acc[bb][r] >= thr[bb];
-          if (__ballot(hit)) {
-            if (hit) {
-              const int pos = count[bb];
-              if (pos < capH)
-                list[bb][pos] = make_uint2(static_cast<uint32_t>(tbase + acc_row(r, half)),
-                                           __float_as_uint(acc[bb][r]));
-              count[bb] = pos + 1;
-            }
+        do {
+          const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
+          bits &= bits - 1;
+          const unsigned r = b & 15u;
+          const float v = stash[(b >> 2) * (4 * kThreads) + (b & 3u)];
+          // accumulator r holds key row r + (r & 12) + 4*half of the tile
+          const uint2 e = make_uint2(jbase + r + (r & 12u), __float_as_uint(v));
+          if (b < 16) {
+            list[0][min(count[0], last)] = e;
+            ++count[0];
+          } else {
+            list[1][min(count[1], last)] = e;
+            ++count[1];
           }
-        }
+        } while (bits);
       }
     }
+    if (more) regs.store(lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
+    __syncthreads();
   }
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    if (qq[bb] < N) cnt[(hq + qq[bb]) * 2 + half] = count[bb];
+    if (qq[bb] < N) cnt[(hq + qq[bb]) * 2 + half] = static_cast<int>(count[bb]);
   }
   int mine = 0;
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) mine += (qq[bb] < N) ? min(count[bb], capH) : 0;
+  for (int bb = 0; bb < 2; ++bb) mine += (qq[bb] < N) ? static_cast<int>(min(count[bb], last + 1)) : 0;
   const int tot = wave_sum_i(mine);
   if (l == 0 && tot) atomicAdd(&hdr->candidates, static_cast<unsigned long long>(tot));
 }
