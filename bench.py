@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of the dynamic top-k sparse attention forward on one MI355X.
 
-One step = one call of sparse_attn_fwd (projection -> bf16-MFMA scorer and
+One step = one call of sparse_attn_fwd (projection -> 16-bit MFMA scorer and
 filter -> exact re-rank -> gather attention) over the whole 128K headline
 workload: B=1, H=32, N=131072, D=128, d_proj=64, k=512, bf16, non-causal,
 seeded synthetic inputs resident in HBM before timing starts.
@@ -86,6 +86,8 @@ def main() -> int:
     ap.add_argument("--workload", default="headline_128k")
     ap.add_argument("--heads-per-chunk", type=int, default=0,
                     help="workspace sized for this many heads per chunk (0 = library default)")
+    ap.add_argument("--filter-dtype", choices=("f16", "bf16"), default="f16",
+                    help="16-bit operand type of the MFMA filter (indices do not depend on it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -97,6 +99,7 @@ def main() -> int:
     import dynamic_top_sparse_amd as sa
     from dynamic_top_sparse_amd import workloads as W
 
+    sa.sparse_attn_set_filter_dtype(torch.float16 if args.filter_dtype == "f16" else torch.bfloat16)
     w = W.get(args.workload)
     if w.mode != "topk":
         print("bench.py times the top-k forward; choose a top-k workload", file=sys.stderr)
@@ -139,7 +142,8 @@ def main() -> int:
         d["launches"] += 1
         d["ms_total"] += ms
     per_step = {n: d["ms_total"] / args.steps for n, d in kern.items()}
-    scorer_names = ("init", "project", "sample", "threshold", "filter", "rerank", "fallback")
+    scorer_names = ("init", "project", "pack", "sample", "threshold", "filter", "rerank",
+                    "filter_retry", "rerank_retry", "fallback")
     t_scorer = sum(per_step.get(n, 0.0) for n in scorer_names) / 1e3
     t_gather = per_step.get("gather", 0.0) / 1e3
 
@@ -193,7 +197,9 @@ def main() -> int:
         "selection": {"candidates_per_query": stats["candidates"] / max(stats["queries"], 1),
                       "rescored_per_query": stats["rescored"] / max(stats["queries"], 1),
                       "fallback_queries": stats["fallback_queries"],
-                      "overflow_queries": stats["overflow_queries"]},
+                      "overflow_queries": stats["overflow_queries"],
+                      "retried_queries": stats["retried"],
+                      "filter_dtype": str(sa.sparse_attn_get_filter_dtype()).replace("torch.", "")},
         "roofline": roof,
     }
     if not args.no_cpu_baseline:

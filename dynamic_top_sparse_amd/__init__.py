@@ -22,7 +22,7 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "lib", "libsparse_attn.so")
 
-SA_F32, SA_BF16 = 0, 1
+SA_F32, SA_BF16, SA_F16 = 0, 1, 2
 SA_OK = 0
 SA_K_MAX = 2048
 STATUS_NAMES = {
@@ -36,7 +36,7 @@ EXPORTS = (
     "sparse_attn_scores_topk", "sparse_attn_gather", "sparse_attn_fwd",
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
     "sparse_attn_workspace_stats", "sparse_attn_profile_enable", "sparse_attn_profile_read",
-    "sparse_attn_status_string",
+    "sparse_attn_set_filter_dtype", "sparse_attn_get_filter_dtype", "sparse_attn_status_string",
 )
 
 
@@ -84,6 +84,8 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                        i32, vp]),
         "sparse_attn_profile_enable": (ctypes.c_int, [i32]),
         "sparse_attn_profile_read": (ctypes.c_int, [ctypes.POINTER(sa_kernel_time), i32]),
+        "sparse_attn_set_filter_dtype": (ctypes.c_int, [i32]),
+        "sparse_attn_get_filter_dtype": (ctypes.c_int, []),
         "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -273,13 +275,25 @@ def sparse_attn_check_status(stream: Optional[int] = None) -> int:
 
 
 def sparse_attn_workspace_stats(workspace: torch.Tensor) -> dict:
-    out = (ctypes.c_int64 * 5)()
+    out = (ctypes.c_int64 * 6)()
     n = load_library().sparse_attn_workspace_stats(
-        _dev(workspace, "workspace"), workspace.numel(), out, 5, _stream(workspace))
+        _dev(workspace, "workspace"), workspace.numel(), out, 6, _stream(workspace))
     if n < 0:
         raise SparseAttnError(n, "sparse_attn_workspace_stats")
-    keys = ("fallback_queries", "overflow_queries", "candidates", "rescored", "queries")
+    keys = ("fallback_queries", "overflow_queries", "candidates", "rescored", "queries",
+            "retried")
     return {kk: int(out[i]) for i, kk in enumerate(keys[:n])}
+
+
+def sparse_attn_set_filter_dtype(dtype: torch.dtype) -> None:
+    """16-bit operand type of the MFMA filter: torch.float16 (default) or
+    torch.bfloat16.  Indices do not depend on it (see include/sparse_attn.h)."""
+    code = {torch.float16: SA_F16, torch.bfloat16: SA_BF16}[dtype]
+    _check(load_library().sparse_attn_set_filter_dtype(code), "sparse_attn_set_filter_dtype")
+
+
+def sparse_attn_get_filter_dtype() -> torch.dtype:
+    return torch.float16 if load_library().sparse_attn_get_filter_dtype() == SA_F16 else torch.bfloat16
 
 
 def sparse_attn_profile_enable(on: bool = True) -> None:
@@ -302,5 +316,5 @@ __all__ = [
     "sparse_attn_gather", "sparse_attn_fwd", "sparse_attn_band_indices",
     "sparse_attn_scores_dump", "sparse_attn_check_status", "sparse_attn_workspace_stats",
     "default_score_scale", "default_softmax_scale", "sparse_attn_profile_enable",
-    "sparse_attn_profile_read",
+    "sparse_attn_profile_read", "sparse_attn_set_filter_dtype", "sparse_attn_get_filter_dtype",
 ]

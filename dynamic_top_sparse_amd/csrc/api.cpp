@@ -5,6 +5,8 @@
 
 #include <cmath>
 #include <cstdint>
+#include <algorithm>
+#include <atomic>
 #include <cstring>
 
 #include "sa_internal.h"
@@ -15,6 +17,9 @@ namespace sa {
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// 16-bit operand type of the MFMA filter (sparse_attn_set_filter_dtype).
+std::atomic<int> g_filter_dtype{SA_F16};
 constexpr int kDefaultChunkHeads = 8;
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -61,13 +66,17 @@ hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const voi
                           int32_t* idx_chunk, int first, hipStream_t s) {
   SA_TIMED("init", launch_init_chunk(p, b, first, s));
   SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
+  SA_TIMED("pack", launch_pack_keys(p, b, nh, s));
   // the sample pass only matters when some query has more valid keys than
   // its candidate lists can hold outright
   const bool need_sample = p.N > 2 * p.capH - 64;
-  if (need_sample) SA_TIMED("sample", launch_sample_maxima(p, b, nh, s));
+  if (need_sample) SA_TIMED("sample", launch_sample_maxima(p, b, nh, scale, s));
   SA_TIMED("threshold", launch_threshold(p, b, nh, scale, s));
-  SA_TIMED("filter", launch_filter(p, b, nh, scale, s));
-  SA_TIMED("rerank", launch_finalize(p, b, nh, scale, idx_chunk, s));
+  SA_TIMED("filter", launch_filter(p, b, nh, scale, false, s));
+  SA_TIMED("rerank", launch_finalize(p, b, nh, scale, idx_chunk, false, s));
+  // queries whose threshold was not good enough, again with a proven one
+  SA_TIMED("filter_retry", launch_filter(p, b, nh, scale, true, s));
+  SA_TIMED("rerank_retry", launch_finalize(p, b, nh, scale, idx_chunk, true, s));
   SA_TIMED("fallback", launch_fallback(p, b, nh, scale, idx_chunk, s));
   return hipSuccess;
 }
@@ -124,13 +133,16 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
                int with_idx, int heads_per_chunk) {
   p.B = B; p.H = H; p.N = N; p.D = D; p.dp = dp; p.k = k; p.causal = causal ? 1 : 0;
   p.dtype = dtype;
+  p.filt = g_filter_dtype.load() == SA_BF16 ? 1 : 0;
   p.BH = B * H;
   p.hc = heads_per_chunk < 1 ? 1 : (heads_per_chunk > p.BH ? p.BH : heads_per_chunk);
   p.Npad = round_up(N, kRowPad);
   p.Ns = (N + kSampleStride - 1) / kSampleStride;
   p.Nspad = p.Npad / kSampleStride;
   p.NB = 2 * ((p.Ns + 31) / 32);
-  p.capH = round_up(2 * k > 256 ? 2 * k : 256, 64);
+  // two query halves of capH candidates each (1.5 k, at least 256, at most
+  // 2048); a list that overflows is filtered again with a proven threshold
+  p.capH = std::min(2048, round_up(std::max(3 * k / 2, 256), 64));
   p.with_idx = with_idx ? 1 : 0;
   const size_t hc = static_cast<size_t>(p.hc);
   const size_t Np = static_cast<size_t>(p.Npad);
@@ -148,12 +160,14 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.off_qlo16 = take(hc * Np * dp * 2);
   p.off_klo16 = take(hc * Np * dp * 2);
   p.off_ksamp = take(hc * static_cast<size_t>(p.Nspad) * dp * 2);
-  p.off_qstat = take(hc * Np * 8);
-  p.off_kstat = take(hc * 2 * 4);
+  p.off_qstat = take(hc * Np * 16);
+  p.off_kstat = take(hc * kKeyStatWords * 4);
   p.off_bm = take(hc * static_cast<size_t>(p.NB) * Np * 4);
   p.off_tau = take(hc * Np * 4);
   p.off_cand = take(hc * Np * 2 * static_cast<size_t>(p.capH) * 8);
   p.off_cnt = take(hc * Np * 2 * 4);
+  p.off_rlist = take(hc * Np * 4);
+  p.off_rcount = take(hc * 4);
   p.off_fblist = take(hc * Np * 4);
   p.off_fbscratch = take(static_cast<size_t>(kFallbackBlocks) * Np * 4);
   p.off_idx = take(p.with_idx ? hc * static_cast<size_t>(N) * k * 4 : 0);
@@ -170,12 +184,14 @@ Bufs bufs_of(const Plan& p, void* ws) {
   b.qlo16 = reinterpret_cast<bf16_t*>(base + p.off_qlo16);
   b.klo16 = reinterpret_cast<bf16_t*>(base + p.off_klo16);
   b.ksamp = reinterpret_cast<bf16_t*>(base + p.off_ksamp);
-  b.qstat = reinterpret_cast<float2*>(base + p.off_qstat);
+  b.qstat = reinterpret_cast<float4*>(base + p.off_qstat);
   b.kstat = reinterpret_cast<uint32_t*>(base + p.off_kstat);
   b.bm = reinterpret_cast<float*>(base + p.off_bm);
   b.tau = reinterpret_cast<float*>(base + p.off_tau);
   b.cand = reinterpret_cast<uint2*>(base + p.off_cand);
   b.cnt = reinterpret_cast<int*>(base + p.off_cnt);
+  b.rlist = reinterpret_cast<int*>(base + p.off_rlist);
+  b.rcount = reinterpret_cast<int*>(base + p.off_rcount);
   b.fblist = reinterpret_cast<int*>(base + p.off_fblist);
   b.fbscratch = reinterpret_cast<float*>(base + p.off_fbscratch);
   b.idx = p.with_idx ? reinterpret_cast<int32_t*>(base + p.off_idx) : nullptr;
@@ -325,6 +341,14 @@ int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const 
   return SA_OK;
 }
 
+int sparse_attn_set_filter_dtype(int32_t dtype) {
+  if (dtype != SA_F16 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  g_filter_dtype.store(dtype);
+  return SA_OK;
+}
+
+int sparse_attn_get_filter_dtype(void) { return g_filter_dtype.load(); }
+
 int sparse_attn_check_status(void* stream) {
   int v = 0;
   if (read_and_clear_device_flag(&v, static_cast<hipStream_t>(stream)) != hipSuccess)
@@ -342,11 +366,11 @@ int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, i
   if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
     return SA_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_HIP;
-  const int64_t vals[5] = {static_cast<int64_t>(h.fallback_queries),
+  const int64_t vals[6] = {static_cast<int64_t>(h.fallback_queries),
                            static_cast<int64_t>(h.overflow_queries),
                            static_cast<int64_t>(h.candidates), static_cast<int64_t>(h.rescored),
-                           static_cast<int64_t>(h.queries)};
-  const int m = n < 5 ? n : 5;
+                           static_cast<int64_t>(h.queries), static_cast<int64_t>(h.retried)};
+  const int m = n < 6 ? n : 6;
   for (int i = 0; i < m; ++i) out[i] = vals[i];
   return m;
 }

@@ -5,7 +5,7 @@
 // valid) is applied to the exact fp32 score s of exact_score().  Ties go to
 // the lower key index; rows are written in ascending key order, then -1.
 //
-// Re-rank, one wavefront per query.  Each candidate carries its bf16 MFMA
+// Re-rank, one wavefront per query.  Each candidate carries its 16-bit MFMA
 // score s~; with the per-query margin m every exact score lies in
 // [l, u] = [s~ - m, s~ + m] (rounded outwards).  Let lo be the k-th largest l
 // and hi the (k+1)-th largest u (or tau if larger).  Then
@@ -15,6 +15,12 @@
 // and ranked by (s descending, key ascending) to fill the rest of the row.
 // The candidate list of each query half is already in ascending key order
 // (the filter streams keys in order), so the output row is a merge.
+//
+// A query whose list overflowed, or whose threshold turned out too high, is
+// not lost: the k-th best lower bound among the candidates it does hold is a
+// proven threshold (k keys reach it), so the query is queued to be filtered
+// again with it.  Only what remains unresolved after that second round goes
+// to the exact fallback.
 #include <float.h>
 
 #include "sa_internal.h"
@@ -31,49 +37,137 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
-// K-th largest (1-based) of the keys key(i), i in [0, n) with ok(i), by an
-// MSB-first radix select with 8-bit digits over a wave-private histogram.
-// Requires 1 <= K <= number of admitted keys.
-template <typename KeyT, typename KeyFn>
-__device__ KeyT wave_kth_largest(int n, int K, int* hist, KeyFn key_of) {
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long t = __shfl_xor(v, o, kWave);
+    v = t < v ? t : v;
+  }
+  return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const unsigned long long t = __shfl_xor(v, o, kWave);
+    v = t > v ? t : v;
+  }
+  return v;
+}
+template <typename KeyT>
+__device__ __forceinline__ KeyT wave_min_k(KeyT v);
+template <> __device__ __forceinline__ uint32_t wave_min_k(uint32_t v) { return wave_min_u32(v); }
+template <> __device__ __forceinline__ unsigned long long wave_min_k(unsigned long long v) { return wave_min_u64(v); }
+template <typename KeyT>
+__device__ __forceinline__ KeyT wave_max_k(KeyT v);
+template <> __device__ __forceinline__ uint32_t wave_max_k(uint32_t v) { return wave_max_u32(v); }
+template <> __device__ __forceinline__ unsigned long long wave_max_k(unsigned long long v) { return wave_max_u64(v); }
+
+template <typename KeyT>
+__device__ __forceinline__ int key_bits(KeyT span) {
+  return sizeof(KeyT) == 8 ? 64 - __builtin_clzll(static_cast<unsigned long long>(span))
+                           : 32 - __builtin_clz(static_cast<uint32_t>(span));
+}
+
+// K-th largest (1-based) key among the elements a wavefront owns, exactly.
+// `each(fn)` calls fn(key, valid) once per element slot with a uniform trip
+// count.  The key range is cut into 256 buckets, the bucket holding the K-th
+// key is kept, and this repeats until at most 64 keys are left; those are
+// ranked directly.  Buckets spread keys that share their leading bits, so the
+// LDS histogram sees few colliding atomics.  Requires 1 <= K <= #valid keys.
+template <typename KeyT, typename Each>
+__device__ KeyT wave_select(int K, int* hist, KeyT* cbuf, Each each) {
   const int l = lane_id();
-  KeyT prefix = 0, pmask = 0;
-  constexpr int kBits = 8 * sizeof(KeyT);
-  for (int shift = kBits - 8; shift >= 0; shift -= 8) {
+  KeyT lo = ~static_cast<KeyT>(0), hi = 0;
+  each([&](KeyT key, bool ok) {
+    if (ok) {
+      lo = key < lo ? key : lo;
+      hi = key > hi ? key : hi;
+    }
+  });
+  lo = wave_min_k(lo);
+  hi = wave_max_k(hi);
+  int in_range = 65;
+  while (lo != hi) {
+    const KeyT span = hi - lo;
+    const int nb = key_bits<KeyT>(span);
+    const int shift = nb > 8 ? nb - 8 : 0;          // (span >> shift) < 256
     for (int b = l; b < 256; b += kWave) hist[b] = 0;
     wave_sync();
-    for (int i = l; i < n; i += kWave) {
-      KeyT key;
-      if (key_of(i, key) && (key & pmask) == prefix)
-        atomicAdd(&hist[static_cast<int>((key >> shift) & 255)], 1);
-    }
+    each([&](KeyT key, bool ok) {
+      if (ok && key >= lo && key <= hi) atomicAdd(&hist[static_cast<int>((key - lo) >> shift)], 1);
+    });
     wave_sync();
-    // lane L owns bins 255-4L .. 252-4L (descending)
     int c[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) c[t] = hist[255 - 4 * l - t];
-    const int s = c[0] + c[1] + c[2] + c[3];
-    const int incl = wave_incl_scan(s);
+    for (int t = 0; t < 4; ++t) c[t] = hist[255 - 4 * l - t];   // lane L: bins 255-4L ..
+    const int sum = c[0] + c[1] + c[2] + c[3];
+    const int incl = wave_incl_scan(sum);
     const unsigned long long crossing = __ballot(incl >= K);
     const int F = crossing ? __builtin_ctzll(crossing) : 0;
-    int digit = 0, above = 0;
+    int digit = 0, above = 0, cnt = 0;
     if (l == F) {
-      int cum = incl - s;
+      int cum = incl - sum;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (cum + c[t] >= K) { digit = 255 - 4 * l - t; break; }
+        if (cum + c[t] >= K) { digit = 255 - 4 * l - t; cnt = c[t]; break; }
         cum += c[t];
       }
       above = cum;
     }
     digit = __shfl(digit, F, kWave);
     above = __shfl(above, F, kWave);
+    cnt = __shfl(cnt, F, kWave);
     K -= above;
-    prefix |= static_cast<KeyT>(digit) << shift;
-    pmask |= static_cast<KeyT>(255) << shift;
+    const KeyT nlo = lo + (static_cast<KeyT>(digit) << shift);
+    const KeyT width = (static_cast<KeyT>(1) << shift) - 1;
+    hi = (hi - nlo) < width ? hi : nlo + width;
+    lo = nlo;
+    in_range = cnt;
     wave_sync();
+    if (cnt <= 64) break;
   }
-  return prefix;
+  if (lo == hi) return lo;          // every remaining key is equal
+  // gather the <= 64 keys of [lo, hi] and rank them
+  int base = 0;
+  each([&](KeyT key, bool ok) {
+    const bool in = ok && key >= lo && key <= hi;
+    const unsigned long long m = __ballot(in);
+    if (in) cbuf[base + __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0))] = key;
+    base += __builtin_popcountll(m);
+  });
+  wave_sync();
+  const int m = base;
+  (void)in_range;
+  const KeyT mine = l < m ? cbuf[l] : static_cast<KeyT>(0);
+  int greater = 0, equal = 0;
+  for (int u = 0; u < m; ++u) {
+    const KeyT o = cbuf[u];
+    greater += o > mine ? 1 : 0;
+    equal += o == mine ? 1 : 0;
+  }
+  const unsigned long long hit = __ballot(l < m && greater < K && greater + equal >= K);
+  const int src = hit ? __builtin_ctzll(hit) : 0;
+  KeyT result;
+  if (sizeof(KeyT) == 8) {
+    const unsigned long long r = __shfl(static_cast<unsigned long long>(mine), src, kWave);
+    result = static_cast<KeyT>(r);
+  } else {
+    result = static_cast<KeyT>(__shfl(static_cast<int>(mine), src, kWave));
+  }
+  wave_sync();
+  return result;
 }
 
 // First position in the ascending list a[0..n) whose value is >= x.
@@ -86,169 +180,244 @@ __device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
   return lo;
 }
 
+__device__ __forceinline__ unsigned long long rank_key(float s, int j) {
+  return (static_cast<unsigned long long>(order_key(s)) << 32) |
+         static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(j));
+}
+
+// Per-wave LDS of the re-rank: histogram (1 KB), rank buffer (512 B), the
+// uncertain keys and their exact scores (ucap x 8 B), and the candidates
+// (cap x 8 B: order key of the filter score, key index), whose key array
+// becomes the output row in place.
+__host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
+  return (1024 + 512 + static_cast<size_t>(ucap) * 8 + static_cast<size_t>(cap) * 8 + 15) /
+         16 * 16;
+}
+
 template <int DP>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
-    const uint2* __restrict__ cand, const int* __restrict__ cnt, const float* __restrict__ tau,
-    const float2* __restrict__ qstat, const uint32_t* __restrict__ kstat,
+    const uint2* __restrict__ cand, const int* __restrict__ cnt, float* __restrict__ tau,
+    const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ q32, const float* __restrict__ k32, int N, int Npad, int k,
-    int causal, int capH, float scale, int32_t* __restrict__ idx, int* __restrict__ fblist,
-    WsHeader* __restrict__ hdr) {
+    int causal, int capH, int ucap, float scale, int32_t* __restrict__ idx,
+    const int* __restrict__ qlist, const int* __restrict__ qlist_count, int* __restrict__ rlist,
+    int* __restrict__ rcount, int* __restrict__ fblist, WsHeader* __restrict__ hdr) {
   extern __shared__ unsigned char smem[];
   const int wpb = blockDim.x / kWave;
   const int w = threadIdx.x / kWave;
   const int l = lane_id();
   const int cap = 2 * capH;
-  // per-wave LDS: keys, scores, class, histogram, q row
-  unsigned char* base = smem + static_cast<size_t>(w) * (cap * 9 + 256 * 4 + DP * 4);
-  int* cj = reinterpret_cast<int*>(base);
-  float* cs = reinterpret_cast<float*>(base + cap * 4);
-  int* hist = reinterpret_cast<int*>(base + cap * 8);
-  float* qrow = reinterpret_cast<float*>(base + cap * 8 + 1024);
-  unsigned char* cls = base + cap * 8 + 1024 + DP * 4;
+  unsigned char* base = smem + static_cast<size_t>(w) * rerank_lds_per_wave(cap, ucap);
+  int* hist = reinterpret_cast<int*>(base);
+  unsigned long long* cbuf = reinterpret_cast<unsigned long long*>(base + 1024);
+  int* uj = reinterpret_cast<int*>(base + 1536);
+  float* us = reinterpret_cast<float*>(base + 1536 + ucap * 4);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(base + 1536 + ucap * 8);
+  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 8 + cap * 4);
 
   const int h = blockIdx.y;
-  const int q = blockIdx.x * wpb + w;
-  if (q >= N) return;
   const size_t hq = static_cast<size_t>(h) * Npad;
+  // first pass: every query; retry pass: the queries listed for this head
+  int q = blockIdx.x * wpb + w;
+  if (qlist != nullptr) {
+    if (q >= qlist_count[h]) return;
+    q = qlist[hq + q];
+  } else if (q >= N) {
+    return;
+  }
   int32_t* out = idx + (static_cast<size_t>(h) * N + q) * k;
   const int n_valid = causal ? q + 1 : N;
   const int k_i = min(k, n_valid);
+  // Unresolved query: on the first pass, if a proven threshold is known
+  // (k keys certainly score at least tau_new), filter it again with that
+  // threshold; otherwise resolve it with the exact fallback.
+  auto unresolved = [&](float tau_new) {
+    if (l == 0) {
+      if (qlist == nullptr && tau_new == tau_new) {
+        tau[hq + q] = tau_new;
+        rlist[hq + atomicAdd(&rcount[h], 1)] = q;
+        atomicAdd(&hdr->retried, 1ull);
+      } else {
+        const unsigned slot = atomicAdd(&hdr->fb_count, 1u);
+        fblist[slot] = static_cast<int>(hq + q);
+        atomicAdd(&hdr->queries, 1ull);
+      }
+    }
+  };
 
   if (n_valid <= k) {  // every valid key is kept
     for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
     if (l == 0) atomicAdd(&hdr->queries, 1ull);
     return;
   }
-  const int c0 = cnt[(hq + q) * 2], c1 = cnt[(hq + q) * 2 + 1];
-  const float tq = tau[hq + q];
-  if (c0 > capH || c1 > capH) {
-    if (l == 0) {
-      const unsigned slot = atomicAdd(&hdr->fb_count, 1u);
-      fblist[slot] = static_cast<int>(hq + q);
-      atomicAdd(&hdr->overflow_queries, 1ull);
-      atomicAdd(&hdr->queries, 1ull);
-    }
-    return;
-  }
+  // an overflowing list still holds capH genuine candidates per half
+  const int r0 = cnt[(hq + q) * 2], r1 = cnt[(hq + q) * 2 + 1];
+  const bool overflow = r0 > capH || r1 > capH;
+  const int c0 = min(r0, capH), c1 = min(r1, capH);
   const int c = c0 + c1;
-  const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
-  const uint2* list1 = list0 + capH;
-  for (int i = l; i < c; i += kWave) {
-    const uint2 e = i < c0 ? list0[i] : list1[i - c0];
-    cj[i] = static_cast<int>(e.x);
-    cs[i] = __uint_as_float(e.y) * scale;
-  }
-  for (int t = l; t < DP; t += kWave) qrow[t] = q32[(hq + q) * DP + t];
-  wave_sync();
-
-  const float2 st = qstat[hq + q];
-  const float m = score_margin(st.x, st.y, __uint_as_float(kstat[2 * h]),
-                               __uint_as_float(kstat[2 * h + 1]), scale);
-  auto lower = [&](float s) { return (s - m) - (fabsf(s) + m) * (1.0f / 4194304.0f); };
-  auto upper = [&](float s) { return (s + m) + (fabsf(s) + m) * (1.0f / 4194304.0f); };
-
-  // the threshold is proven to lie below the k-th best exact score only if
-  // k candidates have a lower bound >= tau
-  int ok_cnt = 0;
-  for (int i = l; i < c; i += kWave) ok_cnt += lower(cs[i]) >= tq ? 1 : 0;
-  ok_cnt = wave_sum_i(ok_cnt);
-  if (ok_cnt < k_i) {
-    if (l == 0) {
-      const unsigned slot = atomicAdd(&hdr->fb_count, 1u);
-      fblist[slot] = static_cast<int>(hq + q);
-      atomicAdd(&hdr->queries, 1ull);
-    }
+  const float tq = tau[hq + q];
+  if (overflow && l == 0 && qlist == nullptr) atomicAdd(&hdr->overflow_queries, 1ull);
+  if (c < k_i + (overflow ? 0 : 1)) {  // too few keys for a proven bound
+    unresolved(__builtin_nanf(""));
     return;
   }
-
-  const uint32_t lo_key = wave_kth_largest<uint32_t>(c, k_i, hist, [&](int i, uint32_t& key) {
-    key = order_key(lower(cs[i]));
-    return true;
+  // Stage the candidates in LDS once (index i runs over half 0, then half 1)
+  // as (order key of the filter score s~ = sum * f, key index).
+  const float4 st = qstat[hq + q];
+  const float kinv =
+      __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
+  const float f = scale * st.z * kinv;
+  {
+    const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
+    const uint2* list1 = list0 + capH;
+#pragma unroll 8
+    for (int i = l; i < c; i += kWave) {
+      const uint2 e = i < c0 ? list0[i] : list1[i - c0];
+      ck[i] = order_key(__uint_as_float(e.y) * f);
+      cj[i] = static_cast<int>(e.x);
+    }
+  }
+  wave_sync();
+  auto each_cand = [&](auto fn) {
+#pragma unroll 1
+    for (int i0 = 0; i0 < c; i0 += kWave) {
+      const int i = i0 + l;
+      const bool ok = i < c;
+      fn(ok ? ck[i] : 0u, ok);
+    }
+  };
+  // The k-th largest filter score gives lo = (k-th) - m, a proven threshold
+  // for any subset of the keys: k of them score >= lo.
+  const float m = score_margin(st.x, st.y, __uint_as_float(kstat[kKeyStatWords * h]),
+                               __uint_as_float(kstat[kKeyStatWords * h + 1]), scale, DP);
+  auto lower = [&](float x) { return (x - m) - (fabsf(x) + m) * (1.0f / 4194304.0f); };
+  auto upper = [&](float x) { return (x + m) + (fabsf(x) + m) * (1.0f / 4194304.0f); };
+  const uint32_t ak = wave_select<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf), each_cand);
+  const float lo = lower(key_to_float(ak));
+  // The list covers every key that can reach the top-k only if the filter's
+  // threshold is proven, i.e. the k best candidates are certainly above it.
+  if (overflow || !(lo >= tq)) {
+    unresolved(lo);
+    return;
+  }
+  // the (k+1)-th largest: equal to the k-th if that value repeats, else the
+  // largest value below it
+  int n_ge = 0;
+  uint32_t below = 0;
+  each_cand([&](uint32_t key, bool ok) {
+    if (ok) {
+      n_ge += key >= ak ? 1 : 0;
+      if (key < ak) below = max(below, key);
+    }
   });
-  const float lo = key_to_float(lo_key);
-  float hi = tq;
-  if (c >= k_i + 1) {
-    const uint32_t hi_key = wave_kth_largest<uint32_t>(c, k_i + 1, hist, [&](int i, uint32_t& key) {
-      key = order_key(upper(cs[i]));
-      return true;
-    });
-    hi = fmaxf(hi, key_to_float(hi_key));
-  }
+  n_ge = wave_sum_i(n_ge);
+  below = wave_max_u32(below);
+  const uint32_t bk = n_ge > k_i ? ak : below;
+  const float hi = fmaxf(tq, upper(key_to_float(bk)));
+  // Certainly kept: l > hi; certainly out: u < lo.  Both tests are monotone in
+  // the filter score, so they become key thresholds: kept iff ck > in_key,
+  // out iff ck < out_key (keys between are uncertain).
+  auto cls_of = [&](uint32_t key) {
+    const float x = key_to_float(key);
+    return lower(x) > hi ? 1 : (upper(x) < lo ? 0 : 2);
+  };
 
-  // classify; re-score the uncertain band exactly
-  int n_in = 0, n_unc = 0;
-  for (int i = l; i < c; i += kWave) {
-    const float s = cs[i];
-    unsigned char k_cls;
-    if (lower(s) > hi) {
-      k_cls = 1;
-      ++n_in;
-    } else if (upper(s) < lo) {
-      k_cls = 0;
-    } else {
-      k_cls = 2;
-      ++n_unc;
-      cs[i] = exact_score<DP>(qrow, k32 + (hq + cj[i]) * DP, scale);
-    }
-    cls[i] = k_cls;
-  }
-  n_in = wave_sum_i(n_in);
-  n_unc = wave_sum_i(n_unc);
-  wave_sync();
-  const int need = k_i - n_in;
-  if (need > n_unc) {
-    // cannot happen when the margins hold; resolve the query exactly anyway
-    if (l == 0) {
-      const unsigned slot = atomicAdd(&hdr->fb_count, 1u);
-      fblist[slot] = static_cast<int>(hq + q);
-      atomicAdd(&hdr->queries, 1ull);
-    }
-    return;
-  }
-  unsigned long long kth = ~0ull;
-  if (need > 0) {
-    kth = wave_kth_largest<unsigned long long>(c, need, hist, [&](int i, unsigned long long& key) {
-      if (cls[i] != 2) return false;
-      key = (static_cast<unsigned long long>(order_key(cs[i])) << 32) |
-            static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(cj[i]));
-      return true;
-    });
-  }
-  // Compact the kept keys of each half, in key order, into `sel` (the score
-  // array, reused): half 0 fills sel[0, n0), half 1 fills sel[n0, n0 + n1).
-  // A write never passes the chunk being read, and the wave syncs between
-  // reading a chunk's scores and overwriting them.
-  int* sel = reinterpret_cast<int*>(cs);
-  int run = 0, n0 = 0;
+  // list the uncertain keys
+  int n_in = 0, nU = 0;
+#pragma unroll 1
   for (int i0 = 0; i0 < c; i0 += kWave) {
     const int i = i0 + l;
-    int take = 0, key = 0;
-    if (i < c) {
-      key = cj[i];
-      if (cls[i] == 1) {
-        take = 1;
-      } else if (cls[i] == 2 && need > 0) {
-        const unsigned long long k64 =
-            (static_cast<unsigned long long>(order_key(cs[i])) << 32) |
-            static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(key));
-        take = k64 >= kth ? 1 : 0;
+    const int cc = i < c ? cls_of(ck[i]) : 0;
+    n_in += cc == 1 ? 1 : 0;
+    const unsigned long long mk = __ballot(cc == 2);
+    if (cc == 2) {
+      const int pos = nU + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                               static_cast<uint32_t>(mk >> 32),
+                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
+      if (pos < ucap) uj[pos] = cj[i];
+    }
+    nU += __builtin_popcountll(mk);
+  }
+  n_in = wave_sum_i(n_in);
+  const int need = k_i - n_in;
+  if (nU > ucap || need > nU) {
+    unresolved(__builtin_nanf(""));
+    return;
+  }
+  wave_sync();
+  // exact re-score of the uncertain keys: G lanes per key, 16 bytes each
+  {
+    constexpr int G = DP / 4;
+    constexpr int KPI = kWave / G;     // keys per pass
+    constexpr int UNR = 4;             // passes in flight
+    const int g = l % G, grp = l / G;
+    const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
+#pragma unroll 1
+    for (int u0 = 0; u0 < nU; u0 += KPI * UNR) {
+      float4 kv[UNR];
+#pragma unroll
+      for (int t = 0; t < UNR; ++t) {
+        const int u = u0 + t * KPI + grp;
+        kv[t] = u < nU ? reinterpret_cast<const float4*>(k32 + (hq + uj[u]) * DP)[g]
+                       : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int t = 0; t < UNR; ++t) {
+        float p = group_partial<DP>(qv, kv[t]);
+#pragma unroll
+        for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
+        const int u = u0 + t * KPI + grp;
+        if (g == 0 && u < nU) us[u] = p * scale;
       }
     }
-    const int incl = wave_incl_scan(take);
-    const int first_half = (i < c0 && take) ? 1 : 0;
-    n0 += wave_sum_i(first_half);
+  }
+  wave_sync();
+  unsigned long long kth = ~0ull;
+  if (need > 0) {
+    kth = wave_select<unsigned long long>(need, hist, cbuf, [&](auto fn) {
+#pragma unroll 1
+      for (int u0 = 0; u0 < nU; u0 += kWave) {
+        const int u = u0 + l;
+        fn(u < nU ? rank_key(us[u], uj[u]) : 0ull, u < nU);
+      }
+    });
+  }
+  // Compact the kept keys in list order (each half ascending) in place into
+  // cj: a chunk's reads all happen before its writes, and writes never pass
+  // the chunk.  The uncertain keys are met in the order they were listed.
+  int run = 0, n0 = 0, ucount = 0;
+#pragma unroll 1
+  for (int i0 = 0; i0 < c; i0 += kWave) {
+    const int i = i0 + l;
+    const int cc = i < c ? cls_of(ck[i]) : 0;
+    const int key = i < c ? cj[i] : 0;
+    const unsigned long long mk = __ballot(cc == 2);
+    bool take = cc == 1;
+    if (cc == 2) {
+      const int pos = ucount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                   static_cast<uint32_t>(mk >> 32),
+                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
+      take = need > 0 && rank_key(us[pos], uj[pos]) >= kth;
+    }
+    ucount += __builtin_popcountll(mk);
+    const unsigned long long tk = __ballot(take);
     wave_sync();
-    if (take) sel[run + incl - 1] = key;
-    run += __shfl(incl, kWave - 1, kWave);
+    if (take)
+      cj[run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                   static_cast<uint32_t>(tk >> 32),
+                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tk), 0)))] = key;
+    run += __builtin_popcountll(tk);
+    n0 += __builtin_popcountll(__ballot(take && i < c0));
     wave_sync();
   }
+  const int* sel = cj;
   const int n1 = run - n0;
-  // merge the two ascending lists into the output row
-  for (int p = l; p < n0; p += kWave) out[p + lower_bound(sel + n0, n1, sel[p])] = sel[p];
-  for (int p = l; p < n1; p += kWave) out[p + lower_bound(sel, n0, sel[n0 + p])] = sel[n0 + p];
+  for (int p2 = l; p2 < n0; p2 += kWave) out[p2 + lower_bound(sel + n0, n1, sel[p2])] = sel[p2];
+  for (int p2 = l; p2 < n1; p2 += kWave)
+    out[p2 + lower_bound(sel, n0, sel[n0 + p2])] = sel[n0 + p2];
   for (int t = run + l; t < k; t += kWave) out[t] = -1;
   if (l == 0) {
-    atomicAdd(&hdr->rescored, static_cast<unsigned long long>(n_unc));
+    atomicAdd(&hdr->rescored, static_cast<unsigned long long>(nU));
     atomicAdd(&hdr->queries, 1ull);
   }
 }
@@ -354,10 +523,11 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
 
 template <int DP>
 hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t* idx,
-                      hipStream_t s) {
-  // as many waves (queries) per workgroup as the per-wave LDS allows
-  const size_t per_wave = static_cast<size_t>(2 * p.capH) * 9 + 1024 + DP * 4;
-  int wpb = static_cast<int>((160 * 1024) / per_wave);
+                      bool retry, hipStream_t s) {
+  // the uncertain band is ~8x narrower with fp16 filter operands than bf16
+  const int ucap = p.filt ? 512 : 256;
+  const size_t per_wave = rerank_lds_per_wave(2 * p.capH, ucap);
+  int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
   const dim3 grid((p.N + wpb - 1) / wpb, nh);
   const size_t lds = static_cast<size_t>(wpb) * per_wave;
@@ -365,9 +535,11 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt, b.tau,
-                     b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal, p.capH,
-                     scale, idx, b.fblist, b.hdr);
+  hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt,
+                     b.tau, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
+                     p.capH, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
+                     retry ? b.rcount : static_cast<int*>(nullptr), b.rlist, b.rcount, b.fblist,
+                     b.hdr);
   return hipGetLastError();
 }
 
@@ -382,12 +554,12 @@ hipError_t fallback_t(const Plan& p, const Bufs& b, float scale, int32_t* idx, h
 }  // namespace
 
 hipError_t launch_finalize(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, hipStream_t s) {
+                           int32_t* idx_chunk, bool retry, hipStream_t s) {
   switch (p.dp) {
-    case 16: return finalize_t<16>(p, b, nh, score_scale, idx_chunk, s);
-    case 32: return finalize_t<32>(p, b, nh, score_scale, idx_chunk, s);
-    case 64: return finalize_t<64>(p, b, nh, score_scale, idx_chunk, s);
-    case 128: return finalize_t<128>(p, b, nh, score_scale, idx_chunk, s);
+    case 16: return finalize_t<16>(p, b, nh, score_scale, idx_chunk, retry, s);
+    case 32: return finalize_t<32>(p, b, nh, score_scale, idx_chunk, retry, s);
+    case 64: return finalize_t<64>(p, b, nh, score_scale, idx_chunk, retry, s);
+    case 128: return finalize_t<128>(p, b, nh, score_scale, idx_chunk, retry, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,13 +1,17 @@
 // Scorer projection: q_low = Q·Pq and k_low = K·Pk for every row of a head
 // chunk (page "mhpq.cn/news/1098205", §2.2: the scorer's q_proj / k_proj map
-// each head's d_model-wide vectors to d_proj dimensions).
+// each head's vectors to d_proj dimensions).
 //
 // Per row it writes the fp32 projection (accumulated with FMAs in ascending
-// order of the model dimension, the fixed order every exact score relies
-// on), its bf16 rounding for the MFMA filter, and two norms that bound the
-// filter's error: ||x_low|| and ||x_low - bf16(x_low)||, both rounded up.
-// Key rows also feed a per-head maximum of those norms and every 16th key
-// row is copied to the threshold sample.  Rows N..Npad-1 are zero padding.
+// order of the model dimension, a fixed order that every exact score relies
+// on) and, for the filter, a 16-bit copy scaled by a power of two (one
+// exponent per query row, one per key head), plus the norms that bound the
+// filter's error: ||x_low|| and ||x_low - x~|| (x~ the 16-bit row back in
+// true units), both rounded up.  Keys need their head's exponent before they
+// can be rounded, so they take two kernels: the projection (fp32 rows, the
+// head's max |k| and max ||k||) and the pack (16-bit rows, residual norms,
+// and every 16th row copied to the threshold sample).  Rows N..Npad-1 are
+// zero padding.
 #include "sa_internal.h"
 
 namespace sa {
@@ -21,17 +25,18 @@ constexpr int kThreads = 256;
 // sum of squares and of the square root).
 constexpr float kNormUp = 1.0f + 1.0f / 65536.0f;
 
-template <typename T, int D, int DP>
+template <typename T, int D, int DP, typename F>
 __global__ __launch_bounds__(kThreads) void project_kernel(
     const T* __restrict__ X, const T* __restrict__ P, int N, int Npad, int is_key,
-    float* __restrict__ lo32, bf16_t* __restrict__ lo16, float2* __restrict__ stat,
-    bf16_t* __restrict__ samp, uint32_t* __restrict__ kstat) {
+    float* __restrict__ lo32, uint16_t* __restrict__ lo16, float4* __restrict__ qstat,
+    uint32_t* __restrict__ kstat) {
   constexpr int kXFloats = kRows * (D + 1);
   constexpr int kLoFloats = 2 * kRows * (DP + 1);
   __shared__ float sP[D * DP];
   // the staged input rows are dead once accumulated, so the projected rows
-  // and their bf16 residuals reuse that space
+  // and their rounding residuals reuse that space
   __shared__ float sXLo[kXFloats > kLoFloats ? kXFloats : kLoFloats];
+  __shared__ int sE[kRows];
   __shared__ float sMax[2][kRows];
   float* sX = sXLo;
   float* sLo = sXLo;
@@ -70,41 +75,101 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
     const int r = g + i * kGroups;
     const int row = row0 + r;
     const float v = (row < N) ? acc[i] : 0.0f;
-    const bf16_t vb = f32_to_bf16(v);
     lo32[(base + row) * DP + c] = v;
-    lo16[(base + row) * DP + c] = vb;
-    if (samp != nullptr && (row % kSampleStride) == 0)
-      samp[(static_cast<size_t>(h) * (Npad / kSampleStride) + row / kSampleStride) * DP + c] = vb;
     sLo[r * (DP + 1) + c] = v;
-    sRes[r * (DP + 1) + c] = v - bf16_to_f32(vb);
   }
   __syncthreads();
   if (tid < kRows) {
-    float s2 = 0.0f, r2 = 0.0f;
+    float mx = 0.0f, s2 = 0.0f;
     for (int cc = 0; cc < DP; ++cc) {
       const float a = sLo[tid * (DP + 1) + cc];
-      const float b = sRes[tid * (DP + 1) + cc];
+      mx = fmaxf(mx, fabsf(a));
       s2 = __builtin_fmaf(a, a, s2);
-      r2 = __builtin_fmaf(b, b, r2);
     }
-    const float n = __builtin_sqrtf(s2) * kNormUp;
-    const float rn = __builtin_sqrtf(r2) * kNormUp;
-    if (stat != nullptr) stat[base + row0 + tid] = make_float2(n, rn);
-    sMax[0][tid] = n;
-    sMax[1][tid] = rn;
+    sE[tid] = scale_exponent(mx);
+    sMax[0][tid] = __builtin_sqrtf(s2) * kNormUp;
+    sMax[1][tid] = mx;
   }
+  __syncthreads();
   if (is_key) {
-    __syncthreads();
     if (tid < 2) {
       float m = 0.0f;
       for (int r = 0; r < kRows; ++r) m = fmaxf(m, sMax[tid][r]);
       // non-negative floats order like their bit patterns
-      atomicMax(&kstat[2 * h + tid], __float_as_uint(m));
+      atomicMax(&kstat[kKeyStatWords * h + (tid == 0 ? 0 : 2)], __float_as_uint(m));
     }
+    return;
+  }
+  // queries: 16-bit rows with the row's own exponent, and residuals
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int r = g + i * kGroups;
+    const int row = row0 + r;
+    const int e = sE[r];
+    const float v = sLo[r * (DP + 1) + c];
+    const uint16_t u = F::round(__builtin_ldexpf(v, e));
+    lo16[(base + row) * DP + c] = u;
+    sRes[r * (DP + 1) + c] = v - __builtin_ldexpf(F::back(u), -e);
+  }
+  __syncthreads();
+  if (tid < kRows) {
+    float r2 = 0.0f;
+    for (int cc = 0; cc < DP; ++cc) {
+      const float b = sRes[tid * (DP + 1) + cc];
+      r2 = __builtin_fmaf(b, b, r2);
+    }
+    qstat[base + row0 + tid] =
+        make_float4(sMax[0][tid], __builtin_sqrtf(r2) * kNormUp, __builtin_ldexpf(1.0f, -sE[tid]), 0.0f);
   }
 }
 
-__global__ void init_chunk_kernel(WsHeader* hdr, uint32_t* kstat, int nh, int first_chunk) {
+// Keys: 16-bit rows with the head's exponent, the threshold sample, and the
+// head's largest residual norm.
+template <int DP, typename F>
+__global__ __launch_bounds__(kThreads) void pack_keys_kernel(
+    const float* __restrict__ k32, int Npad, uint32_t* __restrict__ kstat,
+    uint16_t* __restrict__ k16, uint16_t* __restrict__ samp) {
+  __shared__ float sRes[kRows * (DP + 1)];
+  __shared__ float sMax[kRows];
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int row0 = blockIdx.x * kRows;
+  const int E = scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2]));
+  const size_t base = static_cast<size_t>(h) * Npad;
+  constexpr int kGroups = kThreads / DP;
+  constexpr int kRowsPerThread = kRows / kGroups;
+  const int c = tid % DP;
+  const int g = tid / DP;
+#pragma unroll
+  for (int i = 0; i < kRowsPerThread; ++i) {
+    const int r = g + i * kGroups;
+    const int row = row0 + r;
+    const float v = k32[(base + row) * DP + c];
+    const uint16_t u = F::round(__builtin_ldexpf(v, E));
+    k16[(base + row) * DP + c] = u;
+    if ((row % kSampleStride) == 0)
+      samp[(static_cast<size_t>(h) * (Npad / kSampleStride) + row / kSampleStride) * DP + c] = u;
+    sRes[r * (DP + 1) + c] = v - __builtin_ldexpf(F::back(u), -E);
+  }
+  __syncthreads();
+  if (tid < kRows) {
+    float r2 = 0.0f;
+    for (int cc = 0; cc < DP; ++cc) {
+      const float b = sRes[tid * (DP + 1) + cc];
+      r2 = __builtin_fmaf(b, b, r2);
+    }
+    sMax[tid] = __builtin_sqrtf(r2) * kNormUp;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float m = 0.0f;
+    for (int r = 0; r < kRows; ++r) m = fmaxf(m, sMax[r]);
+    atomicMax(&kstat[kKeyStatWords * h + 1], __float_as_uint(m));
+  }
+}
+
+__global__ void init_chunk_kernel(WsHeader* hdr, uint32_t* kstat, int* rcount, int nh,
+                                  int first_chunk) {
   const int t = threadIdx.x;
   if (t == 0) {
     if (first_chunk) {
@@ -113,38 +178,66 @@ __global__ void init_chunk_kernel(WsHeader* hdr, uint32_t* kstat, int nh, int fi
       hdr->candidates = 0;
       hdr->rescored = 0;
       hdr->queries = 0;
+      hdr->retried = 0;
     }
     hdr->fb_count = 0;
     hdr->fb_next = 0;
   }
-  for (int i = t; i < 2 * nh; i += blockDim.x) kstat[i] = 0u;
+  for (int i = t; i < kKeyStatWords * nh; i += blockDim.x) kstat[i] = 0u;
+  for (int i = t; i < nh; i += blockDim.x) rcount[i] = 0;
 }
 
-template <typename T, int D, int DP>
+template <typename T, int D, int DP, typename F>
 hipError_t project_t(const Plan& p, const Bufs& b, const void* Q, const void* K,
                      const void* Pq, const void* Pk, int h0, int nh, hipStream_t s) {
   const dim3 grid(p.Npad / kRows, nh, 1);
   const T* Qh = static_cast<const T*>(Q) + static_cast<size_t>(h0) * p.N * D;
   const T* Kh = static_cast<const T*>(K) + static_cast<size_t>(h0) * p.N * D;
-  hipLaunchKernelGGL((project_kernel<T, D, DP>), grid, dim3(kThreads), 0, s, Qh,
+  hipLaunchKernelGGL((project_kernel<T, D, DP, F>), grid, dim3(kThreads), 0, s, Qh,
                      static_cast<const T*>(Pq), p.N, p.Npad, 0, b.qlo32, b.qlo16, b.qstat,
-                     static_cast<bf16_t*>(nullptr), b.kstat);
+                     b.kstat);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((project_kernel<T, D, DP>), grid, dim3(kThreads), 0, s, Kh,
-                     static_cast<const T*>(Pk), p.N, p.Npad, 1, b.klo32, b.klo16,
-                     static_cast<float2*>(nullptr), b.ksamp, b.kstat);
+  hipLaunchKernelGGL((project_kernel<T, D, DP, F>), grid, dim3(kThreads), 0, s, Kh,
+                     static_cast<const T*>(Pk), p.N, p.Npad, 1, b.klo32,
+                     static_cast<uint16_t*>(nullptr), static_cast<float4*>(nullptr), b.kstat);
   return hipGetLastError();
 }
 
-template <typename T, int D>
+template <typename T, int D, typename F>
 hipError_t project_d(const Plan& p, const Bufs& b, const void* Q, const void* K,
                      const void* Pq, const void* Pk, int h0, int nh, hipStream_t s) {
   switch (p.dp) {
-    case 16: return project_t<T, D, 16>(p, b, Q, K, Pq, Pk, h0, nh, s);
-    case 32: return project_t<T, D, 32>(p, b, Q, K, Pq, Pk, h0, nh, s);
-    case 64: return project_t<T, D, 64>(p, b, Q, K, Pq, Pk, h0, nh, s);
-    case 128: return project_t<T, D, 128>(p, b, Q, K, Pq, Pk, h0, nh, s);
+    case 16: return project_t<T, D, 16, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+    case 32: return project_t<T, D, 32, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+    case 64: return project_t<T, D, 64, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+    case 128: return project_t<T, D, 128, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, typename F>
+hipError_t project_tf(const Plan& p, const Bufs& b, const void* Q, const void* K,
+                      const void* Pq, const void* Pk, int h0, int nh, hipStream_t s) {
+  if (p.D == 64) return project_d<T, 64, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+  if (p.D == 128) return project_d<T, 128, F>(p, b, Q, K, Pq, Pk, h0, nh, s);
+  return hipErrorInvalidValue;
+}
+
+template <typename F>
+hipError_t pack_f(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
+  const dim3 grid(p.Npad / kRows, nh, 1);
+  switch (p.dp) {
+#define SA_PACK(DPV)                                                                          \
+  case DPV:                                                                                   \
+    hipLaunchKernelGGL((pack_keys_kernel<DPV, F>), grid, dim3(kThreads), 0, s, b.klo32, p.Npad, \
+                       b.kstat, b.klo16, b.ksamp);                                            \
+    return hipGetLastError();
+    SA_PACK(16)
+    SA_PACK(32)
+    SA_PACK(64)
+    SA_PACK(128)
+#undef SA_PACK
   }
   return hipErrorInvalidValue;
 }
@@ -152,7 +245,7 @@ hipError_t project_d(const Plan& p, const Bufs& b, const void* Q, const void* K,
 }  // namespace
 
 hipError_t launch_init_chunk(const Plan& p, const Bufs& b, int first_chunk, hipStream_t s) {
-  hipLaunchKernelGGL(init_chunk_kernel, dim3(1), dim3(256), 0, s, b.hdr, b.kstat, p.hc,
+  hipLaunchKernelGGL(init_chunk_kernel, dim3(1), dim3(256), 0, s, b.hdr, b.kstat, b.rcount, p.hc,
                      first_chunk);
   return hipGetLastError();
 }
@@ -160,13 +253,15 @@ hipError_t launch_init_chunk(const Plan& p, const Bufs& b, int first_chunk, hipS
 hipError_t launch_project(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, hipStream_t s) {
   if (p.dtype == 0) {
-    if (p.D == 64) return project_d<float, 64>(p, b, Q, K, Pq, Pk, h0, nh, s);
-    if (p.D == 128) return project_d<float, 128>(p, b, Q, K, Pq, Pk, h0, nh, s);
-  } else {
-    if (p.D == 64) return project_d<bf16_t, 64>(p, b, Q, K, Pq, Pk, h0, nh, s);
-    if (p.D == 128) return project_d<bf16_t, 128>(p, b, Q, K, Pq, Pk, h0, nh, s);
+    return p.filt ? project_tf<float, FiltBf16>(p, b, Q, K, Pq, Pk, h0, nh, s)
+                  : project_tf<float, FiltF16>(p, b, Q, K, Pq, Pk, h0, nh, s);
   }
-  return hipErrorInvalidValue;
+  return p.filt ? project_tf<bf16_t, FiltBf16>(p, b, Q, K, Pq, Pk, h0, nh, s)
+                : project_tf<bf16_t, FiltF16>(p, b, Q, K, Pq, Pk, h0, nh, s);
+}
+
+hipError_t launch_pack_keys(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
+  return p.filt ? pack_f<FiltBf16>(p, b, nh, s) : pack_f<FiltF16>(p, b, nh, s);
 }
 
 }  // namespace sa

@@ -51,31 +51,103 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 }
 
 // ---------------------------------------------------------- exact score ---
-// The fp32 score that decides the selection: the dot product of the fp32
-// low-dimensional rows, accumulated with fused multiply-adds in ascending
-// coordinate order, then multiplied by score_scale.  Every kernel that needs
-// the exact score (re-rank, fallback, dump) calls this one function.
+// The fp32 score that decides the selection, in one fixed evaluation order
+// shared by every kernel that needs it (re-rank, fallback, dump):
+//   p_g = q[4g]k[4g] + q[4g+1]k[4g+1] + ... as a chain of fused multiply-adds
+//         over the 4 coordinates of group g (g = 0 .. DP/4-1),
+//   then an xor-butterfly over the groups: at step o (DP/8, ..., 2, 1) every
+//   p_g becomes p_g + p_{g^o}; the result is p_0 · scale.
+// A wavefront evaluates it with one lane per group and __shfl_xor steps;
+// exact_score() below is the same arithmetic for one thread.
+template <int DP>
+__device__ __forceinline__ float group_partial(const float4 q, const float4 k) {
+  return __builtin_fmaf(q.w, k.w, __builtin_fmaf(q.z, k.z, __builtin_fmaf(q.y, k.y,
+         __builtin_fmaf(q.x, k.x, 0.0f))));
+}
+
 template <int DP>
 __device__ __forceinline__ float exact_score(const float* __restrict__ q,
                                              const float* __restrict__ k, float scale) {
-  float acc = 0.0f;
+  constexpr int G = DP / 4;
+  float p[G];
 #pragma unroll
-  for (int c = 0; c < DP; ++c) acc = __builtin_fmaf(q[c], k[c], acc);
-  return acc * scale;
+  for (int g = 0; g < G; ++g)
+    p[g] = group_partial<DP>(make_float4(q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]),
+                             make_float4(k[4 * g], k[4 * g + 1], k[4 * g + 2], k[4 * g + 3]));
+#pragma unroll
+  for (int o = G / 2; o >= 1; o >>= 1) {
+    float t[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) t[g] = p[g] + p[g ^ o];
+#pragma unroll
+    for (int g = 0; g < G; ++g) p[g] = t[g];
+  }
+  return p[0] * scale;
 }
 
-// Margin between the bf16 MFMA score and the exact fp32 score of query
-// (qn = ||q_low||, qr = ||q_low - bf16(q_low)||) against any key of the
-// head (kn = max ||k_low||, kr = max residual).  With q~, k~ the bf16 rows:
-//   q·k - q~·k~ = q·(k - k~) + (q - q~)·k~,  |.| <= qn*kr + qr*||k~||
-// and ||k~|| <= kn (1 + 2^-8).  Both the MFMA and the exact dot product add
-// at most d_proj rounding errors of 2^-23 relative to qn*kn each (d_proj <=
-// 128), covered with ample room by the 2^-13 term; the final 2^-10 factor
-// and the absolute floor cover the rounding of this expression itself and
-// flushed subnormals.
+// ------------------------------------------------- 16-bit filter operands ---
+// The filter scores pairs with a 16-bit MFMA (fp16 by default, bf16 as an
+// option).  Rows are scaled by a power of two before rounding so that the
+// largest element lands in [2^14, 2^15): each query row has its own exponent
+// e_q, each key head one exponent E for all its keys.  Elements that would
+// become subnormal are flushed to zero; the residual norms below include
+// them, so no precision assumption about the MFMA is needed.
+__device__ __forceinline__ int scale_exponent(float maxabs) {
+  if (!(maxabs > 0.0f)) return 0;
+  int p;
+  (void)__builtin_frexpf(maxabs, &p);       // maxabs = f * 2^p, f in [0.5, 1)
+  const int e = 15 - p;
+  return e < -64 ? -64 : (e > 64 ? 64 : e);
+}
+
+struct FiltF16 {
+  typedef __attribute__((ext_vector_type(8))) _Float16 vec8;
+  __device__ __forceinline__ static uint16_t round(float x) {
+    if (fabsf(x) < 6.103515625e-05f) x = 0.0f;   // below the fp16 normal range
+    const _Float16 h = static_cast<_Float16>(x);
+    uint16_t u;
+    __builtin_memcpy(&u, &h, 2);
+    return u;
+  }
+  __device__ __forceinline__ static float back(uint16_t u) {
+    _Float16 h;
+    __builtin_memcpy(&h, &u, 2);
+    return static_cast<float>(h);
+  }
+  __device__ __forceinline__ static f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
+    vec8 va, vb;
+    __builtin_memcpy(&va, &a, 16);
+    __builtin_memcpy(&vb, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(va, vb, c, 0, 0, 0);
+  }
+};
+
+struct FiltBf16 {
+  __device__ __forceinline__ static uint16_t round(float x) {
+    if (fabsf(x) < 1.1754943508e-38f) x = 0.0f;  // below the fp32/bf16 normal range
+    return f32_to_bf16(x);
+  }
+  __device__ __forceinline__ static float back(uint16_t u) { return bf16_to_f32(u); }
+  __device__ __forceinline__ static f32x16 mfma(uint4 a, uint4 b, f32x16 c) {
+    bf16x8 va, vb;
+    __builtin_memcpy(&va, &a, 16);
+    __builtin_memcpy(&vb, &b, 16);
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, c, 0, 0, 0);
+  }
+};
+
+// Margin between the 16-bit MFMA score and the exact fp32 score of a query
+// (qn = ||q_low||, qr = ||q_low - q~||, q~ the rounded row in true units)
+// against any key of the head (kn = max ||k_low||, kr = max ||k_low - k~||):
+//   q·k - q~·k~ = q·(k - k~) + (q - q~)·k~,   |.| <= qn*kr + qr*||k~||,
+// with ||k~|| <= kn (1 + 2^-8).  The MFMA sum and the exact fp32 evaluation
+// each add at most (d_proj + 8) roundings of 2^-23 relative to qn*kn
+// (covered twice by the eps term); the final factor and the absolute floor
+// cover the rounding of this expression and flushed tiny values.
 __device__ __forceinline__ float score_margin(float qn, float qr, float kn, float kr,
-                                              float scale) {
-  const float m = scale * (qn * kr + (1.01f * qr + 0.0001220703125f * qn) * kn);
+                                              float scale, int dp) {
+  const float eps = static_cast<float>(dp + 16) * (1.0f / 4194304.0f);
+  const float m = scale * (qn * kr + (1.01f * qr + eps * qn) * kn);
   return m * (1.0f + 1.0f / 1024.0f) + 1e-28f;
 }
 
@@ -112,15 +184,14 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // A few counters at the start of the workspace (all int64 / int32).
 struct WsHeader {
   unsigned long long fallback_queries;   // resolved by the exact fallback
-  unsigned long long overflow_queries;   // candidate buffer too small
+  unsigned long long overflow_queries;   // candidate lists overflowed (first pass)
   unsigned long long candidates;         // candidates written by the filter
   unsigned long long rescored;           // keys re-scored exactly in the re-rank
-  unsigned long long queries;            // queries processed
-  unsigned int key_norm_max;             // max ||k_low|| of the chunk (fp32 bits)
-  unsigned int key_res_max;              // max ||k_low - bf16(k_low)|| (fp32 bits)
+  unsigned long long queries;            // queries resolved
+  unsigned long long retried;            // queries filtered again with a proven threshold
   unsigned int fb_count;                 // queries queued for the fallback
   unsigned int fb_next;                  // fallback work-queue cursor
-  unsigned int pad[6];
+  unsigned int pad[2];
 };
 static_assert(sizeof(WsHeader) % 16 == 0, "header keeps 16-byte alignment");
 

@@ -21,6 +21,7 @@ constexpr int kKMax = 2048;             // largest supported k
 // Byte offsets of one head chunk's buffers inside the workspace.
 struct Plan {
   int B, H, N, D, dp, k, causal, dtype;
+  int filt;       // 16-bit filter operands: 0 = fp16, 1 = bf16
   int BH;         // B*H heads
   int hc;         // heads per chunk
   int Npad;       // N rounded up to kRowPad
@@ -30,14 +31,17 @@ struct Plan {
   int capH;       // candidate capacity of one query half
   int with_idx;   // room for idx rows of the chunk
   size_t off_hdr, off_qlo32, off_klo32, off_qlo16, off_klo16, off_ksamp, off_qstat,
-      off_kstat, off_bm, off_tau, off_cand, off_cnt, off_fblist, off_fbscratch, off_idx,
-      total;
+      off_kstat, off_bm, off_tau, off_cand, off_cnt, off_rlist, off_rcount, off_fblist,
+      off_fbscratch, off_idx, total;
 };
 
 // Fills every field from the arguments and heads_per_chunk; returns false
 // when the sizes do not fit the index arithmetic.
 bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, int dtype,
                int with_idx, int heads_per_chunk);
+
+// Number of kstat words per head.
+constexpr int kKeyStatWords = 4;
 
 // Pointers of the chunk buffers for a given workspace base.
 struct Bufs {
@@ -47,12 +51,14 @@ struct Bufs {
   bf16_t* qlo16;
   bf16_t* klo16;
   bf16_t* ksamp;
-  float2* qstat;        // (||q_low||, ||q_low - bf16(q_low)||), upper bounds
-  uint32_t* kstat;      // per head: max ||k_low||, max residual (fp32 bits)
+  float4* qstat;        // per query: ||q_low||, ||q_low - q~||, 2^-e_q (norms rounded up)
+  uint32_t* kstat;      // per head: max ||k_low||, max ||k_low - k~||, max |k_low|_inf (fp32 bits)
   float* bm;            // sample block maxima [hc][NB][Npad]
   float* tau;           // per-query threshold [hc][Npad]
   uint2* cand;          // candidates [hc][Npad][2][capH] = (key, raw MFMA sum bits)
   int* cnt;             // candidates per query half [hc][Npad][2]
+  int* rlist;           // per head: queries to filter again with a proven threshold
+  int* rcount;          // per head: entries of rlist
   int* fblist;          // queries queued for the exact fallback
   float* fbscratch;     // [kFallbackBlocks][Npad] exact scores
   int32_t* idx;         // optional idx rows [hc][N][k]
@@ -65,13 +71,16 @@ Bufs bufs_of(const Plan& p, void* ws);
 hipError_t launch_init_chunk(const Plan& p, const Bufs& b, int first_chunk, hipStream_t s);
 hipError_t launch_project(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, hipStream_t s);
-hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, hipStream_t s);
+hipError_t launch_pack_keys(const Plan& p, const Bufs& b, int nh, hipStream_t s);
+hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, float score_scale,
+                                hipStream_t s);
 hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_scale,
                             hipStream_t s);
-hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale,
+// retry = false: every query; retry = true: the queries listed in rlist.
+hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale, bool retry,
                          hipStream_t s);
 hipError_t launch_finalize(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, hipStream_t s);
+                           int32_t* idx_chunk, bool retry, hipStream_t s);
 hipError_t launch_fallback(const Plan& p, const Bufs& b, int nh, float score_scale,
                            int32_t* idx_chunk, hipStream_t s);
 hipError_t launch_dump(const Plan& p, const Bufs& b, int nh, float score_scale,

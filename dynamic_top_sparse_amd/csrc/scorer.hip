@@ -1,10 +1,10 @@
-// The scorer contraction on bf16 MFMA and the streaming per-query filter
+// The scorer contraction on 16-bit MFMA and the streaming per-query filter
 // (page "mhpq.cn/news/1098205", §2.2: scores are scaled dot products of the
 // low-dimensional rows, S = d_proj^-1/2 · q_low·k_lowᵀ; §3.2: torch.topk
 // keeps the k best keys per query).  No score matrix is ever written: tiles of
 // 32 keys x 32 queries live in MFMA accumulators and are reduced on the spot.
 //
-// The bf16 MFMA result s~ differs from the exact fp32 score s by at most a
+// The 16-bit MFMA result s~ differs from the exact fp32 score s by at most a
 // margin m_i per query (a Cauchy-Schwarz bound built from the row norms the
 // projection kernel stores).  The filter therefore proves, rather than
 // guesses, that it keeps every key of the exact top-k:
@@ -19,8 +19,8 @@
 // score, so no key outside the list can belong to the top-k.  Queries whose
 // check fails, or whose list overflows, are handed to the exact fallback.
 //
-// MFMA orientation (v_mfma_f32_32x32x16_bf16): A = 32 keys from LDS, B = 32
-// queries held in registers.  Lane l then owns query l%32 and, in its 16
+// MFMA orientation (v_mfma_f32_32x32x16_f16 or _bf16, by the filter
+// precision): A = 32 keys from LDS, B = 32 queries held in registers.  Lane l then owns query l%32 and, in its 16
 // accumulators, keys 8*(r/4) + 4*(l/32) + r%4 of the tile, so the threshold
 // is one register per lane and each lane appends to its own list.
 #include <float.h>
@@ -50,57 +50,63 @@ __device__ __forceinline__ int lds_unit(int key, int u) {
   return key * U + (u ^ (key & (U - 1)));
 }
 
-// One thread's share of a staged key chunk, held in registers between the
-// global loads (issued a chunk ahead) and the LDS writes.
+// A thread's share of a staged key chunk is held in a plain register array
+// between the global loads (issued a chunk ahead) and the LDS writes.
 template <int DP>
-struct ChunkRegs {
+struct Stage {
   static constexpr int kPerThread = Tile<DP>::kChunkUnits / kThreads;
-  uint4 r[kPerThread];
-
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ rows, int key0) {
-    const uint4* src = reinterpret_cast<const uint4*>(rows + static_cast<size_t>(key0) * DP);
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) r[i] = src[threadIdx.x + i * kThreads];
-  }
-  __device__ __forceinline__ void store(uint4* __restrict__ lds) const {
-    constexpr int U = Tile<DP>::kUnits;
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int e = threadIdx.x + i * kThreads;
-      lds[lds_unit<DP>(e / U, e % U)] = r[i];
-    }
-  }
 };
 
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) {
-  bf16x8 r;
-  __builtin_memcpy(&r, &v, 16);
-  return r;
+// (native clang vectors: HIP's uint4 wrapper keeps the array in scratch)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int DP>
+__device__ __forceinline__ void chunk_load(u32x4 (&r)[Stage<DP>::kPerThread],
+                                           const bf16_t* __restrict__ rows, int key0) {
+  const u32x4* src = reinterpret_cast<const u32x4*>(rows + static_cast<size_t>(key0) * DP);
+#pragma unroll
+  for (int i = 0; i < Stage<DP>::kPerThread; ++i) r[i] = src[threadIdx.x + i * kThreads];
+}
+
+template <int DP>
+__device__ __forceinline__ void chunk_store(const u32x4 (&r)[Stage<DP>::kPerThread],
+                                            uint4* __restrict__ lds) {
+  constexpr int U = Tile<DP>::kUnits;
+  u32x4* dst = reinterpret_cast<u32x4*>(lds);
+#pragma unroll
+  for (int i = 0; i < Stage<DP>::kPerThread; ++i) {
+    const int e = threadIdx.x + i * kThreads;
+    dst[lds_unit<DP>(e / U, e % U)] = r[i];
+  }
 }
 
 // B fragments (queries) of one 32-query block: lane l holds query row l%32,
-// model coordinates [16*ks + 8*(l/32), +8).
+// model coordinates [16*ks + 8*(l/32), +8), as raw 16-bit values.
 template <int DP>
-__device__ __forceinline__ void load_query_frags(bf16x8 (&b)[Tile<DP>::kKSteps],
+__device__ __forceinline__ void load_query_frags(uint4 (&b)[Tile<DP>::kKSteps],
                                                  const bf16_t* __restrict__ q16, int q) {
   const int l = lane_id();
   const uint4* row = reinterpret_cast<const uint4*>(q16 + static_cast<size_t>(q) * DP);
 #pragma unroll
-  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks) b[ks] = as_bf16x8(row[2 * ks + (l >> 5)]);
+  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks) b[ks] = row[2 * ks + (l >> 5)];
 }
 
-template <int DP>
+template <int DP, typename F>
 __device__ __forceinline__ f32x16 tile_scores(const uint4* __restrict__ lds, int tile_in_chunk,
-                                              const bf16x8 (&b)[Tile<DP>::kKSteps]) {
+                                              const uint4 (&b)[Tile<DP>::kKSteps]) {
   const int l = lane_id();
   const int key = tile_in_chunk * 32 + (l & 31);
   f32x16 acc = {};
 #pragma unroll
-  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks) {
-    const bf16x8 a = as_bf16x8(lds[lds_unit<DP>(key, 2 * ks + (l >> 5))]);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[ks], acc, 0, 0, 0);
-  }
+  for (int ks = 0; ks < Tile<DP>::kKSteps; ++ks)
+    acc = F::mfma(lds[lds_unit<DP>(key, 2 * ks + (l >> 5))], b[ks], acc);
   return acc;
+}
+
+// Factor that turns a raw MFMA sum of query q into its filter score
+// s~ = sum * 2^-(e_q + E) * score_scale (exact power-of-two rescaling).
+__device__ __forceinline__ float score_factor(float qinv, float kinv, float scale) {
+  return scale * qinv * kinv;
 }
 
 // Key row of accumulator r for this lane, relative to the tile base.
@@ -109,10 +115,11 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 }
 
 // ------------------------------------------------------------ sample pass ---
-template <int DP>
+template <int DP, typename F>
 __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
-    const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp, int N, int Npad, int Ns,
-    int NB, int causal, float* __restrict__ bm) {
+    const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp,
+    const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat, float scale, int N,
+    int Npad, int Ns, int NB, int causal, float* __restrict__ bm) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kQueriesPerBlock;
@@ -124,29 +131,33 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
   const bf16_t* sh = samp + static_cast<size_t>(h) * (Npad / kSampleStride) * DP;
   float* bmh = bm + static_cast<size_t>(h) * NB * Npad;
 
-  bf16x8 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
+  uint4 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
   load_query_frags<DP>(b0, qh, qw + (l & 31));
   load_query_frags<DP>(b1, qh, qw + 32 + (l & 31));
   const int qa = qw + (l & 31), qb = qw + 32 + (l & 31);
+  const float kinv = __builtin_ldexpf(
+      1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
+  const float fa = score_factor(qstat[static_cast<size_t>(h) * Npad + qa].z, kinv, scale);
+  const float fb = score_factor(qstat[static_cast<size_t>(h) * Npad + qb].z, kinv, scale);
 
   // sample keys t with stride*t <= last query of the block (causal), else all
   int s_end = Ns;
   if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / kSampleStride + 1);
   const int nchunks = (s_end + kKeysPerChunk - 1) / kKeysPerChunk;
-  ChunkRegs<DP> regs;
-  regs.load(sh, 0);
-  regs.store(lds);
+  u32x4 regs[Stage<DP>::kPerThread];
+  chunk_load<DP>(regs, sh, 0);
+  chunk_store<DP>(regs, lds);
   __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
     const bool more = ch + 1 < nchunks;
-    if (more) regs.load(sh, (ch + 1) * kKeysPerChunk);
+    if (more) chunk_load<DP>(regs, sh, (ch + 1) * kKeysPerChunk);
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
 #pragma unroll 1
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       const int tbase = ch * kKeysPerChunk + tt * 32;
       if (tbase >= s_end) break;
-      f32x16 a0 = tile_scores<DP>(buf, tt, b0);
-      f32x16 a1 = tile_scores<DP>(buf, tt, b1);
+      f32x16 a0 = tile_scores<DP, F>(buf, tt, b0);
+      f32x16 a1 = tile_scores<DP, F>(buf, tt, b1);
       float m0 = -INFINITY, m1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -159,10 +170,10 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
         m1 = fmaxf(m1, ok1 ? a1[r] : -INFINITY);
       }
       const int tile = tbase / 32;
-      bmh[static_cast<size_t>(2 * tile + half) * Npad + qa] = m0;
-      bmh[static_cast<size_t>(2 * tile + half) * Npad + qb] = m1;
+      bmh[static_cast<size_t>(2 * tile + half) * Npad + qa] = m0 * fa;
+      bmh[static_cast<size_t>(2 * tile + half) * Npad + qb] = m1 * fb;
     }
-    if (more) regs.store(lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
+    if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
   }
 }
@@ -173,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
 // maximum (rounding down only adds candidates).
 __global__ __launch_bounds__(kThreads) void threshold_kernel(
     const float* __restrict__ bm, int N, int Npad, int Ns, int NB, int k, int causal, int capH,
-    float beta, float scale, float* __restrict__ tau) {
+    float beta, float* __restrict__ tau) {
   __shared__ int hist[16 * kThreads];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
@@ -212,7 +223,8 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
     }
   }
   if (active) {
-    if (prefix > order_key(-INFINITY)) result = key_to_float(prefix) * scale;
+    // block maxima are stored as filter scores already (score factor applied)
+    if (prefix > order_key(-INFINITY)) result = key_to_float(prefix);
   }
   tau[static_cast<size_t>(h) * Npad + q] = active ? result : -INFINITY;
 }
@@ -240,55 +252,96 @@ __device__ __forceinline__ unsigned valid_rows(int lim) {
 }
 
 
-template <int DP>
+template <int DP, typename F>
 __global__ __launch_bounds__(kThreads) void filter_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
-    const float2* __restrict__ qstat, const uint32_t* __restrict__ kstat,
+    const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ tau, int N, int Npad, int causal, int capH, float scale,
+    const int* __restrict__ qlist, const int* __restrict__ qlist_count,
     uint2* __restrict__ cand, int* __restrict__ cnt, WsHeader* __restrict__ hdr) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   __shared__ float4 stash_all[8 * kThreads];   // 32 scores per lane, [8][threads]
+  __shared__ int s_kend[kThreads / kWave];
   float4* stash4 = stash_all + threadIdx.x;
   const float* stash = reinterpret_cast<const float*>(stash4);
   const int h = blockIdx.y;
-  const int nqb = Npad / kQueriesPerBlock;
-  // causal rows near the end see the most keys: start with them
-  const int qblk = causal ? (nqb - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
-  const int q0 = qblk * kQueriesPerBlock;
   const int w = threadIdx.x >> 6;
   const int l = lane_id();
   const int half = l >> 5;
-  const int qw = q0 + w * kWaveQueries;
   const size_t hq = static_cast<size_t>(h) * Npad;
+  // Queries of this lane (blocks 0 and 1).  Normally 256 consecutive rows per
+  // workgroup (causal: the longest rows first); in list mode (a retry with a
+  // new threshold) rows listed in qlist for this head.
+  int qq[2];
+  bool live[2];
+  if (qlist == nullptr) {
+    const int nqb = Npad / kQueriesPerBlock;
+    const int qblk = causal ? (nqb - 1 - static_cast<int>(blockIdx.x)) : static_cast<int>(blockIdx.x);
+    const int qw = qblk * kQueriesPerBlock + w * kWaveQueries;
+    qq[0] = qw + (l & 31);
+    qq[1] = qw + 32 + (l & 31);
+    live[0] = qq[0] < N;
+    live[1] = qq[1] < N;
+  } else {
+    const int count = qlist_count[h];
+    const int slot0 = static_cast<int>(blockIdx.x) * kQueriesPerBlock;
+    if (slot0 >= count) return;                 // whole workgroup: nothing listed here
+    const int sa = slot0 + w * kWaveQueries + (l & 31);
+    live[0] = sa < count;
+    live[1] = sa + 32 < count;
+    qq[0] = live[0] ? qlist[hq + sa] : 0;
+    qq[1] = live[1] ? qlist[hq + sa + 32] : 0;
+  }
+  // first live query of the wave (causal diagonal test) and the keys the
+  // workgroup must stream
+  int qmin = min(live[0] ? qq[0] : 0x7FFFFFFF, live[1] ? qq[1] : 0x7FFFFFFF);
+  int qmax = max(live[0] ? qq[0] : -1, live[1] ? qq[1] : -1);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    qmin = min(qmin, __shfl_xor(qmin, o, kWave));
+    qmax = max(qmax, __shfl_xor(qmax, o, kWave));
+  }
+  if (l == 0) s_kend[w] = qmax;
+  __syncthreads();
+  int kend = N;
+  if (causal) {
+    int m = -1;
+#pragma unroll
+    for (int i = 0; i < kThreads / kWave; ++i) m = max(m, s_kend[i]);
+    kend = min(N, m + 1);
+  }
+  const int qw = qmin;
   const bf16_t* qh = q16 + hq * DP;
   const bf16_t* kh = k16 + hq * DP;
-  const float kn = __uint_as_float(kstat[2 * h]);
-  const float kr = __uint_as_float(kstat[2 * h + 1]);
+  const float kn = __uint_as_float(kstat[kKeyStatWords * h]);
+  const float kr = __uint_as_float(kstat[kKeyStatWords * h + 1]);
+  const float kinv =
+      __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
 
-  const int qa = qw + (l & 31), qb = qw + 32 + (l & 31);
-  bf16x8 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
+  const int qa = qq[0], qb = qq[1];
+  uint4 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
   load_query_frags<DP>(b0, qh, qa);
   load_query_frags<DP>(b1, qh, qb);
 
-  // Per-lane threshold on the raw MFMA sum: pairs with s~ >= tau - m pass.
-  // The bound is moved down by a few ulps so that rounding of the scaled
-  // score can never drop such a pair.
+  // Per-lane threshold on the raw MFMA sum: pairs with s~ >= tau - m pass,
+  // where s~ = sum * f and f = score_factor(...) is a power-of-two multiple of
+  // the score scale.  The bound is moved down by a few ulps so that rounding
+  // of the scaled score can never drop such a pair.
   float thr[2];
-  const int qq[2] = {qa, qb};
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int q = qq[bb];
     float t = INFINITY;
-    if (q < N) {
+    if (live[bb]) {
       const float tq = tau[hq + q];
       if (tq == -INFINITY) {
         t = -FLT_MAX;
       } else {
-        const float2 st = qstat[hq + q];
-        const float m = score_margin(st.x, st.y, kn, kr, scale);
+        const float4 st = qstat[hq + q];
+        const float m = score_margin(st.x, st.y, kn, kr, scale, DP);
         float lim = tq - m;
         lim -= fabsf(lim) * (1.0f / 1048576.0f) + 1e-30f;
-        t = lim / scale;
+        t = lim / score_factor(st.z, kinv, scale);
         t -= fabsf(t) * (1.0f / 1048576.0f) + 1e-30f;
       }
     }
@@ -300,28 +353,27 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   unsigned count[2] = {0u, 0u};
   const unsigned last = static_cast<unsigned>(capH - 1);
 
-  const int kend = causal ? min(N, q0 + kQueriesPerBlock) : N;
   const int nchunks = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
-  ChunkRegs<DP> regs;
-  regs.load(kh, 0);
-  regs.store(lds);
+  u32x4 regs[Stage<DP>::kPerThread];
+  chunk_load<DP>(regs, kh, 0);
+  chunk_store<DP>(regs, lds);
   __syncthreads();
   for (int ch = 0; ch < nchunks; ++ch) {
     const bool more = ch + 1 < nchunks;
-    if (more) regs.load(kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
+    if (more) chunk_load<DP>(regs, kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
     const int ntiles = min(kKeysPerChunk / 32, (kend - ch * kKeysPerChunk + 31) / 32);
     // accumulators of two tiles: the next tile's MFMAs run while this tile's
     // scores are filtered (past the last tile they read stale LDS, unused)
     f32x16 acc[2][2];
-    acc[0][0] = tile_scores<DP>(buf, 0, b0);
-    acc[0][1] = tile_scores<DP>(buf, 0, b1);
+    acc[0][0] = tile_scores<DP, F>(buf, 0, b0);
+    acc[0][1] = tile_scores<DP, F>(buf, 0, b1);
 #pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       if (tt >= ntiles) break;
       if (tt + 1 < kKeysPerChunk / 32) {
-        acc[(tt + 1) & 1][0] = tile_scores<DP>(buf, tt + 1, b0);
-        acc[(tt + 1) & 1][1] = tile_scores<DP>(buf, tt + 1, b1);
+        acc[(tt + 1) & 1][0] = tile_scores<DP, F>(buf, tt + 1, b0);
+        acc[(tt + 1) & 1][1] = tile_scores<DP, F>(buf, tt + 1, b1);
       }
       const int tbase = ch * kKeysPerChunk + tt * 32;
       const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
@@ -362,66 +414,83 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
         } while (bits);
       }
     }
-    if (more) regs.store(lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
+    if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
   }
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    if (qq[bb] < N) cnt[(hq + qq[bb]) * 2 + half] = static_cast<int>(count[bb]);
+    if (live[bb]) cnt[(hq + qq[bb]) * 2 + half] = static_cast<int>(count[bb]);
   }
   int mine = 0;
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) mine += (qq[bb] < N) ? static_cast<int>(min(count[bb], last + 1)) : 0;
+  for (int bb = 0; bb < 2; ++bb) mine += live[bb] ? static_cast<int>(min(count[bb], last + 1)) : 0;
   const int tot = wave_sum_i(mine);
   if (l == 0 && tot) atomicAdd(&hdr->candidates, static_cast<unsigned long long>(tot));
 }
 
-template <int DP>
-hipError_t sample_t(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
+template <int DP, typename F>
+hipError_t sample_t(const Plan& p, const Bufs& b, int nh, float scale, hipStream_t s) {
   const dim3 grid(p.Npad / kQueriesPerBlock, nh);
-  hipLaunchKernelGGL((sample_maxima_kernel<DP>), grid, dim3(kThreads), 0, s, b.qlo16, b.ksamp,
-                     p.N, p.Npad, p.Ns, p.NB, p.causal, b.bm);
+  hipLaunchKernelGGL((sample_maxima_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.ksamp,
+                     b.qstat, b.kstat, scale, p.N, p.Npad, p.Ns, p.NB, p.causal, b.bm);
   return hipGetLastError();
 }
 
-template <int DP>
-hipError_t filter_t(const Plan& p, const Bufs& b, int nh, float scale, hipStream_t s) {
+template <int DP, typename F>
+hipError_t filter_t(const Plan& p, const Bufs& b, int nh, float scale, bool retry,
+                    hipStream_t s) {
   const dim3 grid(p.Npad / kQueriesPerBlock, nh);
-  hipLaunchKernelGGL((filter_kernel<DP>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16, b.qstat,
-                     b.kstat, b.tau, p.N, p.Npad, p.causal, p.capH, scale, b.cand, b.cnt,
-                     b.hdr);
+  hipLaunchKernelGGL((filter_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
+                     b.qstat, b.kstat, b.tau, p.N, p.Npad, p.causal, p.capH, scale,
+                     retry ? b.rlist : static_cast<int*>(nullptr),
+                     retry ? b.rcount : static_cast<int*>(nullptr), b.cand, b.cnt, b.hdr);
   return hipGetLastError();
+}
+
+template <typename F>
+hipError_t sample_f(const Plan& p, const Bufs& b, int nh, float scale, hipStream_t s) {
+  switch (p.dp) {
+    case 16: return sample_t<16, F>(p, b, nh, scale, s);
+    case 32: return sample_t<32, F>(p, b, nh, scale, s);
+    case 64: return sample_t<64, F>(p, b, nh, scale, s);
+    case 128: return sample_t<128, F>(p, b, nh, scale, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename F>
+hipError_t filter_f(const Plan& p, const Bufs& b, int nh, float scale, bool retry,
+                    hipStream_t s) {
+  switch (p.dp) {
+    case 16: return filter_t<16, F>(p, b, nh, scale, retry, s);
+    case 32: return filter_t<32, F>(p, b, nh, scale, retry, s);
+    case 64: return filter_t<64, F>(p, b, nh, scale, retry, s);
+    case 128: return filter_t<128, F>(p, b, nh, scale, retry, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
-  switch (p.dp) {
-    case 16: return sample_t<16>(p, b, nh, s);
-    case 32: return sample_t<32>(p, b, nh, s);
-    case 64: return sample_t<64>(p, b, nh, s);
-    case 128: return sample_t<128>(p, b, nh, s);
-  }
-  return hipErrorInvalidValue;
+hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, float score_scale,
+                                hipStream_t s) {
+  return p.filt ? sample_f<FiltBf16>(p, b, nh, score_scale, s)
+                : sample_f<FiltF16>(p, b, nh, score_scale, s);
 }
 
 hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_scale,
                             hipStream_t s) {
   const dim3 grid(p.Npad / kThreads, nh);
+  (void)score_scale;
   hipLaunchKernelGGL(threshold_kernel, grid, dim3(kThreads), 0, s, b.bm, p.N, p.Npad, p.Ns,
-                     p.NB, p.k, p.causal, p.capH, kTauBeta, score_scale, b.tau);
+                     p.NB, p.k, p.causal, p.capH, kTauBeta, b.tau);
   return hipGetLastError();
 }
 
-hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale,
+hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale, bool retry,
                          hipStream_t s) {
-  switch (p.dp) {
-    case 16: return filter_t<16>(p, b, nh, score_scale, s);
-    case 32: return filter_t<32>(p, b, nh, score_scale, s);
-    case 64: return filter_t<64>(p, b, nh, score_scale, s);
-    case 128: return filter_t<128>(p, b, nh, score_scale, s);
-  }
-  return hipErrorInvalidValue;
+  return p.filt ? filter_f<FiltBf16>(p, b, nh, score_scale, retry, s)
+                : filter_f<FiltF16>(p, b, nh, score_scale, retry, s);
 }
 
 }  // namespace sa

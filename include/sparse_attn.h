@@ -46,7 +46,7 @@ extern "C" {
 
 #define SA_K_MAX 2048
 
-typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+typedef enum { SA_F32 = 0, SA_BF16 = 1, SA_F16 = 2 } sa_dtype;  /* SA_F16: filter only */
 
 typedef enum {
   SA_OK = 0,
@@ -147,6 +147,20 @@ int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const 
                             void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Operand type of the 16-bit MFMA filter inside sparse_attn_scores_topk and
+ * sparse_attn_fwd: SA_F16 (default) or SA_BF16.  Rows are scaled by powers
+ * of two before rounding (one exponent per query row, one per key head), so
+ * either type covers the fp32 range.  The returned indices are the same for
+ * both: the filter only discards keys that provably cannot be in the top-k,
+ * and the final choice uses the exact fp32 score.  fp16 keeps 11 significant
+ * bits instead of 8, which shrinks the band of keys that must be re-scored
+ * exactly.  Process-wide; affects calls made after it returns.
+ * Returns SA_OK or SA_ERR_UNSUPPORTED.
+ */
+int sparse_attn_set_filter_dtype(int32_t dtype);
+int sparse_attn_get_filter_dtype(void);
+
+/*
  * Synchronizes `stream`, then reports and clears the sticky device flag:
  * SA_ERR_DEVICE_INDEX if a gather saw an index >= N since the last check,
  * SA_ERR_HIP if synchronization failed, SA_OK otherwise.
@@ -157,9 +171,10 @@ int sparse_attn_check_status(void* stream);
  * Diagnostics of the last sparse_attn_scores_topk / sparse_attn_fwd call
  * that used workspace `ws` (synchronizes `stream`).  Writes up to n values to
  * out: [0] queries resolved by the exact fallback path, [1] queries whose
- * candidate buffer overflowed, [2] total candidates written, [3] total keys
- * re-scored exactly, [4] queries processed, summed over all head chunks of
- * the call.  Returns the number of values written or a negative status.
+ * first candidate list overflowed, [2] total candidates written, [3] total
+ * keys re-scored exactly, [4] queries resolved, [5] queries filtered a second
+ * time with a proven threshold, summed over all head chunks of the call.
+ * Returns the number of values written or a negative status.
  */
 int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, int32_t n,
                                 void* stream);

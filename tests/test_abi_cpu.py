@@ -47,6 +47,14 @@ D = sa.sa_dims
 A = 0x100000  # a 16-byte-aligned fake address: never dereferenced in these tests
 
 
+def test_filter_dtype_option(lib):
+    assert lib.sparse_attn_get_filter_dtype() == 2          # fp16 by default
+    assert lib.sparse_attn_set_filter_dtype(0) == -3        # fp32 is not a filter type
+    assert lib.sparse_attn_set_filter_dtype(1) == 0
+    assert lib.sparse_attn_get_filter_dtype() == 1
+    assert lib.sparse_attn_set_filter_dtype(2) == 0
+
+
 def test_status_strings(lib):
     for code in range(0, -8, -1):
         assert lib.sparse_attn_status_string(code)

@@ -57,6 +57,10 @@ def run_case(w: W.Workload, seed=0, rows=None, check_all=True):
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2), "fused and split paths disagree"
     stats = sa.sparse_attn_workspace_stats(ws)
+    # the exact fallback keeps results right even when the filter is broken,
+    # so a flood of fallbacks must fail the test on its own
+    if w.N >= 4096:
+        assert stats["fallback_queries"] <= 0.05 * w.queries, stats
     idx_np = _rows_np(idx)
     if rows is None:
         ranges = [(0, N)]
@@ -170,6 +174,16 @@ def test_tiny_fp32_workload_all_rows():
     run_case(W.get("tiny_fp32"))
 
 
+@pytest.fixture(params=[torch.float16, torch.bfloat16], ids=["filter_f16", "filter_bf16"])
+def filter_dtype(request):
+    """Runs a test with each 16-bit operand type of the MFMA filter; the
+    indices must not depend on it."""
+    before = sa.sparse_attn_get_filter_dtype()
+    sa.sparse_attn_set_filter_dtype(request.param)
+    yield request.param
+    sa.sparse_attn_set_filter_dtype(before)
+
+
 @pytest.mark.parametrize("N,k,dp,D,dtype,causal", [
     (5000, 64, 16, 64, "f32", False),       # sample + filter path, ragged tail
     (5000, 64, 64, 128, "bf16", False),
@@ -179,17 +193,17 @@ def test_tiny_fp32_workload_all_rows():
     (600, 700, 16, 64, "f32", False),       # k > N: all keys, -1 padding
     (1, 5, 16, 64, "f32", True),            # a single query
 ])
-def test_topk_and_forward_small_shapes_all_rows(N, k, dp, D, dtype, causal):
+def test_topk_and_forward_small_shapes_all_rows(N, k, dp, D, dtype, causal, filter_dtype):
     w = W.Workload("case", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
     run_case(w, seed=N + k)
 
 
-def test_mixture_causal_small_all_rows():
+def test_mixture_causal_small_all_rows(filter_dtype):
     w = W.get("causal_mixture", B=2, H=2, N=6000, k=64)
     run_case(w, seed=5)
 
 
-def test_exact_ties_go_to_lower_index():
+def test_exact_ties_go_to_lower_index(filter_dtype):
     """Duplicated key rows give bit-identical scores; the lower index wins."""
     w = W.Workload("ties", 1, 1, 3000, 64, "f32", d_proj=16, k=40)
     x = W.make_inputs(w, 9)
@@ -237,3 +251,17 @@ def test_full_size_workloads_sampled_rows(name):
     print(name, stats)
     assert stats["queries"] == w.queries
     assert stats["fallback_queries"] <= 0.01 * w.queries
+
+
+def test_filter_dtype_does_not_change_indices():
+    w = W.get("bf16_32k", N=6000, H=2, k=96)
+    g = _cuda(W.make_inputs(w, 11))
+    before = sa.sparse_attn_get_filter_dtype()
+    try:
+        sa.sparse_attn_set_filter_dtype(torch.float16)
+        a = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k)
+        sa.sparse_attn_set_filter_dtype(torch.bfloat16)
+        b = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k)
+    finally:
+        sa.sparse_attn_set_filter_dtype(before)
+    assert torch.equal(a, b)
