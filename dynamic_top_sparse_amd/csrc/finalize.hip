@@ -217,208 +217,216 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
 
   const int h = blockIdx.y;
   const size_t hq = static_cast<size_t>(h) * Npad;
+  // Statistics are kept per wave and added to the header once at the end:
+  // one device-scope atomic per query on a shared word would serialise.
+  unsigned long long st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
   // first pass: every query; retry pass: the queries listed for this head
-  int q = blockIdx.x * wpb + w;
-  if (qlist != nullptr) {
-    if (q >= qlist_count[h]) return;
-    q = qlist[hq + q];
-  } else if (q >= N) {
-    return;
-  }
-  int32_t* out = idx + (static_cast<size_t>(h) * N + q) * k;
-  const int n_valid = causal ? q + 1 : N;
-  const int k_i = min(k, n_valid);
-  // Unresolved query: on the first pass, if a proven threshold is known
-  // (k keys certainly score at least tau_new), filter it again with that
-  // threshold; otherwise resolve it with the exact fallback.
-  auto unresolved = [&](float tau_new) {
-    if (l == 0) {
+  const int nq = qlist != nullptr ? qlist_count[h] : N;
+#pragma unroll 1
+  for (int slot = blockIdx.x * wpb + w; slot < nq; slot += gridDim.x * wpb) {
+    wave_sync();  // the previous query's LDS reads are done
+    const int q = qlist != nullptr ? qlist[hq + slot] : slot;
+    int32_t* out = idx + (static_cast<size_t>(h) * N + q) * k;
+    const int n_valid = causal ? q + 1 : N;
+    const int k_i = min(k, n_valid);
+    // Unresolved query: on the first pass, if a proven threshold is known
+    // (k keys certainly score at least tau_new), filter it again with that
+    // threshold; otherwise resolve it with the exact fallback.
+    auto unresolved = [&](float tau_new) {
       if (qlist == nullptr && tau_new == tau_new) {
-        tau[hq + q] = tau_new;
-        rlist[hq + atomicAdd(&rcount[h], 1)] = q;
-        atomicAdd(&hdr->retried, 1ull);
+        if (l == 0) {
+          tau[hq + q] = tau_new;
+          rlist[hq + atomicAdd(&rcount[h], 1)] = q;
+        }
+        ++st_retried;
       } else {
-        const unsigned slot = atomicAdd(&hdr->fb_count, 1u);
-        fblist[slot] = static_cast<int>(hq + q);
-        atomicAdd(&hdr->queries, 1ull);
+        if (l == 0) {
+          const unsigned fslot = atomicAdd(&hdr->fb_count, 1u);
+          fblist[fslot] = static_cast<int>(hq + q);
+        }
+        ++st_queries;
       }
-    }
-  };
+    };
 
-  if (n_valid <= k) {  // every valid key is kept
-    for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
-    if (l == 0) atomicAdd(&hdr->queries, 1ull);
-    return;
-  }
-  // an overflowing list still holds capH genuine candidates per half
-  const int r0 = cnt[(hq + q) * 2], r1 = cnt[(hq + q) * 2 + 1];
-  const bool overflow = r0 > capH || r1 > capH;
-  const int c0 = min(r0, capH), c1 = min(r1, capH);
-  const int c = c0 + c1;
-  const float tq = tau[hq + q];
-  if (overflow && l == 0 && qlist == nullptr) atomicAdd(&hdr->overflow_queries, 1ull);
-  if (c < k_i + (overflow ? 0 : 1)) {  // too few keys for a proven bound
-    unresolved(__builtin_nanf(""));
-    return;
-  }
-  // Stage the candidates in LDS once (index i runs over half 0, then half 1)
-  // as (order key of the filter score s~ = sum * f, key index).
-  const float4 st = qstat[hq + q];
-  const float kinv =
-      __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
-  const float f = scale * st.z * kinv;
-  {
-    const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
-    const uint2* list1 = list0 + capH;
-#pragma unroll 8
-    for (int i = l; i < c; i += kWave) {
-      const uint2 e = i < c0 ? list0[i] : list1[i - c0];
-      ck[i] = order_key(__uint_as_float(e.y) * f);
-      cj[i] = static_cast<int>(e.x);
+    if (n_valid <= k) {  // every valid key is kept
+      for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
+      ++st_queries;
+      continue;
     }
-  }
-  wave_sync();
-  auto each_cand = [&](auto fn) {
-#pragma unroll 1
-    for (int i0 = 0; i0 < c; i0 += kWave) {
-      const int i = i0 + l;
-      const bool ok = i < c;
-      fn(ok ? ck[i] : 0u, ok);
+    // an overflowing list still holds capH genuine candidates per half
+    const int r0 = cnt[(hq + q) * 2], r1 = cnt[(hq + q) * 2 + 1];
+    const bool overflow = r0 > capH || r1 > capH;
+    const int c0 = min(r0, capH), c1 = min(r1, capH);
+    const int c = c0 + c1;
+    const float tq = tau[hq + q];
+    if (overflow && qlist == nullptr) ++st_overflow;
+    if (c < k_i + (overflow ? 0 : 1)) {  // too few keys for a proven bound
+      unresolved(__builtin_nanf(""));
+      continue;
     }
-  };
-  // The k-th largest filter score gives lo = (k-th) - m, a proven threshold
-  // for any subset of the keys: k of them score >= lo.
-  const float m = score_margin(st.x, st.y, __uint_as_float(kstat[kKeyStatWords * h]),
-                               __uint_as_float(kstat[kKeyStatWords * h + 1]), scale, DP);
-  auto lower = [&](float x) { return (x - m) - (fabsf(x) + m) * (1.0f / 4194304.0f); };
-  auto upper = [&](float x) { return (x + m) + (fabsf(x) + m) * (1.0f / 4194304.0f); };
-  const uint32_t ak = wave_select<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf), each_cand);
-  const float lo = lower(key_to_float(ak));
-  // The list covers every key that can reach the top-k only if the filter's
-  // threshold is proven, i.e. the k best candidates are certainly above it.
-  if (overflow || !(lo >= tq)) {
-    unresolved(lo);
-    return;
-  }
-  // the (k+1)-th largest: equal to the k-th if that value repeats, else the
-  // largest value below it
-  int n_ge = 0;
-  uint32_t below = 0;
-  each_cand([&](uint32_t key, bool ok) {
-    if (ok) {
-      n_ge += key >= ak ? 1 : 0;
-      if (key < ak) below = max(below, key);
-    }
-  });
-  n_ge = wave_sum_i(n_ge);
-  below = wave_max_u32(below);
-  const uint32_t bk = n_ge > k_i ? ak : below;
-  const float hi = fmaxf(tq, upper(key_to_float(bk)));
-  // Certainly kept: l > hi; certainly out: u < lo.  Both tests are monotone in
-  // the filter score, so they become key thresholds: kept iff ck > in_key,
-  // out iff ck < out_key (keys between are uncertain).
-  auto cls_of = [&](uint32_t key) {
-    const float x = key_to_float(key);
-    return lower(x) > hi ? 1 : (upper(x) < lo ? 0 : 2);
-  };
-
-  // list the uncertain keys
-  int n_in = 0, nU = 0;
-#pragma unroll 1
-  for (int i0 = 0; i0 < c; i0 += kWave) {
-    const int i = i0 + l;
-    const int cc = i < c ? cls_of(ck[i]) : 0;
-    n_in += cc == 1 ? 1 : 0;
-    const unsigned long long mk = __ballot(cc == 2);
-    if (cc == 2) {
-      const int pos = nU + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                               static_cast<uint32_t>(mk >> 32),
-                               __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
-      if (pos < ucap) uj[pos] = cj[i];
-    }
-    nU += __builtin_popcountll(mk);
-  }
-  n_in = wave_sum_i(n_in);
-  const int need = k_i - n_in;
-  if (nU > ucap || need > nU) {
-    unresolved(__builtin_nanf(""));
-    return;
-  }
-  wave_sync();
-  // exact re-score of the uncertain keys: G lanes per key, 16 bytes each
-  {
-    constexpr int G = DP / 4;
-    constexpr int KPI = kWave / G;     // keys per pass
-    constexpr int UNR = 4;             // passes in flight
-    const int g = l % G, grp = l / G;
-    const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
-#pragma unroll 1
-    for (int u0 = 0; u0 < nU; u0 += KPI * UNR) {
-      float4 kv[UNR];
-#pragma unroll
-      for (int t = 0; t < UNR; ++t) {
-        const int u = u0 + t * KPI + grp;
-        kv[t] = u < nU ? reinterpret_cast<const float4*>(k32 + (hq + uj[u]) * DP)[g]
-                       : make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-#pragma unroll
-      for (int t = 0; t < UNR; ++t) {
-        float p = group_partial<DP>(qv, kv[t]);
-#pragma unroll
-        for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
-        const int u = u0 + t * KPI + grp;
-        if (g == 0 && u < nU) us[u] = p * scale;
+    // Stage the candidates in LDS once (index i runs over half 0, then half 1)
+    // as (order key of the filter score s~ = sum * f, key index).
+    const float4 st = qstat[hq + q];
+    const float kinv =
+        __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
+    const float f = scale * st.z * kinv;
+    {
+      const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
+      const uint2* list1 = list0 + capH;
+  #pragma unroll 8
+      for (int i = l; i < c; i += kWave) {
+        const uint2 e = i < c0 ? list0[i] : list1[i - c0];
+        ck[i] = order_key(__uint_as_float(e.y) * f);
+        cj[i] = static_cast<int>(e.x);
       }
     }
-  }
-  wave_sync();
-  unsigned long long kth = ~0ull;
-  if (need > 0) {
-    kth = wave_select<unsigned long long>(need, hist, cbuf, [&](auto fn) {
-#pragma unroll 1
-      for (int u0 = 0; u0 < nU; u0 += kWave) {
-        const int u = u0 + l;
-        fn(u < nU ? rank_key(us[u], uj[u]) : 0ull, u < nU);
+    wave_sync();
+    auto each_cand = [&](auto fn) {
+  #pragma unroll 1
+      for (int i0 = 0; i0 < c; i0 += kWave) {
+        const int i = i0 + l;
+        const bool ok = i < c;
+        fn(ok ? ck[i] : 0u, ok);
+      }
+    };
+    // The k-th largest filter score gives lo = (k-th) - m, a proven threshold
+    // for any subset of the keys: k of them score >= lo.
+    const float m = score_margin(st.x, st.y, __uint_as_float(kstat[kKeyStatWords * h]),
+                                 __uint_as_float(kstat[kKeyStatWords * h + 1]), scale, DP);
+    auto lower = [&](float x) { return (x - m) - (fabsf(x) + m) * (1.0f / 4194304.0f); };
+    auto upper = [&](float x) { return (x + m) + (fabsf(x) + m) * (1.0f / 4194304.0f); };
+    const uint32_t ak = wave_select<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf), each_cand);
+    const float lo = lower(key_to_float(ak));
+    // The list covers every key that can reach the top-k only if the filter's
+    // threshold is proven, i.e. the k best candidates are certainly above it.
+    if (overflow || !(lo >= tq)) {
+      unresolved(lo);
+      continue;
+    }
+    // the (k+1)-th largest: equal to the k-th if that value repeats, else the
+    // largest value below it
+    int n_ge = 0;
+    uint32_t below = 0;
+    each_cand([&](uint32_t key, bool ok) {
+      if (ok) {
+        n_ge += key >= ak ? 1 : 0;
+        if (key < ak) below = max(below, key);
       }
     });
-  }
-  // Compact the kept keys in list order (each half ascending) in place into
-  // cj: a chunk's reads all happen before its writes, and writes never pass
-  // the chunk.  The uncertain keys are met in the order they were listed.
-  int run = 0, n0 = 0, ucount = 0;
-#pragma unroll 1
-  for (int i0 = 0; i0 < c; i0 += kWave) {
-    const int i = i0 + l;
-    const int cc = i < c ? cls_of(ck[i]) : 0;
-    const int key = i < c ? cj[i] : 0;
-    const unsigned long long mk = __ballot(cc == 2);
-    bool take = cc == 1;
-    if (cc == 2) {
-      const int pos = ucount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                   static_cast<uint32_t>(mk >> 32),
-                                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
-      take = need > 0 && rank_key(us[pos], uj[pos]) >= kth;
+    n_ge = wave_sum_i(n_ge);
+    below = wave_max_u32(below);
+    const uint32_t bk = n_ge > k_i ? ak : below;
+    const float hi = fmaxf(tq, upper(key_to_float(bk)));
+    // Certainly kept: l > hi; certainly out: u < lo.  Both tests are monotone in
+    // the filter score, so they become key thresholds: kept iff ck > in_key,
+    // out iff ck < out_key (keys between are uncertain).
+    auto cls_of = [&](uint32_t key) {
+      const float x = key_to_float(key);
+      return lower(x) > hi ? 1 : (upper(x) < lo ? 0 : 2);
+    };
+
+    // list the uncertain keys
+    int n_in = 0, nU = 0;
+  #pragma unroll 1
+    for (int i0 = 0; i0 < c; i0 += kWave) {
+      const int i = i0 + l;
+      const int cc = i < c ? cls_of(ck[i]) : 0;
+      n_in += cc == 1 ? 1 : 0;
+      const unsigned long long mk = __ballot(cc == 2);
+      if (cc == 2) {
+        const int pos = nU + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                 static_cast<uint32_t>(mk >> 32),
+                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
+        if (pos < ucap) uj[pos] = cj[i];
+      }
+      nU += __builtin_popcountll(mk);
     }
-    ucount += __builtin_popcountll(mk);
-    const unsigned long long tk = __ballot(take);
+    n_in = wave_sum_i(n_in);
+    const int need = k_i - n_in;
+    if (nU > ucap || need > nU) {
+      unresolved(__builtin_nanf(""));
+      continue;
+    }
     wave_sync();
-    if (take)
-      cj[run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                   static_cast<uint32_t>(tk >> 32),
-                   __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tk), 0)))] = key;
-    run += __builtin_popcountll(tk);
-    n0 += __builtin_popcountll(__ballot(take && i < c0));
+    // exact re-score of the uncertain keys: G lanes per key, 16 bytes each
+    {
+      constexpr int G = DP / 4;
+      constexpr int KPI = kWave / G;     // keys per pass
+      constexpr int UNR = 4;             // passes in flight
+      const int g = l % G, grp = l / G;
+      const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
+  #pragma unroll 1
+      for (int u0 = 0; u0 < nU; u0 += KPI * UNR) {
+        float4 kv[UNR];
+  #pragma unroll
+        for (int t = 0; t < UNR; ++t) {
+          const int u = u0 + t * KPI + grp;
+          kv[t] = u < nU ? reinterpret_cast<const float4*>(k32 + (hq + uj[u]) * DP)[g]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+  #pragma unroll
+        for (int t = 0; t < UNR; ++t) {
+          float p = group_partial<DP>(qv, kv[t]);
+  #pragma unroll
+          for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
+          const int u = u0 + t * KPI + grp;
+          if (g == 0 && u < nU) us[u] = p * scale;
+        }
+      }
+    }
     wave_sync();
+    unsigned long long kth = ~0ull;
+    if (need > 0) {
+      kth = wave_select<unsigned long long>(need, hist, cbuf, [&](auto fn) {
+  #pragma unroll 1
+        for (int u0 = 0; u0 < nU; u0 += kWave) {
+          const int u = u0 + l;
+          fn(u < nU ? rank_key(us[u], uj[u]) : 0ull, u < nU);
+        }
+      });
+    }
+    // Compact the kept keys in list order (each half ascending) in place into
+    // cj: a chunk's reads all happen before its writes, and writes never pass
+    // the chunk.  The uncertain keys are met in the order they were listed.
+    int run = 0, n0 = 0, ucount = 0;
+  #pragma unroll 1
+    for (int i0 = 0; i0 < c; i0 += kWave) {
+      const int i = i0 + l;
+      const int cc = i < c ? cls_of(ck[i]) : 0;
+      const int key = i < c ? cj[i] : 0;
+      const unsigned long long mk = __ballot(cc == 2);
+      bool take = cc == 1;
+      if (cc == 2) {
+        const int pos = ucount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                                     static_cast<uint32_t>(mk >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
+        take = need > 0 && rank_key(us[pos], uj[pos]) >= kth;
+      }
+      ucount += __builtin_popcountll(mk);
+      const unsigned long long tk = __ballot(take);
+      wave_sync();
+      if (take)
+        cj[run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+                     static_cast<uint32_t>(tk >> 32),
+                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tk), 0)))] = key;
+      run += __builtin_popcountll(tk);
+      n0 += __builtin_popcountll(__ballot(take && i < c0));
+      wave_sync();
+    }
+    const int* sel = cj;
+    const int n1 = run - n0;
+    for (int p2 = l; p2 < n0; p2 += kWave) out[p2 + lower_bound(sel + n0, n1, sel[p2])] = sel[p2];
+    for (int p2 = l; p2 < n1; p2 += kWave)
+      out[p2 + lower_bound(sel, n0, sel[n0 + p2])] = sel[n0 + p2];
+    for (int t = run + l; t < k; t += kWave) out[t] = -1;
+    st_rescored += static_cast<unsigned long long>(nU);
+    ++st_queries;
   }
-  const int* sel = cj;
-  const int n1 = run - n0;
-  for (int p2 = l; p2 < n0; p2 += kWave) out[p2 + lower_bound(sel + n0, n1, sel[p2])] = sel[p2];
-  for (int p2 = l; p2 < n1; p2 += kWave)
-    out[p2 + lower_bound(sel, n0, sel[n0 + p2])] = sel[n0 + p2];
-  for (int t = run + l; t < k; t += kWave) out[t] = -1;
   if (l == 0) {
-    atomicAdd(&hdr->rescored, static_cast<unsigned long long>(nU));
-    atomicAdd(&hdr->queries, 1ull);
+    if (st_queries) atomicAdd(&hdr->queries, st_queries);
+    if (st_rescored) atomicAdd(&hdr->rescored, st_rescored);
+    if (st_overflow) atomicAdd(&hdr->overflow_queries, st_overflow);
+    if (st_retried) atomicAdd(&hdr->retried, st_retried);
   }
 }
 
@@ -529,7 +537,12 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   const size_t per_wave = rerank_lds_per_wave(2 * p.capH, ucap);
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
-  const dim3 grid((p.N + wpb - 1) / wpb, nh);
+  // persistent waves: about 2048 workgroups over the chunk, each wave
+  // striding over the queries of its head
+  int gx = (p.N + wpb - 1) / wpb;
+  const int per_head = (2048 + nh - 1) / nh;
+  gx = gx < per_head ? gx : per_head;
+  const dim3 grid(gx, nh);
   const size_t lds = static_cast<size_t>(wpb) * per_wave;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finalize_kernel<DP>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
