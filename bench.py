@@ -89,6 +89,9 @@ def main() -> int:
     ap.add_argument("--filter-dtype", choices=("f16", "bf16"), default="f16",
                     help="16-bit operand type of the MFMA filter (indices do not depend on it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB: the known-size "
+                         "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -130,6 +133,13 @@ def main() -> int:
     recs = sa.sparse_attn_profile_read()
     sa.sparse_attn_profile_enable(False)
     stats = sa.sparse_attn_workspace_stats(ws)
+    if args.copy_probe_mib > 0:
+        src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     ms_step = (t1 - t0) * 1e3 / args.steps
     a = algorithmic(w)

@@ -137,12 +137,23 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.BH = B * H;
   p.hc = heads_per_chunk < 1 ? 1 : (heads_per_chunk > p.BH ? p.BH : heads_per_chunk);
   p.Npad = round_up(N, kRowPad);
-  p.Ns = (N + kSampleStride - 1) / kSampleStride;
-  p.Nspad = p.Npad / kSampleStride;
-  p.NB = 2 * ((p.Ns + 31) / 32);
+  // sample stride: the largest power of two <= beta*k/32 (in [1, 16]), so
+  // that the sample rank stays near 48 and the threshold stays steady
+  p.sstride = 1;
+  while (p.sstride < kMaxSampleStride && 2 * p.sstride * 32 <= kTauBeta * k) p.sstride *= 2;
+  p.Ns = (N + p.sstride - 1) / p.sstride;
+  p.Nspad = p.Npad / p.sstride;
   // two query halves of capH candidates each (1.5 k, at least 256, at most
   // 2048); a list that overflows is filtered again with a proven threshold
   p.capH = std::min(2048, round_up(std::max(3 * k / 2, 256), 64));
+  // block maxima per query: fewer than 8r + 40 (the block size keeps under
+  // 8r blocks, plus tile rounding), with r <= beta*k/s + beta*k/n + 1 for the
+  // rows that use a threshold (n > 2 capH - 64 valid keys)
+  {
+    const int rmax = static_cast<int>(kTauBeta * k / p.sstride +
+                                      kTauBeta * k / std::max(1, 2 * p.capH - 64)) + 2;
+    p.NB = 8 * rmax + 40;
+  }
   p.with_idx = with_idx ? 1 : 0;
   const size_t hc = static_cast<size_t>(p.hc);
   const size_t Np = static_cast<size_t>(p.Npad);
@@ -164,8 +175,10 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.off_kstat = take(hc * kKeyStatWords * 4);
   p.off_bm = take(hc * static_cast<size_t>(p.NB) * Np * 4);
   p.off_tau = take(hc * Np * 4);
+  p.off_thr = take(hc * Np * 4);
   p.off_cand = take(hc * Np * 2 * static_cast<size_t>(p.capH) * 8);
   p.off_cnt = take(hc * Np * 2 * 4);
+  p.off_rcnt = take(hc * Np * 2 * kRetrySplit * 4);
   p.off_rlist = take(hc * Np * 4);
   p.off_rcount = take(hc * 4);
   p.off_fblist = take(hc * Np * 4);
@@ -188,8 +201,10 @@ Bufs bufs_of(const Plan& p, void* ws) {
   b.kstat = reinterpret_cast<uint32_t*>(base + p.off_kstat);
   b.bm = reinterpret_cast<float*>(base + p.off_bm);
   b.tau = reinterpret_cast<float*>(base + p.off_tau);
+  b.thr = reinterpret_cast<float*>(base + p.off_thr);
   b.cand = reinterpret_cast<uint2*>(base + p.off_cand);
   b.cnt = reinterpret_cast<int*>(base + p.off_cnt);
+  b.rcnt = reinterpret_cast<int*>(base + p.off_rcnt);
   b.rlist = reinterpret_cast<int*>(base + p.off_rlist);
   b.rcount = reinterpret_cast<int*>(base + p.off_rcount);
   b.fblist = reinterpret_cast<int*>(base + p.off_fblist);

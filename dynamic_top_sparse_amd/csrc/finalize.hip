@@ -22,6 +22,7 @@
 // again with it.  Only what remains unresolved after that second round goes
 // to the exact fallback.
 #include <float.h>
+#include <limits.h>
 
 #include "sa_internal.h"
 
@@ -86,17 +87,8 @@ __device__ __forceinline__ int key_bits(KeyT span) {
 // ranked directly.  Buckets spread keys that share their leading bits, so the
 // LDS histogram sees few colliding atomics.  Requires 1 <= K <= #valid keys.
 template <typename KeyT, typename Each>
-__device__ KeyT wave_select(int K, int* hist, KeyT* cbuf, Each each) {
+__device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo, KeyT hi) {
   const int l = lane_id();
-  KeyT lo = ~static_cast<KeyT>(0), hi = 0;
-  each([&](KeyT key, bool ok) {
-    if (ok) {
-      lo = key < lo ? key : lo;
-      hi = key > hi ? key : hi;
-    }
-  });
-  lo = wave_min_k(lo);
-  hi = wave_max_k(hi);
   int in_range = 65;
   while (lo != hi) {
     const KeyT span = hi - lo;
@@ -170,14 +162,55 @@ __device__ KeyT wave_select(int K, int* hist, KeyT* cbuf, Each each) {
   return result;
 }
 
-// First position in the ascending list a[0..n) whose value is >= x.
-__device__ __forceinline__ int lower_bound(const int* a, int n, int x) {
-  int lo = 0, hi = n;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (a[mid] < x) lo = mid + 1; else hi = mid;
+// As wave_select_in, with the key range found first.
+template <typename KeyT, typename Each>
+__device__ KeyT wave_select(int K, int* hist, KeyT* cbuf, Each each) {
+  KeyT lo = ~static_cast<KeyT>(0), hi = 0;
+  each([&](KeyT key, bool ok) {
+    if (ok) {
+      lo = key < lo ? key : lo;
+      hi = key > hi ? key : hi;
+    }
+  });
+  return wave_select_in<KeyT>(K, hist, cbuf, each, wave_min_k(lo), wave_max_k(hi));
+}
+
+__device__ __forceinline__ int lane_rank(unsigned long long mask) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(
+      static_cast<uint32_t>(mask >> 32), __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0)));
+}
+
+// Writes the merge of the ascending, disjoint lists a[0..na) and b[0..nb) to
+// out[0..na+nb): each lane finds where its run of 8 outputs starts with a
+// binary search along the cross diagonal, then merges its run sequentially.
+__device__ __forceinline__ void merge_rows(const int* a, int na, const int* b, int nb,
+                                           int32_t* __restrict__ out) {
+  constexpr int T = 8;
+  const int total = na + nb;
+  for (int start = lane_id() * T; start < total; start += kWave * T) {
+    int lo = max(0, start - nb), hi = min(start, na);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (a[mid] < b[start - mid - 1]) lo = mid + 1; else hi = mid;
+    }
+    int ia = lo, ib = start - lo;
+    int va = ia < na ? a[ia] : INT_MAX, vb = ib < nb ? b[ib] : INT_MAX;
+    const int n = min(T, total - start);
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (t < n) {
+        const bool from_a = va < vb;
+        out[start + t] = from_a ? va : vb;
+        if (from_a) {
+          ++ia;
+          va = ia < na ? a[ia] : INT_MAX;
+        } else {
+          ++ib;
+          vb = ib < nb ? b[ib] : INT_MAX;
+        }
+      }
+    }
   }
-  return lo;
 }
 
 __device__ __forceinline__ unsigned long long rank_key(float s, int j) {
@@ -196,7 +229,9 @@ __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
 
 template <int DP>
 __global__ __launch_bounds__(kThreads) void finalize_kernel(
-    const uint2* __restrict__ cand, const int* __restrict__ cnt, float* __restrict__ tau,
+    const uint2* __restrict__ cand, const int* __restrict__ cnt, const int* __restrict__ rcnt,
+    float* __restrict__ tau,
+    const float* __restrict__ thr,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ q32, const float* __restrict__ k32, int N, int Npad, int k,
     int causal, int capH, int ucap, float scale, int32_t* __restrict__ idx,
@@ -235,7 +270,9 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     auto unresolved = [&](float tau_new) {
       if (qlist == nullptr && tau_new == tau_new) {
         if (l == 0) {
-          tau[hq + q] = tau_new;
+          // lowered by a few ulps: the retry re-derives its filter scores with
+          // another threshold, which may round them differently
+          tau[hq + q] = tau_new - (fabsf(tau_new) * (1.0f / 1048576.0f) + 1e-30f);
           rlist[hq + atomicAdd(&rcount[h], 1)] = q;
         }
         ++st_retried;
@@ -253,36 +290,68 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       ++st_queries;
       continue;
     }
-    // an overflowing list still holds capH genuine candidates per half
-    const int r0 = cnt[(hq + q) * 2], r1 = cnt[(hq + q) * 2 + 1];
+    // One candidate list per query half; the retry pass counted its hits per
+    // key segment.  An overflowing list still holds capH genuine candidates.
+    int r0 = 0, r1 = 0;
+    if (qlist == nullptr) {
+      r0 = cnt[(hq + q) * 2];
+      r1 = cnt[(hq + q) * 2 + 1];
+    } else {
+      for (int s2 = 0; s2 < kRetrySplit; ++s2) {
+        r0 += rcnt[(hq + q) * 2 * kRetrySplit + s2];
+        r1 += rcnt[((hq + q) * 2 + 1) * kRetrySplit + s2];
+      }
+    }
     const bool overflow = r0 > capH || r1 > capH;
     const int c0 = min(r0, capH), c1 = min(r1, capH);
     const int c = c0 + c1;
     const float tq = tau[hq + q];
     if (overflow && qlist == nullptr) ++st_overflow;
-    if (c < k_i + (overflow ? 0 : 1)) {  // too few keys for a proven bound
-      unresolved(__builtin_nanf(""));
-      continue;
-    }
     // Stage the candidates in LDS once (index i runs over half 0, then half 1)
-    // as (order key of the filter score s~ = sum * f, key index).
+    // as (order key of the filter score s~ = sum * f, key index).  The
+    // filter parked sum - thr (its accumulators start at -thr).
     const float4 st = qstat[hq + q];
     const float kinv =
         __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
     const float f = scale * st.z * kinv;
+    const float tv = thr[hq + q];
+    uint32_t kmin = ~0u, kmax = 0u;
     {
       const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
       const uint2* list1 = list0 + capH;
-  #pragma unroll 8
+      #pragma unroll 8
       for (int i = l; i < c; i += kWave) {
         const uint2 e = i < c0 ? list0[i] : list1[i - c0];
-        ck[i] = order_key(__uint_as_float(e.y) * f);
+        const uint32_t key = order_key((__uint_as_float(e.y) + tv) * f);
+        ck[i] = key;
         cj[i] = static_cast<int>(e.x);
+        kmin = min(kmin, key);
+        kmax = max(kmax, key);
       }
     }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
     wave_sync();
+    if (c < k_i + (overflow ? 0 : 1)) {
+      // Too few keys for a proven bound: the threshold was set too high.
+      // Retry with a lower one, guessed from an exponential fit to the tail
+      // the candidates do show (c keys at or above tau - m, the largest at
+      // s_max), aiming at about 1.5 k keys; the retry proves it or, failing
+      // that, the query goes to the exact fallback.
+      float guess = __builtin_nanf("");
+      if (!overflow && c >= 2 && tq > -INFINITY) {
+        const float base = tq - score_margin(st.x, st.y, __uint_as_float(kstat[kKeyStatWords * h]),
+                                             __uint_as_float(kstat[kKeyStatWords * h + 1]),
+                                             scale, DP);
+        const float span = fmaxf(key_to_float(kmax) - base, 1e-6f);
+        const float lambda = __logf(static_cast<float>(c)) / span;
+        guess = base - __logf(1.5f * static_cast<float>(k_i) / static_cast<float>(c)) / lambda;
+      }
+      unresolved(guess);
+      continue;
+    }
     auto each_cand = [&](auto fn) {
-  #pragma unroll 1
+      #pragma unroll 1
       for (int i0 = 0; i0 < c; i0 += kWave) {
         const int i = i0 + l;
         const bool ok = i < c;
@@ -295,7 +364,8 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
                                  __uint_as_float(kstat[kKeyStatWords * h + 1]), scale, DP);
     auto lower = [&](float x) { return (x - m) - (fabsf(x) + m) * (1.0f / 4194304.0f); };
     auto upper = [&](float x) { return (x + m) + (fabsf(x) + m) * (1.0f / 4194304.0f); };
-    const uint32_t ak = wave_select<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf), each_cand);
+    const uint32_t ak = wave_select_in<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf),
+                                                 each_cand, kmin, kmax);
     const float lo = lower(key_to_float(ak));
     // The list covers every key that can reach the top-k only if the filter's
     // threshold is proven, i.e. the k best candidates are certainly above it.
@@ -303,46 +373,39 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       unresolved(lo);
       continue;
     }
-    // the (k+1)-th largest: equal to the k-th if that value repeats, else the
-    // largest value below it
-    int n_ge = 0;
-    uint32_t below = 0;
-    each_cand([&](uint32_t key, bool ok) {
-      if (ok) {
-        n_ge += key >= ak ? 1 : 0;
-        if (key < ak) below = max(below, key);
-      }
-    });
-    n_ge = wave_sum_i(n_ge);
-    below = wave_max_u32(below);
-    const uint32_t bk = n_ge > k_i ? ak : below;
-    const float hi = fmaxf(tq, upper(key_to_float(bk)));
-    // Certainly kept: l > hi; certainly out: u < lo.  Both tests are monotone in
-    // the filter score, so they become key thresholds: kept iff ck > in_key,
-    // out iff ck < out_key (keys between are uncertain).
+    // The upper bound of the k-th value stands in for that of the (k+1)-th:
+    // it is not smaller, so a key above it is still certainly kept.
+    const float hi = fmaxf(tq, upper(key_to_float(ak)));
+    // Certainly kept: l > hi; certainly out: u < lo; uncertain otherwise.
     auto cls_of = [&](uint32_t key) {
       const float x = key_to_float(key);
       return lower(x) > hi ? 1 : (upper(x) < lo ? 0 : 2);
     };
 
-    // list the uncertain keys
-    int n_in = 0, nU = 0;
-  #pragma unroll 1
+    // One pass classifies and compacts: certainly-kept and uncertain keys
+    // stay, in list order, in place in cj (a chunk is read before it is
+    // written, and writes never pass the chunk); uncertain ones carry bit 31
+    // and are also listed in uj for the exact re-score.
+    int run = 0, n0c = 0, nU = 0;
+    #pragma unroll 1
     for (int i0 = 0; i0 < c; i0 += kWave) {
       const int i = i0 + l;
-      const int cc = i < c ? cls_of(ck[i]) : 0;
-      n_in += cc == 1 ? 1 : 0;
-      const unsigned long long mk = __ballot(cc == 2);
+      const bool ok = i < c;
+      const int cc = ok ? cls_of(ck[i]) : 0;
+      const int key = ok ? cj[i] : 0;
+      const unsigned long long mu = __ballot(cc == 2);
+      const unsigned long long mk = __ballot(cc != 0);
       if (cc == 2) {
-        const int pos = nU + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                 static_cast<uint32_t>(mk >> 32),
-                                 __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
-        if (pos < ucap) uj[pos] = cj[i];
+        const int pos = nU + lane_rank(mu);
+        if (pos < ucap) uj[pos] = key;
       }
-      nU += __builtin_popcountll(mk);
+      wave_sync();
+      if (cc != 0) cj[run + lane_rank(mk)] = cc == 2 ? (key | INT_MIN) : key;
+      nU += __builtin_popcountll(mu);
+      run += __builtin_popcountll(mk);
+      n0c += __builtin_popcountll(__ballot(cc != 0 && i < c0));
     }
-    n_in = wave_sum_i(n_in);
-    const int need = k_i - n_in;
+    const int need = k_i - (run - nU);
     if (nU > ucap || need > nU) {
       unresolved(__builtin_nanf(""));
       continue;
@@ -355,19 +418,19 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
       constexpr int UNR = 4;             // passes in flight
       const int g = l % G, grp = l / G;
       const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
-  #pragma unroll 1
+      #pragma unroll 1
       for (int u0 = 0; u0 < nU; u0 += KPI * UNR) {
         float4 kv[UNR];
-  #pragma unroll
+        #pragma unroll
         for (int t = 0; t < UNR; ++t) {
           const int u = u0 + t * KPI + grp;
           kv[t] = u < nU ? reinterpret_cast<const float4*>(k32 + (hq + uj[u]) * DP)[g]
                          : make_float4(0.f, 0.f, 0.f, 0.f);
         }
-  #pragma unroll
+        #pragma unroll
         for (int t = 0; t < UNR; ++t) {
           float p = group_partial<DP>(qv, kv[t]);
-  #pragma unroll
+          #pragma unroll
           for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
           const int u = u0 + t * KPI + grp;
           if (g == 0 && u < nU) us[u] = p * scale;
@@ -378,47 +441,38 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     unsigned long long kth = ~0ull;
     if (need > 0) {
       kth = wave_select<unsigned long long>(need, hist, cbuf, [&](auto fn) {
-  #pragma unroll 1
+        #pragma unroll 1
         for (int u0 = 0; u0 < nU; u0 += kWave) {
           const int u = u0 + l;
           fn(u < nU ? rank_key(us[u], uj[u]) : 0ull, u < nU);
         }
       });
     }
-    // Compact the kept keys in list order (each half ascending) in place into
-    // cj: a chunk's reads all happen before its writes, and writes never pass
-    // the chunk.  The uncertain keys are met in the order they were listed.
-    int run = 0, n0 = 0, ucount = 0;
-  #pragma unroll 1
-    for (int i0 = 0; i0 < c; i0 += kWave) {
+    // Drop the uncertain keys that lose (in place again); they are met in the
+    // order they were listed in uj.
+    int run2 = 0, n0 = 0, upos = 0;
+    #pragma unroll 1
+    for (int i0 = 0; i0 < run; i0 += kWave) {
       const int i = i0 + l;
-      const int cc = i < c ? cls_of(ck[i]) : 0;
-      const int key = i < c ? cj[i] : 0;
-      const unsigned long long mk = __ballot(cc == 2);
-      bool take = cc == 1;
-      if (cc == 2) {
-        const int pos = ucount + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                                     static_cast<uint32_t>(mk >> 32),
-                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mk), 0)));
+      const bool ok = i < run;
+      const int e = ok ? cj[i] : 0;
+      const bool unc = e < 0;
+      const unsigned long long mu = __ballot(unc);
+      bool take = ok && !unc;
+      if (unc) {
+        const int pos = upos + lane_rank(mu);
         take = need > 0 && rank_key(us[pos], uj[pos]) >= kth;
       }
-      ucount += __builtin_popcountll(mk);
+      upos += __builtin_popcountll(mu);
       const unsigned long long tk = __ballot(take);
       wave_sync();
-      if (take)
-        cj[run + static_cast<int>(__builtin_amdgcn_mbcnt_hi(
-                     static_cast<uint32_t>(tk >> 32),
-                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(tk), 0)))] = key;
-      run += __builtin_popcountll(tk);
-      n0 += __builtin_popcountll(__ballot(take && i < c0));
-      wave_sync();
+      if (take) cj[run2 + lane_rank(tk)] = e & INT_MAX;
+      run2 += __builtin_popcountll(tk);
+      n0 += __builtin_popcountll(__ballot(take && i < n0c));
     }
-    const int* sel = cj;
-    const int n1 = run - n0;
-    for (int p2 = l; p2 < n0; p2 += kWave) out[p2 + lower_bound(sel + n0, n1, sel[p2])] = sel[p2];
-    for (int p2 = l; p2 < n1; p2 += kWave)
-      out[p2 + lower_bound(sel, n0, sel[n0 + p2])] = sel[n0 + p2];
-    for (int t = run + l; t < k; t += kWave) out[t] = -1;
+    wave_sync();
+    merge_rows(cj, n0, cj + n0, run2 - n0, out);
+    for (int t = run2 + l; t < k; t += kWave) out[t] = -1;
     st_rescored += static_cast<unsigned long long>(nU);
     ++st_queries;
   }
@@ -503,26 +557,29 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
       pmask |= 255u << shift;
       __syncthreads();
     }
-    // keys strictly above the k-th score, then ties in ascending key order
-    int gt = 0;
-    for (int j = tid; j < n_valid; j += kThreads) gt += order_key(row[j]) > prefix ? 1 : 0;
-    int gt_total;
-    block_excl_scan(gt, tmp, gt_total);
+    // Keys strictly above the k-th score, then ties in ascending key order.
+    // Each thread owns a contiguous range of keys, so two block scans give
+    // every thread its first output position.
+    const int L = (n_valid + kThreads - 1) / kThreads;
+    const int j0 = min(n_valid, tid * L), j1 = min(n_valid, j0 + L);
+    int gt = 0, eq = 0;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = order_key(row[j]);
+      gt += key > prefix ? 1 : 0;
+      eq += key == prefix ? 1 : 0;
+    }
+    int gt_total, eq_total;
+    const int gt_before = block_excl_scan(gt, tmp, gt_total);
+    const int eq_before = block_excl_scan(eq, tmp, eq_total);
     const int ties_needed = k_i - gt_total;
     int32_t* out = idx + (hq / Npad * static_cast<size_t>(N) + q) * k;
-    int run_take = 0, run_eq = 0;
-    for (int j0 = 0; j0 < n_valid; j0 += kThreads) {
-      const int j = j0 + tid;
-      const uint32_t key = j < n_valid ? order_key(row[j]) : 0u;
-      const int is_eq = (j < n_valid && key == prefix) ? 1 : 0;
-      int eq_total;
-      const int eq_before = run_eq + block_excl_scan(is_eq, tmp, eq_total);
-      const int take = (j < n_valid && (key > prefix || (is_eq && eq_before < ties_needed))) ? 1 : 0;
-      int take_total;
-      const int pos = run_take + block_excl_scan(take, tmp, take_total);
-      if (take) out[pos] = j;
-      run_take += take_total;
-      run_eq += eq_total;
+    int pos = gt_before + min(eq_before, ties_needed);
+    int eq_seen = eq_before;
+    for (int j = j0; j < j1; ++j) {
+      const uint32_t key = order_key(row[j]);
+      const bool tie = key == prefix;
+      if (key > prefix || (tie && eq_seen < ties_needed)) out[pos++] = j;
+      eq_seen += tie ? 1 : 0;
     }
     for (int t = k_i + tid; t < k; t += kThreads) out[t] = -1;
     if (tid == 0) atomicAdd(&hdr->fallback_queries, 1ull);
@@ -548,8 +605,8 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(lds));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt,
-                     b.tau, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
+  hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt, b.rcnt,
+                     b.tau, b.thr, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
                      p.capH, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
                      retry ? b.rcount : static_cast<int*>(nullptr), b.rlist, b.rcount, b.fblist,
                      b.hdr);

@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
 // head's largest residual norm.
 template <int DP, typename F>
 __global__ __launch_bounds__(kThreads) void pack_keys_kernel(
-    const float* __restrict__ k32, int Npad, uint32_t* __restrict__ kstat,
+    const float* __restrict__ k32, int Npad, int sstride, uint32_t* __restrict__ kstat,
     uint16_t* __restrict__ k16, uint16_t* __restrict__ samp) {
   __shared__ float sRes[kRows * (DP + 1)];
   __shared__ float sMax[kRows];
@@ -147,8 +147,8 @@ __global__ __launch_bounds__(kThreads) void pack_keys_kernel(
     const float v = k32[(base + row) * DP + c];
     const uint16_t u = F::round(__builtin_ldexpf(v, E));
     k16[(base + row) * DP + c] = u;
-    if ((row % kSampleStride) == 0)
-      samp[(static_cast<size_t>(h) * (Npad / kSampleStride) + row / kSampleStride) * DP + c] = u;
+    if ((row % sstride) == 0)
+      samp[(static_cast<size_t>(h) * (Npad / sstride) + row / sstride) * DP + c] = u;
     sRes[r * (DP + 1) + c] = v - __builtin_ldexpf(F::back(u), -E);
   }
   __syncthreads();
@@ -231,7 +231,7 @@ hipError_t pack_f(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
 #define SA_PACK(DPV)                                                                          \
   case DPV:                                                                                   \
     hipLaunchKernelGGL((pack_keys_kernel<DPV, F>), grid, dim3(kThreads), 0, s, b.klo32, p.Npad, \
-                       b.kstat, b.klo16, b.ksamp);                                            \
+                       p.sstride, b.kstat, b.klo16, b.ksamp);                                 \
     return hipGetLastError();
     SA_PACK(16)
     SA_PACK(32)

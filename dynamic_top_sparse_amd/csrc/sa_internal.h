@@ -12,11 +12,12 @@ namespace sa {
 // Tunables of the selection pipeline.
 constexpr int kQueriesPerBlock = 256;   // scorer workgroup: 4 waves x 64 queries
 constexpr int kKeysPerChunk = 128;      // keys staged in LDS per step
-constexpr int kSampleStride = 16;       // the threshold sample takes every 16th key
+constexpr int kMaxSampleStride = 16;    // the threshold sample takes every s-th key, s <= 16
 constexpr int kRowPad = 2048;           // N is padded to a multiple of this
-constexpr float kTauBeta = 2.0f;        // sample rank slack (see threshold kernel)
-constexpr int kFallbackBlocks = 64;     // workgroups of the exact fallback
+constexpr float kTauBeta = 1.5f;        // sample rank slack (see threshold kernel)
+constexpr int kFallbackBlocks = 256;    // workgroups of the exact fallback
 constexpr int kKMax = 2048;             // largest supported k
+constexpr int kRetrySplit = 8;          // key segments of the retry filter (capH is a multiple of 64)
 
 // Byte offsets of one head chunk's buffers inside the workspace.
 struct Plan {
@@ -25,13 +26,14 @@ struct Plan {
   int BH;         // B*H heads
   int hc;         // heads per chunk
   int Npad;       // N rounded up to kRowPad
-  int Ns;         // sample keys: ceil(N / kSampleStride)
-  int Nspad;      // Npad / kSampleStride
+  int sstride;    // sample stride s: a power of two, about beta*k/32, in [1, 16]
+  int Ns;         // sample keys: ceil(N / s)
+  int Nspad;      // Npad / s
   int NB;         // block maxima per query: 2 * ceil(Ns / 32)
   int capH;       // candidate capacity of one query half
   int with_idx;   // room for idx rows of the chunk
   size_t off_hdr, off_qlo32, off_klo32, off_qlo16, off_klo16, off_ksamp, off_qstat,
-      off_kstat, off_bm, off_tau, off_cand, off_cnt, off_rlist, off_rcount, off_fblist,
+      off_kstat, off_bm, off_tau, off_thr, off_cand, off_cnt, off_rcnt, off_rlist, off_rcount, off_fblist,
       off_fbscratch, off_idx, total;
 };
 
@@ -39,6 +41,30 @@ struct Plan {
 // when the sizes do not fit the index arithmetic.
 bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, int dtype,
                int with_idx, int heads_per_chunk);
+
+// Threshold sample: rank r of the sample maxima that sets a query's
+// threshold (about beta * k keys are expected above it; the sample stride is
+// chosen so that r is near 48), and the size B of the sample blocks whose
+// maxima are kept for it: the largest power of two that leaves at least 4r
+// blocks, so that the top samples rarely share a block.  Blocks of up to 16
+// samples lie within one 32-sample tile (a lane sees 16 of its samples);
+// larger ones span B/16 tiles.  The kernels that use these must agree.
+__host__ __device__ inline int sample_rank(int k_i, int ns_valid, int n_valid, float beta) {
+  const int r = static_cast<int>(ceilf(beta * static_cast<float>(k_i) *
+                                       static_cast<float>(ns_valid) /
+                                       static_cast<float>(n_valid)));
+  return r < 1 ? 1 : r;
+}
+__host__ __device__ inline int sample_block(int ns_valid, int r) {
+  int B = 1;
+  while (ns_valid / (2 * B) >= 4 * r) B *= 2;
+  return B;
+}
+// Maxima a query keeps: one per block of its valid sample tiles.
+__host__ __device__ inline int sample_blocks(int ns_valid, int B) {
+  const int tiles = (ns_valid + 31) / 32;
+  return B <= 16 ? tiles * (32 / B) : 2 * ((tiles + B / 16 - 1) / (B / 16));
+}
 
 // Number of kstat words per head.
 constexpr int kKeyStatWords = 4;
@@ -55,8 +81,10 @@ struct Bufs {
   uint32_t* kstat;      // per head: max ||k_low||, max ||k_low - k~||, max |k_low|_inf (fp32 bits)
   float* bm;            // sample block maxima [hc][NB][Npad]
   float* tau;           // per-query threshold [hc][Npad]
+  float* thr;           // the filter's threshold on the raw MFMA sum, as used [hc][Npad]
   uint2* cand;          // candidates [hc][Npad][2][capH] = (key, raw MFMA sum bits)
   int* cnt;             // candidates per query half [hc][Npad][2]
+  int* rcnt;            // retry pass: candidates per query half and key segment [hc][Npad][2][kRetrySplit]
   int* rlist;           // per head: queries to filter again with a proven threshold
   int* rcount;          // per head: entries of rlist
   int* fblist;          // queries queued for the exact fallback

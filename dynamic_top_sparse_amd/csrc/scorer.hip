@@ -115,11 +115,31 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 }
 
 // ------------------------------------------------------------ sample pass ---
+// Block maxima of one lane's 16 accumulators (keys 8*(r/4) + r%4 + 4*half of
+// the tile, in r order) for blocks of B consecutive accumulators, stored as
+// values e0 .. e0 + 16/B - 1 of the query's row of maxima.
+__device__ __forceinline__ void store_block_maxima(f32x16 v, int B, float* __restrict__ dst,
+                                                   size_t stride) {
+#pragma unroll
+  for (int lvl = 0; lvl <= 4; ++lvl) {
+    const int b = 1 << lvl;
+    if (lvl > 0) {
+#pragma unroll
+      for (int r = 0; r < 16; r += b) v[r] = fmaxf(v[r], v[r + b / 2]);
+    }
+    if (B == b) {
+#pragma unroll
+      for (int g = 0; g < 16 / b; ++g) dst[g * stride] = v[g * b];
+    }
+  }
+}
+
 template <int DP, typename F>
 __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat, float scale, int N,
-    int Npad, int Ns, int NB, int causal, float* __restrict__ bm) {
+    int Npad, int Ns, int sstride, int k, int causal, int capH, float beta,
+    float* __restrict__ bm) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kQueriesPerBlock;
@@ -128,21 +148,36 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
   const int half = l >> 5;
   const int qw = q0 + w * kWaveQueries;
   const bf16_t* qh = q16 + static_cast<size_t>(h) * Npad * DP;
-  const bf16_t* sh = samp + static_cast<size_t>(h) * (Npad / kSampleStride) * DP;
-  float* bmh = bm + static_cast<size_t>(h) * NB * Npad;
+  const bf16_t* sh = samp + static_cast<size_t>(h) * (Npad / sstride) * DP;
+  // value e of query q of head h: bm[e * (heads * Npad) + h * Npad + q]
+  float* bmh = bm + static_cast<size_t>(h) * Npad;
+  const size_t stride = static_cast<size_t>(gridDim.y) * Npad;
 
   uint4 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
   load_query_frags<DP>(b0, qh, qw + (l & 31));
   load_query_frags<DP>(b1, qh, qw + 32 + (l & 31));
-  const int qa = qw + (l & 31), qb = qw + 32 + (l & 31);
+  const int qq[2] = {qw + (l & 31), qw + 32 + (l & 31)};
   const float kinv = __builtin_ldexpf(
       1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
-  const float fa = score_factor(qstat[static_cast<size_t>(h) * Npad + qa].z, kinv, scale);
-  const float fb = score_factor(qstat[static_cast<size_t>(h) * Npad + qb].z, kinv, scale);
+  const float fa = score_factor(qstat[static_cast<size_t>(h) * Npad + qq[0]].z, kinv, scale);
+  const float fb = score_factor(qstat[static_cast<size_t>(h) * Npad + qq[1]].z, kinv, scale);
+  // Per query: its block size and its last valid sample tile.  Only rows
+  // that use a threshold store maxima, and only for their own valid samples,
+  // so a row never exceeds sample_blocks() values.
+  int Bq[2], last_tile[2];
+  float run[2] = {-INFINITY, -INFINITY};   // running maximum of a block that spans tiles
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    const int q = qq[bb];
+    const int n_valid = causal ? min(q + 1, N) : N;
+    const int nsv = causal ? min(Ns, q / sstride + 1) : Ns;
+    Bq[bb] = sample_block(nsv, sample_rank(min(k, n_valid), nsv, n_valid, beta));
+    last_tile[bb] = q < N && n_valid > 2 * capH - 64 ? (nsv - 1) / 32 : -1;
+  }
 
-  // sample keys t with stride*t <= last query of the block (causal), else all
+  // sample keys t with s*t <= last query of the block (causal), else all
   int s_end = Ns;
-  if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / kSampleStride + 1);
+  if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / sstride + 1);
   const int nchunks = (s_end + kKeysPerChunk - 1) / kKeysPerChunk;
   u32x4 regs[Stage<DP>::kPerThread];
   chunk_load<DP>(regs, sh, 0);
@@ -156,22 +191,41 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       const int tbase = ch * kKeysPerChunk + tt * 32;
       if (tbase >= s_end) break;
-      f32x16 a0 = tile_scores<DP, F>(buf, tt, b0);
-      f32x16 a1 = tile_scores<DP, F>(buf, tt, b1);
-      float m0 = -INFINITY, m1 = -INFINITY;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int t = tbase + acc_row(r, half);
-        const int j = t * kSampleStride;
-        const bool ok = t < s_end;
-        const bool ok0 = ok && (!causal || j <= qa);
-        const bool ok1 = ok && (!causal || j <= qb);
-        m0 = fmaxf(m0, ok0 ? a0[r] : -INFINITY);
-        m1 = fmaxf(m1, ok1 ? a1[r] : -INFINITY);
-      }
+      f32x16 a[2];
+      a[0] = tile_scores<DP, F>(buf, tt, b0);
+      a[1] = tile_scores<DP, F>(buf, tt, b1);
       const int tile = tbase / 32;
-      bmh[static_cast<size_t>(2 * tile + half) * Npad + qa] = m0 * fa;
-      bmh[static_cast<size_t>(2 * tile + half) * Npad + qb] = m1 * fb;
+      // samples past the end or after a query (causal) only occur on edge tiles
+      const bool edge = tbase + 32 > s_end || (causal && (tbase + 31) * sstride > qw);
+#pragma unroll
+      for (int bb = 0; bb < 2; ++bb) {
+        const float fq = bb ? fb : fa;   // > 0: scaling commutes with the maxima
+        if (edge) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int t = tbase + acc_row(r, half);
+            const bool ok = t < s_end && (!causal || t * sstride <= qq[bb]);
+            a[bb][r] = ok ? a[bb][r] : -INFINITY;
+          }
+        }
+        if (tile > last_tile[bb]) continue;
+        const int B = Bq[bb];
+        if (B <= 16) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) a[bb][r] *= fq;
+          store_block_maxima(a[bb], B, bmh + (2 * tile + half) * (16 / B) * stride + qq[bb], stride);
+        } else {
+          float m = a[bb][0];
+#pragma unroll
+          for (int r = 1; r < 16; ++r) m = fmaxf(m, a[bb][r]);
+          run[bb] = fmaxf(run[bb], m * fq);
+          const int G = B / 16;
+          if (tile % G == G - 1 || tile == last_tile[bb]) {
+            bmh[(2 * (tile / G) + half) * stride + qq[bb]] = run[bb];
+            run[bb] = -INFINITY;
+          }
+        }
+      }
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
@@ -179,27 +233,28 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
 }
 
 // -------------------------------------------------------------- threshold ---
-// One thread per query: a 4-bit-digit radix select over the top 16 bits of
-// the block maxima's order keys gives a value <= the r-th largest block
-// maximum (rounding down only adds candidates).
+// One thread per query: tau is (a lower rounding of) the r-th largest of the
+// query's block maxima, found by a 4-bit-digit radix select over the top 16
+// bits of their order keys (rounding down only adds candidates).  About
+// beta * k keys are expected above it.
 __global__ __launch_bounds__(kThreads) void threshold_kernel(
-    const float* __restrict__ bm, int N, int Npad, int Ns, int NB, int k, int causal, int capH,
-    float beta, float* __restrict__ tau) {
+    const float* __restrict__ bm, int N, int Npad, int Ns, int sstride, int k, int causal,
+    int capH, float beta, float* __restrict__ tau) {
   __shared__ int hist[16 * kThreads];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int q = blockIdx.x * kThreads + tid;
-  const float* bmh = bm + static_cast<size_t>(h) * NB * Npad;
+  const size_t stride = static_cast<size_t>(gridDim.y) * Npad;
+  const float* bmh = bm + static_cast<size_t>(h) * Npad;
   if (q >= Npad) return;  // whole-block uniform: Npad is a multiple of 256
   float result = -INFINITY;
   const int n_valid = causal ? q + 1 : N;
   const bool active = q < N && n_valid > 2 * capH - 64;
-  const int ns_valid = causal ? min(Ns, q / kSampleStride + 1) : Ns;
-  const int nb = 2 * ((ns_valid + 31) / 32);
+  const int ns_valid = causal ? min(Ns, q / sstride + 1) : Ns;
   const int k_i = min(k, n_valid);
-  int r = static_cast<int>(ceilf(beta * static_cast<float>(k_i) * static_cast<float>(ns_valid) /
-                                  static_cast<float>(n_valid)));
-  r = max(1, min(r, nb));
+  const int r0 = sample_rank(k_i, ns_valid, n_valid, beta);
+  const int nb = sample_blocks(ns_valid, sample_block(ns_valid, r0));
+  const int r = min(r0, nb);
   uint32_t prefix = 0;
   int K = r;
   for (int pass = 0; pass < 4; ++pass) {
@@ -209,7 +264,7 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
     for (int d = 0; d < 16; ++d) hist[d * kThreads + tid] = 0;
     if (active) {
       for (int e = 0; e < nb; ++e) {
-        const uint32_t key = order_key(bmh[static_cast<size_t>(e) * Npad + q]);
+        const uint32_t key = order_key(bmh[static_cast<size_t>(e) * stride + q]);
         if ((key & pmask) == prefix) hist[((key >> shift) & 15u) * kThreads + tid] += 1;
       }
       int cum = 0, digit = 0;
@@ -230,14 +285,28 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
 }
 
 // ------------------------------------------------------------ filter pass ---
-// Bit r of the result is set when accumulator r misses the threshold: the
-// sign bit of v - thr is shifted in with one v_alignbit per accumulator
-// (v >= thr exactly when v - thr >= +0; masked -inf scores always miss).
-__device__ __forceinline__ unsigned miss_bits(const f32x16& a, float thr) {
+// The MFMA accumulates onto C = -thr (thr: the query's threshold on the raw
+// sum), so a pair passes exactly when its accumulator's sign bit is clear.
+// Bit r of the result is set when accumulator r misses; the sign bits are
+// shifted in with one v_alignbit per accumulator.  Masked (-inf) rows miss.
+__device__ __forceinline__ unsigned miss_bits(const f32x16& a) {
   unsigned nb = 0;
 #pragma unroll
-  for (int r = 15; r >= 0; --r) nb = __builtin_amdgcn_alignbit(nb, __float_as_uint(a[r] - thr), 31);
+  for (int r = 15; r >= 0; --r) nb = __builtin_amdgcn_alignbit(nb, __float_as_uint(a[r]), 31);
   return nb;
+}
+
+template <int DP, typename F>
+__device__ __forceinline__ f32x16 tile_scores_c(const uint4* __restrict__ lds, int tile_in_chunk,
+                                                const uint4 (&b)[Tile<DP>::kKSteps],
+                                                const f32x16& c) {
+  const int l = lane_id();
+  const int key = tile_in_chunk * 32 + (l & 31);
+  f32x16 acc = F::mfma(lds[lds_unit<DP>(key, l >> 5)], b[0], c);
+#pragma unroll
+  for (int ks = 1; ks < Tile<DP>::kKSteps; ++ks)
+    acc = F::mfma(lds[lds_unit<DP>(key, 2 * ks + (l >> 5))], b[ks], acc);
+  return acc;
 }
 
 // Rows of a lane's accumulators are key offsets r + (r & 12) (+4 for the
@@ -251,19 +320,39 @@ __device__ __forceinline__ unsigned valid_rows(int lim) {
   return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
 }
 
+// Appends the passing accumulators of one 32-query block to the lane's list.
+// A lane cannot index its accumulators by a run-time bit number, so it parks
+// its 16 values in its own LDS column (stash[r][lane]: conflict-free, and a
+// hit's address is one shift-add) and reads back the ones whose bit is set.
+__device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, float* stash,
+                                           unsigned jbase, uint2* lst, unsigned& count,
+                                           unsigned last) {
+  if (bits) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
+  }
+  while (bits) {
+    const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
+    bits &= bits - 1;
+    const float v = stash[b * kThreads];
+    // accumulator r holds key row r + (r & 12) (+4 in the upper half-wave)
+    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
+    ++count;
+  }
+}
 
 template <int DP, typename F>
 __global__ __launch_bounds__(kThreads) void filter_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
-    const float* __restrict__ tau, int N, int Npad, int causal, int capH, float scale,
-    const int* __restrict__ qlist, const int* __restrict__ qlist_count,
-    uint2* __restrict__ cand, int* __restrict__ cnt, WsHeader* __restrict__ hdr) {
+    const float* __restrict__ tau, float* __restrict__ thr_out, int N, int Npad, int causal,
+    int capH, float scale, const int* __restrict__ qlist, const int* __restrict__ qlist_count,
+    uint2* __restrict__ cand, int* __restrict__ cnt, int* __restrict__ rcnt, int mode,
+    WsHeader* __restrict__ hdr) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
-  __shared__ float4 stash_all[8 * kThreads];   // 32 scores per lane, [8][threads]
+  __shared__ float stash_all[16 * kThreads];   // 16 scores per lane, [16][threads]
   __shared__ int s_kend[kThreads / kWave];
-  float4* stash4 = stash_all + threadIdx.x;
-  const float* stash = reinterpret_cast<const float*>(stash4);
+  float* stash = stash_all + threadIdx.x;
   const int h = blockIdx.y;
   const int w = threadIdx.x >> 6;
   const int l = lane_id();
@@ -271,7 +360,12 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   const size_t hq = static_cast<size_t>(h) * Npad;
   // Queries of this lane (blocks 0 and 1).  Normally 256 consecutive rows per
   // workgroup (causal: the longest rows first); in list mode (a retry with a
-  // new threshold) rows listed in qlist for this head.
+  // new threshold) rows listed in qlist for this head.  Those are few, so
+  // kRetrySplit workgroups share each 256 of them, one key segment each, in
+  // two launches: mode 1 counts each segment's hits, mode 2 writes them at
+  // the segment's offset in the query's list, which so stays in key order.
+  const int nseg = qlist == nullptr ? 1 : kRetrySplit;
+  const int seg = qlist == nullptr ? 0 : static_cast<int>(blockIdx.x) % kRetrySplit;
   int qq[2];
   bool live[2];
   if (qlist == nullptr) {
@@ -284,7 +378,7 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     live[1] = qq[1] < N;
   } else {
     const int count = qlist_count[h];
-    const int slot0 = static_cast<int>(blockIdx.x) * kQueriesPerBlock;
+    const int slot0 = static_cast<int>(blockIdx.x) / kRetrySplit * kQueriesPerBlock;
     if (slot0 >= count) return;                 // whole workgroup: nothing listed here
     const int sa = slot0 + w * kWaveQueries + (l & 31);
     live[0] = sa < count;
@@ -323,19 +417,24 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   load_query_frags<DP>(b0, qh, qa);
   load_query_frags<DP>(b1, qh, qb);
 
-  // Per-lane threshold on the raw MFMA sum: pairs with s~ >= tau - m pass,
-  // where s~ = sum * f and f = score_factor(...) is a power-of-two multiple of
-  // the score scale.  The bound is moved down by a few ulps so that rounding
-  // of the scaled score can never drop such a pair.
-  float thr[2];
+  // Threshold on the raw MFMA sum: pairs with s~ >= tau - m pass, where
+  // s~ = sum * f and f = score_factor(...) is a power-of-two multiple of the
+  // score scale.  The bound is moved down by a few ulps so that rounding of
+  // the scaled score can never drop such a pair.  tau = -inf keeps every
+  // valid key (C = 0, all bits set).  The value used is stored for the
+  // re-rank, which adds it back to the parked accumulators.
+  f32x16 cinit[2];
+  bool all_pass[2];
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
     const int q = qq[bb];
-    float t = INFINITY;
+    float c = -INFINITY;     // idle lanes: every pair misses
+    all_pass[bb] = false;
     if (live[bb]) {
       const float tq = tau[hq + q];
+      float t = 0.0f;
       if (tq == -INFINITY) {
-        t = -FLT_MAX;
+        all_pass[bb] = true;
       } else {
         const float4 st = qstat[hq + q];
         const float m = score_margin(st.x, st.y, kn, kr, scale, DP);
@@ -344,21 +443,42 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
         t = lim / score_factor(st.z, kinv, scale);
         t -= fabsf(t) * (1.0f / 1048576.0f) + 1e-30f;
       }
+      c = -t;
+      if (half == 0) thr_out[hq + q] = t;
     }
-    thr[bb] = t;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) cinit[bb][r] = c;
   }
+  // list position of this workgroup's first entry (the hits of the earlier
+  // segments come first); entries past the capacity land on the last slot,
+  // and the re-rank sees the overflow from the counts
   uint2* list[2];
-  list[0] = cand + ((hq + qa) * 2 + half) * static_cast<size_t>(capH);
-  list[1] = cand + ((hq + qb) * 2 + half) * static_cast<size_t>(capH);
+  unsigned last[2];
+#pragma unroll
+  for (int bb = 0; bb < 2; ++bb) {
+    int off = 0;
+    if (mode == 2) {
+      const int* rc = rcnt + ((hq + qq[bb]) * 2 + half) * kRetrySplit;
+      for (int s2 = 0; s2 < seg; ++s2) off += rc[s2];
+    }
+    off = min(off, capH - 1);
+    list[bb] = cand + ((hq + qq[bb]) * 2 + half) * static_cast<size_t>(capH) + off;
+    last[bb] = static_cast<unsigned>(capH - 1 - off);
+  }
   unsigned count[2] = {0u, 0u};
-  const unsigned last = static_cast<unsigned>(capH - 1);
 
-  const int nchunks = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
+  // this workgroup's chunks: all of [0, kend), or its segment of them
+  const int nch_all = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
+  const int per_seg = (nch_all + nseg - 1) / nseg;
+  const int ch0 = min(nch_all, seg * per_seg);
+  const int nchunks = min(nch_all, ch0 + per_seg);
   u32x4 regs[Stage<DP>::kPerThread];
-  chunk_load<DP>(regs, kh, 0);
-  chunk_store<DP>(regs, lds);
+  if (ch0 < nchunks) {
+    chunk_load<DP>(regs, kh, ch0 * kKeysPerChunk);
+    chunk_store<DP>(regs, lds + (ch0 & 1) * Tile<DP>::kChunkUnits);
+  }
   __syncthreads();
-  for (int ch = 0; ch < nchunks; ++ch) {
+  for (int ch = ch0; ch < nchunks; ++ch) {
     const bool more = ch + 1 < nchunks;
     if (more) chunk_load<DP>(regs, kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
@@ -366,52 +486,30 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     // accumulators of two tiles: the next tile's MFMAs run while this tile's
     // scores are filtered (past the last tile they read stale LDS, unused)
     f32x16 acc[2][2];
-    acc[0][0] = tile_scores<DP, F>(buf, 0, b0);
-    acc[0][1] = tile_scores<DP, F>(buf, 0, b1);
+    acc[0][0] = tile_scores_c<DP, F>(buf, 0, b0, cinit[0]);
+    acc[0][1] = tile_scores_c<DP, F>(buf, 0, b1, cinit[1]);
 #pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       if (tt >= ntiles) break;
       if (tt + 1 < kKeysPerChunk / 32) {
-        acc[(tt + 1) & 1][0] = tile_scores<DP, F>(buf, tt + 1, b0);
-        acc[(tt + 1) & 1][1] = tile_scores<DP, F>(buf, tt + 1, b1);
+        acc[(tt + 1) & 1][0] = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
+        acc[(tt + 1) & 1][1] = tile_scores_c<DP, F>(buf, tt + 1, b1, cinit[1]);
       }
       const int tbase = ch * kKeysPerChunk + tt * 32;
       const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
-      // bits 0-15: hits of query block 0, bits 16-31: query block 1
-      unsigned bits = (~miss_bits(acc[tt & 1][0], thr[0]) & 0xFFFFu) |
-                      (~miss_bits(acc[tt & 1][1], thr[1]) << 16);
+      unsigned bits0 = all_pass[0] ? 0xFFFFu : (~miss_bits(acc[tt & 1][0]) & 0xFFFFu);
+      unsigned bits1 = all_pass[1] ? 0xFFFFu : (~miss_bits(acc[tt & 1][1]) & 0xFFFFu);
       if (edge) {
-        const int lim0 = (causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase);
-        const int lim1 = (causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase);
-        bits &= valid_rows(lim0) | (valid_rows(lim1) << 16);
+        bits0 &= valid_rows((causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase));
+        bits1 &= valid_rows((causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase));
       }
-      if (bits) {
-        // park this lane's 32 tile scores (lane-interleaved: conflict-free)
-        // so that its hits can be read by index
-#pragma unroll
-        for (int bb = 0; bb < 2; ++bb) {
-          const f32x16& a = acc[tt & 1][bb];
-#pragma unroll
-          for (int v4 = 0; v4 < 4; ++v4)
-            stash4[(4 * bb + v4) * kThreads] =
-                make_float4(a[4 * v4], a[4 * v4 + 1], a[4 * v4 + 2], a[4 * v4 + 3]);
-        }
-        do {
-          const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
-          bits &= bits - 1;
-          const unsigned r = b & 15u;
-          const float v = stash[(b >> 2) * (4 * kThreads) + (b & 3u)];
-          // accumulator r holds key row r + (r & 12) + 4*half of the tile
-          const uint2 e = make_uint2(jbase + r + (r & 12u), __float_as_uint(v));
-          if (b < 16) {
-            list[0][min(count[0], last)] = e;
-            ++count[0];
-          } else {
-            list[1][min(count[1], last)] = e;
-            ++count[1];
-          }
-        } while (bits);
+      if (mode == 1) {
+        count[0] += __builtin_popcount(bits0);
+        count[1] += __builtin_popcount(bits1);
+      } else {
+        drain_hits(acc[tt & 1][0], bits0, stash, jbase, list[0], count[0], last[0]);
+        drain_hits(acc[tt & 1][1], bits1, stash, jbase, list[1], count[1], last[1]);
       }
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
@@ -419,11 +517,17 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
   }
 #pragma unroll
   for (int bb = 0; bb < 2; ++bb) {
-    if (live[bb]) cnt[(hq + qq[bb]) * 2 + half] = static_cast<int>(count[bb]);
+    if (live[bb]) {
+      if (mode == 0)
+        cnt[(hq + qq[bb]) * 2 + half] = static_cast<int>(count[bb]);
+      else if (mode == 1)
+        rcnt[((hq + qq[bb]) * 2 + half) * kRetrySplit + seg] = static_cast<int>(count[bb]);
+    }
   }
   int mine = 0;
 #pragma unroll
-  for (int bb = 0; bb < 2; ++bb) mine += live[bb] ? static_cast<int>(min(count[bb], last + 1)) : 0;
+  for (int bb = 0; bb < 2; ++bb)
+    mine += live[bb] && mode != 1 ? static_cast<int>(min(count[bb], last[bb] + 1)) : 0;
   const int tot = wave_sum_i(mine);
   if (l == 0 && tot) atomicAdd(&hdr->candidates, static_cast<unsigned long long>(tot));
 }
@@ -432,19 +536,25 @@ template <int DP, typename F>
 hipError_t sample_t(const Plan& p, const Bufs& b, int nh, float scale, hipStream_t s) {
   const dim3 grid(p.Npad / kQueriesPerBlock, nh);
   hipLaunchKernelGGL((sample_maxima_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.ksamp,
-                     b.qstat, b.kstat, scale, p.N, p.Npad, p.Ns, p.NB, p.causal, b.bm);
+                     b.qstat, b.kstat, scale, p.N, p.Npad, p.Ns, p.sstride, p.k, p.causal,
+                     p.capH, kTauBeta, b.bm);
   return hipGetLastError();
 }
 
 template <int DP, typename F>
 hipError_t filter_t(const Plan& p, const Bufs& b, int nh, float scale, bool retry,
                     hipStream_t s) {
-  const dim3 grid(p.Npad / kQueriesPerBlock, nh);
-  hipLaunchKernelGGL((filter_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
-                     b.qstat, b.kstat, b.tau, p.N, p.Npad, p.causal, p.capH, scale,
-                     retry ? b.rlist : static_cast<int*>(nullptr),
-                     retry ? b.rcount : static_cast<int*>(nullptr), b.cand, b.cnt, b.hdr);
-  return hipGetLastError();
+  const dim3 grid(p.Npad / kQueriesPerBlock * (retry ? kRetrySplit : 1), nh);
+  for (int mode = retry ? 1 : 0; mode <= (retry ? 2 : 0); ++mode) {
+    hipLaunchKernelGGL((filter_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
+                       b.qstat, b.kstat, b.tau, b.thr, p.N, p.Npad, p.causal, p.capH, scale,
+                       retry ? b.rlist : static_cast<int*>(nullptr),
+                       retry ? b.rcount : static_cast<int*>(nullptr), b.cand, b.cnt, b.rcnt,
+                       mode, b.hdr);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename F>
@@ -483,7 +593,7 @@ hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_sc
   const dim3 grid(p.Npad / kThreads, nh);
   (void)score_scale;
   hipLaunchKernelGGL(threshold_kernel, grid, dim3(kThreads), 0, s, b.bm, p.N, p.Npad, p.Ns,
-                     p.NB, p.k, p.causal, p.capH, kTauBeta, b.tau);
+                     p.sstride, p.k, p.causal, p.capH, kTauBeta, b.tau);
   return hipGetLastError();
 }
 
