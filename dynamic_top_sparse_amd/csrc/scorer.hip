@@ -320,29 +320,40 @@ __device__ __forceinline__ unsigned valid_rows(int lim) {
   return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
 }
 
-// Appends the passing accumulators of one 32-query block to the lane's list.
-// A lane cannot index its accumulators by a run-time bit number, so it parks
-// its 16 values in its own LDS column (stash[r][lane]: conflict-free, and a
-// hit's address is one shift-add) and reads back the ones whose bit is set.
-__device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, float* stash,
-                                           unsigned jbase, uint2* lst, unsigned& count,
-                                           unsigned last) {
-  if (bits) {
+// Appends the passing accumulators of one 32-query block to the lane's list,
+// in key order.  Accumulators start at -thr, so hits are exactly the
+// non-negative ones: a lane with a single hit (the common case) finds its
+// value as the maximum of its 16 accumulators.  A lane cannot index its
+// registers by a run-time number, so the rare lane with more hits (or on an
+// edge tile, where masked rows may also be non-negative) parks its values in
+// its own LDS column (stash[r][lane]: conflict-free) and reads them back.
+__device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, bool edge,
+                                           float* stash, unsigned jbase, uint2* lst,
+                                           unsigned& count, unsigned last) {
+  if (bits == 0u) return;
+  if (!edge && (bits & (bits - 1u)) == 0u) {
+    float v = a[0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
-  }
-  while (bits) {
+    for (int r = 1; r < 16; ++r) v = fmaxf(v, a[r]);
     const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
-    bits &= bits - 1;
-    const float v = stash[b * kThreads];
     // accumulator r holds key row r + (r & 12) (+4 in the upper half-wave)
     lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
     ++count;
+    return;
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
+  do {
+    const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
+    bits &= bits - 1u;
+    const float v = stash[b * kThreads];
+    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
+    ++count;
+  } while (bits);
 }
 
 template <int DP, typename F>
-__global__ __launch_bounds__(kThreads) void filter_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void filter_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ tau, float* __restrict__ thr_out, int N, int Npad, int causal,
@@ -351,7 +362,9 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     WsHeader* __restrict__ hdr) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   __shared__ float stash_all[16 * kThreads];   // 16 scores per lane, [16][threads]
-  __shared__ int s_kend[kThreads / kWave];
+  // per-wave last query, read before the first chunk barrier, so it can share
+  // the stash's space
+  int* s_kend = reinterpret_cast<int*>(stash_all);
   float* stash = stash_all + threadIdx.x;
   const int h = blockIdx.y;
   const int w = threadIdx.x >> 6;
@@ -483,18 +496,15 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
     if (more) chunk_load<DP>(regs, kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
     const int ntiles = min(kKeysPerChunk / 32, (kend - ch * kKeysPerChunk + 31) / 32);
-    // accumulators of two tiles: the next tile's MFMAs run while this tile's
-    // scores are filtered (past the last tile they read stale LDS, unused)
-    f32x16 acc[2][2];
-    acc[0][0] = tile_scores_c<DP, F>(buf, 0, b0, cinit[0]);
-    acc[0][1] = tile_scores_c<DP, F>(buf, 0, b1, cinit[1]);
+    // one tile's accumulators at a time: the registers this saves give three
+    // waves per SIMD, which overlap one wave's filtering with another's MFMAs
+    // better than a second set of accumulators within a wave does
 #pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       if (tt >= ntiles) break;
-      if (tt + 1 < kKeysPerChunk / 32) {
-        acc[(tt + 1) & 1][0] = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
-        acc[(tt + 1) & 1][1] = tile_scores_c<DP, F>(buf, tt + 1, b1, cinit[1]);
-      }
+      f32x16 acc[2][2];
+      acc[tt & 1][0] = tile_scores_c<DP, F>(buf, tt, b0, cinit[0]);
+      acc[tt & 1][1] = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
       const int tbase = ch * kKeysPerChunk + tt * 32;
       const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
@@ -508,8 +518,8 @@ __global__ __launch_bounds__(kThreads) void filter_kernel(
         count[0] += __builtin_popcount(bits0);
         count[1] += __builtin_popcount(bits1);
       } else {
-        drain_hits(acc[tt & 1][0], bits0, stash, jbase, list[0], count[0], last[0]);
-        drain_hits(acc[tt & 1][1], bits1, stash, jbase, list[1], count[1], last[1]);
+        drain_hits(acc[tt & 1][0], bits0, edge, stash, jbase, list[0], count[0], last[0]);
+        drain_hits(acc[tt & 1][1], bits1, edge, stash, jbase, list[1], count[1], last[1]);
       }
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
