@@ -155,6 +155,9 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
     p.NB = 8 * rmax + 40;
   }
   p.with_idx = with_idx ? 1 : 0;
+  // K and V rows of a head beyond one XCD's L2: the fused forward gathers by
+  // key range
+  p.gsplit = N > 8192 ? 1 : 0;
   const size_t hc = static_cast<size_t>(p.hc);
   const size_t Np = static_cast<size_t>(p.Npad);
   // queue entries and per-chunk row indices are int
@@ -184,6 +187,8 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.off_fblist = take(hc * Np * 4);
   p.off_fbscratch = take(static_cast<size_t>(kFallbackBlocks) * Np * 4);
   p.off_idx = take(p.with_idx ? hc * static_cast<size_t>(N) * k * 4 : 0);
+  p.off_seg = take(p.gsplit ? Np * (kGatherRanges + 1) * 4 : 0);
+  p.off_part = take(p.gsplit ? Np * kGatherRanges * static_cast<size_t>(D + 4) * 4 : 0);
   p.total = off;
   return true;
 }
@@ -210,6 +215,8 @@ Bufs bufs_of(const Plan& p, void* ws) {
   b.fblist = reinterpret_cast<int*>(base + p.off_fblist);
   b.fbscratch = reinterpret_cast<float*>(base + p.off_fbscratch);
   b.idx = p.with_idx ? reinterpret_cast<int32_t*>(base + p.off_idx) : nullptr;
+  b.seg = p.gsplit ? reinterpret_cast<int*>(base + p.off_seg) : nullptr;
+  b.part = p.gsplit ? reinterpret_cast<float*>(base + p.off_part) : nullptr;
   return b;
 }
 
@@ -310,9 +317,19 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
     const unsigned char* Kc = static_cast<const unsigned char*>(K) + off;
     const unsigned char* Vc = static_cast<const unsigned char*>(V) + off;
     unsigned char* Oc = static_cast<unsigned char*>(O) + off;
-    if (timed_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc, s) !=
-        hipSuccess)
+    if (p.gsplit) {
+      const size_t head = static_cast<size_t>(d.N) * d.D * esz;
+      for (int hh = 0; hh < nh; ++hh) {
+        if (launch_gather_split(Qc + hh * head, Kc + hh * head, Vc + hh * head,
+                                idx_chunk + static_cast<size_t>(hh) * d.N * k, k, d.N, d.D,
+                                softmax_scale, dtype, b.seg, b.part, Oc + hh * head,
+                                s) != hipSuccess)
+          return SA_ERR_HIP;
+      }
+    } else if (timed_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc,
+                            s) != hipSuccess) {
       return SA_ERR_HIP;
+    }
   }
   return SA_OK;
 }

@@ -28,6 +28,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kUnroll = 8;   // row loads in flight per lane
+constexpr int kXcds = 8;     // XCDs of the chip: workgroups are dealt to them in turn
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -66,96 +67,156 @@ template <> struct Vec<bf16_t> {
   }
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void gather_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int32_t* __restrict__ idx, int k, int N, float scale, T* __restrict__ O) {
-  constexpr int EPL = Vec<T>::kElems;                     // elements per lane
-  constexpr int LPR = D / EPL;                            // lanes per row
-  constexpr int RPI = kWave / LPR;                        // rows per load instruction
-  extern __shared__ int smem[];
-  const int w = threadIdx.x / kWave;
+// ---------------------------------------------------- per-wave attention ---
+// One wavefront attends one query over entries [t0, t1) of its index row.
+// The entries are first copied to the wave's LDS (`row` below points at that
+// copy, so every later key load waits on LDS rather than on a global load);
+// logits go to the wave's LDS buffer `slog` (index t - t0; room for t1 - t0
+// rounded up to 16), then become the unnormalised weights e^(x - m).
+
+// Logits, bf16 I/O: q.K[j] on the 16x16x32 bf16 MFMA, 16 keys per group.  A
+// = the group's K rows (lane l: row l % 16, dims 32 ks + 8 (l / 16) .. +8), B =
+// the query in every column, so each column holds the 16 dot products (lane
+// l: keys 4 (l / 16) + r).  bf16 products are exact in fp32 and accumulate
+// in fp32, as on the VALU; the MFMA only saves the per-row reductions.
+template <int D>
+__device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ qrow,
+                                            const bf16_t* __restrict__ K,
+                                            const int32_t* __restrict__ row, int t0, int t1,
+                                            int N, float scale, float* slog, int& bad) {
+  constexpr int KS = D / 32;
+  constexpr int G = 2;                       // key groups in flight
   const int l = lane_id();
-  int* sidx = smem + static_cast<size_t>(w) * 2 * k;
-  float* slog = reinterpret_cast<float*>(sidx + k);
-  const int h = blockIdx.y;
-  const int q = blockIdx.x * kWaves + w;
-  if (q >= N) return;
-  const size_t hN = static_cast<size_t>(h) * N;
-  const T* Kh = K + hN * D;
-  const T* Vh = V + hN * D;
-  const int32_t* row = idx + (hN + q) * k;
-  for (int t = l; t < k; t += kWave) sidx[t] = row[t];
+  bf16x8 qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * (l >> 4));
+    __builtin_memcpy(&qf[ks], &u, 16);
+  }
+  for (int tg = t0; tg < t1; tg += 16 * G) {
+    bf16x8 kf[G][KS];
+    unsigned okm[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = tg + 16 * g + (l & 15);
+      const int j = t < t1 ? row[t - t0] : -1;
+      const bool ok = j >= 0 && j < N;
+      bad |= (t < t1 && j >= N) ? 1 : 0;
+      okm[g] = static_cast<unsigned>(__ballot(ok)) & 0xFFFFu;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint4 u = ok ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j) * D +
+                                                              32 * ks + 8 * (l >> 4))
+                           : make_uint4(0, 0, 0, 0);
+        __builtin_memcpy(&kf[g][ks], &u, 16);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g][ks], qf[ks], c, 0, 0, 0);
+      if ((l & 15) == 0 && tg + 16 * g < t1) {
+        const int key = 4 * (l >> 4);
+        float4 v;
+        v.x = (okm[g] >> (key + 0)) & 1u ? c[0] * scale : -INFINITY;
+        v.y = (okm[g] >> (key + 1)) & 1u ? c[1] * scale : -INFINITY;
+        v.z = (okm[g] >> (key + 2)) & 1u ? c[2] * scale : -INFINITY;
+        v.w = (okm[g] >> (key + 3)) & 1u ? c[3] * scale : -INFINITY;
+        *reinterpret_cast<float4*>(slog + (tg - t0) + 16 * g + key) = v;
+      }
+    }
+  }
+}
 
-  const int g = l / LPR;           // row group of this lane
-  const int e0 = (l % LPR) * EPL;  // first element of this lane's slice
-  float qv[EPL];
-  Vec<T>::unpack(*reinterpret_cast<const uint4*>(Q + (hN + q) * D + e0), qv);
-  wave_sync();
-
-  int bad = 0;
-  // logits
-  for (int t0 = 0; t0 < k; t0 += RPI * kUnroll) {
-    uint4 kv[kUnroll];
+// Logits, fp32 I/O: each row is spread over LPR lanes, partial dots reduced
+// across them.
+template <int D>
+__device__ __forceinline__ void logits_f32(const float* __restrict__ qrow,
+                                           const float* __restrict__ K,
+                                           const int32_t* __restrict__ row, int t0, int t1,
+                                           int N, float scale, float* slog, int& bad) {
+  constexpr int EPL = 4, LPR = D / EPL, RPI = kWave / LPR;
+  const int l = lane_id();
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  const float4 q4 = *reinterpret_cast<const float4*>(qrow + e0);
+  for (int tb = t0; tb < t1; tb += RPI * kUnroll) {
+    float4 kv[kUnroll];
     bool ok[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * RPI + g;
-      const int j = t < k ? sidx[t] : -1;
+      const int t = tb + u * RPI + g;
+      const int j = t < t1 ? row[t - t0] : -1;
       ok[u] = j >= 0 && j < N;
-      bad |= (t < k && j >= N) ? 1 : 0;
-      kv[u] = ok[u] ? *reinterpret_cast<const uint4*>(Kh + static_cast<size_t>(j) * D + e0)
-                    : make_uint4(0, 0, 0, 0);
+      bad |= (t < t1 && j >= N) ? 1 : 0;
+      kv[u] = ok[u] ? *reinterpret_cast<const float4*>(K + static_cast<size_t>(j) * D + e0)
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      float kf[EPL];
-      Vec<T>::unpack(kv[u], kf);
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qv[e], kf[e], dot);
+      float dot = __builtin_fmaf(q4.w, kv[u].w, __builtin_fmaf(q4.z, kv[u].z,
+                  __builtin_fmaf(q4.y, kv[u].y, q4.x * kv[u].x)));
 #pragma unroll
       for (int o = LPR / 2; o > 0; o >>= 1) dot += __shfl_xor(dot, o, kWave);
-      const int t = t0 + u * RPI + g;
-      if ((l % LPR) == 0 && t < k) slog[t] = ok[u] ? dot * scale : -INFINITY;
+      const int t = tb + u * RPI + g;
+      if ((l % LPR) == 0 && t < t1) slog[t - t0] = ok[u] ? dot * scale : -INFINITY;
     }
   }
-  wave_sync();
-  float mx = -INFINITY;
-  for (int t = l; t < k; t += kWave) mx = fmaxf(mx, slog[t]);
-  mx = wave_max(mx);
-  T* out = O + (hN + q) * D;
-  if (bad) atomicOr(&g_index_error_flag, 1);
-  if (mx == -INFINITY) {  // no valid entry: zero output
-    float z[EPL];
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) z[e] = 0.0f;
-    if (g == 0) *reinterpret_cast<uint4*>(out + e0) = Vec<T>::pack(z);
-    return;
-  }
-  float sum = 0.0f;
-  for (int t = l; t < k; t += kWave) {
-    const float x = slog[t];
-    const float p = x == -INFINITY ? 0.0f : expf(x - mx);
-    slog[t] = p;
-    sum += p;
-  }
-  sum = wave_sum(sum);
-  wave_sync();
+}
 
-  float acc[EPL];
+template <typename T, int D>
+__device__ __forceinline__ void logits(const T* qrow, const T* K, const int32_t* row, int t0,
+                                       int t1, int N, float scale, float* slog, int& bad) {
+  if constexpr (sizeof(T) == 2)
+    logits_bf16<D>(qrow, K, row, t0, t1, N, scale, slog, bad);
+  else
+    logits_f32<D>(qrow, K, row, t0, t1, N, scale, slog, bad);
+}
+
+// Softmax numerators in place: slog[t] <- e^(slog[t] - m).  Returns m (-inf
+// when no entry is valid) and the sum.
+__device__ __forceinline__ float softmax_weights(float* slog, int n, float& sum) {
+  const int l = lane_id();
+  float mx = -INFINITY;
+  for (int t = l; t < n; t += kWave) mx = fmaxf(mx, slog[t]);
+  mx = wave_max(mx);
+  float s = 0.0f;
+  if (mx != -INFINITY) {
+    for (int t = l; t < n; t += kWave) {
+      const float x = slog[t];
+      const float p = x == -INFINITY ? 0.0f : expf(x - mx);
+      slog[t] = p;
+      s += p;
+    }
+  }
+  sum = wave_sum(s);
+  return mx;
+}
+
+// acc <- sum_t w_t V[j_t] over [t0, t1): each row spread over LPR lanes
+// (EPL elements each), partial sums reduced across the row groups; lanes of
+// group 0 end up holding elements e0 .. e0 + EPL - 1.
+template <typename T, int D>
+__device__ __forceinline__ void weighted_rows(const T* __restrict__ V,
+                                              const int32_t* __restrict__ row, int t0, int t1,
+                                              int N, const float* slog,
+                                              float (&acc)[Vec<T>::kElems]) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, RPI = kWave / LPR;
+  const int l = lane_id();
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
-  for (int t0 = 0; t0 < k; t0 += RPI * kUnroll) {
+  for (int tb = t0; tb < t1; tb += RPI * kUnroll) {
     uint4 vv[kUnroll];
     float wt[kUnroll];
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = t0 + u * RPI + g;
-      const int j = t < k ? sidx[t] : -1;
+      const int t = tb + u * RPI + g;
+      const int j = t < t1 ? row[t - t0] : -1;
       const bool ok = j >= 0 && j < N;
-      wt[u] = ok ? slog[t] : 0.0f;
-      vv[u] = ok ? *reinterpret_cast<const uint4*>(Vh + static_cast<size_t>(j) * D + e0)
+      wt[u] = ok ? slog[t - t0] : 0.0f;
+      vv[u] = ok ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j) * D + e0)
                  : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
@@ -171,12 +232,239 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
   }
-  if (g == 0) {
-    float r[EPL];
+}
+
+// Per-wave LDS of the gather kernels: the entries and the logits of up to k
+// entries (+16 slack each).
+__host__ __device__ constexpr int gather_slog_floats(int k) { return (k + 16 + 3) / 4 * 4; }
+__host__ __device__ constexpr int gather_wave_floats(int k) { return 2 * gather_slog_floats(k); }
+
+// Copies entries [t0, t1) of a global index row to the wave's LDS.
+__device__ __forceinline__ void stage_entries(const int32_t* __restrict__ row, int t0, int t1,
+                                              int* sidx) {
+  for (int t = t0 + lane_id(); t < t1; t += kWave) sidx[t - t0] = row[t];
+  wave_sync();
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void gather_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, int k, int N, float scale, T* __restrict__ O) {
+  constexpr int EPL = Vec<T>::kElems;
+  constexpr int LPR = D / EPL;
+  extern __shared__ float slog_all[];
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  float* slog = slog_all + w * gather_wave_floats(k);
+  int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
+  const int h = blockIdx.y;
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= N) return;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const T* Kh = K + hN * D;
+  const T* Vh = V + hN * D;
+  stage_entries(idx + (hN + q) * k, 0, k, sidx);
+  const int32_t* row = sidx;
+  int bad = 0;
+  logits<T, D>(Q + (hN + q) * D, Kh, row, 0, k, N, scale, slog, bad);
+  if (bad) atomicOr(&g_index_error_flag, 1);
+  wave_sync();
+  float sum;
+  const float mx = softmax_weights(slog, k, sum);
+  T* out = O + (hN + q) * D;
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float acc[EPL];
+  if (mx == -INFINITY) {  // no valid entry: zero output
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) r[e] = acc[e] / sum;
-    *reinterpret_cast<uint4*>(out + e0) = Vec<T>::pack(r);
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    if (g == 0) *reinterpret_cast<uint4*>(out + e0) = Vec<T>::pack(acc);
+    return;
   }
+  wave_sync();
+  weighted_rows<T, D>(Vh, row, 0, k, N, slog, acc);
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] /= sum;
+    *reinterpret_cast<uint4*>(out + e0) = Vec<T>::pack(acc);
+  }
+}
+
+// --------------------------------------------------------- split gather ---
+// The fused forward's idx rows are ascending, so the keys of a row that fall
+// in one key range form one contiguous segment of it.  A head's K and V rows
+// (64 MB at N = 128K, D = 128, bf16) are far larger than one XCD's 4 MB L2,
+// and a row is read by about k queries, so the gather splits the keys into
+// kGatherRanges ranges and orders its workgroups so that each XCD serves one
+// range at a time (workgroups are handed to the 8 XCDs in turn): an XCD's
+// working set is then one range, about its L2.  Each (query, range) writes an
+// online-softmax partial (max m, sum l of e^(x-m), unnormalised sum of
+// e^(x-m) V) and a merge combines the partials of a query.
+
+// seg[q][r] = first position of row q whose key is >= r * L, r = 0..R; the
+// rows hold valid keys ascending, then -1.
+__global__ __launch_bounds__(kThreads) void segment_kernel(const int32_t* __restrict__ idx,
+                                                           int k, int N, int L,
+                                                           int* __restrict__ seg) {
+  extern __shared__ int srow_all[];
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= N) return;
+  int* srow = srow_all + w * k;
+  const int32_t* row = idx + static_cast<size_t>(q) * k;
+  int n = 0;
+  for (int t = l; t < k; t += kWave) {
+    const int j = row[t];
+    srow[t] = j;
+    n += j >= 0 ? 1 : 0;
+  }
+  n = wave_sum_i(n);
+  wave_sync();
+  if (l <= kGatherRanges) {
+    const int x = l * L;
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (srow[mid] < x) lo = mid + 1; else hi = mid;
+    }
+    seg[static_cast<size_t>(q) * (kGatherRanges + 1) + l] = l == kGatherRanges ? n : lo;
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void gather_part_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, const int* __restrict__ seg, int k, int N, int QB,
+    float scale, float* __restrict__ part) {
+  constexpr int EPL = Vec<T>::kElems;
+  constexpr int LPR = D / EPL;
+  constexpr int R = kGatherRanges;
+  extern __shared__ float slog_all[];
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  // workgroup i -> (range, query block); consecutive workgroups land on
+  // consecutive XCDs, so XCD x serves ranges x, x + 8, ... one after another
+  const int i = static_cast<int>(blockIdx.x);
+  const int x = i % kXcds, rest = i / kXcds;
+  const int qb = rest % QB, r = rest / QB * kXcds + x;
+  const int q = qb * kWaves + w;
+  if (q >= N) return;
+  float* slog = slog_all + w * gather_wave_floats(k);
+  int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
+  const int s0 = seg[static_cast<size_t>(q) * (R + 1) + r];
+  const int s1 = seg[static_cast<size_t>(q) * (R + 1) + r + 1];
+  float* rec = part + (static_cast<size_t>(q) * R + r) * (D + 4);
+  if (s0 >= s1) {
+    if (l == 0) rec[0] = -INFINITY;   // empty: the merge skips it
+    return;
+  }
+  stage_entries(idx + static_cast<size_t>(q) * k, s0, s1, sidx);
+  const int32_t* row = sidx;
+  int bad = 0;
+  logits<T, D>(Q + static_cast<size_t>(q) * D, K, row, s0, s1, N, scale, slog, bad);
+  if (bad) atomicOr(&g_index_error_flag, 1);
+  wave_sync();
+  float sum;
+  const float mx = softmax_weights(slog, s1 - s0, sum);
+  if (mx == -INFINITY) {
+    if (l == 0) rec[0] = -INFINITY;
+    return;
+  }
+  wave_sync();
+  float acc[EPL];
+  weighted_rows<T, D>(V, row, s0, s1, N, slog, acc);
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  if (g == 0) {
+    float4* dst = reinterpret_cast<float4*>(rec + 4 + e0);
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) dst[e / 4] = make_float4(acc[e], acc[e + 1], acc[e + 2], acc[e + 3]);
+  }
+  if (l == 0) {
+    rec[0] = mx;
+    rec[1] = sum;
+  }
+}
+
+// O_q = sum_r e^(m_r - M) acc_r / sum_r e^(m_r - M) l_r, M = max_r m_r.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __restrict__ part,
+                                                                int N, T* __restrict__ O) {
+  constexpr int R = kGatherRanges;
+  constexpr int EPM = D / kWave;     // output elements per lane
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= N) return;
+  const float* recs = part + static_cast<size_t>(q) * R * (D + 4);
+  float m = -INFINITY, lsum = 0.0f;
+  if (l < R) {
+    m = recs[static_cast<size_t>(l) * (D + 4)];
+    if (m != -INFINITY) lsum = recs[static_cast<size_t>(l) * (D + 4) + 1];
+  }
+  const float M = wave_max(m);
+  T* out = O + static_cast<size_t>(q) * D + l * EPM;
+  float acc[EPM];
+#pragma unroll
+  for (int e = 0; e < EPM; ++e) acc[e] = 0.0f;
+  if (M == -INFINITY) {  // no valid entry: zero output
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(0.0f);
+    return;
+  }
+  const float wr = m == -INFINITY ? 0.0f : expf(m - M);
+  const float L = wave_sum(wr * lsum);
+#pragma unroll 4
+  for (int r = 0; r < R; ++r) {
+    const float wv = __shfl(wr, r, kWave);
+    if (wv != 0.0f) {
+      const float* a = recs + static_cast<size_t>(r) * (D + 4) + 4 + l * EPM;
+#pragma unroll
+      for (int e = 0; e < EPM; ++e) acc[e] = __builtin_fmaf(wv, a[e], acc[e]);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(acc[e] / L);
+}
+
+template <typename T, int D>
+hipError_t gather_split_t(const void* Q, const void* K, const void* V, const int32_t* idx,
+                          int k, int N, float scale, int* seg, float* part, void* O,
+                          hipStream_t s, const char* const names[3]) {
+  const int L = (N + kGatherRanges - 1) / kGatherRanges;
+  const int QB = (N + kWaves - 1) / kWaves;
+  const size_t lds = static_cast<size_t>(kWaves) * k * sizeof(int);
+  const size_t lds_part = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&segment_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(kWaves) * kKMax * 4);
+    if (e != hipSuccess) return e;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_part_kernel<T, D>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize,
+                            static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipError_t e;
+  prof_begin(names[0], s);
+  hipLaunchKernelGGL(segment_kernel, dim3(QB), dim3(kThreads), lds, s, idx, k, N, L, seg);
+  e = hipGetLastError();
+  prof_end(s);
+  if (e != hipSuccess) return e;
+  prof_begin(names[1], s);
+  hipLaunchKernelGGL((gather_part_kernel<T, D>), dim3(QB * kGatherRanges), dim3(kThreads), lds_part, s,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
+                     idx, seg, k, N, QB, scale, part);
+  e = hipGetLastError();
+  prof_end(s);
+  if (e != hipSuccess) return e;
+  prof_begin(names[2], s);
+  hipLaunchKernelGGL((gather_merge_kernel<T, D>), dim3(QB), dim3(kThreads), 0, s, part, N,
+                     static_cast<T*>(O));
+  e = hipGetLastError();
+  prof_end(s);
+  return e;
 }
 
 __global__ void band_kernel(long long total, int N, int w_left, int w_right,
@@ -195,12 +483,12 @@ __global__ void band_kernel(long long total, int N, int w_left, int w_right,
 template <typename T, int D>
 hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
                     int nheads, int N, float scale, void* O, hipStream_t s) {
-  const size_t lds = static_cast<size_t>(kWaves) * 2 * k * sizeof(int);
+  const size_t lds = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_kernel<T, D>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kWaves) * 2 * kKMax * 4);
+                                       static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
@@ -222,6 +510,20 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
   } else {
     if (D == 64) return gather_t<bf16_t, 64>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
     if (D == 128) return gather_t<bf16_t, 128>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
+                               int k, int N, int D, float softmax_scale, int dtype, int* seg,
+                               float* part, void* O, hipStream_t s) {
+  static const char* const names[3] = {"gather_seg", "gather", "gather_merge"};
+  if (dtype == 0) {
+    if (D == 64) return gather_split_t<float, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
+    if (D == 128) return gather_split_t<float, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
+  } else {
+    if (D == 64) return gather_split_t<bf16_t, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
+    if (D == 128) return gather_split_t<bf16_t, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
   }
   return hipErrorInvalidValue;
 }

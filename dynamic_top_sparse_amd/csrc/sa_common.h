@@ -9,6 +9,7 @@ namespace sa {
 typedef uint16_t bf16_t;  // storage of a bfloat16 value
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kWave = 64;
 

@@ -17,6 +17,7 @@ constexpr int kRowPad = 2048;           // N is padded to a multiple of this
 constexpr float kTauBeta = 1.5f;        // sample rank slack (see threshold kernel)
 constexpr int kFallbackBlocks = 256;    // workgroups of the exact fallback
 constexpr int kKMax = 2048;             // largest supported k
+constexpr int kGatherRanges = 16;       // key ranges of the split gather (a multiple of 8)
 constexpr int kRetrySplit = 8;          // key segments of the retry filter (capH is a multiple of 64)
 
 // Byte offsets of one head chunk's buffers inside the workspace.
@@ -32,9 +33,10 @@ struct Plan {
   int NB;         // block maxima per query: 2 * ceil(Ns / 32)
   int capH;       // candidate capacity of one query half
   int with_idx;   // room for idx rows of the chunk
+  int gsplit;     // the fused forward gathers by key range (N > 8192)
   size_t off_hdr, off_qlo32, off_klo32, off_qlo16, off_klo16, off_ksamp, off_qstat,
       off_kstat, off_bm, off_tau, off_thr, off_cand, off_cnt, off_rcnt, off_rlist, off_rcount, off_fblist,
-      off_fbscratch, off_idx, total;
+      off_fbscratch, off_idx, off_seg, off_part, total;
 };
 
 // Fills every field from the arguments and heads_per_chunk; returns false
@@ -90,6 +92,8 @@ struct Bufs {
   int* fblist;          // queries queued for the exact fallback
   float* fbscratch;     // [kFallbackBlocks][Npad] exact scores
   int32_t* idx;         // optional idx rows [hc][N][k]
+  int* seg;             // split gather, one head: segment starts [Npad][kGatherRanges + 1]
+  float* part;          // split gather, one head: partials [Npad][kGatherRanges][D + 4]
 };
 Bufs bufs_of(const Plan& p, void* ws);
 
@@ -116,6 +120,10 @@ hipError_t launch_dump(const Plan& p, const Bufs& b, int nh, float score_scale,
 hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                          int k, int nheads, int N, int D, float softmax_scale, int dtype,
                          void* O, hipStream_t s);
+// Split gather of one head whose idx rows are ascending (the fused forward's).
+hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
+                               int k, int N, int D, float softmax_scale, int dtype, int* seg,
+                               float* part, void* O, hipStream_t s);
 hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
                        hipStream_t s);
 

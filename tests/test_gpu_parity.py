@@ -244,6 +244,17 @@ def _ranges(N, causal):
     return r
 
 
+@pytest.mark.parametrize("dtype,D,causal", [("f32", 64, False), ("bf16", 128, False),
+                                             ("bf16", 128, True)])
+def test_fused_forward_key_range_gather(dtype, D, causal):
+    """Past N = 8192 the fused forward gathers by key range (partials per
+    range, then a merge); ragged N, empty ranges and, causally, rows whose
+    keys all fall in the first ranges."""
+    w = W.get("bf16_32k", N=8200, H=2, D=D, dtype=dtype, d_proj=64 if D == 128 else 16,
+              k=64, causal=causal)
+    run_case(w, seed=5, rows=[(0, 300), (4000, 200), (8000, 200)])
+
+
 @pytest.mark.parametrize("name", ["bf16_32k", "headline_128k", "causal_mixture"])
 def test_full_size_workloads_sampled_rows(name):
     w = W.get(name)
