@@ -11,6 +11,17 @@ eff_tflops counts algorithmic flops only:
   F_proj = 4·B·H·N·D·d_proj, F_score = 2·d_proj·(pairs), F_gather = 4·D·Σk_i.
 Per-kernel times come from HIP events the library records around each of its
 launches on the launch stream (sparse_attn_profile_enable).
+
+roofline: the kernel with the largest time per step, its algorithmic amount
+per launch over its average launch time:
+  filter   2·d_proj·pairs flops (16-bit MFMA, dense peak 2516.6 TFLOP/s)
+  gather   K and V rows of the kept keys + the idx row + the q row, bytes
+           (HBM peak 8 TB/s; the partial kernel of the key-range split)
+  rerank   candidate entries (8 B) + idx row + exact-rescored k_low rows
+traffic (HBM bytes per launch of that kernel) is taken from the rocprofv3
+FETCH_SIZE / WRITE_SIZE readings recorded in TRAFFIC below, scaled by what the
+same counters read for a plain 1 GiB copy, and only while the kernel's source
+file is unchanged since (else null).
 """
 from __future__ import annotations
 
@@ -26,6 +37,32 @@ sys.path.insert(0, ROOT)
 METRIC = "queries/s + eff. TFLOP/s, top-k sparse attn fwd, N=128K H=32 D=128 k=512"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+# rocprofv3 --pmc readings of the headline command (see profiles/), per launch
+# of the kernel, already scaled by the plain-copy factors (FETCH_SIZE reads half
+# a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
+# kernel's source file when the counters were taken.
+TRAFFIC = {
+    # profiles/headline_128k_hbm_traffic.md
+    "filter": {"fetch_bytes": 12.455e9, "write_bytes": 27.362e9,
+               "src": "e8285951b369366e6329c3b8c55c4c419de5d389b041557f5e73d56419d37fcd"},
+    "gather": {"fetch_bytes": 3.399e9, "write_bytes": 1.141e9,
+               "src": "ed1430e282f23960857216c8aaa1bc621732143821619c37b9b6e55536df13c7"},
+    "rerank": {"fetch_bytes": 8.952e9, "write_bytes": 1.345e9,
+               "src": "5b5eff95582079b9f0e9eb99cccd62031f2885d5175c2c950eca4dd469dd3feb"},
+}
+KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
+
+
+def source_sha(kernel: str):
+    import hashlib
+    name = KERNEL_SOURCE.get(kernel)
+    if name is None:
+        return None
+    path = os.path.join(ROOT, "dynamic_top_sparse_amd", "csrc", name)
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
 
 
 def algorithmic(w) -> dict:
@@ -44,11 +81,13 @@ def algorithmic(w) -> dict:
         "F_gather": 4.0 * D * sum_k * BH,
         # per head: K and V rows of every kept key, the idx row, q in, O out
         "gather_bytes_per_head": float(sum_k * 2 * D * e + N * k * 4 + N * 2 * D * e),
+        # the same without O (written by the merge of the key-range split)
+        "gather_part_bytes_per_head": float(sum_k * 2 * D * e + N * k * 4 + N * D * e),
         "pairs_per_head": float(pairs),
     }
 
 
-def cpu_baseline(x, w, target_s: float = 15.0) -> dict:
+def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: query rows of head (0, 0), including that head's projections."""
     import numpy as np
@@ -154,31 +193,42 @@ def main() -> int:
     per_step = {n: d["ms_total"] / args.steps for n, d in kern.items()}
     scorer_names = ("init", "project", "pack", "sample", "threshold", "filter", "rerank",
                     "filter_retry", "rerank_retry", "fallback")
+    gather_names = ("gather_seg", "gather", "gather_merge")
     t_scorer = sum(per_step.get(n, 0.0) for n in scorer_names) / 1e3
-    t_gather = per_step.get("gather", 0.0) / 1e3
+    t_gather = sum(per_step.get(n, 0.0) for n in gather_names) / 1e3
 
-    heads_per_launch = None
-    n_gather = kern.get("gather", {}).get("launches", 0)
-    if n_gather:
-        heads_per_launch = (w.B * w.H * args.steps) / n_gather
+    n_filter = kern.get("filter", {}).get("launches", 0)
+    heads_per_chunk = (w.B * w.H * args.steps) / n_filter if n_filter else None
     # roofline of the kernel with the largest time per step
     dom = max(per_step, key=per_step.get)
     avg_launch_s = kern[dom]["ms_total"] / kern[dom]["launches"] / 1e3
-    launches_per_step = kern[dom]["launches"] / args.steps
-    heads = w.B * w.H / launches_per_step
+    heads = w.B * w.H * args.steps / kern[dom]["launches"]
     if dom == "filter":
         amount = 2.0 * w.d_proj * a["pairs_per_head"] * heads
         roof = {"kernel": dom, "bound": "mfma", "achieved": amount / avg_launch_s / 1e12,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
         roof["algorithmic_per_launch"] = f"{amount:.4g} flop (2*d_proj*pairs, {heads:g} heads)"
-    else:
-        amount = a["gather_bytes_per_head"] * heads
+    elif dom == "rerank":
+        nq = w.N * heads
+        cand = stats["candidates"] / max(stats["queries"], 1)
+        resc = stats["rescored"] / max(stats["queries"], 1)
+        amount = nq * (8.0 * cand + 4.0 * w.k + 4.0 * w.d_proj * resc)
         roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_launch_s / 1e9,
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
-        roof["algorithmic_per_launch"] = (f"{amount:.4g} B (K,V rows of kept keys + idx + q + o, "
+        roof["algorithmic_per_launch"] = (f"{amount:.4g} B (candidates, idx rows, rescored "
+                                          f"k_low rows; {heads:g} heads)")
+    else:
+        per_head = a["gather_part_bytes_per_head"] if "gather_merge" in per_step \
+            else a["gather_bytes_per_head"]
+        amount = per_head * heads
+        roof = {"kernel": dom, "bound": "hbm", "achieved": amount / avg_launch_s / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+        roof["algorithmic_per_launch"] = (f"{amount:.4g} B (K,V rows of kept keys + idx + q, "
                                           f"{heads:g} heads)")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    tr = TRAFFIC.get(dom)
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr and \
+        tr.get("src") == source_sha(dom) else None
     roof["avg_launch_ms"] = avg_launch_s * 1e3
 
     result = {
@@ -196,12 +246,13 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "d_proj": w.d_proj, "k": w.k, "causal": w.causal, "dist": w.dist,
-                   "seed": W.default_seed(), "heads_per_chunk": heads_per_launch},
+                   "seed": W.default_seed(), "heads_per_chunk": heads_per_chunk},
         "eff_tflops": flops / (ms_step / 1e3) / 1e12,
         "scorer_frac_of_bf16_peak": ((a["F_proj"] + a["F_score"]) / t_scorer / 1e12
                                      / PEAK_BF16_TFLOPS) if t_scorer else None,
         "gather_frac_of_hbm_peak": ((a["gather_bytes_per_head"] * w.B * w.H) / t_gather / 1e9
                                     / PEAK_HBM_GBS) if t_gather else None,
+        "gather_stage_ms": t_gather * 1e3,
         "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
                                                                   key=lambda kv: -kv[1])},
         "selection": {"candidates_per_query": stats["candidates"] / max(stats["queries"], 1),
