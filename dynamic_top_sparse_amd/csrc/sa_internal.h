@@ -17,7 +17,7 @@ constexpr int kRowPad = 2048;           // N is padded to a multiple of this
 constexpr float kTauBeta = 1.5f;        // sample rank slack (see threshold kernel)
 constexpr int kFallbackBlocks = 256;    // workgroups of the exact fallback
 constexpr int kKMax = 2048;             // largest supported k
-constexpr int kGatherRanges = 16;       // key ranges of the split gather (a multiple of 8)
+constexpr int kGatherRanges = 8;        // key ranges of the split gather (a multiple of 8)
 constexpr int kRetrySplit = 8;          // key segments of the retry filter (capH is a multiple of 64)
 
 // Byte offsets of one head chunk's buffers inside the workspace.
