@@ -143,9 +143,10 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   while (p.sstride < kMaxSampleStride && 2 * p.sstride * 32 <= kTauBeta * k) p.sstride *= 2;
   p.Ns = (N + p.sstride - 1) / p.sstride;
   p.Nspad = p.Npad / p.sstride;
-  // two query halves of capH candidates each (1.5 k, at least 256, at most
-  // 2048); a list that overflows is filtered again with a proven threshold
-  p.capH = std::min(2048, round_up(std::max(3 * k / 2, 256), 64));
+  // two query halves of capH candidates each (1.25 k, at least 256, at most
+  // 2048; about 0.85 k land in a half at the headline size); a list that
+  // overflows is filtered again with a proven threshold
+  p.capH = std::min(2048, round_up(std::max(5 * k / 4, 256), 64));
   // block maxima per query: fewer than 8r + 40 (the block size keeps under
   // 8r blocks, plus tile rounding), with r <= beta*k/s + beta*k/n + 1 for the
   // rows that use a threshold (n > 2 capH - 64 valid keys)

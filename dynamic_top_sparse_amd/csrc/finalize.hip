@@ -319,7 +319,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     {
       const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
       const uint2* list1 = list0 + capH;
-      #pragma unroll 8
+      #pragma unroll 16
       for (int i = l; i < c; i += kWave) {
         const uint2 e = i < c0 ? list0[i] : list1[i - c0];
         const uint32_t key = order_key((__uint_as_float(e.y) + tv) * f);
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     {
       constexpr int G = DP / 4;
       constexpr int KPI = kWave / G;     // keys per pass
-      constexpr int UNR = 4;             // passes in flight
+      constexpr int UNR = 16;            // passes in flight (64 keys at d_proj 64)
       const int g = l % G, grp = l / G;
       const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
       #pragma unroll 1
@@ -590,7 +590,8 @@ template <int DP>
 hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t* idx,
                       bool retry, hipStream_t s) {
   // the uncertain band is ~8x narrower with fp16 filter operands than bf16
-  const int ucap = p.filt ? 512 : 256;
+  // (about 37 and 280 keys at the headline size)
+  const int ucap = p.filt ? 512 : 128;
   const size_t per_wave = rerank_lds_per_wave(2 * p.capH, ucap);
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);

@@ -42,12 +42,14 @@ struct Tile {
 };
 
 // Swizzled position (in 16-byte units) of unit u of key row `key` within a
-// staged chunk: the XOR spreads the 32 rows an A-fragment read touches over
-// the LDS banks.
+// staged chunk.  gfx950's LDS serves a 128-bit read 16 lanes at a time over
+// 64 banks (256 bytes), i.e. 16 keys at one unit: XOR-ing the unit with bits
+// 1..3 of the key puts those 16 rows of 128 bytes on 16 distinct bank groups
+// (the bank-conflict counter reads 0).
 template <int DP>
 __device__ __forceinline__ int lds_unit(int key, int u) {
   constexpr int U = Tile<DP>::kUnits;
-  return key * U + (u ^ (key & (U - 1)));
+  return key * U + (u ^ ((key >> 1) & (U - 1)));
 }
 
 // A thread's share of a staged key chunk is held in a plain register array
@@ -490,6 +492,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     chunk_load<DP>(regs, kh, ch0 * kKeysPerChunk);
     chunk_store<DP>(regs, lds + (ch0 & 1) * Tile<DP>::kChunkUnits);
   }
+  // Retire every load made so far (query fragments, thresholds): otherwise
+  // the loop keeps waits for them on the memory counter, which stores and
+  // the chunk prefetch share, and the MFMAs stall on those instead.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int ch = ch0; ch < nchunks; ++ch) {
     const bool more = ch + 1 < nchunks;
