@@ -2,9 +2,10 @@
 // chunk (page "mhpq.cn/news/1098205", §2.2: the scorer's q_proj / k_proj map
 // each head's vectors to d_proj dimensions).
 //
-// Per row it writes the fp32 projection (accumulated with FMAs in ascending
-// order of the model dimension, a fixed order that every exact score relies
-// on) and, for the filter, a 16-bit copy scaled by a power of two (one
+// Per row it writes the fp32 projection (bf16 rows: products on the bf16
+// MFMA, exact in fp32, summed in fp32; fp32 rows: FMAs in ascending order of
+// the model dimension) -- the values every exact score is computed from --
+// and, for the filter, a 16-bit copy scaled by a power of two (one
 // exponent per query row, one per key head), plus the norms that bound the
 // filter's error: ||x_low|| and ||x_low - x~|| (x~ the 16-bit row back in
 // true units), both rounded up.  Keys need their head's exponent before they
@@ -48,35 +49,70 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
   const T* Xh = X + static_cast<size_t>(h) * N * D;
 
   for (int e = tid; e < D * DP; e += kThreads) sP[e] = io<T>::to_f32(P[e]);
-  for (int e = tid; e < kRows * D; e += kThreads) {
-    const int r = e / D, d = e % D;
-    const int row = row0 + r;
-    sX[r * (D + 1) + d] = (row < N) ? io<T>::to_f32(Xh[static_cast<size_t>(row) * D + d]) : 0.0f;
-  }
-  __syncthreads();
-
   constexpr int kGroups = kThreads / DP;    // row groups
   constexpr int kRowsPerThread = kRows / kGroups;
   const int c = tid % DP;
   const int g = tid / DP;
-  float acc[kRowsPerThread];
-#pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) acc[i] = 0.0f;
-  for (int d = 0; d < D; ++d) {
-    const float pv = sP[d * DP + c];
-#pragma unroll
-    for (int i = 0; i < kRowsPerThread; ++i)
-      acc[i] = __builtin_fmaf(sX[(g + i * kGroups) * (D + 1) + d], pv, acc[i]);
-  }
   const size_t base = static_cast<size_t>(h) * Npad;
-  __syncthreads();  // every thread is done reading sX
+  // bf16 rows: 32x32 output tiles on the bf16 MFMA (the products are exact in
+  // fp32, the sums fp32); fp32 rows: FMAs in ascending order of d.
+  constexpr bool kMfma = sizeof(T) == 2 && DP % 32 == 0;
+  if constexpr (kMfma) {
+    __syncthreads();
+    const int w = tid >> 6, l = tid & 63;
+    constexpr int CT = DP / 32;              // column tiles
+    for (int t = w; t < (kRows / 32) * CT; t += kThreads / 64) {
+      const int rt = t / CT, ct = t % CT;
+      const int arow = row0 + 32 * rt + (l & 31);
+      f32x16 acc = {};
 #pragma unroll
-  for (int i = 0; i < kRowsPerThread; ++i) {
-    const int r = g + i * kGroups;
-    const int row = row0 + r;
-    const float v = (row < N) ? acc[i] : 0.0f;
-    lo32[(base + row) * DP + c] = v;
-    sLo[r * (DP + 1) + c] = v;
+      for (int ks = 0; ks < D / 16; ++ks) {
+        const int k0 = 16 * ks + 8 * (l >> 5);
+        uint4 ua = make_uint4(0, 0, 0, 0);
+        if (arow < N) ua = *reinterpret_cast<const uint4*>(Xh + static_cast<size_t>(arow) * D + k0);
+        bf16x8 va, vb;
+        __builtin_memcpy(&va, &ua, 16);
+        uint16_t pb[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) pb[i] = f32_to_bf16(sP[(k0 + i) * DP + 32 * ct + (l & 31)]);
+        __builtin_memcpy(&vb, pb, 16);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
+      }
+      // lane l, register r: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * rt + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
+        const int cc = 32 * ct + (l & 31);
+        const float v = (row0 + rr < N) ? acc[r] : 0.0f;
+        lo32[(base + row0 + rr) * DP + cc] = v;
+        sLo[rr * (DP + 1) + cc] = v;
+      }
+    }
+  } else {
+    for (int e = tid; e < kRows * D; e += kThreads) {
+      const int r = e / D, d = e % D;
+      const int row = row0 + r;
+      sX[r * (D + 1) + d] = (row < N) ? io<T>::to_f32(Xh[static_cast<size_t>(row) * D + d]) : 0.0f;
+    }
+    __syncthreads();
+    float acc[kRowsPerThread];
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) acc[i] = 0.0f;
+    for (int d = 0; d < D; ++d) {
+      const float pv = sP[d * DP + c];
+#pragma unroll
+      for (int i = 0; i < kRowsPerThread; ++i)
+        acc[i] = __builtin_fmaf(sX[(g + i * kGroups) * (D + 1) + d], pv, acc[i]);
+    }
+    __syncthreads();  // every thread is done reading sX
+#pragma unroll
+    for (int i = 0; i < kRowsPerThread; ++i) {
+      const int r = g + i * kGroups;
+      const int row = row0 + r;
+      const float v = (row < N) ? acc[i] : 0.0f;
+      lo32[(base + row) * DP + c] = v;
+      sLo[r * (DP + 1) + c] = v;
+    }
   }
   __syncthreads();
   if (tid < kRows) {
