@@ -322,45 +322,53 @@ __device__ __forceinline__ unsigned valid_rows(int lim) {
   return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
 }
 
+__device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
+
 // Appends the passing accumulators of one 32-query block to the lane's list,
 // in key order.  Accumulators start at -thr, so hits are exactly the
-// non-negative ones: a lane with a single hit (the common case) finds its
-// value as the maximum of its 16 accumulators.  A lane cannot index its
-// registers by a run-time number, so the rare lane with more hits (or on an
-// edge tile, where masked rows may also be non-negative) parks its values in
-// its own LDS column (stash[r][lane]: conflict-free) and reads them back.
+// non-negative ones, and as signed integers their bit patterns are the
+// largest: a lane with a single hit (the common case) finds its value as the
+// integer maximum of its 16 accumulators (eight three-way maxima).  A lane
+// cannot index its registers by a run-time number, so the rarer lane with
+// more hits (or on an edge tile, where masked rows may also be non-negative)
+// parks its values in its own LDS column (stash[r][lane]: conflict-free) and
+// reads them back.
 __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, bool edge,
                                            float* stash, unsigned jbase, uint2* lst,
                                            unsigned& count, unsigned last) {
-  if (bits == 0u) return;
-  if (!edge && (bits & (bits - 1u)) == 0u) {
-    float v = a[0];
+  const unsigned nb = static_cast<unsigned>(__builtin_popcount(bits));
+  if (!edge && nb == 1u) {
+    int x[16];
 #pragma unroll
-    for (int r = 1; r < 16; ++r) v = fmaxf(v, a[r]);
+    for (int r = 0; r < 16; ++r) x[r] = __float_as_int(a[r]);
+    const int m = imax3(imax3(imax3(x[0], x[1], x[2]), imax3(x[3], x[4], x[5]),
+                              imax3(x[6], x[7], x[8])),
+                        imax3(x[9], x[10], x[11]), imax3(x[12], x[13], imax3(x[14], x[15], x[15])));
     const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
     // accumulator r holds key row r + (r & 12) (+4 in the upper half-wave)
-    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
+    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), static_cast<unsigned>(m));
     ++count;
-    return;
   }
+  if (nb > 1u || (edge && nb != 0u)) {
 #pragma unroll
-  for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
-  do {
-    const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
-    bits &= bits - 1u;
-    const float v = stash[b * kThreads];
-    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
-    ++count;
-  } while (bits);
+    for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
+    do {
+      const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
+      bits &= bits - 1u;
+      const float v = stash[b * kThreads];
+      lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
+      ++count;
+    } while (bits);
+  }
 }
 
-template <int DP, typename F>
+template <int DP, typename F, int mode>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void filter_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ k16,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ tau, float* __restrict__ thr_out, int N, int Npad, int causal,
     int capH, float scale, const int* __restrict__ qlist, const int* __restrict__ qlist_count,
-    uint2* __restrict__ cand, int* __restrict__ cnt, int* __restrict__ rcnt, int mode,
+    uint2* __restrict__ cand, int* __restrict__ cnt, int* __restrict__ rcnt,
     WsHeader* __restrict__ hdr) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   __shared__ float stash_all[16 * kThreads];   // 16 scores per lane, [16][threads]
@@ -481,6 +489,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     last[bb] = static_cast<unsigned>(capH - 1 - off);
   }
   unsigned count[2] = {0u, 0u};
+  // all-pass lists take every valid key: their hit mask is all ones
+  const unsigned apm[2] = {all_pass[0] ? 0xFFFFu : 0u, all_pass[1] ? 0xFFFFu : 0u};
 
   // this workgroup's chunks: all of [0, kend), or its segment of them
   const int nch_all = (kend + kKeysPerChunk - 1) / kKeysPerChunk;
@@ -502,31 +512,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (more) chunk_load<DP>(regs, kh, (ch + 1) * kKeysPerChunk);   // in flight during this chunk
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
     const int ntiles = min(kKeysPerChunk / 32, (kend - ch * kKeysPerChunk + 31) / 32);
-    // one tile's accumulators at a time: the registers this saves give three
-    // waves per SIMD, which overlap one wave's filtering with another's MFMAs
-    // better than a second set of accumulators within a wave does
+    // The two query blocks' MFMA chains alternate with the other block's hit
+    // handling, so a wave keeps the matrix core busy while its VALU work runs
+    // (one set of accumulators per block: three waves per SIMD still fit).
+    f32x16 a0 = tile_scores_c<DP, F>(buf, 0, b0, cinit[0]);
 #pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       if (tt >= ntiles) break;
-      f32x16 acc[2][2];
-      acc[tt & 1][0] = tile_scores_c<DP, F>(buf, tt, b0, cinit[0]);
-      acc[tt & 1][1] = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
+      const f32x16 a1 = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
       const int tbase = ch * kKeysPerChunk + tt * 32;
       const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
-      unsigned bits0 = all_pass[0] ? 0xFFFFu : (~miss_bits(acc[tt & 1][0]) & 0xFFFFu);
-      unsigned bits1 = all_pass[1] ? 0xFFFFu : (~miss_bits(acc[tt & 1][1]) & 0xFFFFu);
-      if (edge) {
-        bits0 &= valid_rows((causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase));
-        bits1 &= valid_rows((causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase));
-      }
-      if (mode == 1) {
+      unsigned bits0 = (~miss_bits(a0) & 0xFFFFu) | apm[0];
+      if (edge) bits0 &= valid_rows((causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase));
+      if (mode == 1)
         count[0] += __builtin_popcount(bits0);
+      else
+        drain_hits(a0, bits0, edge, stash, jbase, list[0], count[0], last[0]);
+      if (tt + 1 < ntiles) a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
+      unsigned bits1 = (~miss_bits(a1) & 0xFFFFu) | apm[1];
+      if (edge) bits1 &= valid_rows((causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase));
+      if (mode == 1)
         count[1] += __builtin_popcount(bits1);
-      } else {
-        drain_hits(acc[tt & 1][0], bits0, edge, stash, jbase, list[0], count[0], last[0]);
-        drain_hits(acc[tt & 1][1], bits1, edge, stash, jbase, list[1], count[1], last[1]);
-      }
+      else
+        drain_hits(a1, bits1, edge, stash, jbase, list[1], count[1], last[1]);
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
@@ -561,16 +570,22 @@ template <int DP, typename F>
 hipError_t filter_t(const Plan& p, const Bufs& b, int nh, float scale, bool retry,
                     hipStream_t s) {
   const dim3 grid(p.Npad / kQueriesPerBlock * (retry ? kRetrySplit : 1), nh);
-  for (int mode = retry ? 1 : 0; mode <= (retry ? 2 : 0); ++mode) {
-    hipLaunchKernelGGL((filter_kernel<DP, F>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
+  if (!retry) {
+    hipLaunchKernelGGL((filter_kernel<DP, F, 0>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
                        b.qstat, b.kstat, b.tau, b.thr, p.N, p.Npad, p.causal, p.capH, scale,
-                       retry ? b.rlist : static_cast<int*>(nullptr),
-                       retry ? b.rcount : static_cast<int*>(nullptr), b.cand, b.cnt, b.rcnt,
-                       mode, b.hdr);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+                       static_cast<int*>(nullptr), static_cast<int*>(nullptr), b.cand, b.cnt,
+                       b.rcnt, b.hdr);
+    return hipGetLastError();
   }
-  return hipSuccess;
+  hipLaunchKernelGGL((filter_kernel<DP, F, 1>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
+                     b.qstat, b.kstat, b.tau, b.thr, p.N, p.Npad, p.causal, p.capH, scale, b.rlist,
+                     b.rcount, b.cand, b.cnt, b.rcnt, b.hdr);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((filter_kernel<DP, F, 2>), grid, dim3(kThreads), 0, s, b.qlo16, b.klo16,
+                     b.qstat, b.kstat, b.tau, b.thr, p.N, p.Npad, p.causal, p.capH, scale, b.rlist,
+                     b.rcount, b.cand, b.cnt, b.rcnt, b.hdr);
+  return hipGetLastError();
 }
 
 template <typename F>
