@@ -74,61 +74,61 @@ template <> struct Vec<bf16_t> {
 // logits go to the wave's LDS buffer `slog` (index t - t0; room for t1 - t0
 // rounded up to 16), then become the unnormalised weights e^(x - m).
 
-// Logits, bf16 I/O: q.K[j] on the 16x16x32 bf16 MFMA, 16 keys per group.  A
-// = the group's K rows (lane l: row l % 16, dims 32 ks + 8 (l / 16) .. +8), B =
-// the query in every column, so each column holds the 16 dot products (lane
-// l: keys 4 (l / 16) + r).  bf16 products are exact in fp32 and accumulate
-// in fp32, as on the VALU; the MFMA only saves the per-row reductions.
+// Sum over the LPR consecutive lanes that hold one row (LPR = 8 or 16: the
+// group lies inside one DPP row, and every lane of it gets the sum).
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (LPR == 16) v += dpp_f<kDppMirror>(v);
+  return v;
+}
+
+// Logits, bf16 I/O: rows are read as the V rows are (LPR lanes x 16 bytes
+// per row, RPI whole rows per load instruction), so each load touches whole
+// 128-byte lines; the vector memory path, not the arithmetic, bounds the
+// gather.  Each lane forms its 8 products with four bf16 dot2 instructions
+// (bf16 products are exact in fp32; the sums are fp32) and the row's lanes
+// add their partial sums.
 template <int D>
 __device__ __forceinline__ void logits_bf16(const bf16_t* __restrict__ qrow,
                                             const bf16_t* __restrict__ K,
                                             const int32_t* __restrict__ row, int t0, int t1,
                                             int N, float scale, float* slog, int& bad) {
-  constexpr int KS = D / 32;
-  constexpr int G = 2;                       // key groups in flight
+  constexpr int EPL = 8, LPR = D / EPL, RPI = kWave / LPR;
   const int l = lane_id();
-  bf16x8 qf[KS];
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + e0);
+  bf16x2 qp[4];
+  __builtin_memcpy(qp, &q4, 16);
+  for (int tb = t0; tb < t1; tb += RPI * kUnroll) {
+    const int nu = min(kUnroll, (t1 - tb + RPI - 1) / RPI);   // loads holding rows (uniform)
+    uint4 kv[kUnroll];
+    bool ok[kUnroll];
 #pragma unroll
-  for (int ks = 0; ks < KS; ++ks) {
-    const uint4 u = *reinterpret_cast<const uint4*>(qrow + 32 * ks + 8 * (l >> 4));
-    __builtin_memcpy(&qf[ks], &u, 16);
-  }
-  for (int tg = t0; tg < t1; tg += 16 * G) {
-    bf16x8 kf[G][KS];
-    unsigned okm[G];
-    const int ng = min(G, (t1 - tg + 15) / 16);   // groups holding entries (uniform)
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g >= ng) break;
-      const int t = tg + 16 * g + (l & 15);
-      const int j = t < t1 ? row[t - t0] : -1;
-      const bool ok = j >= 0 && j < N;
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const int jr = row[t - t0];                  // t - t0 < t1 - t0 + RPI: inside the slack
+      const int j = t < t1 ? jr : -1;
+      ok[u] = j >= 0 && j < N;
       bad |= (t < t1 && j >= N) ? 1 : 0;
-      okm[g] = static_cast<unsigned>(__ballot(ok)) & 0xFFFFu;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint4 u = ok ? *reinterpret_cast<const uint4*>(K + static_cast<size_t>(j) * D +
-                                                              32 * ks + 8 * (l >> 4))
-                           : make_uint4(0, 0, 0, 0);
-        __builtin_memcpy(&kf[g][ks], &u, 16);
-      }
+      // row 0 stands in for an invalid entry, whose logit is -inf below
+      kv[u] = *reinterpret_cast<const uint4*>(K + static_cast<size_t>(ok[u] ? j : 0) * D + e0);
     }
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      if (g >= ng) break;
-      f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      bf16x2 kp[4];
+      __builtin_memcpy(kp, &kv[u], 16);
+      float dot = 0.0f;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[g][ks], qf[ks], c, 0, 0, 0);
-      if ((l & 15) == 0) {
-        const int key = 4 * (l >> 4);
-        float4 v;
-        v.x = (okm[g] >> (key + 0)) & 1u ? c[0] * scale : -INFINITY;
-        v.y = (okm[g] >> (key + 1)) & 1u ? c[1] * scale : -INFINITY;
-        v.z = (okm[g] >> (key + 2)) & 1u ? c[2] * scale : -INFINITY;
-        v.w = (okm[g] >> (key + 3)) & 1u ? c[3] * scale : -INFINITY;
-        *reinterpret_cast<float4*>(slog + (tg - t0) + 16 * g + key) = v;
-      }
+      for (int i = 0; i < 4; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[i], dot, false);
+      dot = group_sum<LPR>(dot);
+      const int t = tb + u * RPI + g;
+      if ((l % LPR) == 0 && t < t1) slog[t - t0] = ok[u] ? dot * scale : -INFINITY;
     }
   }
 }
@@ -152,11 +152,11 @@ __device__ __forceinline__ void logits_f32(const float* __restrict__ qrow,
     for (int u = 0; u < kUnroll; ++u) {
       if (u >= nu) break;
       const int t = tb + u * RPI + g;
-      const int j = t < t1 ? row[t - t0] : -1;
+      const int jr = row[t - t0];                  // t - t0 < t1 - t0 + RPI: inside the slack
+      const int j = t < t1 ? jr : -1;
       ok[u] = j >= 0 && j < N;
       bad |= (t < t1 && j >= N) ? 1 : 0;
-      kv[u] = ok[u] ? *reinterpret_cast<const float4*>(K + static_cast<size_t>(j) * D + e0)
-                    : make_float4(0.f, 0.f, 0.f, 0.f);
+      kv[u] = *reinterpret_cast<const float4*>(K + static_cast<size_t>(ok[u] ? j : 0) * D + e0);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -180,7 +180,13 @@ __device__ __forceinline__ void logits(const T* qrow, const T* K, const int32_t*
     logits_f32<D>(qrow, K, row, t0, t1, N, scale, slog, bad);
 }
 
-// Softmax numerators in place: slog[t] <- e^(slog[t] - m).  Returns m (-inf
+// Logits are kept in base 2: the kernels scale the dot products by
+// softmax_scale * log2(e), so e^(x - m) of the natural-base logits is
+// 2^(x' - m') of the stored ones, one hardware exp2 each (a -inf logit gives
+// exactly 0).
+constexpr float kLog2e = 1.44269504088896340736f;
+
+// Softmax numerators in place: slog[t] <- 2^(slog[t] - m).  Returns m (-inf
 // when no entry is valid) and the sum.
 __device__ __forceinline__ float softmax_weights(float* slog, int n, float& sum) {
   const int l = lane_id();
@@ -191,7 +197,7 @@ __device__ __forceinline__ float softmax_weights(float* slog, int n, float& sum)
   if (mx != -INFINITY) {
     for (int t = l; t < n; t += kWave) {
       const float x = slog[t];
-      const float p = x == -INFINITY ? 0.0f : expf(x - mx);
+      const float p = __builtin_amdgcn_exp2f(x - mx);
       slog[t] = p;
       s += p;
     }
@@ -221,11 +227,12 @@ __device__ __forceinline__ void weighted_rows(const T* __restrict__ V,
     for (int u = 0; u < kUnroll; ++u) {
       if (u >= nu) break;
       const int t = tb + u * RPI + g;
-      const int j = t < t1 ? row[t - t0] : -1;
+      const int jr = row[t - t0];                  // t - t0 < t1 - t0 + RPI: inside the slack
+      const float wr = slog[t - t0];
+      const int j = t < t1 ? jr : -1;
       const bool ok = j >= 0 && j < N;
-      wt[u] = ok ? slog[t - t0] : 0.0f;
-      vv[u] = ok ? *reinterpret_cast<const uint4*>(V + static_cast<size_t>(j) * D + e0)
-                 : make_uint4(0, 0, 0, 0);
+      wt[u] = ok ? wr : 0.0f;   // an invalid entry loads row 0 with weight 0
+      vv[u] = *reinterpret_cast<const uint4*>(V + static_cast<size_t>(ok ? j : 0) * D + e0);
     }
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
@@ -239,12 +246,15 @@ __device__ __forceinline__ void weighted_rows(const T* __restrict__ V,
 #pragma unroll
   for (int o = LPR; o < kWave; o <<= 1) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] += __shfl_xor(acc[e], o, kWave);
+    for (int e = 0; e < EPL; ++e)
+      acc[e] = o == 32 ? sum_xor32(acc[e]) : o == 16 ? sum_xor16(acc[e])
+                                                   : acc[e] + __shfl_xor(acc[e], o, kWave);
   }
 }
 
 // Per-wave LDS of the gather kernels: the entries and the logits of up to k
-// entries (+16 slack each).
+// entries (+16 slack each: the loops read up to 15 entries past a segment's
+// end and discard them, so the reads need no guard).
 __host__ __device__ constexpr int gather_slog_floats(int k) { return (k + 16 + 3) / 4 * 4; }
 __host__ __device__ constexpr int gather_wave_floats(int k) { return 2 * gather_slog_floats(k); }
 
@@ -275,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   stage_entries(idx + (hN + q) * k, 0, k, sidx);
   const int32_t* row = sidx;
   int bad = 0;
-  logits<T, D>(Q + (hN + q) * D, Kh, row, 0, k, N, scale, slog, bad);
+  logits<T, D>(Q + (hN + q) * D, Kh, row, 0, k, N, scale * kLog2e, slog, bad);
   if (bad) atomicOr(&g_index_error_flag, 1);
   wave_sync();
   float sum;
@@ -308,8 +318,8 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // working set is then one range.  Eight ranges (8 MB of K and V each at the
 // headline size) measured faster than sixteen: every (query, range) pays a
 // fixed cost, and halving their number outweighs the lower L2 hit rate.  Each (query, range) writes an
-// online-softmax partial (max m, sum l of e^(x-m), unnormalised sum of
-// e^(x-m) V) and a merge combines the partials of a query.
+// online-softmax partial (max m, sum l of 2^(x-m), unnormalised sum of
+// 2^(x-m) V) and a merge combines the partials of a query.
 
 // seg[q][r] = first position of row q whose key is >= r * L, r = 0..R; the
 // rows hold valid keys ascending, then -1.
@@ -362,8 +372,11 @@ __global__ __launch_bounds__(kThreads) void gather_part_kernel(
   if (q >= N) return;
   float* slog = slog_all + w * gather_wave_floats(k);
   int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
-  const int s0 = seg[static_cast<size_t>(q) * (R + 1) + r];
-  const int s1 = seg[static_cast<size_t>(q) * (R + 1) + r + 1];
+  // the segment bounds are the wave's own (every lane reads the same words):
+  // kept in scalar registers, every loop bound and trip count below is
+  // uniform and needs no lane mask
+  const int s0 = __builtin_amdgcn_readfirstlane(seg[static_cast<size_t>(q) * (R + 1) + r]);
+  const int s1 = __builtin_amdgcn_readfirstlane(seg[static_cast<size_t>(q) * (R + 1) + r + 1]);
   float* rec = part + (static_cast<size_t>(q) * R + r) * (D + 4);
   if (s0 >= s1) {
     if (l == 0) rec[0] = -INFINITY;   // empty: the merge skips it
@@ -372,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void gather_part_kernel(
   stage_entries(idx + static_cast<size_t>(q) * k, s0, s1, sidx);
   const int32_t* row = sidx;
   int bad = 0;
-  logits<T, D>(Q + static_cast<size_t>(q) * D, K, row, s0, s1, N, scale, slog, bad);
+  logits<T, D>(Q + static_cast<size_t>(q) * D, K, row, s0, s1, N, scale * kLog2e, slog, bad);
   if (bad) atomicOr(&g_index_error_flag, 1);
   wave_sync();
   float sum;
@@ -396,7 +409,8 @@ __global__ __launch_bounds__(kThreads) void gather_part_kernel(
   }
 }
 
-// O_q = sum_r e^(m_r - M) acc_r / sum_r e^(m_r - M) l_r, M = max_r m_r.
+// O_q = sum_r 2^(m_r - M) acc_r / sum_r 2^(m_r - M) l_r, M = max_r m_r (base-2
+// logits, as in the partials).
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __restrict__ part,
                                                                 int N, T* __restrict__ O) {
@@ -422,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
     for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(0.0f);
     return;
   }
-  const float wr = m == -INFINITY ? 0.0f : expf(m - M);
+  const float wr = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
   const float L = wave_sum(wr * lsum);
 #pragma unroll 4
   for (int r = 0; r < R; ++r) {

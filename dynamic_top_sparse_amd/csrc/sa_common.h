@@ -10,6 +10,7 @@ typedef uint16_t bf16_t;  // storage of a bfloat16 value
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));   // operand of the bf16 dot2 instruction
 
 constexpr int kWave = 64;
 
@@ -155,19 +156,71 @@ __device__ __forceinline__ float score_margin(float qn, float qr, float kn, floa
 // ------------------------------------------------------ wave primitives ---
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+// v[l] + v[l ^ 16] (or ^ 32) in every lane.  gfx950's permlane swaps move
+// rows 1 and 3 of one register into rows 0 and 2 of another (the 32 variant:
+// the upper half into the lower); swapping a register with itself leaves
+// each lane holding its own value and its partner's, one in each result.
+// These are VALU operations, unlike a shuffle through the LDS crossbar.
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Lane partners inside a 16-lane row through DPP (VALU, no LDS): swaps of
+// neighbours and of pairs in each quad, then the mirrors of each half-row
+// and of the row.  Applied in that order, each step combines two disjoint
+// groups that already agree, so a reduction leaves every lane of the row
+// with the same value.
+constexpr int kDppQuadXor1 = 0xB1;      // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;      // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141;   // row_half_mirror
+constexpr int kDppMirror = 0x140;       // row_mirror
+template <int Ctrl>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), Ctrl, 0xF, 0xF, false));
+}
+template <int Ctrl>
+__device__ __forceinline__ int dpp_i(int v) {
+  return __builtin_amdgcn_update_dpp(0, v, Ctrl, 0xF, 0xF, false);
+}
+__device__ __forceinline__ float row_sum16(float v) {
+  v += dpp_f<kDppQuadXor1>(v);
+  v += dpp_f<kDppQuadXor2>(v);
+  v += dpp_f<kDppHalfMirror>(v);
+  v += dpp_f<kDppMirror>(v);
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+__device__ __forceinline__ float row_max16(float v) {
+  v = fmaxf(v, dpp_f<kDppQuadXor1>(v));
+  v = fmaxf(v, dpp_f<kDppQuadXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
   return v;
 }
+
+__device__ __forceinline__ float wave_max(float v) { return row_max16(max_xor16(max_xor32(v))); }
+__device__ __forceinline__ float wave_sum(float v) { return row_sum16(sum_xor16(sum_xor32(v))); }
 __device__ __forceinline__ int wave_sum_i(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  auto r = __builtin_amdgcn_permlane32_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  v = static_cast<int>(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane16_swap(static_cast<unsigned>(v), static_cast<unsigned>(v), false, false);
+  v = static_cast<int>(r[0] + r[1]);
+  v += dpp_i<kDppQuadXor1>(v);
+  v += dpp_i<kDppQuadXor2>(v);
+  v += dpp_i<kDppHalfMirror>(v);
+  v += dpp_i<kDppMirror>(v);
   return v;
 }
 // Inclusive prefix sum over the wave.
