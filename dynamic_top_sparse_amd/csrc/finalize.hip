@@ -24,6 +24,8 @@
 #include <float.h>
 #include <limits.h>
 
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -39,31 +41,63 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
+// Wave-wide min / max of 32- and 64-bit keys: permlane swaps across rows,
+// then DPP partners inside each row (VALU only; see sa_common.h).
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_reduce_key(T v, Op op) {
+  auto both = [&](auto swap) {
+    if constexpr (sizeof(T) == 8) {
+      const auto lo = swap(static_cast<uint32_t>(v), static_cast<uint32_t>(v), false, false);
+      const auto hi = swap(static_cast<uint32_t>(v >> 32), static_cast<uint32_t>(v >> 32), false, false);
+      const T a = (static_cast<T>(hi[0]) << 32) | lo[0];
+      const T b = (static_cast<T>(hi[1]) << 32) | lo[1];
+      v = op(a, b);
+    } else {
+      const auto r = swap(v, v, false, false);
+      v = op(static_cast<T>(r[0]), static_cast<T>(r[1]));
+    }
+  };
+  both([](uint32_t x, uint32_t y, bool, bool) { return __builtin_amdgcn_permlane32_swap(x, y, false, false); });
+  both([](uint32_t x, uint32_t y, bool, bool) { return __builtin_amdgcn_permlane16_swap(x, y, false, false); });
+  auto step = [&](auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    if constexpr (sizeof(T) == 8) {
+      const uint32_t lo = static_cast<uint32_t>(dpp_i<C>(static_cast<int>(static_cast<uint32_t>(v))));
+      const uint32_t hi = static_cast<uint32_t>(dpp_i<C>(static_cast<int>(static_cast<uint32_t>(v >> 32))));
+      v = op(v, (static_cast<T>(hi) << 32) | lo);
+    } else {
+      v = op(v, static_cast<T>(dpp_i<C>(static_cast<int>(v))));
+    }
+  };
+  step(std::integral_constant<int, kDppQuadXor1>{});
+  step(std::integral_constant<int, kDppQuadXor2>{});
+  step(std::integral_constant<int, kDppHalfMirror>{});
+  step(std::integral_constant<int, kDppMirror>{});
   return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_key(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, static_cast<uint32_t>(__shfl_xor(static_cast<int>(v), o, kWave)));
-  return v;
+  return wave_reduce_key(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
 }
 __device__ __forceinline__ unsigned long long wave_min_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long t = __shfl_xor(v, o, kWave);
-    v = t < v ? t : v;
-  }
-  return v;
+  return wave_reduce_key(v, [](unsigned long long a, unsigned long long b) { return a < b ? a : b; });
 }
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const unsigned long long t = __shfl_xor(v, o, kWave);
-    v = t > v ? t : v;
+  return wave_reduce_key(v, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
+}
+
+// Value of a key held by lane `src` (wave-uniform), read with v_readlane.
+template <typename KeyT>
+__device__ __forceinline__ KeyT lane_key(KeyT v, int src) {
+  if constexpr (sizeof(KeyT) == 8) {
+    const uint32_t lo = __builtin_amdgcn_readlane(static_cast<uint32_t>(v), src);
+    const uint32_t hi = __builtin_amdgcn_readlane(static_cast<uint32_t>(v >> 32), src);
+    return (static_cast<KeyT>(hi) << 32) | lo;
+  } else {
+    return static_cast<KeyT>(__builtin_amdgcn_readlane(static_cast<uint32_t>(v), src));
   }
-  return v;
 }
 template <typename KeyT>
 __device__ __forceinline__ KeyT wave_min_k(KeyT v);
@@ -94,15 +128,14 @@ __device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo,
     const KeyT span = hi - lo;
     const int nb = key_bits<KeyT>(span);
     const int shift = nb > 8 ? nb - 8 : 0;          // (span >> shift) < 256
-    for (int b = l; b < 256; b += kWave) hist[b] = 0;
+    reinterpret_cast<int4*>(hist)[l] = make_int4(0, 0, 0, 0);   // 256 bins, 4 per lane
     wave_sync();
     each([&](KeyT key, bool ok) {
       if (ok && key >= lo && key <= hi) atomicAdd(&hist[static_cast<int>((key - lo) >> shift)], 1);
     });
     wave_sync();
-    int c[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) c[t] = hist[255 - 4 * l - t];   // lane L: bins 255-4L ..
+    const int4 h4 = reinterpret_cast<const int4*>(hist)[63 - l];   // lane L: bins 255-4L ..
+    const int c[4] = {h4.w, h4.z, h4.y, h4.x};
     const int sum = c[0] + c[1] + c[2] + c[3];
     const int incl = wave_incl_scan(sum);
     const unsigned long long crossing = __ballot(incl >= K);
@@ -117,9 +150,9 @@ __device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo,
       }
       above = cum;
     }
-    digit = __shfl(digit, F, kWave);
-    above = __shfl(above, F, kWave);
-    cnt = __shfl(cnt, F, kWave);
+    digit = __builtin_amdgcn_readlane(digit, F);
+    above = __builtin_amdgcn_readlane(above, F);
+    cnt = __builtin_amdgcn_readlane(cnt, F);
     K -= above;
     const KeyT nlo = lo + (static_cast<KeyT>(digit) << shift);
     const KeyT width = (static_cast<KeyT>(1) << shift) - 1;
@@ -145,19 +178,13 @@ __device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo,
   const KeyT mine = l < m ? cbuf[l] : static_cast<KeyT>(0);
   int greater = 0, equal = 0;
   for (int u = 0; u < m; ++u) {
-    const KeyT o = cbuf[u];
+    const KeyT o = lane_key(mine, u);
     greater += o > mine ? 1 : 0;
     equal += o == mine ? 1 : 0;
   }
   const unsigned long long hit = __ballot(l < m && greater < K && greater + equal >= K);
   const int src = hit ? __builtin_ctzll(hit) : 0;
-  KeyT result;
-  if (sizeof(KeyT) == 8) {
-    const unsigned long long r = __shfl(static_cast<unsigned long long>(mine), src, kWave);
-    result = static_cast<KeyT>(r);
-  } else {
-    result = static_cast<KeyT>(__shfl(static_cast<int>(mine), src, kWave));
-  }
+  const KeyT result = lane_key(mine, src);
   wave_sync();
   return result;
 }
@@ -429,9 +456,7 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
         }
         #pragma unroll
         for (int t = 0; t < UNR; ++t) {
-          float p = group_partial<DP>(qv, kv[t]);
-          #pragma unroll
-          for (int o = G / 2; o >= 1; o >>= 1) p += __shfl_xor(p, o, kWave);
+          const float p = group_sum<G>(group_partial<DP>(qv, kv[t]));
           const int u = u0 + t * KPI + grp;
           if (g == 0 && u < nU) us[u] = p * scale;
         }

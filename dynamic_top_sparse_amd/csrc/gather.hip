@@ -74,18 +74,6 @@ template <> struct Vec<bf16_t> {
 // logits go to the wave's LDS buffer `slog` (index t - t0; room for t1 - t0
 // rounded up to 16), then become the unnormalised weights e^(x - m).
 
-// Sum over the LPR consecutive lanes that hold one row (LPR = 8 or 16: the
-// group lies inside one DPP row, and every lane of it gets the sum).
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v) {
-  static_assert(LPR == 8 || LPR == 16, "row groups of 8 or 16 lanes");
-  v += dpp_f<kDppQuadXor1>(v);
-  v += dpp_f<kDppQuadXor2>(v);
-  v += dpp_f<kDppHalfMirror>(v);
-  if constexpr (LPR == 16) v += dpp_f<kDppMirror>(v);
-  return v;
-}
-
 // Logits, bf16 I/O: rows are read as the V rows are (LPR lanes x 16 bytes
 // per row, RPI whole rows per load instruction), so each load touches whole
 // 128-byte lines; the vector memory path, not the arithmetic, bounds the

@@ -57,10 +57,11 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
 // shared by every kernel that needs it (re-rank, fallback, dump):
 //   p_g = q[4g]k[4g] + q[4g+1]k[4g+1] + ... as a chain of fused multiply-adds
 //         over the 4 coordinates of group g (g = 0 .. DP/4-1),
-//   then an xor-butterfly over the groups: at step o (DP/8, ..., 2, 1) every
+//   then an xor-butterfly over the groups: at step o (1, 2, ..., DP/8) every
 //   p_g becomes p_g + p_{g^o}; the result is p_0 · scale.
-// A wavefront evaluates it with one lane per group and __shfl_xor steps;
-// exact_score() below is the same arithmetic for one thread.
+// A wavefront evaluates it with one lane per group and group_sum() (whose
+// steps are exactly these); exact_score() below is the same arithmetic for
+// one thread.
 template <int DP>
 __device__ __forceinline__ float group_partial(const float4 q, const float4 k) {
   return __builtin_fmaf(q.w, k.w, __builtin_fmaf(q.z, k.z, __builtin_fmaf(q.y, k.y,
@@ -77,7 +78,7 @@ __device__ __forceinline__ float exact_score(const float* __restrict__ q,
     p[g] = group_partial<DP>(make_float4(q[4 * g], q[4 * g + 1], q[4 * g + 2], q[4 * g + 3]),
                              make_float4(k[4 * g], k[4 * g + 1], k[4 * g + 2], k[4 * g + 3]));
 #pragma unroll
-  for (int o = G / 2; o >= 1; o >>= 1) {
+  for (int o = 1; o < G; o <<= 1) {
     float t[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) t[g] = p[g] + p[g ^ o];
@@ -210,6 +211,23 @@ __device__ __forceinline__ float row_max16(float v) {
   return v;
 }
 
+// Sum over aligned groups of G lanes (G a power of two up to 64), every lane
+// of a group getting the group's sum.  The steps are the xor-butterfly with
+// partners l^1, l^2, l^4, l^8, l^16, l^32 in that order: the mirror steps
+// pair a lane with l^7 or l^15, which at that point hold the same values as
+// l^4 and l^8.
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G >= 1 && G <= 64 && (G & (G - 1)) == 0, "power-of-two groups");
+  if constexpr (G >= 2) v += dpp_f<kDppQuadXor1>(v);
+  if constexpr (G >= 4) v += dpp_f<kDppQuadXor2>(v);
+  if constexpr (G >= 8) v += dpp_f<kDppHalfMirror>(v);
+  if constexpr (G >= 16) v += dpp_f<kDppMirror>(v);
+  if constexpr (G >= 32) v = sum_xor16(v);
+  if constexpr (G >= 64) v = sum_xor32(v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) { return row_max16(max_xor16(max_xor32(v))); }
 __device__ __forceinline__ float wave_sum(float v) { return row_sum16(sum_xor16(sum_xor32(v))); }
 __device__ __forceinline__ int wave_sum_i(int v) {
@@ -223,15 +241,19 @@ __device__ __forceinline__ int wave_sum_i(int v) {
   v += dpp_i<kDppMirror>(v);
   return v;
 }
-// Inclusive prefix sum over the wave.
+// Inclusive prefix sum over the wave: a Hillis-Steele scan inside each
+// 16-lane row (DPP row shifts; a lane with no source within its row adds 0),
+// then the totals of the rows before are added from lanes 15, 31 and 47.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int l = lane_id();
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    int t = __shfl_up(v, o, kWave);
-    if (l >= o) v += t;
-  }
-  return v;
+  v += dpp_i<0x111>(v);   // row_shr:1
+  v += dpp_i<0x112>(v);   // row_shr:2
+  v += dpp_i<0x114>(v);   // row_shr:4
+  v += dpp_i<0x118>(v);   // row_shr:8
+  const int row = lane_id() >> 4;
+  const int r0 = __builtin_amdgcn_readlane(v, 15);
+  const int r1 = __builtin_amdgcn_readlane(v, 31);
+  const int r2 = __builtin_amdgcn_readlane(v, 47);
+  return v + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
 }
 
 // --------------------------------------------------- workspace header ---
