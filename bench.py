@@ -44,13 +44,13 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
 # kernel's source file when the counters were taken.
 TRAFFIC = {
-    # profiles/headline_128k_hbm_traffic.md
-    "filter": {"fetch_bytes": 12.455e9, "write_bytes": 27.362e9,
-               "src": "e8285951b369366e6329c3b8c55c4c419de5d389b041557f5e73d56419d37fcd"},
-    "gather": {"fetch_bytes": 3.399e9, "write_bytes": 1.141e9,
-               "src": "ed1430e282f23960857216c8aaa1bc621732143821619c37b9b6e55536df13c7"},
-    "rerank": {"fetch_bytes": 8.952e9, "write_bytes": 1.345e9,
-               "src": "5b5eff95582079b9f0e9eb99cccd62031f2885d5175c2c950eca4dd469dd3feb"},
+    # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (8 heads)
+    "filter": {"fetch_bytes": 12.941e9, "write_bytes": 27.299e9,
+               "src": "80bb3dd81a24558c90968271a6ee996ef340a57e1272e500d86bff7888f8cd8e"},
+    "gather": {"fetch_bytes": 10.746e9, "write_bytes": 0.570e9,
+               "src": "cd391d6a58ba2512635d65c4a5c577608da9d4c8421189dd05202ec4ff8e22af"},
+    "rerank": {"fetch_bytes": 9.124e9, "write_bytes": 1.349e9,
+               "src": "b6ad2f30d278b8f01bdab876cb7dc0940e4f6c78bad9d76482e3c31661b47ffe"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
 
