@@ -14,7 +14,7 @@ constexpr int kQueriesPerBlock = 256;   // scorer workgroup: 4 waves x 64 querie
 constexpr int kKeysPerChunk = 128;      // keys staged in LDS per step
 constexpr int kMaxSampleStride = 16;    // the threshold sample takes every s-th key, s <= 16
 constexpr int kRowPad = 2048;           // N is padded to a multiple of this
-constexpr float kTauBeta = 1.5f;        // sample rank slack (see threshold kernel)
+constexpr float kTauBeta = 1.3f;        // sample rank slack (see threshold kernel)
 constexpr int kFallbackBlocks = 256;    // workgroups of the exact fallback
 constexpr int kKMax = 2048;             // largest supported k
 constexpr int kGatherRanges = 8;        // key ranges of the split gather (a multiple of 8)
