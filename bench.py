@@ -87,6 +87,24 @@ def algorithmic(w) -> dict:
     }
 
 
+def pick_heads_per_chunk(w) -> int:
+    """Largest of (all heads, 16, 8) whose workspace takes at most a quarter of
+    the device's memory.  Larger chunks mean fewer, fuller launches: each
+    filter launch is a whole number of workgroup rounds only for some sizes
+    (at the headline size 32 heads run 22 rounds of the chip's resident
+    workgroups where four chunks of 8 run 24)."""
+    import torch
+    import dynamic_top_sparse_amd as sa
+    budget = torch.cuda.get_device_properties(0).total_memory // 4
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    for hc in (w.B * w.H, 16, 8):
+        n = sa.sparse_attn_workspace_size(w.B, w.H, w.N, w.D, w.d_proj, w.k, w.causal, dt,
+                                          True, hc)
+        if 0 < n <= budget:
+            return hc
+    return 8
+
+
 def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: query rows of head (0, 0), including that head's projections."""
@@ -124,7 +142,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="headline_128k")
     ap.add_argument("--heads-per-chunk", type=int, default=0,
-                    help="workspace sized for this many heads per chunk (0 = library default)")
+                    help="workspace sized for this many heads per chunk (0 = the largest of all "
+                         "heads, 16, 8 whose workspace fits in a quarter of device memory)")
     ap.add_argument("--filter-dtype", choices=("f16", "bf16"), default="f16",
                     help="16-bit operand type of the MFMA filter (indices do not depend on it)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -148,7 +167,7 @@ def main() -> int:
         return 2
     x = W.make_inputs(w, W.default_seed())
     g = {k: v.cuda() for k, v in x.items()}
-    hc = args.heads_per_chunk or None
+    hc = args.heads_per_chunk or pick_heads_per_chunk(w)
     ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
                                heads_per_chunk=hc)
     out = torch.empty_like(g["Q"])

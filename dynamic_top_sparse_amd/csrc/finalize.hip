@@ -611,6 +611,20 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
   }
 }
 
+// Compute units of the current device (cached per device).
+int resident_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 template <int DP>
 hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t* idx,
                       bool retry, hipStream_t s) {
@@ -620,10 +634,14 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   const size_t per_wave = rerank_lds_per_wave(2 * p.capH, ucap);
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
-  // persistent waves: about 2048 workgroups over the chunk, each wave
-  // striding over the queries of its head
+  // persistent waves striding over the queries of their head: as many
+  // workgroups as the chip holds at once (LDS bounds how many fit on a CU),
+  // so every wave works until the end instead of a last, partial round
+  const size_t lds_wg = static_cast<size_t>(wpb) * per_wave;
+  const int per_cu = static_cast<int>(max(static_cast<size_t>(1), 163840 / lds_wg));
+  const int resident = resident_cus() * per_cu;
   int gx = (p.N + wpb - 1) / wpb;
-  const int per_head = (2048 + nh - 1) / nh;
+  const int per_head = (resident + nh - 1) / nh;
   gx = gx < per_head ? gx : per_head;
   const dim3 grid(gx, nh);
   const size_t lds = static_cast<size_t>(wpb) * per_wave;
