@@ -177,7 +177,7 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.off_ksamp = take(hc * static_cast<size_t>(p.Nspad) * dp * 2);
   p.off_qstat = take(hc * Np * 16);
   p.off_kstat = take(hc * kKeyStatWords * 4);
-  p.off_bm = take(hc * static_cast<size_t>(p.NB) * Np * 4);
+  p.off_bm = take(hc * static_cast<size_t>(p.NB) * Np * 2);
   p.off_tau = take(hc * Np * 4);
   p.off_thr = take(hc * Np * 4);
   p.off_cand = take(hc * Np * 2 * static_cast<size_t>(p.capH) * 8);
@@ -205,7 +205,7 @@ Bufs bufs_of(const Plan& p, void* ws) {
   b.ksamp = reinterpret_cast<bf16_t*>(base + p.off_ksamp);
   b.qstat = reinterpret_cast<float4*>(base + p.off_qstat);
   b.kstat = reinterpret_cast<uint32_t*>(base + p.off_kstat);
-  b.bm = reinterpret_cast<float*>(base + p.off_bm);
+  b.bm = reinterpret_cast<uint16_t*>(base + p.off_bm);
   b.tau = reinterpret_cast<float*>(base + p.off_tau);
   b.thr = reinterpret_cast<float*>(base + p.off_thr);
   b.cand = reinterpret_cast<uint2*>(base + p.off_cand);

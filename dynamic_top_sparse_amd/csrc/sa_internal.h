@@ -81,7 +81,7 @@ struct Bufs {
   bf16_t* ksamp;
   float4* qstat;        // per query: ||q_low||, ||q_low - q~||, 2^-e_q (norms rounded up)
   uint32_t* kstat;      // per head: max ||k_low||, max ||k_low - k~||, max |k_low|_inf (fp32 bits)
-  float* bm;            // sample block maxima [hc][NB][Npad]
+  uint16_t* bm;         // sample block maxima, top 16 bits of their order keys [NB][hc][Npad]
   float* tau;           // per-query threshold [hc][Npad]
   float* thr;           // the filter's threshold on the raw MFMA sum, as used [hc][Npad]
   uint2* cand;          // candidates [hc][Npad][2][capH] = (key, raw MFMA sum bits)

@@ -120,8 +120,16 @@ __device__ __forceinline__ int acc_row(int r, int half) {
 // Block maxima of one lane's 16 accumulators (keys 8*(r/4) + r%4 + 4*half of
 // the tile, in r order) for blocks of B consecutive accumulators, stored as
 // values e0 .. e0 + 16/B - 1 of the query's row of maxima.
-__device__ __forceinline__ void store_block_maxima(f32x16 v, int B, float* __restrict__ dst,
-                                                   size_t stride) {
+// The maxima are scaled by f (> 0) only when stored: rounding a product is
+// monotonic in the other factor, so max(x) * f is exactly max(x * f).  Only
+// the top 16 bits of each maximum's order key are kept: the threshold is
+// selected on those bits alone (rounded down), so the rest would never be
+// read.
+__device__ __forceinline__ uint16_t max_key16(float v) {
+  return static_cast<uint16_t>(order_key(v) >> 16);
+}
+__device__ __forceinline__ void store_block_maxima(f32x16 v, int B, float f,
+                                                   uint16_t* __restrict__ dst, size_t stride) {
 #pragma unroll
   for (int lvl = 0; lvl <= 4; ++lvl) {
     const int b = 1 << lvl;
@@ -131,7 +139,7 @@ __device__ __forceinline__ void store_block_maxima(f32x16 v, int B, float* __res
     }
     if (B == b) {
 #pragma unroll
-      for (int g = 0; g < 16 / b; ++g) dst[g * stride] = v[g * b];
+      for (int g = 0; g < 16 / b; ++g) dst[g * stride] = max_key16(v[g * b] * f);
     }
   }
 }
@@ -141,7 +149,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     const bf16_t* __restrict__ q16, const bf16_t* __restrict__ samp,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat, float scale, int N,
     int Npad, int Ns, int sstride, int k, int causal, int capH, float beta,
-    float* __restrict__ bm) {
+    uint16_t* __restrict__ bm) {
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kQueriesPerBlock;
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
   const bf16_t* qh = q16 + static_cast<size_t>(h) * Npad * DP;
   const bf16_t* sh = samp + static_cast<size_t>(h) * (Npad / sstride) * DP;
   // value e of query q of head h: bm[e * (heads * Npad) + h * Npad + q]
-  float* bmh = bm + static_cast<size_t>(h) * Npad;
+  uint16_t* bmh = bm + static_cast<size_t>(h) * Npad;
   const size_t stride = static_cast<size_t>(gridDim.y) * Npad;
 
   uint4 b0[Tile<DP>::kKSteps], b1[Tile<DP>::kKSteps];
@@ -213,9 +221,8 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
         if (tile > last_tile[bb]) continue;
         const int B = Bq[bb];
         if (B <= 16) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) a[bb][r] *= fq;
-          store_block_maxima(a[bb], B, bmh + (2 * tile + half) * (16 / B) * stride + qq[bb], stride);
+          store_block_maxima(a[bb], B, fq, bmh + (2 * tile + half) * (16 / B) * stride + qq[bb],
+                             stride);
         } else {
           float m = a[bb][0];
 #pragma unroll
@@ -223,7 +230,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
           run[bb] = fmaxf(run[bb], m * fq);
           const int G = B / 16;
           if (tile % G == G - 1 || tile == last_tile[bb]) {
-            bmh[(2 * (tile / G) + half) * stride + qq[bb]] = run[bb];
+            bmh[(2 * (tile / G) + half) * stride + qq[bb]] = max_key16(run[bb]);
             run[bb] = -INFINITY;
           }
         }
@@ -237,17 +244,18 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
 // -------------------------------------------------------------- threshold ---
 // One thread per query: tau is (a lower rounding of) the r-th largest of the
 // query's block maxima, found by a 4-bit-digit radix select over the top 16
-// bits of their order keys (rounding down only adds candidates).  About
+// bits of their order keys, the part the sample pass stores (rounding down
+// only adds candidates).  About
 // beta * k keys are expected above it.
 __global__ __launch_bounds__(kThreads) void threshold_kernel(
-    const float* __restrict__ bm, int N, int Npad, int Ns, int sstride, int k, int causal,
+    const uint16_t* __restrict__ bm, int N, int Npad, int Ns, int sstride, int k, int causal,
     int capH, float beta, float* __restrict__ tau) {
   __shared__ int hist[16 * kThreads];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
   const int q = blockIdx.x * kThreads + tid;
   const size_t stride = static_cast<size_t>(gridDim.y) * Npad;
-  const float* bmh = bm + static_cast<size_t>(h) * Npad;
+  const uint16_t* bmh = bm + static_cast<size_t>(h) * Npad;
   if (q >= Npad) return;  // whole-block uniform: Npad is a multiple of 256
   float result = -INFINITY;
   const int n_valid = causal ? q + 1 : N;
@@ -266,7 +274,7 @@ __global__ __launch_bounds__(kThreads) void threshold_kernel(
     for (int d = 0; d < 16; ++d) hist[d * kThreads + tid] = 0;
     if (active) {
       for (int e = 0; e < nb; ++e) {
-        const uint32_t key = order_key(bmh[static_cast<size_t>(e) * stride + q]);
+        const uint32_t key = static_cast<uint32_t>(bmh[static_cast<size_t>(e) * stride + q]) << 16;
         if ((key & pmask) == prefix) hist[((key >> shift) & 15u) * kThreads + tid] += 1;
       }
       int cum = 0, digit = 0;
