@@ -34,6 +34,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWavesPerBlock = kThreads / kWave;   // fallback workgroup
+constexpr int kPrefetch = 12;                      // candidate entries per lane loaded a query ahead
 
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -255,7 +256,7 @@ __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
 }
 
 template <int DP>
-__global__ __launch_bounds__(kThreads) void finalize_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void finalize_kernel(
     const uint2* __restrict__ cand, const int* __restrict__ cnt, const int* __restrict__ rcnt,
     float* __restrict__ tau,
     const float* __restrict__ thr,
@@ -284,10 +285,71 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
   unsigned long long st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
   // first pass: every query; retry pass: the queries listed for this head
   const int nq = qlist != nullptr ? qlist_count[h] : N;
+  // Software pipeline over the wave's queries: while query i is ranked, the
+  // candidate lists of query i+1 are loading into registers (the first
+  // kPrefetch*64 entries) and the counts and thresholds of query i+2 are
+  // loading too, so a query's staging rarely waits for memory.
+  struct Meta {
+    int q, r0, r1;
+    float tq, tv;
+    float4 st;
+  };
+  auto load_meta = [&](int slot) {
+    Meta m;
+    m.q = qlist != nullptr ? qlist[hq + slot] : slot;
+    // One candidate list per query half; the retry pass counted its hits per
+    // key segment.  An overflowing list still holds capH genuine candidates.
+    m.r0 = 0;
+    m.r1 = 0;
+    if (qlist == nullptr) {
+      m.r0 = cnt[(hq + m.q) * 2];
+      m.r1 = cnt[(hq + m.q) * 2 + 1];
+    } else {
+      for (int s2 = 0; s2 < kRetrySplit; ++s2) {
+        m.r0 += rcnt[(hq + m.q) * 2 * kRetrySplit + s2];
+        m.r1 += rcnt[((hq + m.q) * 2 + 1) * kRetrySplit + s2];
+      }
+    }
+    m.tq = tau[hq + m.q];
+    m.tv = thr[hq + m.q];
+    m.st = qstat[hq + m.q];
+    return m;
+  };
+  uint2 pre[kPrefetch];
+  // entries l, l+64, ... of the query's candidates (half 0, then half 1);
+  // indices past the lists are clamped to a valid entry and never staged
+  auto load_cands = [&](const Meta& m) {
+    const int c0 = min(m.r0, capH), c = c0 + min(m.r1, capH);
+    const uint2* list0 = cand + (hq + m.q) * 2 * static_cast<size_t>(capH);
+#pragma unroll
+    for (int j = 0; j < kPrefetch; ++j) {
+      const int i = min(l + kWave * j, max(c - 1, 0));
+      pre[j] = list0[i < c0 ? i : capH + (i - c0)];
+    }
+  };
+  const int stride = gridDim.x * wpb;
+  int slot = blockIdx.x * wpb + w;
+  Meta cur{}, nxt{};
+  if (slot < nq) {
+    cur = load_meta(slot);
+    load_cands(cur);
+  }
+  if (slot + stride < nq) nxt = load_meta(slot + stride);
 #pragma unroll 1
-  for (int slot = blockIdx.x * wpb + w; slot < nq; slot += gridDim.x * wpb) {
+  for (; slot < nq; slot += stride) {
     wave_sync();  // the previous query's LDS reads are done
-    const int q = qlist != nullptr ? qlist[hq + slot] : slot;
+    const bool has_next = slot + stride < nq;
+    Meta nn{};
+    bool issued = false;
+    // starts the loads for the next queries; called once per query, as soon
+    // as the registers holding this query's candidates are free
+    auto issue_next = [&]() {
+      if (has_next) load_cands(nxt);
+      if (slot + 2 * stride < nq) nn = load_meta(slot + 2 * stride);
+      issued = true;
+    };
+    do {  // one query; `continue` ends it
+    const int q = cur.q;
     int32_t* out = idx + (static_cast<size_t>(h) * N + q) * k;
     const int n_valid = causal ? q + 1 : N;
     const int k_i = min(k, n_valid);
@@ -313,48 +375,45 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     };
 
     if (n_valid <= k) {  // every valid key is kept
+      issue_next();
       for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
       ++st_queries;
       continue;
     }
-    // One candidate list per query half; the retry pass counted its hits per
-    // key segment.  An overflowing list still holds capH genuine candidates.
-    int r0 = 0, r1 = 0;
-    if (qlist == nullptr) {
-      r0 = cnt[(hq + q) * 2];
-      r1 = cnt[(hq + q) * 2 + 1];
-    } else {
-      for (int s2 = 0; s2 < kRetrySplit; ++s2) {
-        r0 += rcnt[(hq + q) * 2 * kRetrySplit + s2];
-        r1 += rcnt[((hq + q) * 2 + 1) * kRetrySplit + s2];
-      }
-    }
+    const int r0 = cur.r0, r1 = cur.r1;
     const bool overflow = r0 > capH || r1 > capH;
     const int c0 = min(r0, capH), c1 = min(r1, capH);
     const int c = c0 + c1;
-    const float tq = tau[hq + q];
+    const float tq = cur.tq;
     if (overflow && qlist == nullptr) ++st_overflow;
     // Stage the candidates in LDS once (index i runs over half 0, then half 1)
     // as (order key of the filter score s~ = sum * f, key index).  The
     // filter parked sum - thr (its accumulators start at -thr).
-    const float4 st = qstat[hq + q];
+    const float4 st = cur.st;
     const float kinv =
         __builtin_ldexpf(1.0f, -scale_exponent(__uint_as_float(kstat[kKeyStatWords * h + 2])));
     const float f = scale * st.z * kinv;
-    const float tv = thr[hq + q];
+    const float tv = cur.tv;
     uint32_t kmin = ~0u, kmax = 0u;
     {
-      const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
-      const uint2* list1 = list0 + capH;
-      #pragma unroll 16
-      for (int i = l; i < c; i += kWave) {
-        const uint2 e = i < c0 ? list0[i] : list1[i - c0];
+      auto stage = [&](int i, uint2 e) {
         const uint32_t key = order_key((__uint_as_float(e.y) + tv) * f);
         ck[i] = key;
         cj[i] = static_cast<int>(e.x);
         kmin = min(kmin, key);
         kmax = max(kmax, key);
+      };
+#pragma unroll
+      for (int j = 0; j < kPrefetch; ++j) {
+        const int i = l + kWave * j;
+        if (i < c) stage(i, pre[j]);
       }
+      issue_next();
+      const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
+      const uint2* list1 = list0 + capH;
+      #pragma unroll 16
+      for (int i = kWave * kPrefetch + l; i < c; i += kWave)
+        stage(i, i < c0 ? list0[i] : list1[i - c0]);
     }
     kmin = wave_min_u32(kmin);
     kmax = wave_max_u32(kmax);
@@ -500,6 +559,10 @@ __global__ __launch_bounds__(kThreads) void finalize_kernel(
     for (int t = run2 + l; t < k; t += kWave) out[t] = -1;
     st_rescored += static_cast<unsigned long long>(nU);
     ++st_queries;
+    } while (false);
+    if (!issued) issue_next();
+    cur = nxt;
+    nxt = nn;
   }
   if (l == 0) {
     if (st_queries) atomicAdd(&hdr->queries, st_queries);
