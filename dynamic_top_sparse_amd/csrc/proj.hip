@@ -33,7 +33,14 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
     uint32_t* __restrict__ kstat) {
   constexpr int kXFloats = kRows * (D + 1);
   constexpr int kLoFloats = 2 * kRows * (DP + 1);
-  __shared__ float sP[D * DP];
+  // bf16 rows: 32x32 output tiles on the bf16 MFMA (the products are exact in
+  // fp32, the sums fp32); fp32 rows: FMAs in ascending order of d.
+  constexpr bool kMfma = sizeof(T) == 2 && DP % 32 == 0;
+  constexpr int kPtRow = D + 8;             // padded row of the transposed copy
+  // P as fp32 for the FMA path; for the MFMA path P transposed, bf16
+  // (sPt[c * kPtRow + d]), so a lane's 8 consecutive k are one 16-byte read
+  __shared__ float sP[kMfma ? 1 : D * DP];
+  __shared__ uint16_t sPt[kMfma ? DP * kPtRow : 8];
   // the staged input rows are dead once accumulated, so the projected rows
   // and their rounding residuals reuse that space
   __shared__ float sXLo[kXFloats > kLoFloats ? kXFloats : kLoFloats];
@@ -48,15 +55,24 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
   const int row0 = blockIdx.x * kRows;
   const T* Xh = X + static_cast<size_t>(h) * N * D;
 
-  for (int e = tid; e < D * DP; e += kThreads) sP[e] = io<T>::to_f32(P[e]);
+  if constexpr (kMfma) {
+    // 8 consecutive columns of one row of P per 16-byte load
+    for (int e = tid; e < D * DP / 8; e += kThreads) {
+      const int d = e / (DP / 8), c0 = (e % (DP / 8)) * 8;
+      const uint4 u = *reinterpret_cast<const uint4*>(P + static_cast<size_t>(d) * DP + c0);
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        sPt[(c0 + i) * kPtRow + d] = static_cast<uint16_t>(w[i / 2] >> (16 * (i & 1)));
+    }
+  } else {
+    for (int e = tid; e < D * DP; e += kThreads) sP[e] = io<T>::to_f32(P[e]);
+  }
   constexpr int kGroups = kThreads / DP;    // row groups
   constexpr int kRowsPerThread = kRows / kGroups;
   const int c = tid % DP;
   const int g = tid / DP;
   const size_t base = static_cast<size_t>(h) * Npad;
-  // bf16 rows: 32x32 output tiles on the bf16 MFMA (the products are exact in
-  // fp32, the sums fp32); fp32 rows: FMAs in ascending order of d.
-  constexpr bool kMfma = sizeof(T) == 2 && DP % 32 == 0;
   if constexpr (kMfma) {
     __syncthreads();
     const int w = tid >> 6, l = tid & 63;
@@ -72,10 +88,8 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
         if (arow < N) ua = *reinterpret_cast<const uint4*>(Xh + static_cast<size_t>(arow) * D + k0);
         bf16x8 va, vb;
         __builtin_memcpy(&va, &ua, 16);
-        uint16_t pb[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) pb[i] = f32_to_bf16(sP[(k0 + i) * DP + 32 * ct + (l & 31)]);
-        __builtin_memcpy(&vb, pb, 16);
+        const uint4 ub = *reinterpret_cast<const uint4*>(&sPt[(32 * ct + (l & 31)) * kPtRow + k0]);
+        __builtin_memcpy(&vb, &ub, 16);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, vb, acc, 0, 0, 0);
       }
       // lane l, register r: row 8 (r / 4) + 4 (l / 32) + r % 4, column l % 32
