@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     const bool more = ch + 1 < nchunks;
     if (more) chunk_load<DP>(regs, sh, (ch + 1) * kKeysPerChunk);
     const uint4* buf = lds + (ch & 1) * Tile<DP>::kChunkUnits;
-#pragma unroll 1
+#pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       const int tbase = ch * kKeysPerChunk + tt * 32;
       if (tbase >= s_end) break;
