@@ -212,7 +212,7 @@ def main() -> int:
     per_step = {n: d["ms_total"] / args.steps for n, d in kern.items()}
     scorer_names = ("init", "project", "pack", "sample", "threshold", "filter", "rerank",
                     "filter_retry", "rerank_retry", "fallback")
-    gather_names = ("gather_seg", "gather", "gather_merge")
+    gather_names = ("gather", "gather_merge")
     t_scorer = sum(per_step.get(n, 0.0) for n in scorer_names) / 1e3
     t_gather = sum(per_step.get(n, 0.0) for n in gather_names) / 1e3
 

@@ -63,7 +63,7 @@ int check_scorer_args(const void* Q, const void* K, const void* Pq, const void* 
 
 hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, float scale,
-                          int32_t* idx_chunk, int first, hipStream_t s) {
+                          int32_t* idx_chunk, int first, int* seg, hipStream_t s) {
   SA_TIMED("init", launch_init_chunk(p, b, first, s));
   SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
   SA_TIMED("pack", launch_pack_keys(p, b, nh, s));
@@ -73,11 +73,11 @@ hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const voi
   if (need_sample) SA_TIMED("sample", launch_sample_maxima(p, b, nh, scale, s));
   SA_TIMED("threshold", launch_threshold(p, b, nh, scale, s));
   SA_TIMED("filter", launch_filter(p, b, nh, scale, false, s));
-  SA_TIMED("rerank", launch_finalize(p, b, nh, scale, idx_chunk, false, s));
+  SA_TIMED("rerank", launch_finalize(p, b, nh, scale, idx_chunk, false, seg, s));
   // queries whose threshold was not good enough, again with a proven one
   SA_TIMED("filter_retry", launch_filter(p, b, nh, scale, true, s));
-  SA_TIMED("rerank_retry", launch_finalize(p, b, nh, scale, idx_chunk, true, s));
-  SA_TIMED("fallback", launch_fallback(p, b, nh, scale, idx_chunk, s));
+  SA_TIMED("rerank_retry", launch_finalize(p, b, nh, scale, idx_chunk, true, seg, s));
+  SA_TIMED("fallback", launch_fallback(p, b, nh, scale, idx_chunk, seg, s));
   return hipSuccess;
 }
 
@@ -188,7 +188,7 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   p.off_fblist = take(hc * Np * 4);
   p.off_fbscratch = take(static_cast<size_t>(kFallbackBlocks) * Np * 4);
   p.off_idx = take(p.with_idx ? hc * static_cast<size_t>(N) * k * 4 : 0);
-  p.off_seg = take(p.gsplit ? Np * (kGatherRanges + 1) * 4 : 0);
+  p.off_seg = take(p.gsplit ? hc * Np * (kGatherRanges + 1) * 4 : 0);
   p.off_part = take(p.gsplit ? Np * kGatherRanges * static_cast<size_t>(D + 4) * 4 : 0);
   p.total = off;
   return true;
@@ -263,7 +263,7 @@ int sparse_attn_scores_topk(const void* Q, const void* K, const void* Pq, const 
   for (int h0 = 0; h0 < p.BH; h0 += p.hc) {
     const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
     int32_t* idx_chunk = idx + static_cast<size_t>(h0) * d.N * k;
-    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, s) !=
+    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, nullptr, s) !=
         hipSuccess)
       return SA_ERR_HIP;
   }
@@ -310,7 +310,8 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
     const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
     int32_t* idx_chunk =
         idx_or_null ? idx_or_null + static_cast<size_t>(h0) * d.N * k : b.idx;
-    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, s) !=
+    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0,
+                       p.gsplit ? b.seg : nullptr, s) !=
         hipSuccess)
       return SA_ERR_HIP;
     const size_t off = static_cast<size_t>(h0) * d.N * d.D * esz;
@@ -323,8 +324,9 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
       for (int hh = 0; hh < nh; ++hh) {
         if (launch_gather_split(Qc + hh * head, Kc + hh * head, Vc + hh * head,
                                 idx_chunk + static_cast<size_t>(hh) * d.N * k, k, d.N, d.D,
-                                softmax_scale, dtype, b.seg, b.part, Oc + hh * head,
-                                s) != hipSuccess)
+                                softmax_scale, dtype,
+                                b.seg + static_cast<size_t>(hh) * p.Npad * (kGatherRanges + 1),
+                                b.part, Oc + hh * head, s) != hipSuccess)
           return SA_ERR_HIP;
       }
     } else if (timed_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc,

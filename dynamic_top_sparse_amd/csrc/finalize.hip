@@ -241,6 +241,16 @@ __device__ __forceinline__ void merge_rows(const int* a, int na, const int* b, i
   }
 }
 
+// Entries of the ascending list a[0..n) that are below x.
+__device__ __forceinline__ int count_below(const int* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] < x) lo = mid + 1; else hi = mid;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ unsigned long long rank_key(float s, int j) {
   return (static_cast<unsigned long long>(order_key(s)) << 32) |
          static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(j));
@@ -264,7 +274,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* __restrict__ q32, const float* __restrict__ k32, int N, int Npad, int k,
     int causal, int capH, int ucap, float scale, int32_t* __restrict__ idx,
     const int* __restrict__ qlist, const int* __restrict__ qlist_count, int* __restrict__ rlist,
-    int* __restrict__ rcount, int* __restrict__ fblist, WsHeader* __restrict__ hdr) {
+    int* __restrict__ rcount, int* __restrict__ fblist, int* __restrict__ seg, int segL,
+    WsHeader* __restrict__ hdr) {
   extern __shared__ unsigned char smem[];
   const int wpb = blockDim.x / kWave;
   const int w = threadIdx.x / kWave;
@@ -377,6 +388,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (n_valid <= k) {  // every valid key is kept
       issue_next();
       for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
+      if (seg != nullptr && l <= kGatherRanges)
+        seg[(hq + q) * (kGatherRanges + 1) + l] =
+            l == kGatherRanges ? n_valid : min(l * segL, n_valid);
       ++st_queries;
       continue;
     }
@@ -556,6 +570,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
     wave_sync();
     merge_rows(cj, n0, cj + n0, run2 - n0, out);
+    // the row's key-range starts: entries below r*L in either list
+    if (seg != nullptr && l <= kGatherRanges) {
+      const int x = l * segL;
+      seg[(hq + q) * (kGatherRanges + 1) + l] =
+          l == kGatherRanges ? run2 : count_below(cj, n0, x) + count_below(cj + n0, run2 - n0, x);
+    }
     for (int t = run2 + l; t < k; t += kWave) out[t] = -1;
     st_rescored += static_cast<unsigned long long>(nU);
     ++st_queries;
@@ -597,7 +617,7 @@ template <int DP>
 __global__ __launch_bounds__(kThreads) void fallback_kernel(
     const float* __restrict__ q32, const float* __restrict__ k32, const int* __restrict__ fblist,
     int N, int Npad, int k, int causal, float scale, float* __restrict__ scratch,
-    int32_t* __restrict__ idx, WsHeader* __restrict__ hdr) {
+    int32_t* __restrict__ idx, int* __restrict__ seg, int segL, WsHeader* __restrict__ hdr) {
   __shared__ float qrow[DP];
   __shared__ int hist[256];
   __shared__ int tmp[kWavesPerBlock];
@@ -670,6 +690,12 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
       eq_seen += tie ? 1 : 0;
     }
     for (int t = k_i + tid; t < k; t += kThreads) out[t] = -1;
+    if (seg != nullptr) {
+      __syncthreads();   // the row written above is visible to the workgroup
+      if (tid <= kGatherRanges)
+        seg[(hq + q) * (kGatherRanges + 1) + tid] =
+            tid == kGatherRanges ? k_i : count_below(out, k_i, tid * segL);
+    }
     if (tid == 0) atomicAdd(&hdr->fallback_queries, 1ull);
   }
 }
@@ -690,7 +716,7 @@ int resident_cus() {
 
 template <int DP>
 hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t* idx,
-                      bool retry, hipStream_t s) {
+                      bool retry, int* seg, hipStream_t s) {
   // the uncertain band is ~8x narrower with fp16 filter operands than bf16
   // (about 37 and 280 keys at the headline size)
   const int ucap = p.filt ? 512 : 128;
@@ -716,39 +742,40 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
                      b.tau, b.thr, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
                      p.capH, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
                      retry ? b.rcount : static_cast<int*>(nullptr), b.rlist, b.rcount, b.fblist,
-                     b.hdr);
+                     seg, (p.N + kGatherRanges - 1) / kGatherRanges, b.hdr);
   return hipGetLastError();
 }
 
 template <int DP>
-hipError_t fallback_t(const Plan& p, const Bufs& b, float scale, int32_t* idx, hipStream_t s) {
+hipError_t fallback_t(const Plan& p, const Bufs& b, float scale, int32_t* idx, int* seg,
+                      hipStream_t s) {
   hipLaunchKernelGGL((fallback_kernel<DP>), dim3(kFallbackBlocks), dim3(kThreads), 0, s,
                      b.qlo32, b.klo32, b.fblist, p.N, p.Npad, p.k, p.causal, scale,
-                     b.fbscratch, idx, b.hdr);
+                     b.fbscratch, idx, seg, (p.N + kGatherRanges - 1) / kGatherRanges, b.hdr);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_finalize(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, bool retry, hipStream_t s) {
+                           int32_t* idx_chunk, bool retry, int* seg, hipStream_t s) {
   switch (p.dp) {
-    case 16: return finalize_t<16>(p, b, nh, score_scale, idx_chunk, retry, s);
-    case 32: return finalize_t<32>(p, b, nh, score_scale, idx_chunk, retry, s);
-    case 64: return finalize_t<64>(p, b, nh, score_scale, idx_chunk, retry, s);
-    case 128: return finalize_t<128>(p, b, nh, score_scale, idx_chunk, retry, s);
+    case 16: return finalize_t<16>(p, b, nh, score_scale, idx_chunk, retry, seg, s);
+    case 32: return finalize_t<32>(p, b, nh, score_scale, idx_chunk, retry, seg, s);
+    case 64: return finalize_t<64>(p, b, nh, score_scale, idx_chunk, retry, seg, s);
+    case 128: return finalize_t<128>(p, b, nh, score_scale, idx_chunk, retry, seg, s);
   }
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fallback(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, hipStream_t s) {
+                           int32_t* idx_chunk, int* seg, hipStream_t s) {
   (void)nh;
   switch (p.dp) {
-    case 16: return fallback_t<16>(p, b, score_scale, idx_chunk, s);
-    case 32: return fallback_t<32>(p, b, score_scale, idx_chunk, s);
-    case 64: return fallback_t<64>(p, b, score_scale, idx_chunk, s);
-    case 128: return fallback_t<128>(p, b, score_scale, idx_chunk, s);
+    case 16: return fallback_t<16>(p, b, score_scale, idx_chunk, seg, s);
+    case 32: return fallback_t<32>(p, b, score_scale, idx_chunk, seg, s);
+    case 64: return fallback_t<64>(p, b, score_scale, idx_chunk, seg, s);
+    case 128: return fallback_t<128>(p, b, score_scale, idx_chunk, seg, s);
   }
   return hipErrorInvalidValue;
 }

@@ -309,37 +309,6 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // online-softmax partial (max m, sum l of 2^(x-m), unnormalised sum of
 // 2^(x-m) V) and a merge combines the partials of a query.
 
-// seg[q][r] = first position of row q whose key is >= r * L, r = 0..R; the
-// rows hold valid keys ascending, then -1.
-__global__ __launch_bounds__(kThreads) void segment_kernel(const int32_t* __restrict__ idx,
-                                                           int k, int N, int L,
-                                                           int* __restrict__ seg) {
-  extern __shared__ int srow_all[];
-  const int w = threadIdx.x / kWave;
-  const int l = lane_id();
-  const int q = blockIdx.x * kWaves + w;
-  if (q >= N) return;
-  int* srow = srow_all + w * k;
-  const int32_t* row = idx + static_cast<size_t>(q) * k;
-  int n = 0;
-  for (int t = l; t < k; t += kWave) {
-    const int j = row[t];
-    srow[t] = j;
-    n += j >= 0 ? 1 : 0;
-  }
-  n = wave_sum_i(n);
-  wave_sync();
-  if (l <= kGatherRanges) {
-    const int x = l * L;
-    int lo = 0, hi = n;
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (srow[mid] < x) lo = mid + 1; else hi = mid;
-    }
-    seg[static_cast<size_t>(q) * (kGatherRanges + 1) + l] = l == kGatherRanges ? n : lo;
-  }
-}
-
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void gather_part_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -441,38 +410,27 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
 
 template <typename T, int D>
 hipError_t gather_split_t(const void* Q, const void* K, const void* V, const int32_t* idx,
-                          int k, int N, float scale, int* seg, float* part, void* O,
-                          hipStream_t s, const char* const names[3]) {
-  const int L = (N + kGatherRanges - 1) / kGatherRanges;
+                          int k, int N, float scale, const int* seg, float* part,
+                          void* O, hipStream_t s, const char* const names[2]) {
   const int QB = (N + kWaves - 1) / kWaves;
-  const size_t lds = static_cast<size_t>(kWaves) * k * sizeof(int);
   const size_t lds_part = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&segment_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kWaves) * kKMax * 4);
-    if (e != hipSuccess) return e;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_part_kernel<T, D>),
+    const hipError_t e =
+        hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_part_kernel<T, D>),
                             hipFuncAttributeMaxDynamicSharedMemorySize,
                             static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  hipError_t e;
   prof_begin(names[0], s);
-  hipLaunchKernelGGL(segment_kernel, dim3(QB), dim3(kThreads), lds, s, idx, k, N, L, seg);
-  e = hipGetLastError();
-  prof_end(s);
-  if (e != hipSuccess) return e;
-  prof_begin(names[1], s);
   hipLaunchKernelGGL((gather_part_kernel<T, D>), dim3(QB * kGatherRanges), dim3(kThreads), lds_part, s,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      idx, seg, k, N, QB, scale, part);
-  e = hipGetLastError();
+  hipError_t e = hipGetLastError();
   prof_end(s);
   if (e != hipSuccess) return e;
-  prof_begin(names[2], s);
+  prof_begin(names[1], s);
   hipLaunchKernelGGL((gather_merge_kernel<T, D>), dim3(QB), dim3(kThreads), 0, s, part, N,
                      static_cast<T*>(O));
   e = hipGetLastError();
@@ -528,9 +486,9 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
 }
 
 hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
-                               int k, int N, int D, float softmax_scale, int dtype, int* seg,
+                               int k, int N, int D, float softmax_scale, int dtype, const int* seg,
                                float* part, void* O, hipStream_t s) {
-  static const char* const names[3] = {"gather_seg", "gather", "gather_merge"};
+  static const char* const names[2] = {"gather", "gather_merge"};
   if (dtype == 0) {
     if (D == 64) return gather_split_t<float, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
     if (D == 128) return gather_split_t<float, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);

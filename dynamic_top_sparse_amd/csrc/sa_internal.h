@@ -92,7 +92,7 @@ struct Bufs {
   int* fblist;          // queries queued for the exact fallback
   float* fbscratch;     // [kFallbackBlocks][Npad] exact scores
   int32_t* idx;         // optional idx rows [hc][N][k]
-  int* seg;             // split gather, one head: segment starts [Npad][kGatherRanges + 1]
+  int* seg;             // split gather: key-range starts of each row [hc][Npad][kGatherRanges + 1]
   float* part;          // split gather, one head: partials [Npad][kGatherRanges][D + 4]
 };
 Bufs bufs_of(const Plan& p, void* ws);
@@ -111,18 +111,23 @@ hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_sc
 // retry = false: every query; retry = true: the queries listed in rlist.
 hipError_t launch_filter(const Plan& p, const Bufs& b, int nh, float score_scale, bool retry,
                          hipStream_t s);
+// seg: null, or where the kernels that write idx rows also write each row's
+// key-range starts for the split gather ([nh][Npad][kGatherRanges + 1]).
 hipError_t launch_finalize(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, bool retry, hipStream_t s);
+                           int32_t* idx_chunk, bool retry, int* seg, hipStream_t s);
 hipError_t launch_fallback(const Plan& p, const Bufs& b, int nh, float score_scale,
-                           int32_t* idx_chunk, hipStream_t s);
+                           int32_t* idx_chunk, int* seg, hipStream_t s);
 hipError_t launch_dump(const Plan& p, const Bufs& b, int nh, float score_scale,
                        int row_begin, int row_count, float* S_chunk, hipStream_t s);
 hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                          int k, int nheads, int N, int D, float softmax_scale, int dtype,
                          void* O, hipStream_t s);
 // Split gather of one head whose idx rows are ascending (the fused forward's).
+// seg[q][r] (r = 0..kGatherRanges) is the first position of row q whose key
+// is >= r * ceil(N / kGatherRanges); the re-rank and fallback kernels write it
+// beside the rows.
 hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
-                               int k, int N, int D, float softmax_scale, int dtype, int* seg,
+                               int k, int N, int D, float softmax_scale, int dtype, const int* seg,
                                float* part, void* O, hipStream_t s);
 hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
                        hipStream_t s);
