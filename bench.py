@@ -4,7 +4,9 @@
 One step = one call of sparse_attn_fwd (projection -> 16-bit MFMA scorer and
 filter -> exact re-rank -> gather attention) over the whole 128K headline
 workload: B=1, H=32, N=131072, D=128, d_proj=64, k=512, bf16, non-causal,
-seeded synthetic inputs resident in HBM before timing starts.
+seeded synthetic inputs resident in HBM before timing starts.  --workload
+picks one of the other workloads instead; for the band workload a step is
+sparse_attn_band_indices followed by sparse_attn_gather.
 
 Prints one JSON line.  value = queries/s (a query is one (b, h, i) row);
 eff_tflops counts algorithmic flops only:
@@ -69,10 +71,14 @@ def algorithmic(w) -> dict:
     """Algorithmic work of one forward over workload w."""
     B, H, N, D, dp, k = w.B, w.H, w.N, w.D, w.d_proj, w.k
     BH = B * H
-    pairs = N * (N + 1) // 2 if w.causal else N * N
-    if w.causal:
+    if w.mode == "band":
+        pairs = 0
+        sum_k = sum(min(N - 1, i + w.window) - max(0, i - w.window) + 1 for i in range(N))
+    elif w.causal:
+        pairs = N * (N + 1) // 2
         sum_k = sum(min(k, i + 1) for i in range(N))
     else:
+        pairs = N * N
         sum_k = N * min(k, N)
     e = 2 if w.dtype == "bf16" else 4
     return {
@@ -107,7 +113,8 @@ def pick_heads_per_chunk(w) -> int:
 
 def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same
-    workload: query rows of head (0, 0), including that head's projections."""
+    workload: query rows of head (0, 0), including that head's projections
+    (for the band workload: the band rows and their attention)."""
     import numpy as np
     import oracle as O
     try:
@@ -116,23 +123,29 @@ def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
     except Exception:
         threads = 1
     Q1, K1, V1 = (x[n][:1, :1] for n in ("Q", "K", "V"))
-    sscale, ascale = w.d_proj ** -0.5, w.D ** -0.5
+    sscale, ascale = (w.d_proj ** -0.5 if w.d_proj else 0.0), w.D ** -0.5
     rng = np.random.default_rng(0)
 
     def run(rows):
         t = time.perf_counter()
-        O.sparse_attn_fwd(Q1, K1, V1, x["Pq"], x["Pk"], w.k, w.causal, sscale, ascale, rows)
+        if w.mode == "band":
+            idx = O.band_indices(w.N, w.window, w.window, w.k)[rows][None, None]
+            O.gather_attention(Q1, K1, V1, idx, ascale, rows)
+        else:
+            O.sparse_attn_fwd(Q1, K1, V1, x["Pq"], x["Pk"], w.k, w.causal, sscale, ascale, rows)
         return time.perf_counter() - t
 
     pilot = sorted(rng.choice(w.N, 16, replace=False).tolist())
     tp = run(pilot)
-    n_rows = int(min(4096, max(32, 16 * target_s / max(tp, 1e-3))))
+    n_rows = int(min(4096, w.N, max(32, 16 * target_s / max(tp, 1e-3))))
     rows = sorted(rng.choice(w.N, n_rows, replace=False).tolist())
     t = run(rows)
     return {"value": n_rows / t, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{n_rows} random query rows of head (0,0) of the {w.name} workload "
-                      f"through the fp64 oracle forward (scores, top-k, softmax gather), "
-                      f"including that head's key projection; {t:.1f} s"}
+            "sample": (f"{n_rows} random query rows of head (0,0) of the {w.name} workload "
+                       + ("through the fp64 oracle's band indices and softmax gather"
+                          if w.mode == "band" else
+                          "through the fp64 oracle forward (scores, top-k, softmax gather), "
+                          "including that head's key projection") + f"; {t:.1f} s")}
 
 
 def main() -> int:
@@ -161,21 +174,31 @@ def main() -> int:
     from dynamic_top_sparse_amd import workloads as W
 
     sa.sparse_attn_set_filter_dtype(torch.float16 if args.filter_dtype == "f16" else torch.bfloat16)
-    w = W.get(args.workload)
-    if w.mode != "topk":
-        print("bench.py times the top-k forward; choose a top-k workload", file=sys.stderr)
+    try:
+        w = W.get(args.workload)
+    except KeyError:
+        print(f"unknown workload {args.workload!r}; one of {sorted(W.WORKLOADS)}", file=sys.stderr)
         return 2
+    band = w.mode == "band"
     x = W.make_inputs(w, W.default_seed())
     g = {k: v.cuda() for k, v in x.items()}
-    hc = args.heads_per_chunk or pick_heads_per_chunk(w)
-    ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
-                               heads_per_chunk=hc)
     out = torch.empty_like(g["Q"])
-    torch.cuda.synchronize()
+    if band:
+        ws = None
+        idx = torch.empty((w.B, w.H, w.N, w.k), dtype=torch.int32, device="cuda")
 
-    def step():
-        sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
-                           O=out, workspace=ws)
+        def step():
+            sa.sparse_attn_band_indices(w.B, w.H, w.N, w.window, w.window, w.k, idx=idx)
+            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out)
+    else:
+        hc = args.heads_per_chunk or pick_heads_per_chunk(w)
+        ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
+                                   heads_per_chunk=hc)
+
+        def step():
+            sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
+                               O=out, workspace=ws)
+    torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         step()
@@ -190,7 +213,7 @@ def main() -> int:
     t1 = time.perf_counter()
     recs = sa.sparse_attn_profile_read()
     sa.sparse_attn_profile_enable(False)
-    stats = sa.sparse_attn_workspace_stats(ws)
+    stats = sa.sparse_attn_workspace_stats(ws) if ws is not None else None
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -219,7 +242,7 @@ def main() -> int:
     n_filter = kern.get("filter", {}).get("launches", 0)
     heads_per_chunk = (w.B * w.H * args.steps) / n_filter if n_filter else None
     # roofline of the kernel with the largest time per step
-    dom = max(per_step, key=per_step.get)
+    dom = max(per_step, key=per_step.get) if not band else "gather"
     avg_launch_s = kern[dom]["ms_total"] / kern[dom]["launches"] / 1e3
     heads = w.B * w.H * args.steps / kern[dom]["launches"]
     if dom == "filter":
@@ -251,7 +274,8 @@ def main() -> int:
     roof["avg_launch_ms"] = avg_launch_s * 1e3
 
     result = {
-        "metric": METRIC,
+        "metric": METRIC if w.name == "headline_128k" else
+        f"queries/s + eff. TFLOP/s, {'band' if band else 'top-k'} sparse attn fwd, {w.name}",
         "value": queries / (ms_step / 1e3),
         "unit": "queries/s",
         "n_gpus": 1,
@@ -265,7 +289,8 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "D": w.D,
                    "d_proj": w.d_proj, "k": w.k, "causal": w.causal, "dist": w.dist,
-                   "seed": W.default_seed(), "heads_per_chunk": heads_per_chunk},
+                   "seed": W.default_seed(), "heads_per_chunk": heads_per_chunk,
+                   **({"window": w.window} if band else {})},
         "eff_tflops": flops / (ms_step / 1e3) / 1e12,
         "scorer_frac_of_bf16_peak": ((a["F_proj"] + a["F_score"]) / t_scorer / 1e12
                                      / PEAK_BF16_TFLOPS) if t_scorer else None,
@@ -274,14 +299,16 @@ def main() -> int:
         "gather_stage_ms": t_gather * 1e3,
         "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
                                                                   key=lambda kv: -kv[1])},
-        "selection": {"candidates_per_query": stats["candidates"] / max(stats["queries"], 1),
-                      "rescored_per_query": stats["rescored"] / max(stats["queries"], 1),
-                      "fallback_queries": stats["fallback_queries"],
-                      "overflow_queries": stats["overflow_queries"],
-                      "retried_queries": stats["retried"],
-                      "filter_dtype": str(sa.sparse_attn_get_filter_dtype()).replace("torch.", "")},
         "roofline": roof,
     }
+    if stats is not None:
+        result["selection"] = {
+            "candidates_per_query": stats["candidates"] / max(stats["queries"], 1),
+            "rescored_per_query": stats["rescored"] / max(stats["queries"], 1),
+            "fallback_queries": stats["fallback_queries"],
+            "overflow_queries": stats["overflow_queries"],
+            "retried_queries": stats["retried"],
+            "filter_dtype": str(sa.sparse_attn_get_filter_dtype()).replace("torch.", "")}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(result))

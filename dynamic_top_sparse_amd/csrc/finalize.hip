@@ -274,7 +274,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const float* __restrict__ q32, const float* __restrict__ k32, int N, int Npad, int k,
     int causal, int capH, int ucap, float scale, int32_t* __restrict__ idx,
     const int* __restrict__ qlist, const int* __restrict__ qlist_count, int* __restrict__ rlist,
-    int* __restrict__ rcount, int* __restrict__ fblist, int* __restrict__ seg, int segL,
+    int* __restrict__ rcount, int* __restrict__ fblist, int* __restrict__ seg, GatherRanges gr,
     WsHeader* __restrict__ hdr) {
   extern __shared__ unsigned char smem[];
   const int wpb = blockDim.x / kWave;
@@ -390,7 +390,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int t = l; t < k; t += kWave) out[t] = t < n_valid ? t : -1;
       if (seg != nullptr && l <= kGatherRanges)
         seg[(hq + q) * (kGatherRanges + 1) + l] =
-            l == kGatherRanges ? n_valid : min(l * segL, n_valid);
+            l == kGatherRanges ? n_valid : min(gather_range_start(gr, l), n_valid);
       ++st_queries;
       continue;
     }
@@ -572,7 +572,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     merge_rows(cj, n0, cj + n0, run2 - n0, out);
     // the row's key-range starts: entries below r*L in either list
     if (seg != nullptr && l <= kGatherRanges) {
-      const int x = l * segL;
+      const int x = gather_range_start(gr, l);
       seg[(hq + q) * (kGatherRanges + 1) + l] =
           l == kGatherRanges ? run2 : count_below(cj, n0, x) + count_below(cj + n0, run2 - n0, x);
     }
@@ -617,7 +617,7 @@ template <int DP>
 __global__ __launch_bounds__(kThreads) void fallback_kernel(
     const float* __restrict__ q32, const float* __restrict__ k32, const int* __restrict__ fblist,
     int N, int Npad, int k, int causal, float scale, float* __restrict__ scratch,
-    int32_t* __restrict__ idx, int* __restrict__ seg, int segL, WsHeader* __restrict__ hdr) {
+    int32_t* __restrict__ idx, int* __restrict__ seg, GatherRanges gr, WsHeader* __restrict__ hdr) {
   __shared__ float qrow[DP];
   __shared__ int hist[256];
   __shared__ int tmp[kWavesPerBlock];
@@ -694,7 +694,7 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
       __syncthreads();   // the row written above is visible to the workgroup
       if (tid <= kGatherRanges)
         seg[(hq + q) * (kGatherRanges + 1) + tid] =
-            tid == kGatherRanges ? k_i : count_below(out, k_i, tid * segL);
+            tid == kGatherRanges ? k_i : count_below(out, k_i, gather_range_start(gr, tid));
     }
     if (tid == 0) atomicAdd(&hdr->fallback_queries, 1ull);
   }
@@ -742,7 +742,7 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
                      b.tau, b.thr, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
                      p.capH, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
                      retry ? b.rcount : static_cast<int*>(nullptr), b.rlist, b.rcount, b.fblist,
-                     seg, (p.N + kGatherRanges - 1) / kGatherRanges, b.hdr);
+                     seg, gather_ranges(p.N, p.causal), b.hdr);
   return hipGetLastError();
 }
 
@@ -751,7 +751,7 @@ hipError_t fallback_t(const Plan& p, const Bufs& b, float scale, int32_t* idx, i
                       hipStream_t s) {
   hipLaunchKernelGGL((fallback_kernel<DP>), dim3(kFallbackBlocks), dim3(kThreads), 0, s,
                      b.qlo32, b.klo32, b.fblist, p.N, p.Npad, p.k, p.causal, scale,
-                     b.fbscratch, idx, seg, (p.N + kGatherRanges - 1) / kGatherRanges, b.hdr);
+                     b.fbscratch, idx, seg, gather_ranges(p.N, p.causal), b.hdr);
   return hipGetLastError();
 }
 

@@ -305,9 +305,12 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // range at a time (workgroups are handed to the 8 XCDs in turn): an XCD's
 // working set is then one range.  Eight ranges (8 MB of K and V each at the
 // headline size) measured faster than sixteen: every (query, range) pays a
-// fixed cost, and halving their number outweighs the lower L2 hit rate.  Each (query, range) writes an
-// online-softmax partial (max m, sum l of 2^(x-m), unnormalised sum of
-// 2^(x-m) V) and a merge combines the partials of a query.
+// fixed cost, and halving their number outweighs the lower L2 hit rate.
+// Causal rows read low keys far more often than high ones, so there the
+// ranges are cut for equal expected work instead of equal width (see
+// gather_ranges); the kernel itself only reads the rows' range starts.  Each
+// (query, range) writes an online-softmax partial (max m, sum l of 2^(x-m),
+// unnormalised sum of 2^(x-m) V) and a merge combines the partials of a query.
 
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void gather_part_kernel(

@@ -20,6 +20,42 @@ constexpr int kKMax = 2048;             // largest supported k
 constexpr int kGatherRanges = 8;        // key ranges of the split gather (a multiple of 8)
 constexpr int kRetrySplit = 8;          // key segments of the retry filter (capH is a multiple of 64)
 
+// Key ranges of the split gather: range r holds keys [b[r], b[r + 1]),
+// b[0] = 0, b[kGatherRanges] = N.  Each range is served by one XCD, so the
+// ranges should carry equal work.  A non-causal row may select any key: the
+// ranges are equal.  A causal row i selects among keys 0..i; if it picks them
+// evenly, key j is read by about k * ln(N / j) rows, and the work in [0, uN)
+// is a fraction u * (1 - ln u) of the whole, so range r ends where that
+// fraction reaches (r + 1) / kGatherRanges.
+struct GatherRanges {
+  int b[kGatherRanges + 1];
+};
+
+inline GatherRanges gather_ranges(int N, int causal) {
+  static_assert(kGatherRanges == 8, "causal range table is for 8 ranges");
+  // u with u * (1 - ln u) = r / 8, r = 0..8
+  static const double kCausalFrac[kGatherRanges + 1] = {
+      0.0, 0.027132, 0.067702, 0.120268, 0.186682, 0.271132, 0.382404, 0.543687, 1.0};
+  GatherRanges g;
+  const int L = (N + kGatherRanges - 1) / kGatherRanges;
+  for (int r = 0; r <= kGatherRanges; ++r) {
+    const long long x = causal ? static_cast<long long>(kCausalFrac[r] * N + 0.5)
+                               : static_cast<long long>(r) * L;
+    g.b[r] = static_cast<int>(x < N ? x : N);
+  }
+  g.b[kGatherRanges] = N;
+  return g;
+}
+
+// Start of range r (wave-uniform table, lane-varying r): a select chain, so
+// the kernel argument is never indexed by a lane value.
+__device__ __forceinline__ int gather_range_start(const GatherRanges& g, int r) {
+  int x = g.b[0];
+#pragma unroll
+  for (int t = 1; t <= kGatherRanges; ++t) x = r == t ? g.b[t] : x;
+  return x;
+}
+
 // Byte offsets of one head chunk's buffers inside the workspace.
 struct Plan {
   int B, H, N, D, dp, k, causal, dtype;
@@ -124,7 +160,7 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
                          void* O, hipStream_t s);
 // Split gather of one head whose idx rows are ascending (the fused forward's).
 // seg[q][r] (r = 0..kGatherRanges) is the first position of row q whose key
-// is >= r * ceil(N / kGatherRanges); the re-rank and fallback kernels write it
+// is >= gather_ranges(N, causal).b[r]; the re-rank and fallback kernels write it
 // beside the rows.
 hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
                                int k, int N, int D, float softmax_scale, int dtype, const int* seg,
