@@ -46,13 +46,14 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 # a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
 # kernel's source file when the counters were taken.
 TRAFFIC = {
-    # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (8 heads)
-    "filter": {"fetch_bytes": 12.941e9, "write_bytes": 27.299e9,
-               "src": "80bb3dd81a24558c90968271a6ee996ef340a57e1272e500d86bff7888f8cd8e"},
-    "gather": {"fetch_bytes": 10.746e9, "write_bytes": 0.570e9,
-               "src": "cd391d6a58ba2512635d65c4a5c577608da9d4c8421189dd05202ec4ff8e22af"},
-    "rerank": {"fetch_bytes": 9.124e9, "write_bytes": 1.349e9,
-               "src": "b6ad2f30d278b8f01bdab876cb7dc0940e4f6c78bad9d76482e3c31661b47ffe"},
+    # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
+    # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
+    "filter": {"fetch_bytes": 114.907e9, "write_bytes": 93.642e9,
+               "src": "e85f6e26f87e4ef31f35c8e33b8a1fe04ea2f46d59c32d098b7f8707cb9f229f"},
+    "gather": {"fetch_bytes": 10.749e9, "write_bytes": 0.570e9,
+               "src": "ecbb03204d601f27a2ddd00e2f9897b66c10e4744f0e38e4583a4a64ed50da76"},
+    "rerank": {"fetch_bytes": 74.550e9, "write_bytes": 10.888e9,
+               "src": "f09f7391009ad7fca5d9e34ffc401ddb7f551cb5f0499841c17c22abe75e0188"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
 

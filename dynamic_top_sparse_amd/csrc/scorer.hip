@@ -332,20 +332,31 @@ __device__ __forceinline__ unsigned valid_rows(int lim) {
 
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
 
+// On an edge tile, rows past the end or above the causal diagonal are dropped
+// from the hit mask and their accumulators set to the bit pattern 0x80000000,
+// the smallest signed integer, so that no integer maximum picks them.
+__device__ __forceinline__ unsigned mask_edge_rows(f32x16& a, unsigned bits, unsigned valid) {
+#pragma unroll
+  for (int r = 0; r < 16; ++r)
+    if (!((valid >> r) & 1u)) a[r] = __int_as_float(static_cast<int>(0x80000000u));
+  return bits & valid;
+}
+
 // Appends the passing accumulators of one 32-query block to the lane's list,
 // in key order.  Accumulators start at -thr, so hits are exactly the
 // non-negative ones, and as signed integers their bit patterns are the
 // largest: a lane with a single hit (the common case) finds its value as the
-// integer maximum of its 16 accumulators (eight three-way maxima).  A lane
+// integer maximum of its 16 accumulators (eight three-way maxima).  That also
+// holds for an all-pass lane (every valid row is listed, whatever its sign)
+// with one valid row, because masked rows hold the smallest integer.  A lane
 // cannot index its registers by a run-time number, so the rarer lane with
-// more hits (or on an edge tile, where masked rows may also be non-negative)
-// parks its values in its own LDS column (stash[r][lane]: conflict-free) and
-// reads them back.
-__device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, bool edge,
+// more hits parks its values in its own LDS column (stash[r][lane]:
+// conflict-free) and reads them back.
+__device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
                                            float* stash, unsigned jbase, uint2* lst,
                                            unsigned& count, unsigned last) {
   const unsigned nb = static_cast<unsigned>(__builtin_popcount(bits));
-  if (!edge && nb == 1u) {
+  if (nb == 1u) {
     int x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) x[r] = __float_as_int(a[r]);
@@ -357,7 +368,7 @@ __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits, bool 
     lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), static_cast<unsigned>(m));
     ++count;
   }
-  if (nb > 1u || (edge && nb != 0u)) {
+  if (nb > 1u) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) stash[r * kThreads] = a[r];
     do {
@@ -527,23 +538,27 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 #pragma unroll
     for (int tt = 0; tt < kKeysPerChunk / 32; ++tt) {
       if (tt >= ntiles) break;
-      const f32x16 a1 = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
+      f32x16 a1 = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
       const int tbase = ch * kKeysPerChunk + tt * 32;
       const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
       unsigned bits0 = (~miss_bits(a0) & 0xFFFFu) | apm[0];
-      if (edge) bits0 &= valid_rows((causal ? min(N - 1, qq[0]) : N - 1) - static_cast<int>(jbase));
+      if (edge)
+        bits0 = mask_edge_rows(a0, bits0, valid_rows((causal ? min(N - 1, qq[0]) : N - 1) -
+                                                     static_cast<int>(jbase)));
       if (mode == 1)
         count[0] += __builtin_popcount(bits0);
       else
-        drain_hits(a0, bits0, edge, stash, jbase, list[0], count[0], last[0]);
+        drain_hits(a0, bits0, stash, jbase, list[0], count[0], last[0]);
       if (tt + 1 < ntiles) a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
       unsigned bits1 = (~miss_bits(a1) & 0xFFFFu) | apm[1];
-      if (edge) bits1 &= valid_rows((causal ? min(N - 1, qq[1]) : N - 1) - static_cast<int>(jbase));
+      if (edge)
+        bits1 = mask_edge_rows(a1, bits1, valid_rows((causal ? min(N - 1, qq[1]) : N - 1) -
+                                                     static_cast<int>(jbase)));
       if (mode == 1)
         count[1] += __builtin_popcount(bits1);
       else
-        drain_hits(a1, bits1, edge, stash, jbase, list[1], count[1], last[1]);
+        drain_hits(a1, bits1, stash, jbase, list[1], count[1], last[1]);
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
