@@ -352,9 +352,17 @@ __device__ __forceinline__ unsigned mask_edge_rows(f32x16& a, unsigned bits, uns
 // cannot index its registers by a run-time number, so the rarer lane with
 // more hits parks its values in its own LDS column (stash[r][lane]:
 // conflict-free) and reads them back.
+// The entry goes to byte (loff + 8 * min(count, last)) past `base`; in the
+// main pass `base` is the wave's first list (a scalar register) and loff the
+// lane's 32-bit list offset, so an append costs one 32-bit address add.
+__device__ __forceinline__ void put_entry(uint2* base, unsigned loff, unsigned count,
+                                          unsigned last, uint2 e) {
+  *reinterpret_cast<uint2*>(reinterpret_cast<char*>(base) + (loff + (min(count, last) << 3))) = e;
+}
+
 __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
                                            float* stash, unsigned jbase, uint2* lst,
-                                           unsigned& count, unsigned last) {
+                                           unsigned loff, unsigned& count, unsigned last) {
   const unsigned nb = static_cast<unsigned>(__builtin_popcount(bits));
   if (nb == 1u) {
     int x[16];
@@ -365,7 +373,7 @@ __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
                         imax3(x[9], x[10], x[11]), imax3(x[12], x[13], imax3(x[14], x[15], x[15])));
     const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
     // accumulator r holds key row r + (r & 12) (+4 in the upper half-wave)
-    lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), static_cast<unsigned>(m));
+    put_entry(lst, loff, count, last, make_uint2(jbase + b + (b & 12u), static_cast<unsigned>(m)));
     ++count;
   }
   if (nb > 1u) {
@@ -375,7 +383,7 @@ __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
       const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
       bits &= bits - 1u;
       const float v = stash[b * kThreads];
-      lst[min(count, last)] = make_uint2(jbase + b + (b & 12u), __float_as_uint(v));
+      put_entry(lst, loff, count, last, make_uint2(jbase + b + (b & 12u), __float_as_uint(v)));
       ++count;
     } while (bits);
   }
@@ -507,6 +515,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     list[bb] = cand + ((hq + qq[bb]) * 2 + half) * static_cast<size_t>(capH) + off;
     last[bb] = static_cast<unsigned>(capH - 1 - off);
   }
+  // Main pass: the wave's 128 lists are consecutive, so every append
+  // addresses them from the first one (wave-uniform) plus a 32-bit lane
+  // offset.  Retry passes address each lane's own list.
+  uint2* lbase[2] = {list[0], list[1]};
+  unsigned loff[2] = {0u, 0u};
+  if constexpr (mode == 0) {
+    const int qfirst = __builtin_amdgcn_readfirstlane(qq[0] - (l & 31));
+    uint2* wbase = cand + (hq + qfirst) * 2 * static_cast<size_t>(capH);
+#pragma unroll
+    for (int bb = 0; bb < 2; ++bb) {
+      lbase[bb] = wbase;
+      loff[bb] = static_cast<unsigned>((((l & 31) + 32 * bb) * 2 + half) * capH) * 8u;
+    }
+  }
   unsigned count[2] = {0u, 0u};
   // all-pass lists take every valid key: their hit mask is all ones
   const unsigned apm[2] = {all_pass[0] ? 0xFFFFu : 0u, all_pass[1] ? 0xFFFFu : 0u};
@@ -549,7 +571,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (mode == 1)
         count[0] += __builtin_popcount(bits0);
       else
-        drain_hits(a0, bits0, stash, jbase, list[0], count[0], last[0]);
+        drain_hits(a0, bits0, stash, jbase, lbase[0], loff[0], count[0], last[0]);
       if (tt + 1 < ntiles) a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
       unsigned bits1 = (~miss_bits(a1) & 0xFFFFu) | apm[1];
       if (edge)
@@ -558,7 +580,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (mode == 1)
         count[1] += __builtin_popcount(bits1);
       else
-        drain_hits(a1, bits1, stash, jbase, list[1], count[1], last[1]);
+        drain_hits(a1, bits1, stash, jbase, lbase[1], loff[1], count[1], last[1]);
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
