@@ -278,7 +278,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     WsHeader* __restrict__ hdr) {
   extern __shared__ unsigned char smem[];
   const int wpb = blockDim.x / kWave;
-  const int w = threadIdx.x / kWave;
+  // the wave index as a scalar: the query slots, and with them every query's
+  // metadata loads and list addresses, are then wave-uniform scalar values
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane_id();
   const int cap = 2 * capH;
   unsigned char* base = smem + static_cast<size_t>(w) * rerank_lds_per_wave(cap, ucap);
@@ -332,10 +334,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   auto load_cands = [&](const Meta& m) {
     const int c0 = min(m.r0, capH), c = c0 + min(m.r1, capH);
     const uint2* list0 = cand + (hq + m.q) * 2 * static_cast<size_t>(capH);
+    // list0 is wave-uniform: each lane adds a 32-bit byte offset to it
+    const char* lb = reinterpret_cast<const char*>(list0);
 #pragma unroll
     for (int j = 0; j < kPrefetch; ++j) {
       const int i = min(l + kWave * j, max(c - 1, 0));
-      pre[j] = list0[i < c0 ? i : capH + (i - c0)];
+      const unsigned e = static_cast<unsigned>(i < c0 ? i : capH + (i - c0));
+      pre[j] = *reinterpret_cast<const uint2*>(lb + e * 8u);
     }
   };
   const int stride = gridDim.x * wpb;

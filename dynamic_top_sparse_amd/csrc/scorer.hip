@@ -517,7 +517,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   // Main pass: the wave's 128 lists are consecutive, so every append
   // addresses them from the first one (wave-uniform) plus a 32-bit lane
-  // offset.  Retry passes address each lane's own list.
+  // offset (at most 128 lists of capH <= 2048 entries: under 2 MB).  Retry
+  // passes address each lane's own list.
   uint2* lbase[2] = {list[0], list[1]};
   unsigned loff[2] = {0u, 0u};
   if constexpr (mode == 0) {
