@@ -260,7 +260,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   constexpr int EPL = Vec<T>::kElems;
   constexpr int LPR = D / EPL;
   extern __shared__ float slog_all[];
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
   const int l = lane_id();
   float* slog = slog_all + w * gather_wave_floats(k);
   int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(kThreads) void gather_part_kernel(
   constexpr int LPR = D / EPL;
   constexpr int R = kGatherRanges;
   extern __shared__ float slog_all[];
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
   const int l = lane_id();
   // workgroup i -> (range, query block); consecutive workgroups land on
   // consecutive XCDs, so XCD x serves ranges x, x + 8, ... one after another
@@ -376,7 +376,7 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
                                                                 int N, T* __restrict__ O) {
   constexpr int R = kGatherRanges;
   constexpr int EPM = D / kWave;     // output elements per lane
-  const int w = threadIdx.x / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
   const int l = lane_id();
   const int q = blockIdx.x * kWaves + w;
   if (q >= N) return;
