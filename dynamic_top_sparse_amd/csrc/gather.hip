@@ -27,7 +27,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kUnroll = 8;   // row loads in flight per lane
+constexpr int kUnroll = 7;   // row loads in flight per lane (7 keeps the partial kernel at 8 waves per SIMD)
 constexpr int kXcds = 8;     // XCDs of the chip: workgroups are dealt to them in turn
 
 __device__ __forceinline__ void wave_sync() {
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
 // unnormalised sum of 2^(x-m) V) and a merge combines the partials of a query.
 
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void gather_part_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) void gather_part_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int32_t* __restrict__ idx, const int* __restrict__ seg, int k, int N, int QB,
     float scale, float* __restrict__ part) {
