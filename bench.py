@@ -48,12 +48,12 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 114.907e9, "write_bytes": 93.642e9,
-               "src": "e85f6e26f87e4ef31f35c8e33b8a1fe04ea2f46d59c32d098b7f8707cb9f229f"},
-    "gather": {"fetch_bytes": 10.749e9, "write_bytes": 0.570e9,
-               "src": "ecbb03204d601f27a2ddd00e2f9897b66c10e4744f0e38e4583a4a64ed50da76"},
-    "rerank": {"fetch_bytes": 74.550e9, "write_bytes": 10.888e9,
-               "src": "f09f7391009ad7fca5d9e34ffc401ddb7f551cb5f0499841c17c22abe75e0188"},
+    "filter": {"fetch_bytes": 117.295e9, "write_bytes": 93.555e9,
+               "src": "483fb1d1529b8f4bf14365c940fbf6a702f0b7848e335e70276f38af9eb5344e"},
+    "gather": {"fetch_bytes": 10.788e9, "write_bytes": 0.570e9,
+               "src": "4f61e306b83df383ed7f3e38bc3588b14a39231e7b8a9b7f02003768a40535be"},
+    "rerank": {"fetch_bytes": 69.472e9, "write_bytes": 10.888e9,
+               "src": "2ba40cca72df48f50476c7b04c145dfe6c023428d8faab980518edc833d25d7d"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
 
