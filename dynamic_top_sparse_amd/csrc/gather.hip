@@ -378,7 +378,10 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
   constexpr int EPM = D / kWave;     // output elements per lane
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
   const int l = lane_id();
-  const int q = blockIdx.x * kWaves + w;
+  // Last query block first: the partial kernel wrote the partials in query
+  // order, so the most recent ones, still in the memory-side cache, are read
+  // before they are pushed out.
+  const int q = (gridDim.x - 1 - blockIdx.x) * kWaves + w;
   if (q >= N) return;
   const float* recs = part + static_cast<size_t>(q) * R * (D + 4);
   float m = -INFINITY, lsum = 0.0f;
