@@ -235,6 +235,30 @@ def test_small_workspace_runs_head_by_head():
     assert torch.equal(full, one)
 
 
+def test_fused_forward_same_bits_per_chunk_size_and_stream():
+    """The fused forward with the key-range gather (N > 8192) gives the same
+    indices and outputs whether the heads go one at a time or all together,
+    and when it runs on a side stream."""
+    w = W.get("bf16_32k", N=8200, H=3, k=64)
+    g = _cuda(W.make_inputs(w, 8))
+
+    def fwd(ws=None):
+        return sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k,
+                                  workspace=ws, return_idx=True)
+
+    ref_o, ref_i = fwd(sa.allocate_workspace(g["Q"], w.d_proj, w.k, False, heads_per_chunk=3))
+    one_o, one_i = fwd(sa.allocate_workspace(g["Q"], w.d_proj, w.k, False, heads_per_chunk=1))
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, False)
+        s_o, s_i = fwd(ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_i, one_i) and torch.equal(ref_o, one_o)
+    assert torch.equal(ref_i, s_i) and torch.equal(ref_o, s_o)
+
+
 # ------------------------------------------------- full-size workloads ---
 
 def _ranges(N, causal):
