@@ -192,10 +192,18 @@ def filter_dtype(request):
     (2500, 1, 16, 64, "f32", False),        # k = 1
     (600, 700, 16, 64, "f32", False),       # k > N: all keys, -1 padding
     (1, 5, 16, 64, "f32", True),            # a single query
+    (5000, 96, 128, 64, "bf16", True),      # d_proj 128
 ])
 def test_topk_and_forward_small_shapes_all_rows(N, k, dp, D, dtype, causal, filter_dtype):
     w = W.Workload("case", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
     run_case(w, seed=N + k)
+
+
+def test_largest_k_with_key_range_gather_all_rows():
+    """k at its maximum (2048, lists of 2048 entries per half) past the
+    threshold path's minimum N and the key-range gather's, d_proj 128."""
+    w = W.Workload("case", 1, 1, 9000, 128, "bf16", d_proj=128, k=2048)
+    run_case(w, seed=77)
 
 
 def test_mixture_causal_small_all_rows(filter_dtype):
