@@ -48,11 +48,11 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 117.295e9, "write_bytes": 93.555e9,
+    "filter": {"fetch_bytes": 115.377e9, "write_bytes": 93.430e9,
                "src": "483fb1d1529b8f4bf14365c940fbf6a702f0b7848e335e70276f38af9eb5344e"},
-    "gather": {"fetch_bytes": 10.788e9, "write_bytes": 0.570e9,
-               "src": "4f61e306b83df383ed7f3e38bc3588b14a39231e7b8a9b7f02003768a40535be"},
-    "rerank": {"fetch_bytes": 69.472e9, "write_bytes": 10.888e9,
+    "gather": {"fetch_bytes": 10.787e9, "write_bytes": 0.570e9,
+               "src": "a514ea6c2ed123007b168f426b66cfd2001bc7c81c5c709495a5c2a896de3bf6"},
+    "rerank": {"fetch_bytes": 69.470e9, "write_bytes": 10.888e9,
                "src": "2ba40cca72df48f50476c7b04c145dfe6c023428d8faab980518edc833d25d7d"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
