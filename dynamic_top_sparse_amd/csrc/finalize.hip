@@ -418,7 +418,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       auto stage = [&](int i, uint2 e) {
         const uint32_t key = order_key((__uint_as_float(e.y) + tv) * f);
         ck[i] = key;
-        cj[i] = static_cast<int>(e.x);
+        cj[i] = candidate_key(e.x);
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       };

@@ -56,6 +56,14 @@ __device__ __forceinline__ int gather_range_start(const GatherRanges& g, int r) 
   return x;
 }
 
+// A candidate entry's key field.  The filter's accumulator r of tile-half h
+// of the 32-key tile starting at key 32T covers key 32T + 4h + r + (r & 12);
+// the entry stores x = 32T + 16h + r (one add in the filter), and the key is
+// x + (x & 12) - 12 * ((x >> 4) & 1).
+__device__ __forceinline__ int candidate_key(unsigned x) {
+  return static_cast<int>(x + (x & 12u) - 12u * ((x >> 4) & 1u));
+}
+
 // Byte offsets of one head chunk's buffers inside the workspace.
 struct Plan {
   int B, H, N, D, dp, k, causal, dtype;

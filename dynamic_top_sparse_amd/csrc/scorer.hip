@@ -360,8 +360,10 @@ __device__ __forceinline__ void put_entry(uint2* base, unsigned loff, unsigned c
   *reinterpret_cast<uint2*>(reinterpret_cast<char*>(base) + (loff + (min(count, last) << 3))) = e;
 }
 
+// The key field of an entry is jenc + r (jenc = tile start + 16 * tile half;
+// candidate_key() recovers the key).
 __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
-                                           float* stash, unsigned jbase, uint2* lst,
+                                           float* stash, unsigned jenc, uint2* lst,
                                            unsigned loff, unsigned& count, unsigned last) {
   const unsigned nb = static_cast<unsigned>(__builtin_popcount(bits));
   if (nb == 1u) {
@@ -373,7 +375,7 @@ __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
                         imax3(x[9], x[10], x[11]), imax3(x[12], x[13], imax3(x[14], x[15], x[15])));
     const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
     // accumulator r holds key row r + (r & 12) (+4 in the upper half-wave)
-    put_entry(lst, loff, count, last, make_uint2(jbase + b + (b & 12u), static_cast<unsigned>(m)));
+    put_entry(lst, loff, count, last, make_uint2(jenc + b, static_cast<unsigned>(m)));
     ++count;
   }
   if (nb > 1u) {
@@ -383,7 +385,7 @@ __device__ __forceinline__ void drain_hits(const f32x16& a, unsigned bits,
       const unsigned b = static_cast<unsigned>(__builtin_ctz(bits));
       bits &= bits - 1u;
       const float v = stash[b * kThreads];
-      put_entry(lst, loff, count, last, make_uint2(jbase + b + (b & 12u), __float_as_uint(v)));
+      put_entry(lst, loff, count, last, make_uint2(jenc + b, __float_as_uint(v)));
       ++count;
     } while (bits);
   }
@@ -563,7 +565,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (tt >= ntiles) break;
       f32x16 a1 = tile_scores_c<DP, F>(buf, tt, b1, cinit[1]);
       const int tbase = ch * kKeysPerChunk + tt * 32;
-      const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);
+      const unsigned jbase = static_cast<unsigned>(tbase + 4 * half);   // key of accumulator 0
+      const unsigned jenc = static_cast<unsigned>(tbase + 16 * half);   // entry encoding base
       const bool edge = (tbase + 32 > N) || (causal && tbase + 31 > qw);
       unsigned bits0 = (~miss_bits(a0) & 0xFFFFu) | apm[0];
       if (edge)
@@ -572,7 +575,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (mode == 1)
         count[0] += __builtin_popcount(bits0);
       else
-        drain_hits(a0, bits0, stash, jbase, lbase[0], loff[0], count[0], last[0]);
+        drain_hits(a0, bits0, stash, jenc, lbase[0], loff[0], count[0], last[0]);
       if (tt + 1 < ntiles) a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
       unsigned bits1 = (~miss_bits(a1) & 0xFFFFu) | apm[1];
       if (edge)
@@ -581,7 +584,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       if (mode == 1)
         count[1] += __builtin_popcount(bits1);
       else
-        drain_hits(a1, bits1, stash, jbase, lbase[1], loff[1], count[1], last[1]);
+        drain_hits(a1, bits1, stash, jenc, lbase[1], loff[1], count[1], last[1]);
     }
     if (more) chunk_store<DP>(regs, lds + ((ch + 1) & 1) * Tile<DP>::kChunkUnits);
     __syncthreads();
