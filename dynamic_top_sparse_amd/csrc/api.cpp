@@ -157,8 +157,9 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   }
   p.with_idx = with_idx ? 1 : 0;
   // K and V rows of a head beyond one XCD's L2: the fused forward gathers by
-  // key range
-  p.gsplit = N > 8192 ? 1 : 0;
+  // key range (its row offsets are 32-bit bytes within one head)
+  const size_t head_bytes = static_cast<size_t>(N) * D * (dtype ? 2 : 4);
+  p.gsplit = N > 8192 && head_bytes <= 0xFFFFFFFFull ? 1 : 0;
   const size_t hc = static_cast<size_t>(p.hc);
   const size_t Np = static_cast<size_t>(p.Npad);
   // queue entries and per-chunk row indices are int

@@ -296,6 +296,157 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   }
 }
 
+// --------------------------------------------- split gather, bf16 rows ---
+// The split gather serves the fused forward, whose rows hold keys in [0, N)
+// only, so an entry is clamped into range (one v_med3) rather than checked:
+// the few slack entries a last partial load reads past the segment (stale
+// LDS words) then address a real row, and their results are dropped.  Row
+// offsets are 32-bit byte offsets from the head's base (the host keeps the
+// head's rows under 4 GiB), and whole blocks of kUnroll loads run as
+// straight-line code; only the segment's last partial block tests each load.
+template <int D>
+__device__ __forceinline__ unsigned row_offset(const int* __restrict__ row, int t, int N,
+                                               unsigned lane_off) {
+  const int j = min(max(row[t], 0), N - 1);
+  return static_cast<unsigned>(j) * static_cast<unsigned>(D * 2) + lane_off;
+}
+
+// group_sum over aligned groups of G lanes (G <= 16) for U values at once,
+// one butterfly step across all of them at a time: no DPP step then waits
+// on the one before it.
+template <int G, int U>
+__device__ __forceinline__ void group_sum_n(float (&v)[U]) {
+  static_assert(G >= 1 && G <= 16 && (G & (G - 1)) == 0, "power-of-two groups up to 16");
+  if constexpr (G >= 2) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] += dpp_f<kDppQuadXor1>(v[u]);
+  }
+  if constexpr (G >= 4) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] += dpp_f<kDppQuadXor2>(v[u]);
+  }
+  if constexpr (G >= 8) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] += dpp_f<kDppHalfMirror>(v[u]);
+  }
+  if constexpr (G >= 16) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] += dpp_f<kDppMirror>(v[u]);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void logits_bf16_split(const bf16_t* __restrict__ qrow,
+                                                  const bf16_t* __restrict__ Kh,
+                                                  const int* __restrict__ row, int n, int N,
+                                                  float scale, float* __restrict__ slog) {
+  constexpr int EPL = 8, LPR = D / EPL, RPI = kWave / LPR, BLK = RPI * kUnroll;
+  const int l = lane_id();
+  const int g = l / LPR;
+  const unsigned lane_off = static_cast<unsigned>((l % LPR) * EPL * 2);
+  const char* kb = reinterpret_cast<const char*>(Kh);
+  const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + (l % LPR) * EPL);
+  bf16x2 qp[4];
+  __builtin_memcpy(qp, &q4, 16);
+  auto dot_of = [&](const uint4& kv) {   // this lane's part of the row's dot product
+    bf16x2 kp[4];
+    __builtin_memcpy(kp, &kv, 16);
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[i], dot, false);
+    return dot;
+  };
+  int tb = 0;
+  for (; tb + BLK <= n; tb += BLK) {
+    uint4 kv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      kv[u] = *reinterpret_cast<const uint4*>(kb + row_offset<D>(row, tb + u * RPI + g, N, lane_off));
+    float dot[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dot[u] = dot_of(kv[u]);
+    group_sum_n<LPR>(dot);
+    if ((l % LPR) == 0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) slog[tb + u * RPI + g] = dot[u] * scale;
+    }
+  }
+  if (tb < n) {
+    const int nu = (n - tb + RPI - 1) / RPI;   // loads holding rows (uniform)
+    uint4 kv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      kv[u] = *reinterpret_cast<const uint4*>(kb + row_offset<D>(row, tb + u * RPI + g, N, lane_off));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const float dot = group_sum<LPR>(dot_of(kv[u]));
+      if ((l % LPR) == 0 && t < n) slog[t] = dot * scale;
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void weighted_rows_bf16_split(const bf16_t* __restrict__ Vh,
+                                                         const int* __restrict__ row, int n,
+                                                         int N, const float* __restrict__ slog,
+                                                         float (&acc)[8]) {
+  constexpr int EPL = 8, LPR = D / EPL, RPI = kWave / LPR, BLK = RPI * kUnroll;
+  const int l = lane_id();
+  const int g = l / LPR;
+  const unsigned lane_off = static_cast<unsigned>((l % LPR) * EPL * 2);
+  const char* vb = reinterpret_cast<const char*>(Vh);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+  auto add_row = [&](const uint4& v, float w) {
+    float vf[EPL];
+    Vec<bf16_t>::unpack(v, vf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, vf[e], acc[e]);
+  };
+  int tb = 0;
+  for (; tb + BLK <= n; tb += BLK) {
+    uint4 vv[kUnroll];
+    float wt[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = tb + u * RPI + g;
+      wt[u] = slog[t];
+      vv[u] = *reinterpret_cast<const uint4*>(vb + row_offset<D>(row, t, N, lane_off));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) add_row(vv[u], wt[u]);
+  }
+  if (tb < n) {
+    const int nu = (n - tb + RPI - 1) / RPI;   // loads holding rows (uniform)
+    uint4 vv[kUnroll];
+    float wt[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const float wr = slog[t];
+      wt[u] = t < n ? wr : 0.0f;   // slack entries past the segment weigh nothing
+      vv[u] = *reinterpret_cast<const uint4*>(vb + row_offset<D>(row, t, N, lane_off));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      add_row(vv[u], wt[u]);
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e)
+      acc[e] = o == 32 ? sum_xor32(acc[e]) : o == 16 ? sum_xor16(acc[e])
+                                                   : acc[e] + __shfl_xor(acc[e], o, kWave);
+  }
+}
+
 // --------------------------------------------------------- split gather ---
 // The fused forward's idx rows are ascending, so the keys of a row that fall
 // in one key range form one contiguous segment of it.  A head's K and V rows
@@ -344,9 +495,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   }
   stage_entries(idx + static_cast<size_t>(q) * k, s0, s1, sidx);
   const int32_t* row = sidx;
-  int bad = 0;
-  logits<T, D>(Q + static_cast<size_t>(q) * D, K, row, s0, s1, N, scale * kLog2e, slog, bad);
-  if (bad) atomicOr(&g_index_error_flag, 1);
+  if constexpr (sizeof(T) == 2) {
+    logits_bf16_split<D>(Q + static_cast<size_t>(q) * D, K, row, s1 - s0, N, scale * kLog2e, slog);
+  } else {
+    int bad = 0;
+    logits<T, D>(Q + static_cast<size_t>(q) * D, K, row, s0, s1, N, scale * kLog2e, slog, bad);
+    if (bad) atomicOr(&g_index_error_flag, 1);
+  }
   wave_sync();
   float sum;
   const float mx = softmax_weights(slog, s1 - s0, sum);
@@ -356,7 +511,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(8))) v
   }
   wave_sync();
   float acc[EPL];
-  weighted_rows<T, D>(V, row, s0, s1, N, slog, acc);
+  if constexpr (sizeof(T) == 2)
+    weighted_rows_bf16_split<D>(V, row, s1 - s0, N, slog, acc);
+  else
+    weighted_rows<T, D>(V, row, s0, s1, N, slog, acc);
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   if (g == 0) {
     float4* dst = reinterpret_cast<float4*>(rec + 4 + e0);

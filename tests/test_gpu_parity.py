@@ -276,14 +276,16 @@ def _ranges(N, causal):
     return r
 
 
-@pytest.mark.parametrize("dtype,D,causal", [("f32", 64, False), ("bf16", 128, False),
-                                             ("bf16", 128, True)])
-def test_fused_forward_key_range_gather(dtype, D, causal):
+@pytest.mark.parametrize("dtype,D,causal,k", [("f32", 64, False, 64), ("bf16", 128, False, 64),
+                                               ("bf16", 128, True, 64), ("bf16", 64, False, 512),
+                                               ("bf16", 128, True, 512)])
+def test_fused_forward_key_range_gather(dtype, D, causal, k):
     """Past N = 8192 the fused forward gathers by key range (partials per
     range, then a merge); ragged N, empty ranges and, causally, rows whose
-    keys all fall in the first ranges."""
+    keys all fall in the first ranges.  With k = 512 a range holds enough of
+    a row's keys for whole blocks of row loads, not only a last partial one."""
     w = W.get("bf16_32k", N=8200, H=2, D=D, dtype=dtype, d_proj=64 if D == 128 else 16,
-              k=64, causal=causal)
+              k=k, causal=causal)
     run_case(w, seed=5, rows=[(0, 300), (4000, 200), (8000, 200)])
 
 
