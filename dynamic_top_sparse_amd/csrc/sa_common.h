@@ -42,14 +42,18 @@ template <> struct io<bf16_t> {
 // Monotone map of fp32 onto uint32: a < b  <=>  key(a) < key(b); -0.0 and
 // +0.0 map to the same key (equal scores tie, and the tie goes to the lower
 // key index).
+// Non-negative values get the sign bit set, negative ones all bits flipped:
+// u ^ ((u >> 31, arithmetic) | sign bit), with no compare or select.  Adding
+// +0.0 first turns -0.0 into +0.0 (round to nearest) and changes nothing else.
 __device__ __forceinline__ uint32_t order_key(float f) {
-  if (f == 0.0f) f = 0.0f;  // canonicalise -0.0
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(f + 0.0f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
+// Inverse on keys of non-NaN values: a key with the sign bit set came from a
+// non-negative value (clear the bit), any other from a negative one (flip all).
 __device__ __forceinline__ float key_to_float(uint32_t k) {
-  uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
-  return __uint_as_float(u);
+  const uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(k) >> 31);
+  return __uint_as_float(k ^ (~m | 0x80000000u));
 }
 
 // ---------------------------------------------------------- exact score ---
