@@ -242,56 +242,91 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
 }
 
 // -------------------------------------------------------------- threshold ---
-// One thread per query: tau is (a lower rounding of) the r-th largest of the
-// query's block maxima, found by a 4-bit-digit radix select over the top 16
-// bits of their order keys, the part the sample pass stores (rounding down
-// only adds candidates).  About
-// beta * k keys are expected above it.
-__global__ __launch_bounds__(kThreads) void threshold_kernel(
+// tau is (a lower rounding of) the r-th largest of a query's block maxima,
+// found by a 4-bit-digit radix select over the top 16 bits of their order
+// keys, the part the sample pass stores (rounding down only adds
+// candidates).  About beta * k keys are expected above it.
+// A thread selects for two consecutive queries, whose maxima of one index
+// share a 32-bit word, so each pass reads one word per index for both.  Eight
+// of those loads are issued before any is counted, and each thread counts
+// digits in its own LDS columns with LDS atomic adds (no read-modify-write
+// round trip): the kernel is bound by load latency, not by arithmetic.
+constexpr int kThrQ = 2;          // queries per thread
+constexpr int kThrThreads = 256;  // 512 queries per workgroup
+constexpr int kThrUnroll = 8;     // maxima loads in flight per thread
+
+__global__ __launch_bounds__(kThrThreads) void threshold_kernel(
     const uint16_t* __restrict__ bm, int N, int Npad, int Ns, int sstride, int k, int causal,
     int capH, float beta, float* __restrict__ tau) {
-  __shared__ int hist[16 * kThreads];
+  // counts of digit d for query j of thread t: hist[(d * kThrQ + j) * kThrThreads + t]
+  __shared__ uint32_t hist[16 * kThrQ * kThrThreads];
   const int h = blockIdx.y;
   const int tid = threadIdx.x;
-  const int q = blockIdx.x * kThreads + tid;
-  const size_t stride = static_cast<size_t>(gridDim.y) * Npad;
-  const uint16_t* bmh = bm + static_cast<size_t>(h) * Npad;
-  if (q >= Npad) return;  // whole-block uniform: Npad is a multiple of 256
-  float result = -INFINITY;
-  const int n_valid = causal ? q + 1 : N;
-  const bool active = q < N && n_valid > 2 * capH - 64;
-  const int ns_valid = causal ? min(Ns, q / sstride + 1) : Ns;
-  const int k_i = min(k, n_valid);
-  const int r0 = sample_rank(k_i, ns_valid, n_valid, beta);
-  const int nb = sample_blocks(ns_valid, sample_block(ns_valid, r0));
-  const int r = min(r0, nb);
-  uint32_t prefix = 0;
-  int K = r;
+  const int q0 = (static_cast<int>(blockIdx.x) * kThrThreads + tid) * kThrQ;
+  const size_t stride = static_cast<size_t>(gridDim.y) * Npad;   // between a query's maxima
+  // maxima e of queries q0 and q0 + 1: the 32-bit word at bmh + e * stride
+  const uint16_t* bmh = bm + static_cast<size_t>(h) * Npad + q0;
+  int nb[kThrQ], K[kThrQ];
+  uint32_t prefix[kThrQ];
+  int nbmax = 0;
+#pragma unroll
+  for (int j = 0; j < kThrQ; ++j) {
+    const int q = q0 + j;
+    const int n_valid = causal ? q + 1 : N;
+    const bool active = q < N && n_valid > 2 * capH - 64;
+    const int ns_valid = causal ? min(Ns, q / sstride + 1) : Ns;
+    const int k_i = min(k, n_valid);
+    const int r0 = sample_rank(k_i, ns_valid, n_valid, beta);
+    const int nbj = sample_blocks(ns_valid, sample_block(ns_valid, r0));
+    nb[j] = active ? nbj : 0;    // an idle query reads nothing
+    K[j] = min(r0, nbj);
+    prefix[j] = 0;
+    nbmax = max(nbmax, nb[j]);
+  }
+  uint32_t* col = hist + tid;
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 28 - 4 * pass;
     const uint32_t pmask = pass == 0 ? 0u : (0xFFFFFFFFu << (shift + 4));
 #pragma unroll
-    for (int d = 0; d < 16; ++d) hist[d * kThreads + tid] = 0;
-    if (active) {
-      for (int e = 0; e < nb; ++e) {
-        const uint32_t key = static_cast<uint32_t>(bmh[static_cast<size_t>(e) * stride + q]) << 16;
-        if ((key & pmask) == prefix) hist[((key >> shift) & 15u) * kThreads + tid] += 1;
+    for (int i = 0; i < 16 * kThrQ; ++i) col[i * kThrThreads] = 0u;
+    for (int e0 = 0; e0 < nbmax; e0 += kThrUnroll) {
+      uint32_t w[kThrUnroll];
+#pragma unroll
+      for (int u = 0; u < kThrUnroll; ++u) {
+        const int e = min(e0 + u, nbmax - 1);   // past nbmax: a row already read, not counted
+        w[u] = *reinterpret_cast<const uint32_t*>(bmh + static_cast<size_t>(e) * stride);
       }
+#pragma unroll
+      for (int u = 0; u < kThrUnroll; ++u) {
+        const int e = e0 + u;
+#pragma unroll
+        for (int j = 0; j < kThrQ; ++j) {
+          const uint32_t key = j ? (w[u] & 0xFFFF0000u) : (w[u] << 16);   // query q0 + j
+          if (e < nb[j] && (key & pmask) == prefix[j])
+            atomicAdd(&col[(((key >> shift) & 15u) * kThrQ + j) * kThrThreads], 1u);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kThrQ; ++j) {
+      if (nb[j] == 0) continue;
       int cum = 0, digit = 0;
       for (int d = 15; d >= 0; --d) {
-        const int c = hist[d * kThreads + tid];
-        if (cum + c >= K) { digit = d; break; }
+        const int c = static_cast<int>(col[(d * kThrQ + j) * kThrThreads]);
+        if (cum + c >= K[j]) { digit = d; break; }
         cum += c;
       }
-      K -= cum;
-      prefix |= static_cast<uint32_t>(digit) << shift;
+      K[j] -= cum;
+      prefix[j] |= static_cast<uint32_t>(digit) << shift;
     }
   }
-  if (active) {
+#pragma unroll
+  for (int j = 0; j < kThrQ; ++j) {
     // block maxima are stored as filter scores already (score factor applied)
-    if (prefix > order_key(-INFINITY)) result = key_to_float(prefix);
+    float result = -INFINITY;
+    if (nb[j] > 0 && prefix[j] > order_key(-INFINITY)) result = key_to_float(prefix[j]);
+    tau[static_cast<size_t>(h) * Npad + q0 + j] = result;
   }
-  tau[static_cast<size_t>(h) * Npad + q] = active ? result : -INFINITY;
 }
 
 // ------------------------------------------------------------ filter pass ---
@@ -670,9 +705,9 @@ hipError_t launch_sample_maxima(const Plan& p, const Bufs& b, int nh, float scor
 
 hipError_t launch_threshold(const Plan& p, const Bufs& b, int nh, float score_scale,
                             hipStream_t s) {
-  const dim3 grid(p.Npad / kThreads, nh);
+  const dim3 grid(p.Npad / (kThrThreads * kThrQ), nh);   // Npad is a multiple of 512
   (void)score_scale;
-  hipLaunchKernelGGL(threshold_kernel, grid, dim3(kThreads), 0, s, b.bm, p.N, p.Npad, p.Ns,
+  hipLaunchKernelGGL(threshold_kernel, grid, dim3(kThrThreads), 0, s, b.bm, p.N, p.Npad, p.Ns,
                      p.sstride, p.k, p.causal, p.capH, kTauBeta, b.tau);
   return hipGetLastError();
 }
