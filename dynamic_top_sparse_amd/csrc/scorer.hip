@@ -116,6 +116,17 @@ __device__ __forceinline__ int acc_row(int r, int half) {
   return 8 * (r >> 2) + 4 * half + (r & 3);
 }
 
+// Rows of a lane's accumulators are key offsets r + (r & 12) (+4 for the
+// upper half-wave), increasing in r, so the keys beyond `lim` (relative to
+// the lane's first key) form a suffix of r.  Returns the mask of the valid
+// accumulators.
+__device__ __forceinline__ unsigned valid_rows(int lim) {
+  if (lim < 0) return 0u;
+  int r0 = min(4, lim + 1) + min(4, max(0, lim - 7)) + min(4, max(0, lim - 15)) +
+           min(4, max(0, lim - 23));
+  return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
+}
+
 // ------------------------------------------------------------ sample pass ---
 // Block maxima of one lane's 16 accumulators (keys 8*(r/4) + r%4 + 4*half of
 // the tile, in r order) for blocks of B consecutive accumulators, stored as
@@ -153,7 +164,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
   __shared__ uint4 lds[2 * Tile<DP>::kChunkUnits];
   const int h = blockIdx.y;
   const int q0 = blockIdx.x * kQueriesPerBlock;
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);   // wave-uniform, scalar
   const int l = lane_id();
   const int half = l >> 5;
   const int qw = q0 + w * kWaveQueries;
@@ -185,6 +196,7 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
     last_tile[bb] = q < N && n_valid > 2 * capH - 64 ? (nsv - 1) / 32 : -1;
   }
 
+  const int sshift = __builtin_ctz(static_cast<unsigned>(sstride));
   // sample keys t with s*t <= last query of the block (causal), else all
   int s_end = Ns;
   if (causal) s_end = min(Ns, (min(N, q0 + kQueriesPerBlock) - 1) / sstride + 1);
@@ -205,18 +217,21 @@ __global__ __launch_bounds__(kThreads) void sample_maxima_kernel(
       a[0] = tile_scores<DP, F>(buf, tt, b0);
       a[1] = tile_scores<DP, F>(buf, tt, b1);
       const int tile = tbase / 32;
-      // samples past the end or after a query (causal) only occur on edge tiles
+      // samples past the end or after a query (causal) only occur on edge
+      // tiles (a wave-uniform test: qw is the wave's first query)
       const bool edge = tbase + 32 > s_end || (causal && (tbase + 31) * sstride > qw);
 #pragma unroll
       for (int bb = 0; bb < 2; ++bb) {
         const float fq = bb ? fb : fa;   // > 0: scaling commutes with the maxima
         if (edge) {
+          // valid rows: sample t < s_end and, causally, t * sstride <= the
+          // query (sstride is a power of two), a prefix of the rows
+          int lim = s_end - 1;
+          if (causal) lim = min(lim, qq[bb] >> sshift);
+          const unsigned vr = valid_rows(lim - (tbase + 4 * half));
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int t = tbase + acc_row(r, half);
-            const bool ok = t < s_end && (!causal || t * sstride <= qq[bb]);
-            a[bb][r] = ok ? a[bb][r] : -INFINITY;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (!((vr >> r) & 1u)) a[bb][r] = -INFINITY;
         }
         if (tile > last_tile[bb]) continue;
         const int B = Bq[bb];
@@ -352,17 +367,6 @@ __device__ __forceinline__ f32x16 tile_scores_c(const uint4* __restrict__ lds, i
   for (int ks = 1; ks < Tile<DP>::kKSteps; ++ks)
     acc = F::mfma(lds[lds_unit<DP>(key, 2 * ks + (l >> 5))], b[ks], acc);
   return acc;
-}
-
-// Rows of a lane's accumulators are key offsets r + (r & 12) (+4 for the
-// upper half-wave), increasing in r, so the keys beyond `lim` (relative to
-// the lane's first key) form a suffix of r.  Returns the mask of the valid
-// accumulators.
-__device__ __forceinline__ unsigned valid_rows(int lim) {
-  if (lim < 0) return 0u;
-  int r0 = min(4, lim + 1) + min(4, max(0, lim - 7)) + min(4, max(0, lim - 15)) +
-           min(4, max(0, lim - 23));
-  return r0 >= 16 ? 0xFFFFu : ((1u << r0) - 1u);
 }
 
 __device__ __forceinline__ int imax3(int a, int b, int c) { return max(max(a, b), c); }
