@@ -48,11 +48,11 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 115.367e9, "write_bytes": 93.516e9,
-               "src": "1d8086dcc1b9f97c821e7ebe386254e7d3c19d55a4a4a94c6a06ab5416021bc7"},
+    "filter": {"fetch_bytes": 120.957e9, "write_bytes": 93.378e9,
+               "src": "c2fd4f618ca754cb8861533b8c8a12713eb99adaa6da0ee9097139d27472aa58"},
     "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
                "src": "5877c0c9b38d66bf2db13d14434eb11b76d2099e41d909161337876ede489689"},
-    "rerank": {"fetch_bytes": 69.473e9, "write_bytes": 10.888e9,
+    "rerank": {"fetch_bytes": 69.471e9, "write_bytes": 10.888e9,
                "src": "f4407d799910cd43fb4a75b18a8fca50eec3133ed9f1aa1a0616b23d5c45d73e"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
