@@ -7,6 +7,6 @@ from .sparse_attn_oracle import (  # noqa: F401
     f64, project, valid_keys, score_rows, scores, topk_row, topk_rows,
     topk_indices, brute_force_topk, attend_row, gather_attention,
     sparse_attn_fwd, band_indices, dense_attention, local_mask,
-    brute_force_attention,
+    brute_force_attention, attend_row_backward, sparse_attn_backward,
 )
 from .compare import row_invariants, set_overlap  # noqa: F401

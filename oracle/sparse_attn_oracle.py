@@ -27,9 +27,21 @@ float64 with NumPy, one step per statement, following the pages:
      page "nxmr.cn/news/163144", §2.2): query i keeps keys
      max(0, i-w_left) .. min(N-1, i+w_right).
 
+  5. Backward (same page, §2.3, top-k selection and gradient flow): the
+     forward keeps the hard top-k; in the backward the selected positions'
+     gradients flow normally and unselected positions get zero; the scorer
+     receives its gradient through the selected positions' attention
+     weights.  Reading taken here (a straight-through estimator): the
+     scorer score S_ij of a selected pair receives the gradient of that
+     pair's attention logit, dS_ij = dlogit_ij, and unselected pairs receive
+     nothing; from there the chain rule runs through S = score_scale ·
+     (Q·Pq)·(K·Pk)ᵀ to Pq, Pk, Q and K.
+
 Every function below is pinned by tests against things other than itself
-(brute force, closed forms, dense attention, a hand-derived example); see
-tests/test_oracle_pins.py.  Nothing here is "parity unpinned".
+(brute force, closed forms, dense attention, a hand-derived example, torch
+autograd and finite differences for the backward); see
+tests/test_oracle_pins.py and tests/test_oracle_backward.py.  Nothing here
+is "parity unpinned".
 """
 from __future__ import annotations
 
@@ -238,3 +250,85 @@ def brute_force_attention(q: Sequence[float], Krows: Iterable[Sequence[float]],
     tot = sum(w)
     D = len(Vrows[0])
     return [sum(w[t] * Vrows[t][d] for t in range(len(w))) / tot for d in range(D)]
+
+
+# -------------------------------------------------------- 5. backward ---
+
+def attend_row_backward(q, Kh, Vh, sel, softmax_scale, dO_row):
+    """Gradients of one query's output over the key list ``sel`` (entries < 0
+    skipped, repeats counted as often as they appear), for an upstream
+    gradient dO_row: returns (dq [D], dK_rows [k, D], dV_rows [k, D],
+    dlogit [k]) with zero rows for skipped entries.  Softmax backward: with
+    weights p_t and dp_t = dO·V_t, dlogit_t = p_t (dp_t - sum_u p_u dp_u)."""
+    k = sel.shape[0]
+    D = Kh.shape[1]
+    dq = np.zeros(D)
+    dK = np.zeros((k, D))
+    dV = np.zeros((k, Vh.shape[1]))
+    dlogit = np.zeros(k)
+    ok = sel >= 0
+    if not np.any(ok):
+        return dq, dK, dV, dlogit
+    js = sel[ok]
+    logits = softmax_scale * (Kh[js] @ q)
+    w = np.exp(logits - logits.max())
+    p = w / w.sum()
+    dp = Vh[js] @ dO_row
+    dl = p * (dp - np.dot(p, dp))
+    dlogit[ok] = dl
+    dq = softmax_scale * (dl @ Kh[js])
+    dK[ok] = softmax_scale * np.outer(dl, q)
+    dV[ok] = np.outer(p, dO_row)
+    return dq, dK, dV, dlogit
+
+
+def sparse_attn_backward(Q, K, V, Pq, Pk, idx, dO, score_scale: float, softmax_scale: float,
+                         scorer_grad: bool = True):
+    """Backward of the whole forward for fixed index sets ``idx`` [B,H,N,k].
+
+    Attention path: dQ, dK, dV of softmax attention over each row's kept
+    keys; a key receives gradient only from the rows that kept it.
+    Scorer path (scorer_grad, the straight-through reading of §2.3): the
+    score of each kept pair (i, j) receives that pair's logit gradient,
+    dS_ij = dlogit_ij, and with q_low = Q·Pq, k_low = K·Pk,
+    S = score_scale · q_low·k_lowᵀ:
+      dq_low_i = score_scale · sum_j dS_ij k_low_j,
+      dk_low_j = score_scale · sum_i dS_ij q_low_i,
+      dPq = sum over heads and rows of Qᵀ·dq_low, dPk likewise with K,
+      and dQ += dq_low·Pqᵀ, dK += dk_low·Pkᵀ.
+    Returns dQ, dK, dV [B,H,N,D] and dPq, dPk [D, d_proj] (zeros without
+    the scorer path), all float64."""
+    Qa, Ka, Va, dOa = f64(Q), f64(K), f64(V), f64(dO)
+    Pqa, Pka = f64(Pq), f64(Pk)
+    idx = np.asarray(idx).astype(np.int64)
+    B, H, N, D = Qa.shape
+    dQ = np.zeros_like(Qa)
+    dK = np.zeros_like(Ka)
+    dV = np.zeros_like(Va)
+    dPq = np.zeros_like(Pqa)
+    dPk = np.zeros_like(Pka)
+    for b in range(B):
+        for h in range(H):
+            q_low = project(Qa[b, h], Pqa)
+            k_low = project(Ka[b, h], Pka)
+            dq_low = np.zeros_like(q_low)
+            dk_low = np.zeros_like(k_low)
+            for i in range(N):
+                sel = idx[b, h, i]
+                dq, dKr, dVr, dl = attend_row_backward(Qa[b, h, i], Ka[b, h], Va[b, h], sel,
+                                                        softmax_scale, dOa[b, h, i])
+                dQ[b, h, i] += dq
+                for t, j in enumerate(sel):
+                    if j < 0:
+                        continue
+                    dK[b, h, j] += dKr[t]
+                    dV[b, h, j] += dVr[t]
+                    if scorer_grad:
+                        dq_low[i] += score_scale * dl[t] * k_low[j]
+                        dk_low[j] += score_scale * dl[t] * q_low[i]
+            if scorer_grad:
+                dPq += Qa[b, h].T @ dq_low
+                dPk += Ka[b, h].T @ dk_low
+                dQ[b, h] += dq_low @ Pqa.T
+                dK[b, h] += dk_low @ Pka.T
+    return dQ, dK, dV, dPq, dPk
