@@ -33,6 +33,8 @@ import os
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -56,6 +58,10 @@ TRAFFIC = {
                "src": "f4407d799910cd43fb4a75b18a8fca50eec3133ed9f1aa1a0616b23d5c45d73e"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
+
+# rocprofv3 --pmc readings of the filter's MFMA activity on the headline
+# command (see profiles/), with the sha256 of scorer.hip when taken.
+MFMA_COUNTERS: dict = {}
 
 
 def source_sha(kernel: str):
@@ -94,6 +100,28 @@ def algorithmic(w) -> dict:
     }
 
 
+def gather_counter_frac(kern: dict, band: bool):
+    """Counter bytes per launch of the gather's main kernel over its measured
+    average launch time, as a fraction of the HBM peak (headline command's
+    counters only; null when they do not apply)."""
+    tr = TRAFFIC.get("gather")
+    d = kern.get("gather")
+    if band or not tr or not d or tr.get("src") != source_sha("gather") or \
+            "gather_merge" not in kern:
+        return None
+    avg_s = d["ms_total"] / d["launches"] / 1e3
+    return (tr["fetch_bytes"] + tr["write_bytes"]) / avg_s / 1e9 / PEAK_HBM_GBS
+
+
+def filter_mfma_counters():
+    """MFMA activity of the filter from the committed rocprofv3 counter run
+    (null once the filter source has changed since it was taken)."""
+    c = MFMA_COUNTERS.get("filter")
+    if not c or c.get("src") != source_sha("filter"):
+        return None
+    return {k: v for k, v in c.items() if k != "src"}
+
+
 def pick_heads_per_chunk(w) -> int:
     """Largest of (all heads, 16, 8) whose workspace takes at most a quarter of
     the device's memory.  Larger chunks mean fewer, fuller launches: each
@@ -115,14 +143,17 @@ def pick_heads_per_chunk(w) -> int:
 def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
     """The fp64 oracle, as it stands, on a bounded sample of the same
     workload: query rows of head (0, 0), including that head's projections
-    (for the band workload: the band rows and their attention)."""
+    (for the band workload: the band rows and their attention).  BLAS runs on
+    every core this process may use; the rate is extrapolated linearly from
+    the sample to the whole workload."""
     import numpy as np
     import oracle as O
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:
-        threads = 1
+        limiter = None
     Q1, K1, V1 = (x[n][:1, :1] for n in ("Q", "K", "V"))
     sscale, ascale = (w.d_proj ** -0.5 if w.d_proj else 0.0), w.D ** -0.5
     rng = np.random.default_rng(0)
@@ -136,17 +167,25 @@ def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
             O.sparse_attn_fwd(Q1, K1, V1, x["Pq"], x["Pk"], w.k, w.causal, sscale, ascale, rows)
         return time.perf_counter() - t
 
-    pilot = sorted(rng.choice(w.N, 16, replace=False).tolist())
-    tp = run(pilot)
-    n_rows = int(min(4096, w.N, max(32, 16 * target_s / max(tp, 1e-3))))
-    rows = sorted(rng.choice(w.N, n_rows, replace=False).tolist())
-    t = run(rows)
-    return {"value": n_rows / t, "unit": "queries/s", "cores": int(threads), "kind": "oracle",
+    try:
+        pilot = sorted(rng.choice(w.N, 16, replace=False).tolist())
+        tp = run(pilot)
+        n_rows = int(min(4096, w.N, max(32, 16 * target_s / max(tp, 1e-3))))
+        rows = sorted(rng.choice(w.N, n_rows, replace=False).tolist())
+        t = run(rows)
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    mode = "full" if n_rows == w.N and w.B * w.H == 1 else "extrapolated"
+    return {"value": n_rows / t, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "mode": mode, "oracle_seconds": t,
+            "extrapolated_workload_seconds": t * w.queries / n_rows,
             "sample": (f"{n_rows} random query rows of head (0,0) of the {w.name} workload "
                        + ("through the fp64 oracle's band indices and softmax gather"
                           if w.mode == "band" else
                           "through the fp64 oracle forward (scores, top-k, softmax gather), "
-                          "including that head's key projection") + f"; {t:.1f} s")}
+                          "including that head's key projection")
+                       + f"; {t:.1f} s with BLAS on {cores} cores")}
 
 
 def main() -> int:
@@ -174,7 +213,8 @@ def main() -> int:
     import dynamic_top_sparse_amd as sa
     from dynamic_top_sparse_amd import workloads as W
 
-    sa.sparse_attn_set_filter_dtype(torch.float16 if args.filter_dtype == "f16" else torch.bfloat16)
+    fdt = torch.float16 if args.filter_dtype == "f16" else torch.bfloat16
+    prof = sa.Profile()
     try:
         w = W.get(args.workload)
     except KeyError:
@@ -188,32 +228,43 @@ def main() -> int:
         ws = None
         idx = torch.empty((w.B, w.H, w.N, w.k), dtype=torch.int32, device="cuda")
 
-        def step():
-            sa.sparse_attn_band_indices(w.B, w.H, w.N, w.window, w.window, w.k, idx=idx)
-            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out)
+        def step(p=None):
+            sa.sparse_attn_band_indices(w.B, w.H, w.N, w.window, w.window, w.k, idx=idx,
+                                        profile=p)
+            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out, profile=p)
     else:
         hc = args.heads_per_chunk or pick_heads_per_chunk(w)
         ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
                                    heads_per_chunk=hc)
 
-        def step():
+        def step(p=None):
             sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
-                               O=out, workspace=ws)
+                               O=out, workspace=ws, filter_dtype=fdt, profile=p)
+    # 512 MiB written between timed steps (outside their event brackets), so
+    # no step starts with the previous one's data in L2 or the memory-side
+    # cache
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    sa.sparse_attn_profile_enable(True)
-    sa.sparse_attn_profile_read()          # drop anything recorded before
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for e0, e1 in ev:
+        flush.fill_(1)
+        e0.record(stream)
+        step(prof)          # every library launch bracketed by its own events, same stream
+        e1.record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    recs = sa.sparse_attn_profile_read()
-    sa.sparse_attn_profile_enable(False)
+    step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+    recs = prof.read()
+    prof.close()
+    del flush
     stats = sa.sparse_attn_workspace_stats(ws) if ws is not None else None
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
@@ -223,7 +274,7 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    ms_step = (t1 - t0) * 1e3 / args.steps
+    ms_step = float(np.median(step_ms))
     a = algorithmic(w)
     queries = w.queries
     flops = a["F_proj"] + a["F_score"] + a["F_gather"]
@@ -283,6 +334,11 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_step,
+        "ms_per_step_min": step_ms[0],
+        "ms_per_step_mean": float(np.mean(step_ms)),
+        "wall_ms_per_step_incl_flush": (t1 - t0) * 1e3 / args.steps,
+        "timing": ("median of per-step HIP events on the launch stream; a 512 MiB write "
+                   "between steps (outside the events) flushes L2 and the memory-side cache"),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -295,8 +351,17 @@ def main() -> int:
         "eff_tflops": flops / (ms_step / 1e3) / 1e12,
         "scorer_frac_of_bf16_peak": ((a["F_proj"] + a["F_score"]) / t_scorer / 1e12
                                      / PEAK_BF16_TFLOPS) if t_scorer else None,
-        "gather_frac_of_hbm_peak": ((a["gather_bytes_per_head"] * w.B * w.H) / t_gather / 1e9
-                                    / PEAK_HBM_GBS) if t_gather else None,
+        # logical bytes (every kept K/V row counted as if read from HBM), over
+        # the gather stage's time: above 1 when L2 and the memory-side cache
+        # serve repeated rows
+        "gather_logical_bytes_per_s_over_hbm_peak": (
+            (a["gather_bytes_per_head"] * w.B * w.H) / t_gather / 1e9 / PEAK_HBM_GBS)
+        if t_gather else None,
+        # counter-measured bytes between L2 and the fabric (FETCH_SIZE +
+        # WRITE_SIZE, memory-side-cache hits included) per gather launch, over
+        # that launch's time; null once the gather source has changed since
+        # the counters were taken
+        "gather_frac_of_hbm_peak": gather_counter_frac(kern, band),
         "gather_stage_ms": t_gather * 1e3,
         "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
                                                                   key=lambda kv: -kv[1])},
@@ -309,7 +374,9 @@ def main() -> int:
             "fallback_queries": stats["fallback_queries"],
             "overflow_queries": stats["overflow_queries"],
             "retried_queries": stats["retried"],
-            "filter_dtype": str(sa.sparse_attn_get_filter_dtype()).replace("torch.", "")}
+            "margin_violations": stats["margin_violations"],
+            "filter_dtype": args.filter_dtype}
+        result["filter_mfma_counters"] = filter_mfma_counters()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(result))

@@ -35,14 +35,18 @@ EXPORTS = (
     "sparse_attn_workspace_size", "sparse_attn_workspace_size_for_chunk",
     "sparse_attn_scores_topk", "sparse_attn_gather", "sparse_attn_fwd",
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
-    "sparse_attn_workspace_stats", "sparse_attn_profile_enable", "sparse_attn_profile_read",
-    "sparse_attn_set_filter_dtype", "sparse_attn_get_filter_dtype", "sparse_attn_status_string",
+    "sparse_attn_workspace_stats", "sparse_attn_profile_create", "sparse_attn_profile_destroy",
+    "sparse_attn_profile_read", "sparse_attn_status_string",
 )
 
 
 class sa_dims(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("D", ctypes.c_int32)]
+
+
+class sa_options(ctypes.Structure):
+    _fields_ = [("filter_dtype", ctypes.c_int32), ("profile", ctypes.c_void_p)]
 
 
 class sa_kernel_time(ctypes.Structure):
@@ -68,24 +72,25 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         raise RuntimeError(f"{p} is missing: build it with `python -m dynamic_top_sparse_amd.build`")
     lib = ctypes.CDLL(p)
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+    op = ctypes.POINTER(sa_options)
     sig = {
         "sparse_attn_workspace_size": (sz, [sa_dims, i32, i32, i32, i32, i32]),
         "sparse_attn_workspace_size_for_chunk": (sz, [sa_dims, i32, i32, i32, i32, i32, i32]),
         "sparse_attn_scores_topk": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, i32, f32,
-                                                   i32, vp, vp, sz, vp]),
-        "sparse_attn_gather": (ctypes.c_int, [vp, vp, vp, vp, i32, sa_dims, f32, i32, vp, vp]),
+                                                   i32, vp, vp, sz, op, vp]),
+        "sparse_attn_gather": (ctypes.c_int, [vp, vp, vp, vp, i32, sa_dims, f32, i32, vp, op,
+                                              vp]),
         "sparse_attn_fwd": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32, f32,
-                                           i32, vp, vp, vp, sz, vp]),
-        "sparse_attn_band_indices": (ctypes.c_int, [sa_dims, i32, i32, vp, i32, vp]),
+                                           i32, vp, vp, vp, sz, op, vp]),
+        "sparse_attn_band_indices": (ctypes.c_int, [sa_dims, i32, i32, vp, i32, op, vp]),
         "sparse_attn_scores_dump": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, f32, i32,
-                                                   i32, i32, vp, vp, sz, vp]),
+                                                   i32, i32, vp, vp, sz, op, vp]),
         "sparse_attn_check_status": (ctypes.c_int, [vp]),
         "sparse_attn_workspace_stats": (ctypes.c_int, [vp, sz, ctypes.POINTER(ctypes.c_int64),
                                                        i32, vp]),
-        "sparse_attn_profile_enable": (ctypes.c_int, [i32]),
-        "sparse_attn_profile_read": (ctypes.c_int, [ctypes.POINTER(sa_kernel_time), i32]),
-        "sparse_attn_set_filter_dtype": (ctypes.c_int, [i32]),
-        "sparse_attn_get_filter_dtype": (ctypes.c_int, []),
+        "sparse_attn_profile_create": (vp, []),
+        "sparse_attn_profile_destroy": (None, [vp]),
+        "sparse_attn_profile_read": (ctypes.c_int, [vp, ctypes.POINTER(sa_kernel_time), i32]),
         "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     }
     for name, (res, args) in sig.items():
@@ -104,6 +109,36 @@ def status_string(status: int) -> str:
         return STATUS_NAMES.get(status, "unknown status")
 
 
+class Profile:
+    """A caller-owned per-kernel timing record (sa_profile): pass it as
+    ``profile=`` to a call; read() returns [(kernel name, ms)] of the launches
+    recorded since the last read."""
+
+    def __init__(self):
+        self._lib = load_library()
+        self.handle = self._lib.sparse_attn_profile_create()
+        if not self.handle:
+            raise RuntimeError("sparse_attn_profile_create failed")
+
+    def read(self, max_records: int = 65536) -> list:
+        buf = (sa_kernel_time * max_records)()
+        n = self._lib.sparse_attn_profile_read(self.handle, buf, max_records)
+        if n < 0:
+            raise SparseAttnError(n, "sparse_attn_profile_read")
+        return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]
+
+    def close(self) -> None:
+        if self.handle:
+            self._lib.sparse_attn_profile_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
 # ------------------------------------------------------------- helpers ---
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -114,9 +149,73 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
 
 
-def _dev(t: torch.Tensor, name: str) -> int:
+def _filter_code(dtype) -> int:
+    if dtype is None or dtype == torch.float16:
+        return SA_F16
+    if dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError(f"filter dtype must be torch.float16 or torch.bfloat16, not {dtype}")
+
+
+def _options(filter_dtype=None, profile: Optional[Profile] = None):
+    return ctypes.byref(sa_options(_filter_code(filter_dtype),
+                                   profile.handle if profile is not None else None))
+
+
+def _tensor(t, name: str) -> torch.Tensor:
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
+    return t
+
+
+def _like(t, ref: torch.Tensor, name: str, ref_name: str) -> None:
+    """t must have ref's shape, dtype and device."""
+    _tensor(t, name)
+    if tuple(t.shape) != tuple(ref.shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, {ref_name} {tuple(ref.shape)}")
+    if t.dtype != ref.dtype:
+        raise ValueError(f"{name} is {t.dtype} but {ref_name} is {ref.dtype}: one dtype for all")
+    if t.device != ref.device:
+        raise ValueError(f"{name} is on {t.device}, {ref_name} on {ref.device}")
+
+
+def _check_qkv(Q, K, V=None, O=None) -> None:
+    _tensor(Q, "Q")
+    if Q.dim() != 4:
+        raise ValueError("Q, K, V must be [B, H, N, D]")
+    _dtype_code(Q)
+    _like(K, Q, "K", "Q")
+    if V is not None:
+        _like(V, Q, "V", "Q")
+    if O is not None:
+        _like(O, Q, "O", "Q")
+
+
+def _check_proj(Pq, Pk, Q) -> int:
+    _tensor(Pq, "Pq")
+    _tensor(Pk, "Pk")
+    D = Q.shape[3]
+    if Pq.dim() != 2 or Pq.shape[0] != D:
+        raise ValueError(f"Pq must be [D, d_proj] = [{D}, d_proj], got {tuple(Pq.shape)}")
+    _like(Pk, Pq, "Pk", "Pq")
+    if Pq.dtype != Q.dtype or Pq.device != Q.device:
+        raise ValueError("Pq and Pk must have Q's dtype and device")
+    return int(Pq.shape[1])
+
+
+def _check_idx(idx, Q, k: int, name: str = "idx") -> None:
+    _tensor(idx, name)
+    B, H, N, _ = Q.shape
+    if idx.dtype != torch.int32:
+        raise ValueError(f"{name} must be int32, got {idx.dtype}")
+    if tuple(idx.shape) != (B, H, N, k):
+        raise ValueError(f"{name} must be [B, H, N, k] = {(B, H, N, k)}, got {tuple(idx.shape)}")
+    if idx.device != Q.device:
+        raise ValueError(f"{name} is on {idx.device}, Q on {Q.device}")
+
+
+def _dev(t: torch.Tensor, name: str) -> int:
+    _tensor(t, name)
     if not t.is_cuda:
         raise ValueError(f"{name} must be on a GPU (the library has no CPU path)")
     if not t.is_contiguous():
@@ -174,38 +273,57 @@ def allocate_workspace(Q: torch.Tensor, d_proj: int, k: int, causal: bool,
     return torch.empty(n, dtype=torch.uint8, device=Q.device)
 
 
+def _check_workspace(ws, Q) -> None:
+    _tensor(ws, "workspace")
+    if ws.dtype != torch.uint8 or ws.dim() != 1:
+        raise ValueError("workspace must be a 1-D uint8 tensor")
+    if ws.device != Q.device:
+        raise ValueError(f"workspace is on {ws.device}, Q on {Q.device}")
+
+
 def sparse_attn_scores_topk(Q, K, Pq, Pk, k: int, causal: bool = False,
                             score_scale: Optional[float] = None,
                             idx: Optional[torch.Tensor] = None,
-                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+                            workspace: Optional[torch.Tensor] = None,
+                            filter_dtype: Optional[torch.dtype] = None,
+                            profile: Optional[Profile] = None) -> torch.Tensor:
     """idx [B,H,N,k] int32: each query's k best keys by the scorer, ascending
     key order, -1 padded (see include/sparse_attn.h)."""
+    _check_qkv(Q, K)
+    d_proj = _check_proj(Pq, Pk, Q)
     B, H, N, D = Q.shape
-    d_proj = Pq.shape[1]
     scale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
     if idx is None:
         idx = torch.empty((B, H, N, k), dtype=torch.int32, device=Q.device)
+    _check_idx(idx, Q, k)
     if workspace is None:
         workspace = allocate_workspace(Q, d_proj, k, causal)
+    _check_workspace(workspace, Q)
     st = load_library().sparse_attn_scores_topk(
         _dev(Q, "Q"), _dev(K, "K"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q), d_proj, k,
         int(causal), scale, _dtype_code(Q), _dev(idx, "idx"), _dev(workspace, "workspace"),
-        workspace.numel(), _stream(Q))
+        workspace.numel(), _options(filter_dtype, profile), _stream(Q))
     _check(st, "sparse_attn_scores_topk")
     return idx
 
 
 def sparse_attn_gather(Q, K, V, idx, softmax_scale: Optional[float] = None,
-                       O: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       O: Optional[torch.Tensor] = None,
+                       profile: Optional[Profile] = None) -> torch.Tensor:
     """O [B,H,N,D]: softmax attention of each query over its idx row."""
+    _check_qkv(Q, K, V, O)
     B, H, N, D = Q.shape
+    _tensor(idx, "idx")
+    if idx.dim() != 4:
+        raise ValueError("idx must be [B, H, N, k]")
     k = idx.shape[-1]
+    _check_idx(idx, Q, k)
     scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
     if O is None:
         O = torch.empty_like(Q)
     st = load_library().sparse_attn_gather(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(idx, "idx"), k, _dims(Q), scale,
-        _dtype_code(Q), _dev(O, "O"), _stream(Q))
+        _dtype_code(Q), _dev(O, "O"), _options(None, profile), _stream(Q))
     _check(st, "sparse_attn_gather")
     return O
 
@@ -213,37 +331,48 @@ def sparse_attn_gather(Q, K, V, idx, softmax_scale: Optional[float] = None,
 def sparse_attn_fwd(Q, K, V, Pq, Pk, k: int, causal: bool = False,
                     score_scale: Optional[float] = None, softmax_scale: Optional[float] = None,
                     O: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, return_idx: bool = False):
+                    workspace: Optional[torch.Tensor] = None, return_idx: bool = False,
+                    filter_dtype: Optional[torch.dtype] = None,
+                    profile: Optional[Profile] = None):
     """The fused forward; returns O (and idx when return_idx)."""
+    _check_qkv(Q, K, V, O)
+    d_proj = _check_proj(Pq, Pk, Q)
     B, H, N, D = Q.shape
-    d_proj = Pq.shape[1]
     sscale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
     ascale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
     if O is None:
         O = torch.empty_like(Q)
     if return_idx and idx is None:
         idx = torch.empty((B, H, N, k), dtype=torch.int32, device=Q.device)
+    if idx is not None:
+        _check_idx(idx, Q, k)
     if workspace is None:
         workspace = allocate_workspace(Q, d_proj, k, causal, with_idx=idx is None)
+    _check_workspace(workspace, Q)
     st = load_library().sparse_attn_fwd(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q),
         d_proj, k, int(causal), sscale, ascale, _dtype_code(Q), _dev(O, "O"),
         None if idx is None else _dev(idx, "idx"), _dev(workspace, "workspace"),
-        workspace.numel(), _stream(Q))
+        workspace.numel(), _options(filter_dtype, profile), _stream(Q))
     _check(st, "sparse_attn_fwd")
     return (O, idx) if return_idx else O
 
 
 def sparse_attn_band_indices(B: int, H: int, N: int, w_left: int, w_right: int,
                              k: Optional[int] = None, device="cuda",
-                             idx: Optional[torch.Tensor] = None) -> torch.Tensor:
+                             idx: Optional[torch.Tensor] = None,
+                             profile: Optional[Profile] = None) -> torch.Tensor:
     """idx [B,H,N,k]: keys max(0,i-w_left)..min(N-1,i+w_right), then -1."""
     if k is None:
         k = w_left + w_right + 1
     if idx is None:
         idx = torch.empty((B, H, N, k), dtype=torch.int32, device=device)
+    _tensor(idx, "idx")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, H, N, k):
+        raise ValueError(f"idx must be int32 [B, H, N, k] = {(B, H, N, k)}")
     st = load_library().sparse_attn_band_indices(sa_dims(B, H, N, 0), w_left, w_right,
-                                                 _dev(idx, "idx"), k, _stream(idx))
+                                                 _dev(idx, "idx"), k, _options(None, profile),
+                                                 _stream(idx))
     _check(st, "sparse_attn_band_indices")
     return idx
 
@@ -253,17 +382,22 @@ def sparse_attn_scores_dump(Q, K, Pq, Pk, row_begin: int, row_count: int,
                             S: Optional[torch.Tensor] = None,
                             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """S [B,H,row_count,N] fp32: the exact scores the selection uses."""
+    _check_qkv(Q, K)
+    d_proj = _check_proj(Pq, Pk, Q)
     B, H, N, D = Q.shape
-    d_proj = Pq.shape[1]
     scale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
     if S is None:
         S = torch.empty((B, H, row_count, N), dtype=torch.float32, device=Q.device)
+    _tensor(S, "S")
+    if S.dtype != torch.float32 or tuple(S.shape) != (B, H, row_count, N):
+        raise ValueError(f"S must be float32 [B, H, row_count, N] = {(B, H, row_count, N)}")
     if workspace is None:
         workspace = allocate_workspace(Q, d_proj, 1, causal)
+    _check_workspace(workspace, Q)
     st = load_library().sparse_attn_scores_dump(
         _dev(Q, "Q"), _dev(K, "K"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q), d_proj,
         int(causal), scale, _dtype_code(Q), row_begin, row_count, _dev(S, "S"),
-        _dev(workspace, "workspace"), workspace.numel(), _stream(Q))
+        _dev(workspace, "workspace"), workspace.numel(), None, _stream(Q))
     _check(st, "sparse_attn_scores_dump")
     return S
 
@@ -274,47 +408,24 @@ def sparse_attn_check_status(stream: Optional[int] = None) -> int:
     return int(load_library().sparse_attn_check_status(s))
 
 
+STAT_KEYS = ("fallback_queries", "overflow_queries", "candidates", "rescored", "queries",
+             "retried", "margin_violations")
+
+
 def sparse_attn_workspace_stats(workspace: torch.Tensor) -> dict:
-    out = (ctypes.c_int64 * 6)()
+    out = (ctypes.c_int64 * len(STAT_KEYS))()
     n = load_library().sparse_attn_workspace_stats(
-        _dev(workspace, "workspace"), workspace.numel(), out, 6, _stream(workspace))
+        _dev(workspace, "workspace"), workspace.numel(), out, len(STAT_KEYS),
+        _stream(workspace))
     if n < 0:
         raise SparseAttnError(n, "sparse_attn_workspace_stats")
-    keys = ("fallback_queries", "overflow_queries", "candidates", "rescored", "queries",
-            "retried")
-    return {kk: int(out[i]) for i, kk in enumerate(keys[:n])}
-
-
-def sparse_attn_set_filter_dtype(dtype: torch.dtype) -> None:
-    """16-bit operand type of the MFMA filter: torch.float16 (default) or
-    torch.bfloat16.  Indices do not depend on it (see include/sparse_attn.h)."""
-    code = {torch.float16: SA_F16, torch.bfloat16: SA_BF16}[dtype]
-    _check(load_library().sparse_attn_set_filter_dtype(code), "sparse_attn_set_filter_dtype")
-
-
-def sparse_attn_get_filter_dtype() -> torch.dtype:
-    return torch.float16 if load_library().sparse_attn_get_filter_dtype() == SA_F16 else torch.bfloat16
-
-
-def sparse_attn_profile_enable(on: bool = True) -> None:
-    """Bracket every library kernel launch with HIP events (for benchmarks)."""
-    _check(load_library().sparse_attn_profile_enable(int(on)), "sparse_attn_profile_enable")
-
-
-def sparse_attn_profile_read(max_records: int = 65536) -> list:
-    """[(kernel name, ms)] of the launches timed since the last read."""
-    buf = (sa_kernel_time * max_records)()
-    n = load_library().sparse_attn_profile_read(buf, max_records)
-    if n < 0:
-        raise SparseAttnError(n, "sparse_attn_profile_read")
-    return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]
+    return {kk: int(out[i]) for i, kk in enumerate(STAT_KEYS[:n])}
 
 
 __all__ = [
-    "sa_dims", "SparseAttnError", "load_library", "status_string", "LIB_PATH", "EXPORTS",
-    "sparse_attn_workspace_size", "allocate_workspace", "sparse_attn_scores_topk",
-    "sparse_attn_gather", "sparse_attn_fwd", "sparse_attn_band_indices",
-    "sparse_attn_scores_dump", "sparse_attn_check_status", "sparse_attn_workspace_stats",
-    "default_score_scale", "default_softmax_scale", "sparse_attn_profile_enable",
-    "sparse_attn_profile_read", "sparse_attn_set_filter_dtype", "sparse_attn_get_filter_dtype",
+    "sa_dims", "sa_options", "SparseAttnError", "load_library", "status_string", "LIB_PATH",
+    "EXPORTS", "Profile", "sparse_attn_workspace_size", "allocate_workspace",
+    "sparse_attn_scores_topk", "sparse_attn_gather", "sparse_attn_fwd",
+    "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
+    "sparse_attn_workspace_stats", "default_score_scale", "default_softmax_scale",
 ]

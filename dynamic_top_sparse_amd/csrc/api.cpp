@@ -18,9 +18,15 @@ namespace {
 
 constexpr size_t kAlign = 256;
 
-// 16-bit operand type of the MFMA filter (sparse_attn_set_filter_dtype).
-std::atomic<int> g_filter_dtype{SA_F16};
 constexpr int kDefaultChunkHeads = 8;
+
+// The filter operand type an options struct asks for: 0 = fp16, 1 = bf16,
+// -1 = not a filter type.  NULL options mean the defaults.
+int filter_of(const sa_options* o) {
+  if (o == nullptr || o->filter_dtype == SA_F16) return 0;
+  return o->filter_dtype == SA_BF16 ? 1 : -1;
+}
+sa_profile* profile_of(const sa_options* o) { return o == nullptr ? nullptr : o->profile; }
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 int round_up(int x, int m) { return (x + m - 1) / m * m; }
@@ -52,18 +58,19 @@ int check_scorer_args(const void* Q, const void* K, const void* Pq, const void* 
   return SA_OK;
 }
 
-// Runs `call` between the optional timing events of `name`.
-#define SA_TIMED(name, call)          \
-  do {                                \
-    prof_begin(name, s);              \
-    hipError_t e_ = (call);           \
-    prof_end(s);                      \
-    if (e_ != hipSuccess) return e_;  \
+// Runs `call` between the optional timing events of `name` (into `prof`).
+#define SA_TIMED(name, call)                   \
+  do {                                         \
+    const int t_ = prof_begin(prof, name, s);  \
+    hipError_t e_ = (call);                    \
+    prof_end(prof, t_, s);                     \
+    if (e_ != hipSuccess) return e_;           \
   } while (0)
 
 hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, float scale,
-                          int32_t* idx_chunk, int first, int* seg, hipStream_t s) {
+                          int32_t* idx_chunk, int first, int* seg, sa_profile* prof,
+                          hipStream_t s) {
   SA_TIMED("init", launch_init_chunk(p, b, first, s));
   SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
   SA_TIMED("pack", launch_pack_keys(p, b, nh, s));
@@ -83,14 +90,14 @@ hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const voi
 
 hipError_t timed_gather(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
                         int nheads, int N, int D, float scale, int dtype, void* O,
-                        hipStream_t s) {
+                        sa_profile* prof, hipStream_t s) {
   SA_TIMED("gather", launch_gather(Q, K, V, idx, k, nheads, N, D, scale, dtype, O, s));
   return hipSuccess;
 }
 
 hipError_t timed_dump(const Plan& p, const Bufs& b, const void* Q, const void* K, const void* Pq,
                       const void* Pk, int h0, int nh, float scale, int row_begin, int row_count,
-                      float* Sc, int first, hipStream_t s) {
+                      float* Sc, int first, sa_profile* prof, hipStream_t s) {
   SA_TIMED("init", launch_init_chunk(p, b, first, s));
   SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
   SA_TIMED("dump", launch_dump(p, b, nh, scale, row_begin, row_count, Sc, s));
@@ -98,7 +105,7 @@ hipError_t timed_dump(const Plan& p, const Bufs& b, const void* Q, const void* K
 }
 
 hipError_t timed_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
-                      hipStream_t s) {
+                      sa_profile* prof, hipStream_t s) {
   SA_TIMED("band", launch_band(nheads, N, w_left, w_right, idx, k, s));
   return hipSuccess;
 }
@@ -108,9 +115,9 @@ int chunk_heads_for(const sa_dims& d, int dp, int k, int causal, int dtype, int 
                     size_t ws_bytes) {
   const int BH = d.B * d.H;
   Plan p1, p2;
-  if (!make_plan(p1, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, 1)) return 0;
+  if (!make_plan(p1, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, 1, 0)) return 0;
   if (BH == 1) return p1.total <= ws_bytes ? 1 : 0;
-  if (!make_plan(p2, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, 2)) return 0;
+  if (!make_plan(p2, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, 2, 0)) return 0;
   if (p1.total > ws_bytes) return 0;
   const size_t per_head = p2.total - p1.total;
   const size_t fixed = p1.total - per_head;
@@ -119,7 +126,7 @@ int chunk_heads_for(const sa_dims& d, int dp, int k, int causal, int dtype, int 
   // keep head-chunk indices within int range of the queue entries
   while (h > 1) {
     Plan ph;
-    if (make_plan(ph, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, static_cast<int>(h)) &&
+    if (make_plan(ph, d.B, d.H, d.N, d.D, dp, k, causal, dtype, with_idx, static_cast<int>(h), 0) &&
         ph.total <= ws_bytes)
       break;
     --h;
@@ -130,10 +137,10 @@ int chunk_heads_for(const sa_dims& d, int dp, int k, int causal, int dtype, int 
 }  // namespace
 
 bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, int dtype,
-               int with_idx, int heads_per_chunk) {
+               int with_idx, int heads_per_chunk, int filt) {
   p.B = B; p.H = H; p.N = N; p.D = D; p.dp = dp; p.k = k; p.causal = causal ? 1 : 0;
   p.dtype = dtype;
-  p.filt = g_filter_dtype.load() == SA_BF16 ? 1 : 0;
+  p.filt = filt ? 1 : 0;
   p.BH = B * H;
   p.hc = heads_per_chunk < 1 ? 1 : (heads_per_chunk > p.BH ? p.BH : heads_per_chunk);
   p.Npad = round_up(N, kRowPad);
@@ -195,6 +202,18 @@ bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, i
   return true;
 }
 
+hipError_t set_lds_limit_once(const void* kernel, int bytes, std::atomic<int>* flags) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < kMaxDevices;
+  if (cached && flags[dev].load(std::memory_order_acquire) == bytes) return hipSuccess;
+  // racing threads both set the same value: harmless
+  e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && cached) flags[dev].store(bytes, std::memory_order_release);
+  return e;
+}
+
 Bufs bufs_of(const Plan& p, void* ws) {
   unsigned char* base = static_cast<unsigned char*>(ws);
   Bufs b;
@@ -234,7 +253,7 @@ size_t sparse_attn_workspace_size_for_chunk(sa_dims d, int32_t d_proj, int32_t k
   if (check_dims(d, k) != SA_OK || !supported_D(d.D) || !supported_dp(d_proj)) return 0;
   if (dtype != SA_F32 && dtype != SA_BF16) return 0;
   Plan p;
-  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, with_idx, heads_per_chunk))
+  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, with_idx, heads_per_chunk, 0))
     return 0;
   return p.total;
 }
@@ -250,22 +269,26 @@ size_t sparse_attn_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t 
 int sparse_attn_scores_topk(const void* Q, const void* K, const void* Pq, const void* Pk,
                             sa_dims d, int32_t d_proj, int32_t k, int32_t causal,
                             float score_scale, int32_t dtype, int32_t* idx, void* ws,
-                            size_t ws_bytes, void* stream) {
+                            size_t ws_bytes, const sa_options* opts, void* stream) {
   int st = check_scorer_args(Q, K, Pq, Pk, d, d_proj, k, dtype, score_scale);
   if (st != SA_OK) return st;
+  const int filt = filter_of(opts);
+  if (filt < 0) return SA_ERR_UNSUPPORTED;
+  sa_profile* prof = profile_of(opts);
   if (!idx || !ws) return SA_ERR_NULL;
   if (!aligned16(idx) || !aligned16(ws)) return SA_ERR_ALIGN;
   const int hc = chunk_heads_for(d, d_proj, k, causal, dtype, 0, ws_bytes);
   if (hc < 1) return SA_ERR_WORKSPACE;
   Plan p;
-  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, 0, hc)) return SA_ERR_SHAPE;
+  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, 0, hc, filt))
+    return SA_ERR_SHAPE;
   const Bufs b = bufs_of(p, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int h0 = 0; h0 < p.BH; h0 += p.hc) {
     const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
     int32_t* idx_chunk = idx + static_cast<size_t>(h0) * d.N * k;
-    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, nullptr, s) !=
-        hipSuccess)
+    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, nullptr,
+                       prof, s) != hipSuccess)
       return SA_ERR_HIP;
   }
   return SA_OK;
@@ -273,7 +296,7 @@ int sparse_attn_scores_topk(const void* Q, const void* K, const void* Pq, const 
 
 int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                        int32_t k, sa_dims d, float softmax_scale, int32_t dtype, void* O,
-                       void* stream) {
+                       const sa_options* opts, void* stream) {
   if (!Q || !K || !V || !idx || !O) return SA_ERR_NULL;
   int st = check_dims(d, k);
   if (st != SA_OK) return st;
@@ -283,7 +306,7 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
   if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O))
     return SA_ERR_ALIGN;
   return timed_gather(Q, K, V, idx, k, d.B * d.H, d.N, d.D, softmax_scale, dtype, O,
-                      static_cast<hipStream_t>(stream)) == hipSuccess
+                      profile_of(opts), static_cast<hipStream_t>(stream)) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
 }
@@ -291,9 +314,12 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
 int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
                     sa_dims d, int32_t d_proj, int32_t k, int32_t causal, float score_scale,
                     float softmax_scale, int32_t dtype, void* O, int32_t* idx_or_null, void* ws,
-                    size_t ws_bytes, void* stream) {
+                    size_t ws_bytes, const sa_options* opts, void* stream) {
   int st = check_scorer_args(Q, K, Pq, Pk, d, d_proj, k, dtype, score_scale);
   if (st != SA_OK) return st;
+  const int filt = filter_of(opts);
+  if (filt < 0) return SA_ERR_UNSUPPORTED;
+  sa_profile* prof = profile_of(opts);
   if (!V || !O || !ws) return SA_ERR_NULL;
   if (!std::isfinite(softmax_scale)) return SA_ERR_SHAPE;
   if (!aligned16(V) || !aligned16(O) || !aligned16(ws)) return SA_ERR_ALIGN;
@@ -302,7 +328,7 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
   const int hc = chunk_heads_for(d, d_proj, k, causal, dtype, with_idx, ws_bytes);
   if (hc < 1) return SA_ERR_WORKSPACE;
   Plan p;
-  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, with_idx, hc))
+  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k, causal, dtype, with_idx, hc, filt))
     return SA_ERR_SHAPE;
   const Bufs b = bufs_of(p, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -312,8 +338,7 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
     int32_t* idx_chunk =
         idx_or_null ? idx_or_null + static_cast<size_t>(h0) * d.N * k : b.idx;
     if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0,
-                       p.gsplit ? b.seg : nullptr, s) !=
-        hipSuccess)
+                       p.gsplit ? b.seg : nullptr, prof, s) != hipSuccess)
       return SA_ERR_HIP;
     const size_t off = static_cast<size_t>(h0) * d.N * d.D * esz;
     const unsigned char* Qc = static_cast<const unsigned char*>(Q) + off;
@@ -327,11 +352,11 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
                                 idx_chunk + static_cast<size_t>(hh) * d.N * k, k, d.N, d.D,
                                 softmax_scale, dtype,
                                 b.seg + static_cast<size_t>(hh) * p.Npad * (kGatherRanges + 1),
-                                b.part, Oc + hh * head, s) != hipSuccess)
+                                b.part, Oc + hh * head, prof, s) != hipSuccess)
           return SA_ERR_HIP;
       }
     } else if (timed_gather(Qc, Kc, Vc, idx_chunk, k, nh, d.N, d.D, softmax_scale, dtype, Oc,
-                            s) != hipSuccess) {
+                            prof, s) != hipSuccess) {
       return SA_ERR_HIP;
     }
   }
@@ -339,13 +364,13 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
 }
 
 int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t* idx,
-                             int32_t k, void* stream) {
+                             int32_t k, const sa_options* opts, void* stream) {
   if (!idx) return SA_ERR_NULL;
   int st = check_dims(d, k);
   if (st != SA_OK) return st;
   if (w_left < 0 || w_right < 0) return SA_ERR_SHAPE;
   if (!aligned16(idx)) return SA_ERR_ALIGN;
-  return timed_band(d.B * d.H, d.N, w_left, w_right, idx, k,
+  return timed_band(d.B * d.H, d.N, w_left, w_right, idx, k, profile_of(opts),
                     static_cast<hipStream_t>(stream)) == hipSuccess
              ? SA_OK
              : SA_ERR_HIP;
@@ -354,7 +379,7 @@ int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t
 int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const void* Pk,
                             sa_dims d, int32_t d_proj, int32_t causal, float score_scale,
                             int32_t dtype, int32_t row_begin, int32_t row_count, float* S,
-                            void* ws, size_t ws_bytes, void* stream) {
+                            void* ws, size_t ws_bytes, const sa_options* opts, void* stream) {
   int st = check_scorer_args(Q, K, Pq, Pk, d, d_proj, 1, dtype, score_scale);
   if (st != SA_OK) return st;
   if (!S || !ws) return SA_ERR_NULL;
@@ -364,26 +389,18 @@ int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const 
   const int hc = chunk_heads_for(d, d_proj, 1, causal, dtype, 0, ws_bytes);
   if (hc < 1) return SA_ERR_WORKSPACE;
   Plan p;
-  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, 1, causal, dtype, 0, hc)) return SA_ERR_SHAPE;
+  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, 1, causal, dtype, 0, hc, 0)) return SA_ERR_SHAPE;
   const Bufs b = bufs_of(p, ws);
   hipStream_t s = static_cast<hipStream_t>(stream);
   for (int h0 = 0; h0 < p.BH; h0 += p.hc) {
     const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
     float* Sc = S + static_cast<size_t>(h0) * row_count * d.N;
     if (timed_dump(p, b, Q, K, Pq, Pk, h0, nh, score_scale, row_begin, row_count, Sc, h0 == 0,
-                   s) != hipSuccess)
+                   profile_of(opts), s) != hipSuccess)
       return SA_ERR_HIP;
   }
   return SA_OK;
 }
-
-int sparse_attn_set_filter_dtype(int32_t dtype) {
-  if (dtype != SA_F16 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
-  g_filter_dtype.store(dtype);
-  return SA_OK;
-}
-
-int sparse_attn_get_filter_dtype(void) { return g_filter_dtype.load(); }
 
 int sparse_attn_check_status(void* stream) {
   int v = 0;
@@ -402,11 +419,12 @@ int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, i
   if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
     return SA_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_HIP;
-  const int64_t vals[6] = {static_cast<int64_t>(h.fallback_queries),
+  const int64_t vals[7] = {static_cast<int64_t>(h.fallback_queries),
                            static_cast<int64_t>(h.overflow_queries),
                            static_cast<int64_t>(h.candidates), static_cast<int64_t>(h.rescored),
-                           static_cast<int64_t>(h.queries), static_cast<int64_t>(h.retried)};
-  const int m = n < 6 ? n : 6;
+                           static_cast<int64_t>(h.queries), static_cast<int64_t>(h.retried),
+                           static_cast<int64_t>(h.margin_violations)};
+  const int m = n < 7 ? n : 7;
   for (int i = 0; i < m; ++i) out[i] = vals[i];
   return m;
 }

@@ -257,11 +257,11 @@ __device__ __forceinline__ unsigned long long rank_key(float s, int j) {
 }
 
 // Per-wave LDS of the re-rank: histogram (1 KB), rank buffer (512 B), the
-// uncertain keys and their exact scores (ucap x 8 B), and the candidates
-// (cap x 8 B: order key of the filter score, key index), whose key array
-// becomes the output row in place.
+// uncertain keys with their exact and filter scores (ucap x 12 B), and the
+// candidates (cap x 8 B: order key of the filter score, key index), whose key
+// array becomes the output row in place.
 __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
-  return (1024 + 512 + static_cast<size_t>(ucap) * 8 + static_cast<size_t>(cap) * 8 + 15) /
+  return (1024 + 512 + static_cast<size_t>(ucap) * 12 + static_cast<size_t>(cap) * 8 + 15) /
          16 * 16;
 }
 
@@ -288,14 +288,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   unsigned long long* cbuf = reinterpret_cast<unsigned long long*>(base + 1024);
   int* uj = reinterpret_cast<int*>(base + 1536);
   float* us = reinterpret_cast<float*>(base + 1536 + ucap * 4);
-  uint32_t* ck = reinterpret_cast<uint32_t*>(base + 1536 + ucap * 8);
-  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 8 + cap * 4);
+  float* ut = reinterpret_cast<float*>(base + 1536 + ucap * 8);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(base + 1536 + ucap * 12);
+  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 12 + cap * 4);
 
   const int h = blockIdx.y;
   const size_t hq = static_cast<size_t>(h) * Npad;
   // Statistics are kept per wave and added to the header once at the end:
   // one device-scope atomic per query on a shared word would serialise.
   unsigned long long st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
+  unsigned st_viol = 0;
   // first pass: every query; retry pass: the queries listed for this head
   const int nq = qlist != nullptr ? qlist_count[h] : N;
   // Software pipeline over the wave's queries: while query i is ranked, the
@@ -490,19 +492,24 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // One pass classifies and compacts: certainly-kept and uncertain keys
     // stay, in list order, in place in cj (a chunk is read before it is
     // written, and writes never pass the chunk); uncertain ones carry bit 31
-    // and are also listed in uj for the exact re-score.
+    // and are also listed in uj (with their filter score in ut) for the
+    // exact re-score.
     int run = 0, n0c = 0, nU = 0;
     #pragma unroll 1
     for (int i0 = 0; i0 < c; i0 += kWave) {
       const int i = i0 + l;
       const bool ok = i < c;
-      const int cc = ok ? cls_of(ck[i]) : 0;
+      const uint32_t ckey = ok ? ck[i] : 0u;
+      const int cc = ok ? cls_of(ckey) : 0;
       const int key = ok ? cj[i] : 0;
       const unsigned long long mu = __ballot(cc == 2);
       const unsigned long long mk = __ballot(cc != 0);
       if (cc == 2) {
         const int pos = nU + lane_rank(mu);
-        if (pos < ucap) uj[pos] = key;
+        if (pos < ucap) {
+          uj[pos] = key;
+          ut[pos] = key_to_float(ckey);
+        }
       }
       wave_sync();
       if (cc != 0) cj[run + lane_rank(mk)] = cc == 2 ? (key | INT_MIN) : key;
@@ -536,7 +543,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         for (int t = 0; t < UNR; ++t) {
           const float p = group_sum<G>(group_partial<DP>(qv, kv[t]));
           const int u = u0 + t * KPI + grp;
-          if (g == 0 && u < nU) us[u] = p * scale;
+          bool outside = false;
+          if (g == 0 && u < nU) {
+            const float sx = p * scale;
+            us[u] = sx;
+            // the exact score must lie in the interval the margin gives the
+            // filter score; a key outside it means the bound is wrong
+            const float sf = ut[u];
+            outside = sx < lower(sf) || sx > upper(sf);
+          }
+          st_viol += static_cast<unsigned>(__builtin_popcountll(__ballot(outside)));
         }
       }
     }
@@ -594,6 +610,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (st_rescored) atomicAdd(&hdr->rescored, st_rescored);
     if (st_overflow) atomicAdd(&hdr->overflow_queries, st_overflow);
     if (st_retried) atomicAdd(&hdr->retried, st_retried);
+    if (st_viol) atomicAdd(&hdr->margin_violations, st_viol);
   }
 }
 
@@ -707,16 +724,16 @@ __global__ __launch_bounds__(kThreads) void fallback_kernel(
 
 // Compute units of the current device (cached per device).
 int resident_cus() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[kMaxDevices];
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
-    int n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  int n = cached[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
       n = 256;
-    cached[dev] = n;
+    cached[dev].store(n, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return n;
 }
 
 template <int DP>
@@ -739,9 +756,11 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   gx = gx < per_head ? gx : per_head;
   const dim3 grid(gx, nh);
   const size_t lds = static_cast<size_t>(wpb) * per_wave;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&finalize_kernel<DP>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(lds));
+  // one limit for every launch (at most four waves of at most 64 KB in all),
+  // so concurrent calls with other sizes never lower it under each other
+  static std::atomic<int> lds_set[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&finalize_kernel<DP>),
+                                    64 * 1024, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt, b.rcnt,
                      b.tau, b.thr, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,

@@ -575,30 +575,26 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
 template <typename T, int D>
 hipError_t gather_split_t(const void* Q, const void* K, const void* V, const int32_t* idx,
                           int k, int N, float scale, const int* seg, float* part,
-                          void* O, hipStream_t s, const char* const names[2]) {
+                          void* O, sa_profile* prof, hipStream_t s) {
   const int QB = (N + kWaves - 1) / kWaves;
   const size_t lds_part = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    const hipError_t e =
-        hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_part_kernel<T, D>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize,
-                            static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
-  prof_begin(names[0], s);
+  static std::atomic<int> lds_set[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gather_part_kernel<T, D>),
+                                    static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4,
+                                    lds_set);
+  if (e != hipSuccess) return e;
+  int t = prof_begin(prof, "gather", s);
   hipLaunchKernelGGL((gather_part_kernel<T, D>), dim3(QB * kGatherRanges), dim3(kThreads), lds_part, s,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
                      idx, seg, k, N, QB, scale, part);
-  hipError_t e = hipGetLastError();
-  prof_end(s);
+  e = hipGetLastError();
+  prof_end(prof, t, s);
   if (e != hipSuccess) return e;
-  prof_begin(names[1], s);
+  t = prof_begin(prof, "gather_merge", s);
   hipLaunchKernelGGL((gather_merge_kernel<T, D>), dim3(QB), dim3(kThreads), 0, s, part, N,
                      static_cast<T*>(O));
   e = hipGetLastError();
-  prof_end(s);
+  prof_end(prof, t, s);
   return e;
 }
 
@@ -619,14 +615,11 @@ template <typename T, int D>
 hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
                     int nheads, int N, float scale, void* O, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&gather_kernel<T, D>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gather_kernel<T, D>),
+                                          static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4,
+                                          lds_set);
+  if (e != hipSuccess) return e;
   const dim3 grid((N + kWaves - 1) / kWaves, nheads);
   hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(kThreads), lds, s,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
@@ -651,14 +644,13 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
 
 hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
                                int k, int N, int D, float softmax_scale, int dtype, const int* seg,
-                               float* part, void* O, hipStream_t s) {
-  static const char* const names[2] = {"gather", "gather_merge"};
+                               float* part, void* O, sa_profile* prof, hipStream_t s) {
   if (dtype == 0) {
-    if (D == 64) return gather_split_t<float, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
-    if (D == 128) return gather_split_t<float, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
+    if (D == 64) return gather_split_t<float, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
+    if (D == 128) return gather_split_t<float, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
   } else {
-    if (D == 64) return gather_split_t<bf16_t, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
-    if (D == 128) return gather_split_t<bf16_t, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, s, names);
+    if (D == 64) return gather_split_t<bf16_t, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
+    if (D == 128) return gather_split_t<bf16_t, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
   }
   return hipErrorInvalidValue;
 }

@@ -229,6 +229,7 @@ __global__ void init_chunk_kernel(WsHeader* hdr, uint32_t* kstat, int* rcount, i
       hdr->rescored = 0;
       hdr->queries = 0;
       hdr->retried = 0;
+      hdr->margin_violations = 0;
     }
     hdr->fb_count = 0;
     hdr->fb_next = 0;

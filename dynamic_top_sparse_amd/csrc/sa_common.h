@@ -271,7 +271,8 @@ struct WsHeader {
   unsigned long long retried;            // queries filtered again with a proven threshold
   unsigned int fb_count;                 // queries queued for the fallback
   unsigned int fb_next;                  // fallback work-queue cursor
-  unsigned int pad[2];
+  unsigned int margin_violations;        // re-scored keys outside [s~ - m, s~ + m]
+  unsigned int pad;
 };
 static_assert(sizeof(WsHeader) % 16 == 0, "header keeps 16-byte alignment");
 

@@ -5,7 +5,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "sa_common.h"
+#include "sparse_attn.h"
 
 namespace sa {
 
@@ -85,8 +88,9 @@ struct Plan {
 
 // Fills every field from the arguments and heads_per_chunk; returns false
 // when the sizes do not fit the index arithmetic.
+// filt: the filter operand type (0 = fp16, 1 = bf16).
 bool make_plan(Plan& p, int B, int H, int N, int D, int dp, int k, int causal, int dtype,
-               int with_idx, int heads_per_chunk);
+               int with_idx, int heads_per_chunk, int filt);
 
 // Threshold sample: rank r of the sample maxima that sets a query's
 // threshold (about beta * k keys are expected above it; the sample stride is
@@ -172,14 +176,20 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
 // beside the rows.
 hipError_t launch_gather_split(const void* Q, const void* K, const void* V, const int32_t* idx,
                                int k, int N, int D, float softmax_scale, int dtype, const int* seg,
-                               float* part, void* O, hipStream_t s);
+                               float* part, void* O, sa_profile* prof, hipStream_t s);
 hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
                        hipStream_t s);
 
-// Optional per-launch timing (see sparse_attn_profile_enable).  Launch
-// wrappers call prof_begin before and prof_end after a launch.
-void prof_begin(const char* name, hipStream_t s);
-void prof_end(hipStream_t s);
+// Optional per-launch timing into a caller-owned record (NULL: none).
+// prof_begin records the start event and returns the slot that prof_end
+// closes (-1 when nothing was recorded).
+int prof_begin(sa_profile* prof, const char* name, hipStream_t s);
+void prof_end(sa_profile* prof, int token, hipStream_t s);
+
+// Sets a kernel's dynamic-LDS limit once per device (thread-safe); `flags`
+// is a per-kernel array of kMaxDevices flags.
+constexpr int kMaxDevices = 64;
+hipError_t set_lds_limit_once(const void* kernel, int bytes, std::atomic<int>* flags);
 
 // Sticky device flag set by the gather when an index is >= N.
 hipError_t read_and_clear_device_flag(int* value, hipStream_t s);

@@ -33,6 +33,9 @@
  *   stream).  Arguments are validated on the host before anything is
  *   enqueued; on a negative return value nothing was enqueued.
  * - Calls that share a workspace must not overlap in time.
+ * - The library keeps no mutable state between calls: everything a call
+ *   depends on is in its arguments (the options below included), so calls
+ *   from several host threads on different workspaces are independent.
  */
 #ifndef SPARSE_ATTN_H
 #define SPARSE_ATTN_H
@@ -61,6 +64,32 @@ typedef enum {
 
 /* Shape of Q, K, V, O: [B, H, N, D]. */
 typedef struct { int32_t B, H, N, D; } sa_dims;
+
+/*
+ * Per-kernel timing record, owned by the caller (created and destroyed with
+ * sparse_attn_profile_create / _destroy).  A call given one brackets each of
+ * its kernel launches with a pair of HIP events on the launch stream; its
+ * own mutex makes it safe to share between threads.
+ */
+typedef struct sa_profile sa_profile;
+
+/*
+ * Options of a compute call, read while the call runs and never kept.
+ * Passing NULL is the same as { SA_F16, NULL }.
+ *   filter_dtype: operand type of the 16-bit MFMA filter inside
+ *     sparse_attn_scores_topk and sparse_attn_fwd, SA_F16 or SA_BF16.  Rows
+ *     are scaled by powers of two before rounding (one exponent per query
+ *     row, one per key head), so either type covers the fp32 range.  The
+ *     returned indices are the same for both: the filter only discards keys
+ *     that provably cannot be in the top-k, and the final choice uses the
+ *     exact fp32 score.  fp16 keeps 11 significant bits instead of 8, which
+ *     shrinks the band of keys that must be re-scored exactly.
+ *   profile: NULL, or a timing record that receives this call's launches.
+ */
+typedef struct {
+  int32_t filter_dtype;
+  sa_profile* profile;
+} sa_options;
 
 /*
  * Bytes of workspace that sparse_attn_scores_topk, sparse_attn_fwd and
@@ -96,7 +125,7 @@ size_t sparse_attn_workspace_size_for_chunk(sa_dims d, int32_t d_proj, int32_t k
 int sparse_attn_scores_topk(const void* Q, const void* K, const void* Pq, const void* Pk,
                             sa_dims d, int32_t d_proj, int32_t k, int32_t causal,
                             float score_scale, int32_t dtype, int32_t* idx,
-                            void* ws, size_t ws_bytes, void* stream);
+                            void* ws, size_t ws_bytes, const sa_options* opts, void* stream);
 
 /*
  * Attention over index sets (step 3).
@@ -111,17 +140,24 @@ int sparse_attn_scores_topk(const void* Q, const void* K, const void* Pq, const 
  */
 int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                        int32_t k, sa_dims d, float softmax_scale, int32_t dtype, void* O,
-                       void* stream);
+                       const sa_options* opts, void* stream);
 
 /*
- * The whole forward: sparse_attn_scores_topk followed by sparse_attn_gather,
- * head chunk by head chunk.  idx_or_null receives the index sets when not
- * NULL; otherwise they live in the workspace (size it with with_idx = 1).
+ * The whole forward, the two-step allocation of page "mhpq.cn/news/1098205"
+ * §1.3 (score every pair cheaply, then attend only to each query's best k)
+ * as run by the §3.2 forward: sparse_attn_scores_topk followed by
+ * sparse_attn_gather, head chunk by head chunk.
+ *   Q, K, V: [B,H,N,D]; Pq, Pk: [D,d_proj]; O (out): [B,H,N,D].
+ *   idx_or_null receives the index sets when not NULL; otherwise they live
+ *   in the workspace (size it with with_idx = 1).
+ *   O and idx are exactly those of the two separate calls with the same
+ *   arguments.  Errors: as for those two calls.
  */
 int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
                     const void* Pk, sa_dims d, int32_t d_proj, int32_t k, int32_t causal,
                     float score_scale, float softmax_scale, int32_t dtype, void* O,
-                    int32_t* idx_or_null, void* ws, size_t ws_bytes, void* stream);
+                    int32_t* idx_or_null, void* ws, size_t ws_bytes, const sa_options* opts,
+                    void* stream);
 
 /*
  * Band (sliding-window) index sets: the fixed-index special case.
@@ -132,33 +168,26 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
  *   wrapped), truncated to k entries, then -1 padding.  d.D is ignored.
  */
 int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t* idx,
-                             int32_t k, void* stream);
+                             int32_t k, const sa_options* opts, void* stream);
 
 /*
- * The fp32 scores the selection uses, for query rows [row_begin,
- * row_begin + row_count) of every head: S (out) is [B,H,row_count,N] fp32.
- * S[.., r, j] = fl(score_scale · fl(q_low_i · k_low_j)) with the dot product
- * accumulated in a fixed order; pairs excluded by the causal mask are -inf.
- * Needs the same workspace as sparse_attn_scores_topk.
+ * The scorer's output for chosen query rows: the fp32 scores the selection
+ * uses (page "mhpq.cn/news/1098205" §2.2, LightweightScorer: the scaled dot
+ * product d_proj^-1/2 · q_low·k_lowᵀ), written out so that the top-k can be
+ * recomputed from them; that page's troubleshooting notes (§4.4) suggest
+ * comparing the selected top-k indices across runs, which needs exactly
+ * these values.
+ *   Rows [row_begin, row_begin + row_count) of every head: S (out) is
+ *   [B,H,row_count,N] fp32, S[.., r, j] = fl(score_scale · fl(q_low_i ·
+ *   k_low_j)) with the dot product accumulated in a fixed order; pairs
+ *   excluded by the causal mask are -inf.
+ *   Needs the same workspace as sparse_attn_scores_topk.  A row range
+ *   outside [0, N) is SA_ERR_SHAPE.
  */
 int sparse_attn_scores_dump(const void* Q, const void* K, const void* Pq, const void* Pk,
                             sa_dims d, int32_t d_proj, int32_t causal, float score_scale,
                             int32_t dtype, int32_t row_begin, int32_t row_count, float* S,
-                            void* ws, size_t ws_bytes, void* stream);
-
-/*
- * Operand type of the 16-bit MFMA filter inside sparse_attn_scores_topk and
- * sparse_attn_fwd: SA_F16 (default) or SA_BF16.  Rows are scaled by powers
- * of two before rounding (one exponent per query row, one per key head), so
- * either type covers the fp32 range.  The returned indices are the same for
- * both: the filter only discards keys that provably cannot be in the top-k,
- * and the final choice uses the exact fp32 score.  fp16 keeps 11 significant
- * bits instead of 8, which shrinks the band of keys that must be re-scored
- * exactly.  Process-wide; affects calls made after it returns.
- * Returns SA_OK or SA_ERR_UNSUPPORTED.
- */
-int sparse_attn_set_filter_dtype(int32_t dtype);
-int sparse_attn_get_filter_dtype(void);
+                            void* ws, size_t ws_bytes, const sa_options* opts, void* stream);
 
 /*
  * Synchronizes `stream`, then reports and clears the sticky device flag:
@@ -173,22 +202,29 @@ int sparse_attn_check_status(void* stream);
  * out: [0] queries resolved by the exact fallback path, [1] queries whose
  * first candidate list overflowed, [2] total candidates written, [3] total
  * keys re-scored exactly, [4] queries resolved, [5] queries filtered a second
- * time with a proven threshold, summed over all head chunks of the call.
- * Returns the number of values written or a negative status.
+ * time with a proven threshold, [6] re-scored keys whose exact score fell
+ * outside the interval the filter's margin gives for it (0 unless the
+ * margin's rounding bound is wrong), summed over all head chunks of the
+ * call.  Returns the number of values written or a negative status.
  */
 int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, int32_t n,
                                 void* stream);
 
 /*
- * Per-kernel timing for benchmarks.  While enabled, every kernel the library
- * launches is bracketed by a pair of HIP events recorded on the launch
- * stream; sparse_attn_profile_read synchronizes those events and returns
- * (kernel name, milliseconds) records in launch order, then forgets them.
- * Disabled by default; enabling it costs two event records per launch.
+ * Per-kernel timing for benchmarks, in a caller-owned record.
+ * sparse_attn_profile_create returns a new, empty record (NULL if host
+ * memory or HIP events cannot be had); the caller passes it in
+ * sa_options.profile and frees it with sparse_attn_profile_destroy (NULL is
+ * ignored).  sparse_attn_profile_read synchronizes the events of the
+ * launches recorded so far and writes up to n (kernel name, milliseconds)
+ * records in launch order, then forgets all of them; it returns the number
+ * written or a negative status.  Recording costs two event records per
+ * launch; a record not passed to a call costs nothing.
  */
 typedef struct { char name[48]; float ms; } sa_kernel_time;
-int sparse_attn_profile_enable(int32_t on);
-int sparse_attn_profile_read(sa_kernel_time* out, int32_t n);
+sa_profile* sparse_attn_profile_create(void);
+void sparse_attn_profile_destroy(sa_profile* prof);
+int sparse_attn_profile_read(sa_profile* prof, sa_kernel_time* out, int32_t n);
 
 /* Static description of a status code. */
 const char* sparse_attn_status_string(int status);

@@ -47,12 +47,26 @@ D = sa.sa_dims
 A = 0x100000  # a 16-byte-aligned fake address: never dereferenced in these tests
 
 
-def test_filter_dtype_option(lib):
-    assert lib.sparse_attn_get_filter_dtype() == 2          # fp16 by default
-    assert lib.sparse_attn_set_filter_dtype(0) == -3        # fp32 is not a filter type
-    assert lib.sparse_attn_set_filter_dtype(1) == 0
-    assert lib.sparse_attn_get_filter_dtype() == 1
-    assert lib.sparse_attn_set_filter_dtype(2) == 0
+def test_options_and_profile_record(lib):
+    """Options are per call: an unknown filter type is refused on the host;
+    a timing record is created, read empty and destroyed without a GPU."""
+    bad = sa.sa_options(0, None)                           # fp32 is not a filter type
+    assert _topk(lib, opts=ctypes.byref(bad)) == -3
+    assert lib.sparse_attn_fwd(A, A, A, A, A, D(1, 2, 256, 64), 16, 8, 0, 0.25, 0.1, 1, A,
+                               None, A, 1 << 30, ctypes.byref(bad), None) == -3
+    prof = lib.sparse_attn_profile_create()
+    assert prof
+    out = (sa.sa_kernel_time * 4)()
+    assert lib.sparse_attn_profile_read(prof, out, 4) == 0
+    assert lib.sparse_attn_profile_read(None, out, 4) == -1
+    lib.sparse_attn_profile_destroy(prof)
+    lib.sparse_attn_profile_destroy(None)
+
+
+def test_header_has_no_process_wide_setters():
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    for name in re.findall(r"\b(sparse_attn_\w+)\s*\(", text):
+        assert "set_" not in name and "enable" not in name, name
 
 
 def test_status_strings(lib):
@@ -79,9 +93,9 @@ def test_workspace_size_arithmetic(lib):
 
 
 def _topk(lib, Q=A, K=A, Pq=A, Pk=A, d=D(1, 1, 1024, 64), dp=16, k=32, causal=0, scale=0.25,
-          dtype=0, idx=A, ws=A, ws_bytes=0):
+          dtype=0, idx=A, ws=A, ws_bytes=0, opts=None):
     return lib.sparse_attn_scores_topk(Q, K, Pq, Pk, d, dp, k, causal, scale, dtype, idx, ws,
-                                       ws_bytes, None)
+                                       ws_bytes, opts, None)
 
 
 def test_scores_topk_validation(lib):
@@ -103,29 +117,83 @@ def test_scores_topk_validation(lib):
 
 def test_gather_fwd_band_dump_validation(lib):
     d = D(1, 2, 256, 64)
-    assert lib.sparse_attn_gather(A, A, None, A, 8, d, 0.1, 0, A, None) == -1
-    assert lib.sparse_attn_gather(A, A, A, A, 0, d, 0.1, 0, A, None) == -2
-    assert lib.sparse_attn_gather(A, A, A, A, 8, D(1, 2, 256, 32), 0.1, 0, A, None) == -3
-    assert lib.sparse_attn_gather(A, A, A, A + 4, 8, d, 0.1, 0, A, None) == -4
-    assert lib.sparse_attn_gather(A, A, A, A, 8, d, float("inf"), 0, A, None) == -2
+    assert lib.sparse_attn_gather(A, A, None, A, 8, d, 0.1, 0, A, None, None) == -1
+    assert lib.sparse_attn_gather(A, A, A, A, 0, d, 0.1, 0, A, None, None) == -2
+    assert lib.sparse_attn_gather(A, A, A, A, 8, D(1, 2, 256, 32), 0.1, 0, A, None, None) == -3
+    assert lib.sparse_attn_gather(A, A, A, A + 4, 8, d, 0.1, 0, A, None, None) == -4
+    assert lib.sparse_attn_gather(A, A, A, A, 8, d, float("inf"), 0, A, None, None) == -2
     assert lib.sparse_attn_fwd(A, A, A, A, A, d, 16, 8, 0, 0.25, 0.1, 0, None, None, A, 1 << 30,
-                               None) == -1
+                               None, None) == -1
     assert lib.sparse_attn_fwd(A, A, A, A, A, d, 16, 8, 0, 0.25, 0.1, 1, A, A + 2, A, 1 << 30,
-                               None) == -4
+                               None, None) == -4
     assert lib.sparse_attn_fwd(A, A, A, A, A, d, 16, 8, 0, 0.25, 0.1, 1, A, None, A, 64,
-                               None) == -5
-    assert lib.sparse_attn_band_indices(d, -1, 3, A, 5, None) == -2
-    assert lib.sparse_attn_band_indices(d, 1, 3, None, 5, None) == -1
-    assert lib.sparse_attn_band_indices(d, 1, 3, A + 4, 5, None) == -4
+                               None, None) == -5
+    assert lib.sparse_attn_band_indices(d, -1, 3, A, 5, None, None) == -2
+    assert lib.sparse_attn_band_indices(d, 1, 3, None, 5, None, None) == -1
+    assert lib.sparse_attn_band_indices(d, 1, 3, A + 4, 5, None, None) == -4
     assert lib.sparse_attn_scores_dump(A, A, A, A, d, 16, 0, 0.25, 0, 250, 7, A, A, 1 << 30,
-                                       None) == -2               # rows past N
+                                       None, None) == -2         # rows past N
     assert lib.sparse_attn_scores_dump(A, A, A, A, d, 16, 0, 0.25, 0, -1, 1, A, A, 1 << 30,
-                                       None) == -2
+                                       None, None) == -2
     assert lib.sparse_attn_scores_dump(A, A, A, A, d, 16, 0, 0.25, 0, 0, 1, A, A, 16,
-                                       None) == -5
+                                       None, None) == -5
     out = (ctypes.c_int64 * 5)()
     assert lib.sparse_attn_workspace_stats(None, 1024, out, 5, None) == -1
     assert lib.sparse_attn_workspace_stats(A, 8, out, 5, None) == -5
+
+
+def _qkv(B=1, H=2, N=64, D=64, dtype=None):
+    import torch
+    dtype = dtype or torch.float32
+    return [torch.zeros(B, H, N, D, dtype=dtype) for _ in range(3)]
+
+
+@pytest.mark.parametrize("what", ["K_shape", "V_shape", "K_dtype", "O_shape", "O_dtype",
+                                  "Pq_rows", "Pk_shape", "P_dtype", "idx_dtype", "idx_shape",
+                                  "idx_k"])
+def test_binding_rejects_mismatched_tensors(what):
+    """Every tensor is checked against Q before anything reaches the library:
+    a smaller K or V, a mixed dtype, a wrong-width Pk or a short idx would
+    otherwise be read or written past its end by the kernels."""
+    import torch
+    Q, K, V = _qkv()
+    Pq = torch.zeros(64, 16)
+    Pk = torch.zeros(64, 16)
+    idx = torch.zeros(1, 2, 64, 8, dtype=torch.int32)
+    O = None
+    if what == "K_shape":
+        K = torch.zeros(1, 2, 32, 64)
+    elif what == "V_shape":
+        V = torch.zeros(1, 1, 64, 64)
+    elif what == "K_dtype":
+        K = K.to(torch.bfloat16)
+    elif what == "O_shape":
+        O = torch.zeros(1, 2, 64, 32)
+    elif what == "O_dtype":
+        O = torch.zeros(1, 2, 64, 64, dtype=torch.bfloat16)
+    elif what == "Pq_rows":
+        Pq = torch.zeros(32, 16)
+    elif what == "Pk_shape":
+        Pk = torch.zeros(64, 32)
+    elif what == "P_dtype":
+        Pq, Pk = Pq.to(torch.bfloat16), Pk.to(torch.bfloat16)
+    elif what == "idx_dtype":
+        idx = idx.to(torch.int16)
+    elif what == "idx_shape":
+        idx = torch.zeros(1, 2, 63, 8, dtype=torch.int32)
+    elif what == "idx_k":
+        idx = torch.zeros(1, 2, 64, 9, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        if what.startswith("idx"):
+            sa.sparse_attn_scores_topk(Q, K, Pq, Pk, 8, idx=idx, workspace=torch.zeros(1, dtype=torch.uint8))
+        elif what in ("V_shape", "O_shape", "O_dtype"):
+            sa.sparse_attn_fwd(Q, K, V, Pq, Pk, 8, O=O, workspace=torch.zeros(1, dtype=torch.uint8))
+        else:
+            sa.sparse_attn_fwd(Q, K, V, Pq, Pk, 8, workspace=torch.zeros(1, dtype=torch.uint8))
+    if what.startswith("idx") or what in ("K_shape", "V_shape", "K_dtype", "O_shape"):
+        with pytest.raises(ValueError):
+            sa.sparse_attn_gather(Q, K, V, idx if what.startswith("idx") and what != "idx_k"
+                                  else torch.zeros(1, 2, 63, 8, dtype=torch.int32), O=O)
 
 
 def test_binding_refuses_cpu_tensors():

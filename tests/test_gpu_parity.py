@@ -45,18 +45,21 @@ def check_idx_rows(idx_rows, S_dump, S64, rows, k, causal, N):
     return ov
 
 
-def run_case(w: W.Workload, seed=0, rows=None, check_all=True):
-    x = W.make_inputs(w, seed)
+def run_case(w: W.Workload, seed=0, rows=None, check_all=True, filter_dtype=None, x=None):
+    x = W.make_inputs(w, seed) if x is None else x
     g = _cuda(x)
     B, H, N, D = w.B, w.H, w.N, w.D
     ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=False)
     idx = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k, w.causal,
-                                     workspace=ws)
+                                     workspace=ws, filter_dtype=filter_dtype)
     out, idx2 = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
-                                   return_idx=True)
+                                   return_idx=True, filter_dtype=filter_dtype)
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2), "fused and split paths disagree"
     stats = sa.sparse_attn_workspace_stats(ws)
+    # every exactly re-scored key lies in the interval the filter's margin
+    # gives it: the no-miss argument's rounding bound holds on these inputs
+    assert stats["margin_violations"] == 0, stats
     # the exact fallback keeps results right even when the filter is broken,
     # so a flood of fallbacks must fail the test on its own
     if w.N >= 4096:
@@ -176,12 +179,9 @@ def test_tiny_fp32_workload_all_rows():
 
 @pytest.fixture(params=[torch.float16, torch.bfloat16], ids=["filter_f16", "filter_bf16"])
 def filter_dtype(request):
-    """Runs a test with each 16-bit operand type of the MFMA filter; the
+    """Each 16-bit operand type of the MFMA filter (passed per call); the
     indices must not depend on it."""
-    before = sa.sparse_attn_get_filter_dtype()
-    sa.sparse_attn_set_filter_dtype(request.param)
-    yield request.param
-    sa.sparse_attn_set_filter_dtype(before)
+    return request.param
 
 
 @pytest.mark.parametrize("N,k,dp,D,dtype,causal", [
@@ -196,7 +196,7 @@ def filter_dtype(request):
 ])
 def test_topk_and_forward_small_shapes_all_rows(N, k, dp, D, dtype, causal, filter_dtype):
     w = W.Workload("case", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
-    run_case(w, seed=N + k)
+    run_case(w, seed=N + k, filter_dtype=filter_dtype)
 
 
 def test_largest_k_with_key_range_gather_all_rows():
@@ -208,7 +208,7 @@ def test_largest_k_with_key_range_gather_all_rows():
 
 def test_mixture_causal_small_all_rows(filter_dtype):
     w = W.get("causal_mixture", B=2, H=2, N=6000, k=64)
-    run_case(w, seed=5)
+    run_case(w, seed=5, filter_dtype=filter_dtype)
 
 
 def test_exact_ties_go_to_lower_index(filter_dtype):
@@ -219,7 +219,8 @@ def test_exact_ties_go_to_lower_index(filter_dtype):
     K[0, 0, 2000:2600] = K[0, 0, 0:600]     # keys 2000.. repeat keys 0..
     x["K"] = K
     g = _cuda(x)
-    idx = _rows_np(sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k))
+    idx = _rows_np(sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k,
+                                              filter_dtype=filter_dtype))
     S = _rows_np(sa.sparse_attn_scores_dump(g["Q"], g["K"], g["Pq"], g["Pk"], 0, 3000))
     assert np.array_equal(S[0, 0][:, 2000:2600], S[0, 0][:, 0:600])
     want = O.topk_rows(S[0, 0].astype(np.float64), list(range(3000)), w.k, False)
@@ -269,44 +270,169 @@ def test_fused_forward_same_bits_per_chunk_size_and_stream():
 
 # ------------------------------------------------- full-size workloads ---
 
-def _ranges(N, causal):
-    r = [(0, 8), (N // 3, 8), (N - 8, 8)]
+def _sample_ranges(N, causal, k, seed, n_ranges=64, width=16):
+    """Seeded random row ranges (n_ranges x width rows) plus the first and last
+    rows and, causally, the rows around i = k where the valid-key count
+    crosses k; overlapping ranges are trimmed so every row is checked once."""
+    rng = np.random.default_rng(seed)
+    starts = set(int(x) for x in rng.choice(N - width, n_ranges, replace=False))
+    starts |= {0, N - width}
     if causal:
-        r.insert(1, (500, 24))              # rows around i = k: fewer than k valid keys
-    return r
+        starts.add(max(0, k - width // 2))
+    out, last = [], -1
+    for s0 in sorted(starts):
+        a, b = max(s0, last + 1), min(s0 + width, N)
+        if b > a:
+            out.append((a, b - a))
+            last = b - 1
+    return out
 
 
-@pytest.mark.parametrize("dtype,D,causal,k", [("f32", 64, False, 64), ("bf16", 128, False, 64),
-                                               ("bf16", 128, True, 64), ("bf16", 64, False, 512),
-                                               ("bf16", 128, True, 512)])
-def test_fused_forward_key_range_gather(dtype, D, causal, k):
-    """Past N = 8192 the fused forward gathers by key range (partials per
-    range, then a merge); ragged N, empty ranges and, causally, rows whose
-    keys all fall in the first ranges.  With k = 512 a range holds enough of
-    a row's keys for whole blocks of row loads, not only a last partial one."""
-    w = W.get("bf16_32k", N=8200, H=2, D=D, dtype=dtype, d_proj=64 if D == 128 else 16,
-              k=k, causal=causal)
-    run_case(w, seed=5, rows=[(0, 300), (4000, 200), (8000, 200)])
+def check_sampled_heads(w, x, idx, out, heads, ranges):
+    """idx and O of the full-size call, on the given (b, h) heads and row
+    ranges: bit-exact idx against the oracle's top-k of the dumped fp32
+    scores, overlap against fp64 scores, O against the oracle's attention."""
+    sscale = sa.default_score_scale(w.d_proj)
+    ascale = sa.default_softmax_scale(w.D)
+    for (b, h) in heads:
+        sl = {n: x[n][b:b + 1, h:h + 1].contiguous() for n in ("Q", "K", "V")}
+        gq, gk = sl["Q"].cuda(), sl["K"].cuda()
+        gpq, gpk = x["Pq"].cuda(), x["Pk"].cuda()
+        ws = sa.allocate_workspace(gq, w.d_proj, 1, w.causal)
+        k_low = O.project(O.f64(sl["K"][0, 0]), O.f64(x["Pk"]))
+        q_all = O.f64(sl["Q"][0, 0])
+        idx_h = _rows_np(idx[b, h])
+        out_h = _rows_np(out[b, h].float())
+        print(f"checking head ({b}, {h}): {sum(c for _, c in ranges)} rows", flush=True)
+        for (r0, rc) in ranges:
+            rr = list(range(r0, r0 + rc))
+            S = _rows_np(sa.sparse_attn_scores_dump(gq, gk, gpq, gpk, r0, rc, w.causal,
+                                                    workspace=ws))[0, 0]
+            S64 = O.score_rows(O.project(q_all[r0:r0 + rc], O.f64(x["Pq"])), k_low, sscale)
+            if w.causal:
+                S64 = np.where(np.arange(w.N)[None, :] <= np.asarray(rr)[:, None], S64, -np.inf)
+            check_idx_rows(idx_h[r0:r0 + rc], S, S64, rr, w.k, w.causal, w.N)
+            want = O.gather_attention(sl["Q"], sl["K"], sl["V"], idx_h[None, None, r0:r0 + rc],
+                                      ascale, rr)[0, 0]
+            err = np.abs(out_h[r0:r0 + rc] - want).max()
+            assert err <= TOL[w.torch_dtype], (err, (b, h), r0)
 
 
 @pytest.mark.parametrize("name", ["bf16_32k", "headline_128k", "causal_mixture"])
 def test_full_size_workloads_sampled_rows(name):
+    """The three large workloads at their full sizes, in the launch setup the
+    benchmark times (all heads in one fused call): 1024+ seeded random rows
+    on each of two heads, plus the edges and (causal) the rows near i = k."""
     w = W.get(name)
-    stats = run_case(w, rows=_ranges(w.N, w.causal))
-    print(name, stats)
+    x = W.make_inputs(w, 0)
+    g = _cuda(x)
+    ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=False,
+                               heads_per_chunk=w.B * w.H)
+    out, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
+                                  workspace=ws, return_idx=True)
+    torch.cuda.synchronize()
+    stats = sa.sparse_attn_workspace_stats(ws)
+    print(name, stats, flush=True)
     assert stats["queries"] == w.queries
     assert stats["fallback_queries"] <= 0.01 * w.queries
+    assert stats["margin_violations"] == 0, stats
+    del g
+    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    check_sampled_heads(w, x, idx, out, heads, _sample_ranges(w.N, w.causal, w.k, seed=17))
+
+
+# ------------------------------------------ retry and fallback paths ---
+
+def _tied_keys(w, seed, copies, all_same_head=None):
+    """Inputs whose key rows repeat: in every head, `copies` positions hold the
+    very same row (bit-identical scores for every query, so top lists of tied
+    keys overflow), and head `all_same_head` has one row for all its keys."""
+    x = W.make_inputs(w, seed)
+    K = x["K"].clone()
+    rng = np.random.default_rng(seed)
+    for b in range(w.B):
+        for h in range(w.H):
+            if h == all_same_head:
+                K[b, h] = K[b, h, 0]
+            else:
+                pos = rng.choice(w.N, copies, replace=False)
+                K[b, h, torch.as_tensor(pos)] = K[b, h, int(pos[0])]
+    x["K"] = K.contiguous()
+    return x
+
+
+@pytest.mark.parametrize("N,k,causal,dtype", [(3000, 64, False, "f32"), (3000, 64, True, "bf16"),
+                                              (3000, 700, False, "bf16"), (2600, 900, True, "f32")])
+def test_retry_and_fallback_paths_all_rows(N, k, causal, dtype, filter_dtype):
+    """Repeated key rows make lists overflow on the first pass and again on
+    the retry with a proven threshold, so the exact fallback resolves those
+    queries (its radix select and its ordering of tied keys across threads),
+    while other queries of the same call take the retry path.  Every row is
+    checked: idx bit-exact against the oracle's top-k of the dumped scores
+    (ties to the lower index), O against the oracle's attention; causally
+    with rows below and above k valid keys."""
+    w = W.Workload("ties", 1, 3, N, 64 if dtype == "f32" else 128, dtype,
+                   d_proj=16 if dtype == "f32" else 64, k=k, causal=causal)
+    x = _tied_keys(w, seed=N + k, copies=N // 3, all_same_head=2)
+    stats = run_case(w, x=x, filter_dtype=filter_dtype)
+    print(stats, flush=True)
+    assert stats["fallback_queries"] > 0, stats
+    assert stats["retried"] > 0, stats
+    assert stats["queries"] == w.queries
+
+
+# ------------------------------------------------ projection precision ---
+
+def _score_error_bound(Q, K, Pq, Pk, scale, rows):
+    """Elementwise bound on |S_library - S_exact| for fp32 projections and an
+    fp32 score: each projection is a sum of D exact products (or fp32
+    products) rounded in some order, so its error is at most
+    gamma_D * sum_d |x_d P_dc| (gamma_n = n u / (1 - n u), u = 2^-24); the
+    score adds the projections' errors times the other factor, and its own
+    sum of d_proj products at most gamma_dp * sum_c |q_c k_c|."""
+    u = 2.0 ** -24
+    D, dp = Pq.shape
+
+    def gam(n):
+        return n * u / (1 - n * u)
+
+    Qa, Ka = O.f64(Q)[rows], O.f64(K)
+    Pqa, Pka = O.f64(Pq), O.f64(Pk)
+    q, kk = Qa @ Pqa, Ka @ Pka
+    Eq = gam(D + 1) * (np.abs(Qa) @ np.abs(Pqa))
+    Ek = gam(D + 1) * (np.abs(Ka) @ np.abs(Pka))
+    aq, ak = np.abs(q) + Eq, np.abs(kk) + Ek
+    bound = Eq @ np.abs(kk).T + np.abs(q) @ Ek.T + Eq @ Ek.T + gam(dp + 1) * (aq @ ak.T)
+    return scale * bound * (1 + 1e-6) + 1e-30
+
+
+@pytest.mark.parametrize("dtype,D,dp", [("bf16", 128, 64), ("bf16", 64, 32), ("f32", 128, 128)])
+def test_scores_dump_within_rounding_bound_of_fp64(dtype, D, dp):
+    """The library's fp32 scores (bf16 rows on the MFMA projection, fp32 rows
+    on FMAs) lie within the rounding bound of the exact fp64 scores, element
+    by element; a projection or score rounded through a 16-bit type would
+    miss it by orders of magnitude."""
+    w = W.Workload("proj", 1, 2, 2500, D, dtype, d_proj=dp, k=8)
+    x = W.make_inputs(w, 21)
+    g = _cuda(x)
+    scale = sa.default_score_scale(dp)
+    S = _rows_np(sa.sparse_attn_scores_dump(g["Q"], g["K"], g["Pq"], g["Pk"], 0, w.N))
+    rows = np.arange(w.N)
+    worst = 0.0
+    for h in range(w.H):
+        S64 = O.scores(x["Q"], x["K"], x["Pq"], x["Pk"], scale, 0, h)
+        bound = _score_error_bound(x["Q"][0, h], x["K"][0, h], x["Pq"], x["Pk"], scale, rows)
+        err = np.abs(S[0, h].astype(np.float64) - S64)
+        assert np.all(err <= bound), (float((err / bound).max()), h)
+        worst = max(worst, float((err / bound).max()))
+    print(f"largest error / bound: {worst:.3g}")
 
 
 def test_filter_dtype_does_not_change_indices():
     w = W.get("bf16_32k", N=6000, H=2, k=96)
     g = _cuda(W.make_inputs(w, 11))
-    before = sa.sparse_attn_get_filter_dtype()
-    try:
-        sa.sparse_attn_set_filter_dtype(torch.float16)
-        a = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k)
-        sa.sparse_attn_set_filter_dtype(torch.bfloat16)
-        b = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k)
-    finally:
-        sa.sparse_attn_set_filter_dtype(before)
+    a = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k,
+                                   filter_dtype=torch.float16)
+    b = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], w.k,
+                                   filter_dtype=torch.bfloat16)
     assert torch.equal(a, b)
