@@ -8,5 +8,6 @@ from .sparse_attn_oracle import (  # noqa: F401
     topk_indices, brute_force_topk, attend_row, gather_attention,
     sparse_attn_fwd, band_indices, dense_attention, local_mask,
     brute_force_attention, attend_row_backward, sparse_attn_backward,
+    smoothed_topk_row, smoothed_topk_rows, dilated_indices, band_indices_per_batch,
 )
 from .compare import row_invariants, set_overlap  # noqa: F401

@@ -27,6 +27,15 @@ float64 with NumPy, one step per statement, following the pages:
      page "nxmr.cn/news/163144", §2.2): query i keeps keys
      max(0, i-w_left) .. min(N-1, i+w_right).
 
+  6. Index variants feeding the same attention:
+     - boundary smoothing (page "mhpq.cn/news/1098205", §4.2): when the gap
+       between the k-th and (k+1)-th scores is below a threshold, both are
+       kept, so a row holds k or k+1 keys;
+     - dilated window with wrap-around (page "Attention机制优化：原理、挑战与
+       工程实践", §3.3): query i keeps (i + t·dilation) mod N for
+       t = 0 .. window-1, repeats included;
+     - a window radius per batch sample (page "nxmr.cn/news/163144", §6,
+       adaptive attention: each sample gets its own window size w).
   5. Backward (same page, §2.3, top-k selection and gradient flow): the
      forward keeps the hard top-k; in the backward the selected positions'
      gradients flow normally and unselected positions get zero; the scorer
@@ -208,6 +217,55 @@ def band_indices(N: int, w_left: int, w_right: int, width: int) -> np.ndarray:
         lo, hi = max(0, i - w_left), min(N - 1, i + w_right)
         keys = np.arange(lo, hi + 1)[:width]
         out[i, :keys.size] = keys
+    return out
+
+
+# -------------------------------------------------- 6. index variants ---
+
+def smoothed_topk_row(s: np.ndarray, valid: np.ndarray, k: int, gap: float) -> np.ndarray:
+    """Boundary smoothing of one row (page "mhpq.cn/news/1098205", §4.2):
+    order the valid keys by (score descending, index ascending); keep the
+    first k, and also the (k+1)-th when score_k - score_(k+1) < gap.  Output
+    in ascending key order, padded with -1 to k + 1 entries."""
+    cand = np.nonzero(valid)[0]
+    order = cand[np.lexsort((cand, -s[cand]))]
+    keep = min(k, order.size)
+    if order.size > k and (s[order[k - 1]] - s[order[k]]) < gap:
+        keep = k + 1
+    out = np.full(k + 1, -1, dtype=np.int32)
+    out[:keep] = np.sort(order[:keep])
+    return out
+
+
+def smoothed_topk_rows(S: np.ndarray, rows: Sequence[int], k: int, causal: bool,
+                       gap: float) -> np.ndarray:
+    """smoothed_topk_row over score rows S [R, N] of query rows ``rows``."""
+    N = S.shape[1]
+    return np.stack([smoothed_topk_row(S[r], valid_keys(N, int(i), causal), k, gap)
+                     for r, i in enumerate(rows)])
+
+
+def dilated_indices(N: int, window: int, dilation: int, width: int) -> np.ndarray:
+    """idx [N, width]: row i holds (i + t*dilation) mod N for t = 0 ..
+    window-1 (in t order, repeats kept), then -1 padding (page
+    "Attention机制优化：原理、挑战与工程实践", §3.3 sliding window with
+    dilation, wrapped modulo the sequence length)."""
+    out = np.full((N, width), -1, dtype=np.int32)
+    for i in range(N):
+        for t in range(min(window, width)):
+            out[i, t] = (i + t * dilation) % N
+    return out
+
+
+def band_indices_per_batch(B: int, H: int, N: int, radii: Sequence[int], width: int) -> np.ndarray:
+    """idx [B, H, N, width]: band_indices with radius radii[b] for every head
+    of batch sample b (page "nxmr.cn/news/163144", §6: one window size per
+    sample)."""
+    out = np.empty((B, H, N, width), dtype=np.int32)
+    for b in range(B):
+        rows = band_indices(N, int(radii[b]), int(radii[b]), width)
+        for h in range(H):
+            out[b, h] = rows
     return out
 
 
