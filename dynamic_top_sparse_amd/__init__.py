@@ -37,6 +37,9 @@ EXPORTS = (
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
     "sparse_attn_workspace_stats", "sparse_attn_profile_create", "sparse_attn_profile_destroy",
     "sparse_attn_profile_read", "sparse_attn_status_string",
+    "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
+    "sparse_attn_band_indices_per_batch", "sparse_attn_decode_workspace_size",
+    "sparse_attn_decode_append_keys", "sparse_attn_decode",
 )
 
 
@@ -92,6 +95,16 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "sparse_attn_profile_destroy": (None, [vp]),
         "sparse_attn_profile_read": (ctypes.c_int, [vp, ctypes.POINTER(sa_kernel_time), i32]),
         "sparse_attn_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "sparse_attn_scores_topk_smoothed": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32,
+                                                            i32, f32, f32, i32, vp, vp, sz, op,
+                                                            vp]),
+        "sparse_attn_dilated_indices": (ctypes.c_int, [sa_dims, i32, i32, vp, i32, op, vp]),
+        "sparse_attn_band_indices_per_batch": (ctypes.c_int, [sa_dims, vp, vp, i32, op, vp]),
+        "sparse_attn_decode_workspace_size": (sz, [sa_dims, i32, i32]),
+        "sparse_attn_decode_append_keys": (ctypes.c_int, [vp, vp, sa_dims, i32, i32, vp, i32, i32,
+                                                          op, vp]),
+        "sparse_attn_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32,
+                                              f32, i32, vp, vp, vp, vp, sz, op, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -377,6 +390,157 @@ def sparse_attn_band_indices(B: int, H: int, N: int, w_left: int, w_right: int,
     return idx
 
 
+def sparse_attn_scores_topk_smoothed(Q, K, Pq, Pk, k: int, gap: float, causal: bool = False,
+                                     score_scale: Optional[float] = None,
+                                     idx: Optional[torch.Tensor] = None,
+                                     workspace: Optional[torch.Tensor] = None,
+                                     filter_dtype: Optional[torch.dtype] = None,
+                                     profile: Optional[Profile] = None) -> torch.Tensor:
+    """idx [B,H,N,k+1] int32: the top-k, plus the (k+1)-th key where the
+    score gap to the k-th is below `gap` (boundary smoothing)."""
+    _check_qkv(Q, K)
+    d_proj = _check_proj(Pq, Pk, Q)
+    B, H, N, D = Q.shape
+    scale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
+    if idx is None:
+        idx = torch.empty((B, H, N, k + 1), dtype=torch.int32, device=Q.device)
+    _check_idx(idx, Q, k + 1)
+    if workspace is None:
+        workspace = allocate_workspace(Q, d_proj, k + 1, causal)
+    _check_workspace(workspace, Q)
+    st = load_library().sparse_attn_scores_topk_smoothed(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q), d_proj, k,
+        int(causal), scale, float(gap), _dtype_code(Q), _dev(idx, "idx"),
+        _dev(workspace, "workspace"), workspace.numel(), _options(filter_dtype, profile),
+        _stream(Q))
+    _check(st, "sparse_attn_scores_topk_smoothed")
+    return idx
+
+
+def sparse_attn_dilated_indices(B: int, H: int, N: int, window: int, dilation: int,
+                                k: Optional[int] = None, device="cuda",
+                                idx: Optional[torch.Tensor] = None,
+                                profile: Optional[Profile] = None) -> torch.Tensor:
+    """idx [B,H,N,k]: (i + t*dilation) mod N for t < window, then -1."""
+    if k is None:
+        k = window
+    if idx is None:
+        idx = torch.empty((B, H, N, k), dtype=torch.int32, device=device)
+    _tensor(idx, "idx")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, H, N, k):
+        raise ValueError(f"idx must be int32 [B, H, N, k] = {(B, H, N, k)}")
+    st = load_library().sparse_attn_dilated_indices(sa_dims(B, H, N, 0), window, dilation,
+                                                    _dev(idx, "idx"), k,
+                                                    _options(None, profile), _stream(idx))
+    _check(st, "sparse_attn_dilated_indices")
+    return idx
+
+
+def sparse_attn_band_indices_per_batch(H: int, N: int, radii: torch.Tensor,
+                                       k: Optional[int] = None,
+                                       idx: Optional[torch.Tensor] = None,
+                                       profile: Optional[Profile] = None) -> torch.Tensor:
+    """idx [B,H,N,k] with B = len(radii): sample b's rows are its band of
+    radius radii[b] (an int32 tensor on the GPU)."""
+    _tensor(radii, "radii")
+    if radii.dtype != torch.int32 or radii.dim() != 1:
+        raise ValueError("radii must be a 1-D int32 tensor")
+    B = radii.shape[0]
+    if k is None:
+        k = 2 * int(radii.max().item()) + 1
+    if idx is None:
+        idx = torch.empty((B, H, N, k), dtype=torch.int32, device=radii.device)
+    _tensor(idx, "idx")
+    if idx.dtype != torch.int32 or tuple(idx.shape) != (B, H, N, k):
+        raise ValueError(f"idx must be int32 [B, H, N, k] = {(B, H, N, k)}")
+    if idx.device != radii.device:
+        raise ValueError("idx and radii must be on one device")
+    st = load_library().sparse_attn_band_indices_per_batch(
+        sa_dims(B, H, N, 0), _dev(radii, "radii"), _dev(idx, "idx"), k,
+        _options(None, profile), _stream(idx))
+    _check(st, "sparse_attn_band_indices_per_batch")
+    return idx
+
+
+class DecodeCache:
+    """Caller-owned caches of the decode path: K and V caches [B,H,Ncap,D]
+    of the model's dtype and the k_low cache [B,H,Ncap,d_proj] fp32, plus
+    the decode workspace.  append() writes new keys (and values) at the
+    current length; step() runs one query per (b, h) over the cached keys."""
+
+    def __init__(self, B: int, H: int, Ncap: int, D: int, Pq, Pk, k: int,
+                 dtype=torch.bfloat16, device="cuda"):
+        _tensor(Pq, "Pq")
+        _like(Pk, Pq, "Pk", "Pq")
+        if Pq.dim() != 2 or Pq.shape[0] != D or Pq.dtype != dtype:
+            raise ValueError(f"Pq, Pk must be [{D}, d_proj] of {dtype}")
+        self.B, self.H, self.Ncap, self.D, self.k = B, H, Ncap, D, k
+        self.d_proj = int(Pq.shape[1])
+        self.Pq, self.Pk = Pq, Pk
+        self.dtype = dtype
+        self.K = torch.zeros(B, H, Ncap, D, dtype=dtype, device=device)
+        self.V = torch.zeros(B, H, Ncap, D, dtype=dtype, device=device)
+        self.klow = torch.zeros(B, H, Ncap, self.d_proj, dtype=torch.float32, device=device)
+        self.counts = torch.zeros(B, H, Ncap, dtype=torch.int32, device=device)
+        n = int(load_library().sparse_attn_decode_workspace_size(sa_dims(B, H, Ncap, D),
+                                                                 self.d_proj, k))
+        if n == 0:
+            raise SparseAttnError(-3, "sparse_attn_decode_workspace_size")
+        self.workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        self.len = 0
+
+    def append(self, K_new, V_new, profile: Optional[Profile] = None) -> None:
+        """Write T new keys and values [B,H,T,D] at rows len .. len+T-1."""
+        _tensor(K_new, "K_new")
+        if K_new.dim() != 4 or tuple(K_new.shape[:2]) != (self.B, self.H) or \
+                K_new.shape[3] != self.D or K_new.dtype != self.dtype:
+            raise ValueError("K_new must be [B, H, T, D] of the cache's dtype")
+        _like(V_new, K_new, "V_new", "K_new")
+        T = int(K_new.shape[2])
+        if self.len + T > self.Ncap:
+            raise ValueError("the cache is full")
+        st = load_library().sparse_attn_decode_append_keys(
+            _dev(K_new, "K_new"), _dev(self.Pk, "Pk"), sa_dims(self.B, self.H, T, self.D),
+            self.d_proj, _dtype_code(K_new), _dev(self.klow, "klow"), self.Ncap, self.len,
+            _options(None, profile), _stream(K_new))
+        _check(st, "sparse_attn_decode_append_keys")
+        self.K[:, :, self.len:self.len + T] = K_new
+        self.V[:, :, self.len:self.len + T] = V_new
+        self.len += T
+
+    def step(self, q, score_scale: Optional[float] = None,
+             softmax_scale: Optional[float] = None, O: Optional[torch.Tensor] = None,
+             idx: Optional[torch.Tensor] = None, count: bool = False,
+             profile: Optional[Profile] = None):
+        """O [B,H,1,D] (and idx [B,H,k]) of one query per (b, h) over the
+        cached keys 0 .. len-1."""
+        _tensor(q, "q")
+        if tuple(q.shape) != (self.B, self.H, 1, self.D) or q.dtype != self.dtype:
+            raise ValueError(f"q must be [B, H, 1, D] = {(self.B, self.H, 1, self.D)} "
+                             f"of {self.dtype}")
+        if self.len < 1:
+            raise ValueError("the cache is empty")
+        sscale = default_score_scale(self.d_proj) if score_scale is None else float(score_scale)
+        ascale = default_softmax_scale(self.D) if softmax_scale is None else float(softmax_scale)
+        if O is None:
+            O = torch.empty_like(q)
+        _like(O, q, "O", "q")
+        if idx is not None:
+            _tensor(idx, "idx")
+            if idx.dtype != torch.int32 or tuple(idx.shape) != (self.B, self.H, self.k):
+                raise ValueError(f"idx must be int32 [B, H, k] = {(self.B, self.H, self.k)}")
+        st = load_library().sparse_attn_decode(
+            _dev(q, "q"), _dev(self.K, "K"), _dev(self.V, "V"), _dev(self.klow, "klow"),
+            _dev(self.Pq, "Pq"), sa_dims(self.B, self.H, self.Ncap, self.D), self.d_proj,
+            self.len, self.k, sscale, ascale, _dtype_code(q), _dev(O, "O"),
+            None if idx is None else _dev(idx, "idx"),
+            _dev(self.counts, "counts") if count else None,
+            _dev(self.workspace, "workspace"), self.workspace.numel(),
+            _options(None, profile), _stream(q))
+        _check(st, "sparse_attn_decode")
+        return (O, idx) if idx is not None else O
+
+
 def sparse_attn_scores_dump(Q, K, Pq, Pk, row_begin: int, row_count: int,
                             causal: bool = False, score_scale: Optional[float] = None,
                             S: Optional[torch.Tensor] = None,
@@ -428,4 +592,6 @@ __all__ = [
     "sparse_attn_scores_topk", "sparse_attn_gather", "sparse_attn_fwd",
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
     "sparse_attn_workspace_stats", "default_score_scale", "default_softmax_scale",
+    "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
+    "sparse_attn_band_indices_per_batch", "DecodeCache",
 ]

@@ -19,7 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libsparse_attn.so")
-SOURCES = ["api.cpp", "profile.cpp", "proj.hip", "scorer.hip", "finalize.hip", "gather.hip", "dump.hip"]
+SOURCES = ["api.cpp", "profile.cpp", "proj.hip", "scorer.hip", "finalize.hip", "gather.hip", "dump.hip",
+           "variants.hip", "decode.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

@@ -58,6 +58,15 @@ int check_scorer_args(const void* Q, const void* K, const void* Pq, const void* 
   return SA_OK;
 }
 
+// As SA_TIMED, in an entry point: a launch error returns SA_ERR_HIP.
+#define SA_TIMED_STATUS(name, call)            \
+  do {                                         \
+    const int t_ = prof_begin(prof, name, s);  \
+    hipError_t e_ = (call);                    \
+    prof_end(prof, t_, s);                     \
+    if (e_ != hipSuccess) return SA_ERR_HIP;   \
+  } while (0)
+
 // Runs `call` between the optional timing events of `name` (into `prof`).
 #define SA_TIMED(name, call)                   \
   do {                                         \
@@ -70,7 +79,7 @@ int check_scorer_args(const void* Q, const void* K, const void* Pq, const void* 
 hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const void* K,
                           const void* Pq, const void* Pk, int h0, int nh, float scale,
                           int32_t* idx_chunk, int first, int* seg, sa_profile* prof,
-                          hipStream_t s) {
+                          hipStream_t s, const float* smooth_gap = nullptr) {
   SA_TIMED("init", launch_init_chunk(p, b, first, s));
   SA_TIMED("project", launch_project(p, b, Q, K, Pq, Pk, h0, nh, s));
   SA_TIMED("pack", launch_pack_keys(p, b, nh, s));
@@ -85,6 +94,8 @@ hipError_t run_topk_chunk(const Plan& p, const Bufs& b, const void* Q, const voi
   SA_TIMED("filter_retry", launch_filter(p, b, nh, scale, true, s));
   SA_TIMED("rerank_retry", launch_finalize(p, b, nh, scale, idx_chunk, true, seg, s));
   SA_TIMED("fallback", launch_fallback(p, b, nh, scale, idx_chunk, seg, s));
+  if (smooth_gap != nullptr)
+    SA_TIMED("smooth", launch_smooth(p, b, nh, scale, *smooth_gap, idx_chunk, s));
   return hipSuccess;
 }
 
@@ -360,6 +371,152 @@ int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq,
       return SA_ERR_HIP;
     }
   }
+  return SA_OK;
+}
+
+int sparse_attn_scores_topk_smoothed(const void* Q, const void* K, const void* Pq,
+                                     const void* Pk, sa_dims d, int32_t d_proj, int32_t k,
+                                     int32_t causal, float score_scale, float gap, int32_t dtype,
+                                     int32_t* idx, void* ws, size_t ws_bytes,
+                                     const sa_options* opts, void* stream) {
+  if (k < 1) return SA_ERR_SHAPE;
+  if (k >= SA_K_MAX) return SA_ERR_UNSUPPORTED;        // rows hold k + 1 entries
+  const int k1 = k + 1;
+  int st = check_scorer_args(Q, K, Pq, Pk, d, d_proj, k1, dtype, score_scale);
+  if (st != SA_OK) return st;
+  if (std::isnan(gap)) return SA_ERR_SHAPE;
+  const int filt = filter_of(opts);
+  if (filt < 0) return SA_ERR_UNSUPPORTED;
+  sa_profile* prof = profile_of(opts);
+  if (!idx || !ws) return SA_ERR_NULL;
+  if (!aligned16(idx) || !aligned16(ws)) return SA_ERR_ALIGN;
+  const int hc = chunk_heads_for(d, d_proj, k1, causal, dtype, 0, ws_bytes);
+  if (hc < 1) return SA_ERR_WORKSPACE;
+  Plan p;
+  if (!make_plan(p, d.B, d.H, d.N, d.D, d_proj, k1, causal, dtype, 0, hc, filt))
+    return SA_ERR_SHAPE;
+  const Bufs b = bufs_of(p, ws);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int h0 = 0; h0 < p.BH; h0 += p.hc) {
+    const int nh = p.BH - h0 < p.hc ? p.BH - h0 : p.hc;
+    int32_t* idx_chunk = idx + static_cast<size_t>(h0) * d.N * k1;
+    if (run_topk_chunk(p, b, Q, K, Pq, Pk, h0, nh, score_scale, idx_chunk, h0 == 0, nullptr,
+                       prof, s, &gap) != hipSuccess)
+      return SA_ERR_HIP;
+  }
+  return SA_OK;
+}
+
+// ------------------------------------------------------------- decode ---
+namespace {
+struct DecodePlan {
+  size_t off_qlo32, off_qlo16, off_qstat, off_scores, off_idx, total;
+};
+DecodePlan decode_plan(const sa_dims& d, int dp, int k) {
+  const size_t BH = static_cast<size_t>(d.B) * d.H;
+  DecodePlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.off_qlo32 = take(BH * dp * 4);
+  p.off_qlo16 = take(BH * dp * 2);
+  p.off_qstat = take(BH * 16);
+  p.off_scores = take(BH * static_cast<size_t>(d.N) * 4);
+  p.off_idx = take(BH * static_cast<size_t>(k) * 4);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t sparse_attn_decode_workspace_size(sa_dims d, int32_t d_proj, int32_t k) {
+  if (check_dims(d, k) != SA_OK || !supported_dp(d_proj)) return 0;
+  return decode_plan(d, d_proj, k).total;
+}
+
+int sparse_attn_decode_append_keys(const void* K_new, const void* Pk, sa_dims d, int32_t d_proj,
+                                   int32_t dtype, float* klow_cache, int32_t Ncap, int32_t pos,
+                                   const sa_options* opts, void* stream) {
+  if (!K_new || !Pk || !klow_cache) return SA_ERR_NULL;
+  int st = check_dims(d, 1);
+  if (st != SA_OK) return st;
+  if (!supported_D(d.D) || !supported_dp(d_proj)) return SA_ERR_UNSUPPORTED;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (Ncap < 1 || pos < 0 || pos > Ncap - d.N) return SA_ERR_SHAPE;
+  if (!aligned16(K_new) || !aligned16(Pk) || !aligned16(klow_cache)) return SA_ERR_ALIGN;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_TIMED_STATUS("decode_append", launch_project_rows(K_new, Pk, d.B * d.H, d.N, Ncap, d.D,
+                                                       d_proj, dtype, 1,
+                                                       klow_cache + static_cast<size_t>(pos) * d_proj,
+                                                       nullptr, nullptr, s));
+  return SA_OK;
+}
+
+int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
+                       const void* Pq, sa_dims d, int32_t d_proj, int32_t len, int32_t k,
+                       float score_scale, float softmax_scale, int32_t dtype, void* O,
+                       int32_t* idx_or_null, int32_t* counts_or_null, void* ws, size_t ws_bytes,
+                       const sa_options* opts, void* stream) {
+  if (!q || !Kc || !Vc || !klow_cache || !Pq || !O || !ws) return SA_ERR_NULL;
+  int st = check_dims(d, k);
+  if (st != SA_OK) return st;
+  if (!supported_D(d.D) || !supported_dp(d_proj)) return SA_ERR_UNSUPPORTED;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (len < 1 || len > d.N) return SA_ERR_SHAPE;
+  if (!(score_scale > 0.0f) || !std::isfinite(score_scale) || !std::isfinite(softmax_scale))
+    return SA_ERR_SHAPE;
+  if (!aligned16(q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(klow_cache) ||
+      !aligned16(Pq) || !aligned16(O) || !aligned16(ws))
+    return SA_ERR_ALIGN;
+  if ((idx_or_null && !aligned16(idx_or_null)) || (counts_or_null && !aligned16(counts_or_null)))
+    return SA_ERR_ALIGN;
+  const DecodePlan p = decode_plan(d, d_proj, k);
+  if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* qlo32 = reinterpret_cast<float*>(base + p.off_qlo32);
+  uint16_t* qlo16 = reinterpret_cast<uint16_t*>(base + p.off_qlo16);
+  float4* qstat = reinterpret_cast<float4*>(base + p.off_qstat);
+  float* scores = reinterpret_cast<float*>(base + p.off_scores);
+  int32_t* idx = idx_or_null ? idx_or_null : reinterpret_cast<int32_t*>(base + p.off_idx);
+  const int BH = d.B * d.H;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_TIMED_STATUS("decode_project", launch_project_rows(q, Pq, BH, 1, 1, d.D, d_proj, dtype, 0,
+                                                        qlo32, qlo16, qstat, s));
+  SA_TIMED_STATUS("decode_scores", launch_decode_scores(qlo32, 1, klow_cache, d.N, len, BH,
+                                                        d_proj, score_scale, scores, s));
+  SA_TIMED_STATUS("decode_select", launch_decode_select(scores, len, BH, k, idx, counts_or_null,
+                                                        d.N, s));
+  SA_TIMED_STATUS("decode_gather", launch_gather_rows(q, Kc, Vc, idx, k, BH, 1, d.N, d.D,
+                                                      softmax_scale, dtype, O, s));
+  return SA_OK;
+}
+
+int sparse_attn_dilated_indices(sa_dims d, int32_t window, int32_t dilation, int32_t* idx,
+                                int32_t k, const sa_options* opts, void* stream) {
+  if (!idx) return SA_ERR_NULL;
+  int st = check_dims(d, k);
+  if (st != SA_OK) return st;
+  if (window < 0 || dilation < 1) return SA_ERR_SHAPE;
+  if (!aligned16(idx)) return SA_ERR_ALIGN;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_TIMED_STATUS("dilated", launch_dilated(d.B * d.H, d.N, window, dilation, idx, k, s));
+  return SA_OK;
+}
+
+int sparse_attn_band_indices_per_batch(sa_dims d, const int32_t* radii, int32_t* idx,
+                                       int32_t k, const sa_options* opts, void* stream) {
+  if (!idx || !radii) return SA_ERR_NULL;
+  int st = check_dims(d, k);
+  if (st != SA_OK) return st;
+  if (!aligned16(idx)) return SA_ERR_ALIGN;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  SA_TIMED_STATUS("band_batch", launch_band_batch(d.B, d.H, d.N, radii, idx, k, s));
   return SA_OK;
 }
 

@@ -256,7 +256,9 @@ __device__ __forceinline__ void stage_entries(const int32_t* __restrict__ row, i
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void gather_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int32_t* __restrict__ idx, int k, int N, float scale, T* __restrict__ O) {
+    const int32_t* __restrict__ idx, int k, int Nq, int Nk, float scale, T* __restrict__ O) {
+  // Nq query rows (and idx, O rows) and Nk key rows per head: equal in the
+  // forward, one query against a key cache when decoding
   constexpr int EPL = Vec<T>::kElems;
   constexpr int LPR = D / EPL;
   extern __shared__ float slog_all[];
@@ -266,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
   int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
   const int h = blockIdx.y;
   const int q = blockIdx.x * kWaves + w;
-  if (q >= N) return;
-  const size_t hN = static_cast<size_t>(h) * N;
-  const T* Kh = K + hN * D;
-  const T* Vh = V + hN * D;
+  if (q >= Nq) return;
+  const size_t hN = static_cast<size_t>(h) * Nq;
+  const T* Kh = K + static_cast<size_t>(h) * Nk * D;
+  const T* Vh = V + static_cast<size_t>(h) * Nk * D;
+  const int N = Nk;
   stage_entries(idx + (hN + q) * k, 0, k, sidx);
   const int32_t* row = sidx;
   int bad = 0;
@@ -613,7 +616,7 @@ __global__ void band_kernel(long long total, int N, int w_left, int w_right,
 
 template <typename T, int D>
 hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
-                    int nheads, int N, float scale, void* O, hipStream_t s) {
+                    int nheads, int N, int Nk, float scale, void* O, hipStream_t s) {
   const size_t lds = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
   static std::atomic<int> lds_set[kMaxDevices];
   const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gather_kernel<T, D>),
@@ -623,7 +626,7 @@ hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* 
   const dim3 grid((N + kWaves - 1) / kWaves, nheads);
   hipLaunchKernelGGL((gather_kernel<T, D>), grid, dim3(kThreads), lds, s,
                      static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
-                     idx, k, N, scale, static_cast<T*>(O));
+                     idx, k, N, Nk, scale, static_cast<T*>(O));
   return hipGetLastError();
 }
 
@@ -632,12 +635,18 @@ hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* 
 hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
                          int nheads, int N, int D, float softmax_scale, int dtype, void* O,
                          hipStream_t s) {
+  return launch_gather_rows(Q, K, V, idx, k, nheads, N, N, D, softmax_scale, dtype, O, s);
+}
+
+hipError_t launch_gather_rows(const void* Q, const void* K, const void* V, const int32_t* idx,
+                              int k, int nheads, int Nq, int Nk, int D, float softmax_scale,
+                              int dtype, void* O, hipStream_t s) {
   if (dtype == 0) {
-    if (D == 64) return gather_t<float, 64>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
-    if (D == 128) return gather_t<float, 128>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
+    if (D == 64) return gather_t<float, 64>(Q, K, V, idx, k, nheads, Nq, Nk, softmax_scale, O, s);
+    if (D == 128) return gather_t<float, 128>(Q, K, V, idx, k, nheads, Nq, Nk, softmax_scale, O, s);
   } else {
-    if (D == 64) return gather_t<bf16_t, 64>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
-    if (D == 128) return gather_t<bf16_t, 128>(Q, K, V, idx, k, nheads, N, softmax_scale, O, s);
+    if (D == 64) return gather_t<bf16_t, 64>(Q, K, V, idx, k, nheads, Nq, Nk, softmax_scale, O, s);
+    if (D == 128) return gather_t<bf16_t, 128>(Q, K, V, idx, k, nheads, Nq, Nk, softmax_scale, O, s);
   }
   return hipErrorInvalidValue;
 }

@@ -30,7 +30,10 @@ template <typename T, int D, int DP, typename F>
 __global__ __launch_bounds__(kThreads) void project_kernel(
     const T* __restrict__ X, const T* __restrict__ P, int N, int Npad, int is_key,
     float* __restrict__ lo32, uint16_t* __restrict__ lo16, float4* __restrict__ qstat,
-    uint32_t* __restrict__ kstat) {
+    uint32_t* __restrict__ kstat, int pad_rows) {
+  // pad_rows: rows N .. (block end) are written as zeros (the selection's
+  // buffers hold Npad rows); otherwise only rows < N are written (a cache
+  // being appended to).  kstat may be null for keys.
   constexpr int kXFloats = kRows * (D + 1);
   constexpr int kLoFloats = 2 * kRows * (DP + 1);
   // bf16 rows: 32x32 output tiles on the bf16 MFMA (the products are exact in
@@ -98,7 +101,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
         const int rr = 32 * rt + 8 * (r >> 2) + 4 * (l >> 5) + (r & 3);
         const int cc = 32 * ct + (l & 31);
         const float v = (row0 + rr < N) ? acc[r] : 0.0f;
-        lo32[(base + row0 + rr) * DP + cc] = v;
+        if (pad_rows || row0 + rr < N) lo32[(base + row0 + rr) * DP + cc] = v;
         sLo[rr * (DP + 1) + cc] = v;
       }
     }
@@ -124,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
       const int r = g + i * kGroups;
       const int row = row0 + r;
       const float v = (row < N) ? acc[i] : 0.0f;
-      lo32[(base + row) * DP + c] = v;
+      if (pad_rows || row < N) lo32[(base + row) * DP + c] = v;
       sLo[r * (DP + 1) + c] = v;
     }
   }
@@ -142,7 +145,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
   }
   __syncthreads();
   if (is_key) {
-    if (tid < 2) {
+    if (tid < 2 && kstat != nullptr) {
       float m = 0.0f;
       for (int r = 0; r < kRows; ++r) m = fmaxf(m, sMax[tid][r]);
       // non-negative floats order like their bit patterns
@@ -158,11 +161,11 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
     const int e = sE[r];
     const float v = sLo[r * (DP + 1) + c];
     const uint16_t u = F::round(__builtin_ldexpf(v, e));
-    lo16[(base + row) * DP + c] = u;
+    if (pad_rows || row < N) lo16[(base + row) * DP + c] = u;
     sRes[r * (DP + 1) + c] = v - __builtin_ldexpf(F::back(u), -e);
   }
   __syncthreads();
-  if (tid < kRows) {
+  if (tid < kRows && (pad_rows || row0 + tid < N)) {
     float r2 = 0.0f;
     for (int cc = 0; cc < DP; ++cc) {
       const float b = sRes[tid * (DP + 1) + cc];
@@ -246,12 +249,12 @@ hipError_t project_t(const Plan& p, const Bufs& b, const void* Q, const void* K,
   const T* Kh = static_cast<const T*>(K) + static_cast<size_t>(h0) * p.N * D;
   hipLaunchKernelGGL((project_kernel<T, D, DP, F>), grid, dim3(kThreads), 0, s, Qh,
                      static_cast<const T*>(Pq), p.N, p.Npad, 0, b.qlo32, b.qlo16, b.qstat,
-                     b.kstat);
+                     b.kstat, 1);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((project_kernel<T, D, DP, F>), grid, dim3(kThreads), 0, s, Kh,
                      static_cast<const T*>(Pk), p.N, p.Npad, 1, b.klo32,
-                     static_cast<uint16_t*>(nullptr), static_cast<float4*>(nullptr), b.kstat);
+                     static_cast<uint16_t*>(nullptr), static_cast<float4*>(nullptr), b.kstat, 1);
   return hipGetLastError();
 }
 
@@ -293,7 +296,43 @@ hipError_t pack_f(const Plan& p, const Bufs& b, int nh, hipStream_t s) {
   return hipErrorInvalidValue;
 }
 
+template <typename T, int D, int DP>
+hipError_t project_rows_t(const void* X, const void* P, int nh, int rows, int out_stride,
+                          int is_key, float* lo32, uint16_t* lo16, float4* qstat,
+                          hipStream_t s) {
+  const dim3 grid((rows + kRows - 1) / kRows, nh, 1);
+  hipLaunchKernelGGL((project_kernel<T, D, DP, FiltF16>), grid, dim3(kThreads), 0, s,
+                     static_cast<const T*>(X), static_cast<const T*>(P), rows, out_stride, is_key,
+                     lo32, lo16, qstat, static_cast<uint32_t*>(nullptr), 0);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t project_rows_d(const void* X, const void* P, int nh, int rows, int out_stride, int dp,
+                          int is_key, float* lo32, uint16_t* lo16, float4* qstat, hipStream_t s) {
+  switch (dp) {
+    case 16: return project_rows_t<T, D, 16>(X, P, nh, rows, out_stride, is_key, lo32, lo16, qstat, s);
+    case 32: return project_rows_t<T, D, 32>(X, P, nh, rows, out_stride, is_key, lo32, lo16, qstat, s);
+    case 64: return project_rows_t<T, D, 64>(X, P, nh, rows, out_stride, is_key, lo32, lo16, qstat, s);
+    case 128: return project_rows_t<T, D, 128>(X, P, nh, rows, out_stride, is_key, lo32, lo16, qstat, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_project_rows(const void* X, const void* P, int nh, int rows, int out_stride,
+                               int D, int dp, int dtype, int is_key, float* lo32, uint16_t* lo16,
+                               float4* qstat, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 64) return project_rows_d<float, 64>(X, P, nh, rows, out_stride, dp, is_key, lo32, lo16, qstat, s);
+    if (D == 128) return project_rows_d<float, 128>(X, P, nh, rows, out_stride, dp, is_key, lo32, lo16, qstat, s);
+  } else {
+    if (D == 64) return project_rows_d<bf16_t, 64>(X, P, nh, rows, out_stride, dp, is_key, lo32, lo16, qstat, s);
+    if (D == 128) return project_rows_d<bf16_t, 128>(X, P, nh, rows, out_stride, dp, is_key, lo32, lo16, qstat, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_init_chunk(const Plan& p, const Bufs& b, int first_chunk, hipStream_t s) {
   hipLaunchKernelGGL(init_chunk_kernel, dim3(1), dim3(256), 0, s, b.hdr, b.kstat, b.rcount, p.hc,

@@ -170,6 +170,27 @@ hipError_t launch_dump(const Plan& p, const Bufs& b, int nh, float score_scale,
 hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx,
                          int k, int nheads, int N, int D, float softmax_scale, int dtype,
                          void* O, hipStream_t s);
+// Gather with Nq query rows and Nk key rows per head (Q, idx, O rows of head
+// h at h*Nq; K, V rows at h*Nk).
+hipError_t launch_gather_rows(const void* Q, const void* K, const void* V, const int32_t* idx,
+                              int k, int nheads, int Nq, int Nk, int D, float softmax_scale,
+                              int dtype, void* O, hipStream_t s);
+// Projection of `rows` rows of each of nh heads (X rows of head h at
+// h*rows), written at row h*out_stride of lo32 (and lo16 / qstat for
+// queries); nothing beyond `rows` is written.
+hipError_t launch_project_rows(const void* X, const void* P, int nh, int rows, int out_stride,
+                               int D, int dp, int dtype, int is_key, float* lo32, uint16_t* lo16,
+                               float4* qstat, hipStream_t s);
+// Decode (decode.hip): exact scores of one query per head against the first
+// `len` rows of a k_low cache (head stride Ncap rows), then the top-k of
+// those scores per head, ascending, -1 padded; counts (optional) gains one
+// per selected key.
+hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klow, int Ncap,
+                                int len, int nh, int dp, float scale, float* scores,
+                                hipStream_t s);
+hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
+                                int32_t* counts, int Ncap, hipStream_t s);
+
 // Split gather of one head whose idx rows are ascending (the fused forward's).
 // seg[q][r] (r = 0..kGatherRanges) is the first position of row q whose key
 // is >= gather_ranges(N, causal).b[r]; the re-rank and fallback kernels write it
@@ -179,6 +200,14 @@ hipError_t launch_gather_split(const void* Q, const void* K, const void* V, cons
                                float* part, void* O, sa_profile* prof, hipStream_t s);
 hipError_t launch_band(int nheads, int N, int w_left, int w_right, int32_t* idx, int k,
                        hipStream_t s);
+// Index variants (variants.hip).
+hipError_t launch_dilated(int nheads, int N, int window, int dilation, int32_t* idx, int k,
+                          hipStream_t s);
+hipError_t launch_band_batch(int B, int H, int N, const int32_t* radii, int32_t* idx, int k,
+                             hipStream_t s);
+// Boundary smoothing of a chunk's top-(k+1) rows (p.k is k+1), in place.
+hipError_t launch_smooth(const Plan& p, const Bufs& b, int nh, float score_scale, float gap,
+                         int32_t* idx_chunk, hipStream_t s);
 
 // Optional per-launch timing into a caller-owned record (NULL: none).
 // prof_begin records the start event and returns the slot that prof_end

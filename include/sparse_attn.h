@@ -171,6 +171,88 @@ int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t
                              int32_t k, const sa_options* opts, void* stream);
 
 /*
+ * Decode: one new query per (b, h) against the keys cached so far (page
+ * "mhpq.cn/news/1098205", §3.4: at inference the selection runs for each
+ * generated token over the KV cache, and how often a key is selected can
+ * decide which cache entries are kept; page
+ * "Attention机制优化：原理、挑战与工程实践", §4.3: a preallocated cache
+ * updated in place at each step).
+ *
+ * The caller owns the caches: K and V caches [B,H,Ncap,D] (dtype), and a
+ * k_low cache [B,H,Ncap,d_proj] fp32 holding each cached key's projection
+ * K·Pk.  sparse_attn_decode_append_keys writes the projections of T new keys
+ * K_new [B,H,T,D] (d.N = T) at cache rows pos .. pos+T-1 (0 <= pos,
+ * pos + T <= Ncap), with the arithmetic of the prefill's projection, so the
+ * cached values equal the prefill's bit for bit.
+ *
+ * sparse_attn_decode (d.N = Ncap): q [B,H,1,D]; the query of each (b, h)
+ * attends to cache rows 0 .. len-1 (1 <= len <= Ncap; append the query's
+ * own key first for a causal step).  The selection is the top-k of the
+ * exact fp32 scores score_scale · q_low·k_low_j (the prefill's arithmetic:
+ * the index row equals the causal prefill's row len-1 over the same keys),
+ * ties to the lower key index, ascending, -1 padded when len < k.
+ *   O (out): [B,H,1,D]; idx_or_null (out, optional): [B,H,k] int32;
+ *   counts_or_null (in/out, optional): [B,H,Ncap] int32, each selected key's
+ *   count is incremented (selection frequency for cache eviction).
+ *   ws: sparse_attn_decode_workspace_size(d, d_proj, k) bytes.
+ */
+size_t sparse_attn_decode_workspace_size(sa_dims d, int32_t d_proj, int32_t k);
+int sparse_attn_decode_append_keys(const void* K_new, const void* Pk, sa_dims d, int32_t d_proj,
+                                   int32_t dtype, float* klow_cache, int32_t Ncap, int32_t pos,
+                                   const sa_options* opts, void* stream);
+int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
+                       const void* Pq, sa_dims d, int32_t d_proj, int32_t len, int32_t k,
+                       float score_scale, float softmax_scale, int32_t dtype, void* O,
+                       int32_t* idx_or_null, int32_t* counts_or_null, void* ws, size_t ws_bytes,
+                       const sa_options* opts, void* stream);
+
+/*
+ * Index variants feeding sparse_attn_gather.
+ *
+ * Boundary smoothing of the top-k (page "mhpq.cn/news/1098205", §4.2: when
+ * the gap between the k-th and the (k+1)-th scores is below a threshold,
+ * both keys are kept, so the number of kept keys varies a little from row
+ * to row).
+ *   Arguments as for sparse_attn_scores_topk, plus gap; idx (out) is
+ *   [B,H,N,k+1] int32 and the workspace must be sized for k + 1
+ *   (sparse_attn_workspace_size with k + 1).  Row i holds the keys of the
+ *   top-k of the exact fp32 scores (those sparse_attn_scores_dump reports;
+ *   ties to the lower key index), plus the (k+1)-th key when
+ *   s_k - s_(k+1) < gap, the difference taken exactly (in double precision);
+ *   ascending key order, -1 padding to k + 1 entries.  Rows with at most k
+ *   valid keys keep them all.  1 <= k < SA_K_MAX; a NaN gap is SA_ERR_SHAPE.
+ */
+int sparse_attn_scores_topk_smoothed(const void* Q, const void* K, const void* Pq,
+                                     const void* Pk, sa_dims d, int32_t d_proj, int32_t k,
+                                     int32_t causal, float score_scale, float gap, int32_t dtype,
+                                     int32_t* idx, void* ws, size_t ws_bytes,
+                                     const sa_options* opts, void* stream);
+
+/*
+ * Dilated sliding window wrapped around the sequence (page
+ * "Attention机制优化：原理、挑战与工程实践", §3.3: offsets t·dilation,
+ * t < window, taken modulo the sequence length).
+ *   idx (out): [B,H,N,k] int32; entry t of row i is (i + t·dilation) mod N
+ *   for t < min(window, k), then -1.  Keys repeat when window·dilation > N
+ *   and then count as often as they appear in the attention.  d.D is
+ *   ignored.  window >= 0 and dilation >= 1, else SA_ERR_SHAPE.
+ */
+int sparse_attn_dilated_indices(sa_dims d, int32_t window, int32_t dilation, int32_t* idx,
+                                int32_t k, const sa_options* opts, void* stream);
+
+/*
+ * Band with one radius per batch sample (page "nxmr.cn/news/163144", §6
+ * adaptive attention: the window size is a per-sample value computed by the
+ * model, so it is read from device memory).
+ *   radii: DEVICE pointer to B int32 radii (a negative radius counts as 0);
+ *   idx (out): [B,H,N,k] int32, row i of sample b holds keys
+ *   max(0, i-w_b) .. min(N-1, i+w_b) ascending, truncated to k entries,
+ *   then -1 padding.  d.D is ignored.
+ */
+int sparse_attn_band_indices_per_batch(sa_dims d, const int32_t* radii, int32_t* idx,
+                                       int32_t k, const sa_options* opts, void* stream);
+
+/*
  * The scorer's output for chosen query rows: the fp32 scores the selection
  * uses (page "mhpq.cn/news/1098205" §2.2, LightweightScorer: the scaled dot
  * product d_proj^-1/2 · q_low·k_lowᵀ), written out so that the top-k can be

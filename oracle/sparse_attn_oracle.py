@@ -36,6 +36,9 @@ float64 with NumPy, one step per statement, following the pages:
        t = 0 .. window-1, repeats included;
      - a window radius per batch sample (page "nxmr.cn/news/163144", §6,
        adaptive attention: each sample gets its own window size w).
+  7. Decode (page "mhpq.cn/news/1098205", §3.4, inference over the KV
+     cache): one new query against the cached keys; with the cache holding
+     keys 0..n-1 this is the causal forward's row n-1.
   5. Backward (same page, §2.3, top-k selection and gradient flow): the
      forward keeps the hard top-k; in the backward the selected positions'
      gradients flow normally and unselected positions get zero; the scorer
@@ -218,6 +221,21 @@ def band_indices(N: int, w_left: int, w_right: int, width: int) -> np.ndarray:
         keys = np.arange(lo, hi + 1)[:width]
         out[i, :keys.size] = keys
     return out
+
+
+# ------------------------------------------------------------ 7. decode ---
+
+def decode_step(q, Kc, Vc, Pq, Pk, k: int, length: int, score_scale: float,
+                softmax_scale: float):
+    """One decode step of one head (page "mhpq.cn/news/1098205", §3.4): the
+    new query q [D] scores the cached keys Kc[0:length] with the scorer,
+    keeps its top-k (ties to the lower index, ascending, -1 padded) and
+    attends over them.  Returns (idx [k], o [D])."""
+    qa = f64(q)
+    Ka, Va = f64(Kc)[:length], f64(Vc)[:length]
+    s = score_rows(project(qa[None, :], f64(Pq)), project(Ka, f64(Pk)), score_scale)[0]
+    idx = topk_row(s, np.ones(length, dtype=bool), k)
+    return idx, attend_row(qa, Ka, Va, idx.astype(np.int64), softmax_scale)
 
 
 # -------------------------------------------------- 6. index variants ---

@@ -204,3 +204,20 @@ def test_binding_refuses_cpu_tensors():
         sa.sparse_attn_scores_topk(q, q, p, p, 4)
     with pytest.raises((ValueError, RuntimeError)):
         sa.sparse_attn_gather(q, q, q, torch.zeros(1, 1, 64, 4, dtype=torch.int32))
+
+
+def test_index_variant_validation(lib):
+    d = D(2, 3, 100, 64)
+    assert lib.sparse_attn_dilated_indices(d, 4, 2, None, 4, None, None) == -1
+    assert lib.sparse_attn_dilated_indices(d, -1, 2, A, 4, None, None) == -2
+    assert lib.sparse_attn_dilated_indices(d, 4, 0, A, 4, None, None) == -2
+    assert lib.sparse_attn_dilated_indices(d, 4, 2, A + 4, 4, None, None) == -4
+    assert lib.sparse_attn_band_indices_per_batch(d, None, A, 5, None, None) == -1
+    assert lib.sparse_attn_band_indices_per_batch(d, A, A, 0, None, None) == -2
+    sm = lib.sparse_attn_scores_topk_smoothed
+    dd = D(1, 1, 1024, 64)
+    assert sm(A, A, A, A, dd, 16, 0, 0, 0.25, 0.1, 0, A, A, 1 << 30, None, None) == -2
+    assert sm(A, A, A, A, dd, 16, 2048, 0, 0.25, 0.1, 0, A, A, 1 << 30, None, None) == -3
+    assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, float("nan"), 0, A, A, 1 << 30, None, None) == -2
+    assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, 0.1, 0, None, A, 1 << 30, None, None) == -1
+    assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, 0.1, 0, A, A, 64, None, None) == -5

@@ -353,10 +353,10 @@ def _tied_keys(w, seed, copies, all_same_head=None):
     for b in range(w.B):
         for h in range(w.H):
             if h == all_same_head:
-                K[b, h] = K[b, h, 0]
+                K[b, h] = K[b, h, 0].clone()
             else:
                 pos = rng.choice(w.N, copies, replace=False)
-                K[b, h, torch.as_tensor(pos)] = K[b, h, int(pos[0])]
+                K[b, h, torch.as_tensor(pos)] = K[b, h, int(pos[0])].clone()
     x["K"] = K.contiguous()
     return x
 

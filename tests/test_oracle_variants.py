@@ -114,3 +114,25 @@ def test_per_sample_band_equals_dense_attention_per_sample():
         for i in range(N):
             row = [int(x) for x in idx[b, 0, i] if x >= 0]
             assert row == list(range(max(0, i - w), min(N - 1, i + w) + 1))
+
+
+@pytest.mark.parametrize("length,k", [(40, 8), (5, 8), (1, 3), (40, 40)])
+def test_decode_step_is_last_causal_row(length, k):
+    """A decode step over cached keys 0..n-1 is row n-1 of the causal
+    forward (page "mhpq.cn/news/1098205", §3.4 inference with a KV cache)."""
+    rng = np.random.default_rng(length + k)
+    B, H, N, D, dp = 1, 1, 40, 6, 4
+    Q, K, V = (rng.standard_normal((B, H, N, D)) for _ in range(3))
+    Pq, Pk = (rng.standard_normal((D, dp)) for _ in range(2))
+    idx_f, out_f = O.sparse_attn_fwd(Q[:, :, :length], K[:, :, :length], V[:, :, :length],
+                                     Pq, Pk, k, True, 0.5, 0.3)
+    idx_d, o_d = O.decode_step(Q[0, 0, length - 1], K[0, 0], V[0, 0], Pq, Pk, k, length, 0.5,
+                               0.3)
+    np.testing.assert_array_equal(idx_d, idx_f[0, 0, length - 1])
+    np.testing.assert_allclose(o_d, out_f[0, 0, length - 1], rtol=1e-13, atol=1e-13)
+    # by enumeration on the same scores (short caches only)
+    for n in (min(length, 10),):
+        S = O.scores(Q, K, Pq, Pk, 0.5, 0, 0, [n - 1])[0, :n]
+        idx_n, _ = O.decode_step(Q[0, 0, n - 1], K[0, 0], V[0, 0], Pq, Pk, min(k, 4), n, 0.5, 0.3)
+        want = O.brute_force_topk(list(S), [True] * n, min(k, 4))
+        assert [int(x) for x in idx_n if x >= 0] == want
