@@ -1,0 +1,173 @@
+// Decode: one new query per (b, h) against the keys cached so far (page
+// "mhpq.cn/news/1098205", §3.4: at inference the selection runs per
+// generated token over the KV cache, and the keys' selection counts can
+// decide which cache entries to keep; page "Attention机制优化：原理、挑战与
+// 工程实践", §4.3: a preallocated cache updated in place).
+//
+// The scorer's key projections live in a caller-owned k_low cache, filled by
+// the same projection kernel as the prefill (so a key's k_low is bit for bit
+// the prefill's).  A step then
+//   1. projects the query (same kernel again),
+//   2. scores every cached key exactly (exact_score's arithmetic: the lanes
+//      of a group hold four coordinates each and add their partials in the
+//      fixed butterfly order), a memory-bound pass over the k_low cache,
+//   3. selects the top-k of those scores per head (radix select on the
+//      order keys, ties to the lower key index, written ascending),
+//   4. runs the gather attention over the selected K and V cache rows.
+// With the cache holding keys 0..len-1 of a sequence, the step's index row
+// is exactly the causal prefill's row len-1.
+#include "sa_internal.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kScoreUnroll = 8;   // key loads in flight per lane
+
+template <int DP>
+__global__ __launch_bounds__(kThreads) void decode_score_kernel(
+    const float* __restrict__ qlo, int q_stride, const float* __restrict__ klow, int Ncap,
+    int len, float scale, float* __restrict__ scores) {
+  constexpr int G = DP / 4;           // lanes per key, four coordinates each
+  constexpr int KPI = kWave / G;      // keys per pass of a wave
+  const int h = blockIdx.y;
+  const int w = threadIdx.x / kWave;
+  const int l = lane_id();
+  const int g = l % G, grp = l / G;
+  const float4 qv = reinterpret_cast<const float4*>(qlo + static_cast<size_t>(h) * q_stride * DP)[g];
+  const float* kh = klow + static_cast<size_t>(h) * Ncap * DP;
+  float* out = scores + static_cast<size_t>(h) * Ncap;
+  const int per_block = KPI * kWaves * kScoreUnroll;
+  const int j0 = blockIdx.x * per_block + w * KPI * kScoreUnroll;
+  float4 kv[kScoreUnroll];
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    const int j = j0 + u * KPI + grp;
+    kv[u] = j < len ? reinterpret_cast<const float4*>(kh + static_cast<size_t>(j) * DP)[g]
+                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+#pragma unroll
+  for (int u = 0; u < kScoreUnroll; ++u) {
+    const float p = group_sum<G>(group_partial<DP>(qv, kv[u]));
+    const int j = j0 + u * KPI + grp;
+    if (g == 0 && j < len) out[j] = p * scale;
+  }
+}
+
+__device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const int incl = wave_incl_scan(v);
+  if (l == kWave - 1) tmp[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+  for (int i = 0; i < kWaves; ++i) {
+    const int t = tmp[i];
+    if (i < w) off += t;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return off + incl - v;
+}
+
+// One workgroup per head: the k_i-th largest order key by a radix select
+// (four 8-bit digits), then the keys above it and the lowest-index ties, in
+// ascending key order.
+__global__ __launch_bounds__(kThreads) void decode_select_kernel(
+    const float* __restrict__ scores, int len, int k, int32_t* __restrict__ idx,
+    int32_t* __restrict__ counts, int Ncap) {
+  __shared__ int hist[256];
+  __shared__ int tmp[kWaves];
+  __shared__ int s_digit, s_above;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.x;
+  const float* row = scores + static_cast<size_t>(h) * Ncap;
+  const int k_i = min(k, len);
+  uint32_t prefix = 0, pmask = 0;
+  int K = k_i;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < len; j += kThreads) {
+      const uint32_t key = order_key(row[j]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+    }
+    __syncthreads();
+    const int cval = hist[255 - tid];   // thread t owns bin 255 - t
+    int total;
+    const int excl = block_excl_scan(cval, tmp, total);
+    if (excl < K && excl + cval >= K) {
+      s_digit = 255 - tid;
+      s_above = excl;
+    }
+    __syncthreads();
+    K -= s_above;
+    prefix |= static_cast<uint32_t>(s_digit) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  // each thread owns a contiguous range of keys: two block scans give every
+  // thread its first output position
+  const int L = (len + kThreads - 1) / kThreads;
+  const int j0 = min(len, tid * L), j1 = min(len, j0 + L);
+  int gt = 0, eq = 0;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t key = order_key(row[j]);
+    gt += key > prefix ? 1 : 0;
+    eq += key == prefix ? 1 : 0;
+  }
+  int gt_total, eq_total;
+  const int gt_before = block_excl_scan(gt, tmp, gt_total);
+  const int eq_before = block_excl_scan(eq, tmp, eq_total);
+  const int ties_needed = k_i - gt_total;
+  int32_t* out = idx + static_cast<size_t>(h) * k;
+  int32_t* cnt = counts != nullptr ? counts + static_cast<size_t>(h) * Ncap : nullptr;
+  int pos = gt_before + min(eq_before, ties_needed);
+  int eq_seen = eq_before;
+  for (int j = j0; j < j1; ++j) {
+    const uint32_t key = order_key(row[j]);
+    const bool tie = key == prefix;
+    if (key > prefix || (tie && eq_seen < ties_needed)) {
+      out[pos++] = j;
+      if (cnt != nullptr) atomicAdd(&cnt[j], 1);
+    }
+    eq_seen += tie ? 1 : 0;
+  }
+  for (int t = k_i + tid; t < k; t += kThreads) out[t] = -1;
+}
+
+template <int DP>
+hipError_t scores_t(const float* qlo, int q_stride, const float* klow, int Ncap, int len, int nh,
+                    float scale, float* scores, hipStream_t s) {
+  constexpr int KPI = kWave / (DP / 4);
+  const int per_block = KPI * kWaves * kScoreUnroll;
+  const dim3 grid((len + per_block - 1) / per_block, nh);
+  hipLaunchKernelGGL((decode_score_kernel<DP>), grid, dim3(kThreads), 0, s, qlo, q_stride, klow,
+                     Ncap, len, scale, scores);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klow, int Ncap,
+                                int len, int nh, int dp, float scale, float* scores,
+                                hipStream_t s) {
+  switch (dp) {
+    case 16: return scores_t<16>(qlo, q_stride, klow, Ncap, len, nh, scale, scores, s);
+    case 32: return scores_t<32>(qlo, q_stride, klow, Ncap, len, nh, scale, scores, s);
+    case 64: return scores_t<64>(qlo, q_stride, klow, Ncap, len, nh, scale, scores, s);
+    case 128: return scores_t<128>(qlo, q_stride, klow, Ncap, len, nh, scale, scores, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
+                                int32_t* counts, int Ncap, hipStream_t s) {
+  hipLaunchKernelGGL(decode_select_kernel, dim3(nh), dim3(kThreads), 0, s, scores, len, k, idx,
+                     counts, Ncap);
+  return hipGetLastError();
+}
+
+}  // namespace sa
