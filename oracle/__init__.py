@@ -9,6 +9,6 @@ from .sparse_attn_oracle import (  # noqa: F401
     sparse_attn_fwd, band_indices, dense_attention, local_mask,
     brute_force_attention, attend_row_backward, sparse_attn_backward,
     smoothed_topk_row, smoothed_topk_rows, dilated_indices, band_indices_per_batch,
-    decode_step,
+    decode_step, block_means, block_select_row, block_keys_row, block_topk_indices,
 )
 from .compare import row_invariants, set_overlap  # noqa: F401

@@ -36,6 +36,15 @@ float64 with NumPy, one step per statement, following the pages:
        t = 0 .. window-1, repeats included;
      - a window radius per batch sample (page "nxmr.cn/news/163144", §6,
        adaptive attention: each sample gets its own window size w).
+  8. Block-granular selection (the SSA page's _block_sparsify works on
+     blocks of the mask; page "mhpq.cn/news/1098205", §2.1 block-sparse
+     attention computes only some block pairs).  Reading taken here: keys
+     are cut into blocks of `block` consecutive rows, each block is scored
+     as a whole with its mean k_low (so its score is the mean of its keys'
+     scores), each query keeps its kb best blocks and attends to every
+     valid key in them.  Causally a query always keeps its own block (the
+     keys up to itself) and picks kb-1 more among the blocks wholly before
+     it.
   7. Decode (page "mhpq.cn/news/1098205", §3.4, inference over the KV
      cache): one new query against the cached keys; with the cache holding
      keys 0..n-1 this is the causal forward's row n-1.
@@ -236,6 +245,65 @@ def decode_step(q, Kc, Vc, Pq, Pk, k: int, length: int, score_scale: float,
     s = score_rows(project(qa[None, :], f64(Pq)), project(Ka, f64(Pk)), score_scale)[0]
     idx = topk_row(s, np.ones(length, dtype=bool), k)
     return idx, attend_row(qa, Ka, Va, idx.astype(np.int64), softmax_scale)
+
+
+# ------------------------------------------- 8. block-granular selection ---
+
+def block_means(k_low: np.ndarray, block: int) -> np.ndarray:
+    """Mean of each block of `block` consecutive rows of k_low [N, d_proj]
+    (the last block may be shorter): [ceil(N / block), d_proj]."""
+    N = k_low.shape[0]
+    nb = (N + block - 1) // block
+    return np.stack([k_low[J * block:min(N, (J + 1) * block)].mean(axis=0) for J in range(nb)])
+
+
+def block_select_row(sb: np.ndarray, i: int, block: int, kb: int, causal: bool) -> np.ndarray:
+    """Blocks kept by query i from its block scores sb [n_blocks]: the kb
+    best by (score descending, block ascending); causally its own block plus
+    the kb-1 best among the blocks that end before it.  Ascending."""
+    nb = sb.shape[0]
+    if causal:
+        own = i // block
+        cand = np.arange(own)
+        take = min(kb - 1, cand.size)
+        order = cand[np.lexsort((cand, -sb[cand]))]
+        return np.sort(np.concatenate([order[:take], [own]])).astype(np.int64)
+    cand = np.arange(nb)
+    order = cand[np.lexsort((cand, -sb[cand]))]
+    return np.sort(order[:min(kb, nb)]).astype(np.int64)
+
+
+def block_keys_row(blocks: np.ndarray, i: int, N: int, block: int, width: int,
+                   causal: bool) -> np.ndarray:
+    """The keys of the kept blocks (causally only j <= i), ascending, -1
+    padded to `width` entries."""
+    keys = [j for J in blocks for j in range(J * block, min(N, (J + 1) * block))
+            if not causal or j <= i]
+    out = np.full(width, -1, dtype=np.int32)
+    out[:len(keys)] = keys
+    return out
+
+
+def block_topk_indices(Q, K, Pq, Pk, block: int, kb: int, causal: bool, score_scale: float,
+                       rows: Optional[Sequence[int]] = None, block_scores=None) -> np.ndarray:
+    """idx [B, H, R, kb*block] of block-granular selection.  block_scores,
+    when given, is a callable (b, h) -> [R, n_blocks] used instead of the
+    fp64 block scores (to recompute the selection from other values)."""
+    B, H, N = Q.shape[0], Q.shape[1], Q.shape[2]
+    rows = list(range(N)) if rows is None else [int(r) for r in rows]
+    out = np.empty((B, H, len(rows), kb * block), dtype=np.int32)
+    for b in range(B):
+        for h in range(H):
+            if block_scores is None:
+                q_low = project(f64(Q[b, h])[np.asarray(rows)], f64(Pq))
+                kbar = block_means(project(f64(K[b, h]), f64(Pk)), block)
+                SB = score_rows(q_low, kbar, score_scale)
+            else:
+                SB = block_scores(b, h)
+            for r, i in enumerate(rows):
+                kept = block_select_row(SB[r], i, block, kb, causal)
+                out[b, h, r] = block_keys_row(kept, i, N, block, kb * block, causal)
+    return out
 
 
 # -------------------------------------------------- 6. index variants ---

@@ -136,3 +136,62 @@ def test_decode_step_is_last_causal_row(length, k):
         idx_n, _ = O.decode_step(Q[0, 0, n - 1], K[0, 0], V[0, 0], Pq, Pk, min(k, 4), n, 0.5, 0.3)
         want = O.brute_force_topk(list(S), [True] * n, min(k, 4))
         assert [int(x) for x in idx_n if x >= 0] == want
+
+
+# ------------------------------------------------ block-granular selection ---
+
+def _blk_inputs(N, D, dp, seed):
+    rng = np.random.default_rng(seed)
+    Q, K, V = (rng.standard_normal((1, 2, N, D)) for _ in range(3))
+    Pq, Pk = (rng.standard_normal((D, dp)) for _ in range(2))
+    return Q, K, V, Pq, Pk
+
+
+def test_block_score_is_mean_of_fine_scores():
+    """Scoring a block by its mean key gives the mean of its keys' scores
+    (the score is linear in the key), ragged last block included."""
+    Q, K, V, Pq, Pk = _blk_inputs(37, 6, 4, 0)
+    S = O.scores(Q, K, Pq, Pk, 0.5, 0, 1)
+    kbar = O.block_means(O.project(O.f64(K[0, 1]), O.f64(Pk)), 8)
+    SB = O.score_rows(O.project(O.f64(Q[0, 1]), O.f64(Pq)), kbar, 0.5)
+    for J in range(5):
+        np.testing.assert_allclose(SB[:, J], S[:, J * 8:min(37, J * 8 + 8)].mean(axis=1),
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_block_size_one_is_plain_top_k():
+    Q, K, V, Pq, Pk = _blk_inputs(30, 5, 3, 1)
+    np.testing.assert_array_equal(O.block_topk_indices(Q, K, Pq, Pk, 1, 7, False, 0.5),
+                                  O.topk_indices(Q, K, Pq, Pk, 7, False, 0.5))
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_all_blocks_kept_is_dense_attention(causal):
+    Q, K, V, Pq, Pk = _blk_inputs(29, 5, 3, 2)
+    idx = O.block_topk_indices(Q, K, Pq, Pk, 4, 8, causal, 0.5)     # 8 blocks of 4 >= 29
+    got = O.gather_attention(Q, K, V, idx, 0.4)
+    np.testing.assert_allclose(got, O.dense_attention(Q, K, V, 0.4, causal=causal),
+                               rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_block_selection_by_enumeration(causal):
+    """The kept blocks beat every other candidate block (ties to the lower
+    block), found by enumerating all subsets of blocks."""
+    Q, K, V, Pq, Pk = _blk_inputs(26, 5, 3, 3)
+    block, kb = 4, 3
+    kbar = O.block_means(O.project(O.f64(K[0, 0]), O.f64(Pk)), block)
+    SB = np.round(O.score_rows(O.project(O.f64(Q[0, 0]), O.f64(Pq)), kbar, 0.5), 1)  # force ties
+    idx = O.block_topk_indices(Q, K, Pq, Pk, block, kb, causal, 0.5,
+                               block_scores=lambda b, h: SB)
+    for i in range(26):
+        own = i // block
+        cands = list(range(own)) if causal else list(range(SB.shape[1]))
+        want_n = min(kb - 1, len(cands)) if causal else min(kb, len(cands))
+        want = O.brute_force_topk(list(SB[i]), [J in cands for J in range(SB.shape[1])], want_n) \
+            if want_n > 0 else []
+        if causal:
+            want = sorted(want + [own])
+        keys = [j for J in want for j in range(J * block, min(26, J * block + block))
+                if not causal or j <= i]
+        assert [int(x) for x in idx[0, 0, i] if x >= 0] == keys, i
