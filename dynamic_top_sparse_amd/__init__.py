@@ -39,7 +39,8 @@ EXPORTS = (
     "sparse_attn_profile_read", "sparse_attn_status_string",
     "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
     "sparse_attn_band_indices_per_batch", "sparse_attn_decode_workspace_size",
-    "sparse_attn_decode_append_keys", "sparse_attn_decode",
+    "sparse_attn_decode_append_keys", "sparse_attn_decode", "sparse_attn_block_workspace_size",
+    "sparse_attn_block_topk", "sparse_attn_block_scores_dump",
 )
 
 
@@ -105,6 +106,11 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                           op, vp]),
         "sparse_attn_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32,
                                               f32, i32, vp, vp, vp, vp, sz, op, vp]),
+        "sparse_attn_block_workspace_size": (sz, [sa_dims, i32, i32, i32]),
+        "sparse_attn_block_topk": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, i32, i32,
+                                                  f32, i32, vp, vp, sz, op, vp]),
+        "sparse_attn_block_scores_dump": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, f32,
+                                                         i32, i32, i32, vp, vp, sz, op, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -462,6 +468,61 @@ def sparse_attn_band_indices_per_batch(H: int, N: int, radii: torch.Tensor,
     return idx
 
 
+def _block_workspace(Q, d_proj: int, block: int, kb: int) -> torch.Tensor:
+    B, H, N, D = Q.shape
+    n = int(load_library().sparse_attn_block_workspace_size(sa_dims(B, H, N, D), d_proj, block,
+                                                            kb))
+    if n == 0:
+        raise SparseAttnError(-3, "sparse_attn_block_workspace_size")
+    return torch.empty(n, dtype=torch.uint8, device=Q.device)
+
+
+def sparse_attn_block_topk(Q, K, Pq, Pk, block: int, kb: int, causal: bool = False,
+                           score_scale: Optional[float] = None,
+                           idx: Optional[torch.Tensor] = None,
+                           workspace: Optional[torch.Tensor] = None,
+                           profile: Optional[Profile] = None) -> torch.Tensor:
+    """idx [B,H,N,kb*block]: the keys of each query's kb best key blocks."""
+    _check_qkv(Q, K)
+    d_proj = _check_proj(Pq, Pk, Q)
+    B, H, N, D = Q.shape
+    scale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
+    if idx is None:
+        idx = torch.empty((B, H, N, kb * block), dtype=torch.int32, device=Q.device)
+    _check_idx(idx, Q, kb * block)
+    if workspace is None:
+        workspace = _block_workspace(Q, d_proj, block, kb)
+    _check_workspace(workspace, Q)
+    st = load_library().sparse_attn_block_topk(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q), d_proj, block, kb,
+        int(causal), scale, _dtype_code(Q), _dev(idx, "idx"), _dev(workspace, "workspace"),
+        workspace.numel(), _options(None, profile), _stream(Q))
+    _check(st, "sparse_attn_block_topk")
+    return idx
+
+
+def sparse_attn_block_scores_dump(Q, K, Pq, Pk, block: int, row_begin: int, row_count: int,
+                                  score_scale: Optional[float] = None,
+                                  workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """S [B,H,row_count,ceil(N/block)] fp32: the block scores the block
+    selection ranks."""
+    _check_qkv(Q, K)
+    d_proj = _check_proj(Pq, Pk, Q)
+    B, H, N, D = Q.shape
+    scale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
+    NB = (N + block - 1) // block
+    S = torch.empty((B, H, row_count, NB), dtype=torch.float32, device=Q.device)
+    if workspace is None:
+        workspace = _block_workspace(Q, d_proj, block, 1)
+    _check_workspace(workspace, Q)
+    st = load_library().sparse_attn_block_scores_dump(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(Pq, "Pq"), _dev(Pk, "Pk"), _dims(Q), d_proj, block,
+        scale, _dtype_code(Q), row_begin, row_count, _dev(S, "S"), _dev(workspace, "workspace"),
+        workspace.numel(), None, _stream(Q))
+    _check(st, "sparse_attn_block_scores_dump")
+    return S
+
+
 class DecodeCache:
     """Caller-owned caches of the decode path: K and V caches [B,H,Ncap,D]
     of the model's dtype and the k_low cache [B,H,Ncap,d_proj] fp32, plus
@@ -593,5 +654,6 @@ __all__ = [
     "sparse_attn_band_indices", "sparse_attn_scores_dump", "sparse_attn_check_status",
     "sparse_attn_workspace_stats", "default_score_scale", "default_softmax_scale",
     "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
-    "sparse_attn_band_indices_per_batch", "DecodeCache",
+    "sparse_attn_band_indices_per_batch", "DecodeCache", "sparse_attn_block_topk",
+    "sparse_attn_block_scores_dump",
 ]

@@ -495,6 +495,124 @@ int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const floa
   return SA_OK;
 }
 
+// ---------------------------------------------- block-granular selection ---
+namespace {
+constexpr int kBlockKbMaxApi = 32;
+struct BlockPlan {
+  size_t off_q32, off_k32, off_kbar, off_sel, total;
+  int NB;
+};
+bool block_plan(BlockPlan& p, const sa_dims& d, int dp, int block, int kb) {
+  if (block < 1 || kb < 1 || kb > kBlockKbMaxApi) return false;
+  if (static_cast<long long>(block) * kb > SA_K_MAX) return false;
+  const size_t BH = static_cast<size_t>(d.B) * d.H, N = static_cast<size_t>(d.N);
+  p.NB = static_cast<int>((N + block - 1) / block);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.off_q32 = take(BH * N * dp * 4);
+  p.off_k32 = take(BH * N * dp * 4);
+  p.off_kbar = take(BH * static_cast<size_t>(p.NB) * dp * 4);
+  p.off_sel = take(BH * N * kb * 4);
+  p.total = off;
+  return true;
+}
+int check_block_args(const sa_dims& d, int dp, int block, int kb) {
+  int st = check_dims(d, 1);
+  if (st != SA_OK) return st;
+  if (block < 1 || kb < 1) return SA_ERR_SHAPE;
+  if (kb > kBlockKbMaxApi || static_cast<long long>(block) * kb > SA_K_MAX)
+    return SA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(d.N) * block * kb >= (1ll << 31)) return SA_ERR_SHAPE;
+  if (!supported_D(d.D) || !supported_dp(dp)) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+}  // namespace
+
+size_t sparse_attn_block_workspace_size(sa_dims d, int32_t d_proj, int32_t block, int32_t kb) {
+  if (check_block_args(d, d_proj, block, kb) != SA_OK) return 0;
+  BlockPlan p;
+  if (!block_plan(p, d, d_proj, block, kb)) return 0;
+  return p.total;
+}
+
+static int block_common(const void* Q, const void* K, const void* Pq, const void* Pk,
+                        const sa_dims& d, int d_proj, int block, int kb, int causal,
+                        float score_scale, int dtype, void* ws, size_t ws_bytes,
+                        sa_profile* prof, hipStream_t s, BlockPlan& p, float*& q32,
+                        float*& k32, float*& kbar, int32_t*& sel) {
+  if (!Q || !K || !Pq || !Pk || !ws) return SA_ERR_NULL;
+  int st = check_block_args(d, d_proj, block, kb);
+  if (st != SA_OK) return st;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (!(score_scale > 0.0f) || !std::isfinite(score_scale)) return SA_ERR_SHAPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(Pq) || !aligned16(Pk) || !aligned16(ws))
+    return SA_ERR_ALIGN;
+  if (!block_plan(p, d, d_proj, block, kb)) return SA_ERR_UNSUPPORTED;
+  if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  q32 = reinterpret_cast<float*>(base + p.off_q32);
+  k32 = reinterpret_cast<float*>(base + p.off_k32);
+  kbar = reinterpret_cast<float*>(base + p.off_kbar);
+  sel = reinterpret_cast<int32_t*>(base + p.off_sel);
+  const int BH = d.B * d.H;
+  SA_TIMED_STATUS("block_project", launch_project_rows(Q, Pq, BH, d.N, d.N, d.D, d_proj, dtype, 0,
+                                                       q32, nullptr, nullptr, s));
+  SA_TIMED_STATUS("block_project", launch_project_rows(K, Pk, BH, d.N, d.N, d.D, d_proj, dtype, 1,
+                                                       k32, nullptr, nullptr, s));
+  (void)causal;
+  return SA_OK;
+}
+
+int sparse_attn_block_topk(const void* Q, const void* K, const void* Pq, const void* Pk,
+                           sa_dims d, int32_t d_proj, int32_t block, int32_t kb, int32_t causal,
+                           float score_scale, int32_t dtype, int32_t* idx, void* ws,
+                           size_t ws_bytes, const sa_options* opts, void* stream) {
+  if (!idx) return SA_ERR_NULL;
+  if (!aligned16(idx)) return SA_ERR_ALIGN;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BlockPlan p;
+  float *q32, *k32, *kbar;
+  int32_t* sel;
+  int st = block_common(Q, K, Pq, Pk, d, d_proj, block, kb, causal, score_scale, dtype, ws,
+                        ws_bytes, prof, s, p, q32, k32, kbar, sel);
+  if (st != SA_OK) return st;
+  const int BH = d.B * d.H;
+  SA_TIMED_STATUS("block_select", launch_block_select(q32, k32, BH, d.N, d_proj, block, kb,
+                                                      causal ? 1 : 0, score_scale, kbar, sel, s));
+  SA_TIMED_STATUS("block_expand", launch_block_expand(sel, BH, d.N, block, kb, causal ? 1 : 0,
+                                                      idx, s));
+  return SA_OK;
+}
+
+int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, const void* Pk,
+                                  sa_dims d, int32_t d_proj, int32_t block, float score_scale,
+                                  int32_t dtype, int32_t row_begin, int32_t row_count, float* S,
+                                  void* ws, size_t ws_bytes, const sa_options* opts,
+                                  void* stream) {
+  if (!S) return SA_ERR_NULL;
+  if (!aligned16(S)) return SA_ERR_ALIGN;
+  if (row_begin < 0 || row_count < 1 || row_begin > d.N - row_count) return SA_ERR_SHAPE;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  BlockPlan p;
+  float *q32, *k32, *kbar;
+  int32_t* sel;
+  int st = block_common(Q, K, Pq, Pk, d, d_proj, block, 1, 0, score_scale, dtype, ws, ws_bytes,
+                        prof, s, p, q32, k32, kbar, sel);
+  if (st != SA_OK) return st;
+  const int BH = d.B * d.H;
+  SA_TIMED_STATUS("block_means", launch_block_select(q32, k32, BH, d.N, d_proj, block, 1, 0,
+                                                     score_scale, kbar, nullptr, s));
+  SA_TIMED_STATUS("block_dump", launch_block_dump(q32, kbar, BH, d.N, p.NB, d_proj, score_scale,
+                                                  row_begin, row_count, S, s));
+  return SA_OK;
+}
+
 int sparse_attn_dilated_indices(sa_dims d, int32_t window, int32_t dilation, int32_t* idx,
                                 int32_t k, const sa_options* opts, void* stream) {
   if (!idx) return SA_ERR_NULL;

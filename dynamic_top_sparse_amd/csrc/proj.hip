@@ -144,6 +144,7 @@ __global__ __launch_bounds__(kThreads) void project_kernel(
     sMax[1][tid] = mx;
   }
   __syncthreads();
+  if (!is_key && lo16 == nullptr) return;   // fp32 rows and norms only
   if (is_key) {
     if (tid < 2 && kstat != nullptr) {
       float m = 0.0f;

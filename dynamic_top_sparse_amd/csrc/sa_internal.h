@@ -191,6 +191,18 @@ hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klo
 hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
                                 int32_t* counts, int Ncap, hipStream_t s);
 
+// Block-granular selection (block.hip): block means of k_low (kbar
+// [nh][NB][dp]), each query's kept blocks (sel [nh][N][kb], best first; none
+// written when sel is null), their keys as idx rows [nh][N][kb*block], and
+// the block scores of chosen rows.  q32/k32 rows of head h at h*N.
+hipError_t launch_block_select(const float* q32, const float* k32, int nh, int N, int dp,
+                               int block, int kb, int causal, float scale, float* kbar,
+                               int32_t* sel, hipStream_t s);
+hipError_t launch_block_expand(const int32_t* sel, int nh, int N, int block, int kb, int causal,
+                               int32_t* idx, hipStream_t s);
+hipError_t launch_block_dump(const float* q32, const float* kbar, int nh, int N, int NB, int dp,
+                             float scale, int row_begin, int row_count, float* S, hipStream_t s);
+
 // Split gather of one head whose idx rows are ascending (the fused forward's).
 // seg[q][r] (r = 0..kGatherRanges) is the first position of row q whose key
 // is >= gather_ranges(N, causal).b[r]; the re-rank and fallback kernels write it

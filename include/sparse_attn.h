@@ -207,6 +207,37 @@ int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const floa
                        const sa_options* opts, void* stream);
 
 /*
+ * Block-granular selection (block-sparse attention: the SSA page's
+ * _block_sparsify works on blocks of the mask; page "mhpq.cn/news/1098205"
+ * §2.1, block-sparse attention computes only some block pairs).  Keys are cut
+ * into blocks of `block` consecutive rows (the last one may be shorter).
+ * Each block is scored as a whole with its mean projected key,
+ *   kbar_J = fl(sum of the block's k_low rows, in key order) / n_J,
+ *   score_iJ = score_scale · q_low_i·kbar_J (the fixed-order fp32 dot
+ *   product of the token scores),
+ * so a block's score is, up to rounding, the mean of its keys' scores.
+ * Query i keeps its kb best blocks by (score descending, block ascending);
+ * causally it keeps its own block (keys up to i) plus the kb-1 best blocks
+ * that end before it.  idx (out) [B,H,N,kb*block] int32 lists the keys of
+ * the kept blocks in ascending order (causally only j <= i), then -1; it
+ * feeds sparse_attn_gather.  1 <= kb <= 32, kb*block <= SA_K_MAX.
+ * sparse_attn_block_scores_dump writes the block scores of query rows
+ * [row_begin, row_begin+row_count): S [B,H,row_count,ceil(N/block)] fp32.
+ * Both take ws of sparse_attn_block_workspace_size(d, d_proj, block, kb)
+ * bytes (the dump: kb = 1).
+ */
+size_t sparse_attn_block_workspace_size(sa_dims d, int32_t d_proj, int32_t block, int32_t kb);
+int sparse_attn_block_topk(const void* Q, const void* K, const void* Pq, const void* Pk,
+                           sa_dims d, int32_t d_proj, int32_t block, int32_t kb, int32_t causal,
+                           float score_scale, int32_t dtype, int32_t* idx, void* ws,
+                           size_t ws_bytes, const sa_options* opts, void* stream);
+int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, const void* Pk,
+                                  sa_dims d, int32_t d_proj, int32_t block, float score_scale,
+                                  int32_t dtype, int32_t row_begin, int32_t row_count, float* S,
+                                  void* ws, size_t ws_bytes, const sa_options* opts,
+                                  void* stream);
+
+/*
  * Index variants feeding sparse_attn_gather.
  *
  * Boundary smoothing of the top-k (page "mhpq.cn/news/1098205", §4.2: when

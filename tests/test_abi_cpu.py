@@ -221,3 +221,28 @@ def test_index_variant_validation(lib):
     assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, float("nan"), 0, A, A, 1 << 30, None, None) == -2
     assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, 0.1, 0, None, A, 1 << 30, None, None) == -1
     assert sm(A, A, A, A, dd, 16, 8, 0, 0.25, 0.1, 0, A, A, 64, None, None) == -5
+
+
+def test_decode_and_block_validation(lib):
+    d = D(1, 2, 1000, 64)
+    assert lib.sparse_attn_decode_workspace_size(d, 16, 32) > 1000 * 2 * 4
+    assert lib.sparse_attn_decode_workspace_size(d, 24, 32) == 0
+    ws = lib.sparse_attn_decode_workspace_size(d, 16, 32)
+    dec = lib.sparse_attn_decode
+    assert dec(A, A, A, A, A, d, 16, 0, 32, 0.25, 0.1, 0, A, None, None, A, ws, None, None) == -2
+    assert dec(A, A, A, A, A, d, 16, 1001, 32, 0.25, 0.1, 0, A, None, None, A, ws, None, None) == -2
+    assert dec(A, A, A, A, A, d, 16, 10, 32, 0.25, 0.1, 0, A, None, None, A, 16, None, None) == -5
+    assert dec(A, A, None, A, A, d, 16, 10, 32, 0.25, 0.1, 0, A, None, None, A, ws, None, None) == -1
+    app = lib.sparse_attn_decode_append_keys
+    assert app(A, A, D(1, 2, 10, 64), 16, 0, A, 1000, 995, None, None) == -2   # past the cache
+    assert app(A, A, D(1, 2, 10, 64), 16, 0, A, 1000, -1, None, None) == -2
+    assert app(A, A, D(1, 2, 10, 64), 16, 0, A + 4, 1000, 0, None, None) == -4
+    assert lib.sparse_attn_block_workspace_size(d, 16, 64, 4) > 0
+    assert lib.sparse_attn_block_workspace_size(d, 16, 64, 33) == 0       # kb above 32
+    assert lib.sparse_attn_block_workspace_size(d, 16, 512, 8) == 0       # kb*block above 2048
+    bt = lib.sparse_attn_block_topk
+    bws = lib.sparse_attn_block_workspace_size(d, 16, 64, 4)
+    assert bt(A, A, A, A, d, 16, 0, 4, 0, 0.25, 0, A, A, bws, None, None) == -2
+    assert bt(A, A, A, A, d, 16, 64, 33, 0, 0.25, 0, A, A, bws, None, None) == -3
+    assert bt(A, A, A, A, d, 16, 64, 4, 0, 0.25, 0, A, A, 16, None, None) == -5
+    assert bt(A, A, A, A, d, 16, 64, 4, 0, 0.25, 0, None, A, bws, None, None) == -1

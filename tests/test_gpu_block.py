@@ -1,0 +1,69 @@
+"""Block-granular selection (through the C ABI) against the fp64 oracle:
+idx bit-exact against the oracle's block selection recomputed from the
+library's dumped block scores; kept-block overlap against the fp64 block
+scores; attention over the kept keys against the oracle's; block size 1
+equal to the token-level top-k."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_top_sparse_amd as sa
+import oracle as O
+from dynamic_top_sparse_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _blocks_of_row(row, block):
+    return sorted(set(int(j) // block for j in row if j >= 0))
+
+
+@pytest.mark.parametrize("N,D,dp,dtype,block,kb,causal", [
+    (4096, 128, 64, "bf16", 64, 4, False),
+    (3001, 64, 16, "f32", 64, 5, False),        # ragged last block
+    (3001, 128, 64, "bf16", 64, 4, True),
+    (2000, 64, 32, "bf16", 16, 32, True),       # kb at its maximum
+    (700, 64, 16, "f32", 128, 8, False),        # every block kept
+])
+def test_block_selection_all_rows(N, D, dp, dtype, block, kb, causal):
+    w = W.Workload("blk", 1, 2, N, D, dtype, d_proj=dp, k=kb * block, causal=causal)
+    x = W.make_inputs(w, N + kb)
+    g = {n: t.cuda() for n, t in x.items()}
+    idx = _np(sa.sparse_attn_block_topk(g["Q"], g["K"], g["Pq"], g["Pk"], block, kb, causal))
+    SB = _np(sa.sparse_attn_block_scores_dump(g["Q"], g["K"], g["Pq"], g["Pk"], block, 0, N))
+    want = O.block_topk_indices(x["Q"], x["K"], x["Pq"], x["Pk"], block, kb, causal,
+                                sa.default_score_scale(dp),
+                                block_scores=lambda b, h: SB[b, h].astype(np.float64))
+    np.testing.assert_array_equal(idx, want)
+    # against the fp64 block scores: kept blocks differ only at near ties
+    q_low = O.project(O.f64(x["Q"][0, 0]), O.f64(x["Pq"]))
+    kbar = O.block_means(O.project(O.f64(x["K"][0, 0]), O.f64(x["Pk"])), block)
+    SB64 = O.score_rows(q_low, kbar, sa.default_score_scale(dp))
+    bad = 0
+    for i in range(N):
+        got_b = _blocks_of_row(idx[0, 0, i], block)
+        ora_b = list(O.block_select_row(SB64[i], i, block, kb, causal))
+        for a, b2 in zip(sorted(set(ora_b) - set(got_b), key=lambda J: SB64[i, J]),
+                         sorted(set(got_b) - set(ora_b), key=lambda J: -SB64[i, J])):
+            bad += SB64[i, a] - SB64[i, b2] >= 1e-3
+    assert bad <= 0.001 * N * kb, bad
+    out = _np(sa.sparse_attn_gather(g["Q"], g["K"], g["V"], torch.from_numpy(idx).cuda()).float())
+    ref = O.gather_attention(x["Q"], x["K"], x["V"], idx, D ** -0.5)
+    assert np.abs(out - ref).max() <= TOL[w.torch_dtype]
+
+
+def test_block_size_one_is_token_top_k():
+    """Blocks of one key score exactly like the keys themselves, so the block
+    selection is the token-level selection, bit for bit."""
+    w = W.Workload("blk", 1, 2, 3000, 128, "bf16", d_proj=64, k=24)
+    x = W.make_inputs(w, 5)
+    g = {n: t.cuda() for n, t in x.items()}
+    a = sa.sparse_attn_block_topk(g["Q"], g["K"], g["Pq"], g["Pk"], 1, 24)
+    b = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], 24)
+    assert torch.equal(a, b)
