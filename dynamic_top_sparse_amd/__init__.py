@@ -40,7 +40,8 @@ EXPORTS = (
     "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
     "sparse_attn_band_indices_per_batch", "sparse_attn_decode_workspace_size",
     "sparse_attn_decode_append_keys", "sparse_attn_decode", "sparse_attn_block_workspace_size",
-    "sparse_attn_block_topk", "sparse_attn_block_scores_dump",
+    "sparse_attn_block_topk", "sparse_attn_block_scores_dump", "sparse_attn_bwd_workspace_size",
+    "sparse_attn_bwd",
 )
 
 
@@ -107,6 +108,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "sparse_attn_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32,
                                               f32, i32, vp, vp, vp, vp, sz, op, vp]),
         "sparse_attn_block_workspace_size": (sz, [sa_dims, i32, i32, i32]),
+        "sparse_attn_bwd_workspace_size": (sz, [sa_dims, i32, i32, i32]),
+        "sparse_attn_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, sa_dims, i32, i32, f32, f32,
+                                           i32, vp, vp, vp, vp, vp, vp, sz, op, vp]),
         "sparse_attn_block_topk": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, i32, i32,
                                                   f32, i32, vp, vp, sz, op, vp]),
         "sparse_attn_block_scores_dump": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, f32,
@@ -468,6 +472,47 @@ def sparse_attn_band_indices_per_batch(H: int, N: int, radii: torch.Tensor,
     return idx
 
 
+def sparse_attn_bwd(Q, K, V, dO, idx, Pq=None, Pk=None, scorer_grad: bool = True,
+                    score_scale: Optional[float] = None, softmax_scale: Optional[float] = None,
+                    workspace: Optional[torch.Tensor] = None,
+                    profile: Optional[Profile] = None):
+    """Gradients of the forward for index sets idx: returns (dQ, dK, dV) in
+    fp32, plus (dPq, dPk) when scorer_grad (the straight-through gradient
+    of the scorer; Pq, Pk required)."""
+    _check_qkv(Q, K, V, dO)
+    _tensor(idx, "idx")
+    if idx.dim() != 4:
+        raise ValueError("idx must be [B, H, N, k]")
+    k = idx.shape[-1]
+    _check_idx(idx, Q, k)
+    B, H, N, D = Q.shape
+    d_proj = 16
+    if scorer_grad:
+        d_proj = _check_proj(Pq, Pk, Q)
+    sscale = default_score_scale(d_proj) if score_scale is None else float(score_scale)
+    ascale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
+    lib = load_library()
+    if workspace is None:
+        n = int(lib.sparse_attn_bwd_workspace_size(_dims(Q), d_proj, k, int(scorer_grad)))
+        if n == 0:
+            raise SparseAttnError(-3, "sparse_attn_bwd_workspace_size")
+        workspace = torch.empty(n, dtype=torch.uint8, device=Q.device)
+    _check_workspace(workspace, Q)
+    f32 = dict(dtype=torch.float32, device=Q.device)
+    dQ, dK, dV = (torch.empty(B, H, N, D, **f32) for _ in range(3))
+    dPq = torch.empty(D, d_proj, **f32) if scorer_grad else None
+    dPk = torch.empty(D, d_proj, **f32) if scorer_grad else None
+    st = lib.sparse_attn_bwd(
+        _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(Pq, "Pq") if scorer_grad else None,
+        _dev(Pk, "Pk") if scorer_grad else None, _dev(dO, "dO"), _dev(idx, "idx"), _dims(Q),
+        d_proj, k, sscale, ascale, _dtype_code(Q), _dev(dQ, "dQ"), _dev(dK, "dK"),
+        _dev(dV, "dV"), _dev(dPq, "dPq") if scorer_grad else None,
+        _dev(dPk, "dPk") if scorer_grad else None, _dev(workspace, "workspace"),
+        workspace.numel(), _options(None, profile), _stream(Q))
+    _check(st, "sparse_attn_bwd")
+    return (dQ, dK, dV, dPq, dPk) if scorer_grad else (dQ, dK, dV)
+
+
 def _block_workspace(Q, d_proj: int, block: int, kb: int) -> torch.Tensor:
     B, H, N, D = Q.shape
     n = int(load_library().sparse_attn_block_workspace_size(sa_dims(B, H, N, D), d_proj, block,
@@ -655,5 +700,5 @@ __all__ = [
     "sparse_attn_workspace_stats", "default_score_scale", "default_softmax_scale",
     "sparse_attn_scores_topk_smoothed", "sparse_attn_dilated_indices",
     "sparse_attn_band_indices_per_batch", "DecodeCache", "sparse_attn_block_topk",
-    "sparse_attn_block_scores_dump",
+    "sparse_attn_block_scores_dump", "sparse_attn_bwd",
 ]

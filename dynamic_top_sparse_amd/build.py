@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OUT_DIR = os.path.join(PKG, "lib")
 LIB = os.path.join(OUT_DIR, "libsparse_attn.so")
 SOURCES = ["api.cpp", "profile.cpp", "proj.hip", "scorer.hip", "finalize.hip", "gather.hip", "dump.hip",
-           "variants.hip", "decode.hip", "block.hip"]
+           "variants.hip", "decode.hip", "block.hip", "bwd.hip"]
 ARCH = "gfx950"
 
 FLAGS = [

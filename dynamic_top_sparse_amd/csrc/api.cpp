@@ -613,6 +613,122 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
   return SA_OK;
 }
 
+// ----------------------------------------------------------- backward ---
+namespace {
+struct BwdPlan {
+  size_t off_q32, off_k32, off_dql, off_dkl, off_cnt, off_off, off_cur, off_ei, off_ep, off_ed,
+      off_part, total;
+  int nchunks;
+};
+BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
+  const size_t BH = static_cast<size_t>(d.B) * d.H, N = static_cast<size_t>(d.N);
+  const size_t ents = BH * N * static_cast<size_t>(k);
+  BwdPlan p;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  const size_t lo = scorer ? BH * N * dp * 4 : 0;
+  p.off_q32 = take(lo);
+  p.off_k32 = take(lo);
+  p.off_dql = take(lo);
+  p.off_dkl = take(lo);
+  p.off_cnt = take(BH * N * 4);
+  p.off_off = take(BH * N * 4);
+  p.off_cur = take(BH * N * 4);
+  p.off_ei = take(ents * 4);
+  p.off_ep = take(ents * 4);
+  p.off_ed = take(ents * 4);
+  p.nchunks = scorer ? outer_sum_chunks(static_cast<long long>(BH * N)) : 0;
+  p.off_part = take(scorer ? static_cast<size_t>(p.nchunks) * d.D * dp * 4 * 2 : 0);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad) {
+  if (check_dims(d, k) != SA_OK || !supported_D(d.D)) return 0;
+  if (scorer_grad && !supported_dp(d_proj)) return 0;
+  return bwd_plan(d, d_proj, k, scorer_grad != 0).total;
+}
+
+int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
+                    const void* dO, const int32_t* idx, sa_dims d, int32_t d_proj, int32_t k,
+                    float score_scale, float softmax_scale, int32_t dtype, float* dQ, float* dK,
+                    float* dV, float* dPq, float* dPk, void* ws, size_t ws_bytes,
+                    const sa_options* opts, void* stream) {
+  if (!Q || !K || !V || !dO || !idx || !dQ || !dK || !dV || !ws) return SA_ERR_NULL;
+  const bool scorer = dPq != nullptr || dPk != nullptr;
+  if (scorer && (!dPq || !dPk || !Pq || !Pk)) return SA_ERR_NULL;
+  int st = check_dims(d, k);
+  if (st != SA_OK) return st;
+  if (!supported_D(d.D)) return SA_ERR_UNSUPPORTED;
+  if (scorer && !supported_dp(d_proj)) return SA_ERR_UNSUPPORTED;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale) || (scorer && !std::isfinite(score_scale)))
+    return SA_ERR_SHAPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(dO) || !aligned16(idx) ||
+      !aligned16(dQ) || !aligned16(dK) || !aligned16(dV) || !aligned16(ws))
+    return SA_ERR_ALIGN;
+  if (scorer && (!aligned16(Pq) || !aligned16(Pk) || !aligned16(dPq) || !aligned16(dPk)))
+    return SA_ERR_ALIGN;
+  const BwdPlan p = bwd_plan(d, d_proj, k, scorer);
+  if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  float* q32 = reinterpret_cast<float*>(base + p.off_q32);
+  float* k32 = reinterpret_cast<float*>(base + p.off_k32);
+  float* dql = reinterpret_cast<float*>(base + p.off_dql);
+  float* dkl = reinterpret_cast<float*>(base + p.off_dkl);
+  int* cnt = reinterpret_cast<int*>(base + p.off_cnt);
+  int* offs = reinterpret_cast<int*>(base + p.off_off);
+  int* cur = reinterpret_cast<int*>(base + p.off_cur);
+  BwdArgs a{};
+  a.dtype = dtype;
+  a.D = d.D;
+  a.dp = scorer ? d_proj : 0;
+  a.k = k;
+  a.N = d.N;
+  a.nh = d.B * d.H;
+  a.scale = softmax_scale;
+  a.sscale = score_scale;
+  a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.idx = idx;
+  a.q32 = q32; a.k32 = k32;
+  a.dQ = dQ; a.dK = dK; a.dV = dV; a.dqlow = dql; a.dklow = dkl;
+  a.cursor = cur; a.seg_off = offs; a.seg_cnt = cnt;
+  a.ent_i = reinterpret_cast<int*>(base + p.off_ei);
+  a.ent_p = reinterpret_cast<float*>(base + p.off_ep);
+  a.ent_d = reinterpret_cast<float*>(base + p.off_ed);
+  const long long rows = static_cast<long long>(a.nh) * d.N;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (scorer) {
+    SA_TIMED_STATUS("bwd_project", launch_project_rows(Q, Pq, a.nh, d.N, d.N, d.D, d_proj, dtype,
+                                                       0, q32, nullptr, nullptr, s));
+    SA_TIMED_STATUS("bwd_project", launch_project_rows(K, Pk, a.nh, d.N, d.N, d.D, d_proj, dtype,
+                                                       1, k32, nullptr, nullptr, s));
+  }
+  SA_TIMED_STATUS("bwd_count", launch_fill_zero(cnt, align_up(static_cast<size_t>(rows) * 4), s));
+  SA_TIMED_STATUS("bwd_count", launch_bwd_count(idx, a.nh, d.N, k, cnt, s));
+  SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, cur, s));
+  a.pass = 0;
+  SA_TIMED_STATUS("bwd_rows", launch_bwd_pass(a, s));
+  a.pass = 1;
+  SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
+  if (scorer) {
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dql, Pq, dtype, rows, d.D, d_proj, dQ, s));
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dkl, Pk, dtype, rows, d.D, d_proj, dK, s));
+    float* part = reinterpret_cast<float*>(base + p.off_part);
+    const size_t psz = static_cast<size_t>(p.nchunks) * d.D * d_proj;
+    SA_TIMED_STATUS("bwd_scorer", launch_outer_sum(Q, dtype, dql, rows, d.D, d_proj, part,
+                                                   p.nchunks, dPq, s));
+    SA_TIMED_STATUS("bwd_scorer", launch_outer_sum(K, dtype, dkl, rows, d.D, d_proj, part + psz,
+                                                   p.nchunks, dPk, s));
+  }
+  return SA_OK;
+}
+
 int sparse_attn_dilated_indices(sa_dims d, int32_t window, int32_t dilation, int32_t* idx,
                                 int32_t k, const sa_options* opts, void* stream) {
   if (!idx) return SA_ERR_NULL;

@@ -630,7 +630,219 @@ hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* 
   return hipGetLastError();
 }
 
+// ------------------------------------------------------------ backward ---
+// Backward of the attention over index sets (page "mhpq.cn/news/1098205",
+// §2.3: the forward keeps the hard top-k; in the backward the selected
+// positions' gradients flow as usual and the others get none; the scorer is
+// reached through the selected positions' attention weights).  With
+// p_t = softmax(l)_t, dp_t = dO·V[j_t], delta = sum_t p_t dp_t and
+// dl_t = p_t (dp_t - delta):
+//   dQ_i = scale · sum_t dl_t K[j_t]                     (row pass)
+//   dV_j = sum over (i, t) with j_t = j of p_t dO_i       (key pass)
+//   dK_j = scale · sum over the same of dl_t Q_i          (key pass)
+// and, for the scorer (straight-through: a kept pair's score receives its
+// logit's gradient dl_t), dq_low_i = score_scale · sum_t dl_t k_low[j_t]
+// (row pass) and dk_low_j = score_scale · sum dl_t q_low_i (key pass).
+// The row pass appends (i, p_t, dl_t) to key j_t's segment of an entry list
+// (segment offsets from a count and a scan); the key pass then gathers the
+// rows of the queries that kept each key, as the forward gathers key rows.
+constexpr int kBwdChunk = 512;     // key-pass entries staged in LDS at a time
+
+__host__ __device__ constexpr int bwd_row_wave_floats(int k) { return 3 * gather_slog_floats(k); }
+__host__ __device__ constexpr int bwd_key_wave_floats() { return 3 * gather_slog_floats(kBwdChunk); }
+
+template <int EPL>
+__device__ __forceinline__ void store_f32_row(float* dst, const float (&v)[EPL], float f) {
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
+}
+
+template <typename T, int D, int DP>
+__global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const int32_t* __restrict__ idx, int k, int N, float scale,
+    float sscale, const float* __restrict__ k32, float* __restrict__ dQ,
+    float* __restrict__ dqlow, int* __restrict__ cursor, int* __restrict__ ent_i,
+    float* __restrict__ ent_p, float* __restrict__ ent_d) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int SL = gather_slog_floats(k);
+  float* sl = bwd_lds + w * bwd_row_wave_floats(k);      // logits, then p_t
+  float* sd = sl + SL;                                    // dp_t, then dl_t
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const int h = blockIdx.y;
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= N) return;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const T* Kh = K + hN * D;
+  const T* Vh = V + hN * D;
+  stage_entries(idx + (hN + q) * k, 0, k, sidx);
+  int bad = 0;
+  logits<T, D>(Q + (hN + q) * D, Kh, sidx, 0, k, N, scale * kLog2e, sl, bad);
+  logits<T, D>(dO + (hN + q) * D, Vh, sidx, 0, k, N, 1.0f, sd, bad);
+  if (bad) atomicOr(&g_index_error_flag, 1);
+  wave_sync();
+  float sum;
+  const float mx = softmax_weights(sl, k, sum);
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float acc[EPL];
+  if (mx == -INFINITY) {    // no valid entry: no gradient from this row
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
+    if constexpr (DP > 0) {
+      if (l < DP / 4)
+        *reinterpret_cast<float4*>(dqlow + (hN + q) * DP + 4 * l) = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    return;
+  }
+  // p_t, delta, dl_t (invalid entries have p_t = 0 and contribute nothing)
+  const float inv = 1.0f / sum;
+  float dsum = 0.0f;
+  for (int t = l; t < k; t += kWave) {
+    const float p = sl[t] * inv;
+    sl[t] = p;
+    dsum += p != 0.0f ? p * sd[t] : 0.0f;
+  }
+  const float delta = wave_sum(dsum);
+  for (int t = l; t < k; t += kWave) {
+    const float p = sl[t];
+    sd[t] = p != 0.0f ? p * (sd[t] - delta) : 0.0f;
+  }
+  wave_sync();
+  weighted_rows<T, D>(Kh, sidx, 0, k, N, sd, acc);
+  if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, scale);
+  if constexpr (DP > 0) {
+    float a4[4];
+    weighted_rows<float, DP>(k32 + hN * DP, sidx, 0, k, N, sd, a4);
+    if (l < DP / 4) store_f32_row<4>(dqlow + (hN + q) * DP + 4 * l, a4, sscale);
+  }
+  // the entries for the key pass, in the head's region of N*k entries
+  const size_t ebase = hN * static_cast<size_t>(k);
+  for (int t = l; t < k; t += kWave) {
+    const int j = sidx[t];
+    if (j >= 0 && j < N) {
+      const size_t pos = ebase + static_cast<unsigned>(atomicAdd(&cursor[hN + j], 1));
+      ent_i[pos] = q;
+      ent_p[pos] = sl[t];
+      ent_d[pos] = sd[t];
+    }
+  }
+}
+
+template <typename T, int D, int DP>
+__global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
+    const T* __restrict__ Q, const T* __restrict__ dO, const float* __restrict__ q32,
+    const int* __restrict__ seg_off, const int* __restrict__ seg_cnt,
+    const int* __restrict__ ent_i, const float* __restrict__ ent_p,
+    const float* __restrict__ ent_d, int N, int k, float scale, float sscale,
+    float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ dklow) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  constexpr int SL = gather_slog_floats(kBwdChunk);
+  float* sp = bwd_lds + w * bwd_key_wave_floats();
+  float* sd = sp + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const int h = blockIdx.y;
+  const int j = blockIdx.x * kWaves + w;
+  if (j >= N) return;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const T* Qh = Q + hN * D;
+  const T* dOh = dO + hN * D;
+  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[hN + j]);
+  const int n = seg_cnt[hN + j];
+  float av[EPL], ak[EPL], al[4];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) al[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
+    const int m = min(kBwdChunk, n - c0);
+    for (int t = l; t < m; t += kWave) {
+      sidx[t] = ent_i[o0 + c0 + t];
+      sp[t] = ent_p[o0 + c0 + t];
+      sd[t] = ent_d[o0 + c0 + t];
+    }
+    wave_sync();
+    float tmp[EPL];
+    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
+    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    if constexpr (DP > 0) {
+      float t4[4];
+      weighted_rows<float, DP>(q32 + hN * DP, sidx, 0, m, N, sd, t4);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) al[e] += t4[e];
+    }
+    wave_sync();    // the chunk's LDS is read before the next one is staged
+  }
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  if (g == 0) {
+    store_f32_row<EPL>(dV + (hN + j) * D + e0, av, 1.0f);
+    store_f32_row<EPL>(dK + (hN + j) * D + e0, ak, scale);
+  }
+  if constexpr (DP > 0) {
+    if (l < DP / 4) store_f32_row<4>(dklow + (hN + j) * DP + 4 * l, al, sscale);
+  }
+}
+
+template <typename T, int D, int DP>
+hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
+  static std::atomic<int> lds_rows[kMaxDevices], lds_keys[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_kernel<T, D, DP>),
+                                    kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rows);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_kernel<T, D, DP>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_keys);
+  if (e != hipSuccess) return e;
+  const dim3 grid((a.N + kWaves - 1) / kWaves, a.nh);
+  if (a.pass == 0) {
+    hipLaunchKernelGGL((bwd_rows_kernel<T, D, DP>), grid, dim3(kThreads),
+                       kWaves * bwd_row_wave_floats(a.k) * 4, s, static_cast<const T*>(a.Q),
+                       static_cast<const T*>(a.K), static_cast<const T*>(a.V),
+                       static_cast<const T*>(a.dO), a.idx, a.k, a.N, a.scale, a.sscale, a.k32,
+                       a.dQ, a.dqlow, a.cursor, a.ent_i, a.ent_p, a.ent_d);
+  } else {
+    hipLaunchKernelGGL((bwd_keys_kernel<T, D, DP>), grid, dim3(kThreads),
+                       kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
+                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.ent_i,
+                       a.ent_p, a.ent_d, a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t bwd_passes_d(const BwdArgs& a, hipStream_t s) {
+  switch (a.dp) {
+    case 0: return bwd_passes_t<T, D, 0>(a, s);
+    case 16: return bwd_passes_t<T, D, 16>(a, s);
+    case 32: return bwd_passes_t<T, D, 32>(a, s);
+    case 64: return bwd_passes_t<T, D, 64>(a, s);
+    case 128: return bwd_passes_t<T, D, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
 }  // namespace
+
+hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s) {
+  if (a.dtype == 0) {
+    if (a.D == 64) return bwd_passes_d<float, 64>(a, s);
+    if (a.D == 128) return bwd_passes_d<float, 128>(a, s);
+  } else {
+    if (a.D == 64) return bwd_passes_d<bf16_t, 64>(a, s);
+    if (a.D == 128) return bwd_passes_d<bf16_t, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_gather(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
                          int nheads, int N, int D, float softmax_scale, int dtype, void* O,

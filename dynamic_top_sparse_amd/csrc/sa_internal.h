@@ -203,6 +203,35 @@ hipError_t launch_block_expand(const int32_t* sel, int nh, int N, int block, int
 hipError_t launch_block_dump(const float* q32, const float* kbar, int nh, int N, int NB, int dp,
                              float scale, int row_begin, int row_count, float* S, hipStream_t s);
 
+// Backward of the gather attention (gather.hip, the two wave passes) and its
+// helpers (bwd.hip).  dp = 0 leaves out the scorer's gradient.
+struct BwdArgs {
+  int pass;             // 0: row pass, 1: key pass
+  int dtype, D, dp, k, N, nh;
+  float scale, sscale;
+  const void *Q, *K, *V, *dO;
+  const int32_t* idx;
+  const float *q32, *k32;       // fp32 projections (scorer gradient only)
+  float *dQ, *dK, *dV, *dqlow, *dklow;
+  int* cursor;                  // row pass: next free entry of each key's segment
+  const int *seg_off, *seg_cnt; // key pass: each key's segment
+  int* ent_i;
+  float *ent_p, *ent_d;
+};
+hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
+hipError_t launch_bwd_count(const int32_t* idx, int nh, int N, int k, int* cnt, hipStream_t s);
+hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, int* cursor,
+                           hipStream_t s);
+hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// out[r][d] += sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
+hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
+                                int dp, float* out, hipStream_t s);
+// dP[d][c] = sum_r X[r][d] * lo[r][c] over all rows (X of dtype), in a
+// fixed order through per-chunk partials
+hipError_t launch_outer_sum(const void* X, int dtype, const float* lo, long long rows, int D,
+                            int dp, float* partial, int nchunks, float* dP, hipStream_t s);
+int outer_sum_chunks(long long rows);
+
 // Split gather of one head whose idx rows are ascending (the fused forward's).
 // seg[q][r] (r = 0..kGatherRanges) is the first position of row q whose key
 // is >= gather_ranges(N, causal).b[r]; the re-rank and fallback kernels write it

@@ -171,6 +171,40 @@ int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t
                              int32_t k, const sa_options* opts, void* stream);
 
 /*
+ * Backward of the forward for given index sets (page "mhpq.cn/news/1098205",
+ * §2.3: the forward keeps the hard top-k; in the backward the selected
+ * positions' gradients flow as usual, the unselected ones get zero, and the
+ * scorer receives its gradient through the selected positions' attention
+ * weights).
+ *   Q, K, V, dO (upstream gradient of O): [B,H,N,D] of dtype; idx:
+ *   [B,H,N,k] int32 (list semantics as in sparse_attn_gather: -1 skipped,
+ *   repeats counted; entries >= N are skipped and set the sticky flag).
+ *   Out, fp32 whatever the dtype: dQ, dK, dV [B,H,N,D] (overwritten).
+ *   Attention path: with p = softmax(softmax_scale · q_i·K[idx_t]) and
+ *   dl_t = p_t (dO_i·V[idx_t] - sum_u p_u dO_i·V[idx_u]):
+ *   dQ_i = softmax_scale · sum_t dl_t K[idx_t]; each kept key j gets
+ *   dV_j += p_t dO_i and dK_j += softmax_scale · dl_t q_i from every row i
+ *   that kept it; keys no row kept get zero.
+ *   Scorer path, when dPq and dPk are given ([D,d_proj] fp32, overwritten;
+ *   Pq, Pk then required): the straight-through reading of §2.3, each kept
+ *   pair's score score_scale · q_low_i·k_low_j receives its logit's
+ *   gradient dl_t, which the chain rule takes through q_low = Q·Pq and
+ *   k_low = K·Pk to dPq, dPk (summed over every head and row) and into dQ,
+ *   dK.  With dPq = dPk = NULL only the attention path is computed.
+ *   dK and dV add each key's contributions in an order that can differ
+ *   from run to run (the entry lists are filled with atomics), so they agree
+ *   between runs to fp32 rounding, not bit for bit.
+ *   ws: sparse_attn_bwd_workspace_size(d, d_proj, k, scorer) bytes (about
+ *   12 bytes per idx entry plus, for the scorer, four fp32 projections).
+ */
+size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad);
+int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
+                    const void* dO, const int32_t* idx, sa_dims d, int32_t d_proj, int32_t k,
+                    float score_scale, float softmax_scale, int32_t dtype, float* dQ, float* dK,
+                    float* dV, float* dPq, float* dPk, void* ws, size_t ws_bytes,
+                    const sa_options* opts, void* stream);
+
+/*
  * Decode: one new query per (b, h) against the keys cached so far (page
  * "mhpq.cn/news/1098205", §3.4: at inference the selection runs for each
  * generated token over the KV cache, and how often a key is selected can

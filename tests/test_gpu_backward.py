@@ -1,0 +1,112 @@
+"""Backward (through the C ABI) against the fp64 oracle's backward
+(page "mhpq.cn/news/1098205", §2.3: hard top-k forward, gradients through
+the kept positions only, the scorer reached through the kept positions'
+attention weights).  Every gradient is fp32; the bound is fp32 accumulation
+over the entries that feed one output: |err| <= 1e-5 * max(1, max|ref|) for
+dQ, dK, dV and 1e-4 * max|ref| for dPq, dPk, which sum over every row of
+every head."""
+import numpy as np
+import pytest
+import torch
+
+import dynamic_top_sparse_amd as sa
+import oracle as O
+from dynamic_top_sparse_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def _close(got, want, rel, name):
+    scale = max(1.0, float(np.abs(want).max()))
+    err = float(np.abs(got.astype(np.float64) - want).max())
+    assert err <= rel * scale, (name, err, scale)
+    return err / scale
+
+
+@pytest.mark.parametrize("N,k,D,dp,dtype,causal", [
+    (1500, 32, 64, 16, "f32", False),
+    (1200, 48, 128, 64, "bf16", True),
+    (900, 900, 64, 32, "bf16", False),       # every key kept: dense attention's gradient
+    (2000, 7, 128, 128, "f32", True),
+])
+def test_backward_matches_oracle(N, k, D, dp, dtype, causal):
+    w = W.Workload("bwd", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
+    x = W.make_inputs(w, N + k)
+    gen = torch.Generator().manual_seed(N)
+    dO = torch.randn(1, 2, N, D, generator=gen).to(w.torch_dtype)
+    g = {n: t.cuda() for n, t in x.items()}
+    idx = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], k, causal)
+    sscale, ascale = sa.default_score_scale(dp), sa.default_softmax_scale(D)
+    got = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, g["Pq"], g["Pk"])
+    want = O.sparse_attn_backward(x["Q"], x["K"], x["V"], x["Pq"], x["Pk"], _np(idx), dO,
+                                  sscale, ascale, scorer_grad=True)
+    for name, a, b in zip(("dQ", "dK", "dV"), got[:3], want[:3]):
+        _close(_np(a), b, 1e-5, name)
+    for name, a, b in zip(("dPq", "dPk"), got[3:], want[3:]):
+        _close(_np(a), b, 1e-4, name)
+    # the attention path alone
+    att = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False)
+    want0 = O.sparse_attn_backward(x["Q"], x["K"], x["V"], x["Pq"], x["Pk"], _np(idx), dO,
+                                   sscale, ascale, scorer_grad=False)
+    for name, a, b in zip(("dQ", "dK", "dV"), att, want0[:3]):
+        _close(_np(a), b, 1e-5, name)
+
+
+def test_backward_list_semantics():
+    """-1 entries skipped, repeats counted twice, rows without entries give
+    nothing, keys no row kept get zero."""
+    B, H, N, D, k = 1, 2, 600, 64, 12
+    gen = torch.Generator().manual_seed(1)
+    Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen) for _ in range(4))
+    idx = torch.randint(-1, N // 2, (B, H, N, k), generator=gen, dtype=torch.int32)
+    idx[0, 0, 5] = -1
+    idx[0, 1, 7, :4] = 3
+    got = sa.sparse_attn_bwd(Q.cuda(), K.cuda(), V.cuda(), dO.cuda(), idx.cuda(),
+                             scorer_grad=False)
+    want = O.sparse_attn_backward(Q, K, V, np.zeros((D, 16)), np.zeros((D, 16)), idx.numpy(),
+                                  dO, 1.0, D ** -0.5, scorer_grad=False)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, want[:3]):
+        _close(_np(a), b, 1e-5, name)
+    assert torch.all(got[0][0, 0, 5] == 0)
+    assert torch.all(got[1][:, :, N // 2:] == 0) and torch.all(got[2][:, :, N // 2:] == 0)
+    assert sa.sparse_attn_check_status() == 0
+
+
+def test_backward_full_size_bf16_32k_sampled():
+    """The bf16 32K workload (32 heads, N = 32768, k = 256) through the fused
+    forward's index sets: per head, the dV rows sum to the dO rows (softmax
+    weights sum to one); sampled dQ rows and sampled keys' dK, dV rows
+    against the oracle, which gathers the rows that kept each sampled key."""
+    w = W.get("bf16_32k")
+    x = W.make_inputs(w, 0)
+    gen = torch.Generator().manual_seed(2)
+    dO = torch.randn(w.B, w.H, w.N, w.D, generator=gen).to(torch.bfloat16)
+    g = {n: t.cuda() for n, t in x.items()}
+    _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, return_idx=True)
+    dQ, dK, dV = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False)
+    torch.cuda.synchronize()
+    dVs = _np(dV.double().sum(dim=2))
+    dOs = dO.double().sum(dim=2).numpy()
+    assert np.abs(dVs - dOs).max() <= 1e-5 * w.N, np.abs(dVs - dOs).max()
+    ascale = w.D ** -0.5
+    rng = np.random.default_rng(0)
+    for h in (0, w.H - 1):
+        Qh, Kh, Vh, dOh = (O.f64(t[0, h]) for t in (x["Q"], x["K"], x["V"], dO))
+        idx_h = _np(idx[0, h]).astype(np.int64)
+        for i in rng.choice(w.N, 16, replace=False):
+            dq, _, _, _ = O.attend_row_backward(Qh[i], Kh, Vh, idx_h[i], ascale, dOh[i])
+            _close(_np(dQ[0, h, i]), dq, 1e-5, "dQ")
+        for j in rng.choice(w.N, 4, replace=False):
+            rows, ts = np.nonzero(idx_h == j)
+            dk = np.zeros(w.D)
+            dv = np.zeros(w.D)
+            for i, t in zip(rows, ts):
+                _, dKr, dVr, _ = O.attend_row_backward(Qh[i], Kh, Vh, idx_h[i], ascale, dOh[i])
+                dk += dKr[t]
+                dv += dVr[t]
+            _close(_np(dK[0, h, j]), dk, 1e-5, "dK")
+            _close(_np(dV[0, h, j]), dv, 1e-5, "dV")
