@@ -41,6 +41,7 @@ sys.path.insert(0, ROOT)
 METRIC = "queries/s + eff. TFLOP/s, top-k sparse attn fwd, N=128K H=32 D=128 k=512"
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 
 
 # rocprofv3 --pmc readings of the headline command (see profiles/), per launch
@@ -188,6 +189,249 @@ def cpu_baseline(x, w, target_s: float = 20.0) -> dict:
                        + f"; {t:.1f} s with BLAS on {cores} cores")}
 
 
+def time_steps(step, prof, steps: int, warmup: int):
+    """W untimed steps, then K steps each bracketed by HIP events on the
+    current stream with a 512 MiB cache-flushing write between them (outside
+    the events).  Returns (sorted per-step ms, wall ms per step, kernel
+    records of the timed steps)."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e0, e1 in ev:
+        flush.fill_(1)
+        e0.record(stream)
+        step(prof)
+        e1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    del flush
+    return sorted(e0.elapsed_time(e1) for e0, e1 in ev), (t1 - t0) * 1e3 / steps, prof.read()
+
+
+def kernel_table(recs, steps):
+    kern = {}
+    for name, ms in recs:
+        d = kern.setdefault(name, {"launches": 0, "ms_total": 0.0})
+        d["launches"] += 1
+        d["ms_total"] += ms
+    return kern, {n: d["ms_total"] / steps for n, d in kern.items()}
+
+
+def oracle_rate(fn, n_total: int, target_s: float = 20.0):
+    """Times fn(rows) of the oracle on a pilot of 8 rows, then on a sample
+    sized to about target_s; BLAS on every core this process may use."""
+    import numpy as np
+    cores = len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:
+        limiter = None
+    rng = np.random.default_rng(0)
+    try:
+        t = time.perf_counter()
+        fn(sorted(rng.choice(n_total, 8, replace=False).tolist()))
+        tp = time.perf_counter() - t
+        n = int(min(4096, n_total, max(16, 8 * target_s / max(tp, 1e-3))))
+        rows = sorted(rng.choice(n_total, n, replace=False).tolist())
+        t = time.perf_counter()
+        fn(rows)
+        t = time.perf_counter() - t
+    finally:
+        if limiter is not None:
+            limiter.unregister()
+    return n, t, cores
+
+
+def run_op(args, w) -> int:
+    """The rows of the method beyond the forward, measured like the forward:
+    per-step HIP events, cache flush between steps, roofline of the kernel
+    with the largest time, and the fp64 oracle on a bounded sample."""
+    import numpy as np
+    import torch
+    import dynamic_top_sparse_amd as sa
+    import oracle as O
+    from dynamic_top_sparse_amd import workloads as W
+
+    prof = sa.Profile()
+    x = W.make_inputs(w, W.default_seed())
+    g = {k: v.cuda() for k, v in x.items()}
+    B, H, N, D, dp, k = w.B, w.H, w.N, w.D, w.d_proj, w.k
+    e = 2 if w.dtype == "bf16" else 4
+    BH = B * H
+    op = args.op
+    extra = {}
+    if op == "bwd":
+        gen = torch.Generator().manual_seed(1)
+        dO = torch.randn(B, H, N, D, generator=gen).to(w.torch_dtype).cuda()
+        _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], k, w.causal,
+                                    return_idx=True)
+        n_ws = sa.load_library().sparse_attn_bwd_workspace_size(sa.sa_dims(B, H, N, D), dp, k, 1)
+        bws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        sum_k = float((idx >= 0).sum().item())
+
+        def step(p):
+            sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO, idx, g["Pq"], g["Pk"], workspace=bws,
+                               profile=p)
+        units = BH * N
+        metric = f"queries/s, top-k sparse attn backward (dQ, dK, dV, dPq, dPk), {w.name}"
+        # algorithmic bytes of the two wave passes (per launch: all heads)
+        amount = {
+            "bwd_rows": sum_k * (2 * D * e + 4 * dp + 12) + BH * N * (2 * D * e + 4 * k + 4 * D + 4 * dp),
+            "bwd_keys": sum_k * (12 + 2 * D * e + 4 * dp) + BH * N * (8 * D + 4 * dp + 8),
+        }
+        desc = {"bwd_rows": "K, V, k_low rows of kept keys + q, dO, idx rows + entries + dQ, dq_low",
+                "bwd_keys": "entries + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low"}
+        idx_np = idx.cpu().numpy()
+
+        def oracle_fn(rows):
+            Qh, Kh, Vh, dOh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"], dO.cpu()))
+            for i in rows:
+                O.attend_row_backward(Qh[i], Kh, Vh, idx_np[0, 0, i].astype(np.int64), D ** -0.5,
+                                      dOh[i])
+        sample_desc = "rows of head (0,0) through the oracle's per-row backward"
+    elif op == "decode":
+        cache = sa.DecodeCache(B, H, N, D, g["Pq"], g["Pk"], k, dtype=w.torch_dtype)
+        cache.append(g["K"], g["V"])
+        q = g["Q"][:, :, N - 1:N].contiguous()
+        o = torch.empty_like(q)
+
+        def step(p):
+            cache.step(q, O=o, profile=p)
+        units = BH
+        metric = f"decode queries/s (one query per head over a full KV cache), {w.name}"
+        amount = {"decode_scores": float(BH * N * (4 * dp + 4)),
+                  "decode_gather": float(BH * k * 2 * D * e + BH * (k * 4 + 2 * D * e))}
+        desc = {"decode_scores": "k_low cache rows (fp32) + scores",
+                "decode_gather": "K, V cache rows of the kept keys + idx + q, O"}
+
+        def oracle_fn(rows):
+            for _ in rows:
+                O.decode_step(x["Q"][0, 0, N - 1], x["K"][0, 0], x["V"][0, 0], x["Pq"], x["Pk"],
+                              k, N, dp ** -0.5, D ** -0.5)
+        sample_desc = "decode steps of head (0,0) through the oracle (one per sampled row)"
+    elif op == "block":
+        block, kb = 64, max(1, k // 64)
+        idx = torch.empty(B, H, N, kb * block, dtype=torch.int32, device="cuda")
+        n_ws = sa.load_library().sparse_attn_block_workspace_size(sa.sa_dims(B, H, N, D), dp,
+                                                                  block, kb)
+        bws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
+        out = torch.empty_like(g["Q"])
+
+        def step(p):
+            sa.sparse_attn_block_topk(g["Q"], g["K"], g["Pq"], g["Pk"], block, kb, w.causal,
+                                      idx=idx, workspace=bws, profile=p)
+            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out, profile=p)
+        units = BH * N
+        NB = (N + block - 1) // block
+        metric = f"queries/s, block-granular top-{kb} of {block}-key blocks + gather, {w.name}"
+        extra = {"block": block, "kb": kb}
+        amount = {"block_select": float(BH * N * NB * 2 * dp),
+                  "gather": float(BH * N * (kb * block * 2 * D * e + kb * block * 4 + 2 * D * e))}
+        desc = {"block_select": "2*d_proj flop per (query, block) score, fp32 FMA",
+                "gather": "K, V rows of the kept keys + idx + q, O"}
+
+        def oracle_fn(rows):
+            idx_r = O.block_topk_indices(x["Q"][:1, :1], x["K"][:1, :1], x["Pq"], x["Pk"], block,
+                                         kb, w.causal, dp ** -0.5, rows)
+            O.gather_attention(x["Q"][:1, :1], x["K"][:1, :1], x["V"][:1, :1], idx_r, D ** -0.5,
+                               rows)
+        sample_desc = "rows of head (0,0) through the oracle's block selection and gather"
+    elif op == "smooth":
+        gap = 0.02
+        idx = torch.empty(B, H, N, k + 1, dtype=torch.int32, device="cuda")
+        sws = sa.allocate_workspace(g["Q"], dp, k + 1, w.causal)
+        out = torch.empty_like(g["Q"])
+
+        def step(p):
+            sa.sparse_attn_scores_topk_smoothed(g["Q"], g["K"], g["Pq"], g["Pk"], k, gap,
+                                                w.causal, idx=idx, workspace=sws, profile=p)
+            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out, profile=p)
+        units = BH * N
+        metric = f"queries/s, top-{k} with boundary smoothing (gap {gap}) + gather, {w.name}"
+        extra = {"gap": gap}
+        amount = {"filter": float(2 * dp * (N * N if not w.causal else N * (N + 1) // 2) * BH),
+                  "gather": float(BH * N * ((k + 1) * 2 * D * e + (k + 1) * 4 + 2 * D * e))}
+        desc = {"filter": "2*d_proj flop per (query, key) pair", "gather": "K, V rows + idx + q, O"}
+
+        def oracle_fn(rows):
+            S = O.scores(x["Q"][:1, :1], x["K"][:1, :1], x["Pq"], x["Pk"], dp ** -0.5, 0, 0, rows)
+            idx_r = O.smoothed_topk_rows(S, rows, k, w.causal, gap)[None, None]
+            O.gather_attention(x["Q"][:1, :1], x["K"][:1, :1], x["V"][:1, :1], idx_r, D ** -0.5,
+                               rows)
+        sample_desc = "rows of head (0,0) through the oracle's smoothed top-k and gather"
+    else:   # dilated
+        window, dilation = 129, 4
+        idx = torch.empty(B, H, N, window, dtype=torch.int32, device="cuda")
+        out = torch.empty_like(g["Q"])
+
+        def step(p):
+            sa.sparse_attn_dilated_indices(B, H, N, window, dilation, window, idx=idx, profile=p)
+            sa.sparse_attn_gather(g["Q"], g["K"], g["V"], idx, O=out, profile=p)
+        units = BH * N
+        metric = f"queries/s, dilated window ({window} keys, dilation {dilation}) + gather, {w.name}"
+        extra = {"window": window, "dilation": dilation}
+        amount = {"gather": float(BH * N * (window * 2 * D * e + window * 4 + 2 * D * e))}
+        desc = {"gather": "K, V rows of the window + idx + q, O"}
+        didx = O.dilated_indices(N, window, dilation, window)
+
+        def oracle_fn(rows):
+            O.gather_attention(x["Q"][:1, :1], x["K"][:1, :1], x["V"][:1, :1],
+                               didx[rows][None, None], D ** -0.5, rows)
+        sample_desc = "rows of head (0,0) through the oracle's attention over the dilated window"
+
+    step_ms, wall_ms, recs = time_steps(step, prof, args.steps, args.warmup)
+    prof.close()
+    kern, per_step = kernel_table(recs, args.steps)
+    ms = float(np.median(step_ms))
+    dom = max((n for n in per_step if n in amount), key=per_step.get)
+    avg_s = kern[dom]["ms_total"] / kern[dom]["launches"] / 1e3
+    per_launch = amount[dom] / (kern[dom]["launches"] / args.steps)
+    if dom == "filter":
+        roof = {"kernel": dom, "bound": "mfma", "achieved": per_launch / avg_s / 1e12,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s"}
+    elif dom == "block_select":
+        roof = {"kernel": dom, "bound": "alu", "achieved": per_launch / avg_s / 1e12,
+                "peak": PEAK_FP32_TFLOPS, "unit": "TFLOP/s"}
+    else:
+        roof = {"kernel": dom, "bound": "hbm", "achieved": per_launch / avg_s / 1e9,
+                "peak": PEAK_HBM_GBS, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["algorithmic_per_launch"] = f"{per_launch:.4g} ({desc[dom]})"
+    roof["avg_launch_ms"] = avg_s * 1e3
+    result = {
+        "metric": metric, "value": units / (ms / 1e3), "unit": "queries/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "ms_per_step_min": step_ms[0], "ms_per_step_mean": float(np.mean(step_ms)),
+        "wall_ms_per_step_incl_flush": wall_ms,
+        "timing": ("median of per-step HIP events on the launch stream; a 512 MiB write "
+                   "between steps (outside the events) flushes L2 and the memory-side cache"),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {"workload": w.name, "op": op, "B": B, "H": H, "N": N, "D": D, "d_proj": dp,
+                   "k": k, "causal": w.causal, "dist": w.dist, "seed": W.default_seed(), **extra},
+        "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
+                                                                  key=lambda kv: -kv[1])},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        n, t, cores = oracle_rate(oracle_fn, N)
+        result["cpu_baseline"] = {
+            "value": n / t, "unit": "queries/s", "cores": cores, "kind": "oracle",
+            "mode": "extrapolated", "oracle_seconds": t,
+            "sample": f"{n} {sample_desc} of the {w.name} workload; {t:.1f} s"}
+    print(json.dumps(result))
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -199,6 +443,12 @@ def main() -> int:
                          "heads, 16, 8 whose workspace fits in a quarter of device memory)")
     ap.add_argument("--filter-dtype", choices=("f16", "bf16"), default="f16",
                     help="16-bit operand type of the MFMA filter (indices do not depend on it)")
+    ap.add_argument("--op", default="fwd",
+                    choices=("fwd", "bwd", "decode", "block", "smooth", "dilated"),
+                    help="fwd: the forward (default); bwd: the backward over the forward's index "
+                         "sets; decode: one decode step over a full KV cache; block: block-granular "
+                         "selection + gather; smooth: top-k with boundary smoothing + gather; "
+                         "dilated: dilated wrap-around window + gather")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB: the known-size "
@@ -220,6 +470,8 @@ def main() -> int:
     except KeyError:
         print(f"unknown workload {args.workload!r}; one of {sorted(W.WORKLOADS)}", file=sys.stderr)
         return 2
+    if args.op != "fwd":
+        return run_op(args, w)
     band = w.mode == "band"
     x = W.make_inputs(w, W.default_seed())
     g = {k: v.cuda() for k, v in x.items()}

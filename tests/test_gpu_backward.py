@@ -37,7 +37,7 @@ def test_backward_matches_oracle(N, k, D, dp, dtype, causal):
     w = W.Workload("bwd", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
     x = W.make_inputs(w, N + k)
     gen = torch.Generator().manual_seed(N)
-    dO = torch.randn(1, 2, N, D, generator=gen).to(w.torch_dtype)
+    dO = torch.randn(1, 2, N, D, generator=gen, dtype=torch.float32).to(w.torch_dtype)
     g = {n: t.cuda() for n, t in x.items()}
     idx = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], k, causal)
     sscale, ascale = sa.default_score_scale(dp), sa.default_softmax_scale(D)
@@ -61,7 +61,7 @@ def test_backward_list_semantics():
     nothing, keys no row kept get zero."""
     B, H, N, D, k = 1, 2, 600, 64, 12
     gen = torch.Generator().manual_seed(1)
-    Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen) for _ in range(4))
+    Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen, dtype=torch.float32) for _ in range(4))
     idx = torch.randint(-1, N // 2, (B, H, N, k), generator=gen, dtype=torch.int32)
     idx[0, 0, 5] = -1
     idx[0, 1, 7, :4] = 3
@@ -84,7 +84,7 @@ def test_backward_full_size_bf16_32k_sampled():
     w = W.get("bf16_32k")
     x = W.make_inputs(w, 0)
     gen = torch.Generator().manual_seed(2)
-    dO = torch.randn(w.B, w.H, w.N, w.D, generator=gen).to(torch.bfloat16)
+    dO = torch.randn(w.B, w.H, w.N, w.D, generator=gen, dtype=torch.float32).to(torch.bfloat16)
     g = {n: t.cuda() for n, t in x.items()}
     _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, return_idx=True)
     dQ, dK, dV = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False)

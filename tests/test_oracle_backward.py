@@ -20,8 +20,6 @@ import torch
 
 import oracle as O
 
-torch.set_default_dtype(torch.float64)
-
 
 def _inputs(B, H, N, D, dp, seed):
     g = np.random.default_rng(seed)
