@@ -41,7 +41,7 @@ EXPORTS = (
     "sparse_attn_band_indices_per_batch", "sparse_attn_decode_workspace_size",
     "sparse_attn_decode_append_keys", "sparse_attn_decode", "sparse_attn_block_workspace_size",
     "sparse_attn_block_topk", "sparse_attn_block_scores_dump", "sparse_attn_bwd_workspace_size",
-    "sparse_attn_bwd",
+    "sparse_attn_bwd", "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_decode_noalloc",
 )
 
 
@@ -109,6 +109,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                               f32, i32, vp, vp, vp, vp, sz, op, vp]),
         "sparse_attn_block_workspace_size": (sz, [sa_dims, i32, i32, i32]),
         "sparse_attn_bwd_workspace_size": (sz, [sa_dims, i32, i32, i32]),
+        "sparse_attn_decode_noalloc_max_bytes": (sz, []),
+        "sparse_attn_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32,
+                                                      f32, f32, i32, vp, vp, vp, vp]),
         "sparse_attn_bwd": (ctypes.c_int, [vp, vp, vp, vp, vp, vp, vp, sa_dims, i32, i32, f32, f32,
                                            i32, vp, vp, vp, vp, vp, vp, sz, op, vp]),
         "sparse_attn_block_topk": (ctypes.c_int, [vp, vp, vp, vp, sa_dims, i32, i32, i32, i32,
@@ -613,6 +616,33 @@ class DecodeCache:
         self.K[:, :, self.len:self.len + T] = K_new
         self.V[:, :, self.len:self.len + T] = V_new
         self.len += T
+
+    def step_noalloc(self, q, O: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                     count: bool = False, score_scale: Optional[float] = None,
+                     softmax_scale: Optional[float] = None):
+        """step() through sparse_attn_decode_noalloc: the library's own
+        device-resident workspace, no allocation (O must be given)."""
+        _tensor(q, "q")
+        if tuple(q.shape) != (self.B, self.H, 1, self.D) or q.dtype != self.dtype:
+            raise ValueError(f"q must be [B, H, 1, D] = {(self.B, self.H, 1, self.D)} "
+                             f"of {self.dtype}")
+        _like(O, q, "O", "q")
+        if idx is not None:
+            _tensor(idx, "idx")
+            if idx.dtype != torch.int32 or tuple(idx.shape) != (self.B, self.H, self.k):
+                raise ValueError(f"idx must be int32 [B, H, k] = {(self.B, self.H, self.k)}")
+        if self.len < 1:
+            raise ValueError("the cache is empty")
+        sscale = default_score_scale(self.d_proj) if score_scale is None else float(score_scale)
+        ascale = default_softmax_scale(self.D) if softmax_scale is None else float(softmax_scale)
+        st = load_library().sparse_attn_decode_noalloc(
+            _dev(q, "q"), _dev(self.K, "K"), _dev(self.V, "V"), _dev(self.klow, "klow"),
+            _dev(self.Pq, "Pq"), sa_dims(self.B, self.H, self.Ncap, self.D), self.d_proj,
+            self.len, self.k, sscale, ascale, _dtype_code(q), _dev(O, "O"),
+            None if idx is None else _dev(idx, "idx"),
+            _dev(self.counts, "counts") if count else None, _stream(q))
+        _check(st, "sparse_attn_decode_noalloc")
+        return (O, idx) if idx is not None else O
 
     def step(self, q, score_scale: Optional[float] = None,
              softmax_scale: Optional[float] = None, O: Optional[torch.Tensor] = None,

@@ -455,12 +455,13 @@ int sparse_attn_decode_append_keys(const void* K_new, const void* Pk, sa_dims d,
   return SA_OK;
 }
 
-int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
-                       const void* Pq, sa_dims d, int32_t d_proj, int32_t len, int32_t k,
-                       float score_scale, float softmax_scale, int32_t dtype, void* O,
-                       int32_t* idx_or_null, int32_t* counts_or_null, void* ws, size_t ws_bytes,
-                       const sa_options* opts, void* stream) {
-  if (!q || !Kc || !Vc || !klow_cache || !Pq || !O || !ws) return SA_ERR_NULL;
+namespace {
+// Argument checks shared by both decode entry points (the workspace aside).
+int check_decode_args(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
+                      const void* Pq, const sa_dims& d, int d_proj, int len, int k,
+                      float score_scale, float softmax_scale, int dtype, const void* O,
+                      const int32_t* idx_or_null, const int32_t* counts_or_null) {
+  if (!q || !Kc || !Vc || !klow_cache || !Pq || !O) return SA_ERR_NULL;
   int st = check_dims(d, k);
   if (st != SA_OK) return st;
   if (!supported_D(d.D) || !supported_dp(d_proj)) return SA_ERR_UNSUPPORTED;
@@ -469,12 +470,19 @@ int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const floa
   if (!(score_scale > 0.0f) || !std::isfinite(score_scale) || !std::isfinite(softmax_scale))
     return SA_ERR_SHAPE;
   if (!aligned16(q) || !aligned16(Kc) || !aligned16(Vc) || !aligned16(klow_cache) ||
-      !aligned16(Pq) || !aligned16(O) || !aligned16(ws))
+      !aligned16(Pq) || !aligned16(O))
     return SA_ERR_ALIGN;
   if ((idx_or_null && !aligned16(idx_or_null)) || (counts_or_null && !aligned16(counts_or_null)))
     return SA_ERR_ALIGN;
+  return SA_OK;
+}
+
+// The decode launches over a workspace laid out by decode_plan.
+int run_decode(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
+               const void* Pq, const sa_dims& d, int d_proj, int len, int k, float score_scale,
+               float softmax_scale, int dtype, void* O, int32_t* idx_or_null,
+               int32_t* counts_or_null, void* ws, sa_profile* prof, hipStream_t s) {
   const DecodePlan p = decode_plan(d, d_proj, k);
-  if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
   float* qlo32 = reinterpret_cast<float*>(base + p.off_qlo32);
   uint16_t* qlo16 = reinterpret_cast<uint16_t*>(base + p.off_qlo16);
@@ -482,8 +490,6 @@ int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const floa
   float* scores = reinterpret_cast<float*>(base + p.off_scores);
   int32_t* idx = idx_or_null ? idx_or_null : reinterpret_cast<int32_t*>(base + p.off_idx);
   const int BH = d.B * d.H;
-  sa_profile* prof = profile_of(opts);
-  hipStream_t s = static_cast<hipStream_t>(stream);
   SA_TIMED_STATUS("decode_project", launch_project_rows(q, Pq, BH, 1, 1, d.D, d_proj, dtype, 0,
                                                         qlo32, qlo16, qstat, s));
   SA_TIMED_STATUS("decode_scores", launch_decode_scores(qlo32, 1, klow_cache, d.N, len, BH,
@@ -493,6 +499,41 @@ int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const floa
   SA_TIMED_STATUS("decode_gather", launch_gather_rows(q, Kc, Vc, idx, k, BH, 1, d.N, d.D,
                                                       softmax_scale, dtype, O, s));
   return SA_OK;
+}
+}  // namespace
+
+size_t sparse_attn_decode_noalloc_max_bytes(void) { return decode_scratch_bytes(); }
+
+int sparse_attn_decode_noalloc(const void* q, const void* Kc, const void* Vc,
+                               const float* klow_cache, const void* Pq, sa_dims d,
+                               int32_t d_proj, int32_t len, int32_t k, float score_scale,
+                               float softmax_scale, int32_t dtype, void* O, int32_t* idx_or_null,
+                               int32_t* counts_or_null, void* stream) {
+  int st = check_decode_args(q, Kc, Vc, klow_cache, Pq, d, d_proj, len, k, score_scale,
+                             softmax_scale, dtype, O, idx_or_null, counts_or_null);
+  if (st != SA_OK) return st;
+  if (decode_plan(d, d_proj, k).total > decode_scratch_bytes()) return SA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (decode_scratch(&ws) != hipSuccess) return SA_ERR_HIP;
+  return run_decode(q, Kc, Vc, klow_cache, Pq, d, d_proj, len, k, score_scale, softmax_scale,
+                    dtype, O, idx_or_null, counts_or_null, ws, nullptr,
+                    static_cast<hipStream_t>(stream));
+}
+
+int sparse_attn_decode(const void* q, const void* Kc, const void* Vc, const float* klow_cache,
+                       const void* Pq, sa_dims d, int32_t d_proj, int32_t len, int32_t k,
+                       float score_scale, float softmax_scale, int32_t dtype, void* O,
+                       int32_t* idx_or_null, int32_t* counts_or_null, void* ws, size_t ws_bytes,
+                       const sa_options* opts, void* stream) {
+  int st = check_decode_args(q, Kc, Vc, klow_cache, Pq, d, d_proj, len, k, score_scale,
+                             softmax_scale, dtype, O, idx_or_null, counts_or_null);
+  if (st != SA_OK) return st;
+  if (!ws) return SA_ERR_NULL;
+  if (!aligned16(ws)) return SA_ERR_ALIGN;
+  if (ws_bytes < decode_plan(d, d_proj, k).total) return SA_ERR_WORKSPACE;
+  return run_decode(q, Kc, Vc, klow_cache, Pq, d, d_proj, len, k, score_scale, softmax_scale,
+                    dtype, O, idx_or_null, counts_or_null, ws, profile_of(opts),
+                    static_cast<hipStream_t>(stream));
 }
 
 // ---------------------------------------------- block-granular selection ---

@@ -16,9 +16,44 @@
 //   4. runs the gather attention over the selected K and V cache rows.
 // With the cache holding keys 0..len-1 of a sequence, the step's index row
 // is exactly the causal prefill's row len-1.
+#include <mutex>
+
 #include "sa_internal.h"
 
 namespace sa {
+
+// Device-resident workspace of sparse_attn_decode_noalloc, for callers that
+// cannot allocate (code under graph capture, tight serving loops).  Each GPU
+// the library runs on holds its own copy until the process ends; host code
+// reaches it only through the address hipGetSymbolAddress reports for the
+// current device (the array's name is not a device address on the host).
+constexpr size_t kDecodeScratchBytes = size_t(32) << 20;
+__device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+
+size_t decode_scratch_bytes() { return kDecodeScratchBytes; }
+
+// The current device's copy of `scratch`, looked up once per device.
+hipError_t decode_scratch(void** out) {
+  static std::atomic<void*> ptrs[kMaxDevices];
+  static std::mutex mu;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = ptrs[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lk(mu);
+    p = ptrs[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      ptrs[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 namespace {
 

@@ -190,6 +190,10 @@ hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klo
                                 hipStream_t s);
 hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
                                 int32_t* counts, int Ncap, hipStream_t s);
+// The no-allocation decode's device-resident workspace: its size, and its
+// address on the current device (looked up once per device).
+size_t decode_scratch_bytes();
+hipError_t decode_scratch(void** out);
 
 // Block-granular selection (block.hip): block means of k_low (kbar
 // [nh][NB][dp]), each query's kept blocks (sel [nh][N][kb], best first; none

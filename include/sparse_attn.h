@@ -272,6 +272,28 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
                                   void* stream);
 
 /*
+ * sparse_attn_decode without any allocation, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation).  Arguments and results are
+ * those of sparse_attn_decode; the workspace is instead a device-resident
+ * array inside the library, one per GPU, held until the process ends and
+ * found once per device (the first call on a device looks up its address).
+ * Its size is sparse_attn_decode_noalloc_max_bytes() (32 MiB); a call whose
+ * sparse_attn_decode_workspace_size exceeds it returns SA_ERR_WORKSPACE with
+ * nothing enqueued (B*H*Ncap*4 bytes of scores dominate: 32 heads of 128K
+ * keys fit).  The call allocates nothing and records no timing events.
+ * All calls on one GPU share that array: calls that overlap in time on one
+ * GPU (other streams, other threads) race and must be ordered by the
+ * caller.  Nothing in the array needs to start at zero.
+ */
+size_t sparse_attn_decode_noalloc_max_bytes(void);
+int sparse_attn_decode_noalloc(const void* q, const void* Kc, const void* Vc,
+                               const float* klow_cache, const void* Pq, sa_dims d,
+                               int32_t d_proj, int32_t len, int32_t k, float score_scale,
+                               float softmax_scale, int32_t dtype, void* O, int32_t* idx_or_null,
+                               int32_t* counts_or_null, void* stream);
+
+/*
  * Index variants feeding sparse_attn_gather.
  *
  * Boundary smoothing of the top-k (page "mhpq.cn/news/1098205", §4.2: when
