@@ -60,6 +60,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int kScoreUnroll = 8;   // key loads in flight per lane
+constexpr int kSelThreads = 1024; // the select kernel: one big workgroup per head
+constexpr int kSelWaves = kSelThreads / kWave;
 
 template <int DP>
 __global__ __launch_bounds__(kThreads) void decode_score_kernel(
@@ -97,7 +99,7 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
   if (l == kWave - 1) tmp[w] = incl;
   __syncthreads();
   int off = 0, tot = 0;
-  for (int i = 0; i < kWaves; ++i) {
+  for (int i = 0; i < kSelWaves; ++i) {
     const int t = tmp[i];
     if (i < w) off += t;
     tot += t;
@@ -107,33 +109,39 @@ __device__ __forceinline__ int block_excl_scan(int v, int* tmp, int& total) {
   return off + incl - v;
 }
 
-// One workgroup per head: the k_i-th largest order key by a radix select
-// (four 8-bit digits), then the keys above it and the lowest-index ties, in
-// ascending key order.
-__global__ __launch_bounds__(kThreads) void decode_select_kernel(
+// One workgroup of 1024 threads per head: the k_i-th largest order key by a
+// radix select (four 8-bit digits; each wave counts into its own LDS
+// histogram, so the LDS atomics of different waves never meet), then the
+// keys above it and the lowest-index ties, in ascending key order.
+__global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     const float* __restrict__ scores, int len, int k, int32_t* __restrict__ idx,
     int32_t* __restrict__ counts, int Ncap) {
-  __shared__ int hist[256];
-  __shared__ int tmp[kWaves];
+  __shared__ int hist[kSelWaves][256];
+  __shared__ int tmp[kSelWaves];
   __shared__ int s_digit, s_above;
   const int tid = threadIdx.x;
+  const int wv = tid / kWave;
   const int h = blockIdx.x;
   const float* row = scores + static_cast<size_t>(h) * Ncap;
   const int k_i = min(k, len);
   uint32_t prefix = 0, pmask = 0;
   int K = k_i;
   for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
+    for (int b = tid; b < kSelWaves * 256; b += kSelThreads) (&hist[0][0])[b] = 0;
     __syncthreads();
-    for (int j = tid; j < len; j += kThreads) {
+    for (int j = tid; j < len; j += kSelThreads) {
       const uint32_t key = order_key(row[j]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255], 1);
+      if ((key & pmask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 255], 1);
     }
     __syncthreads();
-    const int cval = hist[255 - tid];   // thread t owns bin 255 - t
+    // thread t < 256 owns bin 255 - t (the sum of the waves' counts)
+    int cval = 0;
+    if (tid < 256) {
+      for (int v = 0; v < kSelWaves; ++v) cval += hist[v][255 - tid];
+    }
     int total;
     const int excl = block_excl_scan(cval, tmp, total);
-    if (excl < K && excl + cval >= K) {
+    if (tid < 256 && excl < K && excl + cval >= K) {
       s_digit = 255 - tid;
       s_above = excl;
     }
@@ -145,7 +153,7 @@ __global__ __launch_bounds__(kThreads) void decode_select_kernel(
   }
   // each thread owns a contiguous range of keys: two block scans give every
   // thread its first output position
-  const int L = (len + kThreads - 1) / kThreads;
+  const int L = (len + kSelThreads - 1) / kSelThreads;
   const int j0 = min(len, tid * L), j1 = min(len, j0 + L);
   int gt = 0, eq = 0;
   for (int j = j0; j < j1; ++j) {
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void decode_select_kernel(
     }
     eq_seen += tie ? 1 : 0;
   }
-  for (int t = k_i + tid; t < k; t += kThreads) out[t] = -1;
+  for (int t = k_i + tid; t < k; t += kSelThreads) out[t] = -1;
 }
 
 template <int DP>
@@ -200,7 +208,7 @@ hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klo
 
 hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
                                 int32_t* counts, int Ncap, hipStream_t s) {
-  hipLaunchKernelGGL(decode_select_kernel, dim3(nh), dim3(kThreads), 0, s, scores, len, k, idx,
+  hipLaunchKernelGGL(decode_select_kernel, dim3(nh), dim3(kSelThreads), 0, s, scores, len, k, idx,
                      counts, Ncap);
   return hipGetLastError();
 }

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // Statistics are kept per wave and added to the header once at the end:
   // one device-scope atomic per query on a shared word would serialise.
   unsigned long long st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
-  unsigned st_viol = 0;
+  unsigned viol = 0;   // per lane: re-scored keys outside their margin interval
   // first pass: every query; retry pass: the queries listed for this head
   const int nq = qlist != nullptr ? qlist_count[h] : N;
   // Software pipeline over the wave's queries: while query i is ranked, the
@@ -471,6 +471,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
                                  __uint_as_float(kstat[kKeyStatWords * h + 1]), scale, DP);
     auto lower = [&](float x) { return (x - m) - (fabsf(x) + m) * (1.0f / 4194304.0f); };
     auto upper = [&](float x) { return (x + m) + (fabsf(x) + m) * (1.0f / 4194304.0f); };
+    // |s - s~| bound of the same interval: m + (|s~| + m) 2^-22
+    const float mslop = m + m * (1.0f / 4194304.0f);
     const uint32_t ak = wave_select_in<uint32_t>(k_i, hist, reinterpret_cast<uint32_t*>(cbuf),
                                                  each_cand, kmin, kmax);
     const float lo = lower(key_to_float(ak));
@@ -543,16 +545,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         for (int t = 0; t < UNR; ++t) {
           const float p = group_sum<G>(group_partial<DP>(qv, kv[t]));
           const int u = u0 + t * KPI + grp;
-          bool outside = false;
           if (g == 0 && u < nU) {
             const float sx = p * scale;
             us[u] = sx;
             // the exact score must lie in the interval the margin gives the
-            // filter score; a key outside it means the bound is wrong
+            // filter score (the bounds lower/upper use); a key outside it
+            // means the rounding bound behind the margin is wrong
             const float sf = ut[u];
-            outside = sx < lower(sf) || sx > upper(sf);
+            viol += fabsf(sx - sf) > __builtin_fmaf(fabsf(sf), 1.0f / 4194304.0f, mslop) ? 1u : 0u;
           }
-          st_viol += static_cast<unsigned>(__builtin_popcountll(__ballot(outside)));
         }
       }
     }
@@ -605,6 +606,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     cur = nxt;
     nxt = nn;
   }
+  const unsigned st_viol = static_cast<unsigned>(wave_sum_i(static_cast<int>(viol)));
   if (l == 0) {
     if (st_queries) atomicAdd(&hdr->queries, st_queries);
     if (st_rescored) atomicAdd(&hdr->rescored, st_rescored);

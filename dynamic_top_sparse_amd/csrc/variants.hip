@@ -91,16 +91,36 @@ __global__ __launch_bounds__(kThreads) void smooth_kernel(const float* __restric
   const size_t hq = static_cast<size_t>(h) * Npad;
   int32_t* row = idx + (static_cast<size_t>(h) * N + q) * k1;
   const float* qrow = q32 + (hq + q) * DP;
-  // the two smallest rank keys of the row (worst first)
+  // Exact scores of the row's keys, G lanes per key holding four
+  // coordinates each (group_sum adds their partials in exact_score's fixed
+  // order, so the values are those of the dump); lane 0 of each group keeps
+  // the two smallest rank keys it has seen (worst first).
+  constexpr int G = DP / 4, KPI = kWave / G, U = 8;
+  const int g = l % G, grp = l / G;
+  const float4 qv = reinterpret_cast<const float4*>(qrow)[g];
   unsigned long long m1 = ~0ull, m2 = ~0ull;
-  for (int t = l; t < k1; t += kWave) {
-    const int j = row[t];
-    const unsigned long long r = smooth_rank(exact_score<DP>(qrow, k32 + (hq + j) * DP, scale), j);
-    if (r < m1) {
-      m2 = m1;
-      m1 = r;
-    } else if (r < m2) {
-      m2 = r;
+  for (int t0 = 0; t0 < k1; t0 += KPI * U) {
+    float4 kv[U];
+    int jj[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int t = t0 + u * KPI + grp;
+      jj[u] = t < k1 ? row[t] : -1;
+      kv[u] = jj[u] >= 0 ? reinterpret_cast<const float4*>(k32 + (hq + jj[u]) * DP)[g]
+                         : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float p = group_sum<G>(group_partial<DP>(qv, kv[u]));
+      if (g == 0 && jj[u] >= 0) {
+        const unsigned long long r = smooth_rank(p * scale, jj[u]);
+        if (r < m1) {
+          m2 = m1;
+          m1 = r;
+        } else if (r < m2) {
+          m2 = r;
+        }
+      }
     }
   }
   const unsigned long long w1 = wave_min64(m1);
