@@ -51,18 +51,26 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 120.957e9, "write_bytes": 93.378e9,
+    "filter": {"fetch_bytes": 112.891e9, "write_bytes": 93.508e9,
                "src": "c2fd4f618ca754cb8861533b8c8a12713eb99adaa6da0ee9097139d27472aa58"},
     "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
-               "src": "5877c0c9b38d66bf2db13d14434eb11b76d2099e41d909161337876ede489689"},
-    "rerank": {"fetch_bytes": 69.471e9, "write_bytes": 10.888e9,
-               "src": "f4407d799910cd43fb4a75b18a8fca50eec3133ed9f1aa1a0616b23d5c45d73e"},
+               "src": "00525acd8123ea03ed580e6df67740df22f2ca9cee064c51d23760c6e6f26175"},
+    "rerank": {"fetch_bytes": 69.485e9, "write_bytes": 10.889e9,
+               "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
 
 # rocprofv3 --pmc readings of the filter's MFMA activity on the headline
-# command (see profiles/), with the sha256 of scorer.hip when taken.
-MFMA_COUNTERS: dict = {}
+# command (profiles/filter_128k_mfma_counters.md), with the sha256 of
+# scorer.hip when taken.  mfma_busy_frac = SQ_VALU_MFMA_BUSY_CYCLES over
+# (1024 SIMDs x GRBM_GUI_ACTIVE per XCD); shader_clock_ghz = the cycles per
+# XCD over the dispatch's duration.
+MFMA_COUNTERS: dict = {
+    "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
+               "GRBM_GUI_ACTIVE_all_xcds": 1337055068, "dispatch_ms": 92.64,
+               "mfma_busy_frac": 0.4015, "shader_clock_ghz": 1.804,
+               "src": "c2fd4f618ca754cb8861533b8c8a12713eb99adaa6da0ee9097139d27472aa58"},
+}
 
 
 def source_sha(kernel: str):
@@ -290,9 +298,10 @@ def run_op(args, w) -> int:
         desc = {"bwd_rows": "K, V, k_low rows of kept keys + q, dO, idx rows + entries + dQ, dq_low",
                 "bwd_keys": "entries + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low"}
         idx_np = idx.cpu().numpy()
+        # the head's rows as the oracle takes them, converted once outside the timing
+        Qh, Kh, Vh, dOh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"], dO[0, 0].cpu()))
 
         def oracle_fn(rows):
-            Qh, Kh, Vh, dOh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"], dO.cpu()))
             for i in rows:
                 O.attend_row_backward(Qh[i], Kh, Vh, idx_np[0, 0, i].astype(np.int64), D ** -0.5,
                                       dOh[i])
@@ -308,8 +317,11 @@ def run_op(args, w) -> int:
         units = BH
         metric = f"decode queries/s (one query per head over a full KV cache), {w.name}"
         amount = {"decode_scores": float(BH * N * (4 * dp + 4)),
+                  # four digit passes, the count pass and the output pass over the scores
+                  "decode_select": float(BH * N * 4 * 6),
                   "decode_gather": float(BH * k * 2 * D * e + BH * (k * 4 + 2 * D * e))}
         desc = {"decode_scores": "k_low cache rows (fp32) + scores",
+                "decode_select": "six reads of each head's fp32 scores (L2-resident)",
                 "decode_gather": "K, V cache rows of the kept keys + idx + q, O"}
 
         def oracle_fn(rows):
