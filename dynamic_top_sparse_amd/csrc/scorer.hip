@@ -615,7 +615,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         count[0] += __builtin_popcount(bits0);
       else
         drain_hits(a0, bits0, stash, jenc, lbase[0], loff[0], count[0], last[0]);
-      if (tt + 1 < ntiles) a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
+      if (tt + 1 < ntiles) {
+        a0 = tile_scores_c<DP, F>(buf, tt + 1, b0, cinit[0]);
+      } else if constexpr (mode == 1) {
+        // The hardware does not hold back a VALU read of VGPRs an MFMA is
+        // still writing.  On a chunk's last tile no chain runs here, and in
+        // the counting pass block 0's handling is a popcount, so little
+        // would separate a1's last MFMA from its first read below: pad 16
+        // wait states (12 are needed after a 32x32x16 MFMA on gfx950).
+        // tests/test_mfma_hazards.py checks every path of the built code.
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_nop 7\n\ts_nop 7" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
       unsigned bits1 = (~miss_bits(a1) & 0xFFFFu) | apm[1];
       if (edge)
         bits1 = mask_edge_rows(a1, bits1, valid_rows((causal ? min(N - 1, qq[1]) : N - 1) -
