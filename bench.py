@@ -299,7 +299,8 @@ def run_op(args, w) -> int:
                 "bwd_keys": "entries + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low"}
         idx_np = idx.cpu().numpy()
         # the head's rows as the oracle takes them, converted once outside the timing
-        Qh, Kh, Vh, dOh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"], dO[0, 0].cpu()))
+        Qh, Kh, Vh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"]))
+        dOh = O.f64(dO[0, 0].cpu())
 
         def oracle_fn(rows):
             for i in rows:

@@ -657,7 +657,7 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
 // ----------------------------------------------------------- backward ---
 namespace {
 struct BwdPlan {
-  size_t off_q32, off_k32, off_dql, off_dkl, off_cnt, off_off, off_cur, off_ei, off_ep, off_ed,
+  size_t off_q32, off_k32, off_dql, off_dkl, off_cnt, off_off, off_cnts, off_ent, off_epd,
       off_part, total;
   int nchunks;
 };
@@ -678,10 +678,9 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
   p.off_dkl = take(lo);
   p.off_cnt = take(BH * N * 4);
   p.off_off = take(BH * N * 4);
-  p.off_cur = take(BH * N * 4);
-  p.off_ei = take(ents * 4);
-  p.off_ep = take(ents * 4);
-  p.off_ed = take(ents * 4);
+  p.off_cnts = take(static_cast<size_t>(bwd_slices(d.N, k)) * BH * N * 4);
+  p.off_ent = take(ents * 4);
+  p.off_epd = take(ents * 8);
   p.nchunks = scorer ? outer_sum_chunks(static_cast<long long>(BH * N)) : 0;
   p.off_part = take(scorer ? static_cast<size_t>(p.nchunks) * d.D * dp * 4 * 2 : 0);
   p.total = off;
@@ -724,7 +723,8 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   float* dkl = reinterpret_cast<float*>(base + p.off_dkl);
   int* cnt = reinterpret_cast<int*>(base + p.off_cnt);
   int* offs = reinterpret_cast<int*>(base + p.off_off);
-  int* cur = reinterpret_cast<int*>(base + p.off_cur);
+  int* cnts = reinterpret_cast<int*>(base + p.off_cnts);
+  int* ent = reinterpret_cast<int*>(base + p.off_ent);
   BwdArgs a{};
   a.dtype = dtype;
   a.D = d.D;
@@ -737,10 +737,8 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.idx = idx;
   a.q32 = q32; a.k32 = k32;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.dqlow = dql; a.dklow = dkl;
-  a.cursor = cur; a.seg_off = offs; a.seg_cnt = cnt;
-  a.ent_i = reinterpret_cast<int*>(base + p.off_ei);
-  a.ent_p = reinterpret_cast<float*>(base + p.off_ep);
-  a.ent_d = reinterpret_cast<float*>(base + p.off_ed);
+  a.seg_off = offs; a.seg_cnt = cnt; a.ent = ent;
+  a.epd = reinterpret_cast<float2*>(base + p.off_epd);
   const long long rows = static_cast<long long>(a.nh) * d.N;
   sa_profile* prof = profile_of(opts);
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -750,9 +748,10 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
     SA_TIMED_STATUS("bwd_project", launch_project_rows(K, Pk, a.nh, d.N, d.N, d.D, d_proj, dtype,
                                                        1, k32, nullptr, nullptr, s));
   }
-  SA_TIMED_STATUS("bwd_count", launch_fill_zero(cnt, align_up(static_cast<size_t>(rows) * 4), s));
-  SA_TIMED_STATUS("bwd_count", launch_bwd_count(idx, a.nh, d.N, k, cnt, s));
-  SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, cur, s));
+  SA_TIMED_STATUS("bwd_count", launch_bwd_hist(idx, a.nh, d.N, k, cnts, s));
+  SA_TIMED_STATUS("bwd_scan", launch_bwd_slice_prefix(cnts, bwd_slices(d.N, k), rows, cnt, s));
+  SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, s));
+  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.nh, d.N, k, cnts, offs, ent, s));
   a.pass = 0;
   SA_TIMED_STATUS("bwd_rows", launch_bwd_pass(a, s));
   a.pass = 1;

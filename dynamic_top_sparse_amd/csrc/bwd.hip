@@ -1,7 +1,16 @@
 // Helpers of the backward (page "mhpq.cn/news/1098205", §2.3, gradients of
-// the top-k attention): the key segments of the entry list (how many rows
-// kept each key, then where each key's entries start), and the scorer's
+// the top-k attention): the key segments of the entry list, and the scorer's
 // projection gradients.
+//
+// Key segments (a counting sort of idx's entries by key, per head): the
+// rows are cut into S slices and the keys into windows of kHistWindow; one
+// workgroup per (head, slice, window) counts its keys in an LDS histogram.
+// The counts are added up over slices (each slice keeps its running prefix),
+// scanned over keys into each key's segment start, and a second pass with
+// the same grid places every entry (its index i*k + t within the head) at
+// its slice's next free position of its key's segment, again through LDS
+// counters.  No global atomics; the order of entries within one slice's part
+// of a segment is the order of the LDS atomics.
 //
 // Scorer: with q_low = Q·Pq and k_low = K·Pk, the straight-through gradient
 // reaches dq_low and dk_low (the two passes in gather.hip); then
@@ -9,6 +18,8 @@
 //   dPq = sum over every row of Qᵀ·dq_low, dPk likewise  (outer_sum: fixed
 //   row chunks, then the chunks' partial sums added in chunk order, so the
 //   result does not depend on scheduling).
+#include <algorithm>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -19,32 +30,115 @@ constexpr int kThreads = 256;
 constexpr int kOuterRows = 4096;    // rows per outer-sum chunk
 constexpr int kStageRows = 32;      // rows staged in LDS at a time
 
-__global__ void fill_zero_kernel(uint4* __restrict__ p, size_t n16) {
-  for (size_t i = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x; i < n16;
-       i += static_cast<size_t>(gridDim.x) * blockDim.x)
-    p[i] = make_uint4(0, 0, 0, 0);
+constexpr int kHistThreads = 1024;
+constexpr int kHistWindow = 32768;  // keys per window: 128 KB of LDS counters
+
+// Calls fn(g, idx[g]) for the entries g in [a, b) of the 16-byte aligned
+// array idx, spread over the workgroup: 16-byte loads on the aligned
+// interior, single entries at the two ends.
+template <typename Fn>
+__device__ __forceinline__ void for_entries(const int32_t* __restrict__ idx, long long a,
+                                            long long b, Fn fn) {
+  const long long a4 = min(b, (a + 3) & ~3LL);
+  const long long b4 = max(a4, b & ~3LL);
+  const int tid = threadIdx.x;
+  if (tid < a4 - a) fn(a + tid, idx[a + tid]);
+  if (tid < b - b4) fn(b4 + tid, idx[b4 + tid]);
+  const int4* v = reinterpret_cast<const int4*>(idx);
+  for (long long q = a4 / 4 + tid; q < b4 / 4; q += kHistThreads) {
+    const int4 x = v[q];
+    fn(4 * q, x.x);
+    fn(4 * q + 1, x.y);
+    fn(4 * q + 2, x.z);
+    fn(4 * q + 3, x.w);
+  }
 }
 
-__global__ void bwd_count_kernel(const int32_t* __restrict__ idx, long long total, int N, int k,
-                                 int* __restrict__ cnt) {
-  for (long long e = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; e < total;
-       e += static_cast<long long>(gridDim.x) * blockDim.x) {
-    const int j = idx[e];
-    const long long h = e / (static_cast<long long>(N) * k);
-    if (j >= 0 && j < N) atomicAdd(&cnt[h * N + j], 1);
+struct SliceWindow {
+  int s, w0, W, i0, i1;
+};
+
+__device__ __forceinline__ SliceWindow slice_window(int N, int S, int rows_per_slice) {
+  SliceWindow r;
+  r.s = static_cast<int>(blockIdx.x) % S;
+  r.w0 = static_cast<int>(blockIdx.x) / S * kHistWindow;
+  r.W = min(kHistWindow, N - r.w0);
+  r.i0 = min(N, r.s * rows_per_slice);
+  r.i1 = min(N, r.i0 + rows_per_slice);
+  return r;
+}
+
+// cnt_s[s][h][j] = entries of key j in the rows of slice s (keys outside
+// 0..N-1, -1 included, are skipped).
+__global__ __launch_bounds__(kHistThreads) void bwd_hist_kernel(const int32_t* __restrict__ idx,
+                                                                int N, int k, int S,
+                                                                int rows_per_slice, int nh,
+                                                                int* __restrict__ cnt_s) {
+  extern __shared__ int hist[];
+  const SliceWindow sw = slice_window(N, S, rows_per_slice);
+  const int h = blockIdx.y;
+  for (int t = threadIdx.x; t < sw.W; t += kHistThreads) hist[t] = 0;
+  __syncthreads();
+  const long long hk = static_cast<long long>(h) * N * k;
+  const unsigned w0 = static_cast<unsigned>(sw.w0), W = static_cast<unsigned>(sw.W);
+  for_entries(idx, hk + static_cast<long long>(sw.i0) * k, hk + static_cast<long long>(sw.i1) * k,
+              [&](long long, int j) {
+                const unsigned u = static_cast<unsigned>(j) - w0;
+                if (u < W) atomicAdd(&hist[u], 1);
+              });
+  __syncthreads();
+  int* out = cnt_s + (static_cast<size_t>(sw.s) * nh + h) * N + sw.w0;
+  for (int t = threadIdx.x; t < sw.W; t += kHistThreads) out[t] = hist[t];
+}
+
+// Per key: the total over slices into cnt, and each slice's count replaced by
+// the sum of the earlier slices' counts.
+__global__ void bwd_slice_prefix_kernel(int* __restrict__ cnt_s, int S, long long total,
+                                        int* __restrict__ cnt) {
+  for (long long x = blockIdx.x * static_cast<long long>(blockDim.x) + threadIdx.x; x < total;
+       x += static_cast<long long>(gridDim.x) * blockDim.x) {
+    int run = 0;
+    for (int s = 0; s < S; ++s) {
+      const int v = cnt_s[s * total + x];
+      cnt_s[s * total + x] = run;
+      run += v;
+    }
+    cnt[x] = run;
   }
+}
+
+// Places the entries of one (head, slice, window) in their key segments.
+__global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* __restrict__ idx,
+                                                                int N, int k, int S,
+                                                                int rows_per_slice, int nh,
+                                                                const int* __restrict__ cnt_s,
+                                                                const int* __restrict__ off,
+                                                                int* __restrict__ ent) {
+  extern __shared__ int cur[];
+  const SliceWindow sw = slice_window(N, S, rows_per_slice);
+  const int h = blockIdx.y;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const int* before = cnt_s + (static_cast<size_t>(sw.s) * nh + h) * N + sw.w0;
+  for (int t = threadIdx.x; t < sw.W; t += kHistThreads) cur[t] = off[hN + sw.w0 + t] + before[t];
+  __syncthreads();
+  const long long hk = static_cast<long long>(h) * N * k;
+  int* eh = ent + hk;
+  const unsigned w0 = static_cast<unsigned>(sw.w0), W = static_cast<unsigned>(sw.W);
+  for_entries(idx, hk + static_cast<long long>(sw.i0) * k, hk + static_cast<long long>(sw.i1) * k,
+              [&](long long g, int j) {
+                const unsigned u = static_cast<unsigned>(j) - w0;
+                if (u < W) eh[atomicAdd(&cur[u], 1)] = static_cast<int>(g - hk);
+              });
 }
 
 // One workgroup per head: exclusive scan of the counts, i.e. each key's
 // first entry within the head's region of the entry list.
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restrict__ cnt, int N,
-                                                            int* __restrict__ off,
-                                                            int* __restrict__ cursor) {
+                                                            int* __restrict__ off) {
   __shared__ int tmp[kThreads / kWave];
   const int h = blockIdx.x;
   const int* c = cnt + static_cast<size_t>(h) * N;
   int* o = off + static_cast<size_t>(h) * N;
-  int* cu = cursor + static_cast<size_t>(h) * N;
   const int w = threadIdx.x / kWave, l = lane_id();
   int running = 0;
   for (int b0 = 0; b0 < N; b0 += kThreads) {
@@ -58,11 +152,7 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restric
       before += i < w ? tmp[i] : 0;
       tot += tmp[i];
     }
-    if (j < N) {
-      const int x = running + before + incl - v;
-      o[j] = x;
-      cu[j] = x;
-    }
+    if (j < N) o[j] = running + before + incl - v;
     running += tot;
     __syncthreads();
   }
@@ -183,23 +273,59 @@ hipError_t outer_d(const void* X, const float* lo, long long rows, int dp, float
 
 }  // namespace
 
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
-  const size_t n16 = bytes / 16;    // callers pass multiples of 16 bytes
-  hipLaunchKernelGGL(fill_zero_kernel, dim3(grid_for(static_cast<long long>(n16))), dim3(kThreads),
-                     0, s, static_cast<uint4*>(p), n16);
+int bwd_slices(int N, int k) {
+  const long long e = static_cast<long long>(N) * k;
+  return static_cast<int>(std::min<long long>(16, std::max<long long>(1, e >> 20)));
+}
+
+namespace {
+struct HistGrid {
+  dim3 grid;
+  int S, rows_per_slice;
+  size_t lds;
+};
+HistGrid hist_grid(int nh, int N, int k) {
+  HistGrid g;
+  g.S = bwd_slices(N, k);
+  g.rows_per_slice = (N + g.S - 1) / g.S;
+  const int nwin = (N + kHistWindow - 1) / kHistWindow;
+  g.grid = dim3(g.S * nwin, nh);
+  g.lds = static_cast<size_t>(std::min(N, kHistWindow)) * 4;
+  return g;
+}
+}  // namespace
+
+hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int* cnt_s, hipStream_t s) {
+  static std::atomic<int> lds_set[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_hist_kernel),
+                                    kHistWindow * 4, lds_set);
+  if (e != hipSuccess) return e;
+  const HistGrid g = hist_grid(nh, N, k);
+  hipLaunchKernelGGL(bwd_hist_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, N, k, g.S,
+                     g.rows_per_slice, nh, cnt_s);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_count(const int32_t* idx, int nh, int N, int k, int* cnt, hipStream_t s) {
-  const long long total = static_cast<long long>(nh) * N * k;
-  hipLaunchKernelGGL(bwd_count_kernel, dim3(grid_for(total)), dim3(kThreads), 0, s, idx, total, N,
-                     k, cnt);
+hipError_t launch_bwd_slice_prefix(int* cnt_s, int S, long long total, int* cnt, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_slice_prefix_kernel, dim3(grid_for(total)), dim3(kThreads), 0, s, cnt_s,
+                     S, total, cnt);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, int* cursor,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(bwd_scan_kernel, dim3(nh), dim3(kThreads), 0, s, cnt, N, off, cursor);
+hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_scan_kernel, dim3(nh), dim3(kThreads), 0, s, cnt, N, off);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fill(const int32_t* idx, int nh, int N, int k, const int* cnt_s,
+                           const int* off, int* ent, hipStream_t s) {
+  static std::atomic<int> lds_set[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_fill_kernel),
+                                    kHistWindow * 4, lds_set);
+  if (e != hipSuccess) return e;
+  const HistGrid g = hist_grid(nh, N, k);
+  hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, N, k, g.S,
+                     g.rows_per_slice, nh, cnt_s, off, ent);
   return hipGetLastError();
 }
 

@@ -663,8 +663,7 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const int32_t* __restrict__ idx, int k, int N, float scale,
     float sscale, const float* __restrict__ k32, float* __restrict__ dQ,
-    float* __restrict__ dqlow, int* __restrict__ cursor, int* __restrict__ ent_i,
-    float* __restrict__ ent_p, float* __restrict__ ent_d) {
+    float* __restrict__ dqlow, float2* __restrict__ epd) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -690,6 +689,8 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   float acc[EPL];
   if (mx == -INFINITY) {    // no valid entry: no gradient from this row
+    float2* er = epd + (hN + q) * static_cast<size_t>(k);
+    for (int t = l; t < k; t += kWave) er[t] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
     if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
@@ -720,25 +721,18 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     weighted_rows<float, DP>(k32 + hN * DP, sidx, 0, k, N, sd, a4);
     if (l < DP / 4) store_f32_row<4>(dqlow + (hN + q) * DP + 4 * l, a4, sscale);
   }
-  // the entries for the key pass, in the head's region of N*k entries
-  const size_t ebase = hN * static_cast<size_t>(k);
-  for (int t = l; t < k; t += kWave) {
-    const int j = sidx[t];
-    if (j >= 0 && j < N) {
-      const size_t pos = ebase + static_cast<unsigned>(atomicAdd(&cursor[hN + j], 1));
-      ent_i[pos] = q;
-      ent_p[pos] = sl[t];
-      ent_d[pos] = sd[t];
-    }
-  }
+  // (p_t, dl_t) for the key pass, in idx's layout (entries that name no key
+  // hold p_t = 0 and are never read)
+  float2* er = epd + (hN + q) * static_cast<size_t>(k);
+  for (int t = l; t < k; t += kWave) er[t] = make_float2(sl[t], sd[t]);
 }
 
 template <typename T, int D, int DP>
 __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const T* __restrict__ Q, const T* __restrict__ dO, const float* __restrict__ q32,
     const int* __restrict__ seg_off, const int* __restrict__ seg_cnt,
-    const int* __restrict__ ent_i, const float* __restrict__ ent_p,
-    const float* __restrict__ ent_d, int N, int k, float scale, float sscale,
+    const int* __restrict__ ent, const float2* __restrict__ epd, int N, int k, float scale,
+    float sscale,
     float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ dklow) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
@@ -754,8 +748,10 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
   const size_t hN = static_cast<size_t>(h) * N;
   const T* Qh = Q + hN * D;
   const T* dOh = dO + hN * D;
-  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[hN + j]);
+  const size_t hk = hN * static_cast<size_t>(k);
+  const size_t o0 = hk + static_cast<unsigned>(seg_off[hN + j]);
   const int n = seg_cnt[hN + j];
+  const unsigned uk = static_cast<unsigned>(k);
   float av[EPL], ak[EPL], al[4];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
@@ -764,9 +760,11 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
   for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
     const int m = min(kBwdChunk, n - c0);
     for (int t = l; t < m; t += kWave) {
-      sidx[t] = ent_i[o0 + c0 + t];
-      sp[t] = ent_p[o0 + c0 + t];
-      sd[t] = ent_d[o0 + c0 + t];
+      const unsigned e = static_cast<unsigned>(ent[o0 + c0 + t]);   // i*k + t of the entry
+      const float2 pd = epd[hk + e];
+      sidx[t] = static_cast<int>(e / uk);
+      sp[t] = pd.x;
+      sd[t] = pd.y;
     }
     wave_sync();
     float tmp[EPL];
@@ -809,12 +807,12 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
                        kWaves * bwd_row_wave_floats(a.k) * 4, s, static_cast<const T*>(a.Q),
                        static_cast<const T*>(a.K), static_cast<const T*>(a.V),
                        static_cast<const T*>(a.dO), a.idx, a.k, a.N, a.scale, a.sscale, a.k32,
-                       a.dQ, a.dqlow, a.cursor, a.ent_i, a.ent_p, a.ent_d);
+                       a.dQ, a.dqlow, a.epd);
   } else {
     hipLaunchKernelGGL((bwd_keys_kernel<T, D, DP>), grid, dim3(kThreads),
                        kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.ent_i,
-                       a.ent_p, a.ent_d, a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
+                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.ent,
+                       a.epd, a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
   }
   return hipGetLastError();
 }

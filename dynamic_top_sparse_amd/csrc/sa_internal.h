@@ -217,16 +217,20 @@ struct BwdArgs {
   const int32_t* idx;
   const float *q32, *k32;       // fp32 projections (scorer gradient only)
   float *dQ, *dK, *dV, *dqlow, *dklow;
-  int* cursor;                  // row pass: next free entry of each key's segment
-  const int *seg_off, *seg_cnt; // key pass: each key's segment
-  int* ent_i;
-  float *ent_p, *ent_d;
+  float2* epd;                  // (p_t, dl_t) of every idx entry, in idx's layout
+  const int *seg_off, *seg_cnt; // key pass: each key's segment of `ent`
+  const int* ent;               // per head, the entries i*k + t grouped by key
 };
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
-hipError_t launch_bwd_count(const int32_t* idx, int nh, int N, int k, int* cnt, hipStream_t s);
-hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, int* cursor,
-                           hipStream_t s);
-hipError_t launch_fill_zero(void* p, size_t bytes, hipStream_t s);
+// Key segments of the entry list, built from idx alone: per-slice counts of
+// each key (LDS histograms over windows of keys), their prefix over slices,
+// each key's segment start, then the entries written into their segments.
+int bwd_slices(int N, int k);
+hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int* cnt_s, hipStream_t s);
+hipError_t launch_bwd_slice_prefix(int* cnt_s, int S, long long total, int* cnt, hipStream_t s);
+hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t s);
+hipError_t launch_bwd_fill(const int32_t* idx, int nh, int N, int k, const int* cnt_s,
+                           const int* off, int* ent, hipStream_t s);
 // out[r][d] += sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
 hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
                                 int dp, float* out, hipStream_t s);
