@@ -51,11 +51,11 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 112.891e9, "write_bytes": 93.508e9,
-               "src": "c2fd4f618ca754cb8861533b8c8a12713eb99adaa6da0ee9097139d27472aa58"},
+    "filter": {"fetch_bytes": 111.095e9, "write_bytes": 93.480e9,
+               "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
     "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
-               "src": "00525acd8123ea03ed580e6df67740df22f2ca9cee064c51d23760c6e6f26175"},
-    "rerank": {"fetch_bytes": 69.485e9, "write_bytes": 10.889e9,
+               "src": "7cf6f35137b4cb8d7515197d8dc7bd7aae128bfa87780a0025aaafd4974ea0b0"},
+    "rerank": {"fetch_bytes": 69.490e9, "write_bytes": 10.889e9,
                "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
 }
 KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
@@ -67,9 +67,9 @@ KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "fina
 # XCD over the dispatch's duration.
 MFMA_COUNTERS: dict = {
     "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
-               "GRBM_GUI_ACTIVE_all_xcds": 1337055068, "dispatch_ms": 92.64,
-               "mfma_busy_frac": 0.4015, "shader_clock_ghz": 1.804,
-               "src": "c2fd4f618ca754cb8861533b8c8a12713eb99adaa6da0ee9097139d27472aa58"},
+               "GRBM_GUI_ACTIVE_all_xcds": 1327977764, "dispatch_ms": 93.11,
+               "mfma_busy_frac": 0.4043, "shader_clock_ghz": 1.783,
+               "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
 }
 
 
@@ -233,8 +233,9 @@ def kernel_table(recs, steps):
 
 
 def oracle_rate(fn, n_total: int, target_s: float = 20.0):
-    """Times fn(rows) of the oracle on a pilot of 8 rows, then on a sample
-    sized to about target_s; BLAS on every core this process may use."""
+    """Times fn(rows) of the oracle on a sample sized to about target_s from a
+    64-row pilot (after an 8-row warm-up); BLAS on every core this process
+    may use."""
     import numpy as np
     cores = len(os.sched_getaffinity(0))
     try:
@@ -244,10 +245,12 @@ def oracle_rate(fn, n_total: int, target_s: float = 20.0):
         limiter = None
     rng = np.random.default_rng(0)
     try:
+        fn(sorted(rng.choice(n_total, min(8, n_total), replace=False).tolist()))   # warm-up
+        m = min(64, n_total)
         t = time.perf_counter()
-        fn(sorted(rng.choice(n_total, 8, replace=False).tolist()))
+        fn(sorted(rng.choice(n_total, m, replace=False).tolist()))
         tp = time.perf_counter() - t
-        n = int(min(4096, n_total, max(16, 8 * target_s / max(tp, 1e-3))))
+        n = int(min(32768, n_total, max(16, m * target_s / max(tp, 1e-4))))
         rows = sorted(rng.choice(n_total, n, replace=False).tolist())
         t = time.perf_counter()
         fn(rows)
@@ -292,11 +295,13 @@ def run_op(args, w) -> int:
         metric = f"queries/s, top-k sparse attn backward (dQ, dK, dV, dPq, dPk), {w.name}"
         # algorithmic bytes of the two wave passes (per launch: all heads)
         amount = {
-            "bwd_rows": sum_k * (2 * D * e + 4 * dp + 12) + BH * N * (2 * D * e + 4 * k + 4 * D + 4 * dp),
+            "bwd_rows": sum_k * (2 * D * e + 4 * dp) + BH * N * (2 * D * e + 4 * k + 8 * k + 4 * D + 4 * dp),
             "bwd_keys": sum_k * (12 + 2 * D * e + 4 * dp) + BH * N * (8 * D + 4 * dp + 8),
+            "bwd_fill": float(BH * N * k * (4 + 8) + sum_k * 12),
         }
-        desc = {"bwd_rows": "K, V, k_low rows of kept keys + q, dO, idx rows + entries + dQ, dq_low",
-                "bwd_keys": "entries + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low"}
+        desc = {"bwd_rows": "K, V, k_low rows of kept keys + q, dO, idx rows + (p, dl) + dQ, dq_low",
+                "bwd_keys": "records + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low",
+                "bwd_fill": "idx + (p, dl) read, 12-byte records written"}
         idx_np = idx.cpu().numpy()
         # the head's rows as the oracle takes them, converted once outside the timing
         Qh, Kh, Vh = (O.f64(t[0, 0]) for t in (x["Q"], x["K"], x["V"]))

@@ -679,7 +679,7 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
   p.off_cnt = take(BH * N * 4);
   p.off_off = take(BH * N * 4);
   p.off_cnts = take(static_cast<size_t>(bwd_slices(d.N, k)) * BH * N * 4);
-  p.off_ent = take(ents * 4);
+  p.off_ent = take(ents * sizeof(BwdEntry));
   p.off_epd = take(ents * 8);
   p.nchunks = scorer ? outer_sum_chunks(static_cast<long long>(BH * N)) : 0;
   p.off_part = take(scorer ? static_cast<size_t>(p.nchunks) * d.D * dp * 4 * 2 : 0);
@@ -724,7 +724,7 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   int* cnt = reinterpret_cast<int*>(base + p.off_cnt);
   int* offs = reinterpret_cast<int*>(base + p.off_off);
   int* cnts = reinterpret_cast<int*>(base + p.off_cnts);
-  int* ent = reinterpret_cast<int*>(base + p.off_ent);
+  BwdEntry* rec = reinterpret_cast<BwdEntry*>(base + p.off_ent);
   BwdArgs a{};
   a.dtype = dtype;
   a.D = d.D;
@@ -737,7 +737,7 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.idx = idx;
   a.q32 = q32; a.k32 = k32;
   a.dQ = dQ; a.dK = dK; a.dV = dV; a.dqlow = dql; a.dklow = dkl;
-  a.seg_off = offs; a.seg_cnt = cnt; a.ent = ent;
+  a.seg_off = offs; a.seg_cnt = cnt; a.rec = rec;
   a.epd = reinterpret_cast<float2*>(base + p.off_epd);
   const long long rows = static_cast<long long>(a.nh) * d.N;
   sa_profile* prof = profile_of(opts);
@@ -751,9 +751,9 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   SA_TIMED_STATUS("bwd_count", launch_bwd_hist(idx, a.nh, d.N, k, cnts, s));
   SA_TIMED_STATUS("bwd_scan", launch_bwd_slice_prefix(cnts, bwd_slices(d.N, k), rows, cnt, s));
   SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, s));
-  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.nh, d.N, k, cnts, offs, ent, s));
   a.pass = 0;
   SA_TIMED_STATUS("bwd_rows", launch_bwd_pass(a, s));
+  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.nh, d.N, k, cnts, offs, rec, s));
   a.pass = 1;
   SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
   if (scorer) {

@@ -9,8 +9,9 @@
 // scanned over keys into each key's segment start, and a second pass with
 // the same grid places every entry (its index i*k + t within the head) at
 // its slice's next free position of its key's segment, again through LDS
-// counters.  No global atomics; the order of entries within one slice's part
-// of a segment is the order of the LDS atomics.
+// counters, copying the row pass's (p, dl) beside it.  No global atomics; the
+// order of entries within one slice's part of a segment is the order of the
+// LDS atomics.
 //
 // Scorer: with q_low = Q·Pq and k_low = K·Pk, the straight-through gradient
 // reaches dq_low and dk_low (the two passes in gather.hip); then
@@ -27,7 +28,7 @@ namespace sa {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kOuterRows = 4096;    // rows per outer-sum chunk
+constexpr int kOuterRows = 2048;    // rows per outer-sum chunk
 constexpr int kStageRows = 32;      // rows staged in LDS at a time
 
 constexpr int kHistThreads = 1024;
@@ -109,11 +110,12 @@ __global__ void bwd_slice_prefix_kernel(int* __restrict__ cnt_s, int S, long lon
 
 // Places the entries of one (head, slice, window) in their key segments.
 __global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* __restrict__ idx,
+                                                                const float2* __restrict__ epd,
                                                                 int N, int k, int S,
                                                                 int rows_per_slice, int nh,
                                                                 const int* __restrict__ cnt_s,
                                                                 const int* __restrict__ off,
-                                                                int* __restrict__ ent) {
+                                                                BwdEntry* __restrict__ rec) {
   extern __shared__ int cur[];
   const SliceWindow sw = slice_window(N, S, rows_per_slice);
   const int h = blockIdx.y;
@@ -122,12 +124,19 @@ __global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* _
   for (int t = threadIdx.x; t < sw.W; t += kHistThreads) cur[t] = off[hN + sw.w0 + t] + before[t];
   __syncthreads();
   const long long hk = static_cast<long long>(h) * N * k;
-  int* eh = ent + hk;
+  BwdEntry* rh = rec + hk;
   const unsigned w0 = static_cast<unsigned>(sw.w0), W = static_cast<unsigned>(sw.W);
   for_entries(idx, hk + static_cast<long long>(sw.i0) * k, hk + static_cast<long long>(sw.i1) * k,
               [&](long long g, int j) {
                 const unsigned u = static_cast<unsigned>(j) - w0;
-                if (u < W) eh[atomicAdd(&cur[u], 1)] = static_cast<int>(g - hk);
+                if (u < W) {
+                  const float2 pd = epd[g];
+                  BwdEntry r;
+                  r.e = static_cast<int>(g - hk);
+                  r.p = pd.x;
+                  r.dl = pd.y;
+                  rh[atomicAdd(&cur[u], 1)] = r;
+                }
               });
 }
 
@@ -158,43 +167,91 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restric
   }
 }
 
-// out[r][d] += sum_c lo[r][c] P[d][c]; P staged transposed in LDS (fp32).
+// out[r][d] += sum_c lo[r][c] P[d][c].  P^T (fp32) and a block of lo rows sit
+// in LDS; each thread accumulates a tile of RT rows x 4 columns.
+constexpr int kRptRows = 32;
+
+template <int D, int DP>
+__host__ __device__ constexpr size_t rpt_lds_bytes() {
+  return static_cast<size_t>(DP * D + kRptRows * DP) * 4;
+}
+
 template <typename T, int D, int DP>
 __global__ __launch_bounds__(kThreads) void rows_times_pt_kernel(const float* __restrict__ lo,
                                                                  const T* __restrict__ P,
                                                                  long long rows,
                                                                  float* __restrict__ out) {
-  __shared__ float pt[DP * D];    // pt[c * D + d]
+  extern __shared__ __align__(16) float rpt_lds[];
+  float* pt = rpt_lds;               // pt[c * D + d]
+  float* ls = rpt_lds + DP * D;      // ls[r * DP + c]
   for (int e = threadIdx.x; e < D * DP; e += kThreads) {
     const int d = e / DP, c = e % DP;
     pt[c * D + d] = io<T>::to_f32(P[e]);
   }
-  __syncthreads();
-  constexpr int RPB = kThreads / D;       // rows per pass of a workgroup
-  const int d = threadIdx.x % D;
-  for (long long r = blockIdx.x * static_cast<long long>(RPB) + threadIdx.x / D; r < rows;
-       r += static_cast<long long>(gridDim.x) * RPB) {
-    const float* lr = lo + r * DP;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int c = 0; c < DP; ++c) acc = __builtin_fmaf(lr[c], pt[c * D + d], acc);
-    out[r * D + d] += acc;
+  constexpr int TPR = D / 4;                    // threads across one row's columns
+  constexpr int RT = kRptRows * TPR / kThreads;  // rows per thread
+  const int d0 = (threadIdx.x % TPR) * 4;
+  const int rr0 = (threadIdx.x / TPR) * RT;
+  for (long long rb = blockIdx.x * static_cast<long long>(kRptRows); rb < rows;
+       rb += static_cast<long long>(gridDim.x) * kRptRows) {
+    const int nr = static_cast<int>(rows - rb < kRptRows ? rows - rb : kRptRows);
+    __syncthreads();
+    const float4* src = reinterpret_cast<const float4*>(lo + rb * DP);
+    for (int e = threadIdx.x; e < kRptRows * DP / 4; e += kThreads)
+      reinterpret_cast<float4*>(ls)[e] = e < nr * DP / 4 ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    float acc[RT][4];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+#pragma unroll 4
+    for (int c = 0; c < DP; ++c) {
+      const float4 p = *reinterpret_cast<const float4*>(pt + c * D + d0);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const float x = ls[(rr0 + i) * DP + c];
+        acc[i][0] = __builtin_fmaf(x, p.x, acc[i][0]);
+        acc[i][1] = __builtin_fmaf(x, p.y, acc[i][1]);
+        acc[i][2] = __builtin_fmaf(x, p.z, acc[i][2]);
+        acc[i][3] = __builtin_fmaf(x, p.w, acc[i][3]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const long long r = rb + rr0 + i;
+      if (r < rows) {
+        float4* o = reinterpret_cast<float4*>(out + r * D + d0);
+        float4 v = *o;
+        v.x += acc[i][0];
+        v.y += acc[i][1];
+        v.z += acc[i][2];
+        v.w += acc[i][3];
+        *o = v;
+      }
+    }
   }
 }
 
 // partial[chunk][d][c] = sum over the chunk's rows r (ascending) of
-// X[r][d] lo[r][c]; each thread owns D*DP/256 of the outputs.
+// X[r][d] lo[r][c]; each thread owns a tile of DT x 4 outputs.
 template <typename T, int D, int DP>
 __global__ __launch_bounds__(kThreads) void outer_partial_kernel(const T* __restrict__ X,
                                                                  const float* __restrict__ lo,
                                                                  long long rows,
                                                                  float* __restrict__ partial) {
-  constexpr int U = D * DP / kThreads;
-  __shared__ float xs[kStageRows * D];
-  __shared__ float ls[kStageRows * DP];
-  float acc[U];
+  constexpr int CT = 4, TPC = DP / CT;          // threads across the DP columns
+  constexpr int DT = D * DP / kThreads / CT;    // d's per thread
+  static_assert(TPC * (D / DT) == kThreads, "tile cover");
+  __shared__ __align__(16) float xs[kStageRows * D];
+  __shared__ __align__(16) float ls[kStageRows * DP];
+  const int c0 = (threadIdx.x % TPC) * CT;
+  const int d0 = (threadIdx.x / TPC) * DT;
+  float acc[DT][CT];
 #pragma unroll
-  for (int u = 0; u < U; ++u) acc[u] = 0.0f;
+  for (int i = 0; i < DT; ++i)
+#pragma unroll
+    for (int j = 0; j < CT; ++j) acc[i][j] = 0.0f;
   const long long r0 = blockIdx.x * static_cast<long long>(kOuterRows);
   const long long r1 = r0 + kOuterRows < rows ? r0 + kOuterRows : rows;
   for (long long rb = r0; rb < r1; rb += kStageRows) {
@@ -206,16 +263,22 @@ __global__ __launch_bounds__(kThreads) void outer_partial_kernel(const T* __rest
       ls[e] = e < nr * DP ? lo[rb * DP + e] : 0.0f;
     __syncthreads();
     for (int r = 0; r < nr; ++r) {
+      const float4 l4 = *reinterpret_cast<const float4*>(ls + r * DP + c0);
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int o = threadIdx.x + u * kThreads;
-        acc[u] = __builtin_fmaf(xs[r * D + o / DP], ls[r * DP + o % DP], acc[u]);
+      for (int i = 0; i < DT; ++i) {
+        const float x = xs[r * D + d0 + i];
+        acc[i][0] = __builtin_fmaf(x, l4.x, acc[i][0]);
+        acc[i][1] = __builtin_fmaf(x, l4.y, acc[i][1]);
+        acc[i][2] = __builtin_fmaf(x, l4.z, acc[i][2]);
+        acc[i][3] = __builtin_fmaf(x, l4.w, acc[i][3]);
       }
     }
   }
   float* dst = partial + static_cast<size_t>(blockIdx.x) * D * DP;
 #pragma unroll
-  for (int u = 0; u < U; ++u) dst[threadIdx.x + u * kThreads] = acc[u];
+  for (int i = 0; i < DT; ++i)
+    *reinterpret_cast<float4*>(dst + (d0 + i) * DP + c0) =
+        make_float4(acc[i][0], acc[i][1], acc[i][2], acc[i][3]);
 }
 
 __global__ void outer_reduce_kernel(const float* __restrict__ partial, int nchunks, int n,
@@ -234,21 +297,28 @@ unsigned grid_for(long long total) {
   return static_cast<unsigned>(blocks);
 }
 
+template <typename T, int D, int DP>
+hipError_t rows_pt_t(const float* lo, const void* P, long long rows, float* out, hipStream_t s) {
+  static std::atomic<int> lds_set[kMaxDevices];
+  const size_t lds = rpt_lds_bytes<D, DP>();
+  const hipError_t e = set_lds_limit_once(
+      reinterpret_cast<const void*>(&rows_times_pt_kernel<T, D, DP>), lds, lds_set);
+  if (e != hipSuccess) return e;
+  long long blocks = (rows + kRptRows - 1) / kRptRows;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((rows_times_pt_kernel<T, D, DP>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), lds, s, lo, static_cast<const T*>(P), rows, out);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 hipError_t rows_pt_d(const float* lo, const void* P, long long rows, int dp, float* out,
                      hipStream_t s) {
-  const unsigned grid = grid_for(rows * D);
   switch (dp) {
-#define SA_RPT(DPV)                                                                          \
-  case DPV:                                                                                  \
-    hipLaunchKernelGGL((rows_times_pt_kernel<T, D, DPV>), dim3(grid), dim3(kThreads), 0, s, lo, \
-                       static_cast<const T*>(P), rows, out);                                 \
-    return hipGetLastError();
-    SA_RPT(16)
-    SA_RPT(32)
-    SA_RPT(64)
-    SA_RPT(128)
-#undef SA_RPT
+    case 16: return rows_pt_t<T, D, 16>(lo, P, rows, out, s);
+    case 32: return rows_pt_t<T, D, 32>(lo, P, rows, out, s);
+    case 64: return rows_pt_t<T, D, 64>(lo, P, rows, out, s);
+    case 128: return rows_pt_t<T, D, 128>(lo, P, rows, out, s);
   }
   return hipErrorInvalidValue;
 }
@@ -317,15 +387,15 @@ hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_fill(const int32_t* idx, int nh, int N, int k, const int* cnt_s,
-                           const int* off, int* ent, hipStream_t s) {
+hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N, int k,
+                           const int* cnt_s, const int* off, BwdEntry* rec, hipStream_t s) {
   static std::atomic<int> lds_set[kMaxDevices];
   hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_fill_kernel),
                                     kHistWindow * 4, lds_set);
   if (e != hipSuccess) return e;
   const HistGrid g = hist_grid(nh, N, k);
-  hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, N, k, g.S,
-                     g.rows_per_slice, nh, cnt_s, off, ent);
+  hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, epd, N, k, g.S,
+                     g.rows_per_slice, nh, cnt_s, off, rec);
   return hipGetLastError();
 }
 

@@ -731,8 +731,7 @@ template <typename T, int D, int DP>
 __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     const T* __restrict__ Q, const T* __restrict__ dO, const float* __restrict__ q32,
     const int* __restrict__ seg_off, const int* __restrict__ seg_cnt,
-    const int* __restrict__ ent, const float2* __restrict__ epd, int N, int k, float scale,
-    float sscale,
+    const BwdEntry* __restrict__ rec, int N, int k, float scale, float sscale,
     float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ dklow) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
@@ -748,8 +747,7 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
   const size_t hN = static_cast<size_t>(h) * N;
   const T* Qh = Q + hN * D;
   const T* dOh = dO + hN * D;
-  const size_t hk = hN * static_cast<size_t>(k);
-  const size_t o0 = hk + static_cast<unsigned>(seg_off[hN + j]);
+  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[hN + j]);
   const int n = seg_cnt[hN + j];
   const unsigned uk = static_cast<unsigned>(k);
   float av[EPL], ak[EPL], al[4];
@@ -760,11 +758,10 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
   for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
     const int m = min(kBwdChunk, n - c0);
     for (int t = l; t < m; t += kWave) {
-      const unsigned e = static_cast<unsigned>(ent[o0 + c0 + t]);   // i*k + t of the entry
-      const float2 pd = epd[hk + e];
-      sidx[t] = static_cast<int>(e / uk);
-      sp[t] = pd.x;
-      sd[t] = pd.y;
+      const BwdEntry r = rec[o0 + c0 + t];
+      sidx[t] = static_cast<int>(static_cast<unsigned>(r.e) / uk);   // e = i*k + t
+      sp[t] = r.p;
+      sd[t] = r.dl;
     }
     wave_sync();
     float tmp[EPL];
@@ -811,8 +808,8 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
   } else {
     hipLaunchKernelGGL((bwd_keys_kernel<T, D, DP>), grid, dim3(kThreads),
                        kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.ent,
-                       a.epd, a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
+                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.rec,
+                       a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
   }
   return hipGetLastError();
 }

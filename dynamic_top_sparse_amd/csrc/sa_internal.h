@@ -209,6 +209,12 @@ hipError_t launch_block_dump(const float* q32, const float* kbar, int nh, int N,
 
 // Backward of the gather attention (gather.hip, the two wave passes) and its
 // helpers (bwd.hip).  dp = 0 leaves out the scorer's gradient.
+// One idx entry as the key pass reads it: e = i*k + t within the head, and
+// the row pass's p_t and dl_t (12 bytes, one 3-dword access).
+struct BwdEntry {
+  int e;
+  float p, dl;
+};
 struct BwdArgs {
   int pass;             // 0: row pass, 1: key pass
   int dtype, D, dp, k, N, nh;
@@ -218,8 +224,8 @@ struct BwdArgs {
   const float *q32, *k32;       // fp32 projections (scorer gradient only)
   float *dQ, *dK, *dV, *dqlow, *dklow;
   float2* epd;                  // (p_t, dl_t) of every idx entry, in idx's layout
-  const int *seg_off, *seg_cnt; // key pass: each key's segment of `ent`
-  const int* ent;               // per head, the entries i*k + t grouped by key
+  const int *seg_off, *seg_cnt; // key pass: each key's segment of `rec`
+  const BwdEntry* rec;          // per head, the entries grouped by key
 };
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
 // Key segments of the entry list, built from idx alone: per-slice counts of
@@ -229,8 +235,8 @@ int bwd_slices(int N, int k);
 hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int* cnt_s, hipStream_t s);
 hipError_t launch_bwd_slice_prefix(int* cnt_s, int S, long long total, int* cnt, hipStream_t s);
 hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t s);
-hipError_t launch_bwd_fill(const int32_t* idx, int nh, int N, int k, const int* cnt_s,
-                           const int* off, int* ent, hipStream_t s);
+hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N, int k,
+                           const int* cnt_s, const int* off, BwdEntry* rec, hipStream_t s);
 // out[r][d] += sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
 hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
                                 int dp, float* out, hipStream_t s);
