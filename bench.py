@@ -295,12 +295,12 @@ def run_op(args, w) -> int:
         metric = f"queries/s, top-k sparse attn backward (dQ, dK, dV, dPq, dPk), {w.name}"
         # algorithmic bytes of the two wave passes (per launch: all heads)
         amount = {
-            "bwd_rows": sum_k * (2 * D * e + 4 * dp) + BH * N * (2 * D * e + 4 * k + 8 * k + 4 * D + 4 * dp),
-            "bwd_keys": sum_k * (12 + 2 * D * e + 4 * dp) + BH * N * (8 * D + 4 * dp + 8),
+            "bwd_rows": sum_k * (2 * D * e) + BH * N * (2 * D * e + 4 * k + 8 * k + 4 * D),
+            "bwd_keys": sum_k * (12 + 2 * D * e) + BH * N * (8 * D + 8),
             "bwd_fill": float(BH * N * k * (4 + 8) + sum_k * 12),
         }
-        desc = {"bwd_rows": "K, V, k_low rows of kept keys + q, dO, idx rows + (p, dl) + dQ, dq_low",
-                "bwd_keys": "records + Q, dO, q_low rows of the rows that kept each key + dK, dV, dk_low",
+        desc = {"bwd_rows": "K, V rows of kept keys + q, dO, idx rows + (p, dl) + dQ",
+                "bwd_keys": "records + Q, dO rows of the rows that kept each key + dK, dV",
                 "bwd_fill": "idx + (p, dl) read, 12-byte records written"}
         idx_np = idx.cpu().numpy()
         # the head's rows as the oracle takes them, converted once outside the timing

@@ -657,7 +657,7 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
 // ----------------------------------------------------------- backward ---
 namespace {
 struct BwdPlan {
-  size_t off_q32, off_k32, off_dql, off_dkl, off_cnt, off_off, off_cnts, off_ent, off_epd,
+  size_t off_dql, off_dkl, off_cnt, off_off, off_cnts, off_ent, off_epd,
       off_part, total;
   int nchunks;
 };
@@ -672,8 +672,6 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
     return at;
   };
   const size_t lo = scorer ? BH * N * dp * 4 : 0;
-  p.off_q32 = take(lo);
-  p.off_k32 = take(lo);
   p.off_dql = take(lo);
   p.off_dkl = take(lo);
   p.off_cnt = take(BH * N * 4);
@@ -717,8 +715,6 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   const BwdPlan p = bwd_plan(d, d_proj, k, scorer);
   if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
-  float* q32 = reinterpret_cast<float*>(base + p.off_q32);
-  float* k32 = reinterpret_cast<float*>(base + p.off_k32);
   float* dql = reinterpret_cast<float*>(base + p.off_dql);
   float* dkl = reinterpret_cast<float*>(base + p.off_dkl);
   int* cnt = reinterpret_cast<int*>(base + p.off_cnt);
@@ -728,26 +724,18 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   BwdArgs a{};
   a.dtype = dtype;
   a.D = d.D;
-  a.dp = scorer ? d_proj : 0;
   a.k = k;
   a.N = d.N;
   a.nh = d.B * d.H;
+  a.scorer = scorer ? 1 : 0;
   a.scale = softmax_scale;
-  a.sscale = score_scale;
   a.Q = Q; a.K = K; a.V = V; a.dO = dO; a.idx = idx;
-  a.q32 = q32; a.k32 = k32;
-  a.dQ = dQ; a.dK = dK; a.dV = dV; a.dqlow = dql; a.dklow = dkl;
+  a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.seg_off = offs; a.seg_cnt = cnt; a.rec = rec;
   a.epd = reinterpret_cast<float2*>(base + p.off_epd);
   const long long rows = static_cast<long long>(a.nh) * d.N;
   sa_profile* prof = profile_of(opts);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (scorer) {
-    SA_TIMED_STATUS("bwd_project", launch_project_rows(Q, Pq, a.nh, d.N, d.N, d.D, d_proj, dtype,
-                                                       0, q32, nullptr, nullptr, s));
-    SA_TIMED_STATUS("bwd_project", launch_project_rows(K, Pk, a.nh, d.N, d.N, d.D, d_proj, dtype,
-                                                       1, k32, nullptr, nullptr, s));
-  }
   SA_TIMED_STATUS("bwd_count", launch_bwd_hist(idx, a.nh, d.N, k, cnts, s));
   SA_TIMED_STATUS("bwd_scan", launch_bwd_slice_prefix(cnts, bwd_slices(d.N, k), rows, cnt, s));
   SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, s));
@@ -757,8 +745,16 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   a.pass = 1;
   SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
   if (scorer) {
-    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dql, Pq, dtype, rows, d.D, d_proj, dQ, s));
-    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dkl, Pk, dtype, rows, d.D, d_proj, dK, s));
+    // dQ and dK hold G and H (unscaled): the scorer's low-dimensional
+    // gradients first, then the full ones
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_p(dQ, Pk, dtype, rows, d.D, d_proj,
+                                                      score_scale, dql, s));
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_p(dK, Pq, dtype, rows, d.D, d_proj,
+                                                      score_scale, dkl, s));
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dql, Pq, dtype, rows, d.D, d_proj,
+                                                       softmax_scale, dQ, s));
+    SA_TIMED_STATUS("bwd_scorer", launch_rows_times_pt(dkl, Pk, dtype, rows, d.D, d_proj,
+                                                       softmax_scale, dK, s));
     float* part = reinterpret_cast<float*>(base + p.off_part);
     const size_t psz = static_cast<size_t>(p.nchunks) * d.D * d_proj;
     SA_TIMED_STATUS("bwd_scorer", launch_outer_sum(Q, dtype, dql, rows, d.D, d_proj, part,

@@ -14,8 +14,9 @@
 // LDS atomics.
 //
 // Scorer: with q_low = Q·Pq and k_low = K·Pk, the straight-through gradient
-// reaches dq_low and dk_low (the two passes in gather.hip); then
-//   dQ += dq_low·Pqᵀ, dK += dk_low·Pkᵀ   (rows_times_pt),
+// reaches dq_low = score_scale·G·Pk and dk_low = score_scale·H·Pq, where G and
+// H are the row and key passes' unscaled sums (gather.hip; rows_times_p), then
+//   dQ = scale·G + dq_low·Pqᵀ, dK = scale·H + dk_low·Pkᵀ   (rows_times_pt),
 //   dPq = sum over every row of Qᵀ·dq_low, dPk likewise  (outer_sum: fixed
 //   row chunks, then the chunks' partial sums added in chunk order, so the
 //   result does not depend on scheduling).
@@ -167,8 +168,9 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restric
   }
 }
 
-// out[r][d] += sum_c lo[r][c] P[d][c].  P^T (fp32) and a block of lo rows sit
-// in LDS; each thread accumulates a tile of RT rows x 4 columns.
+// out[r][d] = pre * out[r][d] + sum_c lo[r][c] P[d][c].  P^T (fp32) and a
+// block of lo rows sit in LDS; each thread accumulates a tile of RT rows x 4
+// columns.
 constexpr int kRptRows = 32;
 
 template <int D, int DP>
@@ -179,7 +181,7 @@ __host__ __device__ constexpr size_t rpt_lds_bytes() {
 template <typename T, int D, int DP>
 __global__ __launch_bounds__(kThreads) void rows_times_pt_kernel(const float* __restrict__ lo,
                                                                  const T* __restrict__ P,
-                                                                 long long rows,
+                                                                 long long rows, float pre,
                                                                  float* __restrict__ out) {
   extern __shared__ __align__(16) float rpt_lds[];
   float* pt = rpt_lds;               // pt[c * D + d]
@@ -223,11 +225,70 @@ __global__ __launch_bounds__(kThreads) void rows_times_pt_kernel(const float* __
       if (r < rows) {
         float4* o = reinterpret_cast<float4*>(out + r * D + d0);
         float4 v = *o;
-        v.x += acc[i][0];
-        v.y += acc[i][1];
-        v.z += acc[i][2];
-        v.w += acc[i][3];
+        v.x = __builtin_fmaf(pre, v.x, acc[i][0]);
+        v.y = __builtin_fmaf(pre, v.y, acc[i][1]);
+        v.z = __builtin_fmaf(pre, v.z, acc[i][2]);
+        v.w = __builtin_fmaf(pre, v.w, acc[i][3]);
         *o = v;
+      }
+    }
+  }
+}
+
+// out[r][c] = alpha * sum_d X[r][d] P[d][c] (X fp32 [rows][D], P [D][DP]).
+// P (fp32) and a block of X rows sit in LDS; each thread accumulates a tile
+// of RT rows x CT columns.
+template <int D, int DP>
+__host__ __device__ constexpr size_t rp_lds_bytes() {
+  return static_cast<size_t>(D * DP + kRptRows * D) * 4;
+}
+
+template <typename T, int D, int DP>
+__global__ __launch_bounds__(kThreads) void rows_times_p_kernel(const float* __restrict__ X,
+                                                                const T* __restrict__ P,
+                                                                long long rows, float alpha,
+                                                                float* __restrict__ out) {
+  extern __shared__ __align__(16) float rp_lds[];
+  float* ps = rp_lds;               // ps[d * DP + c]
+  float* xs = rp_lds + D * DP;      // xs[r * D + d]
+  for (int e = threadIdx.x; e < D * DP; e += kThreads) ps[e] = io<T>::to_f32(P[e]);
+  constexpr int CT = DP >= 32 ? 4 : 2;
+  constexpr int TPR = DP / CT;                   // threads across one row's columns
+  constexpr int RT = kRptRows * TPR / kThreads;  // rows per thread
+  static_assert(RT >= 1 && RT * (kThreads / TPR) == kRptRows, "tile cover");
+  const int c0 = (threadIdx.x % TPR) * CT;
+  const int rr0 = (threadIdx.x / TPR) * RT;
+  for (long long rb = blockIdx.x * static_cast<long long>(kRptRows); rb < rows;
+       rb += static_cast<long long>(gridDim.x) * kRptRows) {
+    const int nr = static_cast<int>(rows - rb < kRptRows ? rows - rb : kRptRows);
+    __syncthreads();
+    const float4* src = reinterpret_cast<const float4*>(X + rb * D);
+    for (int e = threadIdx.x; e < kRptRows * D / 4; e += kThreads)
+      reinterpret_cast<float4*>(xs)[e] = e < nr * D / 4 ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    float acc[RT][CT];
+#pragma unroll
+    for (int i = 0; i < RT; ++i)
+#pragma unroll
+      for (int j = 0; j < CT; ++j) acc[i][j] = 0.0f;
+#pragma unroll 4
+    for (int d = 0; d < D; ++d) {
+      float pv[CT];
+#pragma unroll
+      for (int j = 0; j < CT; ++j) pv[j] = ps[d * DP + c0 + j];
+#pragma unroll
+      for (int i = 0; i < RT; ++i) {
+        const float x = xs[(rr0 + i) * D + d];
+#pragma unroll
+        for (int j = 0; j < CT; ++j) acc[i][j] = __builtin_fmaf(x, pv[j], acc[i][j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < RT; ++i) {
+      const long long r = rb + rr0 + i;
+      if (r < rows) {
+#pragma unroll
+        for (int j = 0; j < CT; ++j) out[r * DP + c0 + j] = alpha * acc[i][j];
       }
     }
   }
@@ -298,7 +359,8 @@ unsigned grid_for(long long total) {
 }
 
 template <typename T, int D, int DP>
-hipError_t rows_pt_t(const float* lo, const void* P, long long rows, float* out, hipStream_t s) {
+hipError_t rows_pt_t(const float* lo, const void* P, long long rows, float pre, float* out,
+                     hipStream_t s) {
   static std::atomic<int> lds_set[kMaxDevices];
   const size_t lds = rpt_lds_bytes<D, DP>();
   const hipError_t e = set_lds_limit_once(
@@ -307,18 +369,45 @@ hipError_t rows_pt_t(const float* lo, const void* P, long long rows, float* out,
   long long blocks = (rows + kRptRows - 1) / kRptRows;
   if (blocks > 8192) blocks = 8192;
   hipLaunchKernelGGL((rows_times_pt_kernel<T, D, DP>), dim3(static_cast<unsigned>(blocks)),
-                     dim3(kThreads), lds, s, lo, static_cast<const T*>(P), rows, out);
+                     dim3(kThreads), lds, s, lo, static_cast<const T*>(P), rows, pre, out);
   return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t rows_pt_d(const float* lo, const void* P, long long rows, int dp, float* out,
+hipError_t rows_pt_d(const float* lo, const void* P, long long rows, int dp, float pre, float* out,
                      hipStream_t s) {
   switch (dp) {
-    case 16: return rows_pt_t<T, D, 16>(lo, P, rows, out, s);
-    case 32: return rows_pt_t<T, D, 32>(lo, P, rows, out, s);
-    case 64: return rows_pt_t<T, D, 64>(lo, P, rows, out, s);
-    case 128: return rows_pt_t<T, D, 128>(lo, P, rows, out, s);
+    case 16: return rows_pt_t<T, D, 16>(lo, P, rows, pre, out, s);
+    case 32: return rows_pt_t<T, D, 32>(lo, P, rows, pre, out, s);
+    case 64: return rows_pt_t<T, D, 64>(lo, P, rows, pre, out, s);
+    case 128: return rows_pt_t<T, D, 128>(lo, P, rows, pre, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename T, int D, int DP>
+hipError_t rows_p_t(const float* X, const void* P, long long rows, float alpha, float* out,
+                    hipStream_t s) {
+  static std::atomic<int> lds_set[kMaxDevices];
+  const size_t lds = rp_lds_bytes<D, DP>();
+  const hipError_t e = set_lds_limit_once(
+      reinterpret_cast<const void*>(&rows_times_p_kernel<T, D, DP>), lds, lds_set);
+  if (e != hipSuccess) return e;
+  long long blocks = (rows + kRptRows - 1) / kRptRows;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL((rows_times_p_kernel<T, D, DP>), dim3(static_cast<unsigned>(blocks)),
+                     dim3(kThreads), lds, s, X, static_cast<const T*>(P), rows, alpha, out);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+hipError_t rows_p_d(const float* X, const void* P, long long rows, int dp, float alpha, float* out,
+                    hipStream_t s) {
+  switch (dp) {
+    case 16: return rows_p_t<T, D, 16>(X, P, rows, alpha, out, s);
+    case 32: return rows_p_t<T, D, 32>(X, P, rows, alpha, out, s);
+    case 64: return rows_p_t<T, D, 64>(X, P, rows, alpha, out, s);
+    case 128: return rows_p_t<T, D, 128>(X, P, rows, alpha, out, s);
   }
   return hipErrorInvalidValue;
 }
@@ -400,13 +489,25 @@ hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N,
 }
 
 hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
-                                int dp, float* out, hipStream_t s) {
+                                int dp, float pre, float* out, hipStream_t s) {
   if (dtype == 0) {
-    if (D == 64) return rows_pt_d<float, 64>(lo, P, rows, dp, out, s);
-    if (D == 128) return rows_pt_d<float, 128>(lo, P, rows, dp, out, s);
+    if (D == 64) return rows_pt_d<float, 64>(lo, P, rows, dp, pre, out, s);
+    if (D == 128) return rows_pt_d<float, 128>(lo, P, rows, dp, pre, out, s);
   } else {
-    if (D == 64) return rows_pt_d<bf16_t, 64>(lo, P, rows, dp, out, s);
-    if (D == 128) return rows_pt_d<bf16_t, 128>(lo, P, rows, dp, out, s);
+    if (D == 64) return rows_pt_d<bf16_t, 64>(lo, P, rows, dp, pre, out, s);
+    if (D == 128) return rows_pt_d<bf16_t, 128>(lo, P, rows, dp, pre, out, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_rows_times_p(const float* X, const void* P, int dtype, long long rows, int D,
+                               int dp, float alpha, float* out, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 64) return rows_p_d<float, 64>(X, P, rows, dp, alpha, out, s);
+    if (D == 128) return rows_p_d<float, 128>(X, P, rows, dp, alpha, out, s);
+  } else {
+    if (D == 64) return rows_p_d<bf16_t, 64>(X, P, rows, dp, alpha, out, s);
+    if (D == 128) return rows_p_d<bf16_t, 128>(X, P, rows, dp, alpha, out, s);
   }
   return hipErrorInvalidValue;
 }

@@ -637,15 +637,18 @@ hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* 
 // reached through the selected positions' attention weights).  With
 // p_t = softmax(l)_t, dp_t = dO·V[j_t], delta = sum_t p_t dp_t and
 // dl_t = p_t (dp_t - delta):
-//   dQ_i = scale · sum_t dl_t K[j_t]                     (row pass)
-//   dV_j = sum over (i, t) with j_t = j of p_t dO_i       (key pass)
-//   dK_j = scale · sum over the same of dl_t Q_i          (key pass)
-// and, for the scorer (straight-through: a kept pair's score receives its
-// logit's gradient dl_t), dq_low_i = score_scale · sum_t dl_t k_low[j_t]
-// (row pass) and dk_low_j = score_scale · sum dl_t q_low_i (key pass).
-// The row pass appends (i, p_t, dl_t) to key j_t's segment of an entry list
-// (segment offsets from a count and a scan); the key pass then gathers the
-// rows of the queries that kept each key, as the forward gathers key rows.
+//   G_i = sum_t dl_t K[j_t],  dQ_i = scale · G_i              (row pass)
+//   dV_j = sum over (i, t) with j_t = j of p_t dO_i            (key pass)
+//   H_j = sum over the same of dl_t Q_i,  dK_j = scale · H_j   (key pass)
+// The scorer's gradients need no further gathers: a kept pair's score
+// receives its logit's gradient dl_t (straight-through), so
+//   dq_low_i = score_scale · sum_t dl_t k_low[j_t] = score_scale · G_i·Pk,
+//   dk_low_j = score_scale · H_j·Pq,
+// by linearity (bwd.hip computes them from G and H).  With scorer gradients
+// the passes store G and H unscaled (out_scale 1), else scale·G and scale·H.
+// The row pass writes (p_t, dl_t) in idx's layout; bwd.hip groups them by
+// key, and the key pass gathers the rows of the queries that kept each key,
+// as the forward gathers key rows.
 constexpr int kBwdChunk = 512;     // key-pass entries staged in LDS at a time
 
 __host__ __device__ constexpr int bwd_row_wave_floats(int k) { return 3 * gather_slog_floats(k); }
@@ -658,12 +661,11 @@ __device__ __forceinline__ void store_f32_row(float* dst, const float (&v)[EPL],
     *reinterpret_cast<float4*>(dst + e) = make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
 }
 
-template <typename T, int D, int DP>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const int32_t* __restrict__ idx, int k, int N, float scale,
-    float sscale, const float* __restrict__ k32, float* __restrict__ dQ,
-    float* __restrict__ dqlow, float2* __restrict__ epd) {
+    float out_scale, float* __restrict__ dQ, float2* __restrict__ epd) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -688,16 +690,12 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   const float mx = softmax_weights(sl, k, sum);
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   float acc[EPL];
+  float2* er = epd + (hN + q) * static_cast<size_t>(k);
   if (mx == -INFINITY) {    // no valid entry: no gradient from this row
-    float2* er = epd + (hN + q) * static_cast<size_t>(k);
     for (int t = l; t < k; t += kWave) er[t] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
     if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
-    if constexpr (DP > 0) {
-      if (l < DP / 4)
-        *reinterpret_cast<float4*>(dqlow + (hN + q) * DP + 4 * l) = make_float4(0.f, 0.f, 0.f, 0.f);
-    }
     return;
   }
   // p_t, delta, dl_t (invalid entries have p_t = 0 and contribute nothing)
@@ -715,24 +713,17 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   }
   wave_sync();
   weighted_rows<T, D>(Kh, sidx, 0, k, N, sd, acc);
-  if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, scale);
-  if constexpr (DP > 0) {
-    float a4[4];
-    weighted_rows<float, DP>(k32 + hN * DP, sidx, 0, k, N, sd, a4);
-    if (l < DP / 4) store_f32_row<4>(dqlow + (hN + q) * DP + 4 * l, a4, sscale);
-  }
+  if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, out_scale);
   // (p_t, dl_t) for the key pass, in idx's layout (entries that name no key
   // hold p_t = 0 and are never read)
-  float2* er = epd + (hN + q) * static_cast<size_t>(k);
   for (int t = l; t < k; t += kWave) er[t] = make_float2(sl[t], sd[t]);
 }
 
-template <typename T, int D, int DP>
+template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
-    const T* __restrict__ Q, const T* __restrict__ dO, const float* __restrict__ q32,
-    const int* __restrict__ seg_off, const int* __restrict__ seg_cnt,
-    const BwdEntry* __restrict__ rec, int N, int k, float scale, float sscale,
-    float* __restrict__ dK, float* __restrict__ dV, float* __restrict__ dklow) {
+    const T* __restrict__ Q, const T* __restrict__ dO, const int* __restrict__ seg_off,
+    const int* __restrict__ seg_cnt, const BwdEntry* __restrict__ rec, int N, int k,
+    float out_scale, float* __restrict__ dK, float* __restrict__ dV) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -750,11 +741,9 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
   const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[hN + j]);
   const int n = seg_cnt[hN + j];
   const unsigned uk = static_cast<unsigned>(k);
-  float av[EPL], ak[EPL], al[4];
+  float av[EPL], ak[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
-#pragma unroll
-  for (int e = 0; e < 4; ++e) al[e] = 0.0f;
   for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
     const int m = min(kBwdChunk, n - c0);
     for (int t = l; t < m; t += kWave) {
@@ -771,70 +760,50 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
-    if constexpr (DP > 0) {
-      float t4[4];
-      weighted_rows<float, DP>(q32 + hN * DP, sidx, 0, m, N, sd, t4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) al[e] += t4[e];
-    }
     wave_sync();    // the chunk's LDS is read before the next one is staged
   }
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   if (g == 0) {
     store_f32_row<EPL>(dV + (hN + j) * D + e0, av, 1.0f);
-    store_f32_row<EPL>(dK + (hN + j) * D + e0, ak, scale);
+    store_f32_row<EPL>(dK + (hN + j) * D + e0, ak, out_scale);
   }
-  if constexpr (DP > 0) {
-    if (l < DP / 4) store_f32_row<4>(dklow + (hN + j) * DP + 4 * l, al, sscale);
-  }
-}
-
-template <typename T, int D, int DP>
-hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
-  static std::atomic<int> lds_rows[kMaxDevices], lds_keys[kMaxDevices];
-  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_kernel<T, D, DP>),
-                                    kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rows);
-  if (e != hipSuccess) return e;
-  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_kernel<T, D, DP>),
-                         kWaves * bwd_key_wave_floats() * 4, lds_keys);
-  if (e != hipSuccess) return e;
-  const dim3 grid((a.N + kWaves - 1) / kWaves, a.nh);
-  if (a.pass == 0) {
-    hipLaunchKernelGGL((bwd_rows_kernel<T, D, DP>), grid, dim3(kThreads),
-                       kWaves * bwd_row_wave_floats(a.k) * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.K), static_cast<const T*>(a.V),
-                       static_cast<const T*>(a.dO), a.idx, a.k, a.N, a.scale, a.sscale, a.k32,
-                       a.dQ, a.dqlow, a.epd);
-  } else {
-    hipLaunchKernelGGL((bwd_keys_kernel<T, D, DP>), grid, dim3(kThreads),
-                       kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.dO), a.q32, a.seg_off, a.seg_cnt, a.rec,
-                       a.N, a.k, a.scale, a.sscale, a.dK, a.dV, a.dklow);
-  }
-  return hipGetLastError();
 }
 
 template <typename T, int D>
-hipError_t bwd_passes_d(const BwdArgs& a, hipStream_t s) {
-  switch (a.dp) {
-    case 0: return bwd_passes_t<T, D, 0>(a, s);
-    case 16: return bwd_passes_t<T, D, 16>(a, s);
-    case 32: return bwd_passes_t<T, D, 32>(a, s);
-    case 64: return bwd_passes_t<T, D, 64>(a, s);
-    case 128: return bwd_passes_t<T, D, 128>(a, s);
+hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
+  static std::atomic<int> lds_rows[kMaxDevices], lds_keys[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_kernel<T, D>),
+                                    kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rows);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_kernel<T, D>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_keys);
+  if (e != hipSuccess) return e;
+  const dim3 grid((a.N + kWaves - 1) / kWaves, a.nh);
+  const float out_scale = a.scorer ? 1.0f : a.scale;
+  if (a.pass == 0) {
+    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), grid, dim3(kThreads),
+                       kWaves * bwd_row_wave_floats(a.k) * 4, s, static_cast<const T*>(a.Q),
+                       static_cast<const T*>(a.K), static_cast<const T*>(a.V),
+                       static_cast<const T*>(a.dO), a.idx, a.k, a.N, a.scale, out_scale, a.dQ,
+                       a.epd);
+  } else {
+    hipLaunchKernelGGL((bwd_keys_kernel<T, D>), grid, dim3(kThreads),
+                       kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
+                       static_cast<const T*>(a.dO), a.seg_off, a.seg_cnt, a.rec, a.N, a.k,
+                       out_scale, a.dK, a.dV);
   }
-  return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s) {
   if (a.dtype == 0) {
-    if (a.D == 64) return bwd_passes_d<float, 64>(a, s);
-    if (a.D == 128) return bwd_passes_d<float, 128>(a, s);
+    if (a.D == 64) return bwd_passes_t<float, 64>(a, s);
+    if (a.D == 128) return bwd_passes_t<float, 128>(a, s);
   } else {
-    if (a.D == 64) return bwd_passes_d<bf16_t, 64>(a, s);
-    if (a.D == 128) return bwd_passes_d<bf16_t, 128>(a, s);
+    if (a.D == 64) return bwd_passes_t<bf16_t, 64>(a, s);
+    if (a.D == 128) return bwd_passes_t<bf16_t, 128>(a, s);
   }
   return hipErrorInvalidValue;
 }

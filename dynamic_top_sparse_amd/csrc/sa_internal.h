@@ -217,12 +217,12 @@ struct BwdEntry {
 };
 struct BwdArgs {
   int pass;             // 0: row pass, 1: key pass
-  int dtype, D, dp, k, N, nh;
-  float scale, sscale;
+  int dtype, D, k, N, nh;
+  int scorer;           // scorer gradients follow: store the sums unscaled
+  float scale;
   const void *Q, *K, *V, *dO;
   const int32_t* idx;
-  const float *q32, *k32;       // fp32 projections (scorer gradient only)
-  float *dQ, *dK, *dV, *dqlow, *dklow;
+  float *dQ, *dK, *dV;
   float2* epd;                  // (p_t, dl_t) of every idx entry, in idx's layout
   const int *seg_off, *seg_cnt; // key pass: each key's segment of `rec`
   const BwdEntry* rec;          // per head, the entries grouped by key
@@ -237,9 +237,12 @@ hipError_t launch_bwd_slice_prefix(int* cnt_s, int S, long long total, int* cnt,
 hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t s);
 hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N, int k,
                            const int* cnt_s, const int* off, BwdEntry* rec, hipStream_t s);
-// out[r][d] += sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
+// out[r][d] = pre * out[r][d] + sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
 hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
-                                int dp, float* out, hipStream_t s);
+                                int dp, float pre, float* out, hipStream_t s);
+// out[r][c] = alpha * sum_d X[r][d] * P[d][c] over rows r (X fp32, P [D][dp] of dtype)
+hipError_t launch_rows_times_p(const float* X, const void* P, int dtype, long long rows, int D,
+                               int dp, float alpha, float* out, hipStream_t s);
 // dP[d][c] = sum_r X[r][d] * lo[r][c] over all rows (X of dtype), in a
 // fixed order through per-chunk partials
 hipError_t launch_outer_sum(const void* X, int dtype, const float* lo, long long rows, int D,
