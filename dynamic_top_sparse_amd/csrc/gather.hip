@@ -661,6 +661,118 @@ __device__ __forceinline__ void store_f32_row(float* dst, const float (&v)[EPL],
     *reinterpret_cast<float4*>(dst + e) = make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
 }
 
+// Cross-group combination for the row pass: lanes holding the same row
+// elements in different row groups (xor partners LPR .. 32).
+template <int LPR>
+__device__ __forceinline__ float groups_sum(float v) {
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+    v = o == 32 ? sum_xor32(v) : o == 16 ? sum_xor16(v) : v + __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int LPR>
+__device__ __forceinline__ float groups_max(float v) {
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+    v = o == 32 ? max_xor32(v) : o == 16 ? max_xor16(v) : fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// K pass of the backward row, one read of each kept K row: the logits
+// (base 2, into slog) and, per row group over the entries it loads, the sums
+//   S = sum e_t, U = sum e_t dp_t, A = sum e_t dp_t K_t, B = sum e_t K_t,
+// with e_t = 2^(l_t - m) for the group's running maximum m (the sums are
+// rescaled when m grows).  dp_t comes from sdp.  Then
+//   p_t = e_t / S, delta = U / S, sum_t dl_t K_t = (A - delta B) / S
+// once the groups are combined at the largest m.
+template <typename T, int D>
+__device__ __forceinline__ void bwd_logits_online(const T* __restrict__ qrow,
+                                                  const T* __restrict__ K,
+                                                  const int32_t* __restrict__ row, int n, int N,
+                                                  float scale2, float* slog,
+                                                  const float* sdp, int& bad, float& m,
+                                                  float& S, float& U,
+                                                  float (&A)[Vec<T>::kElems],
+                                                  float (&B)[Vec<T>::kElems]) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, RPI = kWave / LPR;
+  const int l = lane_id();
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float qf[EPL];
+  Vec<T>::unpack(*reinterpret_cast<const uint4*>(qrow + e0), qf);
+  m = -INFINITY;
+  S = U = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) A[e] = B[e] = 0.0f;
+  for (int tb = 0; tb < n; tb += RPI * kUnroll) {
+    const int nu = min(kUnroll, (n - tb + RPI - 1) / RPI);   // loads holding rows (uniform)
+    uint4 kv[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const int jr = row[t];                       // t < n + RPI: inside the slack
+      const int j = t < n ? jr : -1;
+      ok[u] = j >= 0 && j < N;
+      bad |= (t < n && j >= N) ? 1 : 0;
+      kv[u] = *reinterpret_cast<const uint4*>(K + static_cast<size_t>(ok[u] ? j : 0) * D + e0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      float kf[EPL];
+      Vec<T>::unpack(kv[u], kf);
+      float dot = 0.0f;
+      if constexpr (sizeof(T) == 2) {
+        bf16x2 kp[4], qp[4];
+        const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + e0);
+        __builtin_memcpy(kp, &kv[u], 16);
+        __builtin_memcpy(qp, &q4, 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[i], dot, false);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
+      }
+      dot = group_sum<LPR>(dot);
+      const float lt = ok[u] ? dot * scale2 : -INFINITY;
+      if ((l % LPR) == 0 && t < n) slog[t] = lt;
+      if (lt > m) {                 // the whole group agrees: lt and m are group values
+        const float c = __builtin_amdgcn_exp2f(m - lt);   // m = -inf gives 0
+        S *= c;
+        U *= c;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          A[e] *= c;
+          B[e] *= c;
+        }
+        m = lt;
+      }
+      const float ew = ok[u] ? __builtin_amdgcn_exp2f(lt - m) : 0.0f;
+      const float ed = ok[u] ? ew * sdp[t] : 0.0f;
+      S += ew;
+      U += ed;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        A[e] = __builtin_fmaf(ed, kf[e], A[e]);
+        B[e] = __builtin_fmaf(ew, kf[e], B[e]);
+      }
+    }
+  }
+  // combine the groups at the largest maximum
+  const float M = groups_max<LPR>(m);
+  const float c = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+  S = groups_sum<LPR>(S * c);
+  U = groups_sum<LPR>(U * c);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    A[e] = groups_sum<LPR>(A[e] * c);
+    B[e] = groups_sum<LPR>(B[e] * c);
+  }
+  m = M;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -671,52 +783,45 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane_id();
   const int SL = gather_slog_floats(k);
-  float* sl = bwd_lds + w * bwd_row_wave_floats(k);      // logits, then p_t
-  float* sd = sl + SL;                                    // dp_t, then dl_t
+  float* sl = bwd_lds + w * bwd_row_wave_floats(k);      // logits
+  float* sd = sl + SL;                                    // dp_t
   int* sidx = reinterpret_cast<int*>(sd + SL);
   const int h = blockIdx.y;
   const int q = blockIdx.x * kWaves + w;
   if (q >= N) return;
   const size_t hN = static_cast<size_t>(h) * N;
-  const T* Kh = K + hN * D;
-  const T* Vh = V + hN * D;
   stage_entries(idx + (hN + q) * k, 0, k, sidx);
   int bad = 0;
-  logits<T, D>(Q + (hN + q) * D, Kh, sidx, 0, k, N, scale * kLog2e, sl, bad);
-  logits<T, D>(dO + (hN + q) * D, Vh, sidx, 0, k, N, 1.0f, sd, bad);
+  // dp_t = dO·V_t first (V rows), then one pass over the K rows
+  logits<T, D>(dO + (hN + q) * D, V + hN * D, sidx, 0, k, N, 1.0f, sd, bad);
+  wave_sync();
+  float m, S, U, A[EPL], B[EPL];
+  bwd_logits_online<T, D>(Q + (hN + q) * D, K + hN * D, sidx, k, N, scale * kLog2e, sl, sd, bad,
+                          m, S, U, A, B);
   if (bad) atomicOr(&g_index_error_flag, 1);
   wave_sync();
-  float sum;
-  const float mx = softmax_weights(sl, k, sum);
   const int g = l / LPR, e0 = (l % LPR) * EPL;
-  float acc[EPL];
   float2* er = epd + (hN + q) * static_cast<size_t>(k);
-  if (mx == -INFINITY) {    // no valid entry: no gradient from this row
+  float acc[EPL];
+  if (m == -INFINITY) {    // no valid entry: no gradient from this row
     for (int t = l; t < k; t += kWave) er[t] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
     if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
     return;
   }
-  // p_t, delta, dl_t (invalid entries have p_t = 0 and contribute nothing)
-  const float inv = 1.0f / sum;
-  float dsum = 0.0f;
-  for (int t = l; t < k; t += kWave) {
-    const float p = sl[t] * inv;
-    sl[t] = p;
-    dsum += p != 0.0f ? p * sd[t] : 0.0f;
-  }
-  const float delta = wave_sum(dsum);
-  for (int t = l; t < k; t += kWave) {
-    const float p = sl[t];
-    sd[t] = p != 0.0f ? p * (sd[t] - delta) : 0.0f;
-  }
-  wave_sync();
-  weighted_rows<T, D>(Kh, sidx, 0, k, N, sd, acc);
+  const float inv = 1.0f / S;
+  const float delta = U * inv;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = (A[e] - delta * B[e]) * inv;
   if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, out_scale);
   // (p_t, dl_t) for the key pass, in idx's layout (entries that name no key
   // hold p_t = 0 and are never read)
-  for (int t = l; t < k; t += kWave) er[t] = make_float2(sl[t], sd[t]);
+  for (int t = l; t < k; t += kWave) {
+    const float x = sl[t];
+    const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - m) * inv;
+    er[t] = make_float2(p, p != 0.0f ? p * (sd[t] - delta) : 0.0f);
+  }
 }
 
 template <typename T, int D>
