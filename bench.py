@@ -250,7 +250,7 @@ def oracle_rate(fn, n_total: int, target_s: float = 20.0):
         t = time.perf_counter()
         fn(sorted(rng.choice(n_total, m, replace=False).tolist()))
         tp = time.perf_counter() - t
-        n = int(min(32768, n_total, max(16, m * target_s / max(tp, 1e-4))))
+        n = int(min(n_total, max(16, m * target_s / max(tp, 1e-4))))
         rows = sorted(rng.choice(n_total, n, replace=False).tolist())
         t = time.perf_counter()
         fn(rows)
