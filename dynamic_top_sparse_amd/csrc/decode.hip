@@ -62,6 +62,7 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kScoreUnroll = 8;   // key loads in flight per lane
 constexpr int kSelThreads = 1024; // the select kernel: one big workgroup per head
 constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kSelLoads = 8;      // score loads in flight per thread in the select
 
 template <int DP>
 __global__ __launch_bounds__(kThreads) void decode_score_kernel(
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     int32_t* __restrict__ counts, int Ncap) {
   __shared__ int hist[kSelWaves][256];
   __shared__ int tmp[kSelWaves];
+  __shared__ int wcnt[kSelWaves][2];
   __shared__ int s_digit, s_above;
   const int tid = threadIdx.x;
   const int wv = tid / kWave;
@@ -129,9 +131,20 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
   for (int shift = 24; shift >= 0; shift -= 8) {
     for (int b = tid; b < kSelWaves * 256; b += kSelThreads) (&hist[0][0])[b] = 0;
     __syncthreads();
-    for (int j = tid; j < len; j += kSelThreads) {
-      const uint32_t key = order_key(row[j]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 255], 1);
+    // kSelLoads scores in flight per thread before their histogram updates
+    for (int j0 = tid; j0 < len; j0 += kSelThreads * kSelLoads) {
+      float v[kSelLoads];
+#pragma unroll
+      for (int u = 0; u < kSelLoads; ++u) {
+        const int j = j0 + u * kSelThreads;
+        v[u] = j < len ? row[j] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < kSelLoads; ++u) {
+        const int j = j0 + u * kSelThreads;
+        const uint32_t key = order_key(v[u]);
+        if (j < len && (key & pmask) == prefix) atomicAdd(&hist[wv][(key >> shift) & 255], 1);
+      }
     }
     __syncthreads();
     // thread t < 256 owns bin 255 - t (the sum of the waves' counts)
@@ -151,32 +164,47 @@ __global__ __launch_bounds__(kSelThreads) void decode_select_kernel(
     pmask |= 255u << shift;
     __syncthreads();
   }
-  // each thread owns a contiguous range of keys: two block scans give every
-  // thread its first output position
-  const int L = (len + kSelThreads - 1) / kSelThreads;
-  const int j0 = min(len, tid * L), j1 = min(len, j0 + L);
-  int gt = 0, eq = 0;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = order_key(row[j]);
-    gt += key > prefix ? 1 : 0;
-    eq += key == prefix ? 1 : 0;
-  }
-  int gt_total, eq_total;
-  const int gt_before = block_excl_scan(gt, tmp, gt_total);
-  const int eq_before = block_excl_scan(eq, tmp, eq_total);
-  const int ties_needed = k_i - gt_total;
+  // K is now the number of ties with the k_i-th key that are kept (the
+  // lowest indices).  One coalesced pass in tiles of kSelThreads keys: each
+  // key's rank among the ties and its output position come from ballots
+  // within the wave and the earlier waves' counts.
+  const int ties_needed = K;
   int32_t* out = idx + static_cast<size_t>(h) * k;
   int32_t* cnt = counts != nullptr ? counts + static_cast<size_t>(h) * Ncap : nullptr;
-  int pos = gt_before + min(eq_before, ties_needed);
-  int eq_seen = eq_before;
-  for (int j = j0; j < j1; ++j) {
-    const uint32_t key = order_key(row[j]);
-    const bool tie = key == prefix;
-    if (key > prefix || (tie && eq_seen < ties_needed)) {
-      out[pos++] = j;
+  const int lane = lane_id();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int run_sel = 0, run_eq = 0;
+  for (int b0 = 0; b0 < len; b0 += kSelThreads) {
+    const int j = b0 + tid;
+    const uint32_t key = j < len ? order_key(row[j]) : 0u;
+    const bool eq = j < len && key == prefix;
+    const bool gt = j < len && key > prefix;
+    const unsigned long long me = __ballot(eq);
+    if (lane == 0) wcnt[wv][0] = __popcll(me);
+    __syncthreads();
+    int eq_before = run_eq, eq_tile = 0;
+    for (int i = 0; i < kSelWaves; ++i) {
+      const int c = wcnt[i][0];
+      eq_before += i < wv ? c : 0;
+      eq_tile += c;
+    }
+    const bool sel = gt || (eq && eq_before + __popcll(me & below) < ties_needed);
+    const unsigned long long ms = __ballot(sel);
+    if (lane == 0) wcnt[wv][1] = __popcll(ms);
+    __syncthreads();
+    int pos = run_sel, sel_tile = 0;
+    for (int i = 0; i < kSelWaves; ++i) {
+      const int c = wcnt[i][1];
+      pos += i < wv ? c : 0;
+      sel_tile += c;
+    }
+    if (sel) {
+      out[pos + __popcll(ms & below)] = j;
       if (cnt != nullptr) atomicAdd(&cnt[j], 1);
     }
-    eq_seen += tie ? 1 : 0;
+    run_eq += eq_tile;
+    run_sel += sel_tile;
+    __syncthreads();    // wcnt is rewritten by the next tile
   }
   for (int t = k_i + tid; t < k; t += kSelThreads) out[t] = -1;
 }
