@@ -284,7 +284,8 @@ def run_op(args, w) -> int:
         dO = torch.randn(B, H, N, D, generator=gen).to(w.torch_dtype).cuda()
         _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], k, w.causal,
                                     return_idx=True)
-        n_ws = sa.load_library().sparse_attn_bwd_workspace_size(sa.sa_dims(B, H, N, D), dp, k, 1)
+        n_ws = sa.load_library().sparse_attn_bwd_workspace_size(sa.sa_dims(B, H, N, D), dp, k, 1,
+                                                                None)
         bws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
         sum_k = float((idx >= 0).sum().item())
 

@@ -51,7 +51,11 @@ class sa_dims(ctypes.Structure):
 
 
 class sa_options(ctypes.Structure):
-    _fields_ = [("filter_dtype", ctypes.c_int32), ("profile", ctypes.c_void_p)]
+    _fields_ = [("filter_dtype", ctypes.c_int32), ("profile", ctypes.c_void_p),
+                ("bwd_parts", ctypes.c_int32)]
+
+
+BWD_PARTS = {"auto": 0, "whole": 1, "split": 2}
 
 
 class sa_kernel_time(ctypes.Structure):
@@ -108,7 +112,7 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
         "sparse_attn_decode": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32,
                                               f32, i32, vp, vp, vp, vp, sz, op, vp]),
         "sparse_attn_block_workspace_size": (sz, [sa_dims, i32, i32, i32]),
-        "sparse_attn_bwd_workspace_size": (sz, [sa_dims, i32, i32, i32]),
+        "sparse_attn_bwd_workspace_size": (sz, [sa_dims, i32, i32, i32, op]),
         "sparse_attn_decode_noalloc_max_bytes": (sz, []),
         "sparse_attn_decode_noalloc": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32,
                                                       f32, f32, i32, vp, vp, vp, vp]),
@@ -183,9 +187,12 @@ def _filter_code(dtype) -> int:
     raise TypeError(f"filter dtype must be torch.float16 or torch.bfloat16, not {dtype}")
 
 
-def _options(filter_dtype=None, profile: Optional[Profile] = None):
+def _options(filter_dtype=None, profile: Optional[Profile] = None, bwd_parts: str = "auto"):
+    if bwd_parts not in BWD_PARTS:
+        raise ValueError(f"bwd_parts must be one of {sorted(BWD_PARTS)}")
     return ctypes.byref(sa_options(_filter_code(filter_dtype),
-                                   profile.handle if profile is not None else None))
+                                   profile.handle if profile is not None else None,
+                                   BWD_PARTS[bwd_parts]))
 
 
 def _tensor(t, name: str) -> torch.Tensor:
@@ -478,10 +485,11 @@ def sparse_attn_band_indices_per_batch(H: int, N: int, radii: torch.Tensor,
 def sparse_attn_bwd(Q, K, V, dO, idx, Pq=None, Pk=None, scorer_grad: bool = True,
                     score_scale: Optional[float] = None, softmax_scale: Optional[float] = None,
                     workspace: Optional[torch.Tensor] = None,
-                    profile: Optional[Profile] = None):
+                    profile: Optional[Profile] = None, parts: str = "auto"):
     """Gradients of the forward for index sets idx: returns (dQ, dK, dV) in
     fp32, plus (dPq, dPk) when scorer_grad (the straight-through gradient
-    of the scorer; Pq, Pk required)."""
+    of the scorer; Pq, Pk required).  parts: "auto", "whole" or "split",
+    the layout of the library's row and key passes (same results)."""
     _check_qkv(Q, K, V, dO)
     _tensor(idx, "idx")
     if idx.dim() != 4:
@@ -496,7 +504,8 @@ def sparse_attn_bwd(Q, K, V, dO, idx, Pq=None, Pk=None, scorer_grad: bool = True
     ascale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
     lib = load_library()
     if workspace is None:
-        n = int(lib.sparse_attn_bwd_workspace_size(_dims(Q), d_proj, k, int(scorer_grad)))
+        n = int(lib.sparse_attn_bwd_workspace_size(_dims(Q), d_proj, k, int(scorer_grad),
+                                                   _options(None, None, parts)))
         if n == 0:
             raise SparseAttnError(-3, "sparse_attn_bwd_workspace_size")
         workspace = torch.empty(n, dtype=torch.uint8, device=Q.device)
@@ -511,7 +520,7 @@ def sparse_attn_bwd(Q, K, V, dO, idx, Pq=None, Pk=None, scorer_grad: bool = True
         d_proj, k, sscale, ascale, _dtype_code(Q), _dev(dQ, "dQ"), _dev(dK, "dK"),
         _dev(dV, "dV"), _dev(dPq, "dPq") if scorer_grad else None,
         _dev(dPk, "dPk") if scorer_grad else None, _dev(workspace, "workspace"),
-        workspace.numel(), _options(None, profile), _stream(Q))
+        workspace.numel(), _options(None, profile, parts), _stream(Q))
     _check(st, "sparse_attn_bwd")
     return (dQ, dK, dV, dPq, dPk) if scorer_grad else (dQ, dK, dV)
 

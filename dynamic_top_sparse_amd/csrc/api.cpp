@@ -657,11 +657,17 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
 // ----------------------------------------------------------- backward ---
 namespace {
 struct BwdPlan {
-  size_t off_dql, off_dkl, off_cnt, off_off, off_cnts, off_ent, off_epd,
-      off_part, total;
-  int nchunks;
+  size_t off_dql, off_dkl, off_cnt, off_off, off_cnts, off_ent, off_epd, off_stats, off_seg,
+      off_bounds, off_rpart, off_part, total;
+  int nchunks, slices, split_rows, split_keys;
 };
-BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
+// Parts of the backward's passes: automatic picks the key-range split for
+// heads of more than 2^23 row elements (N > 65536 at D = 128: 32 MiB of bf16
+// K and V rows and more), where the whole passes run from the memory-side
+// cache; smaller heads run faster whole (32K at D = 128: 38 against 45 ms).
+int bwd_parts_of(const sa_options* opts) { return opts != nullptr ? opts->bwd_parts : 0; }
+
+BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer, int parts) {
   const size_t BH = static_cast<size_t>(d.B) * d.H, N = static_cast<size_t>(d.N);
   const size_t ents = BH * N * static_cast<size_t>(k);
   BwdPlan p;
@@ -676,9 +682,22 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
   p.off_dkl = take(lo);
   p.off_cnt = take(BH * N * 4);
   p.off_off = take(BH * N * 4);
-  p.off_cnts = take(static_cast<size_t>(bwd_slices(d.N, k)) * BH * N * 4);
+  const bool big = N * static_cast<size_t>(d.D) > (size_t(1) << 23);
+  p.split_rows = parts == SA_BWD_PARTS_SPLIT || (parts == SA_BWD_PARTS_AUTO && big) ? 1 : 0;
+  p.slices = bwd_slices(d.N, k);
+  // the key pass takes its parts from whole groups of row slices
+  if (parts == SA_BWD_PARTS_SPLIT && p.slices % kGatherRanges != 0)
+    p.slices = (p.slices + kGatherRanges - 1) / kGatherRanges * kGatherRanges;
+  p.split_keys = p.split_rows && p.slices % kGatherRanges == 0 ? 1 : 0;
+  p.off_cnts = take(static_cast<size_t>(p.slices) * BH * N * 4);
   p.off_ent = take(ents * sizeof(BwdEntry));
   p.off_epd = take(ents * 8);
+  p.off_stats = take(BH * N * 16);
+  p.off_seg = take(p.split_rows ? BH * N * (kGatherRanges + 1) * 4 : 0);
+  p.off_bounds = take(p.split_rows ? BH * (kGatherRanges + 1) * 4 : 0);
+  const size_t rpart = p.split_rows ? BH * N * kGatherRanges * (2 * d.D + 4) * 4 : 0;
+  const size_t kpart = p.split_keys ? BH * N * kGatherRanges * (2 * d.D) * 4 : 0;
+  p.off_rpart = take(rpart > kpart ? rpart : kpart);
   p.nchunks = scorer ? outer_sum_chunks(static_cast<long long>(BH * N)) : 0;
   p.off_part = take(scorer ? static_cast<size_t>(p.nchunks) * d.D * dp * 4 * 2 : 0);
   p.total = off;
@@ -686,10 +705,13 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer) {
 }
 }  // namespace
 
-size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad) {
+size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad,
+                                      const sa_options* opts) {
   if (check_dims(d, k) != SA_OK || !supported_D(d.D)) return 0;
   if (scorer_grad && !supported_dp(d_proj)) return 0;
-  return bwd_plan(d, d_proj, k, scorer_grad != 0).total;
+  const int parts = bwd_parts_of(opts);
+  if (parts < SA_BWD_PARTS_AUTO || parts > SA_BWD_PARTS_SPLIT) return 0;
+  return bwd_plan(d, d_proj, k, scorer_grad != 0, parts).total;
 }
 
 int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
@@ -712,7 +734,9 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
     return SA_ERR_ALIGN;
   if (scorer && (!aligned16(Pq) || !aligned16(Pk) || !aligned16(dPq) || !aligned16(dPk)))
     return SA_ERR_ALIGN;
-  const BwdPlan p = bwd_plan(d, d_proj, k, scorer);
+  const int parts = bwd_parts_of(opts);
+  if (parts < SA_BWD_PARTS_AUTO || parts > SA_BWD_PARTS_SPLIT) return SA_ERR_SHAPE;
+  const BwdPlan p = bwd_plan(d, d_proj, k, scorer, parts);
   if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
   unsigned char* base = static_cast<unsigned char*>(ws);
   float* dql = reinterpret_cast<float*>(base + p.off_dql);
@@ -733,17 +757,40 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
   a.dQ = dQ; a.dK = dK; a.dV = dV;
   a.seg_off = offs; a.seg_cnt = cnt; a.rec = rec;
   a.epd = reinterpret_cast<float2*>(base + p.off_epd);
+  a.stats = reinterpret_cast<float4*>(base + p.off_stats);
+  a.split_rows = p.split_rows;
+  a.split_keys = p.split_keys;
+  a.slices = p.slices;
+  int* row_seg = reinterpret_cast<int*>(base + p.off_seg);
+  int* bounds = reinterpret_cast<int*>(base + p.off_bounds);
+  a.row_seg = row_seg;
+  a.bounds = bounds;
+  a.slice_pre = cnts;
+  a.part = reinterpret_cast<float*>(base + p.off_rpart);
   const long long rows = static_cast<long long>(a.nh) * d.N;
   sa_profile* prof = profile_of(opts);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  SA_TIMED_STATUS("bwd_count", launch_bwd_hist(idx, a.nh, d.N, k, cnts, s));
-  SA_TIMED_STATUS("bwd_scan", launch_bwd_slice_prefix(cnts, bwd_slices(d.N, k), rows, cnt, s));
+  SA_TIMED_STATUS("bwd_count", launch_bwd_hist(idx, a.nh, d.N, k, p.slices, cnts, s));
+  SA_TIMED_STATUS("bwd_scan", launch_bwd_slice_prefix(cnts, p.slices, rows, cnt, s));
   SA_TIMED_STATUS("bwd_scan", launch_bwd_scan(cnt, a.nh, d.N, offs, s));
   a.pass = 0;
+  if (p.split_rows) {
+    SA_TIMED_STATUS("bwd_scan", launch_bwd_bounds(offs, cnt, a.nh, d.N, bounds, s));
+    SA_TIMED_STATUS("bwd_scan", launch_bwd_row_ranges(idx, bounds, a.nh, d.N, k, row_seg, s));
+  }
   SA_TIMED_STATUS("bwd_rows", launch_bwd_pass(a, s));
-  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.nh, d.N, k, cnts, offs, rec, s));
+  if (p.split_rows)
+    SA_TIMED_STATUS("bwd_rows_merge", launch_bwd_rows_merge(a.part, a.nh, d.N, d.D,
+                                                           scorer ? 1.0f : softmax_scale, dQ,
+                                                           a.stats, s));
+  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.stats, a.nh, d.N, k, p.slices, cnts,
+                                              offs, rec, s));
   a.pass = 1;
   SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
+  if (p.split_keys)
+    SA_TIMED_STATUS("bwd_keys_merge", launch_bwd_keys_merge(a.part, a.nh, d.N, d.D,
+                                                           scorer ? 1.0f : softmax_scale, dK, dV,
+                                                           s));
   if (scorer) {
     // dQ and dK hold G and H (unscaled): the scorer's low-dimensional
     // gradients first, then the full ones

@@ -111,7 +111,8 @@ __global__ void bwd_slice_prefix_kernel(int* __restrict__ cnt_s, int S, long lon
 
 // Places the entries of one (head, slice, window) in their key segments.
 __global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* __restrict__ idx,
-                                                                const float2* __restrict__ epd,
+                                                                const float2* __restrict__ lpd,
+                                                                const float4* __restrict__ stats,
                                                                 int N, int k, int S,
                                                                 int rows_per_slice, int nh,
                                                                 const int* __restrict__ cnt_s,
@@ -131,11 +132,14 @@ __global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* _
               [&](long long g, int j) {
                 const unsigned u = static_cast<unsigned>(j) - w0;
                 if (u < W) {
-                  const float2 pd = epd[g];
+                  // p_t and dl_t from the logit, dp_t and the row's statistics
+                  const float2 ld = lpd[g];
+                  const int e = static_cast<int>(g - hk);
+                  const float4 st = stats[hN + static_cast<unsigned>(e) / static_cast<unsigned>(k)];
                   BwdEntry r;
-                  r.e = static_cast<int>(g - hk);
-                  r.p = pd.x;
-                  r.dl = pd.y;
+                  r.e = e;
+                  r.p = ld.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ld.x - st.x) * st.y;
+                  r.dl = r.p != 0.0f ? r.p * (ld.y - st.z) : 0.0f;
                   rh[atomicAdd(&cur[u], 1)] = r;
                 }
               });
@@ -165,6 +169,162 @@ __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restric
     if (j < N) o[j] = running + before + incl - v;
     running += tot;
     __syncthreads();
+  }
+}
+
+// ----------------------------------------------- key-range split passes ---
+// The row and key passes can run in kGatherRanges parts, part r on XCD r, so
+// that each XCD's L2 serves one part of every head's rows (as the forward's
+// split gather does).  Row pass: part r takes the entries whose key lies in
+// [bounds[r], bounds[r+1]), cut per head so that each part holds about the
+// same number of entries; a row whose valid entries are not an ascending
+// prefix is handled by every part scanning the whole row.  Key pass: part r
+// takes the entries of rows in slices [r S/8, (r+1) S/8), which the fill
+// placed consecutively in each key's segment.  Each part writes a partial
+// result per row or key; the merges add the parts in part order.
+
+// Per head: bounds[h][r] = the smallest key j with at least r/8 of the head's
+// entries below it (off is each key's exclusive entry count), bounds[h][8] = N.
+__global__ void bwd_bounds_kernel(const int* __restrict__ off, const int* __restrict__ cnt, int N,
+                                  int* __restrict__ bounds) {
+  const int h = blockIdx.x, r = threadIdx.x;
+  if (r > kGatherRanges) return;
+  const int* o = off + static_cast<size_t>(h) * N;
+  const long long total = static_cast<long long>(o[N - 1]) + cnt[static_cast<size_t>(h) * N + N - 1];
+  int b;
+  if (r == 0) {
+    b = 0;
+  } else if (r == kGatherRanges) {
+    b = N;
+  } else {
+    const long long target = (total * r + kGatherRanges - 1) / kGatherRanges;
+    int lo = 0, hi = N;        // first j with o[j] >= target (N if none)
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (o[mid] < target) lo = mid + 1; else hi = mid;
+    }
+    b = lo;
+  }
+  bounds[h * (kGatherRanges + 1) + r] = b;
+}
+
+// One wave per row: if the row's valid entries (keys 0..N-1) form a prefix
+// of it in ascending order, seg[row][r] = the number of them below
+// bounds[r] (r = 0..8); else seg[row][0] = -1.
+__global__ __launch_bounds__(kThreads) void bwd_row_ranges_kernel(const int32_t* __restrict__ idx,
+                                                                  const int* __restrict__ bounds,
+                                                                  int N, int k,
+                                                                  int* __restrict__ seg) {
+  constexpr int R = kGatherRanges;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const int q = blockIdx.x * (kThreads / kWave) + w;
+  const int h = blockIdx.y;
+  if (q >= N) return;
+  const size_t row = static_cast<size_t>(h) * N + q;
+  const int32_t* ir = idx + row * k;
+  const int* b = bounds + h * (R + 1);
+  int below[R + 1];
+#pragma unroll
+  for (int r = 0; r <= R; ++r) below[r] = 0;
+  bool ok = true;               // wave-uniform after the ballots
+  int last = -1;                // previous chunk's last entry (valid or not)
+  for (int t0 = 0; t0 < k; t0 += kWave) {
+    const int t = t0 + l;
+    const int j = t < k ? ir[t] : -1;
+    const bool valid = j >= 0 && j < N;
+    int prev = __shfl_up(j, 1, kWave);
+    if (l == 0) prev = last;
+    const bool prev_valid = prev >= 0 && prev < N;
+    // a valid entry right after an invalid one, or below its predecessor
+    const bool bad = valid && ((t > 0 && !prev_valid) || (prev_valid && prev > j));
+    if (__ballot(bad)) ok = false;
+#pragma unroll
+    for (int r = 1; r < R; ++r) below[r] += valid && j < b[r] ? 1 : 0;
+    below[R] += valid ? 1 : 0;
+    last = __shfl(j, kWave - 1, kWave);
+  }
+  int* out = seg + row * (R + 1);
+  if (!ok) {
+    if (l == 0) out[0] = -1;
+    return;
+  }
+#pragma unroll
+  for (int r = 1; r <= R; ++r) below[r] = wave_sum_i(below[r]);
+  if (l == 0) {
+    out[0] = 0;
+#pragma unroll
+    for (int r = 1; r <= R; ++r) out[r] = below[r];
+  }
+}
+
+// Row parts -> dQ (out_scale times G) and the row's statistics
+// (max logit, 1/S, delta); a part record is (m, S, U, -, A[D], B[D]).
+__global__ __launch_bounds__(kThreads) void bwd_rows_merge_kernel(const float* __restrict__ part,
+                                                                  int N, int D, float out_scale,
+                                                                  float* __restrict__ dQ,
+                                                                  float4* __restrict__ stats) {
+  constexpr int R = kGatherRanges;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const int q = blockIdx.x * (kThreads / kWave) + w;
+  if (q >= N) return;
+  const size_t row = static_cast<size_t>(blockIdx.y) * N + q;
+  const int PS = 2 * D + 4;
+  const float* pr = part + row * R * PS;
+  float M = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < R; ++r) M = fmaxf(M, pr[r * PS]);
+  float* dq = dQ + row * D;
+  if (M == -INFINITY) {     // no valid entry in any part
+    for (int e = l; e < D; e += kWave) dq[e] = 0.0f;
+    if (l == 0) stats[row] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+    return;
+  }
+  float c[R];
+  float S = 0.0f, U = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float m = pr[r * PS];
+    c[r] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+    if (m != -INFINITY) {
+      S = __builtin_fmaf(c[r], pr[r * PS + 1], S);
+      U = __builtin_fmaf(c[r], pr[r * PS + 2], U);
+    }
+  }
+  const float inv = 1.0f / S, delta = U * inv;
+  for (int e = l; e < D; e += kWave) {
+    float a = 0.0f, bsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      if (c[r] != 0.0f) {
+        a = __builtin_fmaf(c[r], pr[r * PS + 4 + e], a);
+        bsum = __builtin_fmaf(c[r], pr[r * PS + 4 + D + e], bsum);
+      }
+    }
+    dq[e] = out_scale * ((a - delta * bsum) * inv);
+  }
+  if (l == 0) stats[row] = make_float4(M, inv, delta, 0.0f);
+}
+
+// Key parts (dV[D], H[D]) -> dV and dK (out_scale times H), parts in order.
+__global__ __launch_bounds__(kThreads) void bwd_keys_merge_kernel(const float* __restrict__ part,
+                                                                  int N, int D, float out_scale,
+                                                                  float* __restrict__ dK,
+                                                                  float* __restrict__ dV) {
+  constexpr int R = kGatherRanges;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const int j = blockIdx.x * (kThreads / kWave) + w;
+  if (j >= N) return;
+  const size_t row = static_cast<size_t>(blockIdx.y) * N + j;
+  const float* pr = part + row * R * 2 * D;
+  for (int e = l; e < D; e += kWave) {
+    float v = 0.0f, hsum = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      v += pr[r * 2 * D + e];
+      hsum += pr[r * 2 * D + D + e];
+    }
+    dV[row * D + e] = v;
+    dK[row * D + e] = out_scale * hsum;
   }
 }
 
@@ -443,9 +603,9 @@ struct HistGrid {
   int S, rows_per_slice;
   size_t lds;
 };
-HistGrid hist_grid(int nh, int N, int k) {
+HistGrid hist_grid(int nh, int N, int S) {
   HistGrid g;
-  g.S = bwd_slices(N, k);
+  g.S = S;
   g.rows_per_slice = (N + g.S - 1) / g.S;
   const int nwin = (N + kHistWindow - 1) / kHistWindow;
   g.grid = dim3(g.S * nwin, nh);
@@ -454,12 +614,13 @@ HistGrid hist_grid(int nh, int N, int k) {
 }
 }  // namespace
 
-hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int* cnt_s, hipStream_t s) {
+hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int S, int* cnt_s,
+                           hipStream_t s) {
   static std::atomic<int> lds_set[kMaxDevices];
   hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_hist_kernel),
                                     kHistWindow * 4, lds_set);
   if (e != hipSuccess) return e;
-  const HistGrid g = hist_grid(nh, N, k);
+  const HistGrid g = hist_grid(nh, N, S);
   hipLaunchKernelGGL(bwd_hist_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, N, k, g.S,
                      g.rows_per_slice, nh, cnt_s);
   return hipGetLastError();
@@ -476,15 +637,45 @@ hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t 
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N, int k,
-                           const int* cnt_s, const int* off, BwdEntry* rec, hipStream_t s) {
+hipError_t launch_bwd_fill(const int32_t* idx, const float2* lpd, const float4* stats, int nh,
+                           int N, int k, int S, const int* cnt_s, const int* off, BwdEntry* rec,
+                           hipStream_t s) {
   static std::atomic<int> lds_set[kMaxDevices];
   hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_fill_kernel),
                                     kHistWindow * 4, lds_set);
   if (e != hipSuccess) return e;
-  const HistGrid g = hist_grid(nh, N, k);
-  hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, epd, N, k, g.S,
-                     g.rows_per_slice, nh, cnt_s, off, rec);
+  const HistGrid g = hist_grid(nh, N, S);
+  hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, lpd, stats, N, k,
+                     g.S, g.rows_per_slice, nh, cnt_s, off, rec);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_bounds(const int* off, const int* cnt, int nh, int N, int* bounds,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(bwd_bounds_kernel, dim3(nh), dim3(kWave), 0, s, off, cnt, N, bounds);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_row_ranges(const int32_t* idx, const int* bounds, int nh, int N, int k,
+                                 int* seg, hipStream_t s) {
+  const dim3 grid((N + kThreads / kWave - 1) / (kThreads / kWave), nh);
+  hipLaunchKernelGGL(bwd_row_ranges_kernel, grid, dim3(kThreads), 0, s, idx, bounds, N, k, seg);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows_merge(const float* part, int nh, int N, int D, float out_scale,
+                                 float* dQ, float4* stats, hipStream_t s) {
+  const dim3 grid((N + kThreads / kWave - 1) / (kThreads / kWave), nh);
+  hipLaunchKernelGGL(bwd_rows_merge_kernel, grid, dim3(kThreads), 0, s, part, N, D, out_scale, dQ,
+                     stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_keys_merge(const float* part, int nh, int N, int D, float out_scale,
+                                 float* dK, float* dV, hipStream_t s) {
+  const dim3 grid((N + kThreads / kWave - 1) / (kThreads / kWave), nh);
+  hipLaunchKernelGGL(bwd_keys_merge_kernel, grid, dim3(kThreads), 0, s, part, N, D, out_scale, dK,
+                     dV);
   return hipGetLastError();
 }
 

@@ -777,7 +777,8 @@ template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const T* __restrict__ dO, const int32_t* __restrict__ idx, int k, int N, float scale,
-    float out_scale, float* __restrict__ dQ, float2* __restrict__ epd) {
+    float out_scale, float* __restrict__ dQ, float2* __restrict__ lpd,
+    float4* __restrict__ stats) {
   constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
   extern __shared__ float bwd_lds[];
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -801,13 +802,16 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
   if (bad) atomicOr(&g_index_error_flag, 1);
   wave_sync();
   const int g = l / LPR, e0 = (l % LPR) * EPL;
-  float2* er = epd + (hN + q) * static_cast<size_t>(k);
+  // (logit, dp_t) in idx's layout and the row's (max, 1/S, delta): the fill
+  // forms p_t and dl_t from them (entries that name no key are never read)
+  float2* er = lpd + (hN + q) * static_cast<size_t>(k);
+  for (int t = l; t < k; t += kWave) er[t] = make_float2(sl[t], sd[t]);
   float acc[EPL];
   if (m == -INFINITY) {    // no valid entry: no gradient from this row
-    for (int t = l; t < k; t += kWave) er[t] = make_float2(0.0f, 0.0f);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
     if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
+    if (l == 0) stats[hN + q] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
     return;
   }
   const float inv = 1.0f / S;
@@ -815,12 +819,127 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = (A[e] - delta * B[e]) * inv;
   if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, out_scale);
-  // (p_t, dl_t) for the key pass, in idx's layout (entries that name no key
-  // hold p_t = 0 and are never read)
-  for (int t = l; t < k; t += kWave) {
-    const float x = sl[t];
-    const float p = x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x - m) * inv;
-    er[t] = make_float2(p, p != 0.0f ? p * (sd[t] - delta) : 0.0f);
+  if (l == 0) stats[hN + q] = make_float4(m, inv, delta, 0.0f);
+}
+
+// Row pass, part r of a key-range split (see bwd.hip): the entries of the
+// row whose keys lie in [bounds[r], bounds[r+1]) -- one segment of a row
+// whose valid entries are an ascending prefix, else the whole row with the
+// other keys masked -- give (logit, dp_t) in idx's layout and the part's
+// record (m, S, U, -, A[D], B[D]).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_rows_split_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const int32_t* __restrict__ idx, const int* __restrict__ seg,
+    const int* __restrict__ bounds, int k, int N, float scale, float2* __restrict__ lpd,
+    float* __restrict__ part) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, R = kGatherRanges, PS = 2 * D + 4;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  // consecutive workgroups land on consecutive XCDs: part r runs on XCD r
+  const int r = static_cast<int>(blockIdx.x) % R;
+  const int q = static_cast<int>(blockIdx.x) / R * kWaves + w;
+  const int h = blockIdx.y;
+  if (q >= N) return;
+  const int SL = gather_slog_floats(k);
+  float* sl = bwd_lds + w * bwd_row_wave_floats(k);
+  float* sd = sl + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const size_t hN = static_cast<size_t>(h) * N, row = hN + q;
+  const int* sg = seg + row * (R + 1);
+  const bool sorted = __builtin_amdgcn_readfirstlane(sg[0]) >= 0;
+  const int t0 = sorted ? __builtin_amdgcn_readfirstlane(sg[r]) : 0;
+  const int t1 = sorted ? __builtin_amdgcn_readfirstlane(sg[r + 1]) : k;
+  float* rec = part + (row * R + r) * PS;
+  if (t0 >= t1) {
+    if (l == 0) rec[0] = -INFINITY;   // empty part: the merge skips it
+    return;
+  }
+  const int lo = bounds[h * (R + 1) + r], hi = bounds[h * (R + 1) + r + 1];
+  const int32_t* ir = idx + row * k;
+  const int n = t1 - t0;
+  for (int t = l; t < n; t += kWave) {
+    const int j = ir[t0 + t];
+    sidx[t] = j >= lo && j < hi ? j : -1;
+  }
+  wave_sync();
+  int bad = 0;
+  logits<T, D>(dO + row * D, V + hN * D, sidx, 0, n, N, 1.0f, sd, bad);
+  wave_sync();
+  float m, S, U, A[EPL], B[EPL];
+  bwd_logits_online<T, D>(Q + row * D, K + hN * D, sidx, n, N, scale * kLog2e, sl, sd, bad, m, S,
+                          U, A, B);
+  wave_sync();
+  float2* er = lpd + row * k + t0;
+  for (int t = l; t < n; t += kWave)
+    if (sidx[t] >= 0) er[t] = make_float2(sl[t], sd[t]);
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      *reinterpret_cast<float4*>(rec + 4 + e0 + e) = make_float4(A[e], A[e + 1], A[e + 2], A[e + 3]);
+      *reinterpret_cast<float4*>(rec + 4 + D + e0 + e) =
+          make_float4(B[e], B[e + 1], B[e + 2], B[e + 3]);
+    }
+  }
+  if (l == 0) *reinterpret_cast<float4*>(rec) = make_float4(m, S, U, 0.0f);
+}
+
+// Key pass, part r: the key's records from rows of slices [r S/8, (r+1) S/8)
+// (consecutive in its segment) give the part's (dV[D], H[D]).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
+    const T* __restrict__ Q, const T* __restrict__ dO, const int* __restrict__ seg_off,
+    const int* __restrict__ seg_cnt, const int* __restrict__ slice_pre, int S, long long total,
+    const BwdEntry* __restrict__ rec, int N, int k, float* __restrict__ part) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, R = kGatherRanges;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int r = static_cast<int>(blockIdx.x) % R;
+  const int j = static_cast<int>(blockIdx.x) / R * kWaves + w;
+  const int h = blockIdx.y;
+  if (j >= N) return;
+  constexpr int SL = gather_slog_floats(kBwdChunk);
+  float* sp = bwd_lds + w * bwd_key_wave_floats();
+  float* sd = sp + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const size_t hN = static_cast<size_t>(h) * N, key = hN + j;
+  const int s0 = r * (S / R), s1 = (r + 1) * (S / R);
+  const int a0 = slice_pre[static_cast<size_t>(s0) * total + key];
+  const int a1 = s1 < S ? slice_pre[static_cast<size_t>(s1) * total + key] : seg_cnt[key];
+  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[key] + a0);
+  const int n = a1 - a0;
+  const unsigned uk = static_cast<unsigned>(k);
+  const T* Qh = Q + hN * D;
+  const T* dOh = dO + hN * D;
+  float av[EPL], ak[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
+    const int m = min(kBwdChunk, n - c0);
+    for (int t = l; t < m; t += kWave) {
+      const BwdEntry re = rec[o0 + c0 + t];
+      sidx[t] = static_cast<int>(static_cast<unsigned>(re.e) / uk);
+      sp[t] = re.p;
+      sd[t] = re.dl;
+    }
+    wave_sync();
+    float tmp[EPL];
+    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
+    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    wave_sync();
+  }
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float* pr = part + (key * R + r) * 2 * D;
+  if (g == 0) {
+    store_f32_row<EPL>(pr + e0, av, 1.0f);
+    store_f32_row<EPL>(pr + D + e0, ak, 1.0f);
   }
 }
 
@@ -883,19 +1002,37 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
   e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_kernel<T, D>),
                          kWaves * bwd_key_wave_floats() * 4, lds_keys);
   if (e != hipSuccess) return e;
-  const dim3 grid((a.N + kWaves - 1) / kWaves, a.nh);
+  static std::atomic<int> lds_rs[kMaxDevices], lds_ks[kMaxDevices];
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_split_kernel<T, D>),
+                         kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rs);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_ks);
+  if (e != hipSuccess) return e;
+  const int nb = (a.N + kWaves - 1) / kWaves;
+  const dim3 grid(nb, a.nh), grid_split(nb * kGatherRanges, a.nh);
   const float out_scale = a.scorer ? 1.0f : a.scale;
-  if (a.pass == 0) {
-    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), grid, dim3(kThreads),
-                       kWaves * bwd_row_wave_floats(a.k) * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.K), static_cast<const T*>(a.V),
-                       static_cast<const T*>(a.dO), a.idx, a.k, a.N, a.scale, out_scale, a.dQ,
-                       a.epd);
+  const size_t lds_r = static_cast<size_t>(kWaves) * bwd_row_wave_floats(a.k) * 4;
+  const size_t lds_k = static_cast<size_t>(kWaves) * bwd_key_wave_floats() * 4;
+  if (a.pass == 0 && !a.split_rows) {
+    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), grid, dim3(kThreads), lds_r, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
+                       static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.idx, a.k, a.N,
+                       a.scale, out_scale, a.dQ, a.epd, a.stats);
+  } else if (a.pass == 0) {
+    hipLaunchKernelGGL((bwd_rows_split_kernel<T, D>), grid_split, dim3(kThreads), lds_r, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
+                       static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.idx,
+                       a.row_seg, a.bounds, a.k, a.N, a.scale, a.epd, a.part);
+  } else if (!a.split_keys) {
+    hipLaunchKernelGGL((bwd_keys_kernel<T, D>), grid, dim3(kThreads), lds_k, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
+                       a.seg_cnt, a.rec, a.N, a.k, out_scale, a.dK, a.dV);
   } else {
-    hipLaunchKernelGGL((bwd_keys_kernel<T, D>), grid, dim3(kThreads),
-                       kWaves * bwd_key_wave_floats() * 4, s, static_cast<const T*>(a.Q),
-                       static_cast<const T*>(a.dO), a.seg_off, a.seg_cnt, a.rec, a.N, a.k,
-                       out_scale, a.dK, a.dV);
+    hipLaunchKernelGGL((bwd_keys_split_kernel<T, D>), grid_split, dim3(kThreads), lds_k, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
+                       a.seg_cnt, a.slice_pre, a.slices, static_cast<long long>(a.nh) * a.N,
+                       a.rec, a.N, a.k, a.part);
   }
   return hipGetLastError();
 }

@@ -223,20 +223,37 @@ struct BwdArgs {
   const void *Q, *K, *V, *dO;
   const int32_t* idx;
   float *dQ, *dK, *dV;
-  float2* epd;                  // (p_t, dl_t) of every idx entry, in idx's layout
+  float2* epd;                  // (logit, dp_t) of every idx entry, in idx's layout
+  float4* stats;                // per row: (max logit, 1/S, delta)
   const int *seg_off, *seg_cnt; // key pass: each key's segment of `rec`
   const BwdEntry* rec;          // per head, the entries grouped by key
+  // key-range split of the passes (bwd.hip)
+  int split_rows, split_keys, slices;
+  const int* row_seg;           // per row: part starts (kGatherRanges + 1), or -1
+  const int* bounds;            // per head: part key bounds (kGatherRanges + 1)
+  const int* slice_pre;         // per slice and key: entries of the earlier slices
+  float* part;                  // the parts' records
 };
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
 // Key segments of the entry list, built from idx alone: per-slice counts of
 // each key (LDS histograms over windows of keys), their prefix over slices,
 // each key's segment start, then the entries written into their segments.
 int bwd_slices(int N, int k);
-hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int* cnt_s, hipStream_t s);
+hipError_t launch_bwd_hist(const int32_t* idx, int nh, int N, int k, int S, int* cnt_s,
+                           hipStream_t s);
 hipError_t launch_bwd_slice_prefix(int* cnt_s, int S, long long total, int* cnt, hipStream_t s);
 hipError_t launch_bwd_scan(const int* cnt, int nh, int N, int* off, hipStream_t s);
-hipError_t launch_bwd_fill(const int32_t* idx, const float2* epd, int nh, int N, int k,
-                           const int* cnt_s, const int* off, BwdEntry* rec, hipStream_t s);
+hipError_t launch_bwd_fill(const int32_t* idx, const float2* lpd, const float4* stats, int nh,
+                           int N, int k, int S, const int* cnt_s, const int* off, BwdEntry* rec,
+                           hipStream_t s);
+hipError_t launch_bwd_bounds(const int* off, const int* cnt, int nh, int N, int* bounds,
+                             hipStream_t s);
+hipError_t launch_bwd_row_ranges(const int32_t* idx, const int* bounds, int nh, int N, int k,
+                                 int* seg, hipStream_t s);
+hipError_t launch_bwd_rows_merge(const float* part, int nh, int N, int D, float out_scale,
+                                 float* dQ, float4* stats, hipStream_t s);
+hipError_t launch_bwd_keys_merge(const float* part, int nh, int N, int D, float out_scale,
+                                 float* dK, float* dV, hipStream_t s);
 // out[r][d] = pre * out[r][d] + sum_c lo[r][c] * P[d][c] over rows r (P [D][dp] of dtype)
 hipError_t launch_rows_times_pt(const float* lo, const void* P, int dtype, long long rows, int D,
                                 int dp, float pre, float* out, hipStream_t s);

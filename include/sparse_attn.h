@@ -75,7 +75,7 @@ typedef struct sa_profile sa_profile;
 
 /*
  * Options of a compute call, read while the call runs and never kept.
- * Passing NULL is the same as { SA_F16, NULL }.
+ * Passing NULL is the same as { SA_F16, NULL, SA_BWD_PARTS_AUTO }.
  *   filter_dtype: operand type of the 16-bit MFMA filter inside
  *     sparse_attn_scores_topk and sparse_attn_fwd, SA_F16 or SA_BF16.  Rows
  *     are scaled by powers of two before rounding (one exponent per query
@@ -85,10 +85,18 @@ typedef struct sa_profile sa_profile;
  *     exact fp32 score.  fp16 keeps 11 significant bits instead of 8, which
  *     shrinks the band of keys that must be re-scored exactly.
  *   profile: NULL, or a timing record that receives this call's launches.
+ *   bwd_parts: how sparse_attn_bwd lays out its row and key passes.
+ *     SA_BWD_PARTS_AUTO picks by size; SA_BWD_PARTS_WHOLE runs one wave per
+ *     whole row and per whole key; SA_BWD_PARTS_SPLIT cuts both into eight
+ *     key (row) ranges, one per XCD, and adds the parts.  The results agree
+ *     to fp32 rounding; only the time and the workspace differ (the size
+ *     query takes the same options).
  */
+enum { SA_BWD_PARTS_AUTO = 0, SA_BWD_PARTS_WHOLE = 1, SA_BWD_PARTS_SPLIT = 2 };
 typedef struct {
   int32_t filter_dtype;
   sa_profile* profile;
+  int32_t bwd_parts;
 } sa_options;
 
 /*
@@ -192,12 +200,15 @@ int sparse_attn_band_indices(sa_dims d, int32_t w_left, int32_t w_right, int32_t
  *   k_low = K·Pk to dPq, dPk (summed over every head and row) and into dQ,
  *   dK.  With dPq = dPk = NULL only the attention path is computed.
  *   dK and dV add each key's contributions in an order that can differ
- *   from run to run (the entry lists are filled with atomics), so they agree
- *   between runs to fp32 rounding, not bit for bit.
- *   ws: sparse_attn_bwd_workspace_size(d, d_proj, k, scorer) bytes (about
- *   12 bytes per idx entry plus, for the scorer, four fp32 projections).
+ *   from run to run (the entry lists are grouped by key through LDS
+ *   atomics), so they agree between runs to fp32 rounding, not bit for bit.
+ *   ws: sparse_attn_bwd_workspace_size(d, d_proj, k, scorer, opts) bytes
+ *   (about 20 bytes per idx entry, plus the parts' records when the passes
+ *   are split: about 8·(2·D + 4)·4 bytes per row).
+ *   Errors: SA_ERR_SHAPE for a bwd_parts value other than the three above.
  */
-size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad);
+size_t sparse_attn_bwd_workspace_size(sa_dims d, int32_t d_proj, int32_t k, int32_t scorer_grad,
+                                      const sa_options* opts);
 int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
                     const void* dO, const int32_t* idx, sa_dims d, int32_t d_proj, int32_t k,
                     float score_scale, float softmax_scale, int32_t dtype, float* dQ, float* dK,

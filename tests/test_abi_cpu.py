@@ -246,3 +246,22 @@ def test_decode_and_block_validation(lib):
     assert bt(A, A, A, A, d, 16, 64, 33, 0, 0.25, 0, A, A, bws, None, None) == -3
     assert bt(A, A, A, A, d, 16, 64, 4, 0, 0.25, 0, A, A, 16, None, None) == -5
     assert bt(A, A, A, A, d, 16, 64, 4, 0, 0.25, 0, None, A, bws, None, None) == -1
+
+
+def test_bwd_parts_option_sizes():
+    """The backward's workspace query follows the parts option: the split
+    layout needs room for the parts' records, an unknown value gets 0."""
+    lib = sa.load_library()
+    d = sa.sa_dims(1, 2, 4096, 128)
+    size = {}
+    for name, code in sa.BWD_PARTS.items():
+        o = sa.sa_options(0, None, code)
+        size[name] = lib.sparse_attn_bwd_workspace_size(d, 64, 64, 1, ctypes.byref(o))
+    assert size["whole"] > 0 and size["split"] > size["whole"]
+    assert size["auto"] == size["whole"]          # a small head runs whole
+    assert lib.sparse_attn_bwd_workspace_size(d, 64, 64, 1, None) == size["auto"]
+    bad = sa.sa_options(0, None, 7)
+    assert lib.sparse_attn_bwd_workspace_size(d, 64, 64, 1, ctypes.byref(bad)) == 0
+    with pytest.raises(ValueError):
+        sa._options(None, None, "halves")
+

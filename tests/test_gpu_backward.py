@@ -32,6 +32,7 @@ def _close(got, want, rel, name):
     (1200, 48, 128, 64, "bf16", True),
     (900, 900, 64, 32, "bf16", False),       # every key kept: dense attention's gradient
     (2000, 7, 128, 128, "f32", True),
+    (8500, 40, 64, 16, "f32", True),
 ])
 def test_backward_matches_oracle(N, k, D, dp, dtype, causal):
     w = W.Workload("bwd", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
@@ -41,19 +42,22 @@ def test_backward_matches_oracle(N, k, D, dp, dtype, causal):
     g = {n: t.cuda() for n, t in x.items()}
     idx = sa.sparse_attn_scores_topk(g["Q"], g["K"], g["Pq"], g["Pk"], k, causal)
     sscale, ascale = sa.default_score_scale(dp), sa.default_softmax_scale(D)
-    got = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, g["Pq"], g["Pk"])
     want = O.sparse_attn_backward(x["Q"], x["K"], x["V"], x["Pq"], x["Pk"], _np(idx), dO,
                                   sscale, ascale, scorer_grad=True)
-    for name, a, b in zip(("dQ", "dK", "dV"), got[:3], want[:3]):
-        _close(_np(a), b, 1e-5, name)
-    for name, a, b in zip(("dPq", "dPk"), got[3:], want[3:]):
-        _close(_np(a), b, 1e-4, name)
-    # the attention path alone
-    att = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False)
     want0 = O.sparse_attn_backward(x["Q"], x["K"], x["V"], x["Pq"], x["Pk"], _np(idx), dO,
                                    sscale, ascale, scorer_grad=False)
-    for name, a, b in zip(("dQ", "dK", "dV"), att, want0[:3]):
-        _close(_np(a), b, 1e-5, name)
+    for parts in ("whole", "split"):      # one wave per row / key, or key-range parts
+        got = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, g["Pq"], g["Pk"],
+                                 parts=parts)
+        for name, a, b in zip(("dQ", "dK", "dV"), got[:3], want[:3]):
+            _close(_np(a), b, 1e-5, (parts, name))
+        for name, a, b in zip(("dPq", "dPk"), got[3:], want[3:]):
+            _close(_np(a), b, 1e-4, (parts, name))
+        # the attention path alone
+        att = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False,
+                                 parts=parts)
+        for name, a, b in zip(("dQ", "dK", "dV"), att, want0[:3]):
+            _close(_np(a), b, 1e-5, (parts, name))
 
 
 def test_backward_list_semantics():
@@ -88,6 +92,11 @@ def test_backward_full_size_bf16_32k_sampled():
     g = {n: t.cuda() for n, t in x.items()}
     _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, return_idx=True)
     dQ, dK, dV = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False)
+    # the key-range parts give the same gradients up to fp32 rounding
+    sQ, sK, sV = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO.cuda(), idx, scorer_grad=False,
+                                    parts="split")
+    for name, a, b in (("dQ", sQ, dQ), ("dK", sK, dK), ("dV", sV, dV)):
+        _close(_np(a), _np(b).astype(np.float64), 1e-5, ("split", name))
     torch.cuda.synchronize()
     dVs = _np(dV.double().sum(dim=2))
     dOs = dO.double().sum(dim=2).numpy()
@@ -110,3 +119,30 @@ def test_backward_full_size_bf16_32k_sampled():
                 dv += dVr[t]
             _close(_np(dK[0, h, j]), dk, 1e-5, "dK")
             _close(_np(dV[0, h, j]), dv, 1e-5, "dV")
+
+
+@pytest.mark.parametrize("N,k,H", [(8200, 1024, 1), (3000, 64, 2)])
+def test_backward_split_path_list_semantics(N, k, H):
+    """The passes in key-range parts: rows whose valid entries are an
+    ascending prefix are cut into segments, other rows are scanned whole by
+    every part; the key pass takes its parts from groups of row slices.
+    Mixed rows: sorted ones, reversed ones, -1 entries in the middle,
+    repeats; every element against the oracle."""
+    B, D = 1, 64
+    gen = torch.Generator().manual_seed(N + k)
+    Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen, dtype=torch.float32) for _ in range(4))
+    idx = torch.randint(0, N, (B, H, N, k), generator=gen, dtype=torch.int32)
+    idx, _ = torch.sort(idx, dim=-1)                       # ascending rows with repeats
+    idx[0, 0, 1::3] = idx[0, 0, 1::3].flip(-1)              # every third row descending
+    idx[0, H - 1, 5::7, k // 2] = -1                        # -1 inside a row
+    idx[0, H - 1, 2::5, k - 3:] = -1                        # valid prefix, then -1
+    idx[0, 0, 11] = -1                                      # a row with no valid entry
+    got = sa.sparse_attn_bwd(Q.cuda(), K.cuda(), V.cuda(), dO.cuda(), idx.cuda(),
+                             scorer_grad=False, parts="split")
+    want = O.sparse_attn_backward(Q, K, V, np.zeros((D, 16)), np.zeros((D, 16)), idx.numpy(),
+                                  dO, 1.0, D ** -0.5, scorer_grad=False)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, want[:3]):
+        _close(_np(a), b, 1e-5, name)
+    assert torch.all(got[0][0, 0, 11] == 0)
+    assert sa.sparse_attn_check_status() == 0
+
