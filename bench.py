@@ -47,18 +47,21 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 # rocprofv3 --pmc readings of the headline command (see profiles/), per launch
 # of the kernel, already scaled by the plain-copy factors (FETCH_SIZE reads half
 # a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
-# kernel's source file when the counters were taken.
+# kernel's sources (KERNEL_SOURCE) when the counters were taken.
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 111.095e9, "write_bytes": 93.480e9,
+    "filter": {"fetch_bytes": 108.770e9, "write_bytes": 93.705e9,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
     "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
-               "src": "7cf6f35137b4cb8d7515197d8dc7bd7aae128bfa87780a0025aaafd4974ea0b0"},
-    "rerank": {"fetch_bytes": 69.490e9, "write_bytes": 10.889e9,
+               "src": "0d382caa06a626f2fb8243c17355cf0222b30686a4d2d499f351ed02571b9e10"},
+    "rerank": {"fetch_bytes": 69.484e9, "write_bytes": 10.889e9,
                "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
 }
-KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "finalize.hip"}
+# the sources each kernel's code comes from (their sha256, concatenated in
+# this order, is recorded with the counters)
+KERNEL_SOURCE = {"filter": ["scorer.hip"], "gather": ["gather.hip", "rows.h"],
+                 "rerank": ["finalize.hip"]}
 
 # rocprofv3 --pmc readings of the filter's MFMA activity on the headline
 # command (profiles/filter_128k_mfma_counters.md), with the sha256 of
@@ -67,20 +70,22 @@ KERNEL_SOURCE = {"filter": "scorer.hip", "gather": "gather.hip", "rerank": "fina
 # XCD over the dispatch's duration.
 MFMA_COUNTERS: dict = {
     "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
-               "GRBM_GUI_ACTIVE_all_xcds": 1327977764, "dispatch_ms": 93.11,
-               "mfma_busy_frac": 0.4043, "shader_clock_ghz": 1.783,
+               "GRBM_GUI_ACTIVE_all_xcds": 1289462283, "dispatch_ms": 92.14,
+               "mfma_busy_frac": 0.4164, "shader_clock_ghz": 1.749,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
 }
 
 
 def source_sha(kernel: str):
     import hashlib
-    name = KERNEL_SOURCE.get(kernel)
-    if name is None:
+    names = KERNEL_SOURCE.get(kernel)
+    if names is None:
         return None
-    path = os.path.join(ROOT, "dynamic_top_sparse_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "dynamic_top_sparse_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
 
 
 def algorithmic(w) -> dict:

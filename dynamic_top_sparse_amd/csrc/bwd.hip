@@ -22,13 +22,14 @@
 //   result does not depend on scheduling).
 #include <algorithm>
 
-#include "sa_internal.h"
+#include "rows.h"
 
 namespace sa {
 
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
 constexpr int kOuterRows = 2048;    // rows per outer-sum chunk
 constexpr int kStageRows = 32;      // rows staged in LDS at a time
 
@@ -590,6 +591,416 @@ hipError_t outer_d(const void* X, const float* lo, long long rows, int dp, float
   return hipErrorInvalidValue;
 }
 
+// ------------------------------------------------------------ backward ---
+// Backward of the attention over index sets (page "mhpq.cn/news/1098205",
+// §2.3: the forward keeps the hard top-k; in the backward the selected
+// positions' gradients flow as usual and the others get none; the scorer is
+// reached through the selected positions' attention weights).  With
+// p_t = softmax(l)_t, dp_t = dO·V[j_t], delta = sum_t p_t dp_t and
+// dl_t = p_t (dp_t - delta):
+//   G_i = sum_t dl_t K[j_t],  dQ_i = scale · G_i              (row pass)
+//   dV_j = sum over (i, t) with j_t = j of p_t dO_i            (key pass)
+//   H_j = sum over the same of dl_t Q_i,  dK_j = scale · H_j   (key pass)
+// The scorer's gradients need no further gathers: a kept pair's score
+// receives its logit's gradient dl_t (straight-through), so
+//   dq_low_i = score_scale · sum_t dl_t k_low[j_t] = score_scale · G_i·Pk,
+//   dk_low_j = score_scale · H_j·Pq,
+// by linearity (bwd.hip computes them from G and H).  With scorer gradients
+// the passes store G and H unscaled (out_scale 1), else scale·G and scale·H.
+// The row pass writes (p_t, dl_t) in idx's layout; bwd.hip groups them by
+// key, and the key pass gathers the rows of the queries that kept each key,
+// as the forward gathers key rows.
+constexpr int kBwdChunk = 512;     // key-pass entries staged in LDS at a time
+
+__host__ __device__ constexpr int bwd_row_wave_floats(int k) { return 3 * gather_slog_floats(k); }
+__host__ __device__ constexpr int bwd_key_wave_floats() { return 3 * gather_slog_floats(kBwdChunk); }
+
+template <int EPL>
+__device__ __forceinline__ void store_f32_row(float* dst, const float (&v)[EPL], float f) {
+#pragma unroll
+  for (int e = 0; e < EPL; e += 4)
+    *reinterpret_cast<float4*>(dst + e) = make_float4(v[e] * f, v[e + 1] * f, v[e + 2] * f, v[e + 3] * f);
+}
+
+// Cross-group combination for the row pass: lanes holding the same row
+// elements in different row groups (xor partners LPR .. 32).
+template <int LPR>
+__device__ __forceinline__ float groups_sum(float v) {
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+    v = o == 32 ? sum_xor32(v) : o == 16 ? sum_xor16(v) : v + __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int LPR>
+__device__ __forceinline__ float groups_max(float v) {
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1)
+    v = o == 32 ? max_xor32(v) : o == 16 ? max_xor16(v) : fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// K pass of the backward row, one read of each kept K row: the logits
+// (base 2, into slog) and, per row group over the entries it loads, the sums
+//   S = sum e_t, U = sum e_t dp_t, A = sum e_t dp_t K_t, B = sum e_t K_t,
+// with e_t = 2^(l_t - m) for the group's running maximum m (the sums are
+// rescaled when m grows).  dp_t comes from sdp.  Then
+//   p_t = e_t / S, delta = U / S, sum_t dl_t K_t = (A - delta B) / S
+// once the groups are combined at the largest m.
+template <typename T, int D>
+__device__ __forceinline__ void bwd_logits_online(const T* __restrict__ qrow,
+                                                  const T* __restrict__ K,
+                                                  const int32_t* __restrict__ row, int n, int N,
+                                                  float scale2, float* slog,
+                                                  const float* sdp, int& bad, float& m,
+                                                  float& S, float& U,
+                                                  float (&A)[Vec<T>::kElems],
+                                                  float (&B)[Vec<T>::kElems]) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, RPI = kWave / LPR;
+  const int l = lane_id();
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float qf[EPL];
+  Vec<T>::unpack(*reinterpret_cast<const uint4*>(qrow + e0), qf);
+  m = -INFINITY;
+  S = U = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) A[e] = B[e] = 0.0f;
+  for (int tb = 0; tb < n; tb += RPI * kUnroll) {
+    const int nu = min(kUnroll, (n - tb + RPI - 1) / RPI);   // loads holding rows (uniform)
+    uint4 kv[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const int jr = row[t];                       // t < n + RPI: inside the slack
+      const int j = t < n ? jr : -1;
+      ok[u] = j >= 0 && j < N;
+      bad |= (t < n && j >= N) ? 1 : 0;
+      kv[u] = *reinterpret_cast<const uint4*>(K + static_cast<size_t>(ok[u] ? j : 0) * D + e0);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      float kf[EPL];
+      Vec<T>::unpack(kv[u], kf);
+      float dot = 0.0f;
+      if constexpr (sizeof(T) == 2) {
+        bf16x2 kp[4], qp[4];
+        const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + e0);
+        __builtin_memcpy(kp, &kv[u], 16);
+        __builtin_memcpy(qp, &q4, 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[i], dot, false);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dot = __builtin_fmaf(qf[e], kf[e], dot);
+      }
+      dot = group_sum<LPR>(dot);
+      const float lt = ok[u] ? dot * scale2 : -INFINITY;
+      if ((l % LPR) == 0 && t < n) slog[t] = lt;
+      if (lt > m) {                 // the whole group agrees: lt and m are group values
+        const float c = __builtin_amdgcn_exp2f(m - lt);   // m = -inf gives 0
+        S *= c;
+        U *= c;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          A[e] *= c;
+          B[e] *= c;
+        }
+        m = lt;
+      }
+      const float ew = ok[u] ? __builtin_amdgcn_exp2f(lt - m) : 0.0f;
+      const float ed = ok[u] ? ew * sdp[t] : 0.0f;
+      S += ew;
+      U += ed;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        A[e] = __builtin_fmaf(ed, kf[e], A[e]);
+        B[e] = __builtin_fmaf(ew, kf[e], B[e]);
+      }
+    }
+  }
+  // combine the groups at the largest maximum
+  const float M = groups_max<LPR>(m);
+  const float c = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+  S = groups_sum<LPR>(S * c);
+  U = groups_sum<LPR>(U * c);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    A[e] = groups_sum<LPR>(A[e] * c);
+    B[e] = groups_sum<LPR>(B[e] * c);
+  }
+  m = M;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const int32_t* __restrict__ idx, int k, int N, float scale,
+    float out_scale, float* __restrict__ dQ, float2* __restrict__ lpd,
+    float4* __restrict__ stats, int* __restrict__ err) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int SL = gather_slog_floats(k);
+  float* sl = bwd_lds + w * bwd_row_wave_floats(k);      // logits
+  float* sd = sl + SL;                                    // dp_t
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const int h = blockIdx.y;
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= N) return;
+  const size_t hN = static_cast<size_t>(h) * N;
+  stage_entries(idx + (hN + q) * k, 0, k, sidx);
+  int bad = 0;
+  // dp_t = dO·V_t first (V rows), then one pass over the K rows
+  logits<T, D>(dO + (hN + q) * D, V + hN * D, sidx, 0, k, N, 1.0f, sd, bad);
+  wave_sync();
+  float m, S, U, A[EPL], B[EPL];
+  bwd_logits_online<T, D>(Q + (hN + q) * D, K + hN * D, sidx, k, N, scale * kLog2e, sl, sd, bad,
+                          m, S, U, A, B);
+  if (bad) atomicOr(err, 1);
+  wave_sync();
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  // (logit, dp_t) in idx's layout and the row's (max, 1/S, delta): the fill
+  // forms p_t and dl_t from them (entries that name no key are never read)
+  float2* er = lpd + (hN + q) * static_cast<size_t>(k);
+  for (int t = l; t < k; t += kWave) er[t] = make_float2(sl[t], sd[t]);
+  float acc[EPL];
+  if (m == -INFINITY) {    // no valid entry: no gradient from this row
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = 0.0f;
+    if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, 1.0f);
+    if (l == 0) stats[hN + q] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
+    return;
+  }
+  const float inv = 1.0f / S;
+  const float delta = U * inv;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = (A[e] - delta * B[e]) * inv;
+  if (g == 0) store_f32_row<EPL>(dQ + (hN + q) * D + e0, acc, out_scale);
+  if (l == 0) stats[hN + q] = make_float4(m, inv, delta, 0.0f);
+}
+
+// Row pass, part r of a key-range split (see bwd.hip): the entries of the
+// row whose keys lie in [bounds[r], bounds[r+1]) -- one segment of a row
+// whose valid entries are an ascending prefix, else the whole row with the
+// other keys masked -- give (logit, dp_t) in idx's layout and the part's
+// record (m, S, U, -, A[D], B[D]).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_rows_split_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const T* __restrict__ dO, const int32_t* __restrict__ idx, const int* __restrict__ seg,
+    const int* __restrict__ bounds, int k, int N, float scale, float2* __restrict__ lpd,
+    float* __restrict__ part) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, R = kGatherRanges, PS = 2 * D + 4;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  // consecutive workgroups land on consecutive XCDs: part r runs on XCD r
+  const int r = static_cast<int>(blockIdx.x) % R;
+  const int q = static_cast<int>(blockIdx.x) / R * kWaves + w;
+  const int h = blockIdx.y;
+  if (q >= N) return;
+  const int SL = gather_slog_floats(k);
+  float* sl = bwd_lds + w * bwd_row_wave_floats(k);
+  float* sd = sl + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const size_t hN = static_cast<size_t>(h) * N, row = hN + q;
+  const int* sg = seg + row * (R + 1);
+  const bool sorted = __builtin_amdgcn_readfirstlane(sg[0]) >= 0;
+  const int t0 = sorted ? __builtin_amdgcn_readfirstlane(sg[r]) : 0;
+  const int t1 = sorted ? __builtin_amdgcn_readfirstlane(sg[r + 1]) : k;
+  float* rec = part + (row * R + r) * PS;
+  if (t0 >= t1) {
+    if (l == 0) rec[0] = -INFINITY;   // empty part: the merge skips it
+    return;
+  }
+  const int lo = bounds[h * (R + 1) + r], hi = bounds[h * (R + 1) + r + 1];
+  const int32_t* ir = idx + row * k;
+  const int n = t1 - t0;
+  for (int t = l; t < n; t += kWave) {
+    const int j = ir[t0 + t];
+    sidx[t] = j >= lo && j < hi ? j : -1;
+  }
+  wave_sync();
+  int bad = 0;
+  logits<T, D>(dO + row * D, V + hN * D, sidx, 0, n, N, 1.0f, sd, bad);
+  wave_sync();
+  float m, S, U, A[EPL], B[EPL];
+  bwd_logits_online<T, D>(Q + row * D, K + hN * D, sidx, n, N, scale * kLog2e, sl, sd, bad, m, S,
+                          U, A, B);
+  wave_sync();
+  float2* er = lpd + row * k + t0;
+  for (int t = l; t < n; t += kWave)
+    if (sidx[t] >= 0) er[t] = make_float2(sl[t], sd[t]);
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  if (g == 0) {
+#pragma unroll
+    for (int e = 0; e < EPL; e += 4) {
+      *reinterpret_cast<float4*>(rec + 4 + e0 + e) = make_float4(A[e], A[e + 1], A[e + 2], A[e + 3]);
+      *reinterpret_cast<float4*>(rec + 4 + D + e0 + e) =
+          make_float4(B[e], B[e + 1], B[e + 2], B[e + 3]);
+    }
+  }
+  if (l == 0) *reinterpret_cast<float4*>(rec) = make_float4(m, S, U, 0.0f);
+}
+
+// Key pass, part r: the key's records from rows of slices [r S/8, (r+1) S/8)
+// (consecutive in its segment) give the part's (dV[D], H[D]).
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
+    const T* __restrict__ Q, const T* __restrict__ dO, const int* __restrict__ seg_off,
+    const int* __restrict__ seg_cnt, const int* __restrict__ slice_pre, int S, long long total,
+    const BwdEntry* __restrict__ rec, int N, int k, float* __restrict__ part) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL, R = kGatherRanges;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  const int r = static_cast<int>(blockIdx.x) % R;
+  const int j = static_cast<int>(blockIdx.x) / R * kWaves + w;
+  const int h = blockIdx.y;
+  if (j >= N) return;
+  constexpr int SL = gather_slog_floats(kBwdChunk);
+  float* sp = bwd_lds + w * bwd_key_wave_floats();
+  float* sd = sp + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const size_t hN = static_cast<size_t>(h) * N, key = hN + j;
+  const int s0 = r * (S / R), s1 = (r + 1) * (S / R);
+  const int a0 = slice_pre[static_cast<size_t>(s0) * total + key];
+  const int a1 = s1 < S ? slice_pre[static_cast<size_t>(s1) * total + key] : seg_cnt[key];
+  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[key] + a0);
+  const int n = a1 - a0;
+  const unsigned uk = static_cast<unsigned>(k);
+  const T* Qh = Q + hN * D;
+  const T* dOh = dO + hN * D;
+  float av[EPL], ak[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
+    const int m = min(kBwdChunk, n - c0);
+    for (int t = l; t < m; t += kWave) {
+      const BwdEntry re = rec[o0 + c0 + t];
+      sidx[t] = static_cast<int>(static_cast<unsigned>(re.e) / uk);
+      sp[t] = re.p;
+      sd[t] = re.dl;
+    }
+    wave_sync();
+    float tmp[EPL];
+    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
+    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    wave_sync();
+  }
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  float* pr = part + (key * R + r) * 2 * D;
+  if (g == 0) {
+    store_f32_row<EPL>(pr + e0, av, 1.0f);
+    store_f32_row<EPL>(pr + D + e0, ak, 1.0f);
+  }
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
+    const T* __restrict__ Q, const T* __restrict__ dO, const int* __restrict__ seg_off,
+    const int* __restrict__ seg_cnt, const BwdEntry* __restrict__ rec, int N, int k,
+    float out_scale, float* __restrict__ dK, float* __restrict__ dV) {
+  constexpr int EPL = Vec<T>::kElems, LPR = D / EPL;
+  extern __shared__ float bwd_lds[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int l = lane_id();
+  constexpr int SL = gather_slog_floats(kBwdChunk);
+  float* sp = bwd_lds + w * bwd_key_wave_floats();
+  float* sd = sp + SL;
+  int* sidx = reinterpret_cast<int*>(sd + SL);
+  const int h = blockIdx.y;
+  const int j = blockIdx.x * kWaves + w;
+  if (j >= N) return;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const T* Qh = Q + hN * D;
+  const T* dOh = dO + hN * D;
+  const size_t o0 = hN * static_cast<size_t>(k) + static_cast<unsigned>(seg_off[hN + j]);
+  const int n = seg_cnt[hN + j];
+  const unsigned uk = static_cast<unsigned>(k);
+  float av[EPL], ak[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) av[e] = ak[e] = 0.0f;
+  for (int c0 = 0; c0 < n; c0 += kBwdChunk) {
+    const int m = min(kBwdChunk, n - c0);
+    for (int t = l; t < m; t += kWave) {
+      const BwdEntry r = rec[o0 + c0 + t];
+      sidx[t] = static_cast<int>(static_cast<unsigned>(r.e) / uk);   // e = i*k + t
+      sp[t] = r.p;
+      sd[t] = r.dl;
+    }
+    wave_sync();
+    float tmp[EPL];
+    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
+    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    wave_sync();    // the chunk's LDS is read before the next one is staged
+  }
+  const int g = l / LPR, e0 = (l % LPR) * EPL;
+  if (g == 0) {
+    store_f32_row<EPL>(dV + (hN + j) * D + e0, av, 1.0f);
+    store_f32_row<EPL>(dK + (hN + j) * D + e0, ak, out_scale);
+  }
+}
+
+template <typename T, int D>
+hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
+  static std::atomic<int> lds_rows[kMaxDevices], lds_keys[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_kernel<T, D>),
+                                    kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rows);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_kernel<T, D>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_keys);
+  if (e != hipSuccess) return e;
+  static std::atomic<int> lds_rs[kMaxDevices], lds_ks[kMaxDevices];
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_split_kernel<T, D>),
+                         kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rs);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_ks);
+  if (e != hipSuccess) return e;
+  int* err = nullptr;
+  e = index_error_flag(&err);
+  if (e != hipSuccess) return e;
+  const int nb = (a.N + kWaves - 1) / kWaves;
+  const dim3 grid(nb, a.nh), grid_split(nb * kGatherRanges, a.nh);
+  const float out_scale = a.scorer ? 1.0f : a.scale;
+  const size_t lds_r = static_cast<size_t>(kWaves) * bwd_row_wave_floats(a.k) * 4;
+  const size_t lds_k = static_cast<size_t>(kWaves) * bwd_key_wave_floats() * 4;
+  if (a.pass == 0 && !a.split_rows) {
+    hipLaunchKernelGGL((bwd_rows_kernel<T, D>), grid, dim3(kThreads), lds_r, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
+                       static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.idx, a.k, a.N,
+                       a.scale, out_scale, a.dQ, a.epd, a.stats, err);
+  } else if (a.pass == 0) {
+    hipLaunchKernelGGL((bwd_rows_split_kernel<T, D>), grid_split, dim3(kThreads), lds_r, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.K),
+                       static_cast<const T*>(a.V), static_cast<const T*>(a.dO), a.idx,
+                       a.row_seg, a.bounds, a.k, a.N, a.scale, a.epd, a.part);
+  } else if (!a.split_keys) {
+    hipLaunchKernelGGL((bwd_keys_kernel<T, D>), grid, dim3(kThreads), lds_k, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
+                       a.seg_cnt, a.rec, a.N, a.k, out_scale, a.dK, a.dV);
+  } else {
+    hipLaunchKernelGGL((bwd_keys_split_kernel<T, D>), grid_split, dim3(kThreads), lds_k, s,
+                       static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
+                       a.seg_cnt, a.slice_pre, a.slices, static_cast<long long>(a.nh) * a.N,
+                       a.rec, a.N, a.k, a.part);
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int bwd_slices(int N, int k) {
@@ -722,6 +1133,17 @@ hipError_t launch_outer_sum(const void* X, int dtype, const float* lo, long long
   hipLaunchKernelGGL(outer_reduce_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      s, partial, nchunks, n, dP);
   return hipGetLastError();
+}
+
+hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s) {
+  if (a.dtype == 0) {
+    if (a.D == 64) return bwd_passes_t<float, 64>(a, s);
+    if (a.D == 128) return bwd_passes_t<float, 128>(a, s);
+  } else {
+    if (a.D == 64) return bwd_passes_t<bf16_t, 64>(a, s);
+    if (a.D == 128) return bwd_passes_t<bf16_t, 128>(a, s);
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace sa

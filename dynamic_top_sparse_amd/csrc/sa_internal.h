@@ -235,6 +235,9 @@ struct BwdArgs {
   float* part;                  // the parts' records
 };
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
+// Device address of the sticky out-of-range index flag (gather.hip) on the
+// current device.
+hipError_t index_error_flag(int** out);
 // Key segments of the entry list, built from idx alone: per-slice counts of
 // each key (LDS histograms over windows of keys), their prefix over slices,
 // each key's segment start, then the entries written into their segments.
