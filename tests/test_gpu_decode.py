@@ -81,3 +81,36 @@ def test_decode_selection_counts():
             for j in _np(idx)[0, h]:
                 want[0, h, j] += 1
     np.testing.assert_array_equal(_np(cache.counts).astype(np.int64), want)
+
+
+@pytest.mark.parametrize("same_keys", [False, True])
+def test_decode_select_long_cache(same_keys):
+    """A 20000-key cache: the select keeps the keys at or above the k-th
+    key's leading 11-bit bin in LDS (a small share of random scores); when
+    every key scores the same, that bin holds all 20000 keys and the select
+    runs over the scores in memory instead.  Both against the oracle's top-k
+    of the dumped fp32 scores (all equal: keys 0 .. k-1), with the counts."""
+    N, k = 20000, 100
+    w = W.Workload("dec", 1, 2, N, 64, "f32", d_proj=16, k=k, causal=True)
+    x = W.make_inputs(w, 21)
+    if same_keys:
+        x["K"][:] = x["K"][:, :, :1].clone()
+    g = {n: t.cuda() for n, t in x.items()}
+    cache = sa.DecodeCache(1, 2, N, 64, g["Pq"], g["Pk"], k, dtype=torch.float32)
+    cache.append(g["K"], g["V"])
+    q = g["Q"][:, :, N - 1:N].contiguous()
+    idx = torch.empty(1, 2, k, dtype=torch.int32, device="cuda")
+    out, idx = cache.step(q, idx=idx, count=True)
+    idx = _np(idx)
+    S = _np(sa.sparse_attn_scores_dump(g["Q"], g["K"], g["Pq"], g["Pk"], N - 1, 1, True))
+    for h in range(2):
+        want = O.topk_rows(S[0, h].astype(np.float64), [N - 1], k, True)[0]
+        np.testing.assert_array_equal(idx[0, h], want)
+        if same_keys:
+            np.testing.assert_array_equal(idx[0, h], np.arange(k))
+        counts = np.zeros(N, np.int64)
+        counts[idx[0, h]] += 1
+        np.testing.assert_array_equal(_np(cache.counts[0, h]).astype(np.int64), counts)
+        o_ref = O.attend_row(O.f64(x["Q"][0, h, N - 1]), O.f64(x["K"][0, h]), O.f64(x["V"][0, h]),
+                             idx[0, h].astype(np.int64), sa.default_softmax_scale(64))
+        assert np.abs(_np(out[0, h, 0]) - o_ref).max() <= 1e-5
