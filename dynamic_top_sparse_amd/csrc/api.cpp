@@ -783,8 +783,12 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
     SA_TIMED_STATUS("bwd_rows_merge", launch_bwd_rows_merge(a.part, a.nh, d.N, d.D,
                                                            scorer ? 1.0f : softmax_scale, dQ,
                                                            a.stats, s));
-  SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.stats, a.nh, d.N, k, p.slices, cnts,
-                                              offs, rec, s));
+  if (p.split_rows)
+    SA_TIMED_STATUS("bwd_fill", launch_bwd_fill_parts(idx, a.epd, a.stats, row_seg, bounds, a.nh,
+                                                      d.N, k, p.slices, cnts, offs, rec, s));
+  else
+    SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.stats, a.nh, d.N, k, p.slices, cnts,
+                                                offs, rec, s));
   a.pass = 1;
   SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
   if (p.split_keys)

@@ -146,6 +146,57 @@ __global__ __launch_bounds__(kHistThreads) void bwd_fill_kernel(const int32_t* _
               });
 }
 
+// The fill when the row pass ran in key-range parts: one workgroup per
+// (head, slice, part) reads only the part's segment of each row of the slice
+// (a row whose valid entries are not an ascending prefix: the whole row), so
+// idx and (logit, dp) are read once in all; a part of more than kHistWindow
+// keys is handled in windows of that many, one after another.
+__global__ __launch_bounds__(kHistThreads) void bwd_fill_parts_kernel(
+    const int32_t* __restrict__ idx, const float2* __restrict__ lpd,
+    const float4* __restrict__ stats, const int* __restrict__ row_seg,
+    const int* __restrict__ bounds, int N, int k, int S, int rows_per_slice, int nh,
+    const int* __restrict__ cnt_s, const int* __restrict__ off, BwdEntry* __restrict__ rec) {
+  constexpr int R = kGatherRanges;
+  extern __shared__ int cur[];
+  const int s = static_cast<int>(blockIdx.x) % S, r = static_cast<int>(blockIdx.x) / S;
+  const int h = blockIdx.y;
+  const size_t hN = static_cast<size_t>(h) * N;
+  const long long hk = static_cast<long long>(h) * N * k;
+  const int i0 = min(N, s * rows_per_slice), i1 = min(N, i0 + rows_per_slice);
+  const int lo = bounds[h * (R + 1) + r], hi = bounds[h * (R + 1) + r + 1];
+  const int* before = cnt_s + (static_cast<size_t>(s) * nh + h) * N;
+  BwdEntry* rh = rec + hk;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  constexpr int kFillWaves = kHistThreads / kWave;
+  for (int w0 = lo; w0 < hi; w0 += kHistWindow) {
+    const int W = min(kHistWindow, hi - w0);
+    __syncthreads();      // the previous window's cursors are no longer used
+    for (int t = threadIdx.x; t < W; t += kHistThreads) cur[t] = off[hN + w0 + t] + before[w0 + t];
+    __syncthreads();
+    const unsigned uw0 = static_cast<unsigned>(w0), uW = static_cast<unsigned>(W);
+    for (int i = i0 + w; i < i1; i += kFillWaves) {
+      const size_t row = hN + i;
+      const int* sg = row_seg + row * (R + 1);
+      const bool sorted = sg[0] >= 0;
+      const int t0 = sorted ? sg[r] : 0, t1 = sorted ? sg[r + 1] : k;
+      const float4 st = stats[row];
+      for (int t = t0 + l; t < t1; t += kWave) {
+        const long long g = static_cast<long long>(row) * k + t;
+        const int j = idx[g];
+        const unsigned u = static_cast<unsigned>(j) - uw0;
+        if (u < uW) {
+          const float2 ld = lpd[g];
+          BwdEntry e;
+          e.e = static_cast<int>(g - hk);
+          e.p = ld.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ld.x - st.x) * st.y;
+          e.dl = e.p != 0.0f ? e.p * (ld.y - st.z) : 0.0f;
+          rh[atomicAdd(&cur[u], 1)] = e;
+        }
+      }
+    }
+  }
+}
+
 // One workgroup per head: exclusive scan of the counts, i.e. each key's
 // first entry within the head's region of the entry list.
 __global__ __launch_bounds__(kThreads) void bwd_scan_kernel(const int* __restrict__ cnt, int N,
@@ -1058,6 +1109,21 @@ hipError_t launch_bwd_fill(const int32_t* idx, const float2* lpd, const float4* 
   const HistGrid g = hist_grid(nh, N, S);
   hipLaunchKernelGGL(bwd_fill_kernel, g.grid, dim3(kHistThreads), g.lds, s, idx, lpd, stats, N, k,
                      g.S, g.rows_per_slice, nh, cnt_s, off, rec);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_fill_parts(const int32_t* idx, const float2* lpd, const float4* stats,
+                                 const int* row_seg, const int* bounds, int nh, int N, int k,
+                                 int S, const int* cnt_s, const int* off, BwdEntry* rec,
+                                 hipStream_t s) {
+  static std::atomic<int> lds_set[kMaxDevices];
+  hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_fill_parts_kernel),
+                                    kHistWindow * 4, lds_set);
+  if (e != hipSuccess) return e;
+  const int rps = (N + S - 1) / S;
+  hipLaunchKernelGGL(bwd_fill_parts_kernel, dim3(S * kGatherRanges, nh), dim3(kHistThreads),
+                     static_cast<size_t>(kHistWindow) * 4, s, idx, lpd, stats, row_seg, bounds,
+                     N, k, S, rps, nh, cnt_s, off, rec);
   return hipGetLastError();
 }
 

@@ -251,6 +251,10 @@ hipError_t launch_bwd_fill(const int32_t* idx, const float2* lpd, const float4* 
                            hipStream_t s);
 hipError_t launch_bwd_bounds(const int* off, const int* cnt, int nh, int N, int* bounds,
                              hipStream_t s);
+hipError_t launch_bwd_fill_parts(const int32_t* idx, const float2* lpd, const float4* stats,
+                                 const int* row_seg, const int* bounds, int nh, int N, int k,
+                                 int S, const int* cnt_s, const int* off, BwdEntry* rec,
+                                 hipStream_t s);
 hipError_t launch_bwd_row_ranges(const int32_t* idx, const int* bounds, int nh, int N, int k,
                                  int* seg, hipStream_t s);
 hipError_t launch_bwd_rows_merge(const float* part, int nh, int N, int D, float out_scale,
