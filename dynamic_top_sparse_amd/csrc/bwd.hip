@@ -785,6 +785,110 @@ __device__ __forceinline__ void bwd_logits_online(const T* __restrict__ qrow,
   m = M;
 }
 
+// bwd_logits_online for bf16 rows whose entries all hold keys in [0, N)
+// (a part's segment of an ascending row): the forward split gather's trusted
+// row loads (clamped keys, 32-bit offsets, straight-line blocks of loads,
+// the block's dot products reduced together).
+template <int D>
+__device__ __forceinline__ void bwd_logits_online_trusted(const bf16_t* __restrict__ qrow,
+                                                          const bf16_t* __restrict__ Kh,
+                                                          const int* __restrict__ row, int n,
+                                                          int N, float scale2, float* slog,
+                                                          const float* sdp, float& m, float& S,
+                                                          float& U, float (&A)[8], float (&B)[8]) {
+  constexpr int EPL = 8, LPR = D / EPL, RPI = kWave / LPR, BLK = RPI * kUnroll;
+  const int l = lane_id();
+  const int g = l / LPR;
+  const unsigned lane_off = static_cast<unsigned>((l % LPR) * EPL * 2);
+  const char* kb = reinterpret_cast<const char*>(Kh);
+  const uint4 q4 = *reinterpret_cast<const uint4*>(qrow + (l % LPR) * EPL);
+  bf16x2 qp[4];
+  __builtin_memcpy(qp, &q4, 16);
+  auto dot_of = [&](const uint4& kv) {
+    bf16x2 kp[4];
+    __builtin_memcpy(kp, &kv, 16);
+    float dot = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dot = __builtin_amdgcn_fdot2_f32_bf16(kp[i], qp[i], dot, false);
+    return dot;
+  };
+  m = -INFINITY;
+  S = U = 0.0f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) A[e] = B[e] = 0.0f;
+  auto update = [&](float lt, float dp, const uint4& kv) {   // lt finite
+    if (lt > m) {
+      const float c = __builtin_amdgcn_exp2f(m - lt);
+      S *= c;
+      U *= c;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        A[e] *= c;
+        B[e] *= c;
+      }
+      m = lt;
+    }
+    const float ew = __builtin_amdgcn_exp2f(lt - m), ed = ew * dp;
+    S += ew;
+    U += ed;
+    float kf[EPL];
+    Vec<bf16_t>::unpack(kv, kf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      A[e] = __builtin_fmaf(ed, kf[e], A[e]);
+      B[e] = __builtin_fmaf(ew, kf[e], B[e]);
+    }
+  };
+  int tb = 0;
+  for (; tb + BLK <= n; tb += BLK) {
+    uint4 kv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      kv[u] = *reinterpret_cast<const uint4*>(kb + row_offset<D>(row, tb + u * RPI + g, N, lane_off));
+    float dot[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) dot[u] = dot_of(kv[u]);
+    group_sum_n<LPR>(dot);
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int t = tb + u * RPI + g;
+      const float lt = dot[u] * scale2;
+      if ((l % LPR) == 0) slog[t] = lt;
+      update(lt, sdp[t], kv[u]);
+    }
+  }
+  if (tb < n) {
+    const int nu = (n - tb + RPI - 1) / RPI;   // loads holding rows (uniform)
+    uint4 kv[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      kv[u] = *reinterpret_cast<const uint4*>(kb + row_offset<D>(row, tb + u * RPI + g, N, lane_off));
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const float dot = group_sum<LPR>(dot_of(kv[u]));
+      if (t < n) {                  // group-uniform: slack entries past the segment are dropped
+        const float lt = dot * scale2;
+        if ((l % LPR) == 0) slog[t] = lt;
+        update(lt, sdp[t], kv[u]);
+      }
+    }
+  }
+  const float M = groups_max<LPR>(m);
+  const float c = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
+  S = groups_sum<LPR>(S * c);
+  U = groups_sum<LPR>(U * c);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    A[e] = groups_sum<LPR>(A[e] * c);
+    B[e] = groups_sum<LPR>(B[e] * c);
+  }
+  m = M;
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -876,12 +980,22 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_split_kernel(
     sidx[t] = j >= lo && j < hi ? j : -1;
   }
   wave_sync();
-  int bad = 0;
-  logits<T, D>(dO + row * D, V + hN * D, sidx, 0, n, N, 1.0f, sd, bad);
-  wave_sync();
   float m, S, U, A[EPL], B[EPL];
-  bwd_logits_online<T, D>(Q + row * D, K + hN * D, sidx, n, N, scale * kLog2e, sl, sd, bad, m, S,
-                          U, A, B);
+  if constexpr (sizeof(T) == 2) {
+    if (sorted) {   // the segment's keys all lie in [lo, hi): trusted rows
+      logits_bf16_split<D>(dO + row * D, V + hN * D, sidx, n, N, 1.0f, sd);
+      wave_sync();
+      bwd_logits_online_trusted<D>(Q + row * D, K + hN * D, sidx, n, N, scale * kLog2e, sl, sd, m,
+                                   S, U, A, B);
+    }
+  }
+  if (sizeof(T) != 2 || !sorted) {
+    int bad = 0;
+    logits<T, D>(dO + row * D, V + hN * D, sidx, 0, n, N, 1.0f, sd, bad);
+    wave_sync();
+    bwd_logits_online<T, D>(Q + row * D, K + hN * D, sidx, n, N, scale * kLog2e, sl, sd, bad, m,
+                            S, U, A, B);
+  }
   wave_sync();
   float2* er = lpd + row * k + t0;
   for (int t = l; t < n; t += kWave)
@@ -939,10 +1053,17 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
     }
     wave_sync();
     float tmp[EPL];
-    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+    // the rows are those of queries that kept the key: all in [0, N)
+    if constexpr (sizeof(T) == 2)
+      weighted_rows_bf16_split<D>(dOh, sidx, m, N, sp, tmp);
+    else
+      weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
-    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+    if constexpr (sizeof(T) == 2)
+      weighted_rows_bf16_split<D>(Qh, sidx, m, N, sd, tmp);
+    else
+      weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
     wave_sync();
@@ -990,10 +1111,17 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
     }
     wave_sync();
     float tmp[EPL];
-    weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
+    // the rows are those of queries that kept the key: all in [0, N)
+    if constexpr (sizeof(T) == 2)
+      weighted_rows_bf16_split<D>(dOh, sidx, m, N, sp, tmp);
+    else
+      weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
-    weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
+    if constexpr (sizeof(T) == 2)
+      weighted_rows_bf16_split<D>(Qh, sidx, m, N, sd, tmp);
+    else
+      weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
 #pragma unroll
     for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
     wave_sync();    // the chunk's LDS is read before the next one is staged
