@@ -889,6 +889,67 @@ __device__ __forceinline__ void bwd_logits_online_trusted(const bf16_t* __restri
   m = M;
 }
 
+// The key pass's two weighted sums over the same trusted bf16 rows list:
+// acc1 = sum_t w1_t X1[j_t] and acc2 = sum_t w2_t X2[j_t], the two rows of an
+// entry loaded together (kPair entries of each in flight per lane), partial
+// sums reduced across the row groups at the end as in weighted_rows.
+constexpr int kPair = 4;
+
+template <int D>
+__device__ __forceinline__ void weighted_rows2_bf16(const bf16_t* __restrict__ X1,
+                                                    const float* __restrict__ w1,
+                                                    const bf16_t* __restrict__ X2,
+                                                    const float* __restrict__ w2,
+                                                    const int* __restrict__ row, int n, int N,
+                                                    float (&acc1)[8], float (&acc2)[8]) {
+  constexpr int EPL = 8, LPR = D / EPL, RPI = kWave / LPR, BLK = RPI * kPair;
+  const int l = lane_id();
+  const int g = l / LPR;
+  const unsigned lane_off = static_cast<unsigned>((l % LPR) * EPL * 2);
+  const char* b1 = reinterpret_cast<const char*>(X1);
+  const char* b2 = reinterpret_cast<const char*>(X2);
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc1[e] = acc2[e] = 0.0f;
+  auto add = [&](const uint4& v, float w, float (&acc)[8]) {
+    float vf[EPL];
+    Vec<bf16_t>::unpack(v, vf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] = __builtin_fmaf(w, vf[e], acc[e]);
+  };
+  for (int tb = 0; tb < n; tb += BLK) {
+    const int nu = min(kPair, (n - tb + RPI - 1) / RPI);   // loads holding rows (uniform)
+    uint4 v1[kPair], v2[kPair];
+    float x1[kPair], x2[kPair];
+#pragma unroll
+    for (int u = 0; u < kPair; ++u) {
+      if (u >= nu) break;
+      const int t = tb + u * RPI + g;
+      const unsigned o = row_offset<D>(row, t, N, lane_off);
+      const bool in = t < n;      // slack entries past the list weigh nothing
+      x1[u] = in ? w1[t] : 0.0f;
+      x2[u] = in ? w2[t] : 0.0f;
+      v1[u] = *reinterpret_cast<const uint4*>(b1 + o);
+      v2[u] = *reinterpret_cast<const uint4*>(b2 + o);
+    }
+#pragma unroll
+    for (int u = 0; u < kPair; ++u) {
+      if (u >= nu) break;
+      add(v1[u], x1[u], acc1);
+      add(v2[u], x2[u], acc2);
+    }
+  }
+#pragma unroll
+  for (int o = LPR; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      acc1[e] = o == 32 ? sum_xor32(acc1[e]) : o == 16 ? sum_xor16(acc1[e])
+                                                       : acc1[e] + __shfl_xor(acc1[e], o, kWave);
+      acc2[e] = o == 32 ? sum_xor32(acc2[e]) : o == 16 ? sum_xor16(acc2[e])
+                                                       : acc2[e] + __shfl_xor(acc2[e], o, kWave);
+    }
+  }
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
@@ -1052,20 +1113,24 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
       sd[t] = re.dl;
     }
     wave_sync();
-    float tmp[EPL];
     // the rows are those of queries that kept the key: all in [0, N)
-    if constexpr (sizeof(T) == 2)
-      weighted_rows_bf16_split<D>(dOh, sidx, m, N, sp, tmp);
-    else
+    if constexpr (sizeof(T) == 2) {
+      float t1[EPL], t2[EPL];
+      weighted_rows2_bf16<D>(dOh, sp, Qh, sd, sidx, m, N, t1, t2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        av[e] += t1[e];
+        ak[e] += t2[e];
+      }
+    } else {
+      float tmp[EPL];
       weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
-    if constexpr (sizeof(T) == 2)
-      weighted_rows_bf16_split<D>(Qh, sidx, m, N, sd, tmp);
-    else
+      for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
       weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+      for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    }
     wave_sync();
   }
   const int g = l / LPR, e0 = (l % LPR) * EPL;
@@ -1110,20 +1175,24 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_kernel(
       sd[t] = r.dl;
     }
     wave_sync();
-    float tmp[EPL];
     // the rows are those of queries that kept the key: all in [0, N)
-    if constexpr (sizeof(T) == 2)
-      weighted_rows_bf16_split<D>(dOh, sidx, m, N, sp, tmp);
-    else
+    if constexpr (sizeof(T) == 2) {
+      float t1[EPL], t2[EPL];
+      weighted_rows2_bf16<D>(dOh, sp, Qh, sd, sidx, m, N, t1, t2);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        av[e] += t1[e];
+        ak[e] += t2[e];
+      }
+    } else {
+      float tmp[EPL];
       weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
-    if constexpr (sizeof(T) == 2)
-      weighted_rows_bf16_split<D>(Qh, sidx, m, N, sd, tmp);
-    else
+      for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
       weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+      for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
+    }
     wave_sync();    // the chunk's LDS is read before the next one is staged
   }
   const int g = l / LPR, e0 = (l % LPR) * EPL;
