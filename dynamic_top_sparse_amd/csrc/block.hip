@@ -45,7 +45,7 @@ __device__ __forceinline__ unsigned long long block_rank(float s, int J) {
 
 // One query per thread: its top-kb blocks by (score descending, block
 // ascending), kept in registers as a list sorted best first.
-template <int DP>
+template <int DP, int KB>
 __global__ __launch_bounds__(kThreads) void block_select_kernel(
     const float* __restrict__ q32, const float* __restrict__ kbar, int N, int block, int NB,
     int kb, int causal, float scale, int32_t* __restrict__ sel) {
@@ -66,9 +66,10 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(
   // candidate blocks: all, or (causal) those before the query's own block
   const int ncand = causal ? own : NB;
   const int want = causal ? min(kb - 1, ncand) : min(kb, ncand);
-  unsigned long long best[kBlockKbMax];
+  // (KB >= kb: the list's register length, the smallest of 4, 8, 16, 32)
+  unsigned long long best[KB];
 #pragma unroll
-  for (int t = 0; t < kBlockKbMax; ++t) best[t] = 0ull;   // below every real rank
+  for (int t = 0; t < KB; ++t) best[t] = 0ull;   // below every real rank
   unsigned long long last = 0ull;                         // best[want - 1]
   // blocks the workgroup must score: the largest candidate count among its queries
   const int i_last = min(N, static_cast<int>(blockIdx.x) * kThreads + kThreads) - 1;
@@ -88,7 +89,7 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(
       if (live && J < ncand && want > 0 && r > last) {
         unsigned long long x = r;
 #pragma unroll
-        for (int t = 0; t < kBlockKbMax; ++t) {
+        for (int t = 0; t < KB; ++t) {
           if (t < want && x > best[t]) {
             const unsigned long long y = best[t];
             best[t] = x;
@@ -104,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void block_select_kernel(
   // the expand kernel puts them in key order
   int32_t* out = sel + (static_cast<size_t>(h) * N + i) * kb;
 #pragma unroll
-  for (int t = 0; t < kBlockKbMax; ++t) {
+  for (int t = 0; t < KB; ++t) {
     if (t < kb) {
       int v = -1;
       if (t < want) v = static_cast<int>(0xFFFFFFFFu - static_cast<uint32_t>(best[t] & 0xFFFFFFFFull));
@@ -181,8 +182,19 @@ hipError_t means_sel_t(const float* q32, const float* k32, int nh, int N, int bl
                      kbar);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || sel == nullptr) return e;
-  hipLaunchKernelGGL((block_select_kernel<DP>), dim3((N + kThreads - 1) / kThreads, nh),
-                     dim3(kThreads), 0, s, q32, kbar, N, block, NB, kb, causal, scale, sel);
+  const dim3 grid((N + kThreads - 1) / kThreads, nh);
+  if (kb <= 4)
+    hipLaunchKernelGGL((block_select_kernel<DP, 4>), grid, dim3(kThreads), 0, s, q32, kbar, N,
+                       block, NB, kb, causal, scale, sel);
+  else if (kb <= 8)
+    hipLaunchKernelGGL((block_select_kernel<DP, 8>), grid, dim3(kThreads), 0, s, q32, kbar, N,
+                       block, NB, kb, causal, scale, sel);
+  else if (kb <= 16)
+    hipLaunchKernelGGL((block_select_kernel<DP, 16>), grid, dim3(kThreads), 0, s, q32, kbar, N,
+                       block, NB, kb, causal, scale, sel);
+  else
+    hipLaunchKernelGGL((block_select_kernel<DP, kBlockKbMax>), grid, dim3(kThreads), 0, s, q32,
+                       kbar, N, block, NB, kb, causal, scale, sel);
   return hipGetLastError();
 }
 
