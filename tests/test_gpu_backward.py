@@ -33,6 +33,7 @@ def _close(got, want, rel, name):
     (900, 900, 64, 32, "bf16", False),       # every key kept: dense attention's gradient
     (2000, 7, 128, 128, "f32", True),
     (8500, 40, 64, 16, "f32", True),
+    (1501, 33, 128, 32, "bf16", True),       # ragged: N and k not multiples of the tiles
 ])
 def test_backward_matches_oracle(N, k, D, dp, dtype, causal):
     w = W.Workload("bwd", 1, 2, N, D, dtype, d_proj=dp, k=k, causal=causal)
