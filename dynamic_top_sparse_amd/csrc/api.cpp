@@ -410,10 +410,12 @@ int sparse_attn_scores_topk_smoothed(const void* Q, const void* K, const void* P
 // ------------------------------------------------------------- decode ---
 namespace {
 struct DecodePlan {
-  size_t off_qlo32, off_qlo16, off_qstat, off_scores, off_idx, total;
+  size_t off_qlo32, off_qlo16, off_qstat, off_scores, off_idx, off_hist, off_ccount, off_cand,
+      off_selinfo, off_part, total;
 };
 DecodePlan decode_plan(const sa_dims& d, int dp, int k) {
   const size_t BH = static_cast<size_t>(d.B) * d.H;
+  const size_t nsl = static_cast<size_t>(decode_slices(d.N));
   DecodePlan p;
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -426,6 +428,11 @@ DecodePlan decode_plan(const sa_dims& d, int dp, int k) {
   p.off_qstat = take(BH * 16);
   p.off_scores = take(BH * static_cast<size_t>(d.N) * 4);
   p.off_idx = take(BH * static_cast<size_t>(k) * 4);
+  p.off_hist = take(BH * kDecodeHistBins * 4);
+  p.off_ccount = take(BH * nsl * 4);
+  p.off_cand = take(BH * nsl * kDecodeCandCap * 8);
+  p.off_selinfo = take(BH * 8);
+  p.off_part = take(BH * kGatherRanges * (static_cast<size_t>(d.D) + 4) * 4);
   p.total = off;
   return p;
 }
@@ -489,15 +496,24 @@ int run_decode(const void* q, const void* Kc, const void* Vc, const float* klow_
   float4* qstat = reinterpret_cast<float4*>(base + p.off_qstat);
   float* scores = reinterpret_cast<float*>(base + p.off_scores);
   int32_t* idx = idx_or_null ? idx_or_null : reinterpret_cast<int32_t*>(base + p.off_idx);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(base + p.off_hist);
+  int* ccount = reinterpret_cast<int*>(base + p.off_ccount);
+  uint2* cand = reinterpret_cast<uint2*>(base + p.off_cand);
+  int2* selinfo = reinterpret_cast<int2*>(base + p.off_selinfo);
+  float* part = reinterpret_cast<float*>(base + p.off_part);
   const int BH = d.B * d.H;
+  SA_TIMED_STATUS("decode_clear", launch_decode_clear(hist, BH, s));
   SA_TIMED_STATUS("decode_project", launch_project_rows(q, Pq, BH, 1, 1, d.D, d_proj, dtype, 0,
                                                         qlo32, qlo16, qstat, s));
   SA_TIMED_STATUS("decode_scores", launch_decode_scores(qlo32, 1, klow_cache, d.N, len, BH,
-                                                        d_proj, score_scale, scores, s));
-  SA_TIMED_STATUS("decode_select", launch_decode_select(scores, len, BH, k, idx, counts_or_null,
-                                                        d.N, s));
-  SA_TIMED_STATUS("decode_gather", launch_gather_rows(q, Kc, Vc, idx, k, BH, 1, d.N, d.D,
-                                                      softmax_scale, dtype, O, s));
+                                                        d_proj, score_scale, scores, hist, s));
+  SA_TIMED_STATUS("decode_collect", launch_decode_collect(scores, d.N, len, BH, k, hist, cand,
+                                                          ccount, selinfo, s));
+  SA_TIMED_STATUS("decode_select", launch_decode_select(scores, len, BH, k, cand, ccount,
+                                                        selinfo, idx, counts_or_null, d.N, s));
+  SA_TIMED_STATUS("decode_gather", launch_decode_gather_part(q, Kc, Vc, idx, k, len, BH, d.N,
+                                                             d.D, softmax_scale, dtype, part, s));
+  SA_TIMED_STATUS("decode_gather_merge", launch_decode_gather_merge(part, BH, d.D, dtype, O, s));
   return SA_OK;
 }
 }  // namespace

@@ -181,15 +181,37 @@ hipError_t launch_gather_rows(const void* Q, const void* K, const void* V, const
 hipError_t launch_project_rows(const void* X, const void* P, int nh, int rows, int out_stride,
                                int D, int dp, int dtype, int is_key, float* lo32, uint16_t* lo16,
                                float4* qstat, hipStream_t s);
-// Decode (decode.hip): exact scores of one query per head against the first
-// `len` rows of a k_low cache (head stride Ncap rows), then the top-k of
-// those scores per head, ascending, -1 padded; counts (optional) gains one
-// per selected key.
+// Decode (decode.hip), one query per head against the first `len` rows of
+// a k_low cache (head stride Ncap rows):
+//   clear:   zeroes the per-head histograms of the scores' leading bits;
+//   scores:  exact scores [nh][Ncap] and, added to those histograms, the
+//            count of keys per leading 11-bit bin of the order key;
+//   collect: per slice of kDecodeSliceKeys keys, the keys at or above the
+//            bin of the head's k-th largest score, in index order (at most
+//            kDecodeCandCap per slice, the full count in ccount);
+//   select:  the top-k per head, ascending, -1 padded; counts (optional)
+//            gains one per selected key;
+//   gather:  attention over the selected rows in kGatherRanges parts of the
+//            index row, then their merge.
+constexpr int kDecodeHistBins = 2048;
+constexpr int kDecodeSliceKeys = 2048;
+constexpr int kDecodeCandCap = 512;
+__host__ __device__ inline int decode_slices(int len) { return (len + kDecodeSliceKeys - 1) / kDecodeSliceKeys; }
+hipError_t launch_decode_clear(uint32_t* hist, int nh, hipStream_t s);
 hipError_t launch_decode_scores(const float* qlo, int q_stride, const float* klow, int Ncap,
                                 int len, int nh, int dp, float scale, float* scores,
-                                hipStream_t s);
-hipError_t launch_decode_select(const float* scores, int len, int nh, int k, int32_t* idx,
+                                uint32_t* hist, hipStream_t s);
+hipError_t launch_decode_collect(const float* scores, int Ncap, int len, int nh, int k,
+                                 const uint32_t* hist, uint2* cand, int* ccount, int2* selinfo,
+                                 hipStream_t s);
+hipError_t launch_decode_select(const float* scores, int len, int nh, int k, const uint2* cand,
+                                const int* ccount, const int2* selinfo, int32_t* idx,
                                 int32_t* counts, int Ncap, hipStream_t s);
+hipError_t launch_decode_gather_part(const void* q, const void* Kc, const void* Vc,
+                                     const int32_t* idx, int k, int len, int nh, int Ncap, int D,
+                                     float softmax_scale, int dtype, float* part, hipStream_t s);
+hipError_t launch_decode_gather_merge(const float* part, int nh, int D, int dtype, void* O,
+                                      hipStream_t s);
 // The no-allocation decode's device-resident workspace: its size, and its
 // address on the current device (looked up once per device).
 size_t decode_scratch_bytes();

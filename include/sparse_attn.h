@@ -239,7 +239,10 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
  *   O (out): [B,H,1,D]; idx_or_null (out, optional): [B,H,k] int32;
  *   counts_or_null (in/out, optional): [B,H,Ncap] int32, each selected key's
  *   count is incremented (selection frequency for cache eviction).
- *   ws: sparse_attn_decode_workspace_size(d, d_proj, k) bytes.
+ *   ws: sparse_attn_decode_workspace_size(d, d_proj, k) bytes (about 6 bytes
+ *   per cache row and head: its score and its share of the slots for the
+ *   keys collected near the k-th score); its contents need not start at
+ *   zero (the call clears what it counts into).
  */
 size_t sparse_attn_decode_workspace_size(sa_dims d, int32_t d_proj, int32_t k);
 int sparse_attn_decode_append_keys(const void* K_new, const void* Pk, sa_dims d, int32_t d_proj,
@@ -291,11 +294,12 @@ int sparse_attn_block_scores_dump(const void* Q, const void* K, const void* Pq, 
  * found once per device (the first call on a device looks up its address).
  * Its size is sparse_attn_decode_noalloc_max_bytes() (32 MiB); a call whose
  * sparse_attn_decode_workspace_size exceeds it returns SA_ERR_WORKSPACE with
- * nothing enqueued (B*H*Ncap*4 bytes of scores dominate: 32 heads of 128K
+ * nothing enqueued (about 6 bytes per cache row and head: 32 heads of 128K
  * keys fit).  The call allocates nothing and records no timing events.
  * All calls on one GPU share that array: calls that overlap in time on one
  * GPU (other streams, other threads) race and must be ordered by the
- * caller.  Nothing in the array needs to start at zero.
+ * caller.  Nothing in the array needs to start at zero: each call clears
+ * the part it counts into with a fill kernel of its own.
  */
 size_t sparse_attn_decode_noalloc_max_bytes(void);
 int sparse_attn_decode_noalloc(const void* q, const void* Kc, const void* Vc,

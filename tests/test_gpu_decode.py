@@ -25,6 +25,7 @@ def _np(t):
     ("bf16", 128, 64, 64, 3000, (3000, 1777, 40, 1), (1000, 1500, 500)),
     ("f32", 64, 16, 32, 1500, (1500, 33, 31), (1500,)),
     ("bf16", 64, 32, 200, 4100, (4100, 2049), (4100,)),
+    ("f32", 128, 128, 50, 4500, (4500, 2048, 2047), (2000, 2500)),
 ])
 def test_decode_equals_prefill_last_row_and_oracle(dtype, D, dp, k, N, lengths, chunks):
     w = W.Workload("dec", 2, 3, N, D, dtype, d_proj=dp, k=k, causal=True)
@@ -108,6 +109,44 @@ def test_decode_select_long_cache(same_keys):
         np.testing.assert_array_equal(idx[0, h], want)
         if same_keys:
             np.testing.assert_array_equal(idx[0, h], np.arange(k))
+        counts = np.zeros(N, np.int64)
+        counts[idx[0, h]] += 1
+        np.testing.assert_array_equal(_np(cache.counts[0, h]).astype(np.int64), counts)
+        o_ref = O.attend_row(O.f64(x["Q"][0, h, N - 1]), O.f64(x["K"][0, h]), O.f64(x["V"][0, h]),
+                             idx[0, h].astype(np.int64), sa.default_softmax_scale(64))
+        assert np.abs(_np(out[0, h, 0]) - o_ref).max() <= 1e-5
+
+
+@pytest.mark.parametrize("case", ["spread_ties", "slice_overflow"])
+def test_decode_select_collect_paths(case):
+    """The select finishes over the keys each 2048-key slice of the cache
+    collected near the k-th score.  spread_ties: every 100th key shares one
+    top score (200 keys over ten slices), k = 100: the 100 lowest-index ones,
+    which only the slices taken in order give.  slice_overflow: keys 0..2047
+    (slice 0) share the top score, k = 1024: more than a slice's 512 slots,
+    so the select runs over the scores in memory; keys 0..1023.  Both against
+    the oracle's top-k of the dumped scores, with the counts."""
+    N = 20000
+    k = 100 if case == "spread_ties" else 1024
+    w = W.Workload("dec", 1, 2, N, 64, "f32", d_proj=16, k=k, causal=True)
+    x = W.make_inputs(w, 23)
+    top = np.arange(0, N, 100) if case == "spread_ties" else np.arange(2048)
+    # rows whose projection is about 4 q_low (Pk's columns are nearly
+    # orthonormal): a score far above every random key's
+    q_low = x["Q"][:, :, N - 1:N].double() @ x["Pq"].double()
+    x["K"][:, :, torch.from_numpy(top)] = (4.0 * q_low @ x["Pk"].double().T).float()
+    g = {n: t.cuda() for n, t in x.items()}
+    cache = sa.DecodeCache(1, 2, N, 64, g["Pq"], g["Pk"], k, dtype=torch.float32)
+    cache.append(g["K"], g["V"])
+    q = g["Q"][:, :, N - 1:N].contiguous()
+    idx = torch.empty(1, 2, k, dtype=torch.int32, device="cuda")
+    out, idx = cache.step(q, idx=idx, count=True)
+    idx = _np(idx)
+    S = _np(sa.sparse_attn_scores_dump(g["Q"], g["K"], g["Pq"], g["Pk"], N - 1, 1, True))
+    for h in range(2):
+        want = O.topk_rows(S[0, h].astype(np.float64), [N - 1], k, True)[0]
+        np.testing.assert_array_equal(want, top[:k])     # the construction holds
+        np.testing.assert_array_equal(idx[0, h], want)
         counts = np.zeros(N, np.int64)
         counts[idx[0, h]] += 1
         np.testing.assert_array_equal(_np(cache.counts[0, h]).astype(np.int64), counts)
