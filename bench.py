@@ -328,13 +328,13 @@ def run_op(args, w) -> int:
             cache.step(q, O=o, profile=p)
         units = BH
         metric = f"decode queries/s (one query per head over a full KV cache), {w.name}"
+        nsl = (N + 2047) // 2048      # slices of the score and collect steps
         amount = {"decode_scores": float(BH * N * (4 * dp + 4)),
-                  # four digit passes, the count pass and the output pass over the scores
-                  "decode_select": float(BH * N * 4 * 6),
+                  "decode_collect": float(BH * N * 4 + BH * nsl * 2048 * 4),
                   "decode_gather": float(BH * k * 2 * D * e + BH * (k * 4 + 2 * D * e))}
         desc = {"decode_scores": "k_low cache rows (fp32) + scores",
-                "decode_select": "six reads of each head's fp32 scores (L2-resident)",
-                "decode_gather": "K, V cache rows of the kept keys + idx + q, O"}
+                "decode_collect": "each head's scores + its bin counts, read once per slice",
+                "decode_gather": "K, V cache rows of the kept keys + idx + q (partials apart)"}
 
         def oracle_fn(rows):
             for _ in rows:
@@ -513,9 +513,9 @@ def main() -> int:
         ws = sa.allocate_workspace(g["Q"], w.d_proj, w.k, w.causal, with_idx=True,
                                    heads_per_chunk=hc)
 
-        def step(p=None):
+        def step(p=None, fd=fdt):
             sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, w.causal,
-                               O=out, workspace=ws, filter_dtype=fdt, profile=p)
+                               O=out, workspace=ws, filter_dtype=fd, profile=p)
     # 512 MiB written between timed steps (outside their event brackets), so
     # no step starts with the previous one's data in L2 or the memory-side
     # cache
@@ -540,8 +540,32 @@ def main() -> int:
     step_ms = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
     recs = prof.read()
     prof.close()
-    del flush
     stats = sa.sparse_attn_workspace_stats(ws) if ws is not None else None
+    # the same forward with the filter's other 16-bit operand type (the
+    # indices do not depend on it), timed the same way over a few steps
+    alt_filter = None
+    if not band and args.steps > 0:
+        adt_name = "bf16" if args.filter_dtype == "f16" else "f16"
+        adt = torch.bfloat16 if adt_name == "bf16" else torch.float16
+        n_alt = min(args.steps, 5)
+        step(fd=adt)
+        torch.cuda.synchronize()
+        aprof = sa.Profile()
+        aev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(n_alt)]
+        for e0, e1 in aev:
+            flush.fill_(1)
+            e0.record(stream)
+            step(aprof, fd=adt)
+            e1.record(stream)
+        torch.cuda.synchronize()
+        a_ms = sorted(e0.elapsed_time(e1) for e0, e1 in aev)
+        a_filter = [ms for name, ms in aprof.read() if name == "filter"]
+        aprof.close()
+        alt_filter = {"filter_dtype": adt_name, "steps": n_alt,
+                      "ms_per_step": float(np.median(a_ms)),
+                      "filter_ms_per_launch": float(np.mean(a_filter)) if a_filter else None}
+    del flush
     if args.copy_probe_mib > 0:
         src = torch.ones(args.copy_probe_mib << 18, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
@@ -653,6 +677,14 @@ def main() -> int:
             "margin_violations": stats["margin_violations"],
             "filter_dtype": args.filter_dtype}
         result["filter_mfma_counters"] = filter_mfma_counters()
+    if alt_filter is not None:
+        fl = alt_filter["filter_ms_per_launch"]
+        if fl and n_filter:
+            heads_f = w.B * w.H * args.steps / n_filter
+            alt_filter["filter_frac_of_bf16_peak"] = (
+                2.0 * w.d_proj * a["pairs_per_head"] * heads_f / (fl / 1e3) / 1e12
+                / PEAK_BF16_TFLOPS)
+        result["other_filter_operands"] = alt_filter
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(x, w)
     print(json.dumps(result))
