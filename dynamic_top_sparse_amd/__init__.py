@@ -42,6 +42,7 @@ EXPORTS = (
     "sparse_attn_decode_append_keys", "sparse_attn_decode", "sparse_attn_block_workspace_size",
     "sparse_attn_block_topk", "sparse_attn_block_scores_dump", "sparse_attn_bwd_workspace_size",
     "sparse_attn_bwd", "sparse_attn_decode_noalloc_max_bytes", "sparse_attn_decode_noalloc",
+    "sparse_attn_gather_workspace_size", "sparse_attn_gather_ws",
 )
 
 
@@ -89,6 +90,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
                                                    i32, vp, vp, sz, op, vp]),
         "sparse_attn_gather": (ctypes.c_int, [vp, vp, vp, vp, i32, sa_dims, f32, i32, vp, op,
                                               vp]),
+        "sparse_attn_gather_workspace_size": (sz, [sa_dims, i32, i32]),
+        "sparse_attn_gather_ws": (ctypes.c_int, [vp, vp, vp, vp, i32, sa_dims, f32, i32, vp, vp,
+                                                 sz, op, vp]),
         "sparse_attn_fwd": (ctypes.c_int, [vp, vp, vp, vp, vp, sa_dims, i32, i32, i32, f32, f32,
                                            i32, vp, vp, vp, sz, op, vp]),
         "sparse_attn_band_indices": (ctypes.c_int, [sa_dims, i32, i32, vp, i32, op, vp]),
@@ -342,8 +346,13 @@ def sparse_attn_scores_topk(Q, K, Pq, Pk, k: int, causal: bool = False,
 
 def sparse_attn_gather(Q, K, V, idx, softmax_scale: Optional[float] = None,
                        O: Optional[torch.Tensor] = None,
-                       profile: Optional[Profile] = None) -> torch.Tensor:
-    """O [B,H,N,D]: softmax attention of each query over its idx row."""
+                       profile: Optional[Profile] = None, by_range: bool = True,
+                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """O [B,H,N,D]: softmax attention of each query over its idx row.  With
+    by_range (the default) the call is sparse_attn_gather_ws, which takes
+    rows of ascending keys by key range when N is large (a workspace of
+    sparse_attn_gather_workspace_size bytes, allocated here unless given);
+    otherwise sparse_attn_gather, one pass per row."""
     _check_qkv(Q, K, V, O)
     B, H, N, D = Q.shape
     _tensor(idx, "idx")
@@ -354,7 +363,22 @@ def sparse_attn_gather(Q, K, V, idx, softmax_scale: Optional[float] = None,
     scale = default_softmax_scale(D) if softmax_scale is None else float(softmax_scale)
     if O is None:
         O = torch.empty_like(Q)
-    st = load_library().sparse_attn_gather(
+    lib = load_library()
+    n_ws = int(lib.sparse_attn_gather_workspace_size(_dims(Q), k, _dtype_code(Q))) \
+        if by_range else 0
+    if n_ws > 0:
+        if workspace is None:
+            workspace = torch.empty(n_ws, dtype=torch.uint8, device=Q.device)
+        _tensor(workspace, "workspace")
+        if workspace.dtype != torch.uint8 or workspace.device != Q.device:
+            raise ValueError("workspace must be a uint8 tensor on Q's device")
+        st = lib.sparse_attn_gather_ws(
+            _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(idx, "idx"), k, _dims(Q), scale,
+            _dtype_code(Q), _dev(O, "O"), _dev(workspace, "workspace"), workspace.numel(),
+            _options(None, profile), _stream(Q))
+        _check(st, "sparse_attn_gather_ws")
+        return O
+    st = lib.sparse_attn_gather(
         _dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(idx, "idx"), k, _dims(Q), scale,
         _dtype_code(Q), _dev(O, "O"), _options(None, profile), _stream(Q))
     _check(st, "sparse_attn_gather")

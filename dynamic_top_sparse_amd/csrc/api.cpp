@@ -322,6 +322,85 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
              : SA_ERR_HIP;
 }
 
+// ------------------------------------------- gather with a workspace ---
+namespace {
+struct GatherPlan {
+  size_t off_seg, off_list, off_count, off_part, total;
+};
+// The key-range path applies as in the fused forward: N > 8192 and a head's
+// K rows addressable with 32-bit byte offsets; total = 0 otherwise.
+GatherPlan gather_plan(const sa_dims& d, int dtype) {
+  GatherPlan p{};
+  const size_t esz = dtype == SA_F32 ? 4 : 2;
+  if (!(d.N > 8192 && static_cast<size_t>(d.N) * d.D * esz <= 0xFFFFFFFFull)) return p;
+  const size_t rows = static_cast<size_t>(d.B) * d.H * d.N;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  p.off_seg = take(rows * (kGatherRanges + 1) * 4);
+  p.off_list = take(rows * 4);
+  p.off_count = take(4);
+  p.off_part = take(static_cast<size_t>(d.N) * kGatherRanges * (static_cast<size_t>(d.D) + 4) * 4);
+  p.total = off;
+  return p;
+}
+}  // namespace
+
+size_t sparse_attn_gather_workspace_size(sa_dims d, int32_t k, int32_t dtype) {
+  if (check_dims(d, k) != SA_OK || !supported_D(d.D)) return 0;
+  if (dtype != SA_F32 && dtype != SA_BF16) return 0;
+  return gather_plan(d, dtype).total;
+}
+
+int sparse_attn_gather_ws(const void* Q, const void* K, const void* V, const int32_t* idx,
+                          int32_t k, sa_dims d, float softmax_scale, int32_t dtype, void* O,
+                          void* ws, size_t ws_bytes, const sa_options* opts, void* stream) {
+  if (!Q || !K || !V || !idx || !O) return SA_ERR_NULL;
+  int st = check_dims(d, k);
+  if (st != SA_OK) return st;
+  if (!supported_D(d.D)) return SA_ERR_UNSUPPORTED;
+  if (dtype != SA_F32 && dtype != SA_BF16) return SA_ERR_UNSUPPORTED;
+  if (!std::isfinite(softmax_scale)) return SA_ERR_SHAPE;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(idx) || !aligned16(O))
+    return SA_ERR_ALIGN;
+  sa_profile* prof = profile_of(opts);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const GatherPlan p = gather_plan(d, dtype);
+  if (p.total == 0)
+    return timed_gather(Q, K, V, idx, k, d.B * d.H, d.N, d.D, softmax_scale, dtype, O, prof, s) ==
+                   hipSuccess
+               ? SA_OK
+               : SA_ERR_HIP;
+  if (!ws) return SA_ERR_NULL;
+  if (!aligned16(ws)) return SA_ERR_ALIGN;
+  if (ws_bytes < p.total) return SA_ERR_WORKSPACE;
+  unsigned char* base = static_cast<unsigned char*>(ws);
+  int* seg = reinterpret_cast<int*>(base + p.off_seg);
+  int* list = reinterpret_cast<int*>(base + p.off_list);
+  int* count = reinterpret_cast<int*>(base + p.off_count);
+  float* part = reinterpret_cast<float*>(base + p.off_part);
+  const int BH = d.B * d.H;
+  SA_TIMED_STATUS("gather_check", launch_gather_check(idx, k, BH, d.N, seg, list, count, s));
+  const size_t esz = dtype == SA_F32 ? 4 : 2;
+  const size_t head = static_cast<size_t>(d.N) * d.D * esz;
+  for (int h = 0; h < BH; ++h) {
+    if (launch_gather_split(static_cast<const unsigned char*>(Q) + h * head,
+                            static_cast<const unsigned char*>(K) + h * head,
+                            static_cast<const unsigned char*>(V) + h * head,
+                            idx + static_cast<size_t>(h) * d.N * k, k, d.N, d.D, softmax_scale,
+                            dtype, seg + static_cast<size_t>(h) * d.N * (kGatherRanges + 1), part,
+                            static_cast<unsigned char*>(O) + h * head, prof, s) != hipSuccess)
+      return SA_ERR_HIP;
+  }
+  // rows the ranges could not take (their merged output was zero) last
+  SA_TIMED_STATUS("gather_rest", launch_gather_list(Q, K, V, idx, k, d.N, d.D, softmax_scale,
+                                                    dtype, list, count, O, s));
+  return SA_OK;
+}
+
 int sparse_attn_fwd(const void* Q, const void* K, const void* V, const void* Pq, const void* Pk,
                     sa_dims d, int32_t d_proj, int32_t k, int32_t causal, float score_scale,
                     float softmax_scale, int32_t dtype, void* O, int32_t* idx_or_null, void* ws,

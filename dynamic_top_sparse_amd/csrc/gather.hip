@@ -47,35 +47,26 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 
+// One wave attends query row `row` (Q, idx, O rows at row; the head's K and
+// V rows at Kh, Vh, N of them).
 template <typename T, int D>
-__global__ __launch_bounds__(kThreads) void gather_kernel(
-    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int32_t* __restrict__ idx, int k, int Nq, int Nk, float scale, T* __restrict__ O) {
-  // Nq query rows (and idx, O rows) and Nk key rows per head: equal in the
-  // forward, one query against a key cache when decoding
+__device__ __forceinline__ void gather_row(const T* __restrict__ Q, const T* __restrict__ Kh,
+                                           const T* __restrict__ Vh,
+                                           const int32_t* __restrict__ idx, int k, int N,
+                                           float scale, T* __restrict__ O, size_t row,
+                                           float* slog, int* sidx) {
   constexpr int EPL = Vec<T>::kElems;
   constexpr int LPR = D / EPL;
-  extern __shared__ float slog_all[];
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
   const int l = lane_id();
-  float* slog = slog_all + w * gather_wave_floats(k);
-  int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
-  const int h = blockIdx.y;
-  const int q = blockIdx.x * kWaves + w;
-  if (q >= Nq) return;
-  const size_t hN = static_cast<size_t>(h) * Nq;
-  const T* Kh = K + static_cast<size_t>(h) * Nk * D;
-  const T* Vh = V + static_cast<size_t>(h) * Nk * D;
-  const int N = Nk;
-  stage_entries(idx + (hN + q) * k, 0, k, sidx);
-  const int32_t* row = sidx;
+  stage_entries(idx + row * k, 0, k, sidx);
+  const int32_t* rw = sidx;
   int bad = 0;
-  logits<T, D>(Q + (hN + q) * D, Kh, row, 0, k, N, scale * kLog2e, slog, bad);
+  logits<T, D>(Q + row * D, Kh, rw, 0, k, N, scale * kLog2e, slog, bad);
   if (bad) atomicOr(&g_index_error_flag, 1);
   wave_sync();
   float sum;
   const float mx = softmax_weights(slog, k, sum);
-  T* out = O + (hN + q) * D;
+  T* out = O + row * D;
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   float acc[EPL];
   if (mx == -INFINITY) {  // no valid entry: zero output
@@ -85,13 +76,102 @@ __global__ __launch_bounds__(kThreads) void gather_kernel(
     return;
   }
   wave_sync();
-  weighted_rows<T, D>(Vh, row, 0, k, N, slog, acc);
+  weighted_rows<T, D>(Vh, rw, 0, k, N, slog, acc);
   if (g == 0) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) acc[e] /= sum;
     *reinterpret_cast<uint4*>(out + e0) = Vec<T>::pack(acc);
   }
 }
+
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void gather_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, int k, int Nq, int Nk, float scale, T* __restrict__ O) {
+  // Nq query rows (and idx, O rows) and Nk key rows per head: equal in the
+  // forward, one query against a key cache when decoding
+  extern __shared__ float slog_all[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);   // wave-uniform, scalar
+  float* slog = slog_all + w * gather_wave_floats(k);
+  int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
+  const int h = blockIdx.y;
+  const int q = blockIdx.x * kWaves + w;
+  if (q >= Nq) return;
+  gather_row<T, D>(Q, K + static_cast<size_t>(h) * Nk * D, V + static_cast<size_t>(h) * Nk * D,
+                   idx, k, Nk, scale, O, static_cast<size_t>(h) * Nq + q, slog, sidx);
+}
+
+// The rows listed in `list` (flat row numbers h*N + q, count at *count),
+// each attended as gather_kernel does: the rows the key-range path of
+// sparse_attn_gather_ws cannot take.  A fixed grid of waves walks the list.
+template <typename T, int D>
+__global__ __launch_bounds__(kThreads) void gather_list_kernel(
+    const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
+    const int32_t* __restrict__ idx, int k, int N, float scale, const int* __restrict__ list,
+    const int* __restrict__ count, T* __restrict__ O) {
+  extern __shared__ float slog_all[];
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  float* slog = slog_all + w * gather_wave_floats(k);
+  int* sidx = reinterpret_cast<int*>(slog + gather_slog_floats(k));
+  const int n = *count;
+  for (int i = blockIdx.x * kWaves + w; i < n; i += gridDim.x * kWaves) {
+    const size_t row = static_cast<size_t>(static_cast<unsigned>(list[i]));
+    const size_t h = row / static_cast<unsigned>(N);
+    gather_row<T, D>(Q, K + h * N * D, V + h * N * D, idx, k, N, scale, O, row, slog, sidx);
+    wave_sync();    // this row's LDS reads are done before the next row is staged
+  }
+}
+
+// Row check of sparse_attn_gather_ws, one wave per row.  A row whose valid
+// entries (0 <= j < N) form an ascending prefix (repeats allowed), followed
+// by negative entries only, gets seg[row][r] = its valid entries below the
+// start of key range r (r = 0..8; seg[row][8] = all of them), the form the
+// key-range kernels take.  Any other row (out of order, an entry >= N, a
+// valid entry after a negative one) gets -1 throughout, so the range kernels
+// leave it empty, and joins the list of rows the single-pass kernel takes.
+__global__ __launch_bounds__(kThreads) void gather_row_check_kernel(
+    const int32_t* __restrict__ idx, int k, int N, long long rows, GatherRanges gr,
+    int* __restrict__ seg, int* __restrict__ list, int* __restrict__ count) {
+  constexpr int R = kGatherRanges;
+  const int w = threadIdx.x / kWave, l = lane_id();
+  const long long row = static_cast<long long>(blockIdx.x) * (kThreads / kWave) + w;
+  if (row >= rows) return;
+  const int32_t* ir = idx + row * k;
+  int below[R + 1];
+#pragma unroll
+  for (int r = 0; r <= R; ++r) below[r] = 0;
+  bool ok = true;               // wave-uniform after the ballots
+  int last = -1;                // previous chunk's last entry
+  for (int t0 = 0; t0 < k; t0 += kWave) {
+    const int t = t0 + l;
+    const int j = t < k ? ir[t] : -1;
+    const bool valid = j >= 0 && j < N;
+    int prev = __shfl_up(j, 1, kWave);
+    if (l == 0) prev = last;
+    const bool prev_valid = prev >= 0 && prev < N;
+    const bool bad = j >= N || (valid && ((t > 0 && !prev_valid) || (prev_valid && prev > j)));
+    if (__ballot(bad)) ok = false;
+#pragma unroll
+    for (int r = 1; r < R; ++r) below[r] += valid && j < gr.b[r] ? 1 : 0;
+    below[R] += valid ? 1 : 0;
+    last = __shfl(j, kWave - 1, kWave);
+  }
+  int* out = seg + row * (R + 1);
+  if (!ok) {
+    if (l <= R) out[l] = -1;
+    if (l == 0) list[atomicAdd(count, 1)] = static_cast<int>(row);
+    return;
+  }
+#pragma unroll
+  for (int r = 1; r <= R; ++r) below[r] = wave_sum_i(below[r]);
+  if (l == 0) {
+    out[0] = 0;
+#pragma unroll
+    for (int r = 1; r <= R; ++r) out[r] = below[r];
+  }
+}
+
+__global__ void gather_zero_kernel(int* __restrict__ x) { *x = 0; }
 
 // --------------------------------------------------------- split gather ---
 // The fused forward's idx rows are ascending, so the keys of a row that fall
@@ -273,6 +353,22 @@ hipError_t gather_t(const void* Q, const void* K, const void* V, const int32_t* 
   return hipGetLastError();
 }
 
+template <typename T, int D>
+hipError_t gather_list_t(const void* Q, const void* K, const void* V, const int32_t* idx, int k,
+                         int N, float scale, const int* list, const int* count, void* O,
+                         hipStream_t s) {
+  const size_t lds = static_cast<size_t>(kWaves) * gather_wave_floats(k) * sizeof(float);
+  static std::atomic<int> lds_set[kMaxDevices];
+  const hipError_t e = set_lds_limit_once(reinterpret_cast<const void*>(&gather_list_kernel<T, D>),
+                                          static_cast<int>(kWaves) * gather_wave_floats(kKMax) * 4,
+                                          lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gather_list_kernel<T, D>), dim3(1024), dim3(kThreads), lds, s,
+                     static_cast<const T*>(Q), static_cast<const T*>(K), static_cast<const T*>(V),
+                     idx, k, N, scale, list, count, static_cast<T*>(O));
+  return hipGetLastError();
+}
+
 }  // namespace
 
 
@@ -304,6 +400,31 @@ hipError_t launch_gather_split(const void* Q, const void* K, const void* V, cons
   } else {
     if (D == 64) return gather_split_t<bf16_t, 64>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
     if (D == 128) return gather_split_t<bf16_t, 128>(Q, K, V, idx, k, N, softmax_scale, seg, part, O, prof, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_check(const int32_t* idx, int k, int nheads, int N, int* seg,
+                               int* list, int* count, hipStream_t s) {
+  hipLaunchKernelGGL(gather_zero_kernel, dim3(1), dim3(1), 0, s, count);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const long long rows = static_cast<long long>(nheads) * N;
+  const long long blocks = (rows + kWaves - 1) / kWaves;
+  hipLaunchKernelGGL(gather_row_check_kernel, dim3(static_cast<unsigned>(blocks)), dim3(kThreads),
+                     0, s, idx, k, N, rows, gather_ranges(N, 0), seg, list, count);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_list(const void* Q, const void* K, const void* V, const int32_t* idx,
+                              int k, int N, int D, float softmax_scale, int dtype, const int* list,
+                              const int* count, void* O, hipStream_t s) {
+  if (dtype == 0) {
+    if (D == 64) return gather_list_t<float, 64>(Q, K, V, idx, k, N, softmax_scale, list, count, O, s);
+    if (D == 128) return gather_list_t<float, 128>(Q, K, V, idx, k, N, softmax_scale, list, count, O, s);
+  } else {
+    if (D == 64) return gather_list_t<bf16_t, 64>(Q, K, V, idx, k, N, softmax_scale, list, count, O, s);
+    if (D == 128) return gather_list_t<bf16_t, 128>(Q, K, V, idx, k, N, softmax_scale, list, count, O, s);
   }
   return hipErrorInvalidValue;
 }

@@ -175,6 +175,15 @@ hipError_t launch_gather(const void* Q, const void* K, const void* V, const int3
 hipError_t launch_gather_rows(const void* Q, const void* K, const void* V, const int32_t* idx,
                               int k, int nheads, int Nq, int Nk, int D, float softmax_scale,
                               int dtype, void* O, hipStream_t s);
+// sparse_attn_gather_ws: per row (nheads*N of them) the key-range segment
+// starts seg[row][0..8] of a row the range kernels can take, else -1s and
+// the row's number h*N + q appended to list (count at *count, zeroed here);
+// then the listed rows through the single-pass kernel.
+hipError_t launch_gather_check(const int32_t* idx, int k, int nheads, int N, int* seg,
+                               int* list, int* count, hipStream_t s);
+hipError_t launch_gather_list(const void* Q, const void* K, const void* V, const int32_t* idx,
+                              int k, int N, int D, float softmax_scale, int dtype, const int* list,
+                              const int* count, void* O, hipStream_t s);
 // Projection of `rows` rows of each of nh heads (X rows of head h at
 // h*rows), written at row h*out_stride of lo32 (and lo16 / qstat for
 // queries); nothing beyond `rows` is written.

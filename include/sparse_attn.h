@@ -151,6 +151,28 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
                        const sa_options* opts, void* stream);
 
 /*
+ * sparse_attn_gather with a workspace, for large N: the same attention
+ * (same entry rules, same sticky flag), computed by key range where a row
+ * allows it, so that each XCD's L2 serves one range of the head's K and V
+ * rows, as the fused forward does.  A row qualifies when its valid entries
+ * (0 <= j < N) form an ascending prefix (repeats allowed) followed by
+ * negative entries only, which is what sparse_attn_scores_topk,
+ * sparse_attn_block_topk, the smoothed top-k and the band writers return;
+ * every other row is attended in one pass as by sparse_attn_gather.  O
+ * agrees with sparse_attn_gather's to fp32 rounding (the ranges' partial
+ * softmax sums are merged), not bit for bit.
+ *   ws: sparse_attn_gather_workspace_size(d, k, dtype) bytes (about 40 bytes
+ *   per row plus 8·(D+4)·4 bytes per query of one head).  When that size is
+ *   0 (N <= 8192, or a head's K rows beyond 32-bit byte offsets) the call
+ *   is sparse_attn_gather and ws may be NULL.  The workspace's contents need
+ *   not start at zero.
+ */
+size_t sparse_attn_gather_workspace_size(sa_dims d, int32_t k, int32_t dtype);
+int sparse_attn_gather_ws(const void* Q, const void* K, const void* V, const int32_t* idx,
+                          int32_t k, sa_dims d, float softmax_scale, int32_t dtype, void* O,
+                          void* ws, size_t ws_bytes, const sa_options* opts, void* stream);
+
+/*
  * The whole forward, the two-step allocation of page "mhpq.cn/news/1098205"
  * §1.3 (score every pair cheaply, then attend only to each query's best k)
  * as run by the §3.2 forward: sparse_attn_scores_topk followed by

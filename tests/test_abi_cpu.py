@@ -92,6 +92,31 @@ def test_workspace_size_arithmetic(lib):
     assert lib.sparse_attn_workspace_size(D(0, 1, 1024, 64), 16, 32, 0, 0, 0) == 0
 
 
+def test_gather_ws_size_and_validation(lib):
+    # the key-range path applies past N = 8192: 36 B of segment starts and 4 B of
+    # list per row, a count, and one head's partials (8 ranges x (D + 4) floats)
+    assert lib.sparse_attn_gather_workspace_size(D(1, 2, 8192, 128), 64, 1) == 0
+    n = lib.sparse_attn_gather_workspace_size(D(1, 2, 8200, 128), 64, 1)
+    rows = 2 * 8200
+    assert n >= rows * 40 + 8200 * 8 * 132 * 4
+    assert n < rows * 40 + 8200 * 8 * 132 * 4 + 4 * 256
+    assert lib.sparse_attn_gather_workspace_size(D(1, 2, 8200, 96), 64, 1) == 0
+    assert lib.sparse_attn_gather_workspace_size(D(1, 2, 8200, 128), 64, 2) == 0
+    big = D(1, 2, 8200, 128)
+    g = lambda **kw: lib.sparse_attn_gather_ws(
+        kw.get("Q", A), A, A, kw.get("idx", A), kw.get("k", 64), kw.get("d", big),
+        kw.get("scale", 0.1), kw.get("dtype", 1), A, kw.get("ws", A), kw.get("ws_bytes", n),
+        None, None)
+    assert g(Q=None) == -1
+    assert g(k=0) == -2
+    assert g(scale=float("nan")) == -2
+    assert g(dtype=2) == -3
+    assert g(idx=A + 4) == -4
+    assert g(ws=None) == -1                      # the key-range path needs its workspace
+    assert g(ws=A + 8) == -4
+    assert g(ws_bytes=n - 1) == -5
+
+
 def _topk(lib, Q=A, K=A, Pq=A, Pk=A, d=D(1, 1, 1024, 64), dp=16, k=32, causal=0, scale=0.25,
           dtype=0, idx=A, ws=A, ws_bytes=0, opts=None):
     return lib.sparse_attn_scores_topk(Q, K, Pq, Pk, d, dp, k, causal, scale, dtype, idx, ws,

@@ -121,6 +121,47 @@ def test_gather_flags_out_of_range_index():
     assert np.abs(_rows_np(got) - want).max() <= 1e-5
 
 
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128),
+                                     (torch.bfloat16, 64)])
+def test_gather_by_key_range_mixed_rows(dtype, D):
+    """sparse_attn_gather_ws just past the key-range threshold (N = 8200):
+    rows of ascending keys with -1 tails, repeated keys, keys crowded into
+    one range and an empty row take the key-range path; an unordered row, a
+    -1 before a valid entry and an entry >= N go through the single pass (the
+    entry >= N skipped and flagged).  Every row against the oracle, and the
+    one-pass gather within the same bound."""
+    B, H, N, k = 1, 2, 8200, 64
+    gen = torch.Generator().manual_seed(D + 7)
+    Q, K, V = (torch.randn(B, H, N, D, generator=gen).to(dtype) for _ in range(3))
+    idx = torch.sort(torch.randint(0, N, (B, H, N, k), generator=gen, dtype=torch.int32),
+                     dim=-1).values
+    for i in range(0, N, 5):                    # -1 tails of 0 .. 16 entries
+        t = i % 17
+        if t:
+            idx[:, :, i, k - t:] = -1
+    idx[0, 0, 3] = -1                           # empty row
+    idx[0, 1, 20] = torch.sort(torch.randint(0, 100, (k,), generator=gen,
+                                             dtype=torch.int32)).values   # one range only
+    idx[0, 0, 30, :5] = idx[0, 0, 30, 0]        # repeats, still ascending
+    for i in (7, 100, 5000):                    # unordered
+        idx[0, 0, i] = idx[0, 0, i].flip(0)
+    idx[0, 1, 11, 10] = -1                      # a valid entry after a -1
+    idx[0, 1, 13, k - 1] = N                    # out of range: skipped, flagged
+    assert sa.sparse_attn_check_status() == 0
+    g = {n: t.cuda() for n, t in (("Q", Q), ("K", K), ("V", V))}
+    gi = idx.cuda()
+    got = sa.sparse_attn_gather(g["Q"], g["K"], g["V"], gi, 0.2)
+    assert sa.sparse_attn_check_status() == -7
+    one = sa.sparse_attn_gather(g["Q"], g["K"], g["V"], gi, 0.2, by_range=False)
+    assert sa.sparse_attn_check_status() == -7
+    want = O.gather_attention(Q, K, V, np.where(idx.numpy() >= N, -1, idx.numpy()), 0.2)
+    got_np = _rows_np(got.float())
+    err = np.abs(got_np - want).max()
+    assert err <= TOL[dtype], err
+    assert np.abs(got_np - _rows_np(one.float())).max() <= TOL[dtype]
+    assert torch.all(got[0, 0, 3] == 0)
+
+
 @pytest.mark.parametrize("w_left,w_right,N", [(64, 64, 4096), (5, 5, 1024), (0, 7, 300),
                                               (9, 0, 301)])
 def test_band_indices_match_oracle(w_left, w_right, N):
