@@ -849,12 +849,37 @@ __device__ __forceinline__ void bwd_logits_online_trusted(const bf16_t* __restri
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) dot[u] = dot_of(kv[u]);
     group_sum_n<LPR>(dot);
+    // the block's largest logit first: one rescale per block, not per row
+    float mb = m;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int t = tb + u * RPI + g;
-      const float lt = dot[u] * scale2;
-      if ((l % LPR) == 0) slog[t] = lt;
-      update(lt, sdp[t], kv[u]);
+      dot[u] *= scale2;
+      mb = fmaxf(mb, dot[u]);
+      if ((l % LPR) == 0) slog[tb + u * RPI + g] = dot[u];
+    }
+    if (mb > m) {                   // group-uniform
+      const float c = __builtin_amdgcn_exp2f(m - mb);   // m = -inf gives 0
+      S *= c;
+      U *= c;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        A[e] *= c;
+        B[e] *= c;
+      }
+      m = mb;
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const float ew = __builtin_amdgcn_exp2f(dot[u] - m), ed = ew * sdp[tb + u * RPI + g];
+      S += ew;
+      U += ed;
+      float kf[EPL];
+      Vec<bf16_t>::unpack(kv[u], kf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        A[e] = __builtin_fmaf(ed, kf[e], A[e]);
+        B[e] = __builtin_fmaf(ew, kf[e], B[e]);
+      }
     }
   }
   if (tb < n) {
