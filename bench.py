@@ -51,11 +51,11 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
     # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 123.888e9, "write_bytes": 93.374e9,
+    "filter": {"fetch_bytes": 105.425e9, "write_bytes": 93.499e9,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
-    "gather": {"fetch_bytes": 11.024e9, "write_bytes": 0.570e9,
-               "src": "0b217f78d9b807ba00044fb41f283a0f4dcc4aec81f27975b7798b6372f6888b"},
-    "rerank": {"fetch_bytes": 69.486e9, "write_bytes": 10.889e9,
+    "gather": {"fetch_bytes": 11.026e9, "write_bytes": 0.570e9,
+               "src": "a8410071c224903294910896dfb418e6baff825cb3d755cebd9383437b3678c7"},
+    "rerank": {"fetch_bytes": 69.487e9, "write_bytes": 10.889e9,
                "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
 }
 # the sources each kernel's code comes from (their sha256, concatenated in
@@ -70,8 +70,8 @@ KERNEL_SOURCE = {"filter": ["scorer.hip"], "gather": ["gather.hip", "rows.h"],
 # XCD over the dispatch's duration.
 MFMA_COUNTERS: dict = {
     "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
-               "GRBM_GUI_ACTIVE_all_xcds": 1342870343, "dispatch_ms": 93.65,
-               "mfma_busy_frac": 0.3998, "shader_clock_ghz": 1.792,
+               "GRBM_GUI_ACTIVE_all_xcds": 1348118725, "dispatch_ms": 93.21,
+               "mfma_busy_frac": 0.3982, "shader_clock_ghz": 1.808,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
 }
 

@@ -121,8 +121,8 @@ def test_gather_flags_out_of_range_index():
     assert np.abs(_rows_np(got) - want).max() <= 1e-5
 
 
-@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.bfloat16, 128),
-                                     (torch.bfloat16, 64)])
+@pytest.mark.parametrize("dtype,D", [(torch.float32, 64), (torch.float32, 128),
+                                     (torch.bfloat16, 128), (torch.bfloat16, 64)])
 def test_gather_by_key_range_mixed_rows(dtype, D):
     """sparse_attn_gather_ws just past the key-range threshold (N = 8200):
     rows of ascending keys with -1 tails, repeated keys, keys crowded into
