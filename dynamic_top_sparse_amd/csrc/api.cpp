@@ -328,12 +328,16 @@ struct GatherPlan {
   size_t off_seg, off_list, off_count, off_part, total;
 };
 // The key-range path applies as in the fused forward: N > 8192 and a head's
-// K rows addressable with 32-bit byte offsets; total = 0 otherwise.
+// K rows addressable with 32-bit byte offsets (and every row numbered by an
+// int32 in the list of rows it leaves to the single pass); total = 0
+// otherwise.
 GatherPlan gather_plan(const sa_dims& d, int dtype) {
   GatherPlan p{};
   const size_t esz = dtype == SA_F32 ? 4 : 2;
-  if (!(d.N > 8192 && static_cast<size_t>(d.N) * d.D * esz <= 0xFFFFFFFFull)) return p;
   const size_t rows = static_cast<size_t>(d.B) * d.H * d.N;
+  if (!(d.N > 8192 && static_cast<size_t>(d.N) * d.D * esz <= 0xFFFFFFFFull &&
+        rows <= 0x7FFFFFFFull))
+    return p;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;

@@ -163,8 +163,8 @@ int sparse_attn_gather(const void* Q, const void* K, const void* V, const int32_
  * softmax sums are merged), not bit for bit.
  *   ws: sparse_attn_gather_workspace_size(d, k, dtype) bytes (about 40 bytes
  *   per row plus 8·(D+4)·4 bytes per query of one head).  When that size is
- *   0 (N <= 8192, or a head's K rows beyond 32-bit byte offsets) the call
- *   is sparse_attn_gather and ws may be NULL.  The workspace's contents need
+ *   0 (N <= 8192, a head's K rows beyond 32-bit byte offsets, or more than
+ *   2^31 - 1 rows in all) the call is sparse_attn_gather and ws may be NULL.  The workspace's contents need
  *   not start at zero.
  */
 size_t sparse_attn_gather_workspace_size(sa_dims d, int32_t k, int32_t dtype);

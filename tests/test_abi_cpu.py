@@ -102,6 +102,8 @@ def test_gather_ws_size_and_validation(lib):
     assert n < rows * 40 + 8200 * 8 * 132 * 4 + 4 * 256
     assert lib.sparse_attn_gather_workspace_size(D(1, 2, 8200, 96), 64, 1) == 0
     assert lib.sparse_attn_gather_workspace_size(D(1, 2, 8200, 128), 64, 2) == 0
+    assert lib.sparse_attn_gather_workspace_size(D(1, 2**17, 8200, 64), 1, 1) > 0
+    assert lib.sparse_attn_gather_workspace_size(D(1, 2**18, 8200, 64), 1, 1) == 0   # > 2^31 rows
     big = D(1, 2, 8200, 128)
     g = lambda **kw: lib.sparse_attn_gather_ws(
         kw.get("Q", A), A, A, kw.get("idx", A), kw.get("k", 64), kw.get("d", big),
