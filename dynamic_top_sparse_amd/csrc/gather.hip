@@ -142,19 +142,29 @@ __global__ __launch_bounds__(kThreads) void gather_row_check_kernel(
   for (int r = 0; r <= R; ++r) below[r] = 0;
   bool ok = true;               // wave-uniform after the ballots
   int last = -1;                // previous chunk's last entry
-  for (int t0 = 0; t0 < k; t0 += kWave) {
-    const int t = t0 + l;
-    const int j = t < k ? ir[t] : -1;
-    const bool valid = j >= 0 && j < N;
-    int prev = __shfl_up(j, 1, kWave);
-    if (l == 0) prev = last;
-    const bool prev_valid = prev >= 0 && prev < N;
-    const bool bad = j >= N || (valid && ((t > 0 && !prev_valid) || (prev_valid && prev > j)));
-    if (__ballot(bad)) ok = false;
+  constexpr int kChunks = 4;    // 64-entry chunks loaded before any is checked
+  for (int c0 = 0; c0 < k; c0 += kChunks * kWave) {
+    int jc[kChunks];
 #pragma unroll
-    for (int r = 1; r < R; ++r) below[r] += valid && j < gr.b[r] ? 1 : 0;
-    below[R] += valid ? 1 : 0;
-    last = __shfl(j, kWave - 1, kWave);
+    for (int c = 0; c < kChunks; ++c) {
+      const int t = c0 + c * kWave + l;
+      jc[c] = t < k ? ir[t] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) {
+      const int t = c0 + c * kWave + l;
+      const int j = jc[c];
+      const bool valid = j >= 0 && j < N;
+      int prev = __shfl_up(j, 1, kWave);
+      if (l == 0) prev = last;
+      const bool prev_valid = prev >= 0 && prev < N;
+      const bool bad = j >= N || (valid && ((t > 0 && !prev_valid) || (prev_valid && prev > j)));
+      if (__ballot(bad)) ok = false;
+#pragma unroll
+      for (int r = 1; r < R; ++r) below[r] += valid && j < gr.b[r] ? 1 : 0;
+      below[R] += valid ? 1 : 0;
+      last = __shfl(j, kWave - 1, kWave);
+    }
   }
   int* out = seg + row * (R + 1);
   if (!ok) {
