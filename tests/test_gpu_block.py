@@ -30,6 +30,7 @@ def _blocks_of_row(row, block):
     (3001, 128, 64, "bf16", 64, 4, True),
     (2000, 64, 32, "bf16", 16, 32, True),       # kb at its maximum
     (700, 64, 16, "f32", 128, 8, False),        # every block kept
+    (9000, 128, 64, "bf16", 64, 4, True),       # past 8192: the gather takes the rows by key range
 ])
 def test_block_selection_all_rows(N, D, dp, dtype, block, kb, causal):
     w = W.Workload("blk", 1, 2, N, D, dtype, d_proj=dp, k=kb * block, causal=causal)
