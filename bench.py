@@ -49,13 +49,15 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 # a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
 # kernel's sources (KERNEL_SOURCE) when the counters were taken.
 TRAFFIC = {
-    # profiles/headline_128k_hbm_traffic.md; the filter's is its main launch (32 heads),
-    # the re-rank's its main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 105.425e9, "write_bytes": 93.499e9,
+    # profiles/headline_128k_hbm_traffic.md (bytes) and headline_128k_l2_hits.md (the
+    # gather's L2 hit rate); the filter's is its main launch (32 heads), the re-rank's its
+    # main launch (32 heads), the gather's its partial kernel (one head)
+    "filter": {"fetch_bytes": 126.393e9, "write_bytes": 93.578e9,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
-    "gather": {"fetch_bytes": 11.026e9, "write_bytes": 0.570e9,
-               "src": "a8410071c224903294910896dfb418e6baff825cb3d755cebd9383437b3678c7"},
-    "rerank": {"fetch_bytes": 69.487e9, "write_bytes": 10.889e9,
+    "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
+               "l2_hit_rate": 0.694,
+               "src": "8a355d22095f1654e3d0e31bfc059e39ac9b18035a508f7a5dc1364d545dd810"},
+    "rerank": {"fetch_bytes": 69.481e9, "write_bytes": 10.889e9,
                "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
 }
 # the sources each kernel's code comes from (their sha256, concatenated in
@@ -70,8 +72,8 @@ KERNEL_SOURCE = {"filter": ["scorer.hip"], "gather": ["gather.hip", "rows.h"],
 # XCD over the dispatch's duration.
 MFMA_COUNTERS: dict = {
     "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
-               "GRBM_GUI_ACTIVE_all_xcds": 1348118725, "dispatch_ms": 93.21,
-               "mfma_busy_frac": 0.3982, "shader_clock_ghz": 1.808,
+               "GRBM_GUI_ACTIVE_all_xcds": 1320081496, "dispatch_ms": 96.45,
+               "mfma_busy_frac": 0.4067, "shader_clock_ghz": 1.711,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
 }
 
@@ -125,6 +127,15 @@ def gather_counter_frac(kern: dict, band: bool):
         return None
     avg_s = d["ms_total"] / d["launches"] / 1e3
     return (tr["fetch_bytes"] + tr["write_bytes"]) / avg_s / 1e9 / PEAK_HBM_GBS
+
+
+def l2_hit_rate(kernel: str):
+    """L2 hit rate of a kernel of the headline forward from the committed
+    rocprofv3 TCC_HIT / TCC_MISS run (null once its source has changed)."""
+    tr = TRAFFIC.get(kernel)
+    if not tr or "l2_hit_rate" not in tr or tr.get("src") != source_sha(kernel):
+        return None
+    return tr["l2_hit_rate"]
 
 
 def filter_mfma_counters():
@@ -459,7 +470,7 @@ def run_op(args, w) -> int:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="headline_128k")
     ap.add_argument("--heads-per-chunk", type=int, default=0,
@@ -474,6 +485,9 @@ def main() -> int:
                          "selection + gather; smooth: top-k with boundary smoothing + gather; "
                          "dilated: dilated wrap-around window + gather")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-filter-steps", type=int, default=5,
+                    help="forward steps timed with the filter's other 16-bit operand type after "
+                         "the main ones (0: none, e.g. for a kernel trace of the main forward)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB: the known-size "
                          "reference that scales rocprofv3 FETCH_SIZE / WRITE_SIZE readings")
@@ -544,10 +558,10 @@ def main() -> int:
     # the same forward with the filter's other 16-bit operand type (the
     # indices do not depend on it), timed the same way over a few steps
     alt_filter = None
-    if not band and args.steps > 0:
+    if not band and args.steps > 0 and args.other_filter_steps > 0:
         adt_name = "bf16" if args.filter_dtype == "f16" else "f16"
         adt = torch.bfloat16 if adt_name == "bf16" else torch.float16
-        n_alt = min(args.steps, 5)
+        n_alt = args.other_filter_steps
         step(fd=adt)
         torch.cuda.synchronize()
         aprof = sa.Profile()
@@ -662,6 +676,8 @@ def main() -> int:
         # that launch's time; null once the gather source has changed since
         # the counters were taken
         "gather_frac_of_hbm_peak": gather_counter_frac(kern, band),
+        # TCC_HIT / (TCC_HIT + TCC_MISS) of the gather's partial kernel
+        "gather_l2_hit_rate": None if band else l2_hit_rate("gather"),
         "gather_stage_ms": t_gather * 1e3,
         "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
                                                                   key=lambda kv: -kv[1])},
