@@ -300,16 +300,17 @@ def run_op(args, w) -> int:
         dO = torch.randn(B, H, N, D, generator=gen).to(w.torch_dtype).cuda()
         _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], k, w.causal,
                                     return_idx=True)
-        n_ws = sa.load_library().sparse_attn_bwd_workspace_size(sa.sa_dims(B, H, N, D), dp, k, 1,
-                                                                None)
+        n_ws = sa.load_library().sparse_attn_bwd_workspace_size(
+            sa.sa_dims(B, H, N, D), dp, k, 1, sa._options(bwd_parts=args.bwd_parts))
         bws = torch.empty(n_ws, dtype=torch.uint8, device="cuda")
         sum_k = float((idx >= 0).sum().item())
 
         def step(p):
             sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], dO, idx, g["Pq"], g["Pk"], workspace=bws,
-                               profile=p)
+                               profile=p, parts=args.bwd_parts)
         units = BH * N
         metric = f"queries/s, top-k sparse attn backward (dQ, dK, dV, dPq, dPk), {w.name}"
+        extra = {"bwd_parts": args.bwd_parts}
         # algorithmic bytes of the two wave passes (per launch: all heads)
         amount = {
             "bwd_rows": sum_k * (2 * D * e) + BH * N * (2 * D * e + 4 * k + 8 * k + 4 * D),
@@ -485,6 +486,9 @@ def main() -> int:
                          "selection + gather; smooth: top-k with boundary smoothing + gather; "
                          "dilated: dilated wrap-around window + gather")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--bwd-parts", choices=("auto", "whole", "split"), default="auto",
+                    help="--op bwd: the row and key passes whole, in key-range parts, or as the "
+                         "library picks (parts from 2^22 row elements per head)")
     ap.add_argument("--other-filter-steps", type=int, default=5,
                     help="forward steps timed with the filter's other 16-bit operand type after "
                          "the main ones (0: none, e.g. for a kernel trace of the main forward)")

@@ -761,9 +761,10 @@ struct BwdPlan {
   int nchunks, slices, split_rows, split_keys;
 };
 // Parts of the backward's passes: automatic picks the key-range split for
-// heads of more than 2^23 row elements (N > 65536 at D = 128: 32 MiB of bf16
-// K and V rows and more), where the whole passes run from the memory-side
-// cache; smaller heads run faster whole (32K at D = 128: 38 against 45 ms).
+// heads of at least 2^22 row elements (N >= 32768 at D = 128: 16 MiB of bf16
+// K and V rows and more), whose rows outgrow an XCD's L2 (measured, bf16 at
+// D = 128: 32 heads of 32K, 38.2 against 38.6 ms whole; 4 x 8 causal heads
+// of 64K, 119 against 128 ms); smaller heads run whole.
 int bwd_parts_of(const sa_options* opts) { return opts != nullptr ? opts->bwd_parts : 0; }
 
 BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer, int parts) {
@@ -781,7 +782,7 @@ BwdPlan bwd_plan(const sa_dims& d, int dp, int k, bool scorer, int parts) {
   p.off_dkl = take(lo);
   p.off_cnt = take(BH * N * 4);
   p.off_off = take(BH * N * 4);
-  const bool big = N * static_cast<size_t>(d.D) > (size_t(1) << 23);
+  const bool big = N * static_cast<size_t>(d.D) >= (size_t(1) << 22);
   p.split_rows = parts == SA_BWD_PARTS_SPLIT || (parts == SA_BWD_PARTS_AUTO && big) ? 1 : 0;
   p.slices = bwd_slices(d.N, k);
   // the key pass takes its parts from whole groups of row slices

@@ -287,6 +287,12 @@ def test_bwd_parts_option_sizes():
     assert size["whole"] > 0 and size["split"] > size["whole"]
     assert size["auto"] == size["whole"]          # a small head runs whole
     assert lib.sparse_attn_bwd_workspace_size(d, 64, 64, 1, None) == size["auto"]
+    # from 2^22 row elements per head (N = 32768 at D = 128) automatic splits
+    big = sa.sa_dims(1, 2, 32768, 128)
+    auto_big = lib.sparse_attn_bwd_workspace_size(big, 64, 256, 1, None)
+    split_big = lib.sparse_attn_bwd_workspace_size(big, 64, 256, 1,
+                                                   ctypes.byref(sa.sa_options(0, None, 2)))
+    assert auto_big == split_big
     bad = sa.sa_options(0, None, 7)
     assert lib.sparse_attn_bwd_workspace_size(d, 64, 64, 1, ctypes.byref(bad)) == 0
     with pytest.raises(ValueError):
