@@ -21,6 +21,7 @@
 //   row chunks, then the chunks' partial sums added in chunk order, so the
 //   result does not depend on scheduling).
 #include <algorithm>
+#include <type_traits>
 
 #include "rows.h"
 
@@ -1109,8 +1110,12 @@ __global__ __launch_bounds__(kThreads) void bwd_rows_split_kernel(
 }
 
 // Key pass, part r: the key's records from rows of slices [r S/8, (r+1) S/8)
-// (consecutive in its segment) give the part's (dV[D], H[D]).
-template <typename T, int D>
+// (consecutive in its segment) give the part's dV[D] and H[D].  kWhich -1
+// forms both at once (an entry's dO and Q rows loaded together); 0 forms dV
+// from the dO rows and 1 forms H from the Q rows, in two launches, so that
+// each XCD's L2 holds one row set of its part at a time instead of both
+// (faster for the largest heads, whose part row sets outgrow the L2).
+template <typename T, int D, int kWhich>
 __global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ dO, const int* __restrict__ seg_off,
     const int* __restrict__ seg_cnt, const int* __restrict__ slice_pre, int S, long long total,
@@ -1149,30 +1154,33 @@ __global__ __launch_bounds__(kThreads) void bwd_keys_split_kernel(
     }
     wave_sync();
     // the rows are those of queries that kept the key: all in [0, N)
-    if constexpr (sizeof(T) == 2) {
-      float t1[EPL], t2[EPL];
+    float t1[EPL], t2[EPL];
+    if constexpr (kWhich < 0 && sizeof(T) == 2) {
       weighted_rows2_bf16<D>(dOh, sp, Qh, sd, sidx, m, N, t1, t2);
+    } else if constexpr (sizeof(T) == 2) {
+      weighted_rows_bf16_split<D>(kWhich == 0 ? dOh : Qh, sidx, m, N, kWhich == 0 ? sp : sd, t1);
+    } else {
+      if constexpr (kWhich <= 0) weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, t1);
+      if constexpr (kWhich != 0) weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, t2);
+    }
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) {
+    for (int e = 0; e < EPL; ++e) {
+      if constexpr (kWhich < 0) {
         av[e] += t1[e];
         ak[e] += t2[e];
+      } else if constexpr (kWhich == 0 || sizeof(T) == 2) {
+        (kWhich == 0 ? av[e] : ak[e]) += t1[e];
+      } else {
+        ak[e] += t2[e];
       }
-    } else {
-      float tmp[EPL];
-      weighted_rows<T, D>(dOh, sidx, 0, m, N, sp, tmp);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) av[e] += tmp[e];
-      weighted_rows<T, D>(Qh, sidx, 0, m, N, sd, tmp);
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) ak[e] += tmp[e];
     }
     wave_sync();
   }
   const int g = l / LPR, e0 = (l % LPR) * EPL;
   float* pr = part + (key * R + r) * 2 * D;
   if (g == 0) {
-    store_f32_row<EPL>(pr + e0, av, 1.0f);
-    store_f32_row<EPL>(pr + D + e0, ak, 1.0f);
+    if constexpr (kWhich <= 0) store_f32_row<EPL>(pr + e0, av, 1.0f);
+    if constexpr (kWhich != 0) store_f32_row<EPL>(pr + D + e0, ak, 1.0f);
   }
 }
 
@@ -1250,8 +1258,15 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
   e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_rows_split_kernel<T, D>),
                          kWaves * bwd_row_wave_floats(kKMax) * 4, lds_rs);
   if (e != hipSuccess) return e;
-  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D>),
+  static std::atomic<int> lds_k0[kMaxDevices], lds_k1[kMaxDevices];
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D, -1>),
                          kWaves * bwd_key_wave_floats() * 4, lds_ks);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D, 0>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_k0);
+  if (e != hipSuccess) return e;
+  e = set_lds_limit_once(reinterpret_cast<const void*>(&bwd_keys_split_kernel<T, D, 1>),
+                         kWaves * bwd_key_wave_floats() * 4, lds_k1);
   if (e != hipSuccess) return e;
   int* err = nullptr;
   e = index_error_flag(&err);
@@ -1276,10 +1291,23 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
                        static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
                        a.seg_cnt, a.rec, a.N, a.k, out_scale, a.dK, a.dV);
   } else {
-    hipLaunchKernelGGL((bwd_keys_split_kernel<T, D>), grid_split, dim3(kThreads), lds_k, s,
-                       static_cast<const T*>(a.Q), static_cast<const T*>(a.dO), a.seg_off,
-                       a.seg_cnt, a.slice_pre, a.slices, static_cast<long long>(a.nh) * a.N,
-                       a.rec, a.N, a.k, a.part);
+    const long long args_total = static_cast<long long>(a.nh) * a.N;
+    auto keys_split = [&](auto which) {
+      hipLaunchKernelGGL((bwd_keys_split_kernel<T, D, decltype(which)::value>), grid_split,
+                         dim3(kThreads), lds_k, s, static_cast<const T*>(a.Q),
+                         static_cast<const T*>(a.dO), a.seg_off, a.seg_cnt, a.slice_pre,
+                         a.slices, args_total, a.rec, a.N, a.k, a.part);
+      return hipGetLastError();
+    };
+    // heads of more than 2^23 row elements (N > 65536 at D = 128): dV and H in
+    // two launches (128K: 87 -> 78 ms), smaller ones in one (32K: 10.2
+    // against 12.5 ms, 64K causal: 36.3 against 39.2 ms)
+    if (static_cast<long long>(a.N) * a.D > (1ll << 23)) {
+      const hipError_t e0 = keys_split(std::integral_constant<int, 0>{});
+      if (e0 != hipSuccess) return e0;
+      return keys_split(std::integral_constant<int, 1>{});
+    }
+    return keys_split(std::integral_constant<int, -1>{});
   }
   return hipGetLastError();
 }
