@@ -167,31 +167,77 @@ __global__ __launch_bounds__(kHistThreads) void bwd_fill_parts_kernel(
   const int lo = bounds[h * (R + 1) + r], hi = bounds[h * (R + 1) + r + 1];
   const int* before = cnt_s + (static_cast<size_t>(s) * nh + h) * N;
   BwdEntry* rh = rec + hk;
-  const int w = threadIdx.x / kWave, l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kWave);
+  const int l = lane_id();
   constexpr int kFillWaves = kHistThreads / kWave;
+  // A wave takes kFillRows rows at once and walks their part segments as one
+  // list, kFillUnroll entries per lane loaded before any is placed: the
+  // segment bounds, the idx entries and the (logit, dp) pairs each cost one
+  // memory round trip per batch of rows instead of one per row.
+  constexpr int kFillRows = 4, kFillUnroll = 4;
   for (int w0 = lo; w0 < hi; w0 += kHistWindow) {
     const int W = min(kHistWindow, hi - w0);
     __syncthreads();      // the previous window's cursors are no longer used
     for (int t = threadIdx.x; t < W; t += kHistThreads) cur[t] = off[hN + w0 + t] + before[w0 + t];
     __syncthreads();
     const unsigned uw0 = static_cast<unsigned>(w0), uW = static_cast<unsigned>(W);
-    for (int i = i0 + w; i < i1; i += kFillWaves) {
-      const size_t row = hN + i;
-      const int* sg = row_seg + row * (R + 1);
-      const bool sorted = sg[0] >= 0;
-      const int t0 = sorted ? sg[r] : 0, t1 = sorted ? sg[r + 1] : k;
-      const float4 st = stats[row];
-      for (int t = t0 + l; t < t1; t += kWave) {
-        const long long g = static_cast<long long>(row) * k + t;
-        const int j = idx[g];
-        const unsigned u = static_cast<unsigned>(j) - uw0;
-        if (u < uW) {
-          const float2 ld = lpd[g];
-          BwdEntry e;
-          e.e = static_cast<int>(g - hk);
-          e.p = ld.x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ld.x - st.x) * st.y;
-          e.dl = e.p != 0.0f ? e.p * (ld.y - st.z) : 0.0f;
-          rh[atomicAdd(&cur[u], 1)] = e;
+    for (int ib = i0 + w * kFillRows; ib < i1; ib += kFillWaves * kFillRows) {
+      int beg[kFillRows], cum[kFillRows + 1];
+      float4 st[kFillRows];
+      cum[0] = 0;
+#pragma unroll
+      for (int b = 0; b < kFillRows; ++b) {
+        const int i = ib + b;
+        int t0 = 0, t1 = 0;
+        st[b] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        if (i < i1) {
+          const int* sg = row_seg + (hN + i) * (R + 1);
+          const bool sorted = sg[0] >= 0;
+          t0 = sorted ? sg[r] : 0;
+          t1 = sorted ? sg[r + 1] : k;
+          st[b] = stats[hN + i];
+        }
+        beg[b] = t0;
+        cum[b + 1] = cum[b] + (t1 - t0);
+      }
+      const int tot = cum[kFillRows];
+      for (int e0 = 0; e0 < tot; e0 += kWave * kFillUnroll) {
+        long long g[kFillUnroll];
+        int j[kFillUnroll], bsel[kFillUnroll];
+#pragma unroll
+        for (int u = 0; u < kFillUnroll; ++u) {
+          const int e = e0 + u * kWave + l;
+          int b = 0;
+#pragma unroll
+          for (int c = 1; c < kFillRows; ++c) b += e >= cum[c] ? 1 : 0;
+          int t = e, row_beg = 0;
+#pragma unroll
+          for (int c = 0; c < kFillRows; ++c)
+            if (b == c) { t = beg[c] + e - cum[c]; row_beg = ib + c; }
+          bsel[u] = b;
+          g[u] = (static_cast<long long>(hN) + row_beg) * k + t;
+          j[u] = e < tot ? idx[g[u]] : -1;
+        }
+        float2 ld[kFillUnroll];
+#pragma unroll
+        for (int u = 0; u < kFillUnroll; ++u) {
+          ld[u] = make_float2(-INFINITY, 0.0f);
+          if (static_cast<unsigned>(j[u]) - uw0 < uW) ld[u] = lpd[g[u]];
+        }
+#pragma unroll
+        for (int u = 0; u < kFillUnroll; ++u) {
+          const unsigned uu = static_cast<unsigned>(j[u]) - uw0;
+          if (uu < uW) {
+            float4 sb = st[0];
+#pragma unroll
+            for (int c = 1; c < kFillRows; ++c)
+              if (bsel[u] == c) sb = st[c];
+            BwdEntry e;
+            e.e = static_cast<int>(g[u] - hk);
+            e.p = ld[u].x == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(ld[u].x - sb.x) * sb.y;
+            e.dl = e.p != 0.0f ? e.p * (ld[u].y - sb.z) : 0.0f;
+            rh[atomicAdd(&cur[uu], 1)] = e;
+          }
         }
       }
     }
