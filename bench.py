@@ -315,10 +315,15 @@ def run_op(args, w) -> int:
         amount = {
             "bwd_rows": sum_k * (2 * D * e) + BH * N * (2 * D * e + 4 * k + 8 * k + 4 * D),
             "bwd_keys": sum_k * (12 + 2 * D * e) + BH * N * (8 * D + 8),
+            # the largest heads take the key pass in two launches, dV then H
+            "bwd_keys_dv": sum_k * (12 + D * e) + BH * N * (4 * D + 4),
+            "bwd_keys_h": sum_k * (12 + D * e) + BH * N * (4 * D + 4),
             "bwd_fill": float(BH * N * k * (4 + 8) + sum_k * 12),
         }
         desc = {"bwd_rows": "K, V rows of kept keys + q, dO, idx rows + (p, dl) + dQ",
                 "bwd_keys": "records + Q, dO rows of the rows that kept each key + dK, dV",
+                "bwd_keys_dv": "records + dO rows of the rows that kept each key + dV",
+                "bwd_keys_h": "records + Q rows of the rows that kept each key + dK",
                 "bwd_fill": "idx + (p, dl) read, 12-byte records written"}
         idx_np = idx.cpu().numpy()
         # the head's rows as the oracle takes them, converted once outside the timing

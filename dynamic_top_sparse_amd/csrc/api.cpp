@@ -890,7 +890,15 @@ int sparse_attn_bwd(const void* Q, const void* K, const void* V, const void* Pq,
     SA_TIMED_STATUS("bwd_fill", launch_bwd_fill(idx, a.epd, a.stats, a.nh, d.N, k, p.slices, cnts,
                                                 offs, rec, s));
   a.pass = 1;
-  SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
+  if (p.split_keys && bwd_keys_two_launches(d.N, d.D)) {
+    a.keys_which = 0;
+    SA_TIMED_STATUS("bwd_keys_dv", launch_bwd_pass(a, s));
+    a.keys_which = 1;
+    SA_TIMED_STATUS("bwd_keys_h", launch_bwd_pass(a, s));
+  } else {
+    a.keys_which = -1;
+    SA_TIMED_STATUS("bwd_keys", launch_bwd_pass(a, s));
+  }
   if (p.split_keys)
     SA_TIMED_STATUS("bwd_keys_merge", launch_bwd_keys_merge(a.part, a.nh, d.N, d.D,
                                                            scorer ? 1.0f : softmax_scale, dK, dV,

@@ -1345,14 +1345,8 @@ hipError_t bwd_passes_t(const BwdArgs& a, hipStream_t s) {
                          a.slices, args_total, a.rec, a.N, a.k, a.part);
       return hipGetLastError();
     };
-    // heads of more than 2^23 row elements (N > 65536 at D = 128): dV and H in
-    // two launches (128K: 87 -> 78 ms), smaller ones in one (32K: 10.2
-    // against 12.5 ms, 64K causal: 36.3 against 39.2 ms)
-    if (static_cast<long long>(a.N) * a.D > (1ll << 23)) {
-      const hipError_t e0 = keys_split(std::integral_constant<int, 0>{});
-      if (e0 != hipSuccess) return e0;
-      return keys_split(std::integral_constant<int, 1>{});
-    }
+    if (a.keys_which == 0) return keys_split(std::integral_constant<int, 0>{});
+    if (a.keys_which == 1) return keys_split(std::integral_constant<int, 1>{});
     return keys_split(std::integral_constant<int, -1>{});
   }
   return hipGetLastError();
@@ -1505,6 +1499,13 @@ hipError_t launch_outer_sum(const void* X, int dtype, const float* lo, long long
   hipLaunchKernelGGL(outer_reduce_kernel, dim3((n + kThreads - 1) / kThreads), dim3(kThreads), 0,
                      s, partial, nchunks, n, dP);
   return hipGetLastError();
+}
+
+// Heads of more than 2^23 row elements (N > 65536 at D = 128) take dV and H
+// in two launches (128K: 87 -> 78 ms for the pair), smaller ones in one (32K:
+// 10.2 against 12.5 ms, 64K causal: 36.3 against 39.2 ms).
+bool bwd_keys_two_launches(int N, int D) {
+  return static_cast<long long>(N) * D > (1ll << 23);
 }
 
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s) {

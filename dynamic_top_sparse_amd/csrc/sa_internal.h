@@ -264,8 +264,13 @@ struct BwdArgs {
   const int* bounds;            // per head: part key bounds (kGatherRanges + 1)
   const int* slice_pre;         // per slice and key: entries of the earlier slices
   float* part;                  // the parts' records
+  // split key pass: -1 sums dV and H in one launch; 0 only dV (dO rows),
+  // 1 only H (Q rows), for heads large enough that two launches are faster
+  int keys_which;
 };
 hipError_t launch_bwd_pass(const BwdArgs& a, hipStream_t s);
+// Whether the split key pass runs as two launches (dV, then H).
+bool bwd_keys_two_launches(int N, int D);
 // Device address of the sticky out-of-range index flag (gather.hip) on the
 // current device.
 hipError_t index_error_flag(int** out);

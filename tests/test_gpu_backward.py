@@ -147,3 +147,74 @@ def test_backward_split_path_list_semantics(N, k, H):
     assert torch.all(got[0][0, 0, 11] == 0)
     assert sa.sparse_attn_check_status() == 0
 
+
+
+def test_backward_two_launch_key_pass_every_element():
+    """A head of more than 2^23 row elements (N = 65600, D = 128) takes the
+    key pass in two launches, dV from the dO rows, then H from the Q rows;
+    sorted rows, descending rows, -1 inside and at the end of rows, every
+    element against the oracle."""
+    B, H, N, D, k = 1, 1, 65600, 128, 16
+    gen = torch.Generator().manual_seed(65600)
+    Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen, dtype=torch.float32) for _ in range(4))
+    idx = torch.randint(0, N, (B, H, N, k), generator=gen, dtype=torch.int32)
+    idx, _ = torch.sort(idx, dim=-1)
+    idx[0, 0, 1::5] = idx[0, 0, 1::5].flip(-1)
+    idx[0, 0, 3::7, k // 2] = -1
+    idx[0, 0, 2::9, k - 2:] = -1
+    got = sa.sparse_attn_bwd(Q.cuda(), K.cuda(), V.cuda(), dO.cuda(), idx.cuda(),
+                             scorer_grad=False)
+    want = O.sparse_attn_backward(Q, K, V, np.zeros((D, 16)), np.zeros((D, 16)), idx.numpy(),
+                                  dO, 1.0, D ** -0.5, scorer_grad=False)
+    for name, a, b in zip(("dQ", "dK", "dV"), got, want[:3]):
+        _close(_np(a), b, 1e-5, name)
+    assert sa.sparse_attn_check_status() == 0
+
+
+def test_backward_full_size_headline_128k_sampled():
+    """The 128K headline sizes (32 heads, N = 131072, D = 128, k = 512, bf16)
+    through the fused forward's index sets, in the launch setup the benchmark
+    times (key-range parts, the key pass in two launches): every element
+    against the whole-row passes (one wave per query and per key, no parts);
+    per head, the dV rows sum to the dO rows; sampled dQ rows and sampled
+    keys' dK, dV rows of two heads against the oracle."""
+    w = W.get("headline_128k")
+    x = W.make_inputs(w, 0)
+    gen = torch.Generator().manual_seed(3)
+    dO = torch.randn(w.B, w.H, w.N, w.D, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+    g = {n: t.cuda() for n, t in x.items()}
+    gdO = dO.cuda()
+    _, idx = sa.sparse_attn_fwd(g["Q"], g["K"], g["V"], g["Pq"], g["Pk"], w.k, return_idx=True)
+    dQ, dK, dV = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], gdO, idx, scorer_grad=False)
+    print("parts backward done", flush=True)
+    whole = sa.sparse_attn_bwd(g["Q"], g["K"], g["V"], gdO, idx, scorer_grad=False,
+                               parts="whole")
+    for name, a, b in (("dQ", dQ, whole[0]), ("dK", dK, whole[1]), ("dV", dV, whole[2])):
+        err = (a - b).abs().max().item()
+        ref = max(1.0, b.abs().max().item())
+        assert err <= 1e-5 * ref, ("whole", name, err, ref)
+    del whole
+    torch.cuda.synchronize()
+    dVs = dV.double().sum(dim=2).cpu().numpy()
+    dOs = dO.double().sum(dim=2).numpy()
+    assert np.abs(dVs - dOs).max() <= 1e-5 * w.N, np.abs(dVs - dOs).max()
+    ascale = w.D ** -0.5
+    rng = np.random.default_rng(1)
+    for h in (0, w.H - 1):
+        Qh, Kh, Vh, dOh = (O.f64(t[0, h]) for t in (x["Q"], x["K"], x["V"], dO))
+        idx_h = _np(idx[0, h]).astype(np.int64)
+        for i in rng.choice(w.N, 16, replace=False):
+            dq, _, _, _ = O.attend_row_backward(Qh[i], Kh, Vh, idx_h[i], ascale, dOh[i])
+            _close(_np(dQ[0, h, i]), dq, 1e-5, "dQ")
+        for j in rng.choice(w.N, 3, replace=False):
+            rows, ts = np.nonzero(idx_h == j)
+            dk = np.zeros(w.D)
+            dv = np.zeros(w.D)
+            for i, t in zip(rows, ts):
+                _, dKr, dVr, _ = O.attend_row_backward(Qh[i], Kh, Vh, idx_h[i], ascale, dOh[i])
+                dk += dKr[t]
+                dv += dVr[t]
+            _close(_np(dK[0, h, j]), dk, 1e-5, "dK")
+            _close(_np(dV[0, h, j]), dv, 1e-5, "dV")
+        print(f"head {h}: sampled rows and keys match the oracle", flush=True)
+    assert sa.sparse_attn_check_status() == 0
