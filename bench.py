@@ -47,7 +47,10 @@ PEAK_FP32_TFLOPS = 157.3      # MI355X fp32 vector
 # rocprofv3 --pmc readings of the headline command (see profiles/), per launch
 # of the kernel, already scaled by the plain-copy factors (FETCH_SIZE reads half
 # a known copy's bytes, WRITE_SIZE all of them).  "src" is the sha256 of the
-# kernel's sources (KERNEL_SOURCE) when the counters were taken.
+# kernel's sources (KERNEL_SOURCE) when the counters were taken.  They hold
+# for that command only: the headline workload, fp16 filter operands, all 32
+# heads in one selection launch (COUNTER_RUN); other runs report null.
+COUNTER_RUN = {"workload": "headline_128k", "filter_dtype": "f16", "heads_per_launch": 32}
 TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md (bytes) and headline_128k_l2_hits.md (the
     # gather's L2 hit rate); the filter's is its main launch (32 heads), the re-rank's its
@@ -116,13 +119,19 @@ def algorithmic(w) -> dict:
     }
 
 
-def gather_counter_frac(kern: dict, band: bool):
+def counters_apply(workload: str, filter_dtype: str, heads_per_launch) -> bool:
+    """Whether this run is the command the committed counters were taken on."""
+    return (workload == COUNTER_RUN["workload"] and filter_dtype == COUNTER_RUN["filter_dtype"]
+            and heads_per_launch == COUNTER_RUN["heads_per_launch"])
+
+
+def gather_counter_frac(kern: dict, band: bool, applies: bool):
     """Counter bytes per launch of the gather's main kernel over its measured
     average launch time, as a fraction of the HBM peak (headline command's
     counters only; null when they do not apply)."""
     tr = TRAFFIC.get("gather")
     d = kern.get("gather")
-    if band or not tr or not d or tr.get("src") != source_sha("gather") or \
+    if band or not applies or not tr or not d or tr.get("src") != source_sha("gather") or \
             "gather_merge" not in kern:
         return None
     avg_s = d["ms_total"] / d["launches"] / 1e3
@@ -643,8 +652,9 @@ def main() -> int:
         roof["algorithmic_per_launch"] = (f"{amount:.4g} B (K,V rows of kept keys + idx + q, "
                                           f"{heads:g} heads)")
     roof["frac"] = roof["achieved"] / roof["peak"]
+    applies = counters_apply(w.name, args.filter_dtype, heads_per_chunk)
     tr = TRAFFIC.get(dom)
-    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if tr and \
+    roof["traffic"] = (tr["fetch_bytes"] + tr["write_bytes"]) if applies and tr and \
         tr.get("src") == source_sha(dom) else None
     roof["avg_launch_ms"] = avg_launch_s * 1e3
 
@@ -684,9 +694,9 @@ def main() -> int:
         # WRITE_SIZE, memory-side-cache hits included) per gather launch, over
         # that launch's time; null once the gather source has changed since
         # the counters were taken
-        "gather_frac_of_hbm_peak": gather_counter_frac(kern, band),
+        "gather_frac_of_hbm_peak": gather_counter_frac(kern, band, applies),
         # TCC_HIT / (TCC_HIT + TCC_MISS) of the gather's partial kernel
-        "gather_l2_hit_rate": None if band else l2_hit_rate("gather"),
+        "gather_l2_hit_rate": l2_hit_rate("gather") if applies and not band else None,
         "gather_stage_ms": t_gather * 1e3,
         "kernel_ms_per_step": {n: round(v, 3) for n, v in sorted(per_step.items(),
                                                                   key=lambda kv: -kv[1])},
@@ -701,7 +711,7 @@ def main() -> int:
             "retried_queries": stats["retried"],
             "margin_violations": stats["margin_violations"],
             "filter_dtype": args.filter_dtype}
-        result["filter_mfma_counters"] = filter_mfma_counters()
+        result["filter_mfma_counters"] = filter_mfma_counters() if applies else None
     if alt_filter is not None:
         fl = alt_filter["filter_ms_per_launch"]
         if fl and n_filter:

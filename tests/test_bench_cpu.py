@@ -45,3 +45,19 @@ def test_bench_runs_on_one_gpu_only():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_counters_apply_to_their_command_only():
+    """The committed rocprofv3 readings describe the headline command (fp16
+    filter operands, 32 heads per selection launch); any other run must report
+    them as null rather than borrow them."""
+    assert bench.counters_apply("headline_128k", "f16", 32)
+    assert bench.counters_apply("headline_128k", "f16", 32.0)
+    assert not bench.counters_apply("bf16_32k", "f16", 32)
+    assert not bench.counters_apply("causal_mixture", "f16", 32)
+    assert not bench.counters_apply("headline_128k", "bf16", 32)
+    assert not bench.counters_apply("headline_128k", "f16", 16)
+    assert not bench.counters_apply("headline_128k", "f16", None)
+    assert bench.gather_counter_frac({"gather": {"ms_total": 1.0, "launches": 1},
+                                      "gather_merge": {"ms_total": 1.0, "launches": 1}},
+                                     False, False) is None
