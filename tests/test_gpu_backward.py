@@ -149,13 +149,14 @@ def test_backward_split_path_list_semantics(N, k, H):
 
 
 
-def test_backward_two_launch_key_pass_every_element():
-    """A head of more than 2^23 row elements (N = 65600, D = 128) takes the
-    key pass in two launches, dV from the dO rows, then H from the Q rows;
-    sorted rows, descending rows, -1 inside and at the end of rows, every
-    element against the oracle."""
-    B, H, N, D, k = 1, 1, 65600, 128, 16
-    gen = torch.Generator().manual_seed(65600)
+@pytest.mark.parametrize("N,D,k", [(65600, 128, 16), (131200, 64, 8)])
+def test_backward_two_launch_key_pass_every_element(N, D, k):
+    """A head of more than 2^23 row elements (N = 65600 at D = 128, N =
+    131200 at D = 64) takes the key pass in two launches, dV from the dO
+    rows, then H from the Q rows; sorted rows, descending rows, -1 inside and
+    at the end of rows, every element against the oracle."""
+    B, H = 1, 1
+    gen = torch.Generator().manual_seed(N + D)
     Q, K, V, dO = (torch.randn(B, H, N, D, generator=gen, dtype=torch.float32) for _ in range(4))
     idx = torch.randint(0, N, (B, H, N, k), generator=gen, dtype=torch.int32)
     idx, _ = torch.sort(idx, dim=-1)
