@@ -266,7 +266,7 @@ __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
 }
 
 template <int DP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void finalize_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void finalize_kernel(
     const uint2* __restrict__ cand, const int* __restrict__ cnt, const int* __restrict__ rcnt,
     float* __restrict__ tau,
     const float* __restrict__ thr,
@@ -296,7 +296,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const size_t hq = static_cast<size_t>(h) * Npad;
   // Statistics are kept per wave and added to the header once at the end:
   // one device-scope atomic per query on a shared word would serialise.
-  unsigned long long st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
+  // (32-bit, and each updated by plain arithmetic, so that they stay in
+  // registers: a wave takes at most N of one head's queries)
+  unsigned st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
   unsigned viol = 0;   // per lane: re-scored keys outside their margin interval
   // first pass: every query; retry pass: the queries listed for this head
   const int nq = qlist != nullptr ? qlist_count[h] : N;
@@ -375,20 +377,21 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     // (k keys certainly score at least tau_new), filter it again with that
     // threshold; otherwise resolve it with the exact fallback.
     auto unresolved = [&](float tau_new) {
-      if (qlist == nullptr && tau_new == tau_new) {
+      const unsigned again = qlist == nullptr && tau_new == tau_new ? 1u : 0u;
+      st_retried += again;
+      st_queries += 1u - again;
+      if (again) {
         if (l == 0) {
           // lowered by a few ulps: the retry re-derives its filter scores with
           // another threshold, which may round them differently
           tau[hq + q] = tau_new - (fabsf(tau_new) * (1.0f / 1048576.0f) + 1e-30f);
           rlist[hq + atomicAdd(&rcount[h], 1)] = q;
         }
-        ++st_retried;
       } else {
         if (l == 0) {
           const unsigned fslot = atomicAdd(&hdr->fb_count, 1u);
           fblist[fslot] = static_cast<int>(hq + q);
         }
-        ++st_queries;
       }
     };
 
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     const int c0 = min(r0, capH), c1 = min(r1, capH);
     const int c = c0 + c1;
     const float tq = cur.tq;
-    if (overflow && qlist == nullptr) ++st_overflow;
+    st_overflow += overflow && qlist == nullptr ? 1u : 0u;
     // Stage the candidates in LDS once (index i runs over half 0, then half 1)
     // as (order key of the filter score s~ = sum * f, key index).  The
     // filter parked sum - thr (its accumulators start at -thr).
@@ -529,7 +532,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     {
       constexpr int G = DP / 4;
       constexpr int KPI = kWave / G;     // keys per pass
-      constexpr int UNR = 16;            // passes in flight (64 keys at d_proj 64)
+      constexpr int UNR = 8;             // passes in flight (32 keys at d_proj 64)
       const int g = l % G, grp = l / G;
       const float4 qv = reinterpret_cast<const float4*>(q32 + (hq + q) * DP)[g];
       #pragma unroll 1
@@ -599,7 +602,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
           l == kGatherRanges ? run2 : count_below(cj, n0, x) + count_below(cj + n0, run2 - n0, x);
     }
     for (int t = run2 + l; t < k; t += kWave) out[t] = -1;
-    st_rescored += static_cast<unsigned long long>(nU);
+    st_rescored += static_cast<unsigned>(nU);
     ++st_queries;
     } while (false);
     if (!issued) issue_next();
@@ -608,10 +611,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
   const unsigned st_viol = static_cast<unsigned>(wave_sum_i(static_cast<int>(viol)));
   if (l == 0) {
-    if (st_queries) atomicAdd(&hdr->queries, st_queries);
-    if (st_rescored) atomicAdd(&hdr->rescored, st_rescored);
-    if (st_overflow) atomicAdd(&hdr->overflow_queries, st_overflow);
-    if (st_retried) atomicAdd(&hdr->retried, st_retried);
+    if (st_queries) atomicAdd(&hdr->queries, static_cast<unsigned long long>(st_queries));
+    if (st_rescored) atomicAdd(&hdr->rescored, static_cast<unsigned long long>(st_rescored));
+    if (st_overflow)
+      atomicAdd(&hdr->overflow_queries, static_cast<unsigned long long>(st_overflow));
+    if (st_retried) atomicAdd(&hdr->retried, static_cast<unsigned long long>(st_retried));
     if (st_viol) atomicAdd(&hdr->margin_violations, st_viol);
   }
 }
