@@ -55,13 +55,13 @@ TRAFFIC = {
     # profiles/headline_128k_hbm_traffic.md (bytes) and headline_128k_l2_hits.md (the
     # gather's L2 hit rate); the filter's is its main launch (32 heads), the re-rank's its
     # main launch (32 heads), the gather's its partial kernel (one head)
-    "filter": {"fetch_bytes": 126.393e9, "write_bytes": 93.578e9,
+    "filter": {"fetch_bytes": 122.844e9, "write_bytes": 93.407e9,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
-    "gather": {"fetch_bytes": 11.025e9, "write_bytes": 0.570e9,
+    "gather": {"fetch_bytes": 11.024e9, "write_bytes": 0.570e9,
                "l2_hit_rate": 0.694,
                "src": "8a355d22095f1654e3d0e31bfc059e39ac9b18035a508f7a5dc1364d545dd810"},
-    "rerank": {"fetch_bytes": 69.481e9, "write_bytes": 10.889e9,
-               "src": "7ef4fb41a1b72a502e803dec62d1989d0ac8ba61449ac97f87bf54e14bfd4a4b"},
+    "rerank": {"fetch_bytes": 67.440e9, "write_bytes": 8.751e9,
+               "src": "0e62a907b2a000c45cd5385a8d1dea329a74be874efc050c39b7d9cfb94959da"},
 }
 # the sources each kernel's code comes from (their sha256, concatenated in
 # this order, is recorded with the counters)
@@ -75,8 +75,8 @@ KERNEL_SOURCE = {"filter": ["scorer.hip"], "gather": ["gather.hip", "rows.h"],
 # XCD over the dispatch's duration.
 MFMA_COUNTERS: dict = {
     "filter": {"SQ_INSTS_MFMA": 2147483648, "SQ_VALU_MFMA_BUSY_CYCLES": 68719476736,
-               "GRBM_GUI_ACTIVE_all_xcds": 1320081496, "dispatch_ms": 96.45,
-               "mfma_busy_frac": 0.4067, "shader_clock_ghz": 1.711,
+               "GRBM_GUI_ACTIVE_all_xcds": 1313034725, "dispatch_ms": 92.09,
+               "mfma_busy_frac": 0.4089, "shader_clock_ghz": 1.782,
                "src": "3021e687f2adad69fa230cd6b911cb844de524181d9058865db90509957ce0af"},
 }
 
