@@ -266,7 +266,7 @@ __device__ __forceinline__ void write_selected(int n, uint32_t T, int ties, KeyA
       eq_before += i < wv ? c : 0;
       eq_tile += c;
     }
-    const bool sel = gt || (eq && eq_before + __popcll(me & below) < ties);
+    const bool sel = gt || (eq && eq_before + static_cast<int>(__popcll(me & below)) < ties);
     const unsigned long long ms = __ballot(sel);
     if (lane == 0) wcnt[wv][1] = __popcll(ms);
     __syncthreads();
