@@ -710,6 +710,7 @@ def main() -> int:
             "overflow_queries": stats["overflow_queries"],
             "retried_queries": stats["retried"],
             "margin_violations": stats["margin_violations"],
+            "rerank_queries_from_memory": stats.get("wide_queries"),
             "filter_dtype": args.filter_dtype}
         result["filter_mfma_counters"] = filter_mfma_counters() if applies else None
     if alt_filter is not None:

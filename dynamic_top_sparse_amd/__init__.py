@@ -742,7 +742,7 @@ def sparse_attn_check_status(stream: Optional[int] = None) -> int:
 
 
 STAT_KEYS = ("fallback_queries", "overflow_queries", "candidates", "rescored", "queries",
-             "retried", "margin_violations")
+             "retried", "margin_violations", "wide_queries")
 
 
 def sparse_attn_workspace_stats(workspace: torch.Tensor) -> dict:

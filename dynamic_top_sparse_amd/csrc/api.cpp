@@ -1005,12 +1005,13 @@ int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, i
   if (hipMemcpyAsync(&h, ws, sizeof(h), hipMemcpyDeviceToHost, s) != hipSuccess)
     return SA_ERR_HIP;
   if (hipStreamSynchronize(s) != hipSuccess) return SA_ERR_HIP;
-  const int64_t vals[7] = {static_cast<int64_t>(h.fallback_queries),
+  const int64_t vals[8] = {static_cast<int64_t>(h.fallback_queries),
                            static_cast<int64_t>(h.overflow_queries),
                            static_cast<int64_t>(h.candidates), static_cast<int64_t>(h.rescored),
                            static_cast<int64_t>(h.queries), static_cast<int64_t>(h.retried),
-                           static_cast<int64_t>(h.margin_violations)};
-  const int m = n < 7 ? n : 7;
+                           static_cast<int64_t>(h.margin_violations),
+                           static_cast<int64_t>(h.wide_queries)};
+  const int m = n < 8 ? n : 8;
   for (int i = 0; i < m; ++i) out[i] = vals[i];
   return m;
 }

@@ -257,12 +257,42 @@ __device__ __forceinline__ unsigned long long rank_key(float s, int j) {
 }
 
 // Per-wave LDS of the re-rank: histogram (1 KB), rank buffer (512 B), the
-// uncertain keys with their exact and filter scores (ucap x 12 B), and the
-// candidates (cap x 8 B: order key of the filter score, key index), whose key
-// array becomes the output row in place.
+// uncertain keys with their exact and filter scores (ucap x 12 B), and room
+// for lcap candidates (8 B each: order key of the filter score, key index),
+// whose key array becomes the output row in place.  A query with more than
+// lcap candidates is ranked from its lists in global memory instead, and only
+// the keys that can still be kept (fewer than k + ucap) reach LDS.
 __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
   return (1024 + 512 + static_cast<size_t>(ucap) * 12 + static_cast<size_t>(cap) * 8 + 15) /
          16 * 16;
+}
+
+// Waves of the re-rank one CU holds for a per-wave LDS size (workgroups of
+// up to four waves within 64 KB, 160 KB per CU, four waves per SIMD at most).
+inline int rerank_waves_per_cu(size_t per_wave) {
+  int wpb = static_cast<int>((64 * 1024) / per_wave);
+  wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
+  const int per_cu = static_cast<int>(163840 / (static_cast<size_t>(wpb) * per_wave));
+  return per_cu * wpb < 16 ? per_cu * wpb : 16;
+}
+
+// LDS candidate room of a re-rank wave: the whole list capacity (2 capH)
+// unless a smaller room, still at least k + ucap, lets more waves share a CU
+// (queries with more candidates then take the path over memory).
+inline int rerank_lds_cap(int capH, int k, int ucap) {
+  const int full = 2 * capH;
+  int best = full, best_waves = rerank_waves_per_cu(rerank_lds_per_wave(full, ucap));
+  for (int lc = full - 64; lc >= k + ucap && lc > 0; lc -= 64) {
+    const int wv = rerank_waves_per_cu(rerank_lds_per_wave(lc, ucap));
+    if (wv > best_waves) {
+      best = lc;
+      best_waves = wv;
+    }
+  }
+  // the largest room that keeps that many waves
+  for (int lc = best + 64; lc < full; lc += 64)
+    if (rerank_waves_per_cu(rerank_lds_per_wave(lc, ucap)) == best_waves) best = lc;
+  return best;
 }
 
 template <int DP>
@@ -272,7 +302,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float* __restrict__ thr,
     const float4* __restrict__ qstat, const uint32_t* __restrict__ kstat,
     const float* __restrict__ q32, const float* __restrict__ k32, int N, int Npad, int k,
-    int causal, int capH, int ucap, float scale, int32_t* __restrict__ idx,
+    int causal, int capH, int lcap, int ucap, float scale, int32_t* __restrict__ idx,
     const int* __restrict__ qlist, const int* __restrict__ qlist_count, int* __restrict__ rlist,
     int* __restrict__ rcount, int* __restrict__ fblist, int* __restrict__ seg, GatherRanges gr,
     WsHeader* __restrict__ hdr) {
@@ -282,15 +312,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // metadata loads and list addresses, are then wave-uniform scalar values
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int l = lane_id();
-  const int cap = 2 * capH;
-  unsigned char* base = smem + static_cast<size_t>(w) * rerank_lds_per_wave(cap, ucap);
+  unsigned char* base = smem + static_cast<size_t>(w) * rerank_lds_per_wave(lcap, ucap);
   int* hist = reinterpret_cast<int*>(base);
   unsigned long long* cbuf = reinterpret_cast<unsigned long long*>(base + 1024);
   int* uj = reinterpret_cast<int*>(base + 1536);
   float* us = reinterpret_cast<float*>(base + 1536 + ucap * 4);
   float* ut = reinterpret_cast<float*>(base + 1536 + ucap * 8);
   uint32_t* ck = reinterpret_cast<uint32_t*>(base + 1536 + ucap * 12);
-  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 12 + cap * 4);
+  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 12 + lcap * 4);
 
   const int h = blockIdx.y;
   const size_t hq = static_cast<size_t>(h) * Npad;
@@ -300,6 +329,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   // registers: a wave takes at most N of one head's queries)
   unsigned st_queries = 0, st_rescored = 0, st_overflow = 0, st_retried = 0;
   unsigned viol = 0;   // per lane: re-scored keys outside their margin interval
+  unsigned st_wide = 0;
   // first pass: every query; retry pass: the queries listed for this head
   const int nq = qlist != nullptr ? qlist_count[h] : N;
   // Software pipeline over the wave's queries: while query i is ranked, the
@@ -408,6 +438,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const bool overflow = r0 > capH || r1 > capH;
     const int c0 = min(r0, capH), c1 = min(r1, capH);
     const int c = c0 + c1;
+    // more candidates than LDS holds: rank them from the lists in memory
+    const bool wide = c > lcap;
+    st_wide += wide ? 1u : 0u;
     const float tq = cur.tq;
     st_overflow += overflow && qlist == nullptr ? 1u : 0u;
     // Stage the candidates in LDS once (index i runs over half 0, then half 1)
@@ -419,11 +452,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     const float f = scale * st.z * kinv;
     const float tv = cur.tv;
     uint32_t kmin = ~0u, kmax = 0u;
+    const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
+    const uint2* list1 = list0 + capH;
     {
       auto stage = [&](int i, uint2 e) {
         const uint32_t key = order_key((__uint_as_float(e.y) + tv) * f);
-        ck[i] = key;
-        cj[i] = candidate_key(e.x);
+        if (!wide) {
+          ck[i] = key;
+          cj[i] = candidate_key(e.x);
+        }
         kmin = min(kmin, key);
         kmax = max(kmax, key);
       };
@@ -433,8 +470,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         if (i < c) stage(i, pre[j]);
       }
       issue_next();
-      const uint2* list0 = cand + (hq + q) * 2 * static_cast<size_t>(capH);
-      const uint2* list1 = list0 + capH;
       #pragma unroll 16
       for (int i = kWave * kPrefetch + l; i < c; i += kWave)
         stage(i, i < c0 ? list0[i] : list1[i - c0]);
@@ -460,12 +495,34 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       unresolved(guess);
       continue;
     }
+    // entry i of the lists in memory (wide queries), four per lane in flight
+    constexpr int WB = 4;
+    auto glob_entries = [&](int i0, uint2 (&e)[WB]) {
+#pragma unroll
+      for (int t = 0; t < WB; ++t) {
+        const int i = min(i0 + t * kWave + l, c - 1);
+        e[t] = i < c0 ? list0[i] : list1[i - c0];
+      }
+    };
     auto each_cand = [&](auto fn) {
-      #pragma unroll 1
-      for (int i0 = 0; i0 < c; i0 += kWave) {
-        const int i = i0 + l;
-        const bool ok = i < c;
-        fn(ok ? ck[i] : 0u, ok);
+      if (!wide) {
+        #pragma unroll 1
+        for (int i0 = 0; i0 < c; i0 += kWave) {
+          const int i = i0 + l;
+          const bool ok = i < c;
+          fn(ok ? ck[i] : 0u, ok);
+        }
+      } else {
+        #pragma unroll 1
+        for (int i0 = 0; i0 < c; i0 += WB * kWave) {
+          uint2 e[WB];
+          glob_entries(i0, e);
+#pragma unroll
+          for (int t = 0; t < WB; ++t) {
+            const bool ok = i0 + t * kWave + l < c;
+            fn(ok ? order_key((__uint_as_float(e[t].y) + tv) * f) : 0u, ok);
+          }
+        }
       }
     };
     // The k-th largest filter score gives lo = (k-th) - m, a proven threshold
@@ -499,14 +556,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     // written, and writes never pass the chunk); uncertain ones carry bit 31
     // and are also listed in uj (with their filter score in ut) for the
     // exact re-score.
+    // (A wide query's kept and uncertain keys number under k + ucap <= lcap
+    // while nU <= ucap, since the certainly kept ones score above the k-th;
+    // writes past lcap are dropped and the query then fails the nU test.)
     int run = 0, n0c = 0, nU = 0;
-    #pragma unroll 1
-    for (int i0 = 0; i0 < c; i0 += kWave) {
-      const int i = i0 + l;
+    auto classify = [&](int i, uint32_t ckey, int key) {
       const bool ok = i < c;
-      const uint32_t ckey = ok ? ck[i] : 0u;
       const int cc = ok ? cls_of(ckey) : 0;
-      const int key = ok ? cj[i] : 0;
       const unsigned long long mu = __ballot(cc == 2);
       const unsigned long long mk = __ballot(cc != 0);
       if (cc == 2) {
@@ -517,13 +573,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
         }
       }
       wave_sync();
-      if (cc != 0) cj[run + lane_rank(mk)] = cc == 2 ? (key | INT_MIN) : key;
+      const int pos = run + lane_rank(mk);
+      if (cc != 0 && pos < lcap) cj[pos] = cc == 2 ? (key | INT_MIN) : key;
       nU += __builtin_popcountll(mu);
       run += __builtin_popcountll(mk);
       n0c += __builtin_popcountll(__ballot(cc != 0 && i < c0));
+    };
+    if (!wide) {
+      #pragma unroll 1
+      for (int i0 = 0; i0 < c; i0 += kWave) {
+        const int i = i0 + l;
+        const bool ok = i < c;
+        classify(i, ok ? ck[i] : 0u, ok ? cj[i] : 0);
+      }
+    } else {
+      #pragma unroll 1
+      for (int i0 = 0; i0 < c; i0 += WB * kWave) {
+        uint2 e[WB];
+        glob_entries(i0, e);
+#pragma unroll
+        for (int t = 0; t < WB; ++t)
+          classify(i0 + t * kWave + l, order_key((__uint_as_float(e[t].y) + tv) * f),
+                   candidate_key(e[t].x));
+      }
     }
     const int need = k_i - (run - nU);
-    if (nU > ucap || need > nU) {
+    if (nU > ucap || need > nU || run > lcap) {
       unresolved(__builtin_nanf(""));
       continue;
     }
@@ -617,6 +692,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       atomicAdd(&hdr->overflow_queries, static_cast<unsigned long long>(st_overflow));
     if (st_retried) atomicAdd(&hdr->retried, static_cast<unsigned long long>(st_retried));
     if (st_viol) atomicAdd(&hdr->margin_violations, st_viol);
+    if (st_wide) atomicAdd(&hdr->wide_queries, st_wide);
   }
 }
 
@@ -748,7 +824,8 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   // the uncertain band is ~8x narrower with fp16 filter operands than bf16
   // (about 37 and 280 keys at the headline size)
   const int ucap = p.filt ? 512 : 128;
-  const size_t per_wave = rerank_lds_per_wave(2 * p.capH, ucap);
+  const int lcap = rerank_lds_cap(p.capH, p.k, ucap);
+  const size_t per_wave = rerank_lds_per_wave(lcap, ucap);
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
   // persistent waves striding over the queries of their head: as many
@@ -770,7 +847,7 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((finalize_kernel<DP>), grid, dim3(wpb * kWave), lds, s, b.cand, b.cnt, b.rcnt,
                      b.tau, b.thr, b.qstat, b.kstat, b.qlo32, b.klo32, p.N, p.Npad, p.k, p.causal,
-                     p.capH, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
+                     p.capH, lcap, ucap, scale, idx, retry ? b.rlist : static_cast<int*>(nullptr),
                      retry ? b.rcount : static_cast<int*>(nullptr), b.rlist, b.rcount, b.fblist,
                      seg, gather_ranges(p.N, p.causal), b.hdr);
   return hipGetLastError();

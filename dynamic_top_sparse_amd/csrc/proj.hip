@@ -234,6 +234,7 @@ __global__ void init_chunk_kernel(WsHeader* hdr, uint32_t* kstat, int* rcount, i
       hdr->queries = 0;
       hdr->retried = 0;
       hdr->margin_violations = 0;
+      hdr->wide_queries = 0;
     }
     hdr->fb_count = 0;
     hdr->fb_next = 0;

@@ -272,7 +272,7 @@ struct WsHeader {
   unsigned int fb_count;                 // queries queued for the fallback
   unsigned int fb_next;                  // fallback work-queue cursor
   unsigned int margin_violations;        // re-scored keys outside [s~ - m, s~ + m]
-  unsigned int pad;
+  unsigned int wide_queries;             // re-ranked from their lists in memory
 };
 static_assert(sizeof(WsHeader) % 16 == 0, "header keeps 16-byte alignment");
 

@@ -410,8 +410,10 @@ int sparse_attn_check_status(void* stream);
  * keys re-scored exactly, [4] queries resolved, [5] queries filtered a second
  * time with a proven threshold, [6] re-scored keys whose exact score fell
  * outside the interval the filter's margin gives for it (0 unless the
- * margin's rounding bound is wrong), summed over all head chunks of the
- * call.  Returns the number of values written or a negative status.
+ * margin's rounding bound is wrong), [7] queries the re-rank ranked from
+ * their candidate lists in memory because they held more candidates than its
+ * LDS room, summed over all head chunks of the call.  Returns the number of
+ * values written or a negative status.
  */
 int sparse_attn_workspace_stats(const void* ws, size_t ws_bytes, int64_t* out, int32_t n,
                                 void* stream);
