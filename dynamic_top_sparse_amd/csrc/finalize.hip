@@ -669,14 +669,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
       n0 += __builtin_popcountll(__ballot(take && i < n0c));
     }
     wave_sync();
-    merge_rows(cj, n0, cj + n0, run2 - n0, out);
+    // The merged row goes to the order-key area (free by now, at least k
+    // entries), then to out in coalesced stores, -1 past the kept keys.
+    int* mrow = reinterpret_cast<int*>(ck);
+    merge_rows(cj, n0, cj + n0, run2 - n0, mrow);
     // the row's key-range starts: entries below r*L in either list
     if (seg != nullptr && l <= kGatherRanges) {
       const int x = gather_range_start(gr, l);
       seg[(hq + q) * (kGatherRanges + 1) + l] =
           l == kGatherRanges ? run2 : count_below(cj, n0, x) + count_below(cj + n0, run2 - n0, x);
     }
-    for (int t = run2 + l; t < k; t += kWave) out[t] = -1;
+    wave_sync();
+    #pragma unroll 1
+    for (int t = l; t < k; t += kWave) out[t] = t < run2 ? mrow[t] : -1;
     st_rescored += static_cast<unsigned>(nU);
     ++st_queries;
     } while (false);
