@@ -120,7 +120,9 @@ __device__ __forceinline__ int key_bits(KeyT span) {
 // count.  The key range is cut into 256 buckets, the bucket holding the K-th
 // key is kept, and this repeats until at most 64 keys are left; those are
 // ranked directly.  Buckets spread keys that share their leading bits, so the
-// LDS histogram sees few colliding atomics.  Requires 1 <= K <= #valid keys.
+// LDS histogram sees few colliding atomics.  The histogram holds 16-bit
+// counts, two buckets per word (512 B): callers pass fewer than 65536 keys.
+// Requires 1 <= K <= #valid keys.
 template <typename KeyT, typename Each>
 __device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo, KeyT hi) {
   const int l = lane_id();
@@ -129,14 +131,18 @@ __device__ KeyT wave_select_in(int K, int* hist, KeyT* cbuf, Each each, KeyT lo,
     const KeyT span = hi - lo;
     const int nb = key_bits<KeyT>(span);
     const int shift = nb > 8 ? nb - 8 : 0;          // (span >> shift) < 256
-    reinterpret_cast<int4*>(hist)[l] = make_int4(0, 0, 0, 0);   // 256 bins, 4 per lane
+    reinterpret_cast<int2*>(hist)[l] = make_int2(0, 0);   // 256 bins, 4 per lane
     wave_sync();
     each([&](KeyT key, bool ok) {
-      if (ok && key >= lo && key <= hi) atomicAdd(&hist[static_cast<int>((key - lo) >> shift)], 1);
+      if (ok && key >= lo && key <= hi) {
+        const int b = static_cast<int>((key - lo) >> shift);
+        atomicAdd(&hist[b >> 1], 1 << ((b & 1) << 4));
+      }
     });
     wave_sync();
-    const int4 h4 = reinterpret_cast<const int4*>(hist)[63 - l];   // lane L: bins 255-4L ..
-    const int c[4] = {h4.w, h4.z, h4.y, h4.x};
+    const int2 h2 = reinterpret_cast<const int2*>(hist)[63 - l];   // lane L: bins 255-4L ..
+    const int c[4] = {static_cast<int>(static_cast<uint32_t>(h2.y) >> 16), h2.y & 0xFFFF,
+                      static_cast<int>(static_cast<uint32_t>(h2.x) >> 16), h2.x & 0xFFFF};
     const int sum = c[0] + c[1] + c[2] + c[3];
     const int incl = wave_incl_scan(sum);
     const unsigned long long crossing = __ballot(incl >= K);
@@ -256,15 +262,16 @@ __device__ __forceinline__ unsigned long long rank_key(float s, int j) {
          static_cast<unsigned long long>(0xFFFFFFFFu - static_cast<uint32_t>(j));
 }
 
-// Per-wave LDS of the re-rank: histogram (1 KB), rank buffer (512 B), the
-// uncertain keys with their exact and filter scores (ucap x 12 B), and room
+// Per-wave LDS of the re-rank: histogram (512 B), the uncertain keys with
+// their exact and filter scores (ucap x 12 B; ucap >= 128, so the filter
+// scores' 512 B double as the selects' rank buffer, which is never in use
+// while they are), and room
 // for lcap candidates (8 B each: order key of the filter score, key index),
 // whose key array becomes the output row in place.  A query with more than
 // lcap candidates is ranked from its lists in global memory instead, and only
 // the keys that can still be kept (fewer than k + ucap) reach LDS.
 __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
-  return (1024 + 512 + static_cast<size_t>(ucap) * 12 + static_cast<size_t>(cap) * 8 + 15) /
-         16 * 16;
+  return (512 + static_cast<size_t>(ucap) * 12 + static_cast<size_t>(cap) * 8 + 15) / 16 * 16;
 }
 
 // Waves of the re-rank one CU holds for a per-wave LDS size (workgroups of
@@ -314,12 +321,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int l = lane_id();
   unsigned char* base = smem + static_cast<size_t>(w) * rerank_lds_per_wave(lcap, ucap);
   int* hist = reinterpret_cast<int*>(base);
-  unsigned long long* cbuf = reinterpret_cast<unsigned long long*>(base + 1024);
-  int* uj = reinterpret_cast<int*>(base + 1536);
-  float* us = reinterpret_cast<float*>(base + 1536 + ucap * 4);
-  float* ut = reinterpret_cast<float*>(base + 1536 + ucap * 8);
-  uint32_t* ck = reinterpret_cast<uint32_t*>(base + 1536 + ucap * 12);
-  int* cj = reinterpret_cast<int*>(base + 1536 + ucap * 12 + lcap * 4);
+  int* uj = reinterpret_cast<int*>(base + 512);
+  float* us = reinterpret_cast<float*>(base + 512 + ucap * 4);
+  float* ut = reinterpret_cast<float*>(base + 512 + ucap * 8);
+  // rank buffer of the selects (64 keys of 8 B): the filter scores' area,
+  // read only between the classification and the exact re-score
+  unsigned long long* cbuf = reinterpret_cast<unsigned long long*>(ut);
+  uint32_t* ck = reinterpret_cast<uint32_t*>(base + 512 + ucap * 12);
+  int* cj = reinterpret_cast<int*>(base + 512 + ucap * 12 + lcap * 4);
 
   const int h = blockIdx.y;
   const size_t hq = static_cast<size_t>(h) * Npad;
@@ -828,7 +837,7 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
                       bool retry, int* seg, hipStream_t s) {
   // the uncertain band is ~8x narrower with fp16 filter operands than bf16
   // (about 37 and 280 keys at the headline size)
-  const int ucap = p.filt ? 512 : 128;
+  const int ucap = p.filt ? 512 : 128;   // at least 128: its filter scores hold the rank buffer
   const int lcap = rerank_lds_cap(p.capH, p.k, ucap);
   const size_t per_wave = rerank_lds_per_wave(lcap, ucap);
   int wpb = static_cast<int>((64 * 1024) / per_wave);

@@ -247,16 +247,16 @@ def test_largest_k_with_key_range_gather_all_rows():
     run_case(w, seed=77)
 
 
-@pytest.mark.parametrize("N,causal", [(1100, False), (9000, True), (20000, False)])
-def test_long_candidate_lists_ranked_from_memory_all_rows(N, causal):
-    """At k = 512 with fp16 filter operands the re-rank's LDS room (896
-    candidates, so that four waves share a SIMD) is smaller than a query's two
-    lists (640 each): queries with more candidates are ranked from their lists
-    in memory.  N = 1100: every query keeps all its keys (1100 candidates);
-    causal N = 9000: all-key rows on both sides of the room and threshold
-    rows; N = 20000: threshold rows only, a few above the room (three row
-    ranges checked)."""
-    w = W.Workload("case", 1, 2, N, 64, "bf16", d_proj=64, k=512, causal=causal)
+@pytest.mark.parametrize("N,k,causal", [(1100, 512, False), (9000, 512, True), (20000, 640, False)])
+def test_long_candidate_lists_ranked_from_memory_all_rows(N, k, causal):
+    """With fp16 filter operands the re-rank's LDS room (1024 candidates at
+    k = 512 and 640, so that four waves share a SIMD) is smaller than a
+    query's two lists (640 or 832 entries each): queries with more candidates
+    are ranked from their lists in memory.  N = 1100: every query keeps all
+    its keys (1100 candidates); causal N = 9000: all-key rows on both sides of
+    the room and threshold rows; N = 20000, k = 640: threshold rows, many
+    above the room (three row ranges checked)."""
+    w = W.Workload("case", 1, 2, N, 64, "bf16", d_proj=64, k=k, causal=causal)
     rows = [(0, 384), (9000, 384), (N - 384, 384)] if N > 10000 else None
     stats = run_case(w, seed=N + 3, rows=rows, filter_dtype=torch.float16)
     print(stats, flush=True)
