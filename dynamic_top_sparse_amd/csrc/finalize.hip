@@ -274,13 +274,24 @@ __host__ __device__ constexpr size_t rerank_lds_per_wave(int cap, int ucap) {
   return (512 + static_cast<size_t>(ucap) * 12 + static_cast<size_t>(cap) * 8 + 15) / 16 * 16;
 }
 
+// Re-rank waves per SIMD at most: the kernel is built for four
+// (amdgpu_waves_per_eu(4): at most 128 VGPRs).
+constexpr int kRerankWavesPerSimd = 4;
+
+// Workgroups of the re-rank one CU holds at once: LDS (160 KB per CU) and
+// the waves' registers both bound it.
+inline int rerank_groups_per_cu(int wpb, size_t per_wave) {
+  const int by_lds = static_cast<int>(163840 / (static_cast<size_t>(wpb) * per_wave));
+  const int by_regs = 4 * kRerankWavesPerSimd / wpb;
+  return max(1, min(by_lds, by_regs));
+}
+
 // Waves of the re-rank one CU holds for a per-wave LDS size (workgroups of
-// up to four waves within 64 KB, 160 KB per CU, four waves per SIMD at most).
+// up to four waves within 64 KB).
 inline int rerank_waves_per_cu(size_t per_wave) {
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
-  const int per_cu = static_cast<int>(163840 / (static_cast<size_t>(wpb) * per_wave));
-  return per_cu * wpb < 16 ? per_cu * wpb : 16;
+  return rerank_groups_per_cu(wpb, per_wave) * wpb;
 }
 
 // LDS candidate room of a re-rank wave: the whole list capacity (2 capH)
@@ -303,7 +314,7 @@ inline int rerank_lds_cap(int capH, int k, int ucap) {
 }
 
 template <int DP>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void finalize_kernel(
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(kRerankWavesPerSimd))) void finalize_kernel(
     const uint2* __restrict__ cand, const int* __restrict__ cnt, const int* __restrict__ rcnt,
     float* __restrict__ tau,
     const float* __restrict__ thr,
@@ -843,10 +854,10 @@ hipError_t finalize_t(const Plan& p, const Bufs& b, int nh, float scale, int32_t
   int wpb = static_cast<int>((64 * 1024) / per_wave);
   wpb = wpb < 1 ? 1 : (wpb > 4 ? 4 : wpb);
   // persistent waves striding over the queries of their head: as many
-  // workgroups as the chip holds at once (LDS bounds how many fit on a CU),
-  // so every wave works until the end instead of a last, partial round
-  const size_t lds_wg = static_cast<size_t>(wpb) * per_wave;
-  const int per_cu = static_cast<int>(max(static_cast<size_t>(1), 163840 / lds_wg));
+  // workgroups as the chip holds at once (LDS or registers bound how many
+  // fit on a CU), so every wave works until the end: a workgroup beyond them
+  // would start only when one finishes and then run its whole share alone
+  const int per_cu = rerank_groups_per_cu(wpb, per_wave);
   const int resident = resident_cus() * per_cu;
   int gx = (p.N + wpb - 1) / wpb;
   const int per_head = (resident + nh - 1) / nh;
