@@ -278,34 +278,45 @@ __global__ __launch_bounds__(kThreads) void gather_merge_kernel(const float* __r
   const int q = (gridDim.x - 1 - blockIdx.x) * kWaves + w;
   if (q >= N) return;
   const float* recs = part + static_cast<size_t>(q) * R * (D + 4);
-  float m = -INFINITY, lsum = 0.0f;
-  if (l < R) {
-    m = recs[static_cast<size_t>(l) * (D + 4)];
-    if (m != -INFINITY) lsum = recs[static_cast<size_t>(l) * (D + 4) + 1];
+  // Every load is issued at once: the maxima with their sums and the
+  // partial rows (an empty range's row and sum hold stale values, so they
+  // are selected away, never multiplied by its weight 0).
+  const int lr = l < R ? l : 0;
+  const float m0 = recs[static_cast<size_t>(lr) * (D + 4)];
+  const float s0 = recs[static_cast<size_t>(lr) * (D + 4) + 1];
+  float a[R][EPM];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const float* src = recs + static_cast<size_t>(r) * (D + 4) + 4 + l * EPM;
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) a[r][e] = src[e];
   }
+  // (the compiler would otherwise sink loads past the reductions, or into
+  // the branch it makes of the first range's select: a second round trip)
+  asm volatile("" ::"v"(m0), "v"(s0));
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int e = 0; e < EPM; ++e) asm volatile("" ::"v"(a[r][e]));
+  const float m = l < R ? m0 : -INFINITY;
+  const float lsum = m != -INFINITY ? s0 : 0.0f;
   const float M = wave_max(m);
   T* out = O + static_cast<size_t>(q) * D + l * EPM;
   float acc[EPM];
 #pragma unroll
   for (int e = 0; e < EPM; ++e) acc[e] = 0.0f;
-  if (M == -INFINITY) {  // no valid entry: zero output
-#pragma unroll
-    for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(0.0f);
-    return;
-  }
   const float wr = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
   const float L = wave_sum(wr * lsum);
-#pragma unroll 4
+#pragma unroll
   for (int r = 0; r < R; ++r) {
     const float wv = __shfl(wr, r, kWave);
-    if (wv != 0.0f) {
-      const float* a = recs + static_cast<size_t>(r) * (D + 4) + 4 + l * EPM;
 #pragma unroll
-      for (int e = 0; e < EPM; ++e) acc[e] = __builtin_fmaf(wv, a[e], acc[e]);
-    }
+    for (int e = 0; e < EPM; ++e) acc[e] = wv != 0.0f ? __builtin_fmaf(wv, a[r][e], acc[e]) : acc[e];
   }
+  // no valid entry in any range (M = -inf, L = 0): a zero row
+  const bool none = M == -INFINITY;
 #pragma unroll
-  for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(acc[e] / L);
+  for (int e = 0; e < EPM; ++e) out[e] = io<T>::from_f32(none ? 0.0f : acc[e] / L);
 }
 
 template <typename T, int D>
