@@ -368,50 +368,67 @@ __global__ __launch_bounds__(kThreads) void bwd_row_ranges_kernel(const int32_t*
 
 // Row parts -> dQ (out_scale times G) and the row's statistics
 // (max logit, 1/S, delta); a part record is (m, S, U, -, A[D], B[D]).
+// Every load of a row is issued at once (an empty part's record holds stale
+// values: its terms are selected away, never multiplied by a zero weight).
+template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_rows_merge_kernel(const float* __restrict__ part,
-                                                                  int N, int D, float out_scale,
+                                                                  int N, float out_scale,
                                                                   float* __restrict__ dQ,
                                                                   float4* __restrict__ stats) {
   constexpr int R = kGatherRanges;
+  constexpr int PS = 2 * D + 4;
+  constexpr int EPL = D / kWave;
   const int w = threadIdx.x / kWave, l = lane_id();
   const int q = blockIdx.x * (kThreads / kWave) + w;
   if (q >= N) return;
   const size_t row = static_cast<size_t>(blockIdx.y) * N + q;
-  const int PS = 2 * D + 4;
   const float* pr = part + row * R * PS;
+  float mr[R], sr[R], ur[R], av[R][EPL], bv[R][EPL];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    mr[r] = pr[r * PS];
+    sr[r] = pr[r * PS + 1];
+    ur[r] = pr[r * PS + 2];
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) {
+      av[r][i] = pr[r * PS + 4 + l + kWave * i];
+      bv[r][i] = pr[r * PS + 4 + D + l + kWave * i];
+    }
+  }
+  // (keeps the compiler from sinking loads past the reductions below)
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    asm volatile("" ::"v"(mr[r]), "v"(sr[r]), "v"(ur[r]));
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) asm volatile("" ::"v"(av[r][i]), "v"(bv[r][i]));
+  }
   float M = -INFINITY;
 #pragma unroll
-  for (int r = 0; r < R; ++r) M = fmaxf(M, pr[r * PS]);
-  float* dq = dQ + row * D;
-  if (M == -INFINITY) {     // no valid entry in any part
-    for (int e = l; e < D; e += kWave) dq[e] = 0.0f;
-    if (l == 0) stats[row] = make_float4(-INFINITY, 0.0f, 0.0f, 0.0f);
-    return;
-  }
+  for (int r = 0; r < R; ++r) M = fmaxf(M, mr[r]);
   float c[R];
   float S = 0.0f, U = 0.0f;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const float m = pr[r * PS];
+    const float m = mr[r];
     c[r] = m == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m - M);
-    if (m != -INFINITY) {
-      S = __builtin_fmaf(c[r], pr[r * PS + 1], S);
-      U = __builtin_fmaf(c[r], pr[r * PS + 2], U);
-    }
+    S = m != -INFINITY ? __builtin_fmaf(c[r], sr[r], S) : S;
+    U = m != -INFINITY ? __builtin_fmaf(c[r], ur[r], U) : U;
   }
+  const bool none = M == -INFINITY;     // no valid entry in any part
   const float inv = 1.0f / S, delta = U * inv;
-  for (int e = l; e < D; e += kWave) {
+  float* dq = dQ + row * D;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
     float a = 0.0f, bsum = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      if (c[r] != 0.0f) {
-        a = __builtin_fmaf(c[r], pr[r * PS + 4 + e], a);
-        bsum = __builtin_fmaf(c[r], pr[r * PS + 4 + D + e], bsum);
-      }
+      a = c[r] != 0.0f ? __builtin_fmaf(c[r], av[r][i], a) : a;
+      bsum = c[r] != 0.0f ? __builtin_fmaf(c[r], bv[r][i], bsum) : bsum;
     }
-    dq[e] = out_scale * ((a - delta * bsum) * inv);
+    dq[l + kWave * i] = none ? 0.0f : out_scale * ((a - delta * bsum) * inv);
   }
-  if (l == 0) stats[row] = make_float4(M, inv, delta, 0.0f);
+  if (l == 0)
+    stats[row] = none ? make_float4(-INFINITY, 0.0f, 0.0f, 0.0f) : make_float4(M, inv, delta, 0.0f);
 }
 
 // Key parts (dV[D], H[D]) -> dV and dK (out_scale times H), parts in order.
@@ -1443,8 +1460,14 @@ hipError_t launch_bwd_row_ranges(const int32_t* idx, const int* bounds, int nh, 
 hipError_t launch_bwd_rows_merge(const float* part, int nh, int N, int D, float out_scale,
                                  float* dQ, float4* stats, hipStream_t s) {
   const dim3 grid((N + kThreads / kWave - 1) / (kThreads / kWave), nh);
-  hipLaunchKernelGGL(bwd_rows_merge_kernel, grid, dim3(kThreads), 0, s, part, N, D, out_scale, dQ,
-                     stats);
+  if (D == 128)
+    hipLaunchKernelGGL(bwd_rows_merge_kernel<128>, grid, dim3(kThreads), 0, s, part, N, out_scale,
+                       dQ, stats);
+  else if (D == 64)
+    hipLaunchKernelGGL(bwd_rows_merge_kernel<64>, grid, dim3(kThreads), 0, s, part, N, out_scale,
+                       dQ, stats);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
